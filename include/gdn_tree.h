@@ -1,0 +1,195 @@
+/*
+ * gdn_tree.h - C ABI of libgdntree: tree-structured gated-delta-rule (GDN)
+ * speculative verification and accepted-path commit on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * What is computed (all citations name the page and the place on it):
+ *
+ *   Gated delta rule, state S in R^{d_v x d_k} (TreeWY: Speculative
+ *   Verification for Gated DeltaNet Hybrids, Sec. 1; Bole review, Sec. 1,
+ *   Eq. (1), which stores the same state transposed):
+ *       S~ = a_i S_parent,  u = b_i (v_i - S~ k_i),  S_i = S~ + u k_i^T,  o_i = S_i q_i
+ *   On a draft tree node i starts from the state of its parent pi(i), not of the
+ *   previous packed row (Bole review, Sec. 3.1; GDN Tree-Scan review,
+ *   "Background" and the packed-buffer example).  parent = -1 means the
+ *   committed state S_pre.
+ *
+ *   Four entry points, in the order one speculative step calls them:
+ *     gdn_tree_desc_build   shared descriptor: validation, depth, strict-ancestor
+ *                           mask, conv gather sources (LumoTree, Sec. III-C and V-C)
+ *     conv_ancestry_gather  causal conv1d whose window for node i is its own
+ *                           ancestry, then the conv history (LumoTree, Sec. V-C)
+ *     gdn_tree_verify       every node's output o_i; S_pre is read, never written
+ *                           (LumoTree, Sec. IV-A; Bole review, Algorithm 2 Phase A)
+ *     gdn_tree_commit       replay the accepted root-to-frontier path from S_pre,
+ *                           publish the state in place, and publish the conv
+ *                           history along the same path (LumoTree, Sec. IV-B and
+ *                           V-A; Bole review, Algorithm 2 Phase C)
+ *
+ * Conventions shared by every call
+ *   - Every pointer is device memory unless the comment says "host".  The
+ *     caller owns every buffer; the library allocates nothing and keeps no
+ *     mutable global state (reentrant).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     the library never synchronises with the host.  The caller orders
+ *     desc_build -> conv -> verify -> commit on one stream.
+ *   - Return value: GDN_OK, or a negative GDN_ERR_* found synchronously before
+ *     any launch (bad argument / unsupported size), or GDN_ERR_HIP if a launch
+ *     failed.  Nothing is launched when a negative value is returned.
+ *   - Data-dependent errors are found on the device and OR-ed (atomic) into the
+ *     int32 word `*err` as GDN_EV_* bits; the caller zeroes it.  The request at
+ *     fault is skipped as a whole: none of its outputs, state or history is
+ *     written, and no kernel reads or writes out of bounds.
+ *   - Logical nodes: N per request, 1 <= N <= 64, topologically ordered
+ *     (parent[i] < i).  Physical rows: R per request, node i lives in row
+ *     node_row[i]; rows no node maps to (padding) are never read or written.
+ *   - Row-major layouts; "[B][R][C]" means element (b, r, c) is at
+ *     ((b*R + r)*C + c).
+ */
+#ifndef GDN_TREE_H
+#define GDN_TREE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes ---------------------------------------------------- */
+#define GDN_OK 0
+#define GDN_ERR_ARG (-1)         /* null pointer, negative size, unknown enum */
+#define GDN_ERR_UNSUPPORTED (-4) /* a size the kernels do not implement */
+#define GDN_ERR_HIP (-5)         /* a kernel launch failed */
+
+/* ---- device error bits (OR-ed into *err) ------------------------------- */
+#define GDN_EV_PARENT 1 /* parent[i] outside [-1, i-1] */
+#define GDN_EV_ROW 2    /* node_row[i] outside [0, R) or two nodes share a row */
+#define GDN_EV_STATE 4  /* state_idx[b] outside [0, P); commit also: shared by two requests */
+#define GDN_EV_PATH 8   /* path_len outside [0, Lmax] or path not a parent chain from a
+                           node whose parent is -1 */
+
+/* ---- operand dtypes and flags ----------------------------------------- */
+#define GDN_DT_BF16 0 /* q, k, v are bfloat16 */
+#define GDN_DT_F32 1  /* q, k, v are float32 */
+
+#define GDN_F_NORM_QK 1  /* q, k <- x / sqrt(sum x^2 + 1e-6) inside verify and commit */
+#define GDN_F_OUT_BF16 2 /* verify writes o as bfloat16 (default float32) */
+#define GDN_F_VALU 4     /* verify: force the generic vector-ALU kernel (testing) */
+
+#define GDN_ACT_NONE 0
+#define GDN_ACT_SILU 1 /* z / (1 + exp(-z)) */
+
+#define GDN_MAX_NODES 64
+#define GDN_MAX_CONV_W 4
+
+/* ---- shared tree descriptor (LumoTree, Sec. III-C: parents, depth and the
+ *      logical->physical map read by every stage) -------------------------
+ * The struct itself is host memory; its arrays are device memory.  With
+ * shared = 1 the arrays hold one tree used by all B requests (T = 1),
+ * otherwise one tree per request (T = B). */
+typedef struct gdn_tree_desc {
+    int32_t B;       /* requests, >= 1 */
+    int32_t N;       /* logical nodes per request, 1..64 */
+    int32_t R;       /* physical rows per request, >= N */
+    int32_t W;       /* conv taps, 1..4 (W-1 history entries per request) */
+    int32_t shared;  /* 1: one topology for all requests; 0: one per request */
+    int32_t reserved;
+    const int32_t *parent;   /* in  [T][N]: parent node, -1 = child of S_pre */
+    const int32_t *node_row; /* in  [T][N]: physical row of each node */
+    int32_t *depth;          /* out [T][N]: nodes on the root-to-i path (1 if parent is -1) */
+    uint64_t *anc;           /* out [T][N]: bit j set iff j is a strict ancestor of i */
+    int32_t *conv_src;       /* out [T][N][W-1] (may be NULL when W == 1): conv tap
+                                sources, oldest first; r >= 0 is physical row r of the
+                                request, -(s+1) is conv-history entry s (s = W-2 is the
+                                most recent).  Walk: parent, grandparent, ..., then
+                                history entries W-2, W-3, ... */
+    int32_t *status;         /* out [T]: 0 = valid tree, else GDN_EV_PARENT/GDN_EV_ROW bits */
+} gdn_tree_desc;
+
+/* Validate each tree and build depth, anc, conv_src and status.  A tree with
+ * a nonzero status gets depth = anc = conv_src = 0 and is skipped by every
+ * later call (which then sets no further bit for it).
+ * Cite: LumoTree, Sec. III-C (descriptor drives every stage), Sec. V-C (static
+ * gather indices from the topology); Bole review, Sec. 3.1 (A(i), strict
+ * ancestors) and Algorithm 1 step 4 (ancestor mask M-). */
+int32_t gdn_tree_desc_build(const gdn_tree_desc *d, int32_t *err, void *stream);
+
+/* Ancestry-gathered causal conv1d (LumoTree, Sec. V-C: windows from prior
+ * conv history and candidate inputs, taps in order oldest -> newest, cast
+ * point after the taps):
+ *   y[b][row_i][c] = bf16( act( sum_{t<W-1} w[c][t] * X(conv_src[i][t])[c]
+ *                               + w[c][W-1] * x[b][row_i][c] + bias[c] ) )
+ * X(r >= 0) = x[b][r][c]; X(-(s+1)) = hist[state_idx[b]][s][c].  Accumulation
+ * in float32 in that order, one round-to-nearest-even to bf16 at the end.
+ *   x     bf16 [B][R][C]      hist bf16 [P][W-1][C] (read only here)
+ *   w     bf16 [C][W]         bias float32 [C] or NULL
+ *   y     bf16 [B][R][C]      only node rows written
+ *   state_idx int32 [B]: history slot of each request (checked against P).
+ * C must be a positive multiple of 4; x, hist, y 8-byte aligned.  act is
+ * GDN_ACT_NONE or GDN_ACT_SILU. */
+int32_t conv_ancestry_gather(const gdn_tree_desc *d, const void *x, const void *hist,
+                             int32_t P, const int32_t *state_idx, const void *w,
+                             const float *bias, void *y, int32_t C, int32_t act,
+                             int32_t *err, void *stream);
+
+/* Tree verify: o_i for every node i and value head h (TreeWY, Sec. 1; Bole
+ * review, Sec. 1 Eq. (1) and Sec. 3.1-3.5: the result equals the sequential
+ * recurrence from each node's parent, computed without materialising any
+ * node's state).
+ *   q, k   [B][R] rows; row (b, r) starts at ((b*R + r) * row_stride_qk) and
+ *          holds Hqk heads of dk elements (head g at offset g*dk)
+ *   v      [B][R] rows of stride row_stride_v, Hv heads of dv elements
+ *          (strides let q/k/v alias the conv output: stride C, q at 0,
+ *          k at Hqk*dk, v at 2*Hqk*dk)
+ *   alpha, beta  float32 [B][R][Hv]: decay a_i and write strength b_i,
+ *          already activated
+ *   state_pool   float32 [P][Hv][dv][dk]: committed states, read only
+ *   state_idx    int32 [B]: pool slot of each request
+ *   out    [B][R][Hv][dv] float32 (bf16 with GDN_F_OUT_BF16); node rows only
+ * Value head h reads qk head floor(h*Hqk/Hv).  dk == dv in {32, 64, 128};
+ * Hv % Hqk == 0.  dtype GDN_DT_BF16 or GDN_DT_F32.  bf16 operands at d = 128
+ * run on the matrix cores (fp32 state split into two bf16 halves, fp32
+ * accumulation); other shapes, or GDN_F_VALU, run a vector-ALU kernel. */
+int32_t gdn_tree_verify(const gdn_tree_desc *d, const void *q, const void *k, const void *v,
+                        int64_t row_stride_qk, int64_t row_stride_v, const float *alpha,
+                        const float *beta, const float *state_pool, int32_t P,
+                        const int32_t *state_idx, void *out, int32_t Hqk, int32_t Hv,
+                        int32_t dk, int32_t dv, int32_t dtype, int32_t flags,
+                        int32_t *err, void *stream);
+
+/* Accepted-path commit (LumoTree, Sec. IV-B: recorded accepted operands are
+ * replayed through the gated delta update, in place into the fp32 state bank;
+ * Sec. V-A: one device path drives recurrent replay and conv publication,
+ * padded path entries never advance state; Bole review, Algorithm 2 step 8:
+ * nothing accepted leaves the state as it was).
+ *   path      int32 [B][Lmax]: logical node ids, root-level node first; must
+ *             satisfy parent[path[0]] == -1 and parent[path[j]] == path[j-1]
+ *   path_len  int32 [B]: 0..Lmax; 0 leaves state and history untouched
+ *   k, v, alpha, beta, row strides, Hqk, Hv, dk, dv, dtype: as in verify (the
+ *             same buffers verify read)
+ *   state_pool float32 [P][Hv][dv][dk], updated in place for slot state_idx[b]
+ *   x, hist   optional (both NULL or both set; ignored when the descriptor's
+ *             W is 1): conv input bf16 [B][R][C] and conv history bf16
+ *             [P][W-1][C]; the history of slot state_idx[b] becomes the last
+ *             W-1 entries of (old history ++ x rows of the path).
+ * flags: GDN_F_NORM_QK (must match verify).  state_idx values must be
+ * distinct across requests (a shared slot is GDN_EV_STATE for both). */
+int32_t gdn_tree_commit(const gdn_tree_desc *d, const int32_t *path, const int32_t *path_len,
+                        int32_t Lmax, const void *k, const void *v, int64_t row_stride_qk,
+                        int64_t row_stride_v, const float *alpha, const float *beta,
+                        float *state_pool, int32_t P, const int32_t *state_idx,
+                        const void *x, void *hist, int32_t C, int32_t Hqk, int32_t Hv,
+                        int32_t dk, int32_t dv, int32_t dtype, int32_t flags, int32_t *err,
+                        void *stream);
+
+/* Human-readable name of a return code (host; static string). */
+const char *gdn_status_string(int32_t status);
+
+/* ABI version of this header: 1. */
+int32_t gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_TREE_H */

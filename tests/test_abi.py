@@ -1,0 +1,96 @@
+"""The C-ABI library loads on the CPU host and exports every entry point that
+include/gdn_tree.h declares; argument checks return their codes before any
+device work (no kernel is launched here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import tree_speculative_verification_gdn_amd as g
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn_tree.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z0-9_]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(g.library_path()):
+        pytest.skip("libgdntree.so not built")
+    return g.load_library()
+
+
+def test_header_declares_the_four_entry_points():
+    decl = declared_functions()
+    for name in ("gdn_tree_desc_build", "conv_ancestry_gather", "gdn_tree_verify", "gdn_tree_commit"):
+        assert name in decl
+    assert set(decl) == set(g.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", g.library_path()], capture_output=True, text=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in syms, name
+
+
+def test_status_strings_and_version(lib):
+    assert lib.gdn_abi_version() == 1
+    assert lib.gdn_status_string(0) == b"ok"
+    assert lib.gdn_status_string(-1) == b"invalid argument"
+    assert lib.gdn_status_string(-4) == b"unsupported size"
+
+
+def _desc(**kw):
+    base = dict(B=2, N=7, R=8, W=4, shared=0, reserved=0, parent=16, node_row=32, depth=48,
+                anc=64, conv_src=80, status=96)
+    base.update(kw)
+    return g.gdn_tree_desc(**base)
+
+
+def test_argument_checks_fail_before_launch(lib):
+    # fake (never dereferenced) device addresses: validation rejects before any launch
+    err = ctypes.c_void_p(128)
+    assert lib.gdn_tree_desc_build(None, err, None) == g.GDN_ERR_ARG
+    assert lib.gdn_tree_desc_build(ctypes.byref(_desc(N=65)), err, None) == g.GDN_ERR_UNSUPPORTED
+    assert lib.gdn_tree_desc_build(ctypes.byref(_desc(N=0)), err, None) == g.GDN_ERR_UNSUPPORTED
+    assert lib.gdn_tree_desc_build(ctypes.byref(_desc(R=5)), err, None) == g.GDN_ERR_ARG
+    assert lib.gdn_tree_desc_build(ctypes.byref(_desc(W=5)), err, None) == g.GDN_ERR_UNSUPPORTED
+    assert lib.gdn_tree_desc_build(ctypes.byref(_desc(conv_src=None)), err, None) == g.GDN_ERR_ARG
+    assert lib.gdn_tree_desc_build(ctypes.byref(_desc()), None, None) == g.GDN_ERR_ARG
+    d = ctypes.byref(_desc())
+    p = ctypes.c_void_p(256)
+    # verify: bad head ratio, d_k != d_v, bad dtype, unknown flag, short row stride
+    V = lib.gdn_tree_verify
+    assert V(d, p, p, p, 2048, 4096, p, p, p, 4, p, p, 3, 32, 128, 128, 0, 0, err, None) == g.GDN_ERR_ARG
+    assert V(d, p, p, p, 2048, 4096, p, p, p, 4, p, p, 16, 32, 128, 64, 0, 0, err, None) == g.GDN_ERR_UNSUPPORTED
+    assert V(d, p, p, p, 2048, 4096, p, p, p, 4, p, p, 16, 32, 96, 96, 0, 0, err, None) == g.GDN_ERR_UNSUPPORTED
+    assert V(d, p, p, p, 2048, 4096, p, p, p, 4, p, p, 16, 32, 128, 128, 7, 0, err, None) == g.GDN_ERR_ARG
+    assert V(d, p, p, p, 2048, 4096, p, p, p, 4, p, p, 16, 32, 128, 128, 0, 64, err, None) == g.GDN_ERR_ARG
+    assert V(d, p, p, p, 100, 4096, p, p, p, 4, p, p, 16, 32, 128, 128, 0, 0, err, None) == g.GDN_ERR_ARG
+    assert V(d, None, p, p, 2048, 4096, p, p, p, 4, p, p, 16, 32, 128, 128, 0, 0, err, None) == g.GDN_ERR_ARG
+    # commit: Lmax out of range, x without hist
+    Cm = lib.gdn_tree_commit
+    assert Cm(d, p, p, 0, p, p, 2048, 4096, p, p, p, 4, p, None, None, 0, 16, 32, 128, 128, 0, 0, err, None) == g.GDN_ERR_UNSUPPORTED
+    assert Cm(d, p, p, 65, p, p, 2048, 4096, p, p, p, 4, p, None, None, 0, 16, 32, 128, 128, 0, 0, err, None) == g.GDN_ERR_UNSUPPORTED
+    assert Cm(d, p, p, 7, p, p, 2048, 4096, p, p, p, 4, p, p, None, 8, 16, 32, 128, 128, 0, 0, err, None) == g.GDN_ERR_ARG
+    # conv: channel count not a multiple of 4, bad activation
+    Cv = lib.conv_ancestry_gather
+    assert Cv(d, p, p, 4, p, p, None, p, 8190, 1, err, None) == g.GDN_ERR_UNSUPPORTED
+    assert Cv(d, p, p, 4, p, p, None, p, 8192, 2, err, None) == g.GDN_ERR_ARG
+
+
+def test_binding_refuses_when_library_missing(monkeypatch, tmp_path):
+    monkeypatch.setattr(g, "_lib", None)
+    monkeypatch.setattr(g, "library_path", lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError):
+        g.load_library()

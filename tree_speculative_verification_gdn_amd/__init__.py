@@ -1,0 +1,235 @@
+"""tree_speculative_verification_gdn_amd: tree-structured gated-delta-rule
+verification and accepted-path commit for AMD Instinct MI355X (gfx950).
+
+This module is the thin Python binding of the C ABI in ``include/gdn_tree.h``
+(``libgdntree.so``, built from ``csrc/`` by ``_build.py``).  It marshals torch
+device tensors into pointers, sizes and the caller's HIP stream; every step of
+the computation runs in the library's HIP kernels.  There is no fallback: if
+the shared library is missing, every call raises.
+
+Entry points (same names as the C ABI):
+    gdn_tree_desc_build, conv_ancestry_gather, gdn_tree_verify, gdn_tree_commit
+Helper: TreeDesc (owns the descriptor's device arrays and the C struct).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = [
+    "GDN_OK", "GDN_ERR_ARG", "GDN_ERR_UNSUPPORTED", "GDN_ERR_HIP",
+    "GDN_EV_PARENT", "GDN_EV_ROW", "GDN_EV_STATE", "GDN_EV_PATH",
+    "GDN_DT_BF16", "GDN_DT_F32", "GDN_F_NORM_QK", "GDN_F_OUT_BF16", "GDN_F_VALU",
+    "GDN_ACT_NONE", "GDN_ACT_SILU", "GdnError", "TreeDesc", "library_path", "load_library",
+    "gdn_tree_desc_build", "conv_ancestry_gather", "gdn_tree_verify", "gdn_tree_commit",
+]
+
+# values mirror include/gdn_tree.h
+GDN_OK, GDN_ERR_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, -1, -4, -5
+GDN_EV_PARENT, GDN_EV_ROW, GDN_EV_STATE, GDN_EV_PATH = 1, 2, 4, 8
+GDN_DT_BF16, GDN_DT_F32 = 0, 1
+GDN_F_NORM_QK, GDN_F_OUT_BF16, GDN_F_VALU = 1, 2, 4
+GDN_ACT_NONE, GDN_ACT_SILU = 0, 1
+
+EXPORTED = ("gdn_tree_desc_build", "conv_ancestry_gather", "gdn_tree_verify",
+            "gdn_tree_commit", "gdn_status_string", "gdn_abi_version")
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lock = threading.Lock()
+_lib = None
+
+
+class GdnError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: status {code} ({_status_string(code)})")
+        self.code = code
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libgdntree.so")
+
+
+class gdn_tree_desc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("N", ctypes.c_int32), ("R", ctypes.c_int32),
+        ("W", ctypes.c_int32), ("shared", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("parent", ctypes.c_void_p), ("node_row", ctypes.c_void_p), ("depth", ctypes.c_void_p),
+        ("anc", ctypes.c_void_p), ("conv_src", ctypes.c_void_p), ("status", ctypes.c_void_p),
+    ]
+
+
+def load_library():
+    """Load libgdntree.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing; build it with __graft_entry__.build() "
+                               "(hipcc --offload-arch=gfx950)")
+        lib = ctypes.CDLL(path)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        dp = ctypes.POINTER(gdn_tree_desc)
+        lib.gdn_tree_desc_build.restype = i32
+        lib.gdn_tree_desc_build.argtypes = [dp, vp, vp]
+        lib.conv_ancestry_gather.restype = i32
+        lib.conv_ancestry_gather.argtypes = [dp, vp, vp, i32, vp, vp, vp, vp, i32, i32, vp, vp]
+        lib.gdn_tree_verify.restype = i32
+        lib.gdn_tree_verify.argtypes = [dp, vp, vp, vp, i64, i64, vp, vp, vp, i32, vp, vp,
+                                        i32, i32, i32, i32, i32, i32, vp, vp]
+        lib.gdn_tree_commit.restype = i32
+        lib.gdn_tree_commit.argtypes = [dp, vp, vp, i32, vp, vp, i64, i64, vp, vp, vp, i32, vp,
+                                        vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp]
+        lib.gdn_status_string.restype = ctypes.c_char_p
+        lib.gdn_status_string.argtypes = [i32]
+        lib.gdn_abi_version.restype = i32
+        lib.gdn_abi_version.argtypes = []
+        _lib = lib
+        return lib
+
+
+def _status_string(code: int) -> str:
+    try:
+        return load_library().gdn_status_string(int(code)).decode()
+    except Exception:  # pragma: no cover
+        return "?"
+
+
+# --------------------------------------------------------------------------
+# marshalling helpers
+# --------------------------------------------------------------------------
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return GDN_DT_BF16
+    if t.dtype == torch.float32:
+        return GDN_DT_F32
+    raise ValueError(f"unsupported operand dtype {t.dtype}")
+
+
+def _rows_view(t, name):
+    """(row stride in elements, heads, head dim) of a [B, R, H, D] view whose
+    element (b, r, h, d) sits at (b*R + r)*row_stride + h*D + d."""
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B, R, H, D]")
+    B, R, H, D = t.shape
+    s0, s1, s2, s3 = t.stride()
+    if s3 != 1 or s2 != D or (B > 1 and s0 != R * s1):
+        raise ValueError(f"{name}: layout not expressible as rows of stride {s1}")
+    return s1, H, D
+
+
+def _check(code, what, raise_on_error):
+    if raise_on_error and code < 0:
+        raise GdnError(code, what)
+    return code
+
+
+class TreeDesc:
+    """Descriptor of B requests' draft trees (one per request, or one shared).
+
+    Holds the input arrays (parent, node_row: int32 [T][N] on the device) and
+    the device outputs gdn_tree_desc_build fills (depth, anc, conv_src,
+    status), plus the C struct pointing at them.  Allocation is torch's.
+    """
+
+    def __init__(self, parent, node_row, R: int, W: int = 1, B: int | None = None,
+                 shared: bool = False):
+        import torch
+        if parent.dtype != torch.int32 or node_row.dtype != torch.int32:
+            raise ValueError("parent and node_row must be int32")
+        self.parent = parent.contiguous()
+        self.node_row = node_row.contiguous()
+        T, N = self.parent.shape
+        self.B = int(B if B is not None else T)
+        self.N, self.R, self.W, self.shared = int(N), int(R), int(W), bool(shared)
+        dev = self.parent.device
+        self.depth = torch.zeros((T, N), dtype=torch.int32, device=dev)
+        self.anc = torch.zeros((T, N), dtype=torch.int64, device=dev)
+        self.conv_src = torch.zeros((T, N, max(W - 1, 1)), dtype=torch.int32, device=dev)
+        self.status = torch.zeros((T,), dtype=torch.int32, device=dev)
+        self.c = gdn_tree_desc(self.B, self.N, self.R, self.W, int(self.shared), 0,
+                               self.parent.data_ptr(), self.node_row.data_ptr(),
+                               self.depth.data_ptr(), self.anc.data_ptr(),
+                               self.conv_src.data_ptr() if W > 1 else None,
+                               self.status.data_ptr())
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+# --------------------------------------------------------------------------
+# entry points
+# --------------------------------------------------------------------------
+
+def gdn_tree_desc_build(desc: TreeDesc, err, stream=None, raise_on_error=True) -> int:
+    """Validate trees and build depth / ancestor mask / conv sources / status."""
+    code = load_library().gdn_tree_desc_build(desc.ref(), _ptr(err), _stream(stream))
+    return _check(code, "gdn_tree_desc_build", raise_on_error)
+
+
+def conv_ancestry_gather(desc: TreeDesc, x, hist, state_idx, w, bias, y, act: int, err,
+                         stream=None, raise_on_error=True) -> int:
+    """Ancestry-gathered causal conv1d: x [B][R][C] bf16, hist [P][W-1][C] bf16,
+    w [C][W] bf16, bias fp32 [C] or None -> y [B][R][C] bf16."""
+    C = int(x.shape[-1])
+    P = int(hist.shape[0]) if hist is not None else 1
+    code = load_library().conv_ancestry_gather(desc.ref(), _ptr(x), _ptr(hist), P,
+                                               _ptr(state_idx), _ptr(w), _ptr(bias), _ptr(y),
+                                               C, int(act), _ptr(err), _stream(stream))
+    return _check(code, "conv_ancestry_gather", raise_on_error)
+
+
+def gdn_tree_verify(desc: TreeDesc, q, k, v, alpha, beta, state_pool, state_idx, out, err,
+                    flags: int = 0, stream=None, raise_on_error=True) -> int:
+    """Every node's output.  q, k: [B, R, Hqk, D] views (row-strided), v: [B, R, Hv, D],
+    alpha/beta fp32 [B, R, Hv], state_pool fp32 [P, Hv, D, D], state_idx int32 [B],
+    out [B, R, Hv, D] fp32 (bf16 with GDN_F_OUT_BF16)."""
+    rs_qk, Hqk, dk = _rows_view(q, "q")
+    rs_k, Hk, dk2 = _rows_view(k, "k")
+    rs_v, Hv, dv = _rows_view(v, "v")
+    if rs_k != rs_qk or Hk != Hqk or dk2 != dk or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q and k must share layout and dtype with v")
+    P = int(state_pool.shape[0])
+    code = load_library().gdn_tree_verify(desc.ref(), _ptr(q), _ptr(k), _ptr(v), rs_qk, rs_v,
+                                          _ptr(alpha), _ptr(beta), _ptr(state_pool), P,
+                                          _ptr(state_idx), _ptr(out), Hqk, Hv, dk, dv,
+                                          _dtype_code(q), int(flags), _ptr(err), _stream(stream))
+    return _check(code, "gdn_tree_verify", raise_on_error)
+
+
+def gdn_tree_commit(desc: TreeDesc, path, path_len, k, v, alpha, beta, state_pool, state_idx,
+                    err, Hqk: int | None = None, flags: int = 0, x=None, hist=None,
+                    stream=None, raise_on_error=True) -> int:
+    """Replay path [B, Lmax] (len path_len [B]) into state_pool in place; with
+    x / hist also publish the conv history."""
+    rs_qk, Hk, dk = _rows_view(k, "k")
+    rs_v, Hv, dv = _rows_view(v, "v")
+    Hqk = Hk if Hqk is None else Hqk
+    P = int(state_pool.shape[0])
+    Lmax = int(path.shape[1])
+    C = int(x.shape[-1]) if x is not None else 0
+    code = load_library().gdn_tree_commit(desc.ref(), _ptr(path), _ptr(path_len), Lmax, _ptr(k),
+                                          _ptr(v), rs_qk, rs_v, _ptr(alpha), _ptr(beta),
+                                          _ptr(state_pool), P, _ptr(state_idx), _ptr(x),
+                                          _ptr(hist), C, Hqk, Hv, dk, dv, _dtype_code(k),
+                                          int(flags), _ptr(err), _stream(stream))
+    return _check(code, "gdn_tree_commit", raise_on_error)

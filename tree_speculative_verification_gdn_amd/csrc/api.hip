@@ -1,0 +1,132 @@
+// C ABI of libgdntree (declared in include/gdn_tree.h): synchronous argument
+// validation, then one asynchronous launch on the caller's stream.  No
+// allocation, no host synchronisation, no global mutable state.
+#include "gdn_internal.h"
+
+namespace {
+
+int32_t map_launch(hipError_t e) {
+    if (e == hipSuccess) return GDN_OK;
+    if (e == hipErrorNotSupported) return GDN_ERR_UNSUPPORTED;
+    return GDN_ERR_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int32_t check_desc(const gdn_tree_desc* d) {
+    if (d == nullptr) return GDN_ERR_ARG;
+    if (d->B < 1 || d->R < 1 || d->W < 1 || (d->shared != 0 && d->shared != 1)) return GDN_ERR_ARG;
+    if (d->N < 1 || d->N > GDN_MAX_NODES || d->W > GDN_MAX_CONV_W) return GDN_ERR_UNSUPPORTED;
+    if (d->R < d->N) return GDN_ERR_ARG;
+    if (!d->parent || !d->node_row || !d->depth || !d->anc || !d->status) return GDN_ERR_ARG;
+    if (d->W > 1 && !d->conv_src) return GDN_ERR_ARG;
+    if (!aligned(d->anc, 8)) return GDN_ERR_ARG;
+    return GDN_OK;
+}
+
+int32_t check_heads(int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv, int32_t dtype) {
+    if (Hqk < 1 || Hv < 1 || Hv % Hqk != 0) return GDN_ERR_ARG;
+    if (dtype != GDN_DT_BF16 && dtype != GDN_DT_F32) return GDN_ERR_ARG;
+    if (dk != dv) return GDN_ERR_UNSUPPORTED;
+    if (dk != 32 && dk != 64 && dk != 128) return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t gdn_abi_version(void) { return 1; }
+
+const char* gdn_status_string(int32_t status) {
+    switch (status) {
+        case GDN_OK:
+            return "ok";
+        case GDN_ERR_ARG:
+            return "invalid argument";
+        case GDN_ERR_UNSUPPORTED:
+            return "unsupported size";
+        case GDN_ERR_HIP:
+            return "kernel launch failed";
+        default:
+            return "unknown status";
+    }
+}
+
+int32_t gdn_tree_desc_build(const gdn_tree_desc* d, int32_t* err, void* stream) {
+    int32_t st = check_desc(d);
+    if (st != GDN_OK) return st;
+    if (!err) return GDN_ERR_ARG;
+    return map_launch(gdn::launch_desc_build(*d, err, static_cast<hipStream_t>(stream)));
+}
+
+int32_t conv_ancestry_gather(const gdn_tree_desc* d, const void* x, const void* hist, int32_t P,
+                             const int32_t* state_idx, const void* w, const float* bias, void* y,
+                             int32_t C, int32_t act, int32_t* err, void* stream) {
+    int32_t st = check_desc(d);
+    if (st != GDN_OK) return st;
+    if (!x || !state_idx || !w || !y || !err || P < 1) return GDN_ERR_ARG;
+    if (d->W > 1 && !hist) return GDN_ERR_ARG;
+    if (C < 4 || C % 4 != 0) return GDN_ERR_UNSUPPORTED;
+    if (act != GDN_ACT_NONE && act != GDN_ACT_SILU) return GDN_ERR_ARG;
+    if (!aligned(x, 8) || !aligned(y, 8) || (hist && !aligned(hist, 8))) return GDN_ERR_ARG;
+    return map_launch(gdn::launch_conv(*d, static_cast<const uint16_t*>(x),
+                                       static_cast<const uint16_t*>(hist), P, state_idx,
+                                       static_cast<const uint16_t*>(w), bias,
+                                       static_cast<uint16_t*>(y), C, act, err,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int32_t gdn_tree_verify(const gdn_tree_desc* d, const void* q, const void* k, const void* v,
+                        int64_t row_stride_qk, int64_t row_stride_v, const float* alpha,
+                        const float* beta, const float* state_pool, int32_t P,
+                        const int32_t* state_idx, void* out, int32_t Hqk, int32_t Hv, int32_t dk,
+                        int32_t dv, int32_t dtype, int32_t flags, int32_t* err, void* stream) {
+    int32_t st = check_desc(d);
+    if (st != GDN_OK) return st;
+    st = check_heads(Hqk, Hv, dk, dv, dtype);
+    if (st != GDN_OK) return st;
+    if (!q || !k || !v || !alpha || !beta || !state_pool || !state_idx || !out || !err || P < 1)
+        return GDN_ERR_ARG;
+    if ((flags & ~(GDN_F_NORM_QK | GDN_F_OUT_BF16 | GDN_F_VALU)) != 0) return GDN_ERR_ARG;
+    if (row_stride_qk < static_cast<int64_t>(Hqk) * dk || row_stride_v < static_cast<int64_t>(Hv) * dv)
+        return GDN_ERR_ARG;
+    if (!aligned(state_pool, 16)) return GDN_ERR_ARG;
+    gdn::VerifyArgs a{q, k, v, row_stride_qk, row_stride_v, alpha, beta, state_pool, P,
+                      state_idx, out, Hqk, Hv, dk, dtype, flags, err};
+    return map_launch(gdn::launch_verify(*d, a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t gdn_tree_commit(const gdn_tree_desc* d, const int32_t* path, const int32_t* path_len,
+                        int32_t Lmax, const void* k, const void* v, int64_t row_stride_qk,
+                        int64_t row_stride_v, const float* alpha, const float* beta,
+                        float* state_pool, int32_t P, const int32_t* state_idx, const void* x,
+                        void* hist, int32_t C, int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv,
+                        int32_t dtype, int32_t flags, int32_t* err, void* stream) {
+    int32_t st = check_desc(d);
+    if (st != GDN_OK) return st;
+    st = check_heads(Hqk, Hv, dk, dv, dtype);
+    if (st != GDN_OK) return st;
+    if (!path || !path_len || !k || !v || !alpha || !beta || !state_pool || !state_idx || !err ||
+        P < 1)
+        return GDN_ERR_ARG;
+    if (Lmax < 1 || Lmax > GDN_MAX_NODES) return GDN_ERR_UNSUPPORTED;
+    // the conv history exists only for W > 1; with W == 1 x and hist are ignored
+    if (d->W == 1) {
+        x = nullptr;
+        hist = nullptr;
+    }
+    if ((x == nullptr) != (hist == nullptr)) return GDN_ERR_ARG;
+    if (x != nullptr && C < 1) return GDN_ERR_ARG;
+    if (x != nullptr && (!aligned(x, 2) || !aligned(hist, 2))) return GDN_ERR_ARG;
+    if ((flags & ~GDN_F_NORM_QK) != 0) return GDN_ERR_ARG;
+    if (row_stride_qk < static_cast<int64_t>(Hqk) * dk || row_stride_v < static_cast<int64_t>(Hv) * dv)
+        return GDN_ERR_ARG;
+    if (!aligned(state_pool, 16)) return GDN_ERR_ARG;
+    gdn::CommitArgs a{path, path_len, Lmax, k, v, row_stride_qk, row_stride_v, alpha, beta,
+                      state_pool, P, state_idx, static_cast<const uint16_t*>(x),
+                      static_cast<uint16_t*>(hist), x ? C : 0, Hqk, Hv, dk, dtype, flags, err};
+    return map_launch(gdn::launch_commit(*d, a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

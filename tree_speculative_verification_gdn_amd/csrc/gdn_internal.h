@@ -1,0 +1,101 @@
+// Internal helpers shared by the gfx950 kernels of libgdntree (not part of
+// the ABI).  Host launchers declared here are defined in the kernel files
+// and called by api.hip after argument validation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn_tree.h"
+
+namespace gdn {
+
+constexpr int kMaxNodes = GDN_MAX_NODES;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T>
+__device__ __forceinline__ float load_elem(const T* p);
+template <>
+__device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p) {
+    return bf16_bits_to_f32(*p);
+}
+template <>
+__device__ __forceinline__ float load_elem<float>(const float* p) {
+    return *p;
+}
+
+// Make a wave-uniform value scalar (all lanes hold the same value).
+__device__ __forceinline__ uint32_t uniform_u32(uint32_t x) {
+    return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(x)));
+}
+
+// Map a hardware workgroup id to a logical work item so that logical
+// neighbours run on the same XCD (gfx950 deals consecutive workgroup ids out
+// round-robin over its 8 XCDs, each with its own L2).  Identity when the grid
+// is not a multiple of 8.
+__device__ __forceinline__ uint32_t xcd_local_order(uint32_t hw_id, uint32_t n) {
+    if ((n & 7u) != 0u) return hw_id;
+    return (hw_id & 7u) * (n >> 3) + (hw_id >> 3);
+}
+
+// ---- launchers (host) -------------------------------------------------
+hipError_t launch_desc_build(const gdn_tree_desc& d, int32_t* err, hipStream_t s);
+hipError_t launch_conv(const gdn_tree_desc& d, const uint16_t* x, const uint16_t* hist, int P,
+                       const int32_t* state_idx, const uint16_t* w, const float* bias,
+                       uint16_t* y, int C, int act, int32_t* err, hipStream_t s);
+
+struct VerifyArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    int64_t rs_qk, rs_v;
+    const float* alpha;
+    const float* beta;
+    const float* pool;
+    int P;
+    const int32_t* state_idx;
+    void* out;
+    int Hqk, Hv, D;
+    int dtype, flags;
+    int32_t* err;
+};
+// Returns hipErrorNotSupported (without launching) when no kernel covers the
+// shape; the API maps that to GDN_ERR_UNSUPPORTED.
+hipError_t launch_verify(const gdn_tree_desc& d, const VerifyArgs& a, hipStream_t s);
+bool verify_uses_mfma(const gdn_tree_desc& d, const VerifyArgs& a);
+size_t verify_valu_lds_bytes(int N, int D);
+
+struct CommitArgs {
+    const int32_t* path;
+    const int32_t* path_len;
+    int Lmax;
+    const void* k;
+    const void* v;
+    int64_t rs_qk, rs_v;
+    const float* alpha;
+    const float* beta;
+    float* pool;
+    int P;
+    const int32_t* state_idx;
+    const uint16_t* x;
+    uint16_t* hist;
+    int C;
+    int Hqk, Hv, D;
+    int dtype, flags;
+    int32_t* err;
+};
+hipError_t launch_commit(const gdn_tree_desc& d, const CommitArgs& a, hipStream_t s);
+size_t commit_lds_bytes(int Lmax, int D);
+
+}  // namespace gdn

@@ -1,0 +1,712 @@
+// Tree verify for the gated delta rule on gfx950.
+//
+// What: for every node i of every request b and value head h,
+//   S~ = a_i S_pi(i);  u_i = b_i (v_i - S~ k_i);  S_i = S~ + u_i k_i^T;  o_i = S_i q_i
+// with S_pi(i) = S_pre for parent -1 (TreeWY, Sec. 1; Bole review, Sec. 1 Eq. (1)
+// and Sec. 3.1).
+//
+// How (no node state is ever formed).  Expanding S_p x one level,
+//   S_p x = a_p S_pi(p) x + u_p (k_p . x),
+// so S_pi(i) x for x in {k_i, q_i} is the committed-state product S_pre x
+// carried down the root-to-parent path with one multiply-add per ancestor
+// (the unrolled form is Lemma 1 / Eq. (3)-(4) of the Bole review).  Per
+// (request, head) the kernel therefore needs
+//   (1) CT = [K; Q] S_pre^T      one dense 2N x d_k x d_v contraction,
+//   (2) the Gram entries k_j . k_i and k_j . q_i of ancestor pairs,
+//   (3) a per-value-row scan over the nodes in index order (parent[i] < i):
+//         y   = CT[k_i][r] + sum over ancestors j, root first:  y = a_j y + u_j[r] (k_j . k_i)
+//         u_i = b_i (v_i[r] - a_i y)
+//       and, in parallel over nodes once every u is known,
+//         z   = CT[q_i][r] + same walk with (k_j . q_i)
+//         o_i = a_i z + u_i[r] (k_i . q_i).
+// Value rows r are independent, so the scan needs no cross-lane traffic.
+// S_pre (64 KiB fp32 per head at d = 128) is read exactly once and dominates
+// the bytes: the kernel is HBM-bound once (1) runs on the matrix cores.
+//
+// Two kernels:
+//   verify_mfma_kernel<MB>  bf16 q/k/v, d = 128.  (1) and the Gram block run on
+//       v_mfma_f32_32x32x16_bf16: K/Q are exact in bf16; the fp32 state is split
+//       into hi + lo bf16 halves (S = hi + lo to ~2^-17 relative), two MFMAs per
+//       k-step, fp32 accumulation.
+//   verify_valu_kernel<D, T>  any supported d and dtype, plain fp32 FMAs.
+//
+// Work decomposition: one 256-thread workgroup per (request, value head); the
+// two value heads that share a qk head are placed on the same XCD so their
+// K/Q rows are read from HBM once.
+#include "gdn_internal.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------------------
+// LDS layout of the MFMA kernel (bytes)
+// ---------------------------------------------------------------------------
+constexpr int kD = 128;
+constexpr int kKQStride = 264;   // bf16 row of 128 + 8 bytes pad: conflict-free 8-byte reads
+constexpr int kCTStride = 512;   // fp32 row of 128
+
+// Node slots of the contraction: keys of node i at slot i, queries at slot
+// NP + i, NP = 32 * NPB >= N (a whole number of 32-row blocks, so a node's key
+// and query results sit in the same lane and register of different blocks).
+struct MfmaLds {
+    int a, v, kk, kq, kqs, nrm, sk, sq, al, be, rows, dep, anc, cidx, mf, mh, ml, cr, cq, total;
+    int mstride;  // bytes per row of the bf16 M halves
+};
+
+__host__ __device__ inline int align_up(int x, int a) { return (x + a - 1) / a * a; }
+
+__host__ __device__ inline MfmaLds mfma_lds_layout(int N, int NPB) {
+    MfmaLds L;
+    const int NP = 32 * NPB;
+    const int MB = 2 * NPB;
+    int off = 0;
+    L.mstride = NP * 2 + 8;
+    L.a = off;    off += align_up(MB * 32 * kKQStride, 16);  // K/Q rows (bf16)
+    L.v = off;    off += align_up(N * kD * 2, 16);           // V rows (bf16)
+    L.kk = off;   off += align_up(N * N * 4, 16);  // [i][p]: k_i . k_(ancestor at depth p+1)
+    L.kq = off;   off += align_up(N * N * 4, 16);  // [i][p]: q_i . k_(ancestor at depth p+1)
+    L.kqs = off;  off += align_up(N * 4, 16);      // q_i . k_i
+    L.nrm = off;  off += align_up(2 * NP * 4, 16); // squared norms by slot
+    L.sk = off;   off += align_up(N * 4, 16);
+    L.sq = off;   off += align_up(N * 4, 16);
+    L.al = off;   off += align_up(N * 4, 16);
+    L.be = off;   off += align_up(N * 4, 16);
+    L.rows = off; off += align_up(N * 4, 16);
+    L.dep = off;  off += align_up(N * 4, 16);
+    L.anc = off;  off += align_up(N * 8, 16);
+    L.cidx = off; off += align_up(N * N, 16);      // [i][p]: node at depth p+1 on i's root path
+    L.mf = off;   off += align_up(N * N * 4, 16);  // [i][p]: M[i][path node p] (fp32 scratch)
+    L.mh = off;   off += align_up(NP * L.mstride, 16);
+    L.ml = off;   off += align_up(NP * L.mstride, 16);
+    L.cr = off;   off += align_up(N * 4, 16);      // P_i / |k_i|
+    L.cq = off;   off += align_up(N * 4, 16);      // P_i / |q_i|
+    L.total = off;
+    return L;
+}
+
+// MFMA operand: 8 bf16 of one 128-element LDS row for k-step s and lane half
+// hf.  Slot e of the operand holds element 16s + 4hf + e (e < 4) or
+// 16s + 8 + 4hf + (e - 4) (e >= 4).  The B operand built from the state in
+// registers uses the same element order, which is all the contraction needs.
+__device__ __forceinline__ bf16x8_t lds_operand(const char* base, int row, int s, int hf) {
+    const char* p = base + row * kKQStride + (16 * s + 4 * hf) * 2;
+    const uint2 lo = *reinterpret_cast<const uint2*>(p);
+    const uint2 hi = *reinterpret_cast<const uint2*>(p + 16);
+    uint4 u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    return __builtin_bit_cast(bf16x8_t, u);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+    const bf16x2_t h = __builtin_convertvector((f32x2_t){a, b}, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// Split 8 fp32 values into bf16 hi and lo parts: x ~= hi + lo.
+__device__ __forceinline__ void split_hi_lo(const float4& x0, const float4& x1, bf16x8_t& hi,
+                                            bf16x8_t& lo) {
+    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        h[e] = cvt_pk_bf16(xs[2 * e], xs[2 * e + 1]);
+        const float r0 = xs[2 * e] - __uint_as_float(h[e] << 16);
+        const float r1 = xs[2 * e + 1] - __uint_as_float(h[e] & 0xffff0000u);
+        l[e] = cvt_pk_bf16(r0, r1);
+    }
+    hi = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
+    lo = __builtin_bit_cast(bf16x8_t, make_uint4(l[0], l[1], l[2], l[3]));
+}
+
+__device__ __forceinline__ float sumsq_bf16x4(uint2 u) {
+    const float a = __uint_as_float(u.x << 16), b = __uint_as_float(u.x & 0xffff0000u);
+    const float c = __uint_as_float(u.y << 16), d = __uint_as_float(u.y & 0xffff0000u);
+    return fmaf(a, a, fmaf(b, b, fmaf(c, c, d * d)));
+}
+
+__device__ __forceinline__ void store_out(void* out, size_t idx, float o, bool out_bf16) {
+    if (out_bf16)
+        static_cast<uint16_t*>(out)[idx] = f32_to_bf16_bits(o);
+    else
+        static_cast<float*>(out)[idx] = o;
+}
+
+}  // namespace
+
+// ===========================================================================
+// MFMA kernel: bf16 q/k/v, d_k = d_v = 128, N <= 32*NPB
+//
+// Matrix form of the same recurrence (Bole review, Sec. 3.2-3.5, Eq. (2)-(5)),
+// per (request, head), with P_i the product of the decays on the root-to-i
+// path and hats for the (optionally) normalised q, k:
+//   R = D_beta (V - D_P K^ S_pre^T),  G_ij = b_i (P_i/P_j) k^_i.k^_j  (j strict ancestor of i)
+//   O = D_P Q^ S_pre^T + C (I + G)^-1 R,  C_ij = (P_i/P_j) q^_i.k^_j  (j ancestor of i or i)
+// M = C (I + G)^-1 is formed row by row: M (I + G) = C gives, along node i's
+// own root path, M_ij = C_ij - sum_{j < m <= i on the path} M_im G_mj, a solve of
+// depth^2/2 multiply-adds per node (the tree's depth bounds it, as Lemma 3 of
+// the Bole review bounds the Neumann series) instead of a general solve.
+// The ratios P_i/P_j are taken as products of the decays strictly below j.
+// ===========================================================================
+__device__ __forceinline__ bf16x8_t lds_operand_m(const char* base, int stride, int row, int ks,
+                                                  int hf) {
+    const char* p = base + row * stride + (16 * ks + 4 * hf) * 2;
+    const uint2 lo = *reinterpret_cast<const uint2*>(p);
+    const uint2 hi = *reinterpret_cast<const uint2*>(p + 16);
+    return __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+template <int NPB>
+__global__ void __launch_bounds__(kThreads)
+    verify_mfma_kernel(int N, int R, int shared, const int32_t* __restrict__ node_row,
+                       const uint64_t* __restrict__ anc_g, const int32_t* __restrict__ depth_g,
+                       const int32_t* __restrict__ status, const uint16_t* __restrict__ q,
+                       const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                       int64_t rs_qk, int64_t rs_v, const float* __restrict__ alpha,
+                       const float* __restrict__ beta, const float* __restrict__ pool, int P,
+                       const int32_t* __restrict__ state_idx, void* __restrict__ out, int Hqk,
+                       int Hv, int norm, int out_bf16, int32_t* __restrict__ err) {
+    constexpr int NP = 32 * NPB;
+    constexpr int MB = 2 * NPB;                              // key blocks, then query blocks
+    constexpr int kKQItems = MB * 32 * 32 / kThreads;       // 8-byte K/Q chunks per thread
+    constexpr int kVItems = (NP * 32 + kThreads - 1) / kThreads;
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const MfmaLds L = mfma_lds_layout(N, NPB);
+    char* s_a = lds + L.a;
+    uint16_t* s_v = reinterpret_cast<uint16_t*>(lds + L.v);
+    float* s_kk = reinterpret_cast<float*>(lds + L.kk);
+    float* s_kq = reinterpret_cast<float*>(lds + L.kq);
+    float* s_kqs = reinterpret_cast<float*>(lds + L.kqs);
+    float* s_nrm = reinterpret_cast<float*>(lds + L.nrm);
+    float* s_sk = reinterpret_cast<float*>(lds + L.sk);
+    float* s_sq = reinterpret_cast<float*>(lds + L.sq);
+    float* s_al = reinterpret_cast<float*>(lds + L.al);
+    float* s_be = reinterpret_cast<float*>(lds + L.be);
+    int32_t* s_rows = reinterpret_cast<int32_t*>(lds + L.rows);
+    int32_t* s_dep = reinterpret_cast<int32_t*>(lds + L.dep);
+    uint64_t* s_anc = reinterpret_cast<uint64_t*>(lds + L.anc);
+    uint8_t* s_cidx = reinterpret_cast<uint8_t*>(lds + L.cidx);
+    float* s_mf = reinterpret_cast<float*>(lds + L.mf);
+    char* s_mh = lds + L.mh;
+    char* s_ml = lds + L.ml;
+    float* s_cr = reinterpret_cast<float*>(lds + L.cr);
+    float* s_cq = reinterpret_cast<float*>(lds + L.cq);
+    const int mstride = L.mstride;
+
+    const uint32_t unit = xcd_local_order(blockIdx.x, gridDim.x);
+    const int b = static_cast<int>(unit / Hv);
+    const int h = static_cast<int>(unit % Hv);
+    const int t = shared ? 0 : b;
+    if (status[t] != 0) return;
+    const int slot = state_idx[b];
+    if (slot < 0 || slot >= P) {
+        if (h == 0 && threadIdx.x == 0) atomicOr(err, GDN_EV_STATE);
+        return;
+    }
+    const int g = static_cast<int>((static_cast<int64_t>(h) * Hqk) / Hv);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int hf = lane >> 5;
+    const int l32 = lane & 31;
+    const int r_own = wave * 32 + l32;  // value row this lane owns in every MFMA
+    const size_t tb = static_cast<size_t>(t) * N;
+    const size_t rowb = static_cast<size_t>(b) * R;
+
+    // (a) metadata first (small, dependent loads), then the committed state
+    //     and every K/Q/V chunk, all in flight before any wait
+    if (tid < N) {
+        const int row = node_row[tb + tid];
+        s_rows[tid] = row;
+        s_anc[tid] = anc_g[tb + tid];
+        s_dep[tid] = depth_g[tb + tid];
+        const size_t gi = (rowb + row) * Hv + h;
+        s_al[tid] = alpha[gi];
+        s_be[tid] = beta[gi];
+    }
+    const float* Sb = pool + (static_cast<size_t>(slot) * Hv + h) * (kD * kD) +
+                      static_cast<size_t>(r_own) * kD + 4 * hf;
+    float4 sreg[16];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        sreg[2 * s] = *reinterpret_cast<const float4*>(Sb + 16 * s);
+        sreg[2 * s + 1] = *reinterpret_cast<const float4*>(Sb + 16 * s + 8);
+    }
+    uint2 kq_val[kKQItems];
+#pragma unroll
+    for (int u = 0; u < kKQItems; ++u) {
+        const int it = tid + u * kThreads;
+        const int sl = it >> 5;
+        const int ch = it & 31;
+        const int node = sl < NP ? sl : sl - NP;
+        kq_val[u] = make_uint2(0u, 0u);
+        if (node < N) {
+            const int row = node_row[tb + node];
+            const uint16_t* src = (sl < NP ? k : q) + (rowb + row) * rs_qk +
+                                  static_cast<size_t>(g) * kD + ch * 4;
+            kq_val[u] = *reinterpret_cast<const uint2*>(src);
+        }
+    }
+    uint2 v_val[kVItems];
+#pragma unroll
+    for (int u = 0; u < kVItems; ++u) {
+        const int it = tid + u * kThreads;
+        const int node = it >> 5;
+        v_val[u] = make_uint2(0u, 0u);
+        if (node < N) {
+            const int row = node_row[tb + node];
+            v_val[u] = *reinterpret_cast<const uint2*>(v + (rowb + row) * rs_v +
+                                                       static_cast<size_t>(h) * kD + (it & 31) * 4);
+        }
+    }
+    // M halves start as zero (entries off the ancestor pattern stay zero)
+    for (int e = tid; e < NP * mstride / 4; e += kThreads) {
+        reinterpret_cast<uint32_t*>(s_mh)[e] = 0u;
+        reinterpret_cast<uint32_t*>(s_ml)[e] = 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kKQItems; ++u) {
+        const int it = tid + u * kThreads;
+        const int sl = it >> 5;
+        const int ch = it & 31;
+        *reinterpret_cast<uint2*>(s_a + sl * kKQStride + ch * 8) = kq_val[u];
+        float ss = sumsq_bf16x4(kq_val[u]);  // a row's 32 chunks sit in 32 consecutive lanes
+#pragma unroll
+        for (int off = 16; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+        if (ch == 0) s_nrm[sl] = ss;
+    }
+#pragma unroll
+    for (int u = 0; u < kVItems; ++u) {
+        const int it = tid + u * kThreads;
+        const int node = it >> 5;
+        if (node < N) *reinterpret_cast<uint2*>(s_v + node * kD + (it & 31) * 4) = v_val[u];
+    }
+    __syncthreads();
+
+    // (b) per node: normalisation scales and the root path list
+    if (tid < N) {
+        s_sk[tid] = norm ? 1.0f / sqrtf(s_nrm[tid] + 1e-6f) : 1.0f;
+        s_sq[tid] = norm ? 1.0f / sqrtf(s_nrm[NP + tid] + 1e-6f) : 1.0f;
+        uint64_t m = s_anc[tid];
+        int p = 0;
+        while (m) {  // ancestors in index order are root first
+            const int j = __builtin_ctzll(m);
+            m &= m - 1ull;
+            s_cidx[tid * N + p++] = static_cast<uint8_t>(j);
+        }
+        s_cidx[tid * N + p] = static_cast<uint8_t>(tid);
+    }
+
+    // (c) Gram block on the matrix cores (exact bf16 products, fp32 sums):
+    //     k_i . k_j and q_i . k_j for every ancestor j, stored at j's depth
+    {
+        constexpr int kTiles = MB * NPB;  // all query/key row blocks x key column blocks
+        for (int tile = wave; tile < kTiles; tile += kThreads / 64) {
+            const int ta = tile / NPB;
+            const int tcol = tile % NPB;
+            f32x16_t acc = {};
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const bf16x8_t a = lds_operand(s_a, ta * 32 + l32, s, hf);
+                const bf16x8_t bb = lds_operand(s_a, tcol * 32 + l32, s, hf);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc, 0, 0, 0);
+            }
+            const int col = tcol * 32 + l32;
+            if (col < N) {
+                const int pos = s_dep[col] - 1;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int rs = ta * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
+                    const bool is_q = rs >= NP;
+                    const int i = is_q ? rs - NP : rs;
+                    if (i < N) {
+                        const bool anc_ij = ((s_anc[i] >> col) & 1ull) != 0ull;
+                        if (anc_ij) (is_q ? s_kq : s_kk)[i * N + pos] = acc[e];
+                        if (is_q && col == i) s_kqs[i] = acc[e];
+                    }
+                }
+            }
+        }
+    }
+
+    // (d) CT = [K;Q] S_pre^T on the matrix cores, state split into bf16 hi + lo
+    f32x16_t acc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x16_t{};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        bf16x8_t shi, slo;
+        split_hi_lo(sreg[2 * s], sreg[2 * s + 1], shi, slo);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const bf16x8_t a = lds_operand(s_a, mb * 32 + l32, s, hf);
+            acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, shi, acc[mb], 0, 0, 0);
+            acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, slo, acc[mb], 0, 0, 0);
+        }
+    }
+    __syncthreads();
+
+    // (e) row i of M = C (I + G)^-1 by back-substitution along i's root path
+    if (tid < N) {
+        const int i = tid;
+        const int d = s_dep[i];
+        const uint8_t* path = s_cidx + i * N;
+        float* mrow = s_mf + i * N;
+        const float sq_i = s_sq[i];
+        float wq = 1.0f;  // product of the decays on the path strictly below position p
+        for (int p = d - 1; p >= 0; --p) {
+            const int j = path[p];
+            const float sk_j = s_sk[j];
+            float val = wq * sq_i * sk_j * (p == d - 1 ? s_kqs[i] : s_kq[i * N + p]);
+            float wg = 1.0f;  // decays on the path strictly below p, up to and including s
+            for (int sidx = p + 1; sidx < d; ++sidx) {
+                const int m = path[sidx];
+                wg *= s_al[m];
+                const float gmj = s_be[m] * wg * s_sk[m] * sk_j * s_kk[m * N + p];
+                val = fmaf(-mrow[sidx], gmj, val);
+            }
+            mrow[p] = val;
+            const uint32_t hv = cvt_pk_bf16(val, 0.0f) & 0xffffu;
+            const float rest = val - __uint_as_float(hv << 16);
+            const uint32_t lv = cvt_pk_bf16(rest, 0.0f) & 0xffffu;
+            reinterpret_cast<uint16_t*>(s_mh + i * mstride)[j] = static_cast<uint16_t>(hv);
+            reinterpret_cast<uint16_t*>(s_ml + i * mstride)[j] = static_cast<uint16_t>(lv);
+            wq *= s_al[j];
+        }
+        // wq is now P_i
+        s_cr[i] = wq * s_sk[i];
+        s_cq[i] = wq * sq_i;
+    }
+    __syncthreads();
+
+    // (f) R = beta (v - P k^ S_pre) from the key blocks, as bf16 hi/lo MFMA
+    //     operands (a key block's output layout is a permutation of the
+    //     contraction index that the M operand reads in the same order)
+    bf16x8_t rhi[2 * NPB], rlo[2 * NPB];
+#pragma unroll
+    for (int kb = 0; kb < NPB; ++kb) {
+        float rv[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int i = kb * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
+            float val = 0.0f;
+            if (i < N)
+                val = s_be[i] * (bf16_bits_to_f32(s_v[i * kD + r_own]) - s_cr[i] * acc[kb][e]);
+            rv[e] = val;
+        }
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            uint32_t hh[4], ll[4];
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const float x0 = rv[8 * half + 2 * e2], x1 = rv[8 * half + 2 * e2 + 1];
+                hh[e2] = cvt_pk_bf16(x0, x1);
+                ll[e2] = cvt_pk_bf16(x0 - __uint_as_float(hh[e2] << 16),
+                                     x1 - __uint_as_float(hh[e2] & 0xffff0000u));
+            }
+            rhi[2 * kb + half] = __builtin_bit_cast(bf16x8_t, make_uint4(hh[0], hh[1], hh[2], hh[3]));
+            rlo[2 * kb + half] = __builtin_bit_cast(bf16x8_t, make_uint4(ll[0], ll[1], ll[2], ll[3]));
+        }
+    }
+    // (g) O = P q^ S_pre + M R, accumulated onto the query blocks; write out
+#pragma unroll
+    for (int ob = 0; ob < NPB; ++ob) {
+        f32x16_t o = acc[NPB + ob];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int i = ob * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
+            o[e] *= (i < N) ? s_cq[i] : 0.0f;
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2 * NPB; ++ks) {
+            if (ks > 2 * ob + 1) break;  // M is zero right of the diagonal block
+            const bf16x8_t mh = lds_operand_m(s_mh, mstride, ob * 32 + l32, ks, hf);
+            const bf16x8_t ml = lds_operand_m(s_ml, mstride, ob * 32 + l32, ks, hf);
+            o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mh, rhi[ks], o, 0, 0, 0);
+            o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mh, rlo[ks], o, 0, 0, 0);
+            o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ml, rhi[ks], o, 0, 0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int i = ob * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
+            if (i < N)
+                store_out(out, ((rowb + s_rows[i]) * Hv + h) * kD + r_own, o[e], out_bf16 != 0);
+        }
+    }
+}
+
+// ===========================================================================
+// Vector-ALU kernel: any d in {32, 64, 128}, bf16 or fp32 operands
+// ===========================================================================
+struct ValuLds {
+    int K, Q, V, U, kk, kq, al, be, anc, rows, scale, total;
+};
+
+__host__ __device__ inline ValuLds valu_lds_layout(int N, int D) {
+    ValuLds L;
+    int off = 0;
+    const int nd = align_up(N * D * 4, 16);
+    L.K = off;
+    off += nd;
+    L.Q = off;
+    off += nd;
+    L.V = off;
+    off += nd;
+    L.U = off;
+    off += nd;
+    L.kk = off;
+    off += align_up(N * N * 4, 16);
+    L.kq = off;
+    off += align_up(N * N * 4, 16);
+    L.al = off;
+    off += align_up(N * 4, 16);
+    L.be = off;
+    off += align_up(N * 4, 16);
+    L.anc = off;
+    off += align_up(N * 8, 16);
+    L.rows = off;
+    off += align_up(N * 4, 16);
+    L.scale = off;
+    off += align_up(2 * N * 4, 16);
+    L.total = off;
+    return L;
+}
+
+size_t verify_valu_lds_bytes(int N, int D) { return static_cast<size_t>(valu_lds_layout(N, D).total); }
+
+template <int D, typename T>
+__global__ void __launch_bounds__(kThreads)
+    verify_valu_kernel(int N, int R, int shared, const int32_t* __restrict__ node_row,
+                       const uint64_t* __restrict__ anc_g, const int32_t* __restrict__ status,
+                       const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+                       int64_t rs_qk, int64_t rs_v, const float* __restrict__ alpha,
+                       const float* __restrict__ beta, const float* __restrict__ pool, int P,
+                       const int32_t* __restrict__ state_idx, void* __restrict__ out, int Hqk,
+                       int Hv, int norm, int out_bf16, int32_t* __restrict__ err) {
+    constexpr int TPR = kThreads / D;  // lanes per value row
+    constexpr int EPT = D / TPR;       // state elements per lane
+    constexpr int NQ = EPT / 4;        // float4 chunks per lane
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const ValuLds L = valu_lds_layout(N, D);
+    float* s_K = reinterpret_cast<float*>(lds + L.K);
+    float* s_Q = reinterpret_cast<float*>(lds + L.Q);
+    float* s_V = reinterpret_cast<float*>(lds + L.V);
+    float* s_U = reinterpret_cast<float*>(lds + L.U);
+    float* s_kk = reinterpret_cast<float*>(lds + L.kk);
+    float* s_kq = reinterpret_cast<float*>(lds + L.kq);
+    float* s_al = reinterpret_cast<float*>(lds + L.al);
+    float* s_be = reinterpret_cast<float*>(lds + L.be);
+    uint64_t* s_anc = reinterpret_cast<uint64_t*>(lds + L.anc);
+    int32_t* s_rows = reinterpret_cast<int32_t*>(lds + L.rows);
+    float* s_scale = reinterpret_cast<float*>(lds + L.scale);
+
+    const uint32_t unit = xcd_local_order(blockIdx.x, gridDim.x);
+    const int b = static_cast<int>(unit / Hv);
+    const int h = static_cast<int>(unit % Hv);
+    const int t = shared ? 0 : b;
+    if (status[t] != 0) return;
+    const int slot = state_idx[b];
+    if (slot < 0 || slot >= P) {
+        if (h == 0 && threadIdx.x == 0) atomicOr(err, GDN_EV_STATE);
+        return;
+    }
+    const int g = static_cast<int>((static_cast<int64_t>(h) * Hqk) / Hv);
+    const int tid = threadIdx.x;
+    const int r = tid / TPR;
+    const int part = tid % TPR;
+
+    float4 sv[NQ];
+    const float* Sb = pool + (static_cast<size_t>(slot) * Hv + h) * (D * D) +
+                      static_cast<size_t>(r) * D;
+#pragma unroll
+    for (int c = 0; c < NQ; ++c)
+        sv[c] = *reinterpret_cast<const float4*>(Sb + 4 * (part + TPR * c));
+
+    const size_t tb = static_cast<size_t>(t) * N;
+    if (tid < N) {
+        const int row = node_row[tb + tid];
+        s_rows[tid] = row;
+        s_anc[tid] = anc_g[tb + tid];
+        const size_t gi = (static_cast<size_t>(b) * R + row) * Hv + h;
+        s_al[tid] = alpha[gi];
+        s_be[tid] = beta[gi];
+    }
+    __syncthreads();
+    for (int e = tid; e < N * D; e += kThreads) {
+        const int i = e / D, c = e % D;
+        const size_t rqk = (static_cast<size_t>(b) * R + s_rows[i]) * rs_qk + static_cast<size_t>(g) * D + c;
+        s_K[e] = load_elem(k + rqk);
+        s_Q[e] = load_elem(q + rqk);
+        s_V[e] = load_elem(v + (static_cast<size_t>(b) * R + s_rows[i]) * rs_v +
+                           static_cast<size_t>(h) * D + c);
+    }
+    __syncthreads();
+    if (norm) {
+        if (tid < 2 * N) {
+            const float* rowp = (tid < N) ? s_K + tid * D : s_Q + (tid - N) * D;
+            float ss = 0.f;
+            for (int c = 0; c < D; ++c) {
+                const float xv = rowp[(c + tid) % D];
+                ss = fmaf(xv, xv, ss);
+            }
+            s_scale[tid] = 1.0f / sqrtf(ss + 1e-6f);
+        }
+        __syncthreads();
+        for (int e = tid; e < N * D; e += kThreads) {
+            const int i = e / D;
+            s_K[e] *= s_scale[i];
+            s_Q[e] *= s_scale[N + i];
+        }
+        __syncthreads();
+    }
+    // Gram entries of ancestor pairs (and k_i . q_i)
+    for (int e = tid; e < N * N; e += kThreads) {
+        const int i = e / N, j = e % N;
+        if (j > i) continue;
+        const bool is_anc = ((s_anc[i] >> j) & 1ull) != 0ull;
+        if (!is_anc && j != i) continue;
+        const float* ki = s_K + i * D;
+        const float* qi = s_Q + i * D;
+        const float* kj = s_K + j * D;
+        float dkk = 0.f, dkq = 0.f;
+        for (int c0 = 0; c0 < D; ++c0) {
+            const int c = (c0 + e) % D;
+            dkk = fmaf(ki[c], kj[c], dkk);
+            dkq = fmaf(qi[c], kj[c], dkq);
+        }
+        s_kk[e] = dkk;
+        s_kq[e] = dkq;
+    }
+    __syncthreads();
+
+    for (int i = 0; i < N; ++i) {
+        const float* ki = s_K + i * D;
+        const float* qi = s_Q + i * D;
+        float yk = 0.f, yq = 0.f;
+#pragma unroll
+        for (int c = 0; c < NQ; ++c) {
+            const int col = 4 * (part + TPR * c);
+            const float4 kv = *reinterpret_cast<const float4*>(ki + col);
+            const float4 qv = *reinterpret_cast<const float4*>(qi + col);
+            yk = fmaf(sv[c].x, kv.x, yk);
+            yk = fmaf(sv[c].y, kv.y, yk);
+            yk = fmaf(sv[c].z, kv.z, yk);
+            yk = fmaf(sv[c].w, kv.w, yk);
+            yq = fmaf(sv[c].x, qv.x, yq);
+            yq = fmaf(sv[c].y, qv.y, yq);
+            yq = fmaf(sv[c].z, qv.z, yq);
+            yq = fmaf(sv[c].w, qv.w, yq);
+        }
+#pragma unroll
+        for (int off = 1; off < TPR; off <<= 1) {
+            yk += __shfl_xor(yk, off, 64);
+            yq += __shfl_xor(yq, off, 64);
+        }
+        uint64_t am = s_anc[i];
+        while (am) {
+            const int j = __builtin_ctzll(am);
+            am &= am - 1ull;
+            const float uj = s_U[j * D + r];
+            yk = fmaf(s_al[j], yk, uj * s_kk[i * N + j]);
+            yq = fmaf(s_al[j], yq, uj * s_kq[i * N + j]);
+        }
+        const float u = s_be[i] * (s_V[i * D + r] - s_al[i] * yk);
+        const float o = fmaf(s_al[i], yq, u * s_kq[i * N + i]);
+        if (part == 0) {
+            s_U[i * D + r] = u;
+            const size_t oi = ((static_cast<size_t>(b) * R + s_rows[i]) * Hv + h) * D + r;
+            store_out(out, oi, o, out_bf16 != 0);
+        }
+    }
+}
+
+// ===========================================================================
+// dispatch
+// ===========================================================================
+namespace {
+constexpr size_t kMaxLds = 160 * 1024;
+
+template <typename K>
+hipError_t set_lds(K kernel, size_t bytes) {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+}
+
+template <int NPB>
+hipError_t launch_mfma_t(const gdn_tree_desc& d, const VerifyArgs& a, int norm, int obf,
+                         size_t lds, hipStream_t s) {
+    auto kfn = verify_mfma_kernel<NPB>;
+    hipError_t e = set_lds(kfn, lds);
+    if (e != hipSuccess) return e;
+    const dim3 grid(static_cast<unsigned>(d.B) * static_cast<unsigned>(a.Hv));
+    hipLaunchKernelGGL(kfn, grid, dim3(kThreads), lds, s, d.N, d.R, d.shared, d.node_row, d.anc,
+                       d.depth, d.status, static_cast<const uint16_t*>(a.q),
+                       static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
+                       a.rs_qk, a.rs_v, a.alpha, a.beta, a.pool, a.P, a.state_idx, a.out, a.Hqk,
+                       a.Hv, norm, obf, a.err);
+    return hipGetLastError();
+}
+
+template <int D, typename T>
+hipError_t launch_valu_t(const gdn_tree_desc& d, const VerifyArgs& a, int norm, int obf,
+                         size_t lds, hipStream_t s) {
+    auto kfn = verify_valu_kernel<D, T>;
+    hipError_t e = set_lds(kfn, lds);
+    if (e != hipSuccess) return e;
+    const dim3 grid(static_cast<unsigned>(d.B) * static_cast<unsigned>(a.Hv));
+    hipLaunchKernelGGL(kfn, grid, dim3(kThreads), lds, s, d.N, d.R, d.shared, d.node_row, d.anc,
+                       d.status, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                       static_cast<const T*>(a.v), a.rs_qk, a.rs_v, a.alpha, a.beta, a.pool, a.P,
+                       a.state_idx, a.out, a.Hqk, a.Hv, norm, obf, a.err);
+    return hipGetLastError();
+}
+}  // namespace
+
+bool verify_uses_mfma(const gdn_tree_desc& d, const VerifyArgs& a) {
+    const bool aligned = (a.rs_qk % 4 == 0) && (a.rs_v % 4 == 0) &&
+                         (reinterpret_cast<uintptr_t>(a.q) % 8 == 0) &&
+                         (reinterpret_cast<uintptr_t>(a.k) % 8 == 0) &&
+                         (reinterpret_cast<uintptr_t>(a.v) % 8 == 0);
+    return a.dtype == GDN_DT_BF16 && a.D == kD && !(a.flags & GDN_F_VALU) && aligned && d.N >= 1;
+}
+
+hipError_t launch_verify(const gdn_tree_desc& d, const VerifyArgs& a, hipStream_t s) {
+    const int norm = (a.flags & GDN_F_NORM_QK) ? 1 : 0;
+    const int obf = (a.flags & GDN_F_OUT_BF16) ? 1 : 0;
+    if (verify_uses_mfma(d, a)) {
+        const int NPB = (d.N + 31) / 32;
+        const size_t lds = static_cast<size_t>(mfma_lds_layout(d.N, NPB).total);
+        if (lds > kMaxLds) return hipErrorNotSupported;
+        switch (NPB) {
+            case 1: return launch_mfma_t<1>(d, a, norm, obf, lds, s);
+            case 2: return launch_mfma_t<2>(d, a, norm, obf, lds, s);
+            default: return hipErrorNotSupported;
+        }
+    }
+    const size_t lds = verify_valu_lds_bytes(d.N, a.D);
+    if (lds > kMaxLds) return hipErrorNotSupported;
+    const bool bf = a.dtype == GDN_DT_BF16;
+    switch (a.D) {
+        case 32:
+            return bf ? launch_valu_t<32, uint16_t>(d, a, norm, obf, lds, s)
+                      : launch_valu_t<32, float>(d, a, norm, obf, lds, s);
+        case 64:
+            return bf ? launch_valu_t<64, uint16_t>(d, a, norm, obf, lds, s)
+                      : launch_valu_t<64, float>(d, a, norm, obf, lds, s);
+        case 128:
+            return bf ? launch_valu_t<128, uint16_t>(d, a, norm, obf, lds, s)
+                      : launch_valu_t<128, float>(d, a, norm, obf, lds, s);
+        default:
+            return hipErrorNotSupported;
+    }
+}
+
+}  // namespace gdn
