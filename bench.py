@@ -28,6 +28,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "tree nodes verified/sec (GDN layer, 1 GPU) + achieved HBM GB/s vs peak"
 PEAK_HBM_GBS = 8000.0
+# file stem of the committed profile summaries for each workload
+WORKLOAD_TAG = {"tree27_b128_h32_conv4": "tree27_b128_conv4"}
 
 
 def log(*a):
@@ -56,6 +58,43 @@ def algorithmic_bytes(cfg, case):
     out["commit"] = (active * Hv * D * D * 4 * 2 + int(L.sum()) * (Hqk * D + Hv * D) * 2
                      + int(L.sum()) * Hv * 8 + hist_bytes)
     return out
+
+
+KERNEL_PREFIX = {"conv": "gdn::conv_gather_kernel", "verify": "gdn::verify_",
+                 "commit": "gdn::commit_kernel", "desc": "gdn::desc_build_kernel"}
+
+
+def library_source_hash():
+    """sha256[:16] over the library's kernel sources and the ABI header, in
+    the order the profile summaries under profiles/ record it."""
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "tree_speculative_verification_gdn_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(fh.read())
+    with open(os.path.join(ROOT, "include", "gdn_tree.h"), "rb") as fh:
+        h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, stage):
+    """HBM bytes per launch of ``stage``'s kernel from the committed counter
+    summary (FETCH_SIZE and WRITE_SIZE passes, scaled by a known-size copy),
+    or None when there is none or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha256_16") != library_source_hash():
+        return None
+    for name, k in rec["kernels"].items():
+        if name.startswith(KERNEL_PREFIX[stage]):
+            return int(round(k["traffic_bytes"]))
+    return None
 
 
 def cpu_baseline(cfg, seed, budget_s):
@@ -96,6 +135,9 @@ def main():
     ap.add_argument("--sets", type=int, default=2, help="independent layer input sets rotated per step")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run a plain fp32 copy kernel (out = in * 1) over MIB MiB, three "
+                         "times, as the known-size reference for HBM byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -113,6 +155,16 @@ def main():
     g.load_library()
     cfg = gi.CONFIGS[args.config]
     dev = "cuda"
+
+    if args.copy_calibration > 0:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.randn(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: 3 x {args.copy_calibration} MiB read + written")
+        del src, dst
 
     def to_dev(a):
         a = np.ascontiguousarray(a)
@@ -207,7 +259,8 @@ def main():
     dom = max(("conv", "verify", "commit"), key=lambda n: avg[n])
     achieved = bytes_avg[dom] / (avg[dom] / 1e3) / 1e9
     roofline = dict(bound="hbm", kernel=dom, achieved=round(achieved, 1), peak=PEAK_HBM_GBS,
-                    unit="GB/s", frac=round(achieved / PEAK_HBM_GBS, 4), traffic=None,
+                    unit="GB/s", frac=round(achieved / PEAK_HBM_GBS, 4),
+                    traffic=measured_traffic(WORKLOAD_TAG.get(cfg.name, cfg.name), dom),
                     avg_us=round(avg[dom] * 1e3, 2), algorithmic_bytes=int(bytes_avg[dom]))
 
     cpu = None
