@@ -5,26 +5,72 @@
 // end (the page's point that tap order and cast boundaries fix the recorded
 // values).
 //
-// Layout / schedule: block = (512-channel tile, request).  Each of the 128
-// lanes owns 4 consecutive channels (one 8-byte load per row).  The request's
-// node rows for those channels are staged once in LDS, so every x element is
-// read from HBM once however many descendants tap it; the W-1 history
-// entries stay in registers.  HBM-bound: x (node rows), hist, y.
+// Layout / schedule: workgroup = (channel tile, request), 256 threads.  A row
+// of the tile is covered by TL lanes of CPT channels each (one 8- or 16-byte
+// access per lane), so the workgroup holds 256/TL rows at a time and walks
+// the request's nodes with that stride.  Two memory round trips: (1) the
+// tree's rows and tap sources, the request's slot; (2) every node row of the
+// tile, the W-1 history entries and the weights, all in flight together.
+// Node rows are kept in LDS, so an x element is read from HBM once however
+// many descendants tap it.  HBM-bound: x (node rows), hist, y.
 #include "gdn_internal.h"
 
 namespace gdn {
 
-constexpr int kConvThreads = 128;
-constexpr int kConvCh = 4;
+namespace {
+constexpr int kConvThreads = 256;
+constexpr int kTileLanes = 32;                          // lanes per row
+constexpr int kRowsPerPass = kConvThreads / kTileLanes;  // rows in flight per pass
+constexpr int kMaxPasses = (kMaxNodes + kRowsPerPass - 1) / kRowsPerPass;
 
-__device__ __forceinline__ float silu(float z) {
-    // z * sigmoid(z), with the exponential taken of a non-positive argument
-    const float e = expf(-fabsf(z));
-    const float sig = (z >= 0.f) ? 1.f / (1.f + e) : e / (1.f + e);
-    return z * sig;
+template <int CPT>
+struct Chunk;
+template <>
+struct Chunk<8> {
+    uint4 u;
+};
+template <>
+struct Chunk<4> {
+    uint2 u;
+};
+
+template <int CPT>
+__device__ __forceinline__ Chunk<CPT> load_chunk(const uint16_t* p) {
+    Chunk<CPT> c;
+    c.u = *reinterpret_cast<const decltype(c.u)*>(p);
+    return c;
 }
 
-template <int W>
+template <int CPT>
+__device__ __forceinline__ void unpack(const Chunk<CPT>& c, float* f) {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(&c.u);
+#pragma unroll
+    for (int e = 0; e < CPT / 2; ++e) {
+        f[2 * e] = __uint_as_float(w[e] << 16);
+        f[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+}
+}  // namespace
+
+__device__ __forceinline__ float silu(float z) {
+    // z * sigmoid(z) on the hardware exp2 and reciprocal (about 1 ulp each,
+    // far below the bf16 rounding that follows); the exponential is taken of
+    // a non-positive argument, so it never overflows
+    const float e = __builtin_amdgcn_exp2f(-fabsf(z) * 1.4426950408889634f);
+    const float r = __builtin_amdgcn_rcpf(1.f + e);
+    return z * ((z >= 0.f) ? r : e * r);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const bf16x2_t h = __builtin_convertvector((f32x2_t){a, b}, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+template <int W, int CPT>
 __global__ void __launch_bounds__(kConvThreads)
     conv_gather_kernel(int N, int R, int C, int shared, const int32_t* __restrict__ node_row,
                        const int32_t* __restrict__ conv_src, const int32_t* __restrict__ status,
@@ -33,89 +79,126 @@ __global__ void __launch_bounds__(kConvThreads)
                        const float* __restrict__ bias, int act, uint16_t* __restrict__ y,
                        int32_t* __restrict__ err) {
     constexpr int H = W - 1;
-    extern __shared__ uint2 s_x[];  // [N][kConvThreads] node inputs (4 bf16 each)
+    constexpr int TILE = kTileLanes * CPT;  // channels per workgroup
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    Chunk<CPT>* s_x = reinterpret_cast<Chunk<CPT>*>(lds);  // [N][kTileLanes]
+    int32_t* s_node_of_row = reinterpret_cast<int32_t*>(lds + static_cast<size_t>(N) * kTileLanes *
+                                                                  sizeof(Chunk<CPT>));  // [R]
     __shared__ int32_t s_row[kMaxNodes];
     // tap sources as node indices (>= 0) or history codes -(s+1)
     __shared__ int32_t s_tap[kMaxNodes * (H > 0 ? H : 1)];
 
     const int b = blockIdx.y;
     const int t = shared ? 0 : b;
-    if (status[t] != 0) return;
+    const int tid = threadIdx.x;
+
+    // ---- round trip 1: tree rows, tap sources, the request's slot
+    const int st = status[t];
     const int slot = state_idx[b];
+    if (st != 0) return;
     if (slot < 0 || slot >= P) {
-        if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(err, GDN_EV_STATE);
+        if (blockIdx.x == 0 && tid == 0) atomicOr(err, GDN_EV_STATE);
         return;
     }
-    const int tid = threadIdx.x;
-    int32_t* s_node_of_row = reinterpret_cast<int32_t*>(s_x + static_cast<size_t>(N) * kConvThreads);
-    for (int i = tid; i < N; i += kConvThreads) {
-        const int row = node_row[static_cast<size_t>(t) * N + i];
-        s_row[i] = row;
-        s_node_of_row[row] = i;  // rows of a valid tree are injective and < R
+    const int32_t* rows_t = node_row + static_cast<size_t>(t) * N;
+    const int32_t* src_t = conv_src + static_cast<size_t>(t) * N * (H > 0 ? H : 1);
+    // loads are unconditional, from indexes clamped into range (a load under a
+    // per-lane condition becomes a branch that waits for it)
+    const int my_row = rows_t[min(tid, N - 1)];
+    const int my_src = (H > 0) ? src_t[min(tid, N * H - 1)] : 0;  // N * H <= 192 < 256
+    for (int r = tid; r < R; r += kConvThreads) s_node_of_row[r] = -1;
+    __syncthreads();
+    if (tid < N) {
+        s_row[tid] = my_row;
+        s_node_of_row[my_row] = tid;  // rows of a valid tree are injective and < R
     }
     __syncthreads();
-    // tap sources as node indices (conv_src only names rows of this tree)
-    for (int e = tid; e < N * H; e += kConvThreads) {
-        const int sv = conv_src[static_cast<size_t>(t) * N * H + e];
-        s_tap[e] = sv >= 0 ? s_node_of_row[sv] : sv;
+    // tap sources as node indices; a source the descriptor build cannot have
+    // produced (outside this tree's rows or history) is reported, not followed
+    if (tid < N * H) {
+        const int sv = my_src;
+        int tap = sv;
+        if (sv >= 0) tap = (sv < R) ? s_node_of_row[sv] : -1;
+        const bool bad = (sv >= 0) ? (tap < 0) : (sv < -H);
+        if (bad) {
+            atomicOr(err, GDN_EV_ROW);
+            tap = 0;
+        }
+        s_tap[tid] = tap;
     }
-    const int c0 = min((blockIdx.x * kConvThreads + tid) * kConvCh, C - kConvCh);
-    const bool active = (blockIdx.x * kConvThreads + tid) * kConvCh < C;
 
-    // weights w[c][0..W-1] for the 4 channels
-    float wt[W][kConvCh];
-#pragma unroll
-    for (int j = 0; j < kConvCh; ++j)
-#pragma unroll
-        for (int tap = 0; tap < W; ++tap)
-            wt[tap][j] = bf16_bits_to_f32(w[static_cast<size_t>(c0 + j) * W + tap]);
-    float bs[kConvCh] = {0.f, 0.f, 0.f, 0.f};
-    if (bias) {
-#pragma unroll
-        for (int j = 0; j < kConvCh; ++j) bs[j] = bias[c0 + j];
-    }
-    // history entries of this request's slot
-    float hs[H > 0 ? H : 1][kConvCh];
-#pragma unroll
-    for (int m = 0; m < H; ++m) {
-        const uint2 hv = *reinterpret_cast<const uint2*>(
-            hist + (static_cast<size_t>(slot) * H + m) * C + c0);
-        hs[m][0] = __uint_as_float(hv.x << 16);
-        hs[m][1] = __uint_as_float(hv.x & 0xffff0000u);
-        hs[m][2] = __uint_as_float(hv.y << 16);
-        hs[m][3] = __uint_as_float(hv.y & 0xffff0000u);
-    }
-    // stage node inputs (each lane only ever reads its own column), eight
-    // loads in flight at a time
+    // ---- round trip 2: node rows of the tile, history, weights
+    const int lane = tid % kTileLanes;
+    const int rs = tid / kTileLanes;  // first node of this thread
+    const int c0u = blockIdx.x * TILE + lane * CPT;
+    const bool active = c0u < C;  // C is a multiple of CPT
+    const int c0 = active ? c0u : C - CPT;  // lanes past the end load a valid chunk, store nothing
     const size_t xb = static_cast<size_t>(b) * R;
-    for (int i0 = 0; i0 < N; i0 += 8) {
-        uint2 tmp[8];
+    constexpr int kPasses = kMaxPasses;
+    Chunk<CPT> xin[kPasses];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-            if (i0 + u < N)
-                tmp[u] = *reinterpret_cast<const uint2*>(x + (xb + s_row[i0 + u]) * C + c0);
+    for (int p = 0; p < kPasses; ++p) {
+        const int i = rs + p * kRowsPerPass;
+        if (p * kRowsPerPass < N)  // uniform: whole passes beyond N are skipped
+            xin[p] = load_chunk<CPT>(x + (xb + s_row[min(i, N - 1)]) * C + c0);
+    }
+    float hs[H > 0 ? H : 1][CPT];
+    float wt[W][CPT];
+    float bs[CPT];
+    {
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-            if (i0 + u < N) s_x[(i0 + u) * kConvThreads + tid] = tmp[u];
+        for (int m = 0; m < H; ++m) {
+            const Chunk<CPT> hc = load_chunk<CPT>(hist + (static_cast<size_t>(slot) * H + m) * C + c0);
+            unpack<CPT>(hc, hs[m]);
+        }
+        // weights w[c][0..W-1] of the CPT channels: CPT*W contiguous bf16
+        uint16_t wr[CPT * W];
+        const uint16_t* wp = w + static_cast<size_t>(c0) * W;
+        if (CPT == 8) {  // 16-byte aligned: w is, and c0 * W * 2 is a multiple of 16
+#pragma unroll
+            for (int e = 0; e < CPT * W; e += 8)
+                *reinterpret_cast<uint4*>(wr + e) = *reinterpret_cast<const uint4*>(wp + e);
+        } else {
+#pragma unroll
+            for (int e = 0; e < CPT * W; ++e) wr[e] = wp[e];
+        }
+#pragma unroll
+        for (int j = 0; j < CPT; ++j)
+#pragma unroll
+            for (int tap = 0; tap < W; ++tap) wt[tap][j] = bf16_bits_to_f32(wr[j * W + tap]);
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) bs[j] = bias ? bias[c0 + j] : 0.f;  // bias: uniform
+    }
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+        const int i = rs + p * kRowsPerPass;
+        if (i < N) s_x[i * kTileLanes + lane] = xin[p];
+    }
+    // take delivery of the weights and history here, in the same round trip
+    // as the node rows (left alone, the compiler sinks these loads to their
+    // first use after the barrier, a round trip of their own)
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+#pragma unroll
+        for (int tap = 0; tap < W; ++tap) asm volatile("" ::"v"(wt[tap][j]));
+#pragma unroll
+        for (int m = 0; m < H; ++m) asm volatile("" ::"v"(hs[m][j]));
     }
     __syncthreads();
+    if (!active) return;
 
-    for (int i = 0; i < N; ++i) {
-        float z[kConvCh];
+    for (int i = rs; i < N; i += kRowsPerPass) {
+        float z[CPT];
 #pragma unroll
         for (int tap = 0; tap < H; ++tap) {
             const int sv = s_tap[i * H + tap];
-            float xv[kConvCh];
+            float xv[CPT];
             if (sv >= 0) {
-                const uint2 u = s_x[sv * kConvThreads + tid];
-                xv[0] = __uint_as_float(u.x << 16);
-                xv[1] = __uint_as_float(u.x & 0xffff0000u);
-                xv[2] = __uint_as_float(u.y << 16);
-                xv[3] = __uint_as_float(u.y & 0xffff0000u);
+                unpack<CPT>(s_x[sv * kTileLanes + lane], xv);
             } else {
                 const int m = -sv - 1;
 #pragma unroll
-                for (int j = 0; j < kConvCh; ++j) {
+                for (int j = 0; j < CPT; ++j) {
                     float hvv = hs[0][j];
 #pragma unroll
                     for (int mm = 1; mm < H; ++mm) hvv = (m == mm) ? hs[mm][j] : hvv;
@@ -123,42 +206,54 @@ __global__ void __launch_bounds__(kConvThreads)
                 }
             }
 #pragma unroll
-            for (int j = 0; j < kConvCh; ++j)
+            for (int j = 0; j < CPT; ++j)
                 z[j] = (tap == 0) ? wt[0][j] * xv[j] : fmaf(wt[tap][j], xv[j], z[j]);
         }
-        const uint2 u = s_x[i * kConvThreads + tid];
-        float xi[kConvCh] = {__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                             __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+        float xi[CPT];
+        unpack<CPT>(s_x[i * kTileLanes + lane], xi);
+        Chunk<CPT> o;
+        uint32_t* ow = reinterpret_cast<uint32_t*>(&o.u);
 #pragma unroll
-        for (int j = 0; j < kConvCh; ++j) {
+        for (int j = 0; j < CPT; ++j) {
             float zz = (H == 0) ? wt[H][j] * xi[j] : fmaf(wt[H][j], xi[j], z[j]);
             if (bias) zz += bs[j];
             if (act == GDN_ACT_SILU) zz = silu(zz);
             z[j] = zz;
         }
-        uint2 o;
-        o.x = static_cast<uint32_t>(f32_to_bf16_bits(z[0])) |
-              (static_cast<uint32_t>(f32_to_bf16_bits(z[1])) << 16);
-        o.y = static_cast<uint32_t>(f32_to_bf16_bits(z[2])) |
-              (static_cast<uint32_t>(f32_to_bf16_bits(z[3])) << 16);
-        if (active) *reinterpret_cast<uint2*>(y + (xb + s_row[i]) * C + c0) = o;
+#pragma unroll
+        for (int e = 0; e < CPT / 2; ++e) ow[e] = pack_bf16x2(z[2 * e], z[2 * e + 1]);
+        *reinterpret_cast<decltype(o.u)*>(y + (xb + s_row[i]) * C + c0) = o.u;
     }
+}
+
+size_t conv_lds_bytes(int N, int R, int cpt) {
+    return static_cast<size_t>(N) * kTileLanes * (cpt * 2) + static_cast<size_t>(R) * sizeof(int32_t);
 }
 
 hipError_t launch_conv(const gdn_tree_desc& d, const uint16_t* x, const uint16_t* hist, int P,
                        const int32_t* state_idx, const uint16_t* w, const float* bias,
                        uint16_t* y, int C, int act, int32_t* err, hipStream_t s) {
-    const int tile = kConvThreads * kConvCh;
+    // 16-byte accesses when every 8-channel group is 16-byte aligned
+    const bool wide = (C % 8 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
+                      (reinterpret_cast<uintptr_t>(y) % 16 == 0) &&
+                      (hist == nullptr || reinterpret_cast<uintptr_t>(hist) % 16 == 0) &&
+                      (reinterpret_cast<uintptr_t>(w) % 16 == 0);
+    const int cpt = wide ? 8 : 4;
+    const int tile = kTileLanes * cpt;
     dim3 grid((C + tile - 1) / tile, d.B);
-    const size_t lds = static_cast<size_t>(d.N) * kConvThreads * sizeof(uint2) +
-                       static_cast<size_t>(d.R) * sizeof(int32_t);
-#define GDN_CONV_CASE(WW)                                                                     \
-    case WW:                                                                                  \
-        hipLaunchKernelGGL(conv_gather_kernel<WW>, grid, dim3(kConvThreads), lds, s, d.N,     \
-                           d.R, C, d.shared, d.node_row, d.conv_src, d.status, x, hist, P,    \
-                           state_idx, w, bias, act, y, err);                                  \
+    const size_t lds = conv_lds_bytes(d.N, d.R, cpt);
+    if (lds > 60 * 1024) return hipErrorNotSupported;  // plus static LDS, within the 64 KiB default
+#define GDN_CONV_CASE(WW)                                                                      \
+    case WW:                                                                                   \
+        if (wide)                                                                              \
+            hipLaunchKernelGGL((conv_gather_kernel<WW, 8>), grid, dim3(kConvThreads), lds, s,  \
+                               d.N, d.R, C, d.shared, d.node_row, d.conv_src, d.status, x,     \
+                               hist, P, state_idx, w, bias, act, y, err);                      \
+        else                                                                                   \
+            hipLaunchKernelGGL((conv_gather_kernel<WW, 4>), grid, dim3(kConvThreads), lds, s,  \
+                               d.N, d.R, C, d.shared, d.node_row, d.conv_src, d.status, x,     \
+                               hist, P, state_idx, w, bias, act, y, err);                      \
         break;
-    if (lds > 160 * 1024) return hipErrorNotSupported;
     switch (d.W) {
         GDN_CONV_CASE(1)
         GDN_CONV_CASE(2)

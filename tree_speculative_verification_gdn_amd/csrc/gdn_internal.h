@@ -96,6 +96,6 @@ struct CommitArgs {
     int32_t* err;
 };
 hipError_t launch_commit(const gdn_tree_desc& d, const CommitArgs& a, hipStream_t s);
-size_t commit_lds_bytes(int Lmax, int D);
+size_t commit_lds_bytes(int Lmax, int D, int dtype);
 
 }  // namespace gdn

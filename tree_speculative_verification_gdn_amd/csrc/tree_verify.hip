@@ -75,11 +75,12 @@ __host__ __device__ inline MfmaLds mfma_lds_layout(int N, int NPB) {
     L.nrm = off;  off += align_up(2 * NP * 4, 16); // squared norms by slot
     L.sk = off;   off += align_up(N * 4, 16);
     L.sq = off;   off += align_up(N * 4, 16);
-    L.al = off;   off += align_up(N * 4, 16);
-    L.be = off;   off += align_up(N * 4, 16);
-    L.rows = off; off += align_up(N * 4, 16);
-    L.dep = off;  off += align_up(N * 4, 16);
-    L.anc = off;  off += align_up(N * 8, 16);
+    // per-node arrays written by every lane carry one spare entry (index N)
+    L.al = off;   off += align_up((N + 1) * 4, 16);
+    L.be = off;   off += align_up((N + 1) * 4, 16);
+    L.rows = off; off += align_up((N + 1) * 4, 16);
+    L.dep = off;  off += align_up((N + 1) * 4, 16);
+    L.anc = off;  off += align_up((N + 1) * 8, 16);
     L.cidx = off; off += align_up(N * N, 16);      // [i][p]: node at depth p+1 on i's root path
     L.mf = off;   off += align_up(N * N * 4, 16);  // [i][p]: M[i][path node p] (fp32 scratch)
     L.mh = off;   off += align_up(NP * L.mstride, 16);
@@ -205,12 +206,6 @@ __global__ void __launch_bounds__(kThreads)
     const int b = static_cast<int>(unit / Hv);
     const int h = static_cast<int>(unit % Hv);
     const int t = shared ? 0 : b;
-    if (status[t] != 0) return;
-    const int slot = state_idx[b];
-    if (slot < 0 || slot >= P) {
-        if (h == 0 && threadIdx.x == 0) atomicOr(err, GDN_EV_STATE);
-        return;
-    }
     const int g = static_cast<int>((static_cast<int64_t>(h) * Hqk) / Hv);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -221,17 +216,61 @@ __global__ void __launch_bounds__(kThreads)
     const size_t tb = static_cast<size_t>(t) * N;
     const size_t rowb = static_cast<size_t>(b) * R;
 
-    // (a) metadata first (small, dependent loads), then the committed state
-    //     and every K/Q/V chunk, all in flight before any wait
-    if (tid < N) {
-        const int row = node_row[tb + tid];
-        s_rows[tid] = row;
-        s_anc[tid] = anc_g[tb + tid];
-        s_dep[tid] = depth_g[tb + tid];
-        const size_t gi = (rowb + row) * Hv + h;
-        s_al[tid] = alpha[gi];
-        s_be[tid] = beta[gi];
+    // (a) Memory, in three waves of loads.  A wave's vector loads retire in
+    //     issue order, so the K/Q/V rows go out before the 64 KiB state: the
+    //     Gram block and the M solve below run on them while the state is
+    //     still arriving, and only the state contraction waits for it.
+    //   (a1) the tree's rows (per staging item), ancestors, depths; status, slot.
+    //   Every load below is unconditional, from an index clamped into range, and
+    //   the unused results are dropped afterwards: a load under a per-lane
+    //   condition becomes a branch that waits for it before the next one issues.
+    const int st = status[t];
+    const int slot = state_idx[b];
+    int kq_row[kKQItems], v_row[kVItems];
+#pragma unroll
+    for (int u = 0; u < kKQItems; ++u) {
+        const int sl = (tid + u * kThreads) >> 5;
+        const int node = sl < NP ? sl : sl - NP;
+        kq_row[u] = node_row[tb + min(node, N - 1)];
     }
+#pragma unroll
+    for (int u = 0; u < kVItems; ++u) {
+        const int node = (tid + u * kThreads) >> 5;
+        v_row[u] = node_row[tb + min(node, N - 1)];
+    }
+    const int my_node = min(tid, N - 1);
+    const int my_row = node_row[tb + my_node];
+    const uint64_t my_anc = anc_g[tb + my_node];
+    const int my_dep = depth_g[tb + my_node];
+    if (st != 0) return;
+    if (slot < 0 || slot >= P) {
+        if (h == 0 && tid == 0) atomicOr(err, GDN_EV_STATE);
+        return;
+    }
+    //   (a2) K/Q/V chunks and the gates of every node (rows of a valid tree are
+    //        in range, so the clamped loads are too)
+    uint2 kq_val[kKQItems];
+#pragma unroll
+    for (int u = 0; u < kKQItems; ++u) {
+        const int it = tid + u * kThreads;
+        const int sl = it >> 5;
+        const int ch = it & 31;
+        const uint16_t* src = (sl < NP ? k : q) + (rowb + kq_row[u]) * rs_qk +
+                              static_cast<size_t>(g) * kD + ch * 4;
+        kq_val[u] = *reinterpret_cast<const uint2*>(src);
+    }
+    uint2 v_val[kVItems];
+#pragma unroll
+    for (int u = 0; u < kVItems; ++u) {
+        const int it = tid + u * kThreads;
+        v_val[u] = *reinterpret_cast<const uint2*>(v + (rowb + v_row[u]) * rs_v +
+                                                   static_cast<size_t>(h) * kD + (it & 31) * 4);
+    }
+    const size_t my_gi = (rowb + my_row) * Hv + h;
+    const float my_al = alpha[my_gi];
+    const float my_be = beta[my_gi];
+    asm volatile("" ::: "memory");  // keep the state loads behind the K/Q/V loads
+    //   (a3) the committed state: lane (r_own, hf) holds 64 elements of row r_own
     const float* Sb = pool + (static_cast<size_t>(slot) * Hv + h) * (kD * kD) +
                       static_cast<size_t>(r_own) * kD + 4 * hf;
     float4 sreg[16];
@@ -240,32 +279,18 @@ __global__ void __launch_bounds__(kThreads)
         sreg[2 * s] = *reinterpret_cast<const float4*>(Sb + 16 * s);
         sreg[2 * s + 1] = *reinterpret_cast<const float4*>(Sb + 16 * s + 8);
     }
-    uint2 kq_val[kKQItems];
-#pragma unroll
-    for (int u = 0; u < kKQItems; ++u) {
-        const int it = tid + u * kThreads;
-        const int sl = it >> 5;
-        const int ch = it & 31;
-        const int node = sl < NP ? sl : sl - NP;
-        kq_val[u] = make_uint2(0u, 0u);
-        if (node < N) {
-            const int row = node_row[tb + node];
-            const uint16_t* src = (sl < NP ? k : q) + (rowb + row) * rs_qk +
-                                  static_cast<size_t>(g) * kD + ch * 4;
-            kq_val[u] = *reinterpret_cast<const uint2*>(src);
-        }
-    }
-    uint2 v_val[kVItems];
-#pragma unroll
-    for (int u = 0; u < kVItems; ++u) {
-        const int it = tid + u * kThreads;
-        const int node = it >> 5;
-        v_val[u] = make_uint2(0u, 0u);
-        if (node < N) {
-            const int row = node_row[tb + node];
-            v_val[u] = *reinterpret_cast<const uint2*>(v + (rowb + row) * rs_v +
-                                                       static_cast<size_t>(h) * kD + (it & 31) * 4);
-        }
+
+    // stage the metadata, K/Q (with squared norms) and V in LDS.  Every lane
+    // writes (lanes past N into the spare entry): a store under a per-lane
+    // condition would let the compiler sink the loads above into its branch,
+    // behind the state loads, where using them waits for the whole state.
+    {
+        const int slot_i = tid < N ? tid : N;
+        s_rows[slot_i] = my_row;
+        s_anc[slot_i] = my_anc;
+        s_dep[slot_i] = my_dep;
+        s_al[slot_i] = my_al;
+        s_be[slot_i] = my_be;
     }
     // M halves start as zero (entries off the ancestor pattern stay zero)
     for (int e = tid; e < NP * mstride / 4; e += kThreads) {
@@ -277,6 +302,8 @@ __global__ void __launch_bounds__(kThreads)
         const int it = tid + u * kThreads;
         const int sl = it >> 5;
         const int ch = it & 31;
+        const int node = sl < NP ? sl : sl - NP;
+        if (node >= N) kq_val[u] = make_uint2(0u, 0u);  // zero pad rows of the MFMA blocks
         *reinterpret_cast<uint2*>(s_a + sl * kKQStride + ch * 8) = kq_val[u];
         float ss = sumsq_bf16x4(kq_val[u]);  // a row's 32 chunks sit in 32 consecutive lanes
 #pragma unroll
@@ -336,22 +363,6 @@ __global__ void __launch_bounds__(kThreads)
             }
         }
     }
-
-    // (d) CT = [K;Q] S_pre^T on the matrix cores, state split into bf16 hi + lo
-    f32x16_t acc[MB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x16_t{};
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        bf16x8_t shi, slo;
-        split_hi_lo(sreg[2 * s], sreg[2 * s + 1], shi, slo);
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            const bf16x8_t a = lds_operand(s_a, mb * 32 + l32, s, hf);
-            acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, shi, acc[mb], 0, 0, 0);
-            acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, slo, acc[mb], 0, 0, 0);
-        }
-    }
     __syncthreads();
 
     // (e) row i of M = C (I + G)^-1 by back-substitution along i's root path
@@ -386,6 +397,23 @@ __global__ void __launch_bounds__(kThreads)
         s_cq[i] = wq * sq_i;
     }
     __syncthreads();
+
+    // (d) CT = [K;Q] S_pre^T on the matrix cores, state split into bf16 hi + lo
+    //     (the first use of the state: the only wait for it)
+    f32x16_t acc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x16_t{};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        bf16x8_t shi, slo;
+        split_hi_lo(sreg[2 * s], sreg[2 * s + 1], shi, slo);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const bf16x8_t a = lds_operand(s_a, mb * 32 + l32, s, hf);
+            acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, shi, acc[mb], 0, 0, 0);
+            acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, slo, acc[mb], 0, 0, 0);
+        }
+    }
 
     // (f) R = beta (v - P k^ S_pre) from the key blocks, as bf16 hi/lo MFMA
     //     operands (a key block's output layout is a permutation of the
