@@ -70,7 +70,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, h);
 }
 
-template <int W, int CPT>
+// bytes of the staged rows (N node rows + W-1 history rows), 16-aligned
+__host__ __device__ inline size_t conv_lds_x_bytes(int N, int W, int cpt) {
+    return (static_cast<size_t>(N + W - 1) * kTileLanes * (cpt * 2) + 15) / 16 * 16;
+}
+
+template <int W, int CPT, int PASSES>
 __global__ void __launch_bounds__(kConvThreads)
     conv_gather_kernel(int N, int R, int C, int shared, const int32_t* __restrict__ node_row,
                        const int32_t* __restrict__ conv_src, const int32_t* __restrict__ status,
@@ -80,19 +85,29 @@ __global__ void __launch_bounds__(kConvThreads)
                        int32_t* __restrict__ err) {
     constexpr int H = W - 1;
     constexpr int TILE = kTileLanes * CPT;  // channels per workgroup
+    constexpr int kWW = CPT * W / 2;        // 32-bit words of one lane's weights
+    // LDS: x rows of the nodes, then the H history entries, as rows of
+    // kTileLanes chunks; the tile's weights and bias; the row -> node map
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    Chunk<CPT>* s_x = reinterpret_cast<Chunk<CPT>*>(lds);  // [N][kTileLanes]
-    int32_t* s_node_of_row = reinterpret_cast<int32_t*>(lds + static_cast<size_t>(N) * kTileLanes *
-                                                                  sizeof(Chunk<CPT>));  // [R]
+    Chunk<CPT>* s_x = reinterpret_cast<Chunk<CPT>*>(lds);  // [N + H][kTileLanes]
+    uint32_t* s_w = reinterpret_cast<uint32_t*>(lds + conv_lds_x_bytes(N, W, CPT));  // [kTileLanes][kWW]
+    float* s_b = reinterpret_cast<float*>(reinterpret_cast<char*>(s_w) + kTileLanes * kWW * 4);  // [kTileLanes][CPT]
+    int32_t* s_node_of_row = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(s_b) + TILE * 4);  // [R]
     __shared__ int32_t s_row[kMaxNodes];
-    // tap sources as node indices (>= 0) or history codes -(s+1)
+    // LDS row of each tap: a node's row (< N) or history entry m (N + m)
     __shared__ int32_t s_tap[kMaxNodes * (H > 0 ? H : 1)];
 
     const int b = blockIdx.y;
     const int t = shared ? 0 : b;
     const int tid = threadIdx.x;
 
-    // ---- round trip 1: tree rows, tap sources, the request's slot
+    // ---- round trip 1: tree rows, tap sources, the request's slot.  Loads
+    // are unconditional, from indexes clamped into range (a load under a
+    // per-lane condition becomes a branch that waits for it).
+    const int32_t* rows_t = node_row + static_cast<size_t>(t) * N;
+    const int32_t* src_t = conv_src + static_cast<size_t>(t) * N * (H > 0 ? H : 1);
+    const int my_row = rows_t[min(tid, N - 1)];
+    const int my_src = (H > 0) ? src_t[min(tid, N * H - 1)] : 0;  // N * H <= 192 < 256
     const int st = status[t];
     const int slot = state_idx[b];
     if (st != 0) return;
@@ -100,12 +115,6 @@ __global__ void __launch_bounds__(kConvThreads)
         if (blockIdx.x == 0 && tid == 0) atomicOr(err, GDN_EV_STATE);
         return;
     }
-    const int32_t* rows_t = node_row + static_cast<size_t>(t) * N;
-    const int32_t* src_t = conv_src + static_cast<size_t>(t) * N * (H > 0 ? H : 1);
-    // loads are unconditional, from indexes clamped into range (a load under a
-    // per-lane condition becomes a branch that waits for it)
-    const int my_row = rows_t[min(tid, N - 1)];
-    const int my_src = (H > 0) ? src_t[min(tid, N * H - 1)] : 0;  // N * H <= 192 < 256
     for (int r = tid; r < R; r += kConvThreads) s_node_of_row[r] = -1;
     __syncthreads();
     if (tid < N) {
@@ -113,12 +122,11 @@ __global__ void __launch_bounds__(kConvThreads)
         s_node_of_row[my_row] = tid;  // rows of a valid tree are injective and < R
     }
     __syncthreads();
-    // tap sources as node indices; a source the descriptor build cannot have
+    // tap sources as LDS rows; a source the descriptor build cannot have
     // produced (outside this tree's rows or history) is reported, not followed
     if (tid < N * H) {
         const int sv = my_src;
-        int tap = sv;
-        if (sv >= 0) tap = (sv < R) ? s_node_of_row[sv] : -1;
+        int tap = (sv >= 0) ? ((sv < R) ? s_node_of_row[sv] : -1) : N + (-sv - 1);
         const bool bad = (sv >= 0) ? (tap < 0) : (sv < -H);
         if (bad) {
             atomicOr(err, GDN_EV_ROW);
@@ -127,14 +135,14 @@ __global__ void __launch_bounds__(kConvThreads)
         s_tap[tid] = tap;
     }
 
-    // ---- round trip 2: node rows of the tile, history, weights
+    // ---- round trip 2: node rows of the tile, history, weights, bias
     const int lane = tid % kTileLanes;
     const int rs = tid / kTileLanes;  // first node of this thread
     const int c0u = blockIdx.x * TILE + lane * CPT;
     const bool active = c0u < C;  // C is a multiple of CPT
     const int c0 = active ? c0u : C - CPT;  // lanes past the end load a valid chunk, store nothing
     const size_t xb = static_cast<size_t>(b) * R;
-    constexpr int kPasses = kMaxPasses;
+    constexpr int kPasses = PASSES;  // kPasses * kRowsPerPass >= N
     Chunk<CPT> xin[kPasses];
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
@@ -142,72 +150,67 @@ __global__ void __launch_bounds__(kConvThreads)
         if (p * kRowsPerPass < N)  // uniform: whole passes beyond N are skipped
             xin[p] = load_chunk<CPT>(x + (xb + s_row[min(i, N - 1)]) * C + c0);
     }
-    float hs[H > 0 ? H : 1][CPT];
-    float wt[W][CPT];
-    float bs[CPT];
+    // history entry m = rs (threads with rs >= H load entry H - 1 again)
+    Chunk<CPT> hc;
+    if (H > 0) hc = load_chunk<CPT>(hist + (static_cast<size_t>(slot) * H + min(rs, H - 1)) * C + c0);
+    // weights w[c][0..W-1] of the lane's CPT channels, CPT*W contiguous bf16:
+    // 16-byte group min(rs, ...) per thread (scalar words when not 16-byte aligned)
+    constexpr int kWG = (kWW + 3) / 4;  // 16-byte groups
+    uint4 wg4 = make_uint4(0u, 0u, 0u, 0u);
+    const uint16_t* wp = w + static_cast<size_t>(c0) * W;
     {
-#pragma unroll
-        for (int m = 0; m < H; ++m) {
-            const Chunk<CPT> hc = load_chunk<CPT>(hist + (static_cast<size_t>(slot) * H + m) * C + c0);
-            unpack<CPT>(hc, hs[m]);
-        }
-        // weights w[c][0..W-1] of the CPT channels: CPT*W contiguous bf16
-        uint16_t wr[CPT * W];
-        const uint16_t* wp = w + static_cast<size_t>(c0) * W;
+        const int grp = min(rs, kWG - 1);
         if (CPT == 8) {  // 16-byte aligned: w is, and c0 * W * 2 is a multiple of 16
-#pragma unroll
-            for (int e = 0; e < CPT * W; e += 8)
-                *reinterpret_cast<uint4*>(wr + e) = *reinterpret_cast<const uint4*>(wp + e);
+            wg4 = *reinterpret_cast<const uint4*>(wp + 8 * grp);
         } else {
+            uint32_t ww[4];
 #pragma unroll
-            for (int e = 0; e < CPT * W; ++e) wr[e] = wp[e];
+            for (int e = 0; e < 4; ++e) {
+                const int we = min(4 * grp + e, kWW - 1);
+                ww[e] = static_cast<uint32_t>(wp[2 * we]) | (static_cast<uint32_t>(wp[2 * we + 1]) << 16);
+            }
+            wg4 = make_uint4(ww[0], ww[1], ww[2], ww[3]);
         }
-#pragma unroll
-        for (int j = 0; j < CPT; ++j)
-#pragma unroll
-            for (int tap = 0; tap < W; ++tap) wt[tap][j] = bf16_bits_to_f32(wr[j * W + tap]);
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) bs[j] = bias ? bias[c0 + j] : 0.f;  // bias: uniform
     }
+    float4 bq = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (bias)  // uniform
+        bq = make_float4(bias[c0 + 4 * (rs & 1) + 0 < C ? c0 + 4 * (rs & 1) + 0 : c0],
+                         bias[c0 + 4 * (rs & 1) + 1 < C ? c0 + 4 * (rs & 1) + 1 : c0],
+                         bias[c0 + 4 * (rs & 1) + 2 < C ? c0 + 4 * (rs & 1) + 2 : c0],
+                         bias[c0 + 4 * (rs & 1) + 3 < C ? c0 + 4 * (rs & 1) + 3 : c0]);
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
         const int i = rs + p * kRowsPerPass;
         if (i < N) s_x[i * kTileLanes + lane] = xin[p];
     }
-    // take delivery of the weights and history here, in the same round trip
-    // as the node rows (left alone, the compiler sinks these loads to their
-    // first use after the barrier, a round trip of their own)
+    if (H > 0 && rs < H) s_x[(N + rs) * kTileLanes + lane] = hc;
+    if (rs < kWG) {
+        uint32_t* wd = s_w + lane * kWW + 4 * rs;
+        const uint32_t wv[4] = {wg4.x, wg4.y, wg4.z, wg4.w};
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-#pragma unroll
-        for (int tap = 0; tap < W; ++tap) asm volatile("" ::"v"(wt[tap][j]));
-#pragma unroll
-        for (int m = 0; m < H; ++m) asm volatile("" ::"v"(hs[m][j]));
+        for (int e = 0; e < 4; ++e)
+            if (4 * rs + e < kWW) wd[e] = wv[e];
     }
+    if (bias && rs < CPT / 4) *reinterpret_cast<float4*>(s_b + lane * CPT + 4 * rs) = bq;
     __syncthreads();
     if (!active) return;
 
     for (int i = rs; i < N; i += kRowsPerPass) {
+        uint32_t wr[kWW];
+#pragma unroll
+        for (int e = 0; e < kWW; ++e) wr[e] = s_w[lane * kWW + e];
+        auto wgt = [&](int j, int tap) -> float {
+            const int e = j * W + tap;
+            return (e & 1) ? __uint_as_float(wr[e >> 1] & 0xffff0000u) : __uint_as_float(wr[e >> 1] << 16);
+        };
         float z[CPT];
 #pragma unroll
         for (int tap = 0; tap < H; ++tap) {
-            const int sv = s_tap[i * H + tap];
             float xv[CPT];
-            if (sv >= 0) {
-                unpack<CPT>(s_x[sv * kTileLanes + lane], xv);
-            } else {
-                const int m = -sv - 1;
-#pragma unroll
-                for (int j = 0; j < CPT; ++j) {
-                    float hvv = hs[0][j];
-#pragma unroll
-                    for (int mm = 1; mm < H; ++mm) hvv = (m == mm) ? hs[mm][j] : hvv;
-                    xv[j] = hvv;
-                }
-            }
+            unpack<CPT>(s_x[s_tap[i * H + tap] * kTileLanes + lane], xv);
 #pragma unroll
             for (int j = 0; j < CPT; ++j)
-                z[j] = (tap == 0) ? wt[0][j] * xv[j] : fmaf(wt[tap][j], xv[j], z[j]);
+                z[j] = (tap == 0) ? wgt(j, 0) * xv[j] : fmaf(wgt(j, tap), xv[j], z[j]);
         }
         float xi[CPT];
         unpack<CPT>(s_x[i * kTileLanes + lane], xi);
@@ -215,8 +218,8 @@ __global__ void __launch_bounds__(kConvThreads)
         uint32_t* ow = reinterpret_cast<uint32_t*>(&o.u);
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
-            float zz = (H == 0) ? wt[H][j] * xi[j] : fmaf(wt[H][j], xi[j], z[j]);
-            if (bias) zz += bs[j];
+            float zz = (H == 0) ? wgt(j, H) * xi[j] : fmaf(wgt(j, H), xi[j], z[j]);
+            if (bias) zz += s_b[lane * CPT + j];
             if (act == GDN_ACT_SILU) zz = silu(zz);
             z[j] = zz;
         }
@@ -226,8 +229,9 @@ __global__ void __launch_bounds__(kConvThreads)
     }
 }
 
-size_t conv_lds_bytes(int N, int R, int cpt) {
-    return static_cast<size_t>(N) * kTileLanes * (cpt * 2) + static_cast<size_t>(R) * sizeof(int32_t);
+size_t conv_lds_bytes(int N, int R, int W, int cpt) {
+    return conv_lds_x_bytes(N, W, cpt) + static_cast<size_t>(kTileLanes) * (cpt * W / 2) * 4 +
+           static_cast<size_t>(kTileLanes) * cpt * 4 + static_cast<size_t>(R) * sizeof(int32_t);
 }
 
 hipError_t launch_conv(const gdn_tree_desc& d, const uint16_t* x, const uint16_t* hist, int P,
@@ -241,19 +245,23 @@ hipError_t launch_conv(const gdn_tree_desc& d, const uint16_t* x, const uint16_t
     const int cpt = wide ? 8 : 4;
     const int tile = kTileLanes * cpt;
     dim3 grid((C + tile - 1) / tile, d.B);
-    const size_t lds = conv_lds_bytes(d.N, d.R, cpt);
+    const size_t lds = conv_lds_bytes(d.N, d.R, d.W, cpt);
     if (lds > 60 * 1024) return hipErrorNotSupported;  // plus static LDS, within the 64 KiB default
-#define GDN_CONV_CASE(WW)                                                                      \
-    case WW:                                                                                   \
-        if (wide)                                                                              \
-            hipLaunchKernelGGL((conv_gather_kernel<WW, 8>), grid, dim3(kConvThreads), lds, s,  \
-                               d.N, d.R, C, d.shared, d.node_row, d.conv_src, d.status, x,     \
-                               hist, P, state_idx, w, bias, act, y, err);                      \
-        else                                                                                   \
-            hipLaunchKernelGGL((conv_gather_kernel<WW, 4>), grid, dim3(kConvThreads), lds, s,  \
-                               d.N, d.R, C, d.shared, d.node_row, d.conv_src, d.status, x,     \
-                               hist, P, state_idx, w, bias, act, y, err);                      \
+#define GDN_CONV_LAUNCH(WW, CC, PP)                                                             \
+    hipLaunchKernelGGL((conv_gather_kernel<WW, CC, PP>), grid, dim3(kConvThreads), lds, s, d.N, \
+                       d.R, C, d.shared, d.node_row, d.conv_src, d.status, x, hist, P,          \
+                       state_idx, w, bias, act, y, err)
+#define GDN_CONV_CASE(WW)                                                   \
+    case WW:                                                                \
+        if (wide) {                                                         \
+            if (small) GDN_CONV_LAUNCH(WW, 8, kMaxPasses / 2);              \
+            else GDN_CONV_LAUNCH(WW, 8, kMaxPasses);                        \
+        } else {                                                            \
+            if (small) GDN_CONV_LAUNCH(WW, 4, kMaxPasses / 2);              \
+            else GDN_CONV_LAUNCH(WW, 4, kMaxPasses);                        \
+        }                                                                   \
         break;
+    const bool small = d.N <= (kMaxPasses / 2) * kRowsPerPass;  // fewer row registers
     switch (d.W) {
         GDN_CONV_CASE(1)
         GDN_CONV_CASE(2)
@@ -263,6 +271,7 @@ hipError_t launch_conv(const gdn_tree_desc& d, const uint16_t* x, const uint16_t
             return hipErrorNotSupported;
     }
 #undef GDN_CONV_CASE
+#undef GDN_CONV_LAUNCH
     return hipGetLastError();
 }
 

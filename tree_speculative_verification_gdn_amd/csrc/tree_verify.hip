@@ -49,13 +49,12 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // ---------------------------------------------------------------------------
 constexpr int kD = 128;
 constexpr int kKQStride = 264;   // bf16 row of 128 + 8 bytes pad: conflict-free 8-byte reads
-constexpr int kCTStride = 512;   // fp32 row of 128
 
 // Node slots of the contraction: keys of node i at slot i, queries at slot
 // NP + i, NP = 32 * NPB >= N (a whole number of 32-row blocks, so a node's key
 // and query results sit in the same lane and register of different blocks).
 struct MfmaLds {
-    int a, v, kk, kq, kqs, nrm, sk, sq, al, be, rows, dep, anc, cidx, mf, mh, ml, cr, cq, total;
+    int a, v, gk, gq, nrm, sk, sq, al, be, rows, dep, anc, cidx, mh, ml, cr, cq, total;
     int mstride;  // bytes per row of the bf16 M halves
 };
 
@@ -69,10 +68,9 @@ __host__ __device__ inline MfmaLds mfma_lds_layout(int N, int NPB) {
     L.mstride = NP * 2 + 8;
     L.a = off;    off += align_up(MB * 32 * kKQStride, 16);  // K/Q rows (bf16)
     L.v = off;    off += align_up(N * kD * 2, 16);           // V rows (bf16)
-    L.kk = off;   off += align_up(N * N * 4, 16);  // [i][p]: k_i . k_(ancestor at depth p+1)
-    L.kq = off;   off += align_up(N * N * 4, 16);  // [i][p]: q_i . k_(ancestor at depth p+1)
-    L.kqs = off;  off += align_up(N * 4, 16);      // q_i . k_i
-    L.nrm = off;  off += align_up(2 * NP * 4, 16); // squared norms by slot
+    L.gk = off;   off += align_up(NP * NP * 4, 16);  // [i][j]: k_i . k_j (raw operands)
+    L.gq = off;   off += align_up(NP * NP * 4, 16);  // [i][j]: q_i . k_j
+    L.nrm = off;  off += align_up(2 * NP * 4, 16);   // squared norms by slot
     L.sk = off;   off += align_up(N * 4, 16);
     L.sq = off;   off += align_up(N * 4, 16);
     // per-node arrays written by every lane carry one spare entry (index N)
@@ -82,7 +80,6 @@ __host__ __device__ inline MfmaLds mfma_lds_layout(int N, int NPB) {
     L.dep = off;  off += align_up((N + 1) * 4, 16);
     L.anc = off;  off += align_up((N + 1) * 8, 16);
     L.cidx = off; off += align_up(N * N, 16);      // [i][p]: node at depth p+1 on i's root path
-    L.mf = off;   off += align_up(N * N * 4, 16);  // [i][p]: M[i][path node p] (fp32 scratch)
     L.mh = off;   off += align_up(NP * L.mstride, 16);
     L.ml = off;   off += align_up(NP * L.mstride, 16);
     L.cr = off;   off += align_up(N * 4, 16);      // P_i / |k_i|
@@ -166,7 +163,7 @@ __device__ __forceinline__ bf16x8_t lds_operand_m(const char* base, int stride, 
 }
 
 template <int NPB>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NPB == 1 ? 4 : 2, 8)))
     verify_mfma_kernel(int N, int R, int shared, const int32_t* __restrict__ node_row,
                        const uint64_t* __restrict__ anc_g, const int32_t* __restrict__ depth_g,
                        const int32_t* __restrict__ status, const uint16_t* __restrict__ q,
@@ -183,9 +180,8 @@ __global__ void __launch_bounds__(kThreads)
     const MfmaLds L = mfma_lds_layout(N, NPB);
     char* s_a = lds + L.a;
     uint16_t* s_v = reinterpret_cast<uint16_t*>(lds + L.v);
-    float* s_kk = reinterpret_cast<float*>(lds + L.kk);
-    float* s_kq = reinterpret_cast<float*>(lds + L.kq);
-    float* s_kqs = reinterpret_cast<float*>(lds + L.kqs);
+    float* s_gk = reinterpret_cast<float*>(lds + L.gk);
+    float* s_gq = reinterpret_cast<float*>(lds + L.gq);
     float* s_nrm = reinterpret_cast<float*>(lds + L.nrm);
     float* s_sk = reinterpret_cast<float*>(lds + L.sk);
     float* s_sq = reinterpret_cast<float*>(lds + L.sq);
@@ -195,24 +191,25 @@ __global__ void __launch_bounds__(kThreads)
     int32_t* s_dep = reinterpret_cast<int32_t*>(lds + L.dep);
     uint64_t* s_anc = reinterpret_cast<uint64_t*>(lds + L.anc);
     uint8_t* s_cidx = reinterpret_cast<uint8_t*>(lds + L.cidx);
-    float* s_mf = reinterpret_cast<float*>(lds + L.mf);
     char* s_mh = lds + L.mh;
     char* s_ml = lds + L.ml;
     float* s_cr = reinterpret_cast<float*>(lds + L.cr);
     float* s_cq = reinterpret_cast<float*>(lds + L.cq);
     const int mstride = L.mstride;
 
-    const uint32_t unit = xcd_local_order(blockIdx.x, gridDim.x);
-    const int b = static_cast<int>(unit / Hv);
-    const int h = static_cast<int>(unit % Hv);
-    const int t = shared ? 0 : b;
-    const int g = static_cast<int>((static_cast<int64_t>(h) * Hqk) / Hv);
+    constexpr int kSlots = NP / 8;      // node slots per thread: node tid/32 + 8u
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int hf = lane >> 5;
     const int l32 = lane & 31;
     const int r_own = wave * 32 + l32;  // value row this lane owns in every MFMA
+
+    const uint32_t unit = xcd_local_order(blockIdx.x, gridDim.x);
+    const int b = static_cast<int>(unit / Hv);
+    const int h = static_cast<int>(unit % Hv);
+    const int t = shared ? 0 : b;
+    const int g = static_cast<int>((static_cast<int64_t>(h) * Hqk) / Hv);
     const size_t tb = static_cast<size_t>(t) * N;
     const size_t rowb = static_cast<size_t>(b) * R;
 
@@ -220,24 +217,16 @@ __global__ void __launch_bounds__(kThreads)
     //     issue order, so the K/Q/V rows go out before the 64 KiB state: the
     //     Gram block and the M solve below run on them while the state is
     //     still arriving, and only the state contraction waits for it.
-    //   (a1) the tree's rows (per staging item), ancestors, depths; status, slot.
-    //   Every load below is unconditional, from an index clamped into range, and
-    //   the unused results are dropped afterwards: a load under a per-lane
-    //   condition becomes a branch that waits for it before the next one issues.
+    //   (a1) the tree's rows per node slot, this lane's node's row, ancestors
+    //   and depth; status and slot.  Every load here and below is
+    //   unconditional, from an index clamped into range, and unused results
+    //   are dropped afterwards: a load under a per-lane condition becomes a
+    //   branch that waits for it before the next one issues.
     const int st = status[t];
     const int slot = state_idx[b];
-    int kq_row[kKQItems], v_row[kVItems];
+    int nrow[kSlots];
 #pragma unroll
-    for (int u = 0; u < kKQItems; ++u) {
-        const int sl = (tid + u * kThreads) >> 5;
-        const int node = sl < NP ? sl : sl - NP;
-        kq_row[u] = node_row[tb + min(node, N - 1)];
-    }
-#pragma unroll
-    for (int u = 0; u < kVItems; ++u) {
-        const int node = (tid + u * kThreads) >> 5;
-        v_row[u] = node_row[tb + min(node, N - 1)];
-    }
+    for (int x = 0; x < kSlots; ++x) nrow[x] = node_row[tb + min(tid / 32 + 8 * x, N - 1)];
     const int my_node = min(tid, N - 1);
     const int my_row = node_row[tb + my_node];
     const uint64_t my_anc = anc_g[tb + my_node];
@@ -249,23 +238,20 @@ __global__ void __launch_bounds__(kThreads)
     }
     //   (a2) K/Q/V chunks and the gates of every node (rows of a valid tree are
     //        in range, so the clamped loads are too)
+    static_assert(kKQItems == 2 * kSlots && kVItems == kSlots, "item u uses node slot u mod kSlots");
     uint2 kq_val[kKQItems];
 #pragma unroll
     for (int u = 0; u < kKQItems; ++u) {
-        const int it = tid + u * kThreads;
-        const int sl = it >> 5;
-        const int ch = it & 31;
-        const uint16_t* src = (sl < NP ? k : q) + (rowb + kq_row[u]) * rs_qk +
-                              static_cast<size_t>(g) * kD + ch * 4;
+        const int sl = (tid + u * kThreads) >> 5;
+        const uint16_t* src = (sl < NP ? k : q) + (rowb + nrow[u % kSlots]) * rs_qk +
+                              static_cast<size_t>(g) * kD + (tid & 31) * 4;
         kq_val[u] = *reinterpret_cast<const uint2*>(src);
     }
     uint2 v_val[kVItems];
 #pragma unroll
-    for (int u = 0; u < kVItems; ++u) {
-        const int it = tid + u * kThreads;
-        v_val[u] = *reinterpret_cast<const uint2*>(v + (rowb + v_row[u]) * rs_v +
-                                                   static_cast<size_t>(h) * kD + (it & 31) * 4);
-    }
+    for (int u = 0; u < kVItems; ++u)
+        v_val[u] = *reinterpret_cast<const uint2*>(v + (rowb + nrow[u]) * rs_v +
+                                                   static_cast<size_t>(h) * kD + (tid & 31) * 4);
     const size_t my_gi = (rowb + my_row) * Hv + h;
     const float my_al = alpha[my_gi];
     const float my_be = beta[my_gi];
@@ -332,8 +318,8 @@ __global__ void __launch_bounds__(kThreads)
         s_cidx[tid * N + p] = static_cast<uint8_t>(tid);
     }
 
-    // (c) Gram block on the matrix cores (exact bf16 products, fp32 sums):
-    //     k_i . k_j and q_i . k_j for every ancestor j, stored at j's depth
+    // (c) Gram block on the matrix cores (exact bf16 products, fp32 sums),
+    //     stored dense: k_i . k_j and q_i . k_j for every pair of slots
     {
         constexpr int kTiles = MB * NPB;  // all query/key row blocks x key column blocks
         for (int tile = wave; tile < kTiles; tile += kThreads / 64) {
@@ -346,55 +332,95 @@ __global__ void __launch_bounds__(kThreads)
                 const bf16x8_t bb = lds_operand(s_a, tcol * 32 + l32, s, hf);
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc, 0, 0, 0);
             }
+            float* gdst = (ta < NPB) ? s_gk + ta * 32 * NP : s_gq + (ta - NPB) * 32 * NP;
             const int col = tcol * 32 + l32;
-            if (col < N) {
-                const int pos = s_dep[col] - 1;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int rs = ta * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
-                    const bool is_q = rs >= NP;
-                    const int i = is_q ? rs - NP : rs;
-                    if (i < N) {
-                        const bool anc_ij = ((s_anc[i] >> col) & 1ull) != 0ull;
-                        if (anc_ij) (is_q ? s_kq : s_kk)[i * N + pos] = acc[e];
-                        if (is_q && col == i) s_kqs[i] = acc[e];
-                    }
-                }
-            }
+            for (int e = 0; e < 16; ++e) gdst[(8 * (e >> 2) + 4 * hf + (e & 3)) * NP + col] = acc[e];
         }
     }
     __syncthreads();
 
-    // (e) row i of M = C (I + G)^-1 by back-substitution along i's root path
-    if (tid < N) {
-        const int i = tid;
-        const int d = s_dep[i];
-        const uint8_t* path = s_cidx + i * N;
-        float* mrow = s_mf + i * N;
-        const float sq_i = s_sq[i];
-        float wq = 1.0f;  // product of the decays on the path strictly below position p
-        for (int p = d - 1; p >= 0; --p) {
-            const int j = path[p];
+    // (e) M = C (I + G)^-1, row by row: along node i's root path n_0 .. n_(d-1) = i,
+    //       M_(i,n_p) = C_(i,n_p) - sum_(s > p) M_(i,n_s) G_(n_s,n_p)
+    //     with C_(i,j) = (P_i/P_j) q^_i.k^_j and G_(m,j) = b_m (P_m/P_j) k^_m.k^_j, the
+    //     decay ratios taken as products of the decays strictly below j.  A group
+    //     of kLP lanes holds one node, lane p its path position p: each lane forms
+    //     its G column, then the deepest position is final and is eliminated from
+    //     the shallower ones, one position per step.  Nodes deeper than kLP are
+    //     solved one thread per node afterwards.
+    {
+        constexpr int kLP = 8;
+        const int p = tid & (kLP - 1);
+        const int grp_lane0 = lane & ~(kLP - 1);
+        for (int i0 = 0; i0 < N; i0 += kThreads / kLP) {
+            const int i = i0 + tid / kLP;
+            const int ii = min(i, N - 1);
+            const int d = s_dep[ii];
+            const bool act = i < N && d <= kLP && p < d;
+            const uint8_t* path = s_cidx + ii * N;
+            const int j = path[min(p, d - 1)];
             const float sk_j = s_sk[j];
-            float val = wq * sq_i * sk_j * (p == d - 1 ? s_kqs[i] : s_kq[i * N + p]);
-            float wg = 1.0f;  // decays on the path strictly below p, up to and including s
-            for (int sidx = p + 1; sidx < d; ++sidx) {
-                const int m = path[sidx];
-                wg *= s_al[m];
-                const float gmj = s_be[m] * wg * s_sk[m] * sk_j * s_kk[m * N + p];
-                val = fmaf(-mrow[sidx], gmj, val);
+            float gco[kLP];
+            float r = 1.0f;  // decays of positions p+1 .. s
+#pragma unroll
+            for (int sp = 1; sp < kLP; ++sp) {
+                const bool in = sp > p && sp < d;
+                const int m = path[min(sp, d - 1)];
+                r *= in ? s_al[m] : 1.0f;
+                gco[sp] = in ? s_be[m] * s_sk[m] * sk_j * s_gk[m * NP + j] * r : 0.0f;
             }
-            mrow[p] = val;
-            const uint32_t hv = cvt_pk_bf16(val, 0.0f) & 0xffffu;
-            const float rest = val - __uint_as_float(hv << 16);
-            const uint32_t lv = cvt_pk_bf16(rest, 0.0f) & 0xffffu;
-            reinterpret_cast<uint16_t*>(s_mh + i * mstride)[j] = static_cast<uint16_t>(hv);
-            reinterpret_cast<uint16_t*>(s_ml + i * mstride)[j] = static_cast<uint16_t>(lv);
-            wq *= s_al[j];
+            // r = P_i / P_j now
+            float val = r * s_sq[ii] * sk_j * s_gq[ii * NP + j];
+#pragma unroll
+            for (int sp = kLP - 1; sp >= 1; --sp) {
+                const float ms = __shfl(val, grp_lane0 | sp, 64);  // final M at position sp
+                val = (sp < d && p < sp) ? fmaf(-ms, gco[sp], val) : val;
+            }
+            if (act) {
+                const uint32_t hv = cvt_pk_bf16(val, 0.0f) & 0xffffu;
+                const float rest = val - __uint_as_float(hv << 16);
+                const uint32_t lv = cvt_pk_bf16(rest, 0.0f) & 0xffffu;
+                reinterpret_cast<uint16_t*>(s_mh + i * mstride)[j] = static_cast<uint16_t>(hv);
+                reinterpret_cast<uint16_t*>(s_ml + i * mstride)[j] = static_cast<uint16_t>(lv);
+                if (p == 0) {
+                    const float P_i = r * s_al[j];  // j = n_0: times the root-level decay
+                    s_cr[i] = P_i * s_sk[i];
+                    s_cq[i] = P_i * s_sq[i];
+                }
+            }
         }
-        // wq is now P_i
-        s_cr[i] = wq * s_sk[i];
-        s_cq[i] = wq * sq_i;
+        // nodes deeper than kLP: one thread per node, the same elimination in
+        // place (M values so far read back from their hi + lo halves)
+        if (tid < N && s_dep[tid] > kLP) {
+            const int i = tid;
+            const int d = s_dep[i];
+            const uint8_t* path = s_cidx + i * N;
+            const float sq_i = s_sq[i];
+            uint16_t* mh = reinterpret_cast<uint16_t*>(s_mh + i * mstride);
+            uint16_t* ml = reinterpret_cast<uint16_t*>(s_ml + i * mstride);
+            float wq = 1.0f;  // decays of the positions below p
+            for (int pp = d - 1; pp >= 0; --pp) {
+                const int jj = path[pp];
+                const float sk_j = s_sk[jj];
+                float val = wq * sq_i * sk_j * s_gq[i * NP + jj];
+                float wg = 1.0f;
+                for (int sp = pp + 1; sp < d; ++sp) {
+                    const int m = path[sp];
+                    wg *= s_al[m];
+                    const float gmj = s_be[m] * wg * s_sk[m] * sk_j * s_gk[m * NP + jj];
+                    const float msv = bf16_bits_to_f32(mh[m]) + bf16_bits_to_f32(ml[m]);
+                    val = fmaf(-msv, gmj, val);
+                }
+                const uint32_t hv = cvt_pk_bf16(val, 0.0f) & 0xffffu;
+                const float rest = val - __uint_as_float(hv << 16);
+                const uint32_t lv = cvt_pk_bf16(rest, 0.0f) & 0xffffu;
+                mh[jj] = static_cast<uint16_t>(hv);
+                ml[jj] = static_cast<uint16_t>(lv);
+                wq *= s_al[jj];
+            }
+            s_cr[i] = wq * s_sk[i];
+            s_cq[i] = wq * sq_i;
+        }
     }
     __syncthreads();
 
