@@ -228,3 +228,144 @@ def straddle_rows(case, y_gpu, y_ref):
             if i in path:
                 state_mask[b, hs] = True
     return out_mask, state_mask
+
+
+# --------------------------------------------------------------------------
+# the fused steady-state step: commit of step 1's accepted path, then the
+# conv and verify of step 2's tree (same requests, pool and history)
+# --------------------------------------------------------------------------
+
+def two_step_case(cfg, seed, B=None, extra_slots=0, packing="perm"):
+    """Two consecutive steps of one layer: step 2 has its own trees, rows,
+    operands and paths, and the requests' pool slots and history of step 1."""
+    c1 = gi.make_case(cfg, seed=seed, B=B, extra_slots=extra_slots, packing=packing)
+    c2 = gi.make_case(cfg, seed=seed + 7919, B=B, extra_slots=extra_slots, packing=packing)
+    for key in ("pool", "state_idx", "P", "hist"):
+        if key in c1:
+            c2[key] = c1[key]
+    return c1, c2
+
+
+def _qkv_of(cfg, B, ybits):
+    R, D, Hv, Hqk = cfg.R, cfg.D, cfg.Hv, cfg.Hqk
+    q = ybits[:, :, :Hqk * D].reshape(B, R, Hqk, D)
+    k = ybits[:, :, Hqk * D:2 * Hqk * D].reshape(B, R, Hqk, D)
+    v = ybits[:, :, 2 * Hqk * D:].reshape(B, R, Hv, D)
+    return q, k, v
+
+
+def run_oracle_two_steps(c1, c2):
+    """The oracle: commit step 1's path (with the history publication), then
+    step 2's conv and verify from the committed state and history."""
+    cfg = c1["cfg"]
+    R, Hv, Hqk = cfg.R, cfg.Hv, cfg.Hqk
+    W = cfg.conv_W if cfg.conv_W > 0 else 1
+    B = c1["B"]
+    d1 = oracle.desc_build(c1["parent"], c1["node_row"], R, W)
+    d2 = oracle.desc_build(c2["parent"], c2["node_row"], R, W)
+    res = dict(err=d1["err"] | d2["err"], status1=d1["status"], status2=d2["status"])
+    norm = cfg.norm_qk if cfg.conv_W > 0 else False
+    if cfg.conv_W > 0:
+        y1, e = oracle.conv(c1["node_row"], d1["conv_src"], d1["status"], c1["x"], c1["hist"],
+                            c1["state_idx"], c1["w"], None, cfg.act, R, cfg.conv_C, W)
+        res["err"] |= e
+        y1b = np.where(np.isnan(y1), NAN_BF16, oracle.round_f64_to_bf16_bits(y1)).astype(np.uint16)
+        q1, k1, v1 = _qkv_of(cfg, B, y1b)
+        res["y1"] = y1b
+    else:
+        k1, v1 = c1["k"], c1["v"]
+    pool, hist, e = oracle.commit(c1["parent"], c1["node_row"], d1["status"], c1["path"],
+                                  c1["path_len"], k1, v1, c1["alpha"], c1["beta"], c1["pool"],
+                                  c1["state_idx"], Hqk, Hv, norm, x=c1.get("x"), hist=c1.get("hist"),
+                                  W=W)
+    res["err"] |= e
+    res["pool"] = pool
+    if cfg.conv_W > 0:
+        res["hist"] = hist
+        hbits = oracle.round_f64_to_bf16_bits(hist)
+        y2, e = oracle.conv(c2["node_row"], d2["conv_src"], d2["status"], c2["x"], hbits,
+                            c2["state_idx"], c2["w"], None, cfg.act, R, cfg.conv_C, W)
+        res["err"] |= e
+        y2b = np.where(np.isnan(y2), NAN_BF16, oracle.round_f64_to_bf16_bits(y2)).astype(np.uint16)
+        q2, k2, v2 = _qkv_of(cfg, B, y2b)
+        res["y2"] = y2b
+    else:
+        q2, k2, v2 = c2["q"], c2["k"], c2["v"]
+    out, e = oracle.verify(c2["parent"], c2["node_row"], d2["status"], q2, k2, v2, c2["alpha"],
+                           c2["beta"], pool, c2["state_idx"], Hqk, Hv, norm)
+    res["err"] |= e
+    res["out"] = out
+    return res
+
+
+def run_gpu_two_steps(c1, c2, fused=True, y1_override=None, y2_override=None, flags=0):
+    """Step 1's recorded operands (its conv output for conv configs), then
+    step 2 through the fused calls (conv_ancestry_gather_publish and
+    gdn_tree_commit_verify), or through the separate calls (commit with the
+    history, conv, verify) when fused is False.  With y*_override the
+    device's own conv outputs are kept in res but the GDN stages read the
+    given ones (stage-wise parity)."""
+    import torch
+    import tree_speculative_verification_gdn_amd as g
+
+    cfg = c1["cfg"]
+    B, R, D, Hv, Hqk = c1["B"], cfg.R, cfg.D, cfg.Hv, cfg.Hqk
+    W = cfg.conv_W if cfg.conv_W > 0 else 1
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    d1 = g.TreeDesc(to_dev(c1["parent"]), to_dev(c1["node_row"]), R, W)
+    d2 = g.TreeDesc(to_dev(c2["parent"]), to_dev(c2["node_row"]), R, W)
+    g.gdn_tree_desc_build(d1, err)
+    g.gdn_tree_desc_build(d2, err)
+    pool = to_dev(c1["pool"])
+    sidx = to_dev(c1["state_idx"])
+    a1, b1 = to_dev(c1["alpha"]), to_dev(c1["beta"])
+    a2, b2 = to_dev(c2["alpha"]), to_dev(c2["beta"])
+    p1, l1 = to_dev(c1["path"]), to_dev(c1["path_len"])
+    res = {}
+    if cfg.conv_W > 0:
+        C = cfg.conv_C
+        flags |= g.GDN_F_NORM_QK if cfg.norm_qk else 0
+        hist = to_dev(c1["hist"])
+        w1, w2 = to_dev(c1["w"]), to_dev(c2["w"])
+        x1, x2 = to_dev(c1["x"]), to_dev(c2["x"])
+        y1 = torch.full((B, R, C), float("nan"), dtype=torch.bfloat16, device="cuda")
+        g.conv_ancestry_gather(d1, x1, hist, sidx, w1, None, y1, cfg.act, err)
+        res["y1"] = bits(y1)
+        if y1_override is not None:
+            y1.copy_(to_dev(np.where(y1_override == NAN_BF16, res["y1"], y1_override).astype(np.uint16)))
+        q1 = y1[:, :, :Hqk * D].unflatten(-1, (Hqk, D))
+        k1 = y1[:, :, Hqk * D:2 * Hqk * D].unflatten(-1, (Hqk, D))
+        v1 = y1[:, :, 2 * Hqk * D:].unflatten(-1, (Hv, D))
+        y2 = torch.full((B, R, C), float("nan"), dtype=torch.bfloat16, device="cuda")
+        if fused:
+            g.conv_ancestry_gather_publish(d2, x2, hist, sidx, w2, None, y2, cfg.act, d1, p1, l1,
+                                           x1, err)
+        else:
+            g.gdn_tree_commit(d1, p1, l1, k1, v1, a1, b1, pool, sidx, err, Hqk=Hqk,
+                              flags=flags & g.GDN_F_NORM_QK, x=x1, hist=hist)
+            g.conv_ancestry_gather(d2, x2, hist, sidx, w2, None, y2, cfg.act, err)
+        res["y2"] = bits(y2)
+        if y2_override is not None:
+            y2.copy_(to_dev(np.where(y2_override == NAN_BF16, res["y2"], y2_override).astype(np.uint16)))
+        q2 = y2[:, :, :Hqk * D].unflatten(-1, (Hqk, D))
+        k2 = y2[:, :, Hqk * D:2 * Hqk * D].unflatten(-1, (Hqk, D))
+        v2 = y2[:, :, 2 * Hqk * D:].unflatten(-1, (Hv, D))
+    else:
+        hist = None
+        k1, v1 = to_dev(c1["k"]), to_dev(c1["v"])
+        q2, k2, v2 = to_dev(c2["q"]), to_dev(c2["k"]), to_dev(c2["v"])
+    out = torch.full((B, R, Hv, D), float("nan"), dtype=torch.float32, device="cuda")
+    if fused:
+        g.gdn_tree_commit_verify(d2, q2, k2, v2, a2, b2, pool, sidx, out, d1, p1, l1, k1, v1, a1,
+                                 b1, err, flags=flags)
+    else:
+        if cfg.conv_W == 0:
+            g.gdn_tree_commit(d1, p1, l1, k1, v1, a1, b1, pool, sidx, err, Hqk=Hqk,
+                              flags=flags & g.GDN_F_NORM_QK)
+        g.gdn_tree_verify(d2, q2, k2, v2, a2, b2, pool, sidx, out, err, flags=flags)
+    torch.cuda.synchronize()
+    res.update(err=int(err.item()), out=out.cpu().numpy(), pool=pool.cpu().numpy(),
+               status1=d1.status.cpu().numpy(), status2=d2.status.cpu().numpy())
+    if hist is not None:
+        res["hist"] = bits(hist)
+    return res

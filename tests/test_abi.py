@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.gdn_abi_version() == 1
+    assert lib.gdn_abi_version() == 2
     assert lib.gdn_status_string(0) == b"ok"
     assert lib.gdn_status_string(-1) == b"invalid argument"
     assert lib.gdn_status_string(-4) == b"unsupported size"

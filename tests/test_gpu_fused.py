@@ -1,0 +1,163 @@
+"""GPU parity of the fused steady-state step: conv_ancestry_gather_publish and
+gdn_tree_commit_verify (commit of step 1's accepted path, then step 2's conv
+and verify from the committed state and history) against the oracle's
+commit -> conv -> verify on the same seeded inputs, and against the separate
+calls on the device.
+
+Bars as in the other parity tests: error bits, status and the published
+history bit-exact; conv output within 1 bf16 ulp; outputs and committed states
+within 2e-3 in the max-relative-per-row metric; states the commit must not
+touch bit-unchanged.
+"""
+import numpy as np
+import pytest
+
+import gdn_inputs as gi
+from harness import (bf16_ulp_diff, hist_to_bits, max_rel_rows, node_rows_mask,
+                     run_gpu_two_steps, run_oracle_two_steps, subset, two_step_case)
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+def _committed(c1, orr):
+    """Requests whose step-1 path the oracle committed (state changed)."""
+    ok = []
+    for b in range(c1["B"]):
+        s = c1["state_idx"][b]
+        ok.append(not np.array_equal(orr["pool"][s], c1["pool"][s], equal_nan=True))
+    return np.array(ok)
+
+
+def _cmp(c1, c2, gr, orr, conv=False, tol=TOL):
+    assert gr["err"] == orr["err"], (gr["err"], orr["err"])
+    assert np.array_equal(gr["status1"], orr["status1"])
+    assert np.array_equal(gr["status2"], orr["status2"])
+    m = node_rows_mask(c2) & (orr["status2"] == 0)[:, None]
+    rel_o = max_rel_rows(gr["out"][m], orr["out"][m], 2) if m.any() else 0.0
+    assert rel_o <= tol, f"output max rel {rel_o:.3e}"
+    assert np.isnan(gr["out"][~m]).all()          # padding rows and skipped trees untouched
+    used = c1["state_idx"]
+    rel_s = max_rel_rows(gr["pool"][used], orr["pool"][used], 2)
+    assert rel_s <= tol, f"state max rel {rel_s:.3e}"
+    unused = np.setdiff1d(np.arange(gr["pool"].shape[0]), used)
+    assert np.array_equal(gr["pool"][unused], c1["pool"][unused], equal_nan=True)
+    same = ~_committed(c1, orr)                   # not committed: bit-unchanged
+    assert np.array_equal(gr["pool"][used[same]], c1["pool"][used[same]])
+    if conv:
+        assert np.array_equal(gr["hist"], hist_to_bits(orr["hist"]))
+        m2 = node_rows_mask(c2)
+        d = bf16_ulp_diff(gr["y2"][m2], orr["y2"][m2])
+        tiny = ((np.abs(gi.bf16_bits_to_f32(gr["y2"][m2])) < 2.0 ** -126)
+                & (np.abs(gi.bf16_bits_to_f32(orr["y2"][m2])) < 2.0 ** -126))
+        assert (d[~tiny] <= 1).all(), f"conv ulp diff {d.max()}"
+    return rel_o, rel_s
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_two_steps_tree27(fused):
+    c1, c2 = two_step_case(gi.CONFIGS[3], seed=31, B=8, extra_slots=2)
+    gr = run_gpu_two_steps(c1, c2, fused=fused)
+    orr = run_oracle_two_steps(c1, c2)
+    _cmp(c1, c2, gr, orr)
+
+
+def test_two_steps_chain8_full_path():
+    c1, c2 = two_step_case(gi.CONFIGS[2], seed=5, B=8)
+    gr = run_gpu_two_steps(c1, c2)
+    orr = run_oracle_two_steps(c1, c2)
+    _cmp(c1, c2, gr, orr)
+
+
+def test_two_steps_conv4_publishes_history():
+    c1, c2 = two_step_case(gi.CONFIGS[4], seed=2026, B=8, extra_slots=1)
+    orr = run_oracle_two_steps(c1, c2)
+    # stage-wise: the GDN stages read the oracle's own bf16 conv outputs
+    gr = run_gpu_two_steps(c1, c2, y1_override=orr["y1"], y2_override=orr["y2"])
+    _cmp(c1, c2, gr, orr, conv=True)
+    # the separate calls give the same history and conv output
+    gs = run_gpu_two_steps(c1, c2, fused=False, y1_override=orr["y1"], y2_override=orr["y2"])
+    assert np.array_equal(gs["hist"], gr["hist"])
+    assert np.array_equal(gs["y2"], gr["y2"])
+
+
+def test_two_steps_tree64_long_paths():
+    # 64-node trees: two 32-row blocks per request, paths of up to 9 rows
+    c1, c2 = two_step_case(gi.CONFIGS[5], seed=9, B=6)
+    gr = run_gpu_two_steps(c1, c2)
+    orr = run_oracle_two_steps(c1, c2)
+    _cmp(c1, c2, gr, orr)
+
+
+@pytest.mark.parametrize("N", [20, 64])
+def test_two_steps_long_chains(N):
+    # the staged path does not fit over the Gram block (N = 20) or needs the
+    # second 32-row block (N = 64); every path is the whole chain
+    cfg = gi.CONFIGS[2].replace(N=N, R=N + 3, Hv=4, Hqk=2)
+    c1, c2 = two_step_case(cfg, seed=N, B=3)
+    gr = run_gpu_two_steps(c1, c2)
+    orr = run_oracle_two_steps(c1, c2)
+    _cmp(c1, c2, gr, orr)
+
+
+def test_two_steps_edge_cases():
+    cfg = gi.CONFIGS[3].replace(B=10)
+    c1, c2 = two_step_case(cfg, seed=44, extra_slots=2)
+    c1["path_len"][0] = 0                          # nothing accepted
+    c1["path"][1, 0] = c1["path"][1, 1] if c1["path_len"][1] > 1 else 3
+    c1["path_len"][1] = max(int(c1["path_len"][1]), 1)   # malformed path
+    c1["path_len"][2] = cfg.Lmax + 1               # longer than Lmax
+    c1["parent"][3, 5] = 9                         # step-1 tree malformed: nothing committed
+    c2["parent"][4, 7] = 20                        # step-2 tree malformed: committed, not verified
+    c1["state_idx"][6] = c1["state_idx"][7]        # shared slot: both skipped by the commit
+    c2["state_idx"] = c1["state_idx"]
+    gr = run_gpu_two_steps(c1, c2)
+    orr = run_oracle_two_steps(c1, c2)
+    import tree_speculative_verification_gdn_amd as g
+    assert orr["err"] == g.GDN_EV_PARENT | g.GDN_EV_PATH | g.GDN_EV_STATE
+    _cmp(c1, c2, gr, orr)
+
+
+def test_two_steps_conv4_edge_cases():
+    cfg = gi.CONFIGS[4].replace(B=5)
+    c1, c2 = two_step_case(cfg, seed=12, extra_slots=1)
+    c1["path_len"][0] = 0
+    c1["path"][1, 0] = 4                           # malformed: no publication either
+    orr = run_oracle_two_steps(c1, c2)
+    gr = run_gpu_two_steps(c1, c2, y1_override=orr["y1"], y2_override=orr["y2"])
+    _cmp(c1, c2, gr, orr, conv=True)
+
+
+def test_two_steps_fallback_d32_f32():
+    # fp32 operands at d = 32: commit and verify kernels one after the other
+    c1, c2 = two_step_case(gi.CONFIGS[1], seed=3)
+    gr = run_gpu_two_steps(c1, c2)
+    orr = run_oracle_two_steps(c1, c2)
+    _cmp(c1, c2, gr, orr)
+
+
+def test_two_steps_conv4_full_size_sampled():
+    # the bench's workload at full size on the device; the oracle on a sample
+    cfg = gi.CONFIGS[4]
+    c1, c2 = two_step_case(cfg, seed=2026, packing="bfs")
+    gr = run_gpu_two_steps(c1, c2)
+    gs = run_gpu_two_steps(c1, c2, fused=False)
+    assert gr["err"] == gs["err"] == 0
+    assert np.array_equal(gr["hist"], gs["hist"]) and np.array_equal(gr["y2"], gs["y2"])
+    m = node_rows_mask(c2)
+    # fused and separate differ only in the order of fp32 sums
+    assert max_rel_rows(gr["out"][m], gs["out"][m], 2) <= 1e-4
+    used = c1["state_idx"]
+    assert max_rel_rows(gr["pool"][used], gs["pool"][used], 2) <= 1e-4
+    bs = np.array([0, 33, 64, 127])
+    s1, s2 = subset(c1, bs), subset(c2, bs)
+    s2["pool"], s2["hist"] = s1["pool"], s1["hist"]
+    orr = run_oracle_two_steps(s1, s2)
+    g1 = dict(out=gr["out"][bs], pool=gr["pool"][used[bs]], hist=gr["hist"][used[bs]], y2=gr["y2"][bs],
+              err=gr["err"], status1=gr["status1"][bs], status2=gr["status2"][bs])
+    # own conv outputs downstream: a one-ulp straddle may move an output by 2^-8
+    assert np.array_equal(g1["hist"], hist_to_bits(orr["hist"]))
+    d = bf16_ulp_diff(g1["y2"][node_rows_mask(s2)], orr["y2"][node_rows_mask(s2)])
+    assert d.max() <= 1
+    assert np.isfinite(g1["out"][node_rows_mask(s2)]).all()

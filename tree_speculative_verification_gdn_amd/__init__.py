@@ -8,7 +8,9 @@ the computation runs in the library's HIP kernels.  There is no fallback: if
 the shared library is missing, every call raises.
 
 Entry points (same names as the C ABI):
-    gdn_tree_desc_build, conv_ancestry_gather, gdn_tree_verify, gdn_tree_commit
+    gdn_tree_desc_build, conv_ancestry_gather, gdn_tree_verify, gdn_tree_commit,
+    and the fused steady-state step: conv_ancestry_gather_publish,
+    gdn_tree_commit_verify
 Helper: TreeDesc (owns the descriptor's device arrays and the C struct).
 """
 from __future__ import annotations
@@ -23,6 +25,7 @@ __all__ = [
     "GDN_DT_BF16", "GDN_DT_F32", "GDN_F_NORM_QK", "GDN_F_OUT_BF16", "GDN_F_VALU",
     "GDN_ACT_NONE", "GDN_ACT_SILU", "GdnError", "TreeDesc", "library_path", "load_library",
     "gdn_tree_desc_build", "conv_ancestry_gather", "gdn_tree_verify", "gdn_tree_commit",
+    "conv_ancestry_gather_publish", "gdn_tree_commit_verify",
 ]
 
 # values mirror include/gdn_tree.h
@@ -33,7 +36,8 @@ GDN_F_NORM_QK, GDN_F_OUT_BF16, GDN_F_VALU = 1, 2, 4
 GDN_ACT_NONE, GDN_ACT_SILU = 0, 1
 
 EXPORTED = ("gdn_tree_desc_build", "conv_ancestry_gather", "gdn_tree_verify",
-            "gdn_tree_commit", "gdn_status_string", "gdn_abi_version")
+            "gdn_tree_commit", "conv_ancestry_gather_publish", "gdn_tree_commit_verify",
+            "gdn_status_string", "gdn_abi_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lock = threading.Lock()
@@ -82,6 +86,13 @@ def load_library():
         lib.gdn_tree_commit.restype = i32
         lib.gdn_tree_commit.argtypes = [dp, vp, vp, i32, vp, vp, i64, i64, vp, vp, vp, i32, vp,
                                         vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp]
+        lib.conv_ancestry_gather_publish.restype = i32
+        lib.conv_ancestry_gather_publish.argtypes = [dp, vp, vp, i32, vp, vp, vp, vp, i32, i32,
+                                                     dp, vp, vp, i32, vp, vp, vp]
+        lib.gdn_tree_commit_verify.restype = i32
+        lib.gdn_tree_commit_verify.argtypes = [dp, vp, vp, vp, i64, i64, vp, vp, vp, i32, vp, vp,
+                                               dp, vp, vp, i32, vp, vp, i64, i64, vp, vp,
+                                               i32, i32, i32, i32, i32, i32, vp, vp]
         lib.gdn_status_string.restype = ctypes.c_char_p
         lib.gdn_status_string.argtypes = [i32]
         lib.gdn_abi_version.restype = i32
@@ -233,3 +244,45 @@ def gdn_tree_commit(desc: TreeDesc, path, path_len, k, v, alpha, beta, state_poo
                                           _ptr(hist), C, Hqk, Hv, dk, dv, _dtype_code(k),
                                           int(flags), _ptr(err), _stream(stream))
     return _check(code, "gdn_tree_commit", raise_on_error)
+
+
+def conv_ancestry_gather_publish(desc: TreeDesc, x, hist, state_idx, w, bias, y, act: int,
+                                 prev: TreeDesc, path, path_len, x_prev, err, stream=None,
+                                 raise_on_error=True) -> int:
+    """Publish the conv history of the previous step's accepted path (prev's
+    tree, path [B, Lmax], path_len [B], its conv input x_prev [B, prev R, C]),
+    then convolve desc's tree as conv_ancestry_gather does."""
+    C = int(x.shape[-1])
+    P = int(hist.shape[0]) if hist is not None else 1
+    Lmax = int(path.shape[1])
+    code = load_library().conv_ancestry_gather_publish(
+        desc.ref(), _ptr(x), _ptr(hist), P, _ptr(state_idx), _ptr(w), _ptr(bias), _ptr(y), C,
+        int(act), prev.ref(), _ptr(path), _ptr(path_len), Lmax, _ptr(x_prev), _ptr(err),
+        _stream(stream))
+    return _check(code, "conv_ancestry_gather_publish", raise_on_error)
+
+
+def gdn_tree_commit_verify(desc: TreeDesc, q, k, v, alpha, beta, state_pool, state_idx, out,
+                           prev: TreeDesc, path, path_len, k_prev, v_prev, alpha_prev,
+                           beta_prev, err, flags: int = 0, stream=None,
+                           raise_on_error=True) -> int:
+    """Commit the previous step's accepted path (prev's tree; its recorded
+    k_prev, v_prev, alpha_prev, beta_prev) into state_pool, then verify desc's
+    tree from the committed state into out (layouts as in gdn_tree_verify)."""
+    rs_qk, Hqk, dk = _rows_view(q, "q")
+    rs_k, Hk, dk2 = _rows_view(k, "k")
+    rs_v, Hv, dv = _rows_view(v, "v")
+    if rs_k != rs_qk or Hk != Hqk or dk2 != dk or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q and k must share layout and dtype with v")
+    rs_qkp, Hkp, _ = _rows_view(k_prev, "k_prev")
+    rs_vp, Hvp, _ = _rows_view(v_prev, "v_prev")
+    if Hkp != Hqk or Hvp != Hv or k_prev.dtype != q.dtype or v_prev.dtype != q.dtype:
+        raise ValueError("previous operands must match the new ones in heads and dtype")
+    P = int(state_pool.shape[0])
+    Lmax = int(path.shape[1])
+    code = load_library().gdn_tree_commit_verify(
+        desc.ref(), _ptr(q), _ptr(k), _ptr(v), rs_qk, rs_v, _ptr(alpha), _ptr(beta),
+        _ptr(state_pool), P, _ptr(state_idx), _ptr(out), prev.ref(), _ptr(path), _ptr(path_len),
+        Lmax, _ptr(k_prev), _ptr(v_prev), rs_qkp, rs_vp, _ptr(alpha_prev), _ptr(beta_prev), Hqk,
+        Hv, dk, dv, _dtype_code(q), int(flags), _ptr(err), _stream(stream))
+    return _check(code, "gdn_tree_commit_verify", raise_on_error)

@@ -70,19 +70,48 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, h);
 }
 
+// Kernel arguments (by value).  The previous-step fields are read only by
+// the publishing variant.
+struct ConvKArgs {
+    int N, R, C, shared, P, act;
+    const int32_t* node_row;
+    const int32_t* conv_src;
+    const int32_t* status;
+    const uint16_t* x;
+    uint16_t* hist;
+    const int32_t* state_idx;
+    const uint16_t* w;
+    const float* bias;
+    uint16_t* y;
+    int32_t* err;
+    // previous step: its tree, accepted path and conv input
+    int B, Np, Rp, shared_p, Lmax;
+    const int32_t* parent_p;
+    const int32_t* node_row_p;
+    const int32_t* status_p;
+    const int32_t* path;
+    const int32_t* path_len;
+    const uint16_t* x_prev;
+};
+
 // bytes of the staged rows (N node rows + W-1 history rows), 16-aligned
 __host__ __device__ inline size_t conv_lds_x_bytes(int N, int W, int cpt) {
     return (static_cast<size_t>(N + W - 1) * kTileLanes * (cpt * 2) + 15) / 16 * 16;
 }
 
-template <int W, int CPT, int PASSES>
-__global__ void __launch_bounds__(kConvThreads)
-    conv_gather_kernel(int N, int R, int C, int shared, const int32_t* __restrict__ node_row,
-                       const int32_t* __restrict__ conv_src, const int32_t* __restrict__ status,
-                       const uint16_t* __restrict__ x, const uint16_t* __restrict__ hist, int P,
-                       const int32_t* __restrict__ state_idx, const uint16_t* __restrict__ w,
-                       const float* __restrict__ bias, int act, uint16_t* __restrict__ y,
-                       int32_t* __restrict__ err) {
+template <int W, int CPT, int PASSES, bool PUB>
+__global__ void __launch_bounds__(kConvThreads) conv_gather_kernel(const ConvKArgs a) {
+    const int N = a.N, R = a.R, C = a.C, shared = a.shared, P = a.P, act = a.act;
+    const int32_t* __restrict__ node_row = a.node_row;
+    const int32_t* __restrict__ conv_src = a.conv_src;
+    const int32_t* __restrict__ status = a.status;
+    const uint16_t* __restrict__ x = a.x;
+    uint16_t* __restrict__ hist = a.hist;
+    const int32_t* __restrict__ state_idx = a.state_idx;
+    const uint16_t* __restrict__ w = a.w;
+    const float* __restrict__ bias = a.bias;
+    uint16_t* __restrict__ y = a.y;
+    int32_t* __restrict__ err = a.err;
     constexpr int H = W - 1;
     constexpr int TILE = kTileLanes * CPT;  // channels per workgroup
     constexpr int kWW = CPT * W / 2;        // 32-bit words of one lane's weights
@@ -110,6 +139,19 @@ __global__ void __launch_bounds__(kConvThreads)
     const int my_src = (H > 0) ? src_t[min(tid, N * H - 1)] : 0;  // N * H <= 192 < 256
     const int st = status[t];
     const int slot = state_idx[b];
+    // previous step's accepted path (PUB): its length, nodes, tree status and
+    // whether another request shares the slot
+    int len = 0, pnode = 0, pprev = 0, st_p = 1, dup = 0;
+    if constexpr (PUB) {
+        st_p = a.status_p[a.shared_p ? 0 : b];
+        len = a.path_len[b];
+        pnode = a.path[static_cast<size_t>(b) * a.Lmax + min(tid, a.Lmax - 1)];
+        pprev = __shfl(pnode, tid > 0 ? tid - 1 : 0, 64);  // path[tid - 1] (wave 0)
+        const int s2 = state_idx[min(tid, a.B - 1)];
+        dup = (tid < a.B && tid != b && s2 == slot) ? 1 : 0;
+        for (int b2 = tid + kConvThreads; b2 < a.B; b2 += kConvThreads)  // B > 256 only
+            dup |= (b2 != b && state_idx[b2] == slot) ? 1 : 0;
+    }
     if (st != 0) return;
     if (slot < 0 || slot >= P) {
         if (blockIdx.x == 0 && tid == 0) atomicOr(err, GDN_EV_STATE);
@@ -150,9 +192,20 @@ __global__ void __launch_bounds__(kConvThreads)
         if (p * kRowsPerPass < N)  // uniform: whole passes beyond N are skipped
             xin[p] = load_chunk<CPT>(x + (xb + s_row[min(i, N - 1)]) * C + c0);
     }
-    // history entry m = rs (threads with rs >= H load entry H - 1 again)
-    Chunk<CPT> hc;
-    if (H > 0) hc = load_chunk<CPT>(hist + (static_cast<size_t>(slot) * H + min(rs, H - 1)) * C + c0);
+    // history entry m = rs (threads with rs >= H load entry H - 1 again); with
+    // publication also entry len + rs, which becomes entry rs when the path
+    // is shorter than the history
+    Chunk<CPT> hc, hc_shift;
+    const uint16_t* hs = hist + static_cast<size_t>(slot) * (H > 0 ? H : 1) * C;
+    if (H > 0) hc = load_chunk<CPT>(hs + static_cast<size_t>(min(rs, H - 1)) * C + c0);
+    int par = 0, prow = 0;
+    if constexpr (PUB) {
+        if (H > 0)
+            hc_shift = load_chunk<CPT>(hs + static_cast<size_t>(min(max(len, 0) + rs, H - 1)) * C + c0);
+        const size_t ti = static_cast<size_t>(a.shared_p ? 0 : b) * a.Np + min(max(pnode, 0), a.Np - 1);
+        par = a.parent_p[ti];
+        prow = a.node_row_p[ti];
+    }
     // weights w[c][0..W-1] of the lane's CPT channels, CPT*W contiguous bf16:
     // 16-byte group min(rs, ...) per thread (scalar words when not 16-byte aligned)
     constexpr int kWG = (kWW + 3) / 4;  // 16-byte groups
@@ -182,6 +235,47 @@ __global__ void __launch_bounds__(kConvThreads)
     for (int p = 0; p < kPasses; ++p) {
         const int i = rs + p * kRowsPerPass;
         if (i < N) s_x[i * kTileLanes + lane] = xin[p];
+    }
+    bool pub = false;
+    if constexpr (PUB) {
+        // validate the previous path as the commit does: length in range, a
+        // parent chain from a root-level node of the previous tree, a slot no
+        // other request shares; a malformed path publishes nothing
+        __shared__ int s_bad;
+        __shared__ int32_t s_prow[kMaxNodes];
+        // the old history must be in registers before any lane overwrites it
+        if (H > 0) {
+            const uint32_t* h0 = reinterpret_cast<const uint32_t*>(&hc.u);
+            const uint32_t* h1 = reinterpret_cast<const uint32_t*>(&hc_shift.u);
+#pragma unroll
+            for (int e = 0; e < CPT / 2; ++e) asm volatile("" ::"v"(h0[e]), "v"(h1[e]));
+        }
+        if (tid == 0) s_bad = 0;
+        __syncthreads();
+        const bool len_ok = len >= 0 && len <= a.Lmax;
+        int bad = dup ? GDN_EV_STATE : 0;
+        if (!len_ok) {
+            bad |= GDN_EV_PATH;
+        } else if (tid < len) {  // len <= Lmax <= 64: all in wave 0
+            if (pnode < 0 || pnode >= a.Np || par != (tid == 0 ? -1 : pprev)) bad |= GDN_EV_PATH;
+            s_prow[tid] = prow;
+        }
+        if (st_p == 0 && bad) atomicOr(&s_bad, bad);
+        __syncthreads();
+        bad = s_bad;
+        if (bad && blockIdx.x == 0 && tid == 0) atomicOr(err, bad);
+        pub = st_p == 0 && !bad && len > 0 && H > 0;
+        if (pub) {  // uniform
+            // new entry m = rs: old entry len + rs, or the x row of path node
+            // len + rs - H (oldest first)
+            const int pos = len + rs;
+            const int j = min(max(pos - H, 0), len - 1);
+            const Chunk<CPT> xp = load_chunk<CPT>(
+                a.x_prev + (static_cast<size_t>(b) * a.Rp + s_prow[j]) * C + c0);
+            hc = (pos < H) ? hc_shift : xp;
+            if (rs < H && active)
+                *reinterpret_cast<decltype(hc.u)*>(hist + (static_cast<size_t>(slot) * H + rs) * C + c0) = hc.u;
+        }
     }
     if (H > 0 && rs < H) s_x[(N + rs) * kTileLanes + lane] = hc;
     if (rs < kWG) {
@@ -236,21 +330,40 @@ size_t conv_lds_bytes(int N, int R, int W, int cpt) {
 
 hipError_t launch_conv(const gdn_tree_desc& d, const uint16_t* x, const uint16_t* hist, int P,
                        const int32_t* state_idx, const uint16_t* w, const float* bias,
-                       uint16_t* y, int C, int act, int32_t* err, hipStream_t s) {
+                       uint16_t* y, int C, int act, int32_t* err, hipStream_t s,
+                       const ConvPublish* pub) {
     // 16-byte accesses when every 8-channel group is 16-byte aligned
     const bool wide = (C % 8 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
                       (reinterpret_cast<uintptr_t>(y) % 16 == 0) &&
                       (hist == nullptr || reinterpret_cast<uintptr_t>(hist) % 16 == 0) &&
-                      (reinterpret_cast<uintptr_t>(w) % 16 == 0);
+                      (reinterpret_cast<uintptr_t>(w) % 16 == 0) &&
+                      (pub == nullptr || reinterpret_cast<uintptr_t>(pub->x_prev) % 16 == 0);
     const int cpt = wide ? 8 : 4;
     const int tile = kTileLanes * cpt;
     dim3 grid((C + tile - 1) / tile, d.B);
     const size_t lds = conv_lds_bytes(d.N, d.R, d.W, cpt);
     if (lds > 60 * 1024) return hipErrorNotSupported;  // plus static LDS, within the 64 KiB default
-#define GDN_CONV_LAUNCH(WW, CC, PP)                                                             \
-    hipLaunchKernelGGL((conv_gather_kernel<WW, CC, PP>), grid, dim3(kConvThreads), lds, s, d.N, \
-                       d.R, C, d.shared, d.node_row, d.conv_src, d.status, x, hist, P,          \
-                       state_idx, w, bias, act, y, err)
+    ConvKArgs a{};
+    a.N = d.N; a.R = d.R; a.C = C; a.shared = d.shared; a.P = P; a.act = act;
+    a.node_row = d.node_row; a.conv_src = d.conv_src; a.status = d.status;
+    a.x = x; a.hist = const_cast<uint16_t*>(hist); a.state_idx = state_idx; a.w = w; a.bias = bias;
+    a.y = y; a.err = err;
+    if (pub != nullptr) {
+        a.B = d.B; a.Np = pub->prev->N; a.Rp = pub->prev->R; a.shared_p = pub->prev->shared;
+        a.Lmax = pub->Lmax; a.parent_p = pub->prev->parent; a.node_row_p = pub->prev->node_row;
+        a.status_p = pub->prev->status; a.path = pub->path; a.path_len = pub->path_len;
+        a.x_prev = pub->x_prev;
+    }
+    const bool small = d.N <= (kMaxPasses / 2) * kRowsPerPass;  // fewer row registers
+#define GDN_CONV_LAUNCH(WW, CC, PP)                                                               \
+    do {                                                                                          \
+        if (pub)                                                                                  \
+            hipLaunchKernelGGL((conv_gather_kernel<WW, CC, PP, true>), grid, dim3(kConvThreads), \
+                               lds, s, a);                                                        \
+        else                                                                                      \
+            hipLaunchKernelGGL((conv_gather_kernel<WW, CC, PP, false>), grid, dim3(kConvThreads),\
+                               lds, s, a);                                                        \
+    } while (0)
 #define GDN_CONV_CASE(WW)                                                   \
     case WW:                                                                \
         if (wide) {                                                         \
@@ -261,7 +374,6 @@ hipError_t launch_conv(const gdn_tree_desc& d, const uint16_t* x, const uint16_t
             else GDN_CONV_LAUNCH(WW, 4, kMaxPasses);                        \
         }                                                                   \
         break;
-    const bool small = d.N <= (kMaxPasses / 2) * kRowsPerPass;  // fewer row registers
     switch (d.W) {
         GDN_CONV_CASE(1)
         GDN_CONV_CASE(2)

@@ -51,9 +51,19 @@ __device__ __forceinline__ uint32_t xcd_local_order(uint32_t hw_id, uint32_t n) 
 
 // ---- launchers (host) -------------------------------------------------
 hipError_t launch_desc_build(const gdn_tree_desc& d, int32_t* err, hipStream_t s);
+// Conv-history publication of the previous step's accepted path, done by the
+// conv of the next step before its taps read the history.
+struct ConvPublish {
+    const gdn_tree_desc* prev;  // previous step's tree (validated, status built)
+    const int32_t* path;
+    const int32_t* path_len;
+    int Lmax;
+    const uint16_t* x_prev;     // previous step's conv input [B][prev R][C]
+};
 hipError_t launch_conv(const gdn_tree_desc& d, const uint16_t* x, const uint16_t* hist, int P,
                        const int32_t* state_idx, const uint16_t* w, const float* bias,
-                       uint16_t* y, int C, int act, int32_t* err, hipStream_t s);
+                       uint16_t* y, int C, int act, int32_t* err, hipStream_t s,
+                       const ConvPublish* pub = nullptr);
 
 struct VerifyArgs {
     const void* q;
@@ -97,5 +107,22 @@ struct CommitArgs {
 };
 hipError_t launch_commit(const gdn_tree_desc& d, const CommitArgs& a, hipStream_t s);
 size_t commit_lds_bytes(int Lmax, int D, int dtype);
+
+// Commit of the previous step's accepted path followed by the verify of the
+// next tree, from the committed state (one launch on the matrix-core path).
+struct CommitVerifyArgs {
+    VerifyArgs verify;          // the next tree; verify.pool is the pool below
+    float* pool;                // written: the committed states
+    const gdn_tree_desc* prev;  // the previous step's tree
+    const int32_t* path;
+    const int32_t* path_len;
+    int Lmax;
+    const void* k_prev;
+    const void* v_prev;
+    int64_t rs_qk_prev, rs_v_prev;
+    const float* alpha_prev;
+    const float* beta_prev;
+};
+hipError_t launch_commit_verify(const gdn_tree_desc& d, const CommitVerifyArgs& a, hipStream_t s);
 
 }  // namespace gdn

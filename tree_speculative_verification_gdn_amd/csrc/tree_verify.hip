@@ -56,11 +56,15 @@ constexpr int kKQStride = 264;   // bf16 row of 128 + 8 bytes pad: conflict-free
 struct MfmaLds {
     int a, v, gk, gq, nrm, sk, sq, al, be, rows, dep, anc, cidx, mh, ml, cr, cq, total;
     int mstride;  // bytes per row of the bf16 M halves
+    // previous step's accepted path (fused commit): k rows (MFMA operand
+    // layout), v rows, gates, k scales, rows; placed over the Gram block when
+    // it fits (the Gram block is dead by the time the path is staged)
+    int kp, vp, alp, bep, scp, rowp;
 };
 
 __host__ __device__ inline int align_up(int x, int a) { return (x + a - 1) / a * a; }
 
-__host__ __device__ inline MfmaLds mfma_lds_layout(int N, int NPB) {
+__host__ __device__ inline MfmaLds mfma_lds_layout(int N, int NPB, int Lp = 0) {
     MfmaLds L;
     const int NP = 32 * NPB;
     const int MB = 2 * NPB;
@@ -84,9 +88,38 @@ __host__ __device__ inline MfmaLds mfma_lds_layout(int N, int NPB) {
     L.ml = off;   off += align_up(NP * L.mstride, 16);
     L.cr = off;   off += align_up(N * 4, 16);      // P_i / |k_i|
     L.cq = off;   off += align_up(N * 4, 16);      // P_i / |q_i|
+    // previous path region, Lp rows (0: none).  The path's rows are written
+    // at validation, before the Gram block is formed, so they get space of
+    // their own; the rest is staged after the M solve and may overlay the
+    // Gram block.
+    const int lp = Lp > 0 ? Lp : 0;
+    L.rowp = off; off += align_up(lp * 4, 16);
+    const int psize = align_up(lp * kKQStride, 16) + align_up(lp * kD * 2, 16) + 3 * align_up(lp * 4, 16);
+    int poff = (psize <= 2 * NP * NP * 4) ? L.gk : off;
+    if (poff == off) off += psize;
+    L.kp = poff;   poff += align_up(lp * kKQStride, 16);
+    L.vp = poff;   poff += align_up(lp * kD * 2, 16);
+    L.alp = poff;  poff += align_up(lp * 4, 16);
+    L.bep = poff;  poff += align_up(lp * 4, 16);
+    L.scp = poff;  poff += align_up(lp * 4, 16);
     L.total = off;
     return L;
 }
+
+// The previous step's accepted path for the fused commit (kernel argument).
+struct CommitPrev {
+    int B, Np, Rp, shared_p, Lmax;
+    const int32_t* parent_p;
+    const int32_t* node_row_p;
+    const int32_t* status_p;
+    const int32_t* path;
+    const int32_t* path_len;
+    const uint16_t* kp;
+    const uint16_t* vp;
+    int64_t rs_qk_p, rs_v_p;
+    const float* alpha_p;
+    const float* beta_p;
+};
 
 // MFMA operand: 8 bf16 of one 128-element LDS row for k-step s and lane half
 // hf.  Slot e of the operand holds element 16s + 4hf + e (e < 4) or
@@ -162,22 +195,23 @@ __device__ __forceinline__ bf16x8_t lds_operand_m(const char* base, int stride, 
     return __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
-template <int NPB>
+template <int NPB, bool FUSED>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NPB == 1 ? 4 : 2, 8)))
     verify_mfma_kernel(int N, int R, int shared, const int32_t* __restrict__ node_row,
                        const uint64_t* __restrict__ anc_g, const int32_t* __restrict__ depth_g,
                        const int32_t* __restrict__ status, const uint16_t* __restrict__ q,
                        const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                        int64_t rs_qk, int64_t rs_v, const float* __restrict__ alpha,
-                       const float* __restrict__ beta, const float* __restrict__ pool, int P,
+                       const float* __restrict__ beta, float* __restrict__ pool, int P,
                        const int32_t* __restrict__ state_idx, void* __restrict__ out, int Hqk,
-                       int Hv, int norm, int out_bf16, int32_t* __restrict__ err) {
+                       int Hv, int norm, int out_bf16, int32_t* __restrict__ err,
+                       const CommitPrev cp) {
     constexpr int NP = 32 * NPB;
     constexpr int MB = 2 * NPB;                              // key blocks, then query blocks
     constexpr int kKQItems = MB * 32 * 32 / kThreads;       // 8-byte K/Q chunks per thread
     constexpr int kVItems = (NP * 32 + kThreads - 1) / kThreads;
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    const MfmaLds L = mfma_lds_layout(N, NPB);
+    const MfmaLds L = mfma_lds_layout(N, NPB, FUSED ? cp.Lmax : 0);
     char* s_a = lds + L.a;
     uint16_t* s_v = reinterpret_cast<uint16_t*>(lds + L.v);
     float* s_gk = reinterpret_cast<float*>(lds + L.gk);
@@ -231,34 +265,60 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     const int my_row = node_row[tb + my_node];
     const uint64_t my_anc = anc_g[tb + my_node];
     const int my_dep = depth_g[tb + my_node];
-    if (st != 0) return;
+    //   (a1') fused: the previous step's accepted path, its tree's status and
+    //   whether another request shares the slot
+    int len = 0, pnode = 0, pprev = 0, st_p = 1, dup = 0;
+    if constexpr (FUSED) {
+        st_p = cp.status_p[cp.shared_p ? 0 : b];
+        len = cp.path_len[b];
+        pnode = cp.path[static_cast<size_t>(b) * cp.Lmax + min(tid, cp.Lmax - 1)];
+        pprev = __shfl(pnode, tid > 0 ? tid - 1 : 0, 64);  // path[tid - 1] (wave 0)
+        const int s2 = state_idx[min(tid, cp.B - 1)];
+        dup = (tid < cp.B && tid != b && s2 == slot) ? 1 : 0;
+        for (int b2 = tid + kThreads; b2 < cp.B; b2 += kThreads)  // B > 256 only
+            dup |= (b2 != b && state_idx[b2] == slot) ? 1 : 0;
+    }
     if (slot < 0 || slot >= P) {
-        if (h == 0 && tid == 0) atomicOr(err, GDN_EV_STATE);
+        if ((FUSED || st == 0) && h == 0 && tid == 0) atomicOr(err, GDN_EV_STATE);
         return;
     }
+    // the new tree is verified only if it is well formed; the fused commit of
+    // the previous path happens either way
+    const bool vok = st == 0;
+    if (!FUSED && !vok) return;
     //   (a2) K/Q/V chunks and the gates of every node (rows of a valid tree are
     //        in range, so the clamped loads are too)
     static_assert(kKQItems == 2 * kSlots && kVItems == kSlots, "item u uses node slot u mod kSlots");
     uint2 kq_val[kKQItems];
-#pragma unroll
-    for (int u = 0; u < kKQItems; ++u) {
-        const int sl = (tid + u * kThreads) >> 5;
-        const uint16_t* src = (sl < NP ? k : q) + (rowb + nrow[u % kSlots]) * rs_qk +
-                              static_cast<size_t>(g) * kD + (tid & 31) * 4;
-        kq_val[u] = *reinterpret_cast<const uint2*>(src);
-    }
     uint2 v_val[kVItems];
+    float my_al = 0.f, my_be = 0.f;
+    if (vok) {  // uniform
 #pragma unroll
-    for (int u = 0; u < kVItems; ++u)
-        v_val[u] = *reinterpret_cast<const uint2*>(v + (rowb + nrow[u]) * rs_v +
-                                                   static_cast<size_t>(h) * kD + (tid & 31) * 4);
-    const size_t my_gi = (rowb + my_row) * Hv + h;
-    const float my_al = alpha[my_gi];
-    const float my_be = beta[my_gi];
-    asm volatile("" ::: "memory");  // keep the state loads behind the K/Q/V loads
+        for (int u = 0; u < kKQItems; ++u) {
+            const int sl = (tid + u * kThreads) >> 5;
+            const uint16_t* src = (sl < NP ? k : q) + (rowb + nrow[u % kSlots]) * rs_qk +
+                                  static_cast<size_t>(g) * kD + (tid & 31) * 4;
+            kq_val[u] = *reinterpret_cast<const uint2*>(src);
+        }
+#pragma unroll
+        for (int u = 0; u < kVItems; ++u)
+            v_val[u] = *reinterpret_cast<const uint2*>(v + (rowb + nrow[u]) * rs_v +
+                                                       static_cast<size_t>(h) * kD + (tid & 31) * 4);
+        const size_t my_gi = (rowb + my_row) * Hv + h;
+        my_al = alpha[my_gi];
+        my_be = beta[my_gi];
+    }
+    //   (a2') fused: parents and rows of the previous path's nodes
+    int ppar = 0, pprow = 0;
+    if constexpr (FUSED) {
+        const size_t ti = static_cast<size_t>(cp.shared_p ? 0 : b) * cp.Np + min(max(pnode, 0), cp.Np - 1);
+        ppar = cp.parent_p[ti];
+        pprow = cp.node_row_p[ti];
+    }
+    asm volatile("" ::: "memory");  // keep the state loads behind the loads above
     //   (a3) the committed state: lane (r_own, hf) holds 64 elements of row r_own
-    const float* Sb = pool + (static_cast<size_t>(slot) * Hv + h) * (kD * kD) +
-                      static_cast<size_t>(r_own) * kD + 4 * hf;
+    float* Sb = pool + (static_cast<size_t>(slot) * Hv + h) * (kD * kD) +
+                static_cast<size_t>(r_own) * kD + 4 * hf;
     float4 sreg[16];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -266,163 +326,299 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
         sreg[2 * s + 1] = *reinterpret_cast<const float4*>(Sb + 16 * s + 8);
     }
 
-    // stage the metadata, K/Q (with squared norms) and V in LDS.  Every lane
-    // writes (lanes past N into the spare entry): a store under a per-lane
-    // condition would let the compiler sink the loads above into its branch,
-    // behind the state loads, where using them waits for the whole state.
-    {
-        const int slot_i = tid < N ? tid : N;
-        s_rows[slot_i] = my_row;
-        s_anc[slot_i] = my_anc;
-        s_dep[slot_i] = my_dep;
-        s_al[slot_i] = my_al;
-        s_be[slot_i] = my_be;
-    }
-    // M halves start as zero (entries off the ancestor pattern stay zero)
-    for (int e = tid; e < NP * mstride / 4; e += kThreads) {
-        reinterpret_cast<uint32_t*>(s_mh)[e] = 0u;
-        reinterpret_cast<uint32_t*>(s_ml)[e] = 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < kKQItems; ++u) {
-        const int it = tid + u * kThreads;
-        const int sl = it >> 5;
-        const int ch = it & 31;
-        const int node = sl < NP ? sl : sl - NP;
-        if (node >= N) kq_val[u] = make_uint2(0u, 0u);  // zero pad rows of the MFMA blocks
-        *reinterpret_cast<uint2*>(s_a + sl * kKQStride + ch * 8) = kq_val[u];
-        float ss = sumsq_bf16x4(kq_val[u]);  // a row's 32 chunks sit in 32 consecutive lanes
-#pragma unroll
-        for (int off = 16; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
-        if (ch == 0) s_nrm[sl] = ss;
-    }
-#pragma unroll
-    for (int u = 0; u < kVItems; ++u) {
-        const int it = tid + u * kThreads;
-        const int node = it >> 5;
-        if (node < N) *reinterpret_cast<uint2*>(s_v + node * kD + (it & 31) * 4) = v_val[u];
-    }
-    __syncthreads();
-
-    // (b) per node: normalisation scales and the root path list
-    if (tid < N) {
-        s_sk[tid] = norm ? 1.0f / sqrtf(s_nrm[tid] + 1e-6f) : 1.0f;
-        s_sq[tid] = norm ? 1.0f / sqrtf(s_nrm[NP + tid] + 1e-6f) : 1.0f;
-        uint64_t m = s_anc[tid];
-        int p = 0;
-        while (m) {  // ancestors in index order are root first
-            const int j = __builtin_ctzll(m);
-            m &= m - 1ull;
-            s_cidx[tid * N + p++] = static_cast<uint8_t>(j);
+    // fused: validate the previous path as the commit does (length in range,
+    // a parent chain from a root-level node of the previous tree, a slot no
+    // other request shares), then load its k/v rows and gates
+    bool cok = false;
+    uint2 pk_val = make_uint2(0u, 0u), pv_val = make_uint2(0u, 0u);
+    float p_al = 0.f, p_be = 0.f;
+    float* s_alp = reinterpret_cast<float*>(lds + L.alp);
+    float* s_bep = reinterpret_cast<float*>(lds + L.bep);
+    float* s_scp = reinterpret_cast<float*>(lds + L.scp);
+    int32_t* s_rowp = reinterpret_cast<int32_t*>(lds + L.rowp);
+    char* s_kp = lds + L.kp;
+    uint16_t* s_vp = reinterpret_cast<uint16_t*>(lds + L.vp);
+    if constexpr (FUSED) {
+        __shared__ int s_bad;
+        if (tid == 0) s_bad = 0;
+        __syncthreads();
+        const bool len_ok = len >= 0 && len <= cp.Lmax;
+        int bad = dup ? GDN_EV_STATE : 0;
+        if (!len_ok) {
+            bad |= GDN_EV_PATH;
+        } else if (tid < len) {  // len <= Lmax <= 64: all in wave 0
+            if (pnode < 0 || pnode >= cp.Np || ppar != (tid == 0 ? -1 : pprev)) bad |= GDN_EV_PATH;
+            s_rowp[tid] = pprow;
         }
-        s_cidx[tid * N + p] = static_cast<uint8_t>(tid);
-    }
-
-    // (c) Gram block on the matrix cores (exact bf16 products, fp32 sums),
-    //     stored dense: k_i . k_j and q_i . k_j for every pair of slots
-    {
-        constexpr int kTiles = MB * NPB;  // all query/key row blocks x key column blocks
-        for (int tile = wave; tile < kTiles; tile += kThreads / 64) {
-            const int ta = tile / NPB;
-            const int tcol = tile % NPB;
-            f32x16_t acc = {};
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const bf16x8_t a = lds_operand(s_a, ta * 32 + l32, s, hf);
-                const bf16x8_t bb = lds_operand(s_a, tcol * 32 + l32, s, hf);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc, 0, 0, 0);
-            }
-            float* gdst = (ta < NPB) ? s_gk + ta * 32 * NP : s_gq + (ta - NPB) * 32 * NP;
-            const int col = tcol * 32 + l32;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) gdst[(8 * (e >> 2) + 4 * hf + (e & 3)) * NP + col] = acc[e];
+        if (st_p == 0 && bad) atomicOr(&s_bad, bad);
+        __syncthreads();
+        bad = s_bad;
+        if (bad && h == 0 && tid == 0) atomicOr(err, bad);
+        cok = st_p == 0 && !bad && len > 0;
+        if (cok) {  // uniform: the first 8 path rows' k/v chunks and every gate
+            const int gp = static_cast<int>((static_cast<int64_t>(h) * Hqk) / Hv);
+            const size_t rowbp = static_cast<size_t>(b) * cp.Rp;
+            const int jj = min(tid >> 5, len - 1);
+            const size_t rbp = rowbp + s_rowp[jj];
+            pk_val = *reinterpret_cast<const uint2*>(cp.kp + rbp * cp.rs_qk_p + static_cast<size_t>(gp) * kD +
+                                                     (tid & 31) * 4);
+            pv_val = *reinterpret_cast<const uint2*>(cp.vp + rbp * cp.rs_v_p + static_cast<size_t>(h) * kD +
+                                                     (tid & 31) * 4);
+            const size_t gi = (rowbp + s_rowp[min(tid, len - 1)]) * Hv + h;
+            p_al = cp.alpha_p[gi];
+            p_be = cp.beta_p[gi];
         }
     }
-    __syncthreads();
 
-    // (e) M = C (I + G)^-1, row by row: along node i's root path n_0 .. n_(d-1) = i,
-    //       M_(i,n_p) = C_(i,n_p) - sum_(s > p) M_(i,n_s) G_(n_s,n_p)
-    //     with C_(i,j) = (P_i/P_j) q^_i.k^_j and G_(m,j) = b_m (P_m/P_j) k^_m.k^_j, the
-    //     decay ratios taken as products of the decays strictly below j.  A group
-    //     of kLP lanes holds one node, lane p its path position p: each lane forms
-    //     its G column, then the deepest position is final and is eliminated from
-    //     the shallower ones, one position per step.  Nodes deeper than kLP are
-    //     solved one thread per node afterwards.
-    {
-        constexpr int kLP = 8;
-        const int p = tid & (kLP - 1);
-        const int grp_lane0 = lane & ~(kLP - 1);
-        for (int i0 = 0; i0 < N; i0 += kThreads / kLP) {
-            const int i = i0 + tid / kLP;
-            const int ii = min(i, N - 1);
-            const int d = s_dep[ii];
-            const bool act = i < N && d <= kLP && p < d;
-            const uint8_t* path = s_cidx + ii * N;
-            const int j = path[min(p, d - 1)];
-            const float sk_j = s_sk[j];
-            float gco[kLP];
-            float r = 1.0f;  // decays of positions p+1 .. s
-#pragma unroll
-            for (int sp = 1; sp < kLP; ++sp) {
-                const bool in = sp > p && sp < d;
-                const int m = path[min(sp, d - 1)];
-                r *= in ? s_al[m] : 1.0f;
-                gco[sp] = in ? s_be[m] * s_sk[m] * sk_j * s_gk[m * NP + j] * r : 0.0f;
+    if (vok) {  // uniform: stages (a)-(e) of the new tree
+        // stage the metadata, K/Q (with squared norms) and V in LDS.  Every lane
+        // writes (lanes past N into the spare entry): a store under a per-lane
+        // condition would let the compiler sink the loads above into its branch,
+        // behind the state loads, where using them waits for the whole state.
+        {
+            const int slot_i = tid < N ? tid : N;
+            s_rows[slot_i] = my_row;
+            s_anc[slot_i] = my_anc;
+            s_dep[slot_i] = my_dep;
+            s_al[slot_i] = my_al;
+            s_be[slot_i] = my_be;
+        }
+        // M halves start as zero (entries off the ancestor pattern stay zero)
+        for (int e = tid; e < NP * mstride / 4; e += kThreads) {
+            reinterpret_cast<uint32_t*>(s_mh)[e] = 0u;
+            reinterpret_cast<uint32_t*>(s_ml)[e] = 0u;
+        }
+    #pragma unroll
+        for (int u = 0; u < kKQItems; ++u) {
+            const int it = tid + u * kThreads;
+            const int sl = it >> 5;
+            const int ch = it & 31;
+            const int node = sl < NP ? sl : sl - NP;
+            if (node >= N) kq_val[u] = make_uint2(0u, 0u);  // zero pad rows of the MFMA blocks
+            *reinterpret_cast<uint2*>(s_a + sl * kKQStride + ch * 8) = kq_val[u];
+            float ss = sumsq_bf16x4(kq_val[u]);  // a row's 32 chunks sit in 32 consecutive lanes
+    #pragma unroll
+            for (int off = 16; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+            if (ch == 0) s_nrm[sl] = ss;
+        }
+    #pragma unroll
+        for (int u = 0; u < kVItems; ++u) {
+            const int it = tid + u * kThreads;
+            const int node = it >> 5;
+            if (node < N) *reinterpret_cast<uint2*>(s_v + node * kD + (it & 31) * 4) = v_val[u];
+        }
+        __syncthreads();
+
+        // (b) per node: normalisation scales and the root path list
+        if (tid < N) {
+            s_sk[tid] = norm ? 1.0f / sqrtf(s_nrm[tid] + 1e-6f) : 1.0f;
+            s_sq[tid] = norm ? 1.0f / sqrtf(s_nrm[NP + tid] + 1e-6f) : 1.0f;
+            uint64_t m = s_anc[tid];
+            int p = 0;
+            while (m) {  // ancestors in index order are root first
+                const int j = __builtin_ctzll(m);
+                m &= m - 1ull;
+                s_cidx[tid * N + p++] = static_cast<uint8_t>(j);
             }
-            // r = P_i / P_j now
-            float val = r * s_sq[ii] * sk_j * s_gq[ii * NP + j];
-#pragma unroll
-            for (int sp = kLP - 1; sp >= 1; --sp) {
-                const float ms = __shfl(val, grp_lane0 | sp, 64);  // final M at position sp
-                val = (sp < d && p < sp) ? fmaf(-ms, gco[sp], val) : val;
+            s_cidx[tid * N + p] = static_cast<uint8_t>(tid);
+        }
+
+        // (c) Gram block on the matrix cores (exact bf16 products, fp32 sums),
+        //     stored dense: k_i . k_j and q_i . k_j for every pair of slots
+        {
+            constexpr int kTiles = MB * NPB;  // all query/key row blocks x key column blocks
+            for (int tile = wave; tile < kTiles; tile += kThreads / 64) {
+                const int ta = tile / NPB;
+                const int tcol = tile % NPB;
+                f32x16_t acc = {};
+    #pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const bf16x8_t a = lds_operand(s_a, ta * 32 + l32, s, hf);
+                    const bf16x8_t bb = lds_operand(s_a, tcol * 32 + l32, s, hf);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc, 0, 0, 0);
+                }
+                float* gdst = (ta < NPB) ? s_gk + ta * 32 * NP : s_gq + (ta - NPB) * 32 * NP;
+                const int col = tcol * 32 + l32;
+    #pragma unroll
+                for (int e = 0; e < 16; ++e) gdst[(8 * (e >> 2) + 4 * hf + (e & 3)) * NP + col] = acc[e];
             }
-            if (act) {
-                const uint32_t hv = cvt_pk_bf16(val, 0.0f) & 0xffffu;
-                const float rest = val - __uint_as_float(hv << 16);
-                const uint32_t lv = cvt_pk_bf16(rest, 0.0f) & 0xffffu;
-                reinterpret_cast<uint16_t*>(s_mh + i * mstride)[j] = static_cast<uint16_t>(hv);
-                reinterpret_cast<uint16_t*>(s_ml + i * mstride)[j] = static_cast<uint16_t>(lv);
-                if (p == 0) {
-                    const float P_i = r * s_al[j];  // j = n_0: times the root-level decay
-                    s_cr[i] = P_i * s_sk[i];
-                    s_cq[i] = P_i * s_sq[i];
+        }
+        __syncthreads();
+
+        // (e) M = C (I + G)^-1, row by row: along node i's root path n_0 .. n_(d-1) = i,
+        //       M_(i,n_p) = C_(i,n_p) - sum_(s > p) M_(i,n_s) G_(n_s,n_p)
+        //     with C_(i,j) = (P_i/P_j) q^_i.k^_j and G_(m,j) = b_m (P_m/P_j) k^_m.k^_j, the
+        //     decay ratios taken as products of the decays strictly below j.  A group
+        //     of kLP lanes holds one node, lane p its path position p: each lane forms
+        //     its G column, then the deepest position is final and is eliminated from
+        //     the shallower ones, one position per step.  Nodes deeper than kLP are
+        //     solved one thread per node afterwards.
+        {
+            constexpr int kLP = 8;
+            const int p = tid & (kLP - 1);
+            const int grp_lane0 = lane & ~(kLP - 1);
+            for (int i0 = 0; i0 < N; i0 += kThreads / kLP) {
+                const int i = i0 + tid / kLP;
+                const int ii = min(i, N - 1);
+                const int d = s_dep[ii];
+                const bool act = i < N && d <= kLP && p < d;
+                const uint8_t* path = s_cidx + ii * N;
+                const int j = path[min(p, d - 1)];
+                const float sk_j = s_sk[j];
+                float gco[kLP];
+                float r = 1.0f;  // decays of positions p+1 .. s
+    #pragma unroll
+                for (int sp = 1; sp < kLP; ++sp) {
+                    const bool in = sp > p && sp < d;
+                    const int m = path[min(sp, d - 1)];
+                    r *= in ? s_al[m] : 1.0f;
+                    gco[sp] = in ? s_be[m] * s_sk[m] * sk_j * s_gk[m * NP + j] * r : 0.0f;
+                }
+                // r = P_i / P_j now
+                float val = r * s_sq[ii] * sk_j * s_gq[ii * NP + j];
+    #pragma unroll
+                for (int sp = kLP - 1; sp >= 1; --sp) {
+                    const float ms = __shfl(val, grp_lane0 | sp, 64);  // final M at position sp
+                    val = (sp < d && p < sp) ? fmaf(-ms, gco[sp], val) : val;
+                }
+                if (act) {
+                    const uint32_t hv = cvt_pk_bf16(val, 0.0f) & 0xffffu;
+                    const float rest = val - __uint_as_float(hv << 16);
+                    const uint32_t lv = cvt_pk_bf16(rest, 0.0f) & 0xffffu;
+                    reinterpret_cast<uint16_t*>(s_mh + i * mstride)[j] = static_cast<uint16_t>(hv);
+                    reinterpret_cast<uint16_t*>(s_ml + i * mstride)[j] = static_cast<uint16_t>(lv);
+                    if (p == 0) {
+                        const float P_i = r * s_al[j];  // j = n_0: times the root-level decay
+                        s_cr[i] = P_i * s_sk[i];
+                        s_cq[i] = P_i * s_sq[i];
+                    }
                 }
             }
-        }
-        // nodes deeper than kLP: one thread per node, the same elimination in
-        // place (M values so far read back from their hi + lo halves)
-        if (tid < N && s_dep[tid] > kLP) {
-            const int i = tid;
-            const int d = s_dep[i];
-            const uint8_t* path = s_cidx + i * N;
-            const float sq_i = s_sq[i];
-            uint16_t* mh = reinterpret_cast<uint16_t*>(s_mh + i * mstride);
-            uint16_t* ml = reinterpret_cast<uint16_t*>(s_ml + i * mstride);
-            float wq = 1.0f;  // decays of the positions below p
-            for (int pp = d - 1; pp >= 0; --pp) {
-                const int jj = path[pp];
-                const float sk_j = s_sk[jj];
-                float val = wq * sq_i * sk_j * s_gq[i * NP + jj];
-                float wg = 1.0f;
-                for (int sp = pp + 1; sp < d; ++sp) {
-                    const int m = path[sp];
-                    wg *= s_al[m];
-                    const float gmj = s_be[m] * wg * s_sk[m] * sk_j * s_gk[m * NP + jj];
-                    const float msv = bf16_bits_to_f32(mh[m]) + bf16_bits_to_f32(ml[m]);
-                    val = fmaf(-msv, gmj, val);
+            // nodes deeper than kLP: one thread per node, the same elimination in
+            // place (M values so far read back from their hi + lo halves)
+            if (tid < N && s_dep[tid] > kLP) {
+                const int i = tid;
+                const int d = s_dep[i];
+                const uint8_t* path = s_cidx + i * N;
+                const float sq_i = s_sq[i];
+                uint16_t* mh = reinterpret_cast<uint16_t*>(s_mh + i * mstride);
+                uint16_t* ml = reinterpret_cast<uint16_t*>(s_ml + i * mstride);
+                float wq = 1.0f;  // decays of the positions below p
+                for (int pp = d - 1; pp >= 0; --pp) {
+                    const int jj = path[pp];
+                    const float sk_j = s_sk[jj];
+                    float val = wq * sq_i * sk_j * s_gq[i * NP + jj];
+                    float wg = 1.0f;
+                    for (int sp = pp + 1; sp < d; ++sp) {
+                        const int m = path[sp];
+                        wg *= s_al[m];
+                        const float gmj = s_be[m] * wg * s_sk[m] * sk_j * s_gk[m * NP + jj];
+                        const float msv = bf16_bits_to_f32(mh[m]) + bf16_bits_to_f32(ml[m]);
+                        val = fmaf(-msv, gmj, val);
+                    }
+                    const uint32_t hv = cvt_pk_bf16(val, 0.0f) & 0xffffu;
+                    const float rest = val - __uint_as_float(hv << 16);
+                    const uint32_t lv = cvt_pk_bf16(rest, 0.0f) & 0xffffu;
+                    mh[jj] = static_cast<uint16_t>(hv);
+                    ml[jj] = static_cast<uint16_t>(lv);
+                    wq *= s_al[jj];
                 }
-                const uint32_t hv = cvt_pk_bf16(val, 0.0f) & 0xffffu;
-                const float rest = val - __uint_as_float(hv << 16);
-                const uint32_t lv = cvt_pk_bf16(rest, 0.0f) & 0xffffu;
-                mh[jj] = static_cast<uint16_t>(hv);
-                ml[jj] = static_cast<uint16_t>(lv);
-                wq *= s_al[jj];
+                s_cr[i] = wq * s_sk[i];
+                s_cq[i] = wq * sq_i;
             }
-            s_cr[i] = wq * s_sk[i];
-            s_cq[i] = wq * sq_i;
         }
+        __syncthreads();
     }
-    __syncthreads();
+
+    // fused: replay the previous path into the state in registers, in this
+    // kernel's layout (lane (r_own, hf) holds columns 16s + 4hf + e and
+    // 16s + 8 + 4hf + e of row r_own; its partner hf ^ 1 is lane ^ 32), and
+    // publish the state (LumoTree, Sec. IV-B):
+    //   u = b_j (v_j - a_j S k^_j),  S <- a_j S + u k^_j^T,  k^_j = sc_j k_j
+    if constexpr (FUSED) {
+        if (cok) {  // uniform
+            // the staged path overlays the Gram block, dead after the M solve
+            const int jj = tid >> 5;
+            const int chp = tid & 31;
+            const int cpl = len * 32;  // 8-byte chunks of the path's k (and of v)
+            float ss = sumsq_bf16x4(pk_val);
+#pragma unroll
+            for (int off = 16; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+            if (tid < cpl) {
+                *reinterpret_cast<uint2*>(s_kp + jj * kKQStride + chp * 8) = pk_val;
+                *reinterpret_cast<uint2*>(s_vp + jj * kD + chp * 4) = pv_val;
+                if (chp == 0) s_scp[jj] = norm ? 1.0f / sqrtf(ss + 1e-6f) : 1.0f;
+            }
+            for (int it0 = kThreads; it0 < cpl; it0 += kThreads) {  // paths longer than 8 rows
+                const int it = it0 + tid;
+                const int j2 = min(it >> 5, len - 1);
+                const size_t rbp = static_cast<size_t>(b) * cp.Rp + s_rowp[j2];
+                const int gp = static_cast<int>((static_cast<int64_t>(h) * Hqk) / Hv);
+                const uint2 kc = *reinterpret_cast<const uint2*>(
+                    cp.kp + rbp * cp.rs_qk_p + static_cast<size_t>(gp) * kD + chp * 4);
+                const uint2 vc = *reinterpret_cast<const uint2*>(
+                    cp.vp + rbp * cp.rs_v_p + static_cast<size_t>(h) * kD + chp * 4);
+                float s2 = sumsq_bf16x4(kc);
+#pragma unroll
+                for (int off = 16; off > 0; off >>= 1) s2 += __shfl_xor(s2, off, 64);
+                if (it < cpl) {
+                    *reinterpret_cast<uint2*>(s_kp + (it >> 5) * kKQStride + chp * 8) = kc;
+                    *reinterpret_cast<uint2*>(s_vp + (it >> 5) * kD + chp * 4) = vc;
+                    if (chp == 0) s_scp[it >> 5] = norm ? 1.0f / sqrtf(s2 + 1e-6f) : 1.0f;
+                }
+            }
+            if (tid < len) {
+                s_alp[tid] = p_al;
+                s_bep[tid] = p_be;
+            }
+            __syncthreads();
+            for (int j = 0; j < len; ++j) {
+                float y = 0.f;
+#pragma unroll
+                for (int s8 = 0; s8 < 8; ++s8) {
+                    const bf16x8_t kk = lds_operand(s_kp, j, s8, hf);
+                    const uint4 kw = __builtin_bit_cast(uint4, kk);
+                    const float4 a0 = sreg[2 * s8], a1 = sreg[2 * s8 + 1];
+                    y = fmaf(a0.x, __uint_as_float(kw.x << 16), y);
+                    y = fmaf(a0.y, __uint_as_float(kw.x & 0xffff0000u), y);
+                    y = fmaf(a0.z, __uint_as_float(kw.y << 16), y);
+                    y = fmaf(a0.w, __uint_as_float(kw.y & 0xffff0000u), y);
+                    y = fmaf(a1.x, __uint_as_float(kw.z << 16), y);
+                    y = fmaf(a1.y, __uint_as_float(kw.z & 0xffff0000u), y);
+                    y = fmaf(a1.z, __uint_as_float(kw.w << 16), y);
+                    y = fmaf(a1.w, __uint_as_float(kw.w & 0xffff0000u), y);
+                }
+                y += __shfl_xor(y, 32, 64);
+                const float a = s_alp[j];
+                const float sc = s_scp[j];
+                const float us = s_bep[j] * (bf16_bits_to_f32(s_vp[j * kD + r_own]) - a * (y * sc)) * sc;
+                // read k_j again rather than keep the unpacked copy live across
+                // the reduction
+                asm volatile("" ::: "memory");
+#pragma unroll
+                for (int s8 = 0; s8 < 8; ++s8) {
+                    const bf16x8_t kk = lds_operand(s_kp, j, s8, hf);
+                    const uint4 kw = __builtin_bit_cast(uint4, kk);
+                    float4& a0 = sreg[2 * s8];
+                    float4& a1 = sreg[2 * s8 + 1];
+                    a0.x = fmaf(a, a0.x, us * __uint_as_float(kw.x << 16));
+                    a0.y = fmaf(a, a0.y, us * __uint_as_float(kw.x & 0xffff0000u));
+                    a0.z = fmaf(a, a0.z, us * __uint_as_float(kw.y << 16));
+                    a0.w = fmaf(a, a0.w, us * __uint_as_float(kw.y & 0xffff0000u));
+                    a1.x = fmaf(a, a1.x, us * __uint_as_float(kw.z << 16));
+                    a1.y = fmaf(a, a1.y, us * __uint_as_float(kw.z & 0xffff0000u));
+                    a1.z = fmaf(a, a1.z, us * __uint_as_float(kw.w << 16));
+                    a1.w = fmaf(a, a1.w, us * __uint_as_float(kw.w & 0xffff0000u));
+                }
+            }
+#pragma unroll
+            for (int s8 = 0; s8 < 8; ++s8) {
+                *reinterpret_cast<float4*>(Sb + 16 * s8) = sreg[2 * s8];
+                *reinterpret_cast<float4*>(Sb + 16 * s8 + 8) = sreg[2 * s8 + 1];
+            }
+        }
+        if (!vok) return;
+    }
 
     // (d) CT = [K;Q] S_pre^T on the matrix cores, state split into bf16 hi + lo
     //     (the first use of the state: the only wait for it)
@@ -694,18 +890,18 @@ hipError_t set_lds(K kernel, size_t bytes) {
                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
 }
 
-template <int NPB>
-hipError_t launch_mfma_t(const gdn_tree_desc& d, const VerifyArgs& a, int norm, int obf,
-                         size_t lds, hipStream_t s) {
-    auto kfn = verify_mfma_kernel<NPB>;
+template <int NPB, bool FUSED>
+hipError_t launch_mfma_t(const gdn_tree_desc& d, const VerifyArgs& a, float* pool, int norm,
+                         int obf, size_t lds, const CommitPrev& cp, hipStream_t s) {
+    auto kfn = verify_mfma_kernel<NPB, FUSED>;
     hipError_t e = set_lds(kfn, lds);
     if (e != hipSuccess) return e;
     const dim3 grid(static_cast<unsigned>(d.B) * static_cast<unsigned>(a.Hv));
     hipLaunchKernelGGL(kfn, grid, dim3(kThreads), lds, s, d.N, d.R, d.shared, d.node_row, d.anc,
                        d.depth, d.status, static_cast<const uint16_t*>(a.q),
                        static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
-                       a.rs_qk, a.rs_v, a.alpha, a.beta, a.pool, a.P, a.state_idx, a.out, a.Hqk,
-                       a.Hv, norm, obf, a.err);
+                       a.rs_qk, a.rs_v, a.alpha, a.beta, pool, a.P, a.state_idx, a.out, a.Hqk,
+                       a.Hv, norm, obf, a.err, cp);
     return hipGetLastError();
 }
 
@@ -739,9 +935,12 @@ hipError_t launch_verify(const gdn_tree_desc& d, const VerifyArgs& a, hipStream_
         const int NPB = (d.N + 31) / 32;
         const size_t lds = static_cast<size_t>(mfma_lds_layout(d.N, NPB).total);
         if (lds > kMaxLds) return hipErrorNotSupported;
+        const CommitPrev none{};
+        // the non-fused kernel only reads the state
+        float* pool = const_cast<float*>(a.pool);
         switch (NPB) {
-            case 1: return launch_mfma_t<1>(d, a, norm, obf, lds, s);
-            case 2: return launch_mfma_t<2>(d, a, norm, obf, lds, s);
+            case 1: return launch_mfma_t<1, false>(d, a, pool, norm, obf, lds, none, s);
+            case 2: return launch_mfma_t<2, false>(d, a, pool, norm, obf, lds, none, s);
             default: return hipErrorNotSupported;
         }
     }
@@ -761,6 +960,51 @@ hipError_t launch_verify(const gdn_tree_desc& d, const VerifyArgs& a, hipStream_
         default:
             return hipErrorNotSupported;
     }
+}
+
+hipError_t launch_commit_verify(const gdn_tree_desc& d, const CommitVerifyArgs& a, hipStream_t s) {
+    const VerifyArgs& va = a.verify;
+    const gdn_tree_desc& dp = *a.prev;
+    const bool prev_aligned = (a.rs_qk_prev % 4 == 0) && (a.rs_v_prev % 4 == 0) &&
+                              (reinterpret_cast<uintptr_t>(a.k_prev) % 8 == 0) &&
+                              (reinterpret_cast<uintptr_t>(a.v_prev) % 8 == 0);
+    if (verify_uses_mfma(d, va) && prev_aligned) {
+        const int NPB = (d.N + 31) / 32;
+        const size_t lds = static_cast<size_t>(mfma_lds_layout(d.N, NPB, a.Lmax).total);
+        if (lds <= kMaxLds) {
+            CommitPrev cp{};
+            cp.B = d.B;
+            cp.Np = dp.N;
+            cp.Rp = dp.R;
+            cp.shared_p = dp.shared;
+            cp.Lmax = a.Lmax;
+            cp.parent_p = dp.parent;
+            cp.node_row_p = dp.node_row;
+            cp.status_p = dp.status;
+            cp.path = a.path;
+            cp.path_len = a.path_len;
+            cp.kp = static_cast<const uint16_t*>(a.k_prev);
+            cp.vp = static_cast<const uint16_t*>(a.v_prev);
+            cp.rs_qk_p = a.rs_qk_prev;
+            cp.rs_v_p = a.rs_v_prev;
+            cp.alpha_p = a.alpha_prev;
+            cp.beta_p = a.beta_prev;
+            const int norm = (va.flags & GDN_F_NORM_QK) ? 1 : 0;
+            const int obf = (va.flags & GDN_F_OUT_BF16) ? 1 : 0;
+            switch (NPB) {
+                case 1: return launch_mfma_t<1, true>(d, va, a.pool, norm, obf, lds, cp, s);
+                case 2: return launch_mfma_t<2, true>(d, va, a.pool, norm, obf, lds, cp, s);
+                default: break;
+            }
+        }
+    }
+    // other shapes: the commit, then the verify (the same result in two launches)
+    CommitArgs ca{a.path, a.path_len, a.Lmax, a.k_prev, a.v_prev, a.rs_qk_prev, a.rs_v_prev,
+                  a.alpha_prev, a.beta_prev, a.pool, va.P, va.state_idx, nullptr, nullptr, 0,
+                  va.Hqk, va.Hv, va.D, va.dtype, va.flags & GDN_F_NORM_QK, va.err};
+    hipError_t e = launch_commit(dp, ca, s);
+    if (e != hipSuccess) return e;
+    return launch_verify(d, va, s);
 }
 
 }  // namespace gdn
