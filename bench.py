@@ -1,21 +1,38 @@
 #!/usr/bin/env python3
 """Benchmark of one GDN tree-speculation layer on one MI355X.
 
-A step is one pass of the whole hot path over one batch of synthetic input:
-    gdn_tree_desc_build -> conv_ancestry_gather -> gdn_tree_verify -> gdn_tree_commit
-on the 27-node-tree workload (B = 128 requests, 32 value heads over 16 qk heads,
+A step is one pass of the whole hot path over one batch of synthetic input on
+the 27-node-tree workload (B = 128 requests, 32 value heads over 16 qk heads,
 d_k = d_v = 128, causal conv kernel 4 over 8192 channels, bf16 operands, fp32
-state).  Inputs are resident in HBM before the timed region; two independent
-layers' inputs (about 0.9 GB each) alternate step by step so that no step
-reads data the previous step left in the 256 MB last-level cache.
+state): the descriptor build, the ancestry-gathered conv, the tree verify, the
+commit of an accepted path into the state and the conv-history publication.
 
-Prints ONE JSON line (rank 0): metric, value = tree nodes verified per second,
-per-kernel roofline of the dominant kernel (HIP events on the launch stream),
-and the fp64 CPU oracle timed on the host on a bounded sample.
+Two step shapes (``--mode``):
+  fused     (default) the steady-state decode step:
+              gdn_tree_desc_build -> conv_ancestry_gather_publish ->
+              gdn_tree_commit_verify
+            the commit and history publication of the previous step's
+            accepted path run inside this step's conv and verify, so the
+            state is read once and written once per step.
+  separate  gdn_tree_desc_build -> conv_ancestry_gather -> gdn_tree_verify
+            -> gdn_tree_commit (this step's own path), the state read twice.
+Both commit one path and verify one tree per step.
+
+Inputs are resident in HBM before the timed region.  Two independent layer
+instances (pool, history, weights, about 0.5 GB each with their step data)
+alternate step by step, so no step reads data the previous step left in the
+256 MB last-level cache; in fused mode each instance alternates between two
+step slots, the previous step's slot supplying the path and its recorded
+operands.
+
+Prints ONE JSON line: metric, value = tree nodes verified per second, the
+roofline of the dominant kernel (HIP events on the launch stream) and the
+fp64 CPU oracle timed on the host on a bounded sample.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -30,44 +47,85 @@ METRIC = "tree nodes verified/sec (GDN layer, 1 GPU) + achieved HBM GB/s vs peak
 PEAK_HBM_GBS = 8000.0
 # file stem of the committed profile summaries for each workload
 WORKLOAD_TAG = {"tree27_b128_h32_conv4": "tree27_b128_conv4"}
+KERNEL_PREFIX = {"conv": "gdn::conv_gather_kernel", "verify": "gdn::verify_",
+                 "commit": "gdn::commit_kernel", "desc": "gdn::desc_build_kernel",
+                 "commit_verify": "gdn::verify_"}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(cfg, case):
-    """Bytes each kernel must move through its interface, read once / written
-    once ("Byte model")."""
-    B, N, D, Hv, Hqk = case["B"], cfg.N, cfg.D, cfg.Hv, cfg.Hqk
-    L = case["path_len"].astype(np.int64)
-    W = max(cfg.conv_W, 1)
-    C = cfg.conv_C
-    out = {}
-    out["desc"] = B * N * (4 + 4) + B * N * (4 + 8 + 4 * (W - 1)) + B * 4
-    if cfg.conv_W > 0:
-        out["conv"] = B * N * C * 2 + B * (W - 1) * C * 2 + C * W * 2 + B * N * C * 2
-    else:
-        out["conv"] = 0
-    out["verify"] = (B * Hv * D * D * 4 + B * N * (2 * Hqk * D + Hv * D) * 2 + B * N * Hv * 8
-                     + B * N * Hv * D * 4)
+# --------------------------------------------------------------------------
+# byte model: what each kernel must move through its interface, read once
+# and written once (re-reads, padding rows and cache effects never credited)
+# --------------------------------------------------------------------------
+
+def _common(cfg, case):
+    return case["B"], cfg.N, cfg.D, cfg.Hv, cfg.Hqk, max(cfg.conv_W, 1), cfg.conv_C
+
+
+def bytes_desc(cfg, case):
+    B, N, D, Hv, Hqk, W, C = _common(cfg, case)
+    return B * N * (4 + 4) + B * N * (4 + 8 + 4 * (W - 1)) + B * 4
+
+
+def bytes_conv(cfg, case):
+    B, N, D, Hv, Hqk, W, C = _common(cfg, case)
+    if cfg.conv_W == 0:
+        return 0
+    return B * N * C * 2 + B * (W - 1) * C * 2 + C * W * 2 + B * N * C * 2
+
+
+def bytes_publish(cfg, prev):
+    """History publication of prev's accepted paths: new entries written, the
+    x rows they come from (the old entries are read by the conv anyway)."""
+    B, N, D, Hv, Hqk, W, C = _common(cfg, prev)
+    L = prev["path_len"].astype(np.int64)
+    if cfg.conv_W <= 1:
+        return 0
     active = int((L > 0).sum())
-    hist_bytes = 0
-    if cfg.conv_W > 1:
-        hist_bytes = active * 2 * (W - 1) * C * 2 + int(np.minimum(L, W - 1).sum()) * C * 2
-    out["commit"] = (active * Hv * D * D * 4 * 2 + int(L.sum()) * (Hqk * D + Hv * D) * 2
-                     + int(L.sum()) * Hv * 8 + hist_bytes)
+    return active * (W - 1) * C * 2 + int(np.minimum(L, W - 1).sum()) * C * 2
+
+
+def bytes_verify(cfg, case):
+    B, N, D, Hv, Hqk, W, C = _common(cfg, case)
+    return (B * Hv * D * D * 4 + B * N * (2 * Hqk * D + Hv * D) * 2 + B * N * Hv * 8
+            + B * N * Hv * D * 4)
+
+
+def bytes_commit_state(cfg, case):
+    """State write (and, for the separate commit, the read) of the committed
+    requests plus the path's recorded k/v rows and gates."""
+    B, N, D, Hv, Hqk, W, C = _common(cfg, case)
+    L = case["path_len"].astype(np.int64)
+    active = int((L > 0).sum())
+    return active * Hv * D * D * 4, int(L.sum()) * ((Hqk * D + Hv * D) * 2 + Hv * 8)
+
+
+def byte_model(cfg, cur, prev, mode):
+    out = {"desc": bytes_desc(cfg, cur)}
+    if mode == "fused":
+        state_w, path_rows = bytes_commit_state(cfg, prev)
+        out["conv"] = bytes_conv(cfg, cur) + bytes_publish(cfg, prev)
+        out["commit_verify"] = bytes_verify(cfg, cur) + state_w + path_rows
+    else:
+        state_w, path_rows = bytes_commit_state(cfg, cur)
+        out["conv"] = bytes_conv(cfg, cur)
+        out["verify"] = bytes_verify(cfg, cur)
+        B, N, D, Hv, Hqk, W, C = _common(cfg, cur)
+        hist_read = int((cur["path_len"] > 0).sum()) * (W - 1) * C * 2 if cfg.conv_W > 1 else 0
+        out["commit"] = 2 * state_w + path_rows + bytes_publish(cfg, cur) + hist_read
     return out
 
 
-KERNEL_PREFIX = {"conv": "gdn::conv_gather_kernel", "verify": "gdn::verify_",
-                 "commit": "gdn::commit_kernel", "desc": "gdn::desc_build_kernel"}
-
+# --------------------------------------------------------------------------
+# measured traffic from the committed counter summaries
+# --------------------------------------------------------------------------
 
 def library_source_hash():
     """sha256[:16] over the library's kernel sources and the ABI header, in
     the order the profile summaries under profiles/ record it."""
-    import hashlib
     h = hashlib.sha256()
     d = os.path.join(ROOT, "tree_speculative_verification_gdn_amd", "csrc")
     for f in sorted(os.listdir(d)):
@@ -80,11 +138,11 @@ def library_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, stage):
+def measured_traffic(workload, mode, stage):
     """HBM bytes per launch of ``stage``'s kernel from the committed counter
     summary (FETCH_SIZE and WRITE_SIZE passes, scaled by a known-size copy),
     or None when there is none or the kernels changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{workload}_{mode}_hbm_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
@@ -97,15 +155,20 @@ def measured_traffic(workload, stage):
     return None
 
 
+# --------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands
+# --------------------------------------------------------------------------
+
 def cpu_baseline(cfg, seed, budget_s):
-    """The fp64 oracle (as it stands) on the host cores, on the same workload
-    (all B requests of one layer), repeated until ``budget_s`` of wall time."""
+    """The fp64 oracle on the host cores, on the same workload (all B
+    requests of one layer: desc, conv, verify, commit), repeated until
+    ``budget_s`` of wall time."""
     import oracle
     sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from harness import run_oracle
+    from harness import run_oracle, subset
     import gdn_inputs as gi
     case = gi.make_case(cfg, seed=seed, layer=0, packing="bfs")
-    run_oracle(subset_first(case, 1))  # build / load outside the timing
+    run_oracle(subset(case, np.arange(1)))  # build / load outside the timing
     reps, t0 = 0, time.perf_counter()
     while True:
         run_oracle(case)
@@ -119,10 +182,50 @@ def cpu_baseline(cfg, seed, budget_s):
                        f"in fp64, {reps} repetition(s), {el:.1f} s wall, inputs converted per call")
 
 
-def subset_first(case, n):
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from harness import subset
-    return subset(case, np.arange(n))
+# --------------------------------------------------------------------------
+# device inputs
+# --------------------------------------------------------------------------
+
+class Slot:
+    """One step's data of one layer instance: tree, rows, operands, path."""
+
+    def __init__(self, g, cfg, case, to_dev, dev, torch):
+        W = max(cfg.conv_W, 1)
+        self.case = case
+        self.desc = g.TreeDesc(to_dev(case["parent"]), to_dev(case["node_row"]), cfg.R, W)
+        for key in ("alpha", "beta", "path", "path_len"):
+            setattr(self, key, to_dev(case[key]))
+        B, R, D, Hv, Hqk = case["B"], cfg.R, cfg.D, cfg.Hv, cfg.Hqk
+        if cfg.conv_W > 0:
+            C = cfg.conv_C
+            self.x = to_dev(case["x"])
+            self.y = torch.zeros((B, R, C), dtype=torch.bfloat16, device=dev)
+            self.q = self.y[:, :, :Hqk * D].unflatten(-1, (Hqk, D))
+            self.k = self.y[:, :, Hqk * D:2 * Hqk * D].unflatten(-1, (Hqk, D))
+            self.v = self.y[:, :, 2 * Hqk * D:].unflatten(-1, (Hv, D))
+        else:
+            self.x = None
+            self.q, self.k, self.v = to_dev(case["q"]), to_dev(case["k"]), to_dev(case["v"])
+        self.out = torch.zeros((B, R, Hv, D), dtype=torch.float32, device=dev)
+
+
+class Instance:
+    """One layer instance: its pool, history and weights, and two step slots."""
+
+    def __init__(self, g, cfg, seed, layer, to_dev, dev, torch, slots):
+        import gdn_inputs as gi
+        cases = [gi.make_case(cfg, seed=seed + 7919 * j, layer=layer, packing="bfs") for j in range(slots)]
+        base = cases[0]
+        for c in cases[1:]:
+            for key in ("pool", "state_idx", "P", "hist", "w"):
+                if key in base:
+                    c[key] = base[key]
+        self.pool = to_dev(base["pool"])
+        self.state_idx = to_dev(base["state_idx"])
+        self.hist = to_dev(base["hist"]) if cfg.conv_W > 0 else None
+        self.w = to_dev(base["w"]) if cfg.conv_W > 0 else None
+        self.slots = [Slot(g, cfg, c, to_dev, dev, torch) for c in cases]
+        self.turn = 0
 
 
 def main():
@@ -131,8 +234,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=4)
+    ap.add_argument("--mode", choices=("fused", "separate"), default="fused")
     ap.add_argument("--seed", type=int, default=2026)
-    ap.add_argument("--sets", type=int, default=2, help="independent layer input sets rotated per step")
+    ap.add_argument("--sets", type=int, default=2, help="independent layer instances rotated per step")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -155,6 +259,7 @@ def main():
     g.load_library()
     cfg = gi.CONFIGS[args.config]
     dev = "cuda"
+    fused = args.mode == "fused"
 
     if args.copy_calibration > 0:
         n = args.copy_calibration * (1 << 20) // 4
@@ -173,94 +278,93 @@ def main():
         return torch.from_numpy(a).to(dev)
 
     t0 = time.perf_counter()
-    sets = []
-    for layer in range(args.sets):
-        case = gi.make_case(cfg, seed=args.seed, layer=layer, packing="bfs")
-        s = dict(case=case)
-        W = max(cfg.conv_W, 1)
-        s["desc"] = g.TreeDesc(to_dev(case["parent"]), to_dev(case["node_row"]), cfg.R, W)
-        for key in ("alpha", "beta", "pool", "state_idx", "path", "path_len"):
-            s[key] = to_dev(case[key])
-        B, R, D, Hv, Hqk = case["B"], cfg.R, cfg.D, cfg.Hv, cfg.Hqk
-        if cfg.conv_W > 0:
-            C = cfg.conv_C
-            s["x"], s["hist"], s["w"] = to_dev(case["x"]), to_dev(case["hist"]), to_dev(case["w"])
-            s["y"] = torch.zeros((B, R, C), dtype=torch.bfloat16, device=dev)
-            s["q"] = s["y"][:, :, :Hqk * D].unflatten(-1, (Hqk, D))
-            s["k"] = s["y"][:, :, Hqk * D:2 * Hqk * D].unflatten(-1, (Hqk, D))
-            s["v"] = s["y"][:, :, 2 * Hqk * D:].unflatten(-1, (Hv, D))
-        else:
-            s["x"] = s["hist"] = None
-            s["q"], s["k"], s["v"] = to_dev(case["q"]), to_dev(case["k"]), to_dev(case["v"])
-        s["out"] = torch.zeros((B, R, Hv, D), dtype=torch.float32, device=dev)
-        s["bytes"] = algorithmic_bytes(cfg, case)
-        sets.append(s)
+    insts = [Instance(g, cfg, args.seed, layer, to_dev, dev, torch, 2 if fused else 1)
+             for layer in range(args.sets)]
     err = torch.zeros(1, dtype=torch.int32, device=dev)
     flags = g.GDN_F_NORM_QK if cfg.norm_qk else 0
     torch.cuda.synchronize()
-    log(f"[bench] inputs for {cfg.name} x{args.sets} ready in {time.perf_counter() - t0:.1f} s")
+    log(f"[bench] {args.mode} mode: inputs for {cfg.name} x{args.sets} ready in "
+        f"{time.perf_counter() - t0:.1f} s")
 
-    names = ("desc", "conv", "verify", "commit")
+    names = ("desc", "conv", "commit_verify") if fused else ("desc", "conv", "verify", "commit")
 
-    def step(s, ev=None):
-        if ev is not None:
-            ev[0].record()
-        g.gdn_tree_desc_build(s["desc"], err)
-        if ev is not None:
-            ev[1].record()
-        if cfg.conv_W > 0:
-            g.conv_ancestry_gather(s["desc"], s["x"], s["hist"], s["state_idx"], s["w"], None,
-                                   s["y"], cfg.act, err)
-        if ev is not None:
-            ev[2].record()
-        g.gdn_tree_verify(s["desc"], s["q"], s["k"], s["v"], s["alpha"], s["beta"], s["pool"],
-                          s["state_idx"], s["out"], err, flags=flags)
-        if ev is not None:
-            ev[3].record()
-        g.gdn_tree_commit(s["desc"], s["path"], s["path_len"], s["k"], s["v"], s["alpha"],
-                          s["beta"], s["pool"], s["state_idx"], err, Hqk=cfg.Hqk,
-                          flags=flags & g.GDN_F_NORM_QK, x=s["x"], hist=s["hist"])
-        if ev is not None:
-            ev[4].record()
+    def step(inst, ev=None):
+        cur = inst.slots[inst.turn % len(inst.slots)]
+        prev = inst.slots[(inst.turn - 1) % len(inst.slots)]
+        inst.turn += 1
+        marks = iter(ev) if ev is not None else None
 
-    for i in range(args.warmup):
-        step(sets[i % len(sets)])
+        def mark():
+            if marks is not None:
+                next(marks).record()
+
+        mark()
+        g.gdn_tree_desc_build(cur.desc, err)
+        mark()
+        if fused:
+            if cfg.conv_W > 0:
+                g.conv_ancestry_gather_publish(cur.desc, cur.x, inst.hist, inst.state_idx, inst.w,
+                                               None, cur.y, cfg.act, prev.desc, prev.path,
+                                               prev.path_len, prev.x, err)
+            mark()
+            g.gdn_tree_commit_verify(cur.desc, cur.q, cur.k, cur.v, cur.alpha, cur.beta,
+                                     inst.pool, inst.state_idx, cur.out, prev.desc, prev.path,
+                                     prev.path_len, prev.k, prev.v, prev.alpha, prev.beta, err,
+                                     flags=flags)
+        else:
+            if cfg.conv_W > 0:
+                g.conv_ancestry_gather(cur.desc, cur.x, inst.hist, inst.state_idx, inst.w, None,
+                                       cur.y, cfg.act, err)
+            mark()
+            g.gdn_tree_verify(cur.desc, cur.q, cur.k, cur.v, cur.alpha, cur.beta, inst.pool,
+                              inst.state_idx, cur.out, err, flags=flags)
+            mark()
+            g.gdn_tree_commit(cur.desc, cur.path, cur.path_len, cur.k, cur.v, cur.alpha,
+                              cur.beta, inst.pool, inst.state_idx, err, Hqk=cfg.Hqk,
+                              flags=flags & g.GDN_F_NORM_QK, x=cur.x, hist=inst.hist)
+        mark()
+        return cur, prev
+
+    # the first step of each instance fills its slots' conv outputs
+    for i in range(args.warmup + (2 * args.sets if fused else 0)):
+        step(insts[i % len(insts)])
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    nmarks = len(names) + 1
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nmarks)] for _ in range(args.steps)]
+    bytes_steps = []
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     for i in range(args.steps):
-        step(sets[i % len(sets)], evs[i])
+        cur, prev = step(insts[i % len(insts)], evs[i])
+        bytes_steps.append(byte_model(cfg, cur.case, prev.case, args.mode))
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     if int(err.item()) != 0:
         log(f"[bench] device error word {int(err.item())}")
         sys.exit(3)
 
-    per = {n: [] for n in names}
-    for ev in evs:
-        for j, n in enumerate(names):
-            per[n].append(ev[j].elapsed_time(ev[j + 1]))
-    total_ms = evs[0][0].elapsed_time(evs[-1][4])
+    per = {n: [ev[j].elapsed_time(ev[j + 1]) for ev in evs] for j, n in enumerate(names)}
+    total_ms = evs[0][0].elapsed_time(evs[-1][-1])
     ms_per_step = total_ms / args.steps
     avg = {n: float(np.mean(per[n])) for n in names}
-    bytes_avg = {n: float(np.mean([s["bytes"][n] for s in sets])) for n in names}
+    bytes_avg = {n: float(np.mean([b[n] for b in bytes_steps])) for n in names}
     B, N = cfg.B, cfg.N
     nodes_per_s = B * N / (ms_per_step / 1e3)
     step_bytes = sum(bytes_avg.values())
     for n in names:
         gbs = bytes_avg[n] / (avg[n] / 1e3) / 1e9 if avg[n] > 0 else 0.0
-        log(f"[bench] {n:7s} {avg[n] * 1e3:9.1f} us  {bytes_avg[n] / 1e6:8.1f} MB  "
+        log(f"[bench] {n:13s} {avg[n] * 1e3:9.1f} us  {bytes_avg[n] / 1e6:8.1f} MB  "
             f"{gbs:8.1f} GB/s  {gbs / PEAK_HBM_GBS * 100:5.1f}% of 8 TB/s")
     log(f"[bench] step {ms_per_step * 1e3:.1f} us (events), wall {wall / args.steps * 1e6:.1f} us, "
         f"{step_bytes / 1e6:.1f} MB -> {step_bytes / (ms_per_step / 1e3) / 1e9:.1f} GB/s")
 
-    dom = max(("conv", "verify", "commit"), key=lambda n: avg[n])
+    dom = max((n for n in names if n != "desc"), key=lambda n: avg[n])
     achieved = bytes_avg[dom] / (avg[dom] / 1e3) / 1e9
+    tag = WORKLOAD_TAG.get(cfg.name, cfg.name)
     roofline = dict(bound="hbm", kernel=dom, achieved=round(achieved, 1), peak=PEAK_HBM_GBS,
                     unit="GB/s", frac=round(achieved / PEAK_HBM_GBS, 4),
-                    traffic=measured_traffic(WORKLOAD_TAG.get(cfg.name, cfg.name), dom),
+                    traffic=measured_traffic(tag, args.mode, dom),
                     avg_us=round(avg[dom] * 1e3, 2), algorithmic_bytes=int(bytes_avg[dom]))
 
     cpu = None
@@ -268,6 +372,10 @@ def main():
         cpu = cpu_baseline(cfg, args.seed, args.cpu_budget)
         cpu["value"] = round(cpu["value"], 1)
 
+    steps_desc = ("desc_build + conv_ancestry_gather_publish + gdn_tree_commit_verify (steady "
+                  "state: the previous step's accepted path committed and its conv history "
+                  "published inside this step)" if fused else
+                  "desc_build + conv_ancestry_gather + gdn_tree_verify + gdn_tree_commit")
     line = {
         "metric": METRIC,
         "value": round(nodes_per_s, 1),
@@ -286,10 +394,12 @@ def main():
                         f"B={B}, Hv={cfg.Hv} over Hqk={cfg.Hqk}, d={cfg.D}, bf16 operands, fp32 state"
                         + (f", causal conv W={cfg.conv_W} C={cfg.conv_C} SiLU, q/k normalised in-kernel"
                            if cfg.conv_W else ""),
-            "step": "desc_build + conv_ancestry_gather + gdn_tree_verify + gdn_tree_commit (one layer)",
+            "mode": args.mode,
+            "step": steps_desc + " (one layer)",
             "global_batch": B,
             "nodes_per_request": N,
             "parallelism": "single GPU",
+            "step_bytes": int(step_bytes),
             "step_hbm_gbs": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
             "step_frac_of_peak": round(step_bytes / (ms_per_step / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
             "kernel_us": {n: round(avg[n] * 1e3, 2) for n in names},

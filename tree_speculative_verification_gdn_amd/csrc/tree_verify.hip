@@ -40,6 +40,7 @@ namespace gdn {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kMfmaPath = 8;  // fused commit: paths up to this long replay on the matrix cores
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -94,14 +95,16 @@ __host__ __device__ inline MfmaLds mfma_lds_layout(int N, int NPB, int Lp = 0) {
     // Gram block.
     const int lp = Lp > 0 ? Lp : 0;
     L.rowp = off; off += align_up(lp * 4, 16);
-    const int psize = align_up(lp * kKQStride, 16) + align_up(lp * kD * 2, 16) + 3 * align_up(lp * 4, 16);
+    const int gsz = lp > 0 ? kMfmaPath * kMfmaPath * 4 : 0;  // after the scales: a segment Gram
+    const int psize = align_up(lp * kKQStride, 16) + align_up(lp * kD * 2, 16) + 2 * align_up(lp * 4, 16) +
+                      align_up(lp * 4 + gsz, 16);
     int poff = (psize <= 2 * NP * NP * 4) ? L.gk : off;
     if (poff == off) off += psize;
     L.kp = poff;   poff += align_up(lp * kKQStride, 16);
     L.vp = poff;   poff += align_up(lp * kD * 2, 16);
     L.alp = poff;  poff += align_up(lp * 4, 16);
     L.bep = poff;  poff += align_up(lp * 4, 16);
-    L.scp = poff;  poff += align_up(lp * 4, 16);
+    L.scp = poff;  poff += align_up(lp * 4 + gsz, 16);  // scales, then the segment Gram
     L.total = off;
     return L;
 }
@@ -572,44 +575,118 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                 s_bep[tid] = p_be;
             }
             __syncthreads();
-            for (int j = 0; j < len; ++j) {
-                float y = 0.f;
+            // On the matrix cores, kMfmaPath path nodes at a time (segment
+            // j0 .. j0 + n - 1 of the path, from the state the previous segment
+            // left), with A = product of the segment's decays so far and
+            // w_m = u_m times the decays after m:
+            //   z_j = (S_(j-1) k^_j)_r = A sc_j (S k_j)_r + sum_(m<j) w_m (k^_m . k^_j)
+            //   u_j = b_j (v_j,r - a_j z_j)
+            //   S  <- A S + sum_m (w_m sc_m) k_m^T   (a rank-n update)
+            // S k_j for every j of the segment is one contraction like (d); the
+            // rank-n update is four 32-column contractions whose output layout
+            // is this lane's own state layout.
+            float* s_gp = s_scp + cp.Lmax;  // [kMfmaPath][kMfmaPath] scaled segment Gram
+            for (int j0 = 0; j0 < len; j0 += kMfmaPath) {
+                const int n = min(len - j0, kMfmaPath);
+                auto path_row = [&](int row, int ks) -> bf16x8_t {  // zero past the segment
+                    const bf16x8_t a = lds_operand(s_kp, j0 + min(row, n - 1), ks, hf);
+                    return row < n ? a : bf16x8_t{};
+                };
+                if (wave == 0 && n > 1) {
+                    f32x16_t gacc = {};
 #pragma unroll
-                for (int s8 = 0; s8 < 8; ++s8) {
-                    const bf16x8_t kk = lds_operand(s_kp, j, s8, hf);
-                    const uint4 kw = __builtin_bit_cast(uint4, kk);
-                    const float4 a0 = sreg[2 * s8], a1 = sreg[2 * s8 + 1];
-                    y = fmaf(a0.x, __uint_as_float(kw.x << 16), y);
-                    y = fmaf(a0.y, __uint_as_float(kw.x & 0xffff0000u), y);
-                    y = fmaf(a0.z, __uint_as_float(kw.y << 16), y);
-                    y = fmaf(a0.w, __uint_as_float(kw.y & 0xffff0000u), y);
-                    y = fmaf(a1.x, __uint_as_float(kw.z << 16), y);
-                    y = fmaf(a1.y, __uint_as_float(kw.z & 0xffff0000u), y);
-                    y = fmaf(a1.z, __uint_as_float(kw.w << 16), y);
-                    y = fmaf(a1.w, __uint_as_float(kw.w & 0xffff0000u), y);
-                }
-                y += __shfl_xor(y, 32, 64);
-                const float a = s_alp[j];
-                const float sc = s_scp[j];
-                const float us = s_bep[j] * (bf16_bits_to_f32(s_vp[j * kD + r_own]) - a * (y * sc)) * sc;
-                // read k_j again rather than keep the unpacked copy live across
-                // the reduction
-                asm volatile("" ::: "memory");
+                    for (int ks = 0; ks < 8; ++ks)
+                        gacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(path_row(l32, ks), path_row(l32, ks),
+                                                                       gacc, 0, 0, 0);
 #pragma unroll
-                for (int s8 = 0; s8 < 8; ++s8) {
-                    const bf16x8_t kk = lds_operand(s_kp, j, s8, hf);
-                    const uint4 kw = __builtin_bit_cast(uint4, kk);
-                    float4& a0 = sreg[2 * s8];
-                    float4& a1 = sreg[2 * s8 + 1];
-                    a0.x = fmaf(a, a0.x, us * __uint_as_float(kw.x << 16));
-                    a0.y = fmaf(a, a0.y, us * __uint_as_float(kw.x & 0xffff0000u));
-                    a0.z = fmaf(a, a0.z, us * __uint_as_float(kw.y << 16));
-                    a0.w = fmaf(a, a0.w, us * __uint_as_float(kw.y & 0xffff0000u));
-                    a1.x = fmaf(a, a1.x, us * __uint_as_float(kw.z << 16));
-                    a1.y = fmaf(a, a1.y, us * __uint_as_float(kw.z & 0xffff0000u));
-                    a1.z = fmaf(a, a1.z, us * __uint_as_float(kw.w << 16));
-                    a1.w = fmaf(a, a1.w, us * __uint_as_float(kw.w & 0xffff0000u));
+                    for (int e = 0; e < kMfmaPath / 2; ++e) {  // rows m < kMfmaPath sit in these e
+                        const int m = 8 * (e >> 2) + 4 * hf + (e & 3);
+                        if (l32 < n && m < n)
+                            s_gp[m * kMfmaPath + l32] = gacc[e] * s_scp[j0 + m] * s_scp[j0 + l32];
+                    }
                 }
+                f32x16_t pacc = {};
+#pragma unroll
+                for (int ks = 0; ks < 8; ++ks) {
+                    bf16x8_t shi, slo;
+                    split_hi_lo(sreg[2 * ks], sreg[2 * ks + 1], shi, slo);
+                    const bf16x8_t a = path_row(l32, ks);
+                    pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, shi, pacc, 0, 0, 0);
+                    pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, slo, pacc, 0, 0, 0);
+                }
+                __syncthreads();  // segment Gram in LDS
+                // S k_j of this lane's row: this lane holds j in {4hf .. 4hf+3,
+                // 8+4hf .. 8+4hf+3}, its partner (lane ^ 32) the rest
+                float ctp[kMfmaPath];
+#pragma unroll
+                for (int e = 0; e < kMfmaPath / 2; ++e) {
+                    const float own = pacc[e];
+                    const float oth = __shfl_xor(own, 32, 64);
+                    const int jo = 8 * (e >> 2) + (e & 3);  // j held by the hf = 0 lane
+                    ctp[jo] = hf ? oth : own;
+                    ctp[jo + 4] = hf ? own : oth;
+                }
+                float w[kMfmaPath];
+                float A = 1.0f;
+#pragma unroll
+                for (int j = 0; j < kMfmaPath; ++j) {
+                    w[j] = 0.0f;
+                    if (j < n) {  // uniform
+                        const float a = s_alp[j0 + j];
+                        float z = A * s_scp[j0 + j] * ctp[j];
+#pragma unroll
+                        for (int m = 0; m < j; ++m) z = fmaf(w[m], s_gp[m * kMfmaPath + j], z);
+                        const float u = s_bep[j0 + j] * (bf16_bits_to_f32(s_vp[(j0 + j) * kD + r_own]) - a * z);
+#pragma unroll
+                        for (int m = 0; m < j; ++m) w[m] *= a;
+                        w[j] = u;
+                        A *= a;
+                    }
+                }
+                // B operand of the update: slot e of lane half hf is segment row 8hf + e
+                bf16x8_t uhi, ulo;
+                {
+                    float uu[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float w0 = w[e] * s_scp[j0 + min(e, n - 1)];
+                        float w1 = 0.0f;
+                        if constexpr (kMfmaPath > 8)
+                            w1 = w[min(8 + e, kMfmaPath - 1)] * s_scp[j0 + min(8 + e, n - 1)];
+                        uu[e] = hf ? w1 : w0;
+                    }
+                    split_hi_lo(make_float4(uu[0], uu[1], uu[2], uu[3]), make_float4(uu[4], uu[5], uu[6], uu[7]),
+                                uhi, ulo);
+                }
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb) {
+                    // A operand: k_m[32cb + l32] for segment row m = 8hf + e (zero past it)
+                    uint32_t kw[4];
+                    const uint16_t* col = reinterpret_cast<const uint16_t*>(s_kp) + (32 * cb + l32);
+#pragma unroll
+                    for (int e2 = 0; e2 < 4; ++e2) {
+                        const int m0 = 8 * hf + 2 * e2;
+                        const uint32_t k0 = col[(j0 + min(m0, n - 1)) * (kKQStride / 2)];
+                        const uint32_t k1 = col[(j0 + min(m0 + 1, n - 1)) * (kKQStride / 2)];
+                        kw[e2] = (m0 < n ? k0 : 0u) | ((m0 + 1 < n ? k1 : 0u) << 16);
+                    }
+                    const bf16x8_t ka = __builtin_bit_cast(bf16x8_t, make_uint4(kw[0], kw[1], kw[2], kw[3]));
+                    f32x16_t sacc;
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        sacc[4 * q4 + 0] = A * sreg[4 * cb + q4].x;
+                        sacc[4 * q4 + 1] = A * sreg[4 * cb + q4].y;
+                        sacc[4 * q4 + 2] = A * sreg[4 * cb + q4].z;
+                        sacc[4 * q4 + 3] = A * sreg[4 * cb + q4].w;
+                    }
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, uhi, sacc, 0, 0, 0);
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, ulo, sacc, 0, 0, 0);
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        sreg[4 * cb + q4] = make_float4(sacc[4 * q4], sacc[4 * q4 + 1], sacc[4 * q4 + 2],
+                                                        sacc[4 * q4 + 3]);
+                }
+                __syncthreads();  // the segment Gram is rewritten by the next segment
             }
 #pragma unroll
             for (int s8 = 0; s8 < 8; ++s8) {
