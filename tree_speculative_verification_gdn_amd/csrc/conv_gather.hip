@@ -157,6 +157,14 @@ __global__ void __launch_bounds__(kConvThreads) conv_gather_kernel(const ConvKAr
         if (blockIdx.x == 0 && tid == 0) atomicOr(err, GDN_EV_STATE);
         return;
     }
+    // the previous path nodes' parents and rows, ahead of the node rows below
+    // so that validating the path waits for them alone
+    int par = 0, prow = 0;
+    if constexpr (PUB) {
+        const size_t ti = static_cast<size_t>(a.shared_p ? 0 : b) * a.Np + min(max(pnode, 0), a.Np - 1);
+        par = a.parent_p[ti];
+        prow = a.node_row_p[ti];
+    }
     for (int r = tid; r < R; r += kConvThreads) s_node_of_row[r] = -1;
     __syncthreads();
     if (tid < N) {
@@ -198,13 +206,9 @@ __global__ void __launch_bounds__(kConvThreads) conv_gather_kernel(const ConvKAr
     Chunk<CPT> hc, hc_shift;
     const uint16_t* hs = hist + static_cast<size_t>(slot) * (H > 0 ? H : 1) * C;
     if (H > 0) hc = load_chunk<CPT>(hs + static_cast<size_t>(min(rs, H - 1)) * C + c0);
-    int par = 0, prow = 0;
     if constexpr (PUB) {
         if (H > 0)
             hc_shift = load_chunk<CPT>(hs + static_cast<size_t>(min(max(len, 0) + rs, H - 1)) * C + c0);
-        const size_t ti = static_cast<size_t>(a.shared_p ? 0 : b) * a.Np + min(max(pnode, 0), a.Np - 1);
-        par = a.parent_p[ti];
-        prow = a.node_row_p[ti];
     }
     // weights w[c][0..W-1] of the lane's CPT channels, CPT*W contiguous bf16:
     // 16-byte group min(rs, ...) per thread (scalar words when not 16-byte aligned)
@@ -231,25 +235,14 @@ __global__ void __launch_bounds__(kConvThreads) conv_gather_kernel(const ConvKAr
                          bias[c0 + 4 * (rs & 1) + 1 < C ? c0 + 4 * (rs & 1) + 1 : c0],
                          bias[c0 + 4 * (rs & 1) + 2 < C ? c0 + 4 * (rs & 1) + 2 : c0],
                          bias[c0 + 4 * (rs & 1) + 3 < C ? c0 + 4 * (rs & 1) + 3 : c0]);
-#pragma unroll
-    for (int p = 0; p < kPasses; ++p) {
-        const int i = rs + p * kRowsPerPass;
-        if (i < N) s_x[i * kTileLanes + lane] = xin[p];
-    }
     bool pub = false;
+    Chunk<CPT> xp;
     if constexpr (PUB) {
         // validate the previous path as the commit does: length in range, a
         // parent chain from a root-level node of the previous tree, a slot no
         // other request shares; a malformed path publishes nothing
         __shared__ int s_bad;
         __shared__ int32_t s_prow[kMaxNodes];
-        // the old history must be in registers before any lane overwrites it
-        if (H > 0) {
-            const uint32_t* h0 = reinterpret_cast<const uint32_t*>(&hc.u);
-            const uint32_t* h1 = reinterpret_cast<const uint32_t*>(&hc_shift.u);
-#pragma unroll
-            for (int e = 0; e < CPT / 2; ++e) asm volatile("" ::"v"(h0[e]), "v"(h1[e]));
-        }
         if (tid == 0) s_bad = 0;
         __syncthreads();
         const bool len_ok = len >= 0 && len <= a.Lmax;
@@ -265,14 +258,27 @@ __global__ void __launch_bounds__(kConvThreads) conv_gather_kernel(const ConvKAr
         bad = s_bad;
         if (bad && blockIdx.x == 0 && tid == 0) atomicOr(err, bad);
         pub = st_p == 0 && !bad && len > 0 && H > 0;
-        if (pub) {  // uniform
-            // new entry m = rs: old entry len + rs, or the x row of path node
-            // len + rs - H (oldest first)
-            const int pos = len + rs;
-            const int j = min(max(pos - H, 0), len - 1);
-            const Chunk<CPT> xp = load_chunk<CPT>(
-                a.x_prev + (static_cast<size_t>(b) * a.Rp + s_prow[j]) * C + c0);
-            hc = (pos < H) ? hc_shift : xp;
+        if (pub) {  // uniform: the x row of path node len + rs - H (oldest first)
+            const int j = min(max(len + rs - H, 0), len - 1);
+            xp = load_chunk<CPT>(a.x_prev + (static_cast<size_t>(b) * a.Rp + s_prow[j]) * C + c0);
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+        const int i = rs + p * kRowsPerPass;
+        if (i < N) s_x[i * kTileLanes + lane] = xin[p];
+    }
+    if constexpr (PUB) {
+        // the old history must be in registers before any lane overwrites it
+        if (H > 0) {
+            const uint32_t* h0 = reinterpret_cast<const uint32_t*>(&hc.u);
+            const uint32_t* h1 = reinterpret_cast<const uint32_t*>(&hc_shift.u);
+#pragma unroll
+            for (int e = 0; e < CPT / 2; ++e) asm volatile("" ::"v"(h0[e]), "v"(h1[e]));
+        }
+        __syncthreads();
+        if (pub) {  // new entry m = rs: old entry len + rs, or the x row above
+            hc = (len + rs < H) ? hc_shift : xp;
             if (rs < H && active)
                 *reinterpret_cast<decltype(hc.u)*>(hist + (static_cast<size_t>(slot) * H + rs) * C + c0) = hc.u;
         }
