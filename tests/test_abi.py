@@ -27,9 +27,10 @@ def lib():
     return g.load_library()
 
 
-def test_header_declares_the_four_entry_points():
+def test_header_declares_the_entry_points():
     decl = declared_functions()
-    for name in ("gdn_tree_desc_build", "conv_ancestry_gather", "gdn_tree_verify", "gdn_tree_commit"):
+    for name in ("gdn_tree_desc_build", "conv_ancestry_gather", "gdn_tree_verify", "gdn_tree_commit",
+                 "conv_ancestry_gather_publish", "gdn_tree_commit_verify"):
         assert name in decl
     assert set(decl) == set(g.EXPORTED)
 
@@ -87,6 +88,43 @@ def test_argument_checks_fail_before_launch(lib):
     Cv = lib.conv_ancestry_gather
     assert Cv(d, p, p, 4, p, p, None, p, 8190, 1, err, None) == g.GDN_ERR_UNSUPPORTED
     assert Cv(d, p, p, 4, p, p, None, p, 8192, 2, err, None) == g.GDN_ERR_ARG
+
+
+def test_fused_step_argument_checks_fail_before_launch(lib):
+    err = ctypes.c_void_p(128)
+    d = ctypes.byref(_desc())
+    other_b = ctypes.byref(_desc(B=3))
+    other_w = ctypes.byref(_desc(W=2))
+    p = ctypes.c_void_p(256)
+    # conv with publication: previous tree of another batch or conv width,
+    # Lmax out of range, missing previous input
+    Cp = lib.conv_ancestry_gather_publish
+    assert Cp(d, p, p, 4, p, p, None, p, 8192, 1, other_b, p, p, 7, p, err, None) == g.GDN_ERR_ARG
+    assert Cp(d, p, p, 4, p, p, None, p, 8192, 1, other_w, p, p, 7, p, err, None) == g.GDN_ERR_ARG
+    assert Cp(d, p, p, 4, p, p, None, p, 8192, 1, d, p, p, 0, p, err, None) == g.GDN_ERR_UNSUPPORTED
+    assert Cp(d, p, p, 4, p, p, None, p, 8192, 1, d, p, p, 7, None, err, None) == g.GDN_ERR_ARG
+    assert Cp(d, p, p, 4, p, p, None, p, 8192, 1, None, p, p, 7, p, err, None) == g.GDN_ERR_ARG
+    # commit + verify: previous tree of another batch, Lmax out of range, short
+    # previous row stride, missing previous gates, unknown flag
+    F = lib.gdn_tree_commit_verify
+    args = dict(q=p, k=p, v=p, rqk=2048, rv=4096, a=p, b=p, pool=p, P=4, sidx=p, out=p, prev=d,
+                path=p, plen=p, Lmax=7, kp=p, vp=p, rqkp=2048, rvp=4096, ap=p, bp=p, Hqk=16, Hv=32,
+                dk=128, dv=128, dt=0, fl=0)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return F(d, a["q"], a["k"], a["v"], a["rqk"], a["rv"], a["a"], a["b"], a["pool"], a["P"],
+                 a["sidx"], a["out"], a["prev"], a["path"], a["plen"], a["Lmax"], a["kp"], a["vp"],
+                 a["rqkp"], a["rvp"], a["ap"], a["bp"], a["Hqk"], a["Hv"], a["dk"], a["dv"], a["dt"],
+                 a["fl"], err, None)
+    assert call(prev=other_b) == g.GDN_ERR_ARG
+    assert call(Lmax=65) == g.GDN_ERR_UNSUPPORTED
+    assert call(rqkp=100) == g.GDN_ERR_ARG
+    assert call(bp=None) == g.GDN_ERR_ARG
+    assert call(fl=64) == g.GDN_ERR_ARG
+    assert call(Hqk=3) == g.GDN_ERR_ARG
+    assert call(pool=ctypes.c_void_p(260)) == g.GDN_ERR_ARG  # state pool not 16-byte aligned
 
 
 def test_binding_refuses_when_library_missing(monkeypatch, tmp_path):
