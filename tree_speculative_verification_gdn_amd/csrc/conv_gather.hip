@@ -1,9 +1,10 @@
 // Ancestry-gathered causal conv1d (LumoTree, Sec. V-C).  The window of node i
 // is its own ancestry (parent, grandparent, ...) continued into the request's
-// conv history, exactly as listed in the descriptor's conv_src; taps are
-// applied oldest -> newest with float32 accumulation and one bf16 cast at the
-// end (the page's point that tap order and cast boundaries fix the recorded
-// values).
+// conv history, exactly as listed in the descriptor's conv_src; the taps are
+// summed in float32 (exact bf16 products, taps paired oldest first on the
+// packed dot-product instruction) with one bf16 cast at the end (the page's
+// point that tap order and cast boundaries fix the recorded values: here the
+// conv output is computed once and every later stage reads that bf16 value).
 //
 // Layout / schedule: workgroup = (channel tile, request), 256 threads.  A row
 // of the tile is covered by TL lanes of CPT channels each (one 8- or 16-byte
@@ -114,7 +115,8 @@ __global__ void __launch_bounds__(kConvThreads) conv_gather_kernel(const ConvKAr
     int32_t* __restrict__ err = a.err;
     constexpr int H = W - 1;
     constexpr int TILE = kTileLanes * CPT;  // channels per workgroup
-    constexpr int kWW = CPT * W / 2;        // 32-bit words of one lane's weights
+    constexpr int kWP = (W + 1) / 2;        // tap pairs per channel
+    constexpr int kWW = CPT * kWP;          // 32-bit words of one lane's weights: tap pairs
     // LDS: x rows of the nodes, then the H history entries, as rows of
     // kTileLanes chunks; the tile's weights and bias; the row -> node map
     extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -210,12 +212,14 @@ __global__ void __launch_bounds__(kConvThreads) conv_gather_kernel(const ConvKAr
         if (H > 0)
             hc_shift = load_chunk<CPT>(hs + static_cast<size_t>(min(max(len, 0) + rs, H - 1)) * C + c0);
     }
-    // weights w[c][0..W-1] of the lane's CPT channels, CPT*W contiguous bf16:
-    // 16-byte group min(rs, ...) per thread (scalar words when not 16-byte aligned)
+    // weights w[c][0..W-1] of the lane's CPT channels as tap pairs per channel,
+    // (w[c][2p], w[c][2p+1] or 0).  With W even that is the memory layout:
+    // 16-byte group min(rs, ...) per thread (scalar words when not 16-byte
+    // aligned); with W odd, thread rs builds channel rs's pairs.
     constexpr int kWG = (kWW + 3) / 4;  // 16-byte groups
     uint4 wg4 = make_uint4(0u, 0u, 0u, 0u);
     const uint16_t* wp = w + static_cast<size_t>(c0) * W;
-    {
+    if constexpr (W % 2 == 0) {
         const int grp = min(rs, kWG - 1);
         if (CPT == 8) {  // 16-byte aligned: w is, and c0 * W * 2 is a multiple of 16
             wg4 = *reinterpret_cast<const uint4*>(wp + 8 * grp);
@@ -228,6 +232,13 @@ __global__ void __launch_bounds__(kConvThreads) conv_gather_kernel(const ConvKAr
             }
             wg4 = make_uint4(ww[0], ww[1], ww[2], ww[3]);
         }
+    } else {
+        const int ch = min(rs, CPT - 1);
+        uint32_t ww[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int t = 0; t < W; ++t)
+            ww[t >> 1] |= static_cast<uint32_t>(wp[ch * W + t]) << (16 * (t & 1));
+        wg4 = make_uint4(ww[0], ww[1], ww[2], ww[3]);
     }
     float4 bq = make_float4(0.f, 0.f, 0.f, 0.f);
     if (bias)  // uniform
@@ -284,45 +295,61 @@ __global__ void __launch_bounds__(kConvThreads) conv_gather_kernel(const ConvKAr
         }
     }
     if (H > 0 && rs < H) s_x[(N + rs) * kTileLanes + lane] = hc;
-    if (rs < kWG) {
-        uint32_t* wd = s_w + lane * kWW + 4 * rs;
+    {
         const uint32_t wv[4] = {wg4.x, wg4.y, wg4.z, wg4.w};
+        if constexpr (W % 2 == 0) {
+            if (rs < kWG) {
+                uint32_t* wd = s_w + lane * kWW + 4 * rs;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (4 * rs + e < kWW) wd[e] = wv[e];
+                for (int e = 0; e < 4; ++e)
+                    if (4 * rs + e < kWW) wd[e] = wv[e];
+            }
+        } else if (rs < CPT) {
+#pragma unroll
+            for (int q = 0; q < kWP; ++q) s_w[lane * kWW + rs * kWP + q] = wv[q];
+        }
     }
     if (bias && rs < CPT / 4) *reinterpret_cast<float4*>(s_b + lane * CPT + 4 * rs) = bq;
     __syncthreads();
     if (!active) return;
 
-    for (int i = rs; i < N; i += kRowsPerPass) {
-        uint32_t wr[kWW];
+    // taps in bf16 pairs on v_dot2_f32_bf16 (exact bf16 products, fp32 sums):
+    // for channel c and pair p, (x of tap 2p, x of tap 2p+1) . (w[c][2p], w[c][2p+1])
+    uint32_t wr[kWW];
 #pragma unroll
-        for (int e = 0; e < kWW; ++e) wr[e] = s_w[lane * kWW + e];
-        auto wgt = [&](int j, int tap) -> float {
-            const int e = j * W + tap;
-            return (e & 1) ? __uint_as_float(wr[e >> 1] & 0xffff0000u) : __uint_as_float(wr[e >> 1] << 16);
-        };
+    for (int e = 0; e < kWW; ++e) wr[e] = s_w[lane * kWW + e];
+    constexpr int NW = CPT / 2;  // 32-bit words of a row chunk
+    for (int i = rs; i < N; i += kRowsPerPass) {
+        // the node's window, oldest first: its H taps, then the node itself
+        uint32_t xw[W][NW];
+#pragma unroll
+        for (int t = 0; t < W; ++t) {
+            const int row = (t < H) ? s_tap[i * H + t] : i;
+            const Chunk<CPT> ch = s_x[row * kTileLanes + lane];
+            const uint32_t* cw = reinterpret_cast<const uint32_t*>(&ch.u);
+#pragma unroll
+            for (int q = 0; q < NW; ++q) xw[t][q] = cw[q];
+        }
         float z[CPT];
 #pragma unroll
-        for (int tap = 0; tap < H; ++tap) {
-            float xv[CPT];
-            unpack<CPT>(s_x[s_tap[i * H + tap] * kTileLanes + lane], xv);
+        for (int c = 0; c < CPT; ++c) {
+            const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;  // halves c % 2 of two words
+            float acc = 0.0f;
 #pragma unroll
-            for (int j = 0; j < CPT; ++j)
-                z[j] = (tap == 0) ? wgt(j, 0) * xv[j] : fmaf(wgt(j, tap), xv[j], z[j]);
+            for (int q = 0; q < kWP; ++q) {
+                const uint32_t lo = xw[2 * q][c >> 1];
+                const uint32_t hi = (2 * q + 1 < W) ? xw[2 * q + 1][c >> 1] : 0u;
+                const uint32_t xp = __builtin_amdgcn_perm(hi, lo, sel);
+                acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, xp),
+                                                      __builtin_bit_cast(bf16x2_t, wr[c * kWP + q]), acc,
+                                                      false);
+            }
+            if (bias) acc += s_b[lane * CPT + c];
+            if (act == GDN_ACT_SILU) acc = silu(acc);
+            z[c] = acc;
         }
-        float xi[CPT];
-        unpack<CPT>(s_x[i * kTileLanes + lane], xi);
         Chunk<CPT> o;
         uint32_t* ow = reinterpret_cast<uint32_t*>(&o.u);
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-            float zz = (H == 0) ? wgt(j, H) * xi[j] : fmaf(wgt(j, H), xi[j], z[j]);
-            if (bias) zz += s_b[lane * CPT + j];
-            if (act == GDN_ACT_SILU) zz = silu(zz);
-            z[j] = zz;
-        }
 #pragma unroll
         for (int e = 0; e < CPT / 2; ++e) ow[e] = pack_bf16x2(z[2 * e], z[2 * e + 1]);
         *reinterpret_cast<decltype(o.u)*>(y + (xb + s_row[i]) * C + c0) = o.u;
@@ -330,7 +357,7 @@ __global__ void __launch_bounds__(kConvThreads) conv_gather_kernel(const ConvKAr
 }
 
 size_t conv_lds_bytes(int N, int R, int W, int cpt) {
-    return conv_lds_x_bytes(N, W, cpt) + static_cast<size_t>(kTileLanes) * (cpt * W / 2) * 4 +
+    return conv_lds_x_bytes(N, W, cpt) + static_cast<size_t>(kTileLanes) * (cpt * ((W + 1) / 2)) * 4 +
            static_cast<size_t>(kTileLanes) * cpt * 4 + static_cast<size_t>(R) * sizeof(int32_t);
 }
 
