@@ -214,7 +214,7 @@ def _gates(g_a, g_b, cfg: Config, shape):
 
 def make_case(cfg: Config, seed: int = 2026, layer: int = 0, B: int | None = None,
               packing: str = "perm", extra_slots: int = 0, poison: bool = True,
-              with_pool: bool = True) -> dict:
+              with_pool: bool = True, conv_values: str = "normal") -> dict:
     """All inputs of one layer of ``cfg`` (optionally with a smaller batch B).
 
     Returns a dict of host arrays:
@@ -224,6 +224,13 @@ def make_case(cfg: Config, seed: int = 2026, layer: int = 0, B: int | None = Non
       alpha, beta [B][R][Hv] float32; pool [P][Hv][D][D] float32;
       state_idx [B] int32 (a seeded permutation of pool slots).
     Padding rows (rows no node maps to) and unused pool slots hold NaN.
+
+    conv_values="dyadic" draws x and hist from {k/8 : |k| <= 16} and w from
+    {j/64 : |j| <= 8} instead of the normal distributions: every product is
+    a multiple of 2^-9 and every W-tap sum stays below 2^4 in magnitude, so
+    any fp32 or fp64 summation of the taps is exact and both sides round the
+    same value to bf16 (conv parity without rounding straddles; use it with
+    act = 0).
     """
     B = cfg.B if B is None else B
     N, R, D, Hv, Hqk = cfg.N, cfg.R, cfg.D, cfg.Hv, cfg.Hqk
@@ -251,11 +258,16 @@ def make_case(cfg: Config, seed: int = 2026, layer: int = 0, B: int | None = Non
     P = B + extra_slots
     if cfg.conv_W > 0:
         C, W = cfg.conv_C, cfg.conv_W
-        x = rng(seed, cid, layer, _S_X).standard_normal((B, R, C), dtype=np.float32)
+        if conv_values == "dyadic":
+            x = rng(seed, cid, layer, _S_X).integers(-16, 17, (B, R, C)).astype(np.float32) / 8
+            hist = rng(seed, cid, layer, _S_HIST).integers(-16, 17, (P, W - 1, C)).astype(np.float32) / 8
+            w = rng(seed, cid, layer, _S_W).integers(-8, 9, (C, W)).astype(np.float32) / 64
+        else:
+            x = rng(seed, cid, layer, _S_X).standard_normal((B, R, C), dtype=np.float32)
+            hist = rng(seed, cid, layer, _S_HIST).standard_normal((P, W - 1, C), dtype=np.float32)
+            w = (rng(seed, cid, layer, _S_W).standard_normal((C, W), dtype=np.float32) * np.float32(cfg.w_std))
         if poison:
             x[~used] = np.nan
-        hist = rng(seed, cid, layer, _S_HIST).standard_normal((P, W - 1, C), dtype=np.float32)
-        w = (rng(seed, cid, layer, _S_W).standard_normal((C, W), dtype=np.float32) * np.float32(cfg.w_std))
         out.update(x=f32_to_bf16_bits(x), hist=f32_to_bf16_bits(hist), w=f32_to_bf16_bits(w))
     else:
         q = _unit_rows(rng(seed, cid, layer, _S_Q), (B, R, Hqk, D))

@@ -25,9 +25,10 @@
  *                           publish the state in place, and publish the conv
  *                           history along the same path (LumoTree, Sec. IV-B and
  *                           V-A; Bole review, Algorithm 2 Phase C)
- *   and two that fuse the steady-state step (commit of the previous path with
+ *   two that fuse the steady-state step (commit of the previous path with
  *   the conv and the verify of the next tree): conv_ancestry_gather_publish
- *   and gdn_tree_commit_verify, declared at the end.
+ *   and gdn_tree_commit_verify; and gdn_path_resolve + gdn_layer_step, which
+ *   run a whole layer's step in one launch.  These are declared at the end.
  *
  * Conventions shared by every call
  *   - Every pointer is device memory unless the comment says "host".  The
@@ -246,10 +247,89 @@ int32_t gdn_tree_commit_verify(const gdn_tree_desc *d, const void *q, const void
                                int32_t dv, int32_t dtype, int32_t flags, int32_t *err,
                                void *stream);
 
+/* ---- one launch per layer ------------------------------------------------
+ * A model runs the same step for every GDN layer: commit the previous step's
+ * accepted path, publish its conv history, convolve and verify the new tree.
+ * Everything that depends only on the trees and the path (validation, the
+ * path's physical rows) is done once per step by gdn_path_resolve; each
+ * layer is then one launch of gdn_layer_step, which keeps a (request, head)
+ * pair's whole step on one workgroup: the conv output q/k/v never goes to
+ * memory, and the previous path's k/v are recomputed from its conv input
+ * (the same conv, so the same bf16 values the previous step verified with)
+ * instead of being stored (LumoTree, Sec. IV-B: replay of the accepted
+ * operands; Sec. V-A: one path drives replay and conv publication; Sec. V-C:
+ * the conv window of a node is its ancestry, then the history). */
+
+/* Validate the previous step's accepted path against its tree and resolve it
+ * to physical rows, once per step for all layers.
+ *   d_prev      the previous step's descriptor (built; its status is read)
+ *   path, path_len, Lmax: as in gdn_tree_commit (1 <= Lmax <= 64)
+ *   state_idx   int32 [B], checked against P and for slots shared by two
+ *               requests
+ *   path_rows   out int32 [B][Lmax]: node_row of path[b][j] for j < n_b;
+ *               other entries are left as they were
+ *   path_n      out int32 [B]: n_b = path_len[b] when the path validates;
+ *               0 when path_len[b] is 0, when the previous tree is malformed
+ *               (reported by its own descriptor build) or when the path is
+ *               malformed (GDN_EV_PATH); -1 when state_idx[b] is outside
+ *               [0, P) or shared with another request (GDN_EV_STATE)
+ * Cite: LumoTree, Sec. V-A (one device-produced path drives every
+ * publication; padded entries never advance state). */
+int32_t gdn_path_resolve(const gdn_tree_desc *d_prev, const int32_t *path,
+                         const int32_t *path_len, int32_t Lmax, const int32_t *state_idx,
+                         int32_t P, int32_t *path_rows, int32_t *path_n, int32_t *err,
+                         void *stream);
+
+/* One GDN layer's step in one launch.  With hist = hist_in copied to
+ * hist_out first, it computes what these calls compute in order:
+ *     y_prev = conv_ancestry_gather(d_prev, x_prev, hist)      (path rows only)
+ *     gdn_tree_commit(d_prev, path, k/v of y_prev, alpha_prev, beta_prev,
+ *                     state_pool, x_prev, hist)                 (state, history)
+ *     y = conv_ancestry_gather(d, x, hist);  gdn_tree_verify(d, q/k/v of y, ...)
+ * where the path is the one gdn_path_resolve resolved into path_rows/path_n.
+ *   x         bf16 [B][d->R][C], C = 2*Hqk*128 + Hv*128, channels [q | k | v]
+ *             head-major (qk head g: q at g*128, k at Hqk*128 + g*128; value
+ *             head h: v at 2*Hqk*128 + h*128)
+ *   w, bias, act: conv weights bf16 [C][W], bias float32 [C] or NULL,
+ *             GDN_ACT_NONE / GDN_ACT_SILU; W = d->W
+ *   hist_in   bf16 [P][W-1][C]: the history the previous step's tree was
+ *             convolved with; read only
+ *   hist_out  bf16 [P][W-1][C]: written for every request with n_b >= 0:
+ *             the last W-1 entries of (hist_in ++ x_prev rows of the path);
+ *             must not overlap hist_in.  The next step passes it as hist_in.
+ *             Both may be NULL when W == 1.
+ *   alpha, beta   float32 [B][d->R][Hv]: gates of the new tree
+ *   state_pool float32 [P][Hv][128][128], slot state_idx[b]: read, and
+ *             written with the committed state when n_b > 0
+ *   out       [B][d->R][Hv][128] float32 (bf16 with GDN_F_OUT_BF16)
+ *   y         optional (NULL: not written) bf16 [B][d->R][C]: the new tree's
+ *             conv output, node rows only
+ *   d_prev, x_prev bf16 [B][d_prev->R][C], alpha_prev, beta_prev float32
+ *             [B][d_prev->R][Hv]: the previous step's tree, conv input and
+ *             gates (read at path rows only, but must be valid buffers even
+ *             when every n_b is 0)
+ *   path_rows, path_n, Lmax: from gdn_path_resolve (values are clamped into
+ *             range before use, so no access leaves the buffers)
+ * Requirements: bf16, dk = dv = 128, d->N <= 32, d_prev->B == d->B,
+ * 1 <= Lmax <= 64, x, x_prev, hist_in, hist_out 16-byte aligned, state_pool
+ * 16-byte aligned.  flags: GDN_F_NORM_QK, GDN_F_OUT_BF16.  Errors: a
+ * malformed new tree gets no outputs (its path is still committed and its
+ * history published); n_b = -1 writes neither state nor history. */
+int32_t gdn_layer_step(const gdn_tree_desc *d, const void *x, const void *w, const float *bias,
+                       int32_t act, const void *hist_in, void *hist_out, const float *alpha,
+                       const float *beta, float *state_pool, int32_t P,
+                       const int32_t *state_idx, void *out, void *y,
+                       const gdn_tree_desc *d_prev, const void *x_prev,
+                       const float *alpha_prev, const float *beta_prev,
+                       const int32_t *path_rows, const int32_t *path_n, int32_t Lmax,
+                       int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv, int32_t flags,
+                       int32_t *err, void *stream);
+
 /* Human-readable name of a return code (host; static string). */
 const char *gdn_status_string(int32_t status);
 
-/* ABI version of this header: 2 (1 plus the two fused-step calls). */
+/* ABI version of this header: 3 (1, plus the two fused-step calls in 2,
+ * plus gdn_path_resolve and gdn_layer_step). */
 int32_t gdn_abi_version(void);
 
 #ifdef __cplusplus

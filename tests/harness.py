@@ -235,12 +235,17 @@ def straddle_rows(case, y_gpu, y_ref):
 # conv and verify of step 2's tree (same requests, pool and history)
 # --------------------------------------------------------------------------
 
-def two_step_case(cfg, seed, B=None, extra_slots=0, packing="perm"):
+def two_step_case(cfg, seed, B=None, extra_slots=0, packing="perm", conv_values="normal"):
     """Two consecutive steps of one layer: step 2 has its own trees, rows,
-    operands and paths, and the requests' pool slots and history of step 1."""
-    c1 = gi.make_case(cfg, seed=seed, B=B, extra_slots=extra_slots, packing=packing)
-    c2 = gi.make_case(cfg, seed=seed + 7919, B=B, extra_slots=extra_slots, packing=packing)
-    for key in ("pool", "state_idx", "P", "hist"):
+    operands and paths, and the requests' pool slots, history and conv
+    weights of step 1."""
+    c1 = gi.make_case(cfg, seed=seed, B=B, extra_slots=extra_slots, packing=packing,
+                      conv_values=conv_values)
+    c2 = gi.make_case(cfg, seed=seed + 7919, B=B, extra_slots=extra_slots, packing=packing,
+                      conv_values=conv_values)
+    # the pool, the history and the conv weights belong to the layer: the
+    # same at both steps
+    for key in ("pool", "state_idx", "P", "hist", "w"):
         if key in c1:
             c2[key] = c1[key]
     return c1, c2
@@ -368,4 +373,46 @@ def run_gpu_two_steps(c1, c2, fused=True, y1_override=None, y2_override=None, fl
                status1=d1.status.cpu().numpy(), status2=d2.status.cpu().numpy())
     if hist is not None:
         res["hist"] = bits(hist)
+    return res
+
+
+def run_gpu_layer(c1, c2, flags=0, with_y=True, path_n_override=None):
+    """Step 2 of a conv configuration through the one-launch layer step:
+    gdn_path_resolve of step 1's path, then gdn_layer_step with step 1's conv
+    input, gates and history (hist_in) and a separate hist_out."""
+    import torch
+    import tree_speculative_verification_gdn_amd as g
+
+    cfg = c1["cfg"]
+    B, R, D, Hv, Hqk, C, W = c1["B"], cfg.R, cfg.D, cfg.Hv, cfg.Hqk, cfg.conv_C, cfg.conv_W
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    d1 = g.TreeDesc(to_dev(c1["parent"]), to_dev(c1["node_row"]), R, W)
+    d2 = g.TreeDesc(to_dev(c2["parent"]), to_dev(c2["node_row"]), R, W)
+    g.gdn_tree_desc_build(d1, err)
+    g.gdn_tree_desc_build(d2, err)
+    pool = to_dev(c1["pool"])
+    sidx = to_dev(c1["state_idx"])
+    P = int(pool.shape[0])
+    path = to_dev(c1["path"])
+    Lmax = int(path.shape[1])
+    path_rows = torch.full((B, Lmax), -7, dtype=torch.int32, device="cuda")
+    path_n = torch.full((B,), -9, dtype=torch.int32, device="cuda")
+    g.gdn_path_resolve(d1, path, to_dev(c1["path_len"]), sidx, P, path_rows, path_n, err)
+    if path_n_override is not None:
+        path_n.copy_(to_dev(np.asarray(path_n_override, np.int32)))
+    hist_in = to_dev(c1["hist"])
+    hist_out = torch.full_like(hist_in, float("nan"))
+    out = torch.full((B, R, Hv, D), float("nan"), dtype=torch.float32, device="cuda")
+    y = torch.full((B, R, C), float("nan"), dtype=torch.bfloat16, device="cuda") if with_y else None
+    flags |= g.GDN_F_NORM_QK if cfg.norm_qk else 0
+    g.gdn_layer_step(d2, to_dev(c2["x"]), to_dev(c2["w"]), None, cfg.act, hist_in, hist_out,
+                     to_dev(c2["alpha"]), to_dev(c2["beta"]), pool, sidx, out, d1, to_dev(c1["x"]),
+                     to_dev(c1["alpha"]), to_dev(c1["beta"]), path_rows, path_n, err, Hqk,
+                     flags=flags, y=y)
+    torch.cuda.synchronize()
+    res = dict(err=int(err.item()), out=out.cpu().numpy(), pool=pool.cpu().numpy(),
+               hist_out=bits(hist_out), hist_in=bits(hist_in), path_n=path_n.cpu().numpy(),
+               path_rows=path_rows.cpu().numpy(), status2=d2.status.cpu().numpy())
+    if with_y:
+        res["y2"] = bits(y)
     return res

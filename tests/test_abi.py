@@ -30,7 +30,8 @@ def lib():
 def test_header_declares_the_entry_points():
     decl = declared_functions()
     for name in ("gdn_tree_desc_build", "conv_ancestry_gather", "gdn_tree_verify", "gdn_tree_commit",
-                 "conv_ancestry_gather_publish", "gdn_tree_commit_verify"):
+                 "conv_ancestry_gather_publish", "gdn_tree_commit_verify", "gdn_path_resolve",
+                 "gdn_layer_step"):
         assert name in decl
     assert set(decl) == set(g.EXPORTED)
 
@@ -45,7 +46,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.gdn_abi_version() == 2
+    assert lib.gdn_abi_version() == 3
     assert lib.gdn_status_string(0) == b"ok"
     assert lib.gdn_status_string(-1) == b"invalid argument"
     assert lib.gdn_status_string(-4) == b"unsupported size"
@@ -125,6 +126,48 @@ def test_fused_step_argument_checks_fail_before_launch(lib):
     assert call(fl=64) == g.GDN_ERR_ARG
     assert call(Hqk=3) == g.GDN_ERR_ARG
     assert call(pool=ctypes.c_void_p(260)) == g.GDN_ERR_ARG  # state pool not 16-byte aligned
+
+
+def test_layer_step_argument_checks_fail_before_launch(lib):
+    err = ctypes.c_void_p(128)
+    d = ctypes.byref(_desc(N=27, R=32))
+    other_b = ctypes.byref(_desc(B=3, N=27, R=32))
+    big = ctypes.byref(_desc(N=33, R=40))
+    p = ctypes.c_void_p(256)
+    # path resolve: missing outputs, Lmax out of range, no slots
+    Rz = lib.gdn_path_resolve
+    assert Rz(d, p, p, 7, p, 4, p, None, err, None) == g.GDN_ERR_ARG
+    assert Rz(d, p, p, 0, p, 4, p, p, err, None) == g.GDN_ERR_UNSUPPORTED
+    assert Rz(d, p, p, 65, p, 4, p, p, err, None) == g.GDN_ERR_UNSUPPORTED
+    assert Rz(d, p, p, 7, p, 0, p, p, err, None) == g.GDN_ERR_ARG
+    assert Rz(None, p, p, 7, p, 4, p, p, err, None) == g.GDN_ERR_ARG
+    # layer step: C = 2*16*128 + 32*128 = 8192 channels, history bytes P*(W-1)*C*2
+    L = lib.gdn_layer_step
+    hbytes = 4 * 3 * 8192 * 2
+    args = dict(d=d, x=p, w=p, bias=None, act=1, hin=ctypes.c_void_p(1 << 20),
+                hout=ctypes.c_void_p((1 << 20) + hbytes), a=p, b=p, pool=p, P=4, sidx=p, out=p,
+                y=None, prev=d, xp=p, ap=p, bp=p, prow=p, pn=p, Lmax=7, Hqk=16, Hv=32, dk=128,
+                dv=128, fl=1)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return L(a["d"], a["x"], a["w"], a["bias"], a["act"], a["hin"], a["hout"], a["a"], a["b"],
+                 a["pool"], a["P"], a["sidx"], a["out"], a["y"], a["prev"], a["xp"], a["ap"], a["bp"],
+                 a["prow"], a["pn"], a["Lmax"], a["Hqk"], a["Hv"], a["dk"], a["dv"], a["fl"], err, None)
+    assert call(prev=other_b) == g.GDN_ERR_ARG              # previous tree of another batch
+    assert call(d=big) == g.GDN_ERR_UNSUPPORTED             # N > 32
+    assert call(dk=64, dv=64) == g.GDN_ERR_UNSUPPORTED      # d != 128
+    assert call(Lmax=65) == g.GDN_ERR_UNSUPPORTED
+    assert call(act=2) == g.GDN_ERR_ARG
+    assert call(fl=4) == g.GDN_ERR_ARG                      # only NORM_QK and OUT_BF16
+    assert call(hout=None) == g.GDN_ERR_ARG
+    assert call(hout=args["hin"]) == g.GDN_ERR_ARG          # history buffers overlap
+    assert call(hout=ctypes.c_void_p((1 << 20) + hbytes - 16)) == g.GDN_ERR_ARG
+    assert call(x=ctypes.c_void_p(264)) == g.GDN_ERR_ARG    # x not 16-byte aligned
+    assert call(xp=None) == g.GDN_ERR_ARG
+    assert call(pn=None) == g.GDN_ERR_ARG
+    assert call(Hqk=3) == g.GDN_ERR_ARG
 
 
 def test_binding_refuses_when_library_missing(monkeypatch, tmp_path):

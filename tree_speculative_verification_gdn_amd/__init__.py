@@ -9,8 +9,9 @@ the shared library is missing, every call raises.
 
 Entry points (same names as the C ABI):
     gdn_tree_desc_build, conv_ancestry_gather, gdn_tree_verify, gdn_tree_commit,
-    and the fused steady-state step: conv_ancestry_gather_publish,
-    gdn_tree_commit_verify
+    the fused steady-state step: conv_ancestry_gather_publish,
+    gdn_tree_commit_verify; and one launch per layer: gdn_path_resolve (once
+    per step) + gdn_layer_step (once per layer)
 Helper: TreeDesc (owns the descriptor's device arrays and the C struct).
 """
 from __future__ import annotations
@@ -25,7 +26,8 @@ __all__ = [
     "GDN_DT_BF16", "GDN_DT_F32", "GDN_F_NORM_QK", "GDN_F_OUT_BF16", "GDN_F_VALU",
     "GDN_ACT_NONE", "GDN_ACT_SILU", "GdnError", "TreeDesc", "library_path", "load_library",
     "gdn_tree_desc_build", "conv_ancestry_gather", "gdn_tree_verify", "gdn_tree_commit",
-    "conv_ancestry_gather_publish", "gdn_tree_commit_verify",
+    "conv_ancestry_gather_publish", "gdn_tree_commit_verify", "gdn_path_resolve",
+    "gdn_layer_step",
 ]
 
 # values mirror include/gdn_tree.h
@@ -37,7 +39,7 @@ GDN_ACT_NONE, GDN_ACT_SILU = 0, 1
 
 EXPORTED = ("gdn_tree_desc_build", "conv_ancestry_gather", "gdn_tree_verify",
             "gdn_tree_commit", "conv_ancestry_gather_publish", "gdn_tree_commit_verify",
-            "gdn_status_string", "gdn_abi_version")
+            "gdn_path_resolve", "gdn_layer_step", "gdn_status_string", "gdn_abi_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lock = threading.Lock()
@@ -93,6 +95,12 @@ def load_library():
         lib.gdn_tree_commit_verify.argtypes = [dp, vp, vp, vp, i64, i64, vp, vp, vp, i32, vp, vp,
                                                dp, vp, vp, i32, vp, vp, i64, i64, vp, vp,
                                                i32, i32, i32, i32, i32, i32, vp, vp]
+        lib.gdn_path_resolve.restype = i32
+        lib.gdn_path_resolve.argtypes = [dp, vp, vp, i32, vp, i32, vp, vp, vp, vp]
+        lib.gdn_layer_step.restype = i32
+        lib.gdn_layer_step.argtypes = [dp, vp, vp, vp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp,
+                                       dp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                       vp, vp]
         lib.gdn_status_string.restype = ctypes.c_char_p
         lib.gdn_status_string.argtypes = [i32]
         lib.gdn_abi_version.restype = i32
@@ -286,3 +294,35 @@ def gdn_tree_commit_verify(desc: TreeDesc, q, k, v, alpha, beta, state_pool, sta
         Lmax, _ptr(k_prev), _ptr(v_prev), rs_qkp, rs_vp, _ptr(alpha_prev), _ptr(beta_prev), Hqk,
         Hv, dk, dv, _dtype_code(q), int(flags), _ptr(err), _stream(stream))
     return _check(code, "gdn_tree_commit_verify", raise_on_error)
+
+
+def gdn_path_resolve(prev: TreeDesc, path, path_len, state_idx, P: int, path_rows, path_n, err,
+                     stream=None, raise_on_error=True) -> int:
+    """Validate the previous step's accepted path (path [B, Lmax], path_len
+    [B]) against prev's tree; write its physical rows (path_rows int32 [B,
+    Lmax]) and the number of nodes each layer commits (path_n int32 [B]; -1
+    for a request whose slot is out of range or shared)."""
+    Lmax = int(path.shape[1])
+    code = load_library().gdn_path_resolve(prev.ref(), _ptr(path), _ptr(path_len), Lmax,
+                                           _ptr(state_idx), int(P), _ptr(path_rows),
+                                           _ptr(path_n), _ptr(err), _stream(stream))
+    return _check(code, "gdn_path_resolve", raise_on_error)
+
+
+def gdn_layer_step(desc: TreeDesc, x, w, bias, act: int, hist_in, hist_out, alpha, beta,
+                   state_pool, state_idx, out, prev: TreeDesc, x_prev, alpha_prev, beta_prev,
+                   path_rows, path_n, err, Hqk: int, flags: int = 0, y=None, stream=None,
+                   raise_on_error=True) -> int:
+    """One GDN layer's step in one launch: commit the previous path (resolved
+    by gdn_path_resolve) with its k/v recomputed from x_prev and hist_in,
+    write the new conv history to hist_out, convolve desc's tree (x [B, R, C],
+    channels [q | k | v]) and verify it into out [B, R, Hv, 128].  y, if
+    given, receives the conv output [B, R, C] (bf16)."""
+    P, Hv, dv, dk = (int(d) for d in state_pool.shape)
+    Lmax = int(path_rows.shape[1])
+    code = load_library().gdn_layer_step(
+        desc.ref(), _ptr(x), _ptr(w), _ptr(bias), int(act), _ptr(hist_in), _ptr(hist_out),
+        _ptr(alpha), _ptr(beta), _ptr(state_pool), P, _ptr(state_idx), _ptr(out), _ptr(y),
+        prev.ref(), _ptr(x_prev), _ptr(alpha_prev), _ptr(beta_prev), _ptr(path_rows),
+        _ptr(path_n), Lmax, int(Hqk), Hv, dk, dv, int(flags), _ptr(err), _stream(stream))
+    return _check(code, "gdn_layer_step", raise_on_error)

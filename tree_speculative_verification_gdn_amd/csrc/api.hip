@@ -36,7 +36,7 @@ int32_t check_heads(int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv, int32_t dty
 
 extern "C" {
 
-int32_t gdn_abi_version(void) { return 2; }
+int32_t gdn_abi_version(void) { return 3; }
 
 const char* gdn_status_string(int32_t status) {
     switch (status) {
@@ -197,6 +197,83 @@ int32_t gdn_tree_commit_verify(const gdn_tree_desc* d, const void* q, const void
     a.alpha_prev = alpha_prev;
     a.beta_prev = beta_prev;
     return map_launch(gdn::launch_commit_verify(*d, a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t gdn_path_resolve(const gdn_tree_desc* d_prev, const int32_t* path, const int32_t* path_len,
+                         int32_t Lmax, const int32_t* state_idx, int32_t P, int32_t* path_rows,
+                         int32_t* path_n, int32_t* err, void* stream) {
+    int32_t st = check_desc(d_prev);
+    if (st != GDN_OK) return st;
+    if (!path || !path_len || !state_idx || !path_rows || !path_n || !err || P < 1) return GDN_ERR_ARG;
+    if (Lmax < 1 || Lmax > GDN_MAX_NODES) return GDN_ERR_UNSUPPORTED;
+    return map_launch(gdn::launch_path_resolve(*d_prev, d_prev->B, path, path_len, Lmax, state_idx, P,
+                                               path_rows, path_n, err,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int32_t gdn_layer_step(const gdn_tree_desc* d, const void* x, const void* w, const float* bias,
+                       int32_t act, const void* hist_in, void* hist_out, const float* alpha,
+                       const float* beta, float* state_pool, int32_t P, const int32_t* state_idx,
+                       void* out, void* y, const gdn_tree_desc* d_prev, const void* x_prev,
+                       const float* alpha_prev, const float* beta_prev, const int32_t* path_rows,
+                       const int32_t* path_n, int32_t Lmax, int32_t Hqk, int32_t Hv, int32_t dk,
+                       int32_t dv, int32_t flags, int32_t* err, void* stream) {
+    int32_t st = check_desc(d);
+    if (st != GDN_OK) return st;
+    st = check_desc(d_prev);
+    if (st != GDN_OK) return st;
+    if (d_prev->B != d->B) return GDN_ERR_ARG;
+    st = check_heads(Hqk, Hv, dk, dv, GDN_DT_BF16);
+    if (st != GDN_OK) return st;
+    if (dk != 128 || d->N > 32) return GDN_ERR_UNSUPPORTED;
+    if (!x || !w || !alpha || !beta || !state_pool || !state_idx || !out || !x_prev ||
+        !alpha_prev || !beta_prev || !path_rows || !path_n || !err || P < 1)
+        return GDN_ERR_ARG;
+    if (Lmax < 1 || Lmax > GDN_MAX_NODES) return GDN_ERR_UNSUPPORTED;
+    if (act != GDN_ACT_NONE && act != GDN_ACT_SILU) return GDN_ERR_ARG;
+    if ((flags & ~(GDN_F_NORM_QK | GDN_F_OUT_BF16)) != 0) return GDN_ERR_ARG;
+    const int64_t C = 2 * static_cast<int64_t>(Hqk) * dk + static_cast<int64_t>(Hv) * dv;
+    if (d->W > 1) {
+        if (!hist_in || !hist_out) return GDN_ERR_ARG;
+        // the two history buffers must not overlap: both heads of a qk group
+        // read the old q/k history that one of them writes
+        const uintptr_t bytes = static_cast<uintptr_t>(P) * static_cast<uintptr_t>(d->W - 1) *
+                                static_cast<uintptr_t>(C) * 2u;
+        const uintptr_t i0 = reinterpret_cast<uintptr_t>(hist_in), o0 = reinterpret_cast<uintptr_t>(hist_out);
+        if (i0 < o0 + bytes && o0 < i0 + bytes) return GDN_ERR_ARG;
+        if (!aligned(hist_in, 16) || !aligned(hist_out, 16)) return GDN_ERR_ARG;
+    } else {
+        hist_in = nullptr;
+        hist_out = nullptr;
+    }
+    if (!aligned(x, 16) || !aligned(x_prev, 16) || !aligned(state_pool, 16) || (y && !aligned(y, 8)))
+        return GDN_ERR_ARG;
+    gdn::LayerArgs a{};
+    a.x = static_cast<const uint16_t*>(x);
+    a.w = static_cast<const uint16_t*>(w);
+    a.bias = bias;
+    a.act = act;
+    a.hist_in = static_cast<const uint16_t*>(hist_in);
+    a.hist_out = static_cast<uint16_t*>(hist_out);
+    a.alpha = alpha;
+    a.beta = beta;
+    a.pool = state_pool;
+    a.P = P;
+    a.state_idx = state_idx;
+    a.out = out;
+    a.y = static_cast<uint16_t*>(y);
+    a.prev = d_prev;
+    a.x_prev = static_cast<const uint16_t*>(x_prev);
+    a.alpha_prev = alpha_prev;
+    a.beta_prev = beta_prev;
+    a.path_rows = path_rows;
+    a.path_n = path_n;
+    a.Lmax = Lmax;
+    a.Hqk = Hqk;
+    a.Hv = Hv;
+    a.flags = flags;
+    a.err = err;
+    return map_launch(gdn::launch_layer_step(*d, a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -14,6 +14,7 @@
 // tile, the W-1 history entries and the weights, all in flight together.
 // Node rows are kept in LDS, so an x element is read from HBM once however
 // many descendants tap it.  HBM-bound: x (node rows), hist, y.
+#include "conv_math.h"
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -52,24 +53,6 @@ __device__ __forceinline__ void unpack(const Chunk<CPT>& c, float* f) {
     }
 }
 }  // namespace
-
-__device__ __forceinline__ float silu(float z) {
-    // z * sigmoid(z) on the hardware exp2 and reciprocal (about 1 ulp each,
-    // far below the bf16 rounding that follows); the exponential is taken of
-    // a non-positive argument, so it never overflows
-    const float e = __builtin_amdgcn_exp2f(-fabsf(z) * 1.4426950408889634f);
-    const float r = __builtin_amdgcn_rcpf(1.f + e);
-    return z * ((z >= 0.f) ? r : e * r);
-}
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
-// two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    const bf16x2_t h = __builtin_convertvector((f32x2_t){a, b}, bf16x2_t);
-    return __builtin_bit_cast(uint32_t, h);
-}
 
 // Kernel arguments (by value).  The previous-step fields are read only by
 // the publishing variant.
@@ -333,25 +316,16 @@ __global__ void __launch_bounds__(kConvThreads) conv_gather_kernel(const ConvKAr
         float z[CPT];
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
-            const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;  // halves c % 2 of two words
-            float acc = 0.0f;
+            uint32_t tw[W];
 #pragma unroll
-            for (int q = 0; q < kWP; ++q) {
-                const uint32_t lo = xw[2 * q][c >> 1];
-                const uint32_t hi = (2 * q + 1 < W) ? xw[2 * q + 1][c >> 1] : 0u;
-                const uint32_t xp = __builtin_amdgcn_perm(hi, lo, sel);
-                acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, xp),
-                                                      __builtin_bit_cast(bf16x2_t, wr[c * kWP + q]), acc,
-                                                      false);
-            }
-            if (bias) acc += s_b[lane * CPT + c];
-            if (act == GDN_ACT_SILU) acc = silu(acc);
-            z[c] = acc;
+            for (int t = 0; t < W; ++t) tw[t] = xw[t][c >> 1];
+            z[c] = conv_channel<W>(tw, c & 1, &wr[c * kWP], bias != nullptr,
+                                   bias ? s_b[lane * CPT + c] : 0.0f, act);
         }
         Chunk<CPT> o;
         uint32_t* ow = reinterpret_cast<uint32_t*>(&o.u);
 #pragma unroll
-        for (int e = 0; e < CPT / 2; ++e) ow[e] = pack_bf16x2(z[2 * e], z[2 * e + 1]);
+        for (int e = 0; e < CPT / 2; ++e) ow[e] = conv_pack_bf16x2(z[2 * e], z[2 * e + 1]);
         *reinterpret_cast<decltype(o.u)*>(y + (xb + s_row[i]) * C + c0) = o.u;
     }
 }

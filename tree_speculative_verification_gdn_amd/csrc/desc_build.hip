@@ -83,4 +83,58 @@ hipError_t launch_desc_build(const gdn_tree_desc& d, int32_t* err, hipStream_t s
     return hipGetLastError();
 }
 
+// Previous step's accepted path, once per step for every layer (LumoTree,
+// Sec. V-A: one device-produced path drives every publication).  One wave
+// per request, lane j holds path entry j (Lmax <= 64).  The path must be a
+// parent chain from a node whose parent is -1 (the same checks the commit
+// makes); its rows are the previous tree's node_row of each entry.
+__global__ void __launch_bounds__(64) path_resolve_kernel(
+    int B, int Np, int shared_p, int Lmax, const int32_t* __restrict__ parent_p,
+    const int32_t* __restrict__ node_row_p, const int32_t* __restrict__ status_p,
+    const int32_t* __restrict__ path, const int32_t* __restrict__ path_len,
+    const int32_t* __restrict__ state_idx, int P, int32_t* __restrict__ path_rows,
+    int32_t* __restrict__ path_n, int32_t* __restrict__ err) {
+    const int b = blockIdx.x;
+    const int j = threadIdx.x;
+    const int tp = shared_p ? 0 : b;
+    const int st_p = status_p[tp];
+    const int len = path_len[b];
+    const int slot = state_idx[b];
+    int dup = 0;
+    for (int b2 = j; b2 < B; b2 += 64) dup |= (b2 != b && state_idx[b2] == slot) ? 1 : 0;
+    const int node = path[static_cast<size_t>(b) * Lmax + min(j, Lmax - 1)];
+    const int prev_node = __shfl(node, j > 0 ? j - 1 : 0, 64);
+    const size_t ti = static_cast<size_t>(tp) * Np + min(max(node, 0), Np - 1);
+    const int par = parent_p[ti];
+    const int row = node_row_p[ti];
+    const bool len_ok = len >= 0 && len <= Lmax;
+    const bool bad_j = len_ok && j < len && (node < 0 || node >= Np || par != (j == 0 ? -1 : prev_node));
+    const bool bad = __ballot(bad_j) != 0ull;
+    const bool any_dup = __ballot(dup != 0) != 0ull;
+    const bool slot_bad = slot < 0 || slot >= P || any_dup;
+    const bool path_bad = !len_ok || bad;
+    if (j == 0) {
+        int n, ev = 0;
+        if (slot_bad) {
+            n = -1;
+            ev |= GDN_EV_STATE;
+        } else {
+            n = (st_p != 0 || path_bad) ? 0 : len;
+        }
+        if (st_p == 0 && path_bad) ev |= GDN_EV_PATH;  // a malformed tree is its own build's error
+        path_n[b] = n;
+        if (ev) atomicOr(err, ev);
+    }
+    if (st_p == 0 && !path_bad && j < len) path_rows[static_cast<size_t>(b) * Lmax + j] = row;
+}
+
+hipError_t launch_path_resolve(const gdn_tree_desc& prev, int B, const int32_t* path,
+                               const int32_t* path_len, int Lmax, const int32_t* state_idx, int P,
+                               int32_t* path_rows, int32_t* path_n, int32_t* err, hipStream_t s) {
+    hipLaunchKernelGGL(path_resolve_kernel, dim3(B), dim3(64), 0, s, B, prev.N, prev.shared, Lmax,
+                       prev.parent, prev.node_row, prev.status, path, path_len, state_idx, P,
+                       path_rows, path_n, err);
+    return hipGetLastError();
+}
+
 }  // namespace gdn

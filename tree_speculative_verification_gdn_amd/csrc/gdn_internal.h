@@ -125,4 +125,38 @@ struct CommitVerifyArgs {
 };
 hipError_t launch_commit_verify(const gdn_tree_desc& d, const CommitVerifyArgs& a, hipStream_t s);
 
+// One launch per layer and step: commit of the previous path (its k/v
+// recomputed from its conv input), conv-history publication, conv and verify
+// of the new tree (bf16, d = 128, N <= 32).
+struct LayerArgs {
+    const uint16_t* x;
+    const uint16_t* w;
+    const float* bias;
+    int act;
+    const uint16_t* hist_in;
+    uint16_t* hist_out;
+    const float* alpha;
+    const float* beta;
+    float* pool;
+    int P;
+    const int32_t* state_idx;
+    void* out;
+    uint16_t* y;
+    const gdn_tree_desc* prev;
+    const uint16_t* x_prev;
+    const float* alpha_prev;
+    const float* beta_prev;
+    const int32_t* path_rows;
+    const int32_t* path_n;
+    int Lmax;
+    int Hqk, Hv, flags;
+    int32_t* err;
+};
+hipError_t launch_layer_step(const gdn_tree_desc& d, const LayerArgs& a, hipStream_t s);
+
+// Validation of the previous step's path and its physical rows, once per step.
+hipError_t launch_path_resolve(const gdn_tree_desc& prev, int B, const int32_t* path,
+                               const int32_t* path_len, int Lmax, const int32_t* state_idx, int P,
+                               int32_t* path_rows, int32_t* path_n, int32_t* err, hipStream_t s);
+
 }  // namespace gdn

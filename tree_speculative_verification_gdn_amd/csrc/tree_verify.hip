@@ -33,6 +33,7 @@
 // Work decomposition: one 256-thread workgroup per (request, value head); the
 // two value heads that share a qk head are placed on the same XCD so their
 // K/Q rows are read from HBM once.
+#include "conv_math.h"
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -61,6 +62,9 @@ struct MfmaLds {
     // layout), v rows, gates, k scales, rows; placed over the Gram block when
     // it fits (the Gram block is dead by the time the path is staged)
     int kp, vp, alp, bep, scp, rowp;
+    // one-launch layer step: conv staging (tree, path), conv weights and
+    // bias, tap rows, parents, and the staging of a later path segment's conv
+    int xg, pc, wts, bia, tap, par, stg, sw, sb;
 };
 
 __host__ __device__ inline int align_up(int x, int a) { return (x + a - 1) / a * a; }
@@ -109,6 +113,65 @@ __host__ __device__ inline MfmaLds mfma_lds_layout(int N, int NPB, int Lp = 0) {
     return L;
 }
 
+
+__host__ __device__ inline int imax(int a, int b) { return a > b ? a : b; }
+
+// Layer step (N <= 32, one 32-row block).  One region F is used in turn by
+// (1) the v rows and the new history of the tree's conv, (2) the verify
+// stages up to the M solve, (3) the replay of one path segment (and the
+// staging of a later segment's conv); each set is dead before the next is
+// written.  The previous path's conv rows sit in the key block until the
+// key conv writes it; the conv weights and bias overlay the M halves,
+// written only after the conv.
+__host__ __device__ inline MfmaLds layer_lds_layout(int N, int H, int Lmax) {
+    MfmaLds L{};
+    constexpr int NP = 32;
+    int off = 0;
+    L.mstride = NP * 2 + 8;
+    L.a = off;    off += align_up(2 * 32 * kKQStride, 16);
+    L.v = off;    off += align_up(N * kD * 2, 16);
+    const int F = off;
+    int f = F;
+    L.gk = f;   f += align_up(NP * NP * 4, 16);
+    L.gq = f;   f += align_up(NP * NP * 4, 16);
+    L.nrm = f;  f += align_up(2 * NP * 4, 16);
+    L.sk = f;   f += align_up(N * 4, 16);
+    L.sq = f;   f += align_up(N * 4, 16);
+    L.cidx = f; f += align_up(N * N, 16);
+    int fend = f;
+    L.xg = F;   // v rows of the tree (N x 256 bytes), then the new history [3][H][256]
+    fend = imax(fend, F + align_up((N + 3 * H) * 256, 16));
+    L.pc = L.a; // (history ++ path) rows of the first segment's windows, k | v: 512 bytes
+    f = F;
+    L.kp = f;   f += align_up(kMfmaPath * kKQStride, 16);
+    L.vp = f;   f += align_up(kMfmaPath * kD * 2, 16);
+    L.scp = f;  f += align_up((kMfmaPath + kMfmaPath * kMfmaPath) * 4, 16);
+    L.stg = f;  f += align_up((H + 8) * 256, 16);
+    L.sw = f;   f += align_up(256 * 4, 16);
+    L.sb = f;   f += align_up(kD * 4, 16);
+    fend = imax(fend, f);
+    off = fend;
+    L.be = off;   off += align_up((N + 1) * 4, 16);
+    L.rows = off; off += align_up((N + 1) * 4, 16);
+    L.al = off;   off += align_up((N + 1) * 4, 16);
+    L.dep = off;  off += align_up((N + 1) * 4, 16);
+    L.anc = off;  off += align_up((N + 1) * 8, 16);
+    L.mh = off;
+    L.ml = off + align_up(NP * L.mstride, 16);
+    L.wts = off;                 // [3][256] tap-pair words: k, q, v
+    L.bia = off + 3 * 256 * 4;   // [3][128]
+    off += imax(2 * align_up(NP * L.mstride, 16), 3 * 256 * 4 + 3 * kD * 4);
+    L.cr = off;   off += align_up(N * 4, 16);
+    L.cq = off;   off += align_up(N * 4, 16);
+    L.alp = off;  off += align_up((Lmax + 1) * 4, 16);
+    L.bep = off;  off += align_up((Lmax + 1) * 4, 16);
+    L.tap = off;  off += align_up(N * (H > 0 ? H : 1), 16);
+    L.par = off;  off += align_up((N + 1) * 4, 16);
+    L.rowp = off; off += align_up((Lmax + 1) * 4, 16);
+    L.total = off;
+    return L;
+}
+
 // The previous step's accepted path for the fused commit (kernel argument).
 struct CommitPrev {
     int B, Np, Rp, shared_p, Lmax;
@@ -123,6 +186,66 @@ struct CommitPrev {
     const float* alpha_p;
     const float* beta_p;
 };
+
+// Layer-step inputs (kernel argument): the conv input and weights, the
+// history buffers, and the previous step's path as resolved rows.
+struct LayerIn {
+    int C, act, Rp, Lmax;
+    const uint16_t* x;
+    const uint16_t* w;
+    const float* bias;
+    const uint16_t* hist_in;
+    uint16_t* hist_out;
+    uint16_t* y;
+    const uint16_t* x_prev;
+    const float* alpha_p;
+    const float* beta_p;
+    const int32_t* path_rows;
+    const int32_t* path_n;
+    const int32_t* parent;
+};
+
+constexpr int kModeVerify = 0;
+constexpr int kModeCommitVerify = 1;
+constexpr int kModeLayer = 2;      // paths of at most kMfmaPath nodes (Lmax <= kMfmaPath)
+constexpr int kModeLayerLong = 3;  // any Lmax: later path segments convolved inside the replay
+
+// Conv weights of channel cb + c as tap pairs: word (c * kWP + p) of a
+// 128-channel group holds (w[2p], w[2p+1] or 0); thread tid builds word tid.
+template <int W>
+__device__ __forceinline__ uint32_t conv_weight_word(const uint16_t* w, int cb, int tid) {
+    constexpr int kWP = (W + 1) / 2;
+    const int c = min(tid / kWP, kD - 1);
+    const int p = tid % kWP;
+    const uint16_t* row = w + static_cast<size_t>(cb + c) * W;
+    const uint32_t lo = row[2 * p];
+    const uint32_t hi = row[min(2 * p + 1, W - 1)];
+    return lo | ((2 * p + 1 < W ? hi : 0u) << 16);
+}
+
+// Conv of 4 channels (8-byte chunk `chunk` of each row) for one node whose
+// window rows, oldest first and the node itself last, start at rp[t].
+template <int W>
+__device__ __forceinline__ uint2 conv4_rows(const char* const (&rp)[W], int chunk, const uint32_t* wv,
+                                            const float* bb, bool has_bias, int act) {
+    constexpr int kWP = (W + 1) / 2;
+    uint32_t xw[W][2];
+#pragma unroll
+    for (int t = 0; t < W; ++t) {
+        const uint2 c2 = *reinterpret_cast<const uint2*>(rp[t] + chunk * 8);
+        xw[t][0] = c2.x;
+        xw[t][1] = c2.y;
+    }
+    float z[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        uint32_t tw[W];
+#pragma unroll
+        for (int t = 0; t < W; ++t) tw[t] = xw[t][e >> 1];
+        z[e] = conv_channel<W>(tw, e & 1, wv + e * kWP, has_bias, bb[e], act);
+    }
+    return make_uint2(conv_pack_bf16x2(z[0], z[1]), conv_pack_bf16x2(z[2], z[3]));
+}
 
 // MFMA operand: 8 bf16 of one 128-element LDS row for k-step s and lane half
 // hf.  Slot e of the operand holds element 16s + 4hf + e (e < 4) or
@@ -198,7 +321,7 @@ __device__ __forceinline__ bf16x8_t lds_operand_m(const char* base, int stride, 
     return __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
-template <int NPB, bool FUSED>
+template <int NPB, int MODE, int CW>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NPB == 1 ? 4 : 2, 8)))
     verify_mfma_kernel(int N, int R, int shared, const int32_t* __restrict__ node_row,
                        const uint64_t* __restrict__ anc_g, const int32_t* __restrict__ depth_g,
@@ -208,13 +331,20 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                        const float* __restrict__ beta, float* __restrict__ pool, int P,
                        const int32_t* __restrict__ state_idx, void* __restrict__ out, int Hqk,
                        int Hv, int norm, int out_bf16, int32_t* __restrict__ err,
-                       const CommitPrev cp) {
+                       const CommitPrev cp, const LayerIn li) {
+    constexpr bool FUSED = MODE == kModeCommitVerify;  // commit of a path given as k/v rows
+    constexpr bool LAYER = MODE == kModeLayer || MODE == kModeLayerLong;  // the whole layer step
+    constexpr bool LONGP = MODE == kModeLayerLong;
+    constexpr bool COMMIT = FUSED || LAYER;
+    constexpr int H = CW > 0 ? CW - 1 : 0;             // conv history entries (layer step)
+    constexpr int kWP = (CW + 1) / 2;                  // conv tap pairs per channel
+    static_assert(!LAYER || (NPB == 1 && CW >= 1 && CW <= 4), "layer step: N <= 32, 1 <= W <= 4");
     constexpr int NP = 32 * NPB;
     constexpr int MB = 2 * NPB;                              // key blocks, then query blocks
     constexpr int kKQItems = MB * 32 * 32 / kThreads;       // 8-byte K/Q chunks per thread
     constexpr int kVItems = (NP * 32 + kThreads - 1) / kThreads;
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    const MfmaLds L = mfma_lds_layout(N, NPB, FUSED ? cp.Lmax : 0);
+    const MfmaLds L = LAYER ? layer_lds_layout(N, H, li.Lmax) : mfma_lds_layout(N, NPB, FUSED ? cp.Lmax : 0);
     char* s_a = lds + L.a;
     uint16_t* s_v = reinterpret_cast<uint16_t*>(lds + L.v);
     float* s_gk = reinterpret_cast<float*>(lds + L.gk);
@@ -249,6 +379,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     const int g = static_cast<int>((static_cast<int64_t>(h) * Hqk) / Hv);
     const size_t tb = static_cast<size_t>(t) * N;
     const size_t rowb = static_cast<size_t>(b) * R;
+    // layer step: this unit's q and k (qk head g) and v (head h) channels in
+    // the conv input, order [q | k | v], head-major
+    const int cq0 = g * kD, ck0 = Hqk * kD + g * kD, cv0 = 2 * Hqk * kD + h * kD;
+    const uint16_t* kbase = LAYER ? li.x + ck0 : k + static_cast<size_t>(g) * kD;
+    const uint16_t* qbase = LAYER ? li.x + cq0 : q + static_cast<size_t>(g) * kD;
+    const uint16_t* vbase = LAYER ? li.x + cv0 : v + static_cast<size_t>(h) * kD;
+    const int64_t rsq = LAYER ? static_cast<int64_t>(li.C) : rs_qk;
+    const int64_t rsv = LAYER ? static_cast<int64_t>(li.C) : rs_v;
 
     // (a) Memory, in three waves of loads.  A wave's vector loads retire in
     //     issue order, so the K/Q/V rows go out before the 64 KiB state: the
@@ -281,14 +419,63 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
         for (int b2 = tid + kThreads; b2 < cp.B; b2 += kThreads)  // B > 256 only
             dup |= (b2 != b && state_idx[b2] == slot) ? 1 : 0;
     }
+    //   (a1'') layer step: the resolved path, the tree's parents (conv taps),
+    //   the conv weights (as tap pairs) and bias of the unit's channels
+    int pn = 0, prow = 0, my_par = -1;
+    uint32_t wq[3] = {0u, 0u, 0u};
+    float bq[3] = {0.f, 0.f, 0.f};
+    if constexpr (LAYER) {
+        pn = li.path_n[b];
+        prow = li.path_rows[static_cast<size_t>(b) * li.Lmax + min(tid, li.Lmax - 1)];
+        my_par = li.parent[tb + my_node];
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {  // groups k, q, v
+            const int cb = u == 0 ? ck0 : (u == 1 ? cq0 : cv0);
+            wq[u] = conv_weight_word<CW>(li.w, cb, tid);
+            if (li.bias) bq[u] = li.bias[cb + (tid & (kD - 1))];
+        }
+    }
     if (slot < 0 || slot >= P) {
-        if ((FUSED || st == 0) && h == 0 && tid == 0) atomicOr(err, GDN_EV_STATE);
+        if ((COMMIT || st == 0) && h == 0 && tid == 0) atomicOr(err, GDN_EV_STATE);
         return;
     }
     // the new tree is verified only if it is well formed; the fused commit of
     // the previous path happens either way
     const bool vok = st == 0;
-    if (!FUSED && !vok) return;
+    if (!COMMIT && !vok) return;
+    float* s_alp = reinterpret_cast<float*>(lds + L.alp);
+    float* s_bep = reinterpret_cast<float*>(lds + L.bep);
+    float* s_scp = reinterpret_cast<float*>(lds + L.scp);
+    int32_t* s_rowp = reinterpret_cast<int32_t*>(lds + L.rowp);
+    char* s_kp = lds + L.kp;
+    uint16_t* s_vp = reinterpret_cast<uint16_t*>(lds + L.vp);
+    uint32_t* s_wts = reinterpret_cast<uint32_t*>(lds + L.wts);
+    float* s_bia = reinterpret_cast<float*>(lds + L.bia);
+    int32_t* s_par = reinterpret_cast<int32_t*>(lds + L.par);
+    uint8_t* s_tap = reinterpret_cast<uint8_t*>(lds + L.tap);
+    // layer step: n = -1 writes neither state nor history; nc path nodes commit
+    const int n_res = LAYER ? min(max(pn, -1), li.Lmax) : 0;
+    const int nc = n_res > 0 ? n_res : 0;
+    if constexpr (LAYER) {
+        // every lane writes (spare entries Lmax and N)
+        s_rowp[min(tid, li.Lmax)] = prow;
+        s_par[min(tid, N)] = my_par;
+        s_rows[min(tid, N)] = my_row;
+        s_anc[min(tid, N)] = my_anc;
+        s_dep[min(tid, N)] = my_dep;
+#pragma unroll
+        for (int u = 0; u < 3; ++u) s_wts[u * kThreads + tid] = wq[u];
+        if (li.bias) {
+#pragma unroll
+            for (int u = 0; u < 3; ++u) s_bia[u * kD + (tid & (kD - 1))] = bq[u];
+        }
+        __syncthreads();
+    }
+    // physical row of path node j of the previous tree, clamped into range
+    auto prow_at = [&](int j) -> int {
+        const int r = s_rowp[min(max(j, 0), li.Lmax - 1)];
+        return min(max(r, 0), li.Rp - 1);
+    };
     //   (a2) K/Q/V chunks and the gates of every node (rows of a valid tree are
     //        in range, so the clamped loads are too)
     static_assert(kKQItems == 2 * kSlots && kVItems == kSlots, "item u uses node slot u mod kSlots");
@@ -299,17 +486,49 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
 #pragma unroll
         for (int u = 0; u < kKQItems; ++u) {
             const int sl = (tid + u * kThreads) >> 5;
-            const uint16_t* src = (sl < NP ? k : q) + (rowb + nrow[u % kSlots]) * rs_qk +
-                                  static_cast<size_t>(g) * kD + (tid & 31) * 4;
+            const uint16_t* src = (sl < NP ? kbase : qbase) + (rowb + nrow[u % kSlots]) * rsq + (tid & 31) * 4;
             kq_val[u] = *reinterpret_cast<const uint2*>(src);
         }
 #pragma unroll
         for (int u = 0; u < kVItems; ++u)
-            v_val[u] = *reinterpret_cast<const uint2*>(v + (rowb + nrow[u]) * rs_v +
-                                                       static_cast<size_t>(h) * kD + (tid & 31) * 4);
+            v_val[u] = *reinterpret_cast<const uint2*>(vbase + (rowb + nrow[u]) * rsv + (tid & 31) * 4);
         const size_t my_gi = (rowb + my_row) * Hv + h;
         my_al = alpha[my_gi];
         my_be = beta[my_gi];
+    }
+    //   (a2'') layer step: the previous path's conv input -- the old history
+    //   and the path's rows as the rows (history ++ path) of its first
+    //   segment's windows, k | v channels, plus the q channels of the new
+    //   history -- and the path's gates
+    constexpr int kPC = (H + 8) * 32;  // 16-byte items: H + 8 rows x (k | v)
+    constexpr int kNH = H * 16;        // 16-byte items: H rows x q
+    constexpr int kPItems = LAYER ? (kPC + kNH + kThreads - 1) / kThreads : 1;
+    uint4 pc_val[kPItems];
+    uint4 nh_kv = make_uint4(0u, 0u, 0u, 0u);
+    uint2 pk_val = make_uint2(0u, 0u), pv_val = make_uint2(0u, 0u);
+    float p_al = 0.f, p_be = 0.f;
+    if constexpr (LAYER) {
+#pragma unroll
+        for (int u = 0; u < kPItems; ++u) {
+            const int it = min(tid + u * kThreads, kPC + kNH - 1);
+            int ci, col;  // row of (history ++ path) and channel
+            if (it < kPC) {
+                const int c16 = it & 31;
+                ci = it >> 5;
+                col = c16 < 16 ? ck0 + 8 * c16 : cv0 + 8 * (c16 - 16);
+            } else {
+                ci = nc + ((it - kPC) >> 4);
+                col = cq0 + 8 * ((it - kPC) & 15);
+            }
+            const uint16_t* src = li.x_prev + (static_cast<size_t>(b) * li.Rp + prow_at(ci - H)) * li.C + col;
+            if constexpr (H > 0) {
+                if (ci < H) src = li.hist_in + (static_cast<size_t>(slot) * H + ci) * li.C + col;
+            }
+            pc_val[u] = *reinterpret_cast<const uint4*>(src);
+        }
+        const size_t gi = (static_cast<size_t>(b) * li.Rp + prow_at(min(tid, nc - 1))) * Hv + h;
+        p_al = li.alpha_p[gi];
+        p_be = li.beta_p[gi];
     }
     //   (a2') fused: parents and rows of the previous path's nodes
     int ppar = 0, pprow = 0;
@@ -333,14 +552,6 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     // a parent chain from a root-level node of the previous tree, a slot no
     // other request shares), then load its k/v rows and gates
     bool cok = false;
-    uint2 pk_val = make_uint2(0u, 0u), pv_val = make_uint2(0u, 0u);
-    float p_al = 0.f, p_be = 0.f;
-    float* s_alp = reinterpret_cast<float*>(lds + L.alp);
-    float* s_bep = reinterpret_cast<float*>(lds + L.bep);
-    float* s_scp = reinterpret_cast<float*>(lds + L.scp);
-    int32_t* s_rowp = reinterpret_cast<int32_t*>(lds + L.rowp);
-    char* s_kp = lds + L.kp;
-    uint16_t* s_vp = reinterpret_cast<uint16_t*>(lds + L.vp);
     if constexpr (FUSED) {
         __shared__ int s_bad;
         if (tid == 0) s_bad = 0;
@@ -373,12 +584,207 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
         }
     }
 
+    // layer step: publish the new conv history, convolve the previous path's
+    // first segment into k/v chunks held in registers and the new tree into
+    // the K/Q/V rows (LumoTree, Sec. V-A: the accepted path's conv rows
+    // become the history; Sec. V-C: each window follows the node's ancestry,
+    // then the history)
+    if constexpr (LAYER) {
+        // the loads above are used under per-lane conditions below: take
+        // delivery here (the state, issued after them, stays in flight)
+#pragma unroll
+        for (int u = 0; u < kPItems; ++u)
+            asm volatile("" ::"v"(pc_val[u].x), "v"(pc_val[u].y), "v"(pc_val[u].z), "v"(pc_val[u].w));
+        asm volatile("" ::"v"(p_al), "v"(p_be));
+        if (LONGP && H > 0 && nc > kMfmaPath) {  // uniform: the new history lies past the first segment
+            // (paths longer than one segment only: this waits for the state too)
+            const int e = min(tid, H * 32 - 1);
+            const int c16 = e & 31;
+            const int col = c16 < 16 ? ck0 + 8 * c16 : cv0 + 8 * (c16 - 16);
+            nh_kv = *reinterpret_cast<const uint4*>(
+                li.x_prev + (static_cast<size_t>(b) * li.Rp + prow_at(nc - H + (e >> 5))) * li.C + col);
+        }
+#pragma unroll
+        for (int u = 0; u < kKQItems; ++u) asm volatile("" ::"v"(kq_val[u].x), "v"(kq_val[u].y));
+#pragma unroll
+        for (int u = 0; u < kVItems; ++u) asm volatile("" ::"v"(v_val[u].x), "v"(v_val[u].y));
+        const bool qk_writer = (h % (Hv / Hqk)) == 0;  // one head per qk group writes q/k channels
+        const bool has_bias = li.bias != nullptr;
+        // stage everything in LDS at once.  Each conv group's output
+        // overwrites only input already used: the path's rows in the key
+        // block (the path conv runs first), k rows in the query block, q rows
+        // in the V rows, v rows and the new history (groups k, q, v) in F
+        char* xk = s_a + NP * kKQStride;
+        char* xq = reinterpret_cast<char*>(s_v);
+        char* xv = lds + L.xg;
+        char* hg = xv + N * 256;
+        const int nl = tid >> 5;
+        const int c4 = tid & 31;
+        if (nc > 0) {  // uniform
+            // the path's gates (nc <= Lmax <= 64: wave 0; spare entry Lmax)
+            s_alp[min(tid, li.Lmax)] = p_al;
+            s_bep[min(tid, li.Lmax)] = p_be;
+            uint4* s_pc = reinterpret_cast<uint4*>(lds + L.pc);  // [H + 8][32]: k half, v half
+#pragma unroll
+            for (int u = 0; u < kPItems; ++u) {
+                const int it = tid + u * kThreads;
+                if (it < kPC) s_pc[it] = pc_val[u];
+            }
+        }
+        if (vok) {  // uniform
+            {
+                const int slot_i = tid < N ? tid : N;  // lanes past N write the spare entry
+                s_al[slot_i] = my_al;
+                s_be[slot_i] = my_be;
+            }
+#pragma unroll
+            for (int u = 0; u < kSlots; ++u) {
+                const int node = nl + 8 * u;
+                if (node < N) {
+                    *reinterpret_cast<uint2*>(xk + node * 256 + c4 * 8) = kq_val[u];
+                    *reinterpret_cast<uint2*>(xq + node * 256 + c4 * 8) = kq_val[kSlots + u];
+                    *reinterpret_cast<uint2*>(xv + node * 256 + c4 * 8) = v_val[u];
+                }
+            }
+            if constexpr (H > 0) {
+#pragma unroll
+                for (int u = 0; u < kPItems; ++u) {
+                    const int it = tid + u * kThreads;
+                    if (it < kPC) {
+                        const int c16 = it & 31;
+                        const int m = (it >> 5) - nc;
+                        if ((!LONGP || nc <= kMfmaPath) && m >= 0 && m < H)
+                            *reinterpret_cast<uint4*>(hg + ((c16 < 16 ? 0 : 2) * H + m) * 256 + (c16 & 15) * 16) =
+                                pc_val[u];
+                    } else if (it < kPC + kNH) {
+                        const int e = it - kPC;
+                        *reinterpret_cast<uint4*>(hg + (H + (e >> 4)) * 256 + (e & 15) * 16) = pc_val[u];
+                    }
+                }
+                if (LONGP && nc > kMfmaPath && tid < H * 32) {
+                    const int c16 = tid & 31;
+                    *reinterpret_cast<uint4*>(hg + ((c16 < 16 ? 0 : 2) * H + (tid >> 5)) * 256 + (c16 & 15) * 16) =
+                        nh_kv;
+                }
+                // the new tree's conv taps as staged rows: node j < N, or
+                // history entry s at N + s (s = W-2 the most recent); oldest first
+                if (tid < N) {
+                    int cur = s_par[tid];
+                    int hs = H - 1;
+#pragma unroll
+                    for (int m = 0; m < H; ++m) {
+                        int tap;
+                        if (cur >= 0) {
+                            tap = cur;
+                            cur = s_par[cur];
+                        } else {
+                            tap = N + hs;
+                            --hs;
+                        }
+                        s_tap[tid * H + (H - 1 - m)] = static_cast<uint8_t>(tap);
+                    }
+                }
+            }
+        }
+        // publish: new history entry m = (old history ++ path rows)[nc + m]
+        if constexpr (H > 0) {
+            if (n_res >= 0) {  // uniform
+                uint16_t* ho = li.hist_out + static_cast<size_t>(slot) * H * li.C;
+#pragma unroll
+                for (int u = 0; u < kPItems; ++u) {
+                    const int it = tid + u * kThreads;
+                    int m = 0, col = 0;
+                    bool wr = false;
+                    if (it < kPC) {
+                        const int c16 = it & 31;
+                        m = (it >> 5) - nc;
+                        col = c16 < 16 ? ck0 + 8 * c16 : cv0 + 8 * (c16 - 16);
+                        wr = (!LONGP || nc <= kMfmaPath) && m >= 0 && m < H && (c16 >= 16 || qk_writer);
+                    } else if (it < kPC + kNH) {
+                        m = (it - kPC) >> 4;
+                        col = cq0 + 8 * ((it - kPC) & 15);
+                        wr = qk_writer;
+                    }
+                    if (wr) *reinterpret_cast<uint4*>(ho + static_cast<size_t>(m) * li.C + col) = pc_val[u];
+                }
+                if (LONGP && nc > kMfmaPath && tid < H * 32) {
+                    const int c16 = tid & 31;
+                    const int col = c16 < 16 ? ck0 + 8 * c16 : cv0 + 8 * (c16 - 16);
+                    if (c16 >= 16 || qk_writer)
+                        *reinterpret_cast<uint4*>(ho + static_cast<size_t>(tid >> 5) * li.C + col) = nh_kv;
+                }
+            }
+        }
+        __syncthreads();
+        if (nc > 0) {  // uniform: the previous path's first segment, k and v channels
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int grp = half == 0 ? 0 : 2;
+                uint32_t wv[4 * kWP];
+#pragma unroll
+                for (int e = 0; e < 4 * kWP; ++e) wv[e] = s_wts[grp * kThreads + 4 * c4 * kWP + e];
+                float bb[4] = {0.f, 0.f, 0.f, 0.f};
+                if (has_bias) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) bb[e] = s_bia[grp * kD + 4 * c4 + e];
+                }
+                const char* rp[CW];
+#pragma unroll
+                for (int t = 0; t <= H; ++t) rp[t] = lds + L.pc + (nl + t) * 512 + half * 256;
+                const uint2 o = conv4_rows<CW>(rp, c4, wv, bb, has_bias, li.act);
+                if (half == 0)
+                    pk_val = o;
+                else
+                    pv_val = o;
+            }
+            __syncthreads();
+        }
+        if (vok) {  // uniform: the new tree's conv, groups k, q, v
+#pragma unroll
+            for (int grp = 0; grp < 3; ++grp) {
+                const char* src = grp == 0 ? xk : (grp == 1 ? xq : xv);
+                const int cb = grp == 0 ? ck0 : (grp == 1 ? cq0 : cv0);
+                uint32_t wv[4 * kWP];
+#pragma unroll
+                for (int e = 0; e < 4 * kWP; ++e) wv[e] = s_wts[grp * kThreads + 4 * c4 * kWP + e];
+                float bb[4] = {0.f, 0.f, 0.f, 0.f};
+                if (has_bias) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) bb[e] = s_bia[grp * kD + 4 * c4 + e];
+                }
+#pragma unroll 2
+                for (int x = 0; x < kSlots; ++x) {
+                    const int i = nl + 8 * x;
+                    if (i < N) {
+                        const char* rp[CW];
+#pragma unroll
+                        for (int t = 0; t < H; ++t) {
+                            const int r = s_tap[i * H + t];
+                            rp[t] = r < N ? src + r * 256 : hg + (grp * H + r - N) * 256;
+                        }
+                        rp[H] = src + i * 256;
+                        const uint2 o = conv4_rows<CW>(rp, c4, wv, bb, has_bias, li.act);
+                        char* dst = grp == 2 ? reinterpret_cast<char*>(s_v) + i * (kD * 2)
+                                             : s_a + (grp == 1 ? NP + i : i) * kKQStride;
+                        *reinterpret_cast<uint2*>(dst + c4 * 8) = o;
+                        if (li.y && (grp == 2 || qk_writer))
+                            *reinterpret_cast<uint2*>(li.y + (rowb + s_rows[i]) * li.C + cb + 4 * c4) = o;
+                    } else if (grp < 2) {  // zero pad rows of the MFMA blocks
+                        *reinterpret_cast<uint2*>(s_a + (grp == 1 ? NP + i : i) * kKQStride + c4 * 8) =
+                            make_uint2(0u, 0u);
+                    }
+                }
+                __syncthreads();
+            }
+        }
+    }
+
     if (vok) {  // uniform: stages (a)-(e) of the new tree
         // stage the metadata, K/Q (with squared norms) and V in LDS.  Every lane
         // writes (lanes past N into the spare entry): a store under a per-lane
         // condition would let the compiler sink the loads above into its branch,
         // behind the state loads, where using them waits for the whole state.
-        {
+        if constexpr (!LAYER) {  // (the layer step staged these with its conv input)
             const int slot_i = tid < N ? tid : N;
             s_rows[slot_i] = my_row;
             s_anc[slot_i] = my_anc;
@@ -391,6 +797,18 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
             reinterpret_cast<uint32_t*>(s_mh)[e] = 0u;
             reinterpret_cast<uint32_t*>(s_ml)[e] = 0u;
         }
+        if constexpr (LAYER) {  // K/Q/V rows are staged; squared norms from them
+    #pragma unroll
+            for (int u = 0; u < kKQItems; ++u) {
+                const int it = tid + u * kThreads;
+                const int sl = it >> 5;
+                const int ch = it & 31;
+                float ss = sumsq_bf16x4(*reinterpret_cast<const uint2*>(s_a + sl * kKQStride + ch * 8));
+    #pragma unroll
+                for (int off = 16; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+                if (ch == 0) s_nrm[sl] = ss;
+            }
+        } else {
     #pragma unroll
         for (int u = 0; u < kKQItems; ++u) {
             const int it = tid + u * kThreads;
@@ -409,6 +827,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
             const int it = tid + u * kThreads;
             const int node = it >> 5;
             if (node < N) *reinterpret_cast<uint2*>(s_v + node * kD + (it & 31) * 4) = v_val[u];
+        }
         }
         __syncthreads();
 
@@ -538,11 +957,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     // 16s + 8 + 4hf + e of row r_own; its partner hf ^ 1 is lane ^ 32), and
     // publish the state (LumoTree, Sec. IV-B):
     //   u = b_j (v_j - a_j S k^_j),  S <- a_j S + u k^_j^T,  k^_j = sc_j k_j
-    if constexpr (FUSED) {
-        if (cok) {  // uniform
-            // the staged path overlays the Gram block, dead after the M solve
+    if constexpr (COMMIT) {
+        const bool do_commit = FUSED ? cok : nc > 0;
+        const int plen = FUSED ? len : nc;
+        if (do_commit) {  // uniform
             const int jj = tid >> 5;
             const int chp = tid & 31;
+          if constexpr (FUSED) {
+            // the staged path overlays the Gram block, dead after the M solve
             const int cpl = len * 32;  // 8-byte chunks of the path's k (and of v)
             float ss = sumsq_bf16x4(pk_val);
 #pragma unroll
@@ -574,6 +996,15 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                 s_alp[tid] = p_al;
                 s_bep[tid] = p_be;
             }
+          } else {
+            // the first segment's k/v rows (their conv ran with the tree's)
+            *reinterpret_cast<uint2*>(s_kp + jj * kKQStride + chp * 8) = pk_val;
+            *reinterpret_cast<uint2*>(s_vp + jj * kD + chp * 4) = pv_val;
+            float ss = sumsq_bf16x4(pk_val);
+#pragma unroll
+            for (int off = 16; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+            if (chp == 0) s_scp[jj] = norm ? 1.0f / sqrtf(ss + 1e-6f) : 1.0f;
+          }
             __syncthreads();
             // On the matrix cores, kMfmaPath path nodes at a time (segment
             // j0 .. j0 + n - 1 of the path, from the state the previous segment
@@ -585,11 +1016,69 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
             // S k_j for every j of the segment is one contraction like (d); the
             // rank-n update is four 32-column contractions whose output layout
             // is this lane's own state layout.
-            float* s_gp = s_scp + cp.Lmax;  // [kMfmaPath][kMfmaPath] scaled segment Gram
-            for (int j0 = 0; j0 < len; j0 += kMfmaPath) {
-                const int n = min(len - j0, kMfmaPath);
+            float* s_gp = s_scp + (FUSED ? cp.Lmax : kMfmaPath);  // [kMfmaPath][kMfmaPath] scaled segment Gram
+            for (int j0 = 0; j0 < plen; j0 += kMfmaPath) {
+                const int n = min(plen - j0, kMfmaPath);
+                const int kr0 = FUSED ? j0 : 0;  // staged row of the segment's first node
+                if constexpr (LAYER) {
+                    // a later segment's k/v rows: the conv of its path rows
+                    if (LONGP && j0 > 0) {  // uniform: paths longer than one segment
+                        uint2 kc = make_uint2(0u, 0u), vc = make_uint2(0u, 0u);
+                        uint4* s_stg = reinterpret_cast<uint4*>(lds + L.stg);  // [H + 8][16]
+                        uint32_t* s_sw = reinterpret_cast<uint32_t*>(lds + L.sw);
+                        float* s_sb = reinterpret_cast<float*>(lds + L.sb);
+#pragma unroll 1
+                        for (int half = 0; half < 2; ++half) {
+                            int colb = half == 0 ? ck0 : cv0;
+                            asm volatile("" : "+s"(colb));  // keep these loads inside the loop
+                            const int e = min(tid, (H + 8) * 16 - 1);
+                            const uint4 xv4 = *reinterpret_cast<const uint4*>(
+                                li.x_prev + (static_cast<size_t>(b) * li.Rp + prow_at(j0 + (e >> 4) - H)) * li.C +
+                                colb + 8 * (e & 15));
+                            const uint32_t wword = conv_weight_word<CW>(li.w, colb, tid);
+                            float bword = 0.0f;
+                            if (li.bias) bword = li.bias[colb + (tid & (kD - 1))];
+                            s_stg[e] = xv4;
+                            s_sw[tid] = wword;
+                            s_sb[tid & (kD - 1)] = bword;
+                            __syncthreads();
+                            // two channels at a time: this runs with the whole state live
+                            const char* st0 = reinterpret_cast<const char*>(s_stg) + jj * 256 + chp * 8;
+                            uint2 o;
+#pragma unroll 1
+                            for (int pr = 0; pr < 2; ++pr) {
+                                uint32_t tw[CW];
+#pragma unroll
+                                for (int t = 0; t <= H; ++t)
+                                    tw[t] = *reinterpret_cast<const uint32_t*>(st0 + t * 256 + pr * 4);
+                                const int c0 = 4 * chp + 2 * pr;
+                                const float z0 = conv_channel<CW>(tw, 0, s_sw + c0 * kWP, li.bias != nullptr,
+                                                                  s_sb[c0], li.act);
+                                const float z1 = conv_channel<CW>(tw, 1, s_sw + (c0 + 1) * kWP,
+                                                                  li.bias != nullptr, s_sb[c0 + 1], li.act);
+                                const uint32_t wd = conv_pack_bf16x2(z0, z1);
+                                if (pr == 0)
+                                    o.x = wd;
+                                else
+                                    o.y = wd;
+                            }
+                            if (half == 0)
+                                kc = o;
+                            else
+                                vc = o;
+                            __syncthreads();
+                        }
+                        *reinterpret_cast<uint2*>(s_kp + jj * kKQStride + chp * 8) = kc;
+                        *reinterpret_cast<uint2*>(s_vp + jj * kD + chp * 4) = vc;
+                        float ss = sumsq_bf16x4(kc);
+#pragma unroll
+                        for (int off = 16; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+                        if (chp == 0) s_scp[jj] = norm ? 1.0f / sqrtf(ss + 1e-6f) : 1.0f;
+                        __syncthreads();
+                    }
+                }
                 auto path_row = [&](int row, int ks) -> bf16x8_t {  // zero past the segment
-                    const bf16x8_t a = lds_operand(s_kp, j0 + min(row, n - 1), ks, hf);
+                    const bf16x8_t a = lds_operand(s_kp, kr0 + min(row, n - 1), ks, hf);
                     return row < n ? a : bf16x8_t{};
                 };
                 if (wave == 0 && n > 1) {
@@ -602,7 +1091,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                     for (int e = 0; e < kMfmaPath / 2; ++e) {  // rows m < kMfmaPath sit in these e
                         const int m = 8 * (e >> 2) + 4 * hf + (e & 3);
                         if (l32 < n && m < n)
-                            s_gp[m * kMfmaPath + l32] = gacc[e] * s_scp[j0 + m] * s_scp[j0 + l32];
+                            s_gp[m * kMfmaPath + l32] = gacc[e] * s_scp[kr0 + m] * s_scp[kr0 + l32];
                     }
                 }
                 f32x16_t pacc = {};
@@ -633,10 +1122,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                     w[j] = 0.0f;
                     if (j < n) {  // uniform
                         const float a = s_alp[j0 + j];
-                        float z = A * s_scp[j0 + j] * ctp[j];
+                        float z = A * s_scp[kr0 + j] * ctp[j];
 #pragma unroll
                         for (int m = 0; m < j; ++m) z = fmaf(w[m], s_gp[m * kMfmaPath + j], z);
-                        const float u = s_bep[j0 + j] * (bf16_bits_to_f32(s_vp[(j0 + j) * kD + r_own]) - a * z);
+                        const float u = s_bep[j0 + j] * (bf16_bits_to_f32(s_vp[(kr0 + j) * kD + r_own]) - a * z);
 #pragma unroll
                         for (int m = 0; m < j; ++m) w[m] *= a;
                         w[j] = u;
@@ -649,10 +1138,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                     float uu[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float w0 = w[e] * s_scp[j0 + min(e, n - 1)];
+                        const float w0 = w[e] * s_scp[kr0 + min(e, n - 1)];
                         float w1 = 0.0f;
                         if constexpr (kMfmaPath > 8)
-                            w1 = w[min(8 + e, kMfmaPath - 1)] * s_scp[j0 + min(8 + e, n - 1)];
+                            w1 = w[min(8 + e, kMfmaPath - 1)] * s_scp[kr0 + min(8 + e, n - 1)];
                         uu[e] = hf ? w1 : w0;
                     }
                     split_hi_lo(make_float4(uu[0], uu[1], uu[2], uu[3]), make_float4(uu[4], uu[5], uu[6], uu[7]),
@@ -666,8 +1155,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
 #pragma unroll
                     for (int e2 = 0; e2 < 4; ++e2) {
                         const int m0 = 8 * hf + 2 * e2;
-                        const uint32_t k0 = col[(j0 + min(m0, n - 1)) * (kKQStride / 2)];
-                        const uint32_t k1 = col[(j0 + min(m0 + 1, n - 1)) * (kKQStride / 2)];
+                        const uint32_t k0 = col[(kr0 + min(m0, n - 1)) * (kKQStride / 2)];
+                        const uint32_t k1 = col[(kr0 + min(m0 + 1, n - 1)) * (kKQStride / 2)];
                         kw[e2] = (m0 < n ? k0 : 0u) | ((m0 + 1 < n ? k1 : 0u) << 16);
                     }
                     const bf16x8_t ka = __builtin_bit_cast(bf16x8_t, make_uint4(kw[0], kw[1], kw[2], kw[3]));
@@ -967,10 +1456,11 @@ hipError_t set_lds(K kernel, size_t bytes) {
                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
 }
 
-template <int NPB, bool FUSED>
+template <int NPB, int MODE, int CW = 0>
 hipError_t launch_mfma_t(const gdn_tree_desc& d, const VerifyArgs& a, float* pool, int norm,
-                         int obf, size_t lds, const CommitPrev& cp, hipStream_t s) {
-    auto kfn = verify_mfma_kernel<NPB, FUSED>;
+                         int obf, size_t lds, const CommitPrev& cp, hipStream_t s,
+                         const LayerIn& li = LayerIn{}) {
+    auto kfn = verify_mfma_kernel<NPB, MODE, CW>;
     hipError_t e = set_lds(kfn, lds);
     if (e != hipSuccess) return e;
     const dim3 grid(static_cast<unsigned>(d.B) * static_cast<unsigned>(a.Hv));
@@ -978,7 +1468,7 @@ hipError_t launch_mfma_t(const gdn_tree_desc& d, const VerifyArgs& a, float* poo
                        d.depth, d.status, static_cast<const uint16_t*>(a.q),
                        static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                        a.rs_qk, a.rs_v, a.alpha, a.beta, pool, a.P, a.state_idx, a.out, a.Hqk,
-                       a.Hv, norm, obf, a.err, cp);
+                       a.Hv, norm, obf, a.err, cp, li);
     return hipGetLastError();
 }
 
@@ -1016,8 +1506,8 @@ hipError_t launch_verify(const gdn_tree_desc& d, const VerifyArgs& a, hipStream_
         // the non-fused kernel only reads the state
         float* pool = const_cast<float*>(a.pool);
         switch (NPB) {
-            case 1: return launch_mfma_t<1, false>(d, a, pool, norm, obf, lds, none, s);
-            case 2: return launch_mfma_t<2, false>(d, a, pool, norm, obf, lds, none, s);
+            case 1: return launch_mfma_t<1, kModeVerify>(d, a, pool, norm, obf, lds, none, s);
+            case 2: return launch_mfma_t<2, kModeVerify>(d, a, pool, norm, obf, lds, none, s);
             default: return hipErrorNotSupported;
         }
     }
@@ -1069,8 +1559,8 @@ hipError_t launch_commit_verify(const gdn_tree_desc& d, const CommitVerifyArgs& 
             const int norm = (va.flags & GDN_F_NORM_QK) ? 1 : 0;
             const int obf = (va.flags & GDN_F_OUT_BF16) ? 1 : 0;
             switch (NPB) {
-                case 1: return launch_mfma_t<1, true>(d, va, a.pool, norm, obf, lds, cp, s);
-                case 2: return launch_mfma_t<2, true>(d, va, a.pool, norm, obf, lds, cp, s);
+                case 1: return launch_mfma_t<1, kModeCommitVerify>(d, va, a.pool, norm, obf, lds, cp, s);
+                case 2: return launch_mfma_t<2, kModeCommitVerify>(d, va, a.pool, norm, obf, lds, cp, s);
                 default: break;
             }
         }
@@ -1082,6 +1572,48 @@ hipError_t launch_commit_verify(const gdn_tree_desc& d, const CommitVerifyArgs& 
     hipError_t e = launch_commit(dp, ca, s);
     if (e != hipSuccess) return e;
     return launch_verify(d, va, s);
+}
+
+hipError_t launch_layer_step(const gdn_tree_desc& d, const LayerArgs& a, hipStream_t s) {
+    if (d.N > 32 || d.W < 1 || d.W > 4) return hipErrorNotSupported;
+    const size_t lds = static_cast<size_t>(layer_lds_layout(d.N, d.W - 1, a.Lmax).total);
+    if (lds > kMaxLds) return hipErrorNotSupported;
+    LayerIn li{};
+    li.C = 2 * a.Hqk * kD + a.Hv * kD;
+    li.act = a.act;
+    li.Rp = a.prev->R;
+    li.Lmax = a.Lmax;
+    li.x = a.x;
+    li.w = a.w;
+    li.bias = a.bias;
+    li.hist_in = a.hist_in;
+    li.hist_out = a.hist_out;
+    li.y = a.y;
+    li.x_prev = a.x_prev;
+    li.alpha_p = a.alpha_prev;
+    li.beta_p = a.beta_prev;
+    li.path_rows = a.path_rows;
+    li.path_n = a.path_n;
+    li.parent = d.parent;
+    const VerifyArgs va{nullptr, nullptr, nullptr, 0, 0, a.alpha, a.beta, a.pool, a.P, a.state_idx,
+                        a.out, a.Hqk, a.Hv, kD, GDN_DT_BF16, a.flags, a.err};
+    const int norm = (a.flags & GDN_F_NORM_QK) ? 1 : 0;
+    const int obf = (a.flags & GDN_F_OUT_BF16) ? 1 : 0;
+    const CommitPrev none{};
+    const bool longp = a.Lmax > kMfmaPath;
+#define GDN_LAYER_CASE(WW)                                                                          \
+    case WW:                                                                                        \
+        return longp ? launch_mfma_t<1, kModeLayerLong, WW>(d, va, a.pool, norm, obf, lds, none, s, li) \
+                     : launch_mfma_t<1, kModeLayer, WW>(d, va, a.pool, norm, obf, lds, none, s, li);
+    switch (d.W) {
+        GDN_LAYER_CASE(1)
+        GDN_LAYER_CASE(2)
+        GDN_LAYER_CASE(3)
+        GDN_LAYER_CASE(4)
+        default:
+            return hipErrorNotSupported;
+    }
+#undef GDN_LAYER_CASE
 }
 
 }  // namespace gdn
