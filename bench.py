@@ -7,16 +7,21 @@ d_k = d_v = 128, causal conv kernel 4 over 8192 channels, bf16 operands, fp32
 state): the descriptor build, the ancestry-gathered conv, the tree verify, the
 commit of an accepted path into the state and the conv-history publication.
 
-Two step shapes (``--mode``):
-  fused     (default) the steady-state decode step:
-              gdn_tree_desc_build -> conv_ancestry_gather_publish ->
+Three step shapes (``--mode``):
+  layer     (default) the steady-state decode step in one launch per layer:
+              gdn_step_prepare -> gdn_layer_step
+            (the first once per step for all layers: the new tree's
+            descriptor and the previous path's rows); the layer step
+            commits the previous step's accepted path, publishes its conv
+            history into the other of two history buffers, and convolves and
+            verifies the new tree: the state is read once and written once,
+            the conv output never goes to memory.
+  fused     gdn_tree_desc_build -> conv_ancestry_gather_publish ->
               gdn_tree_commit_verify
-            the commit and history publication of the previous step's
-            accepted path run inside this step's conv and verify, so the
-            state is read once and written once per step.
+            the same step in two launches, the conv output written and read.
   separate  gdn_tree_desc_build -> conv_ancestry_gather -> gdn_tree_verify
             -> gdn_tree_commit (this step's own path), the state read twice.
-Both commit one path and verify one tree per step.
+All three commit one path and verify one tree per step.
 
 Inputs are resident in HBM before the timed region.  Two independent layer
 instances (pool, history, weights, about 0.5 GB each with their step data)
@@ -49,7 +54,8 @@ PEAK_HBM_GBS = 8000.0
 WORKLOAD_TAG = {"tree27_b128_h32_conv4": "tree27_b128_conv4"}
 KERNEL_PREFIX = {"conv": "gdn::conv_gather_kernel", "verify": "gdn::verify_",
                  "commit": "gdn::commit_kernel", "desc": "gdn::desc_build_kernel",
-                 "commit_verify": "gdn::verify_"}
+                 "commit_verify": "gdn::verify_", "prepare": "gdn::step_prepare_kernel",
+                 "layer": "gdn::verify_"}
 
 
 def log(*a):
@@ -103,9 +109,35 @@ def bytes_commit_state(cfg, case):
     return active * Hv * D * D * 4, int(L.sum()) * ((Hqk * D + Hv * D) * 2 + Hv * 8)
 
 
+def bytes_resolve(cfg, prev):
+    """Path validation: path ids and length in, parents and rows of the path
+    nodes, the slots for the duplicate check; rows and counts out."""
+    B, Lmax = prev["path"].shape
+    return B * Lmax * (4 + 4 + 4 + 4) + B * (4 + 4 + 4 + 4)
+
+
+def bytes_layer(cfg, cur, prev):
+    """The one-launch layer step: the state (read; written for requests with
+    an accepted path), the new tree's conv input rows, gates and outputs, the
+    old history read and the new one written, the weights, and of the
+    previous path its k/v-channel conv rows, the q channels of the rows that
+    enter the new history, and its gates."""
+    B, N, D, Hv, Hqk, W, C = _common(cfg, cur)
+    L = prev["path_len"].astype(np.int64)
+    active = int((L > 0).sum())
+    state = B * Hv * D * D * 4 + active * Hv * D * D * 4
+    tree = B * N * C * 2 + B * N * Hv * 8 + B * N * Hv * D * 4
+    hist = 2 * B * (W - 1) * C * 2 + C * W * 2
+    path = (int(L.sum()) * ((Hqk * D + Hv * D) * 2 + Hv * 8)
+            + int(np.minimum(L, W - 1).sum()) * Hqk * D * 2)
+    return state + tree + hist + path
+
+
 def byte_model(cfg, cur, prev, mode):
     out = {"desc": bytes_desc(cfg, cur)}
-    if mode == "fused":
+    if mode == "layer":
+        out = {"prepare": out["desc"] + bytes_resolve(cfg, prev), "layer": bytes_layer(cfg, cur, prev)}
+    elif mode == "fused":
         state_w, path_rows = bytes_commit_state(cfg, prev)
         out["conv"] = bytes_conv(cfg, cur) + bytes_publish(cfg, prev)
         out["commit_verify"] = bytes_verify(cfg, cur) + state_w + path_rows
@@ -210,7 +242,8 @@ class Slot:
 
 
 class Instance:
-    """One layer instance: its pool, history and weights, and two step slots."""
+    """One layer instance: its pool, history (two buffers in layer mode, used
+    in turn as the step's input and output), weights and step slots."""
 
     def __init__(self, g, cfg, seed, layer, to_dev, dev, torch, slots):
         import gdn_inputs as gi
@@ -223,8 +256,13 @@ class Instance:
         self.pool = to_dev(base["pool"])
         self.state_idx = to_dev(base["state_idx"])
         self.hist = to_dev(base["hist"]) if cfg.conv_W > 0 else None
+        self.hist2 = self.hist.clone() if cfg.conv_W > 0 else None
         self.w = to_dev(base["w"]) if cfg.conv_W > 0 else None
         self.slots = [Slot(g, cfg, c, to_dev, dev, torch) for c in cases]
+        B, Lmax = base["path"].shape
+        self.path_rows = torch.zeros((B, Lmax), dtype=torch.int32, device=dev)
+        self.path_n = torch.zeros((B,), dtype=torch.int32, device=dev)
+        self.P = int(base["P"])
         self.turn = 0
 
 
@@ -234,7 +272,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=4)
-    ap.add_argument("--mode", choices=("fused", "separate"), default="fused")
+    ap.add_argument("--mode", choices=("layer", "fused", "separate"), default="layer")
     ap.add_argument("--seed", type=int, default=2026)
     ap.add_argument("--sets", type=int, default=2, help="independent layer instances rotated per step")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -260,6 +298,11 @@ def main():
     cfg = gi.CONFIGS[args.config]
     dev = "cuda"
     fused = args.mode == "fused"
+    layer = args.mode == "layer"
+    if layer and cfg.conv_W == 0:
+        print("--mode layer needs a conv workload (the layer step starts from the conv input)",
+              file=sys.stderr)
+        sys.exit(2)
 
     if args.copy_calibration > 0:
         n = args.copy_calibration * (1 << 20) // 4
@@ -278,15 +321,16 @@ def main():
         return torch.from_numpy(a).to(dev)
 
     t0 = time.perf_counter()
-    insts = [Instance(g, cfg, args.seed, layer, to_dev, dev, torch, 2 if fused else 1)
-             for layer in range(args.sets)]
+    insts = [Instance(g, cfg, args.seed, li, to_dev, dev, torch, 2 if (fused or layer) else 1)
+             for li in range(args.sets)]
     err = torch.zeros(1, dtype=torch.int32, device=dev)
     flags = g.GDN_F_NORM_QK if cfg.norm_qk else 0
     torch.cuda.synchronize()
     log(f"[bench] {args.mode} mode: inputs for {cfg.name} x{args.sets} ready in "
         f"{time.perf_counter() - t0:.1f} s")
 
-    names = ("desc", "conv", "commit_verify") if fused else ("desc", "conv", "verify", "commit")
+    names = (("prepare", "layer") if layer else
+             ("desc", "conv", "commit_verify") if fused else ("desc", "conv", "verify", "commit"))
 
     def step(inst, ev=None):
         cur = inst.slots[inst.turn % len(inst.slots)]
@@ -299,6 +343,19 @@ def main():
                 next(marks).record()
 
         mark()
+        if layer:
+            # once per step for every layer: the new tree's descriptor and the
+            # previous path's rows
+            g.gdn_step_prepare(cur.desc, prev.desc, prev.path, prev.path_len, inst.state_idx, inst.P,
+                               inst.path_rows, inst.path_n, err)
+            mark()
+            hist_in, hist_out = (inst.hist, inst.hist2) if inst.turn % 2 else (inst.hist2, inst.hist)
+            g.gdn_layer_step(cur.desc, cur.x, inst.w, None, cfg.act, hist_in, hist_out, cur.alpha,
+                             cur.beta, inst.pool, inst.state_idx, cur.out, prev.desc, prev.x,
+                             prev.alpha, prev.beta, inst.path_rows, inst.path_n, err, cfg.Hqk,
+                             flags=flags)
+            mark()
+            return cur, prev
         g.gdn_tree_desc_build(cur.desc, err)
         mark()
         if fused:
@@ -359,7 +416,7 @@ def main():
     log(f"[bench] step {ms_per_step * 1e3:.1f} us (events), wall {wall / args.steps * 1e6:.1f} us, "
         f"{step_bytes / 1e6:.1f} MB -> {step_bytes / (ms_per_step / 1e3) / 1e9:.1f} GB/s")
 
-    dom = max((n for n in names if n != "desc"), key=lambda n: avg[n])
+    dom = max((n for n in names if n not in ("desc", "prepare")), key=lambda n: avg[n])
     achieved = bytes_avg[dom] / (avg[dom] / 1e3) / 1e9
     tag = WORKLOAD_TAG.get(cfg.name, cfg.name)
     roofline = dict(bound="hbm", kernel=dom, achieved=round(achieved, 1), peak=PEAK_HBM_GBS,
@@ -372,7 +429,10 @@ def main():
         cpu = cpu_baseline(cfg, args.seed, args.cpu_budget)
         cpu["value"] = round(cpu["value"], 1)
 
-    steps_desc = ("desc_build + conv_ancestry_gather_publish + gdn_tree_commit_verify (steady "
+    steps_desc = ("gdn_step_prepare + gdn_layer_step (steady state: the previous "
+                  "step's accepted path committed and its conv history published inside the "
+                  "layer step, the conv output kept on chip)" if layer else
+                  "desc_build + conv_ancestry_gather_publish + gdn_tree_commit_verify (steady "
                   "state: the previous step's accepted path committed and its conv history "
                   "published inside this step)" if fused else
                   "desc_build + conv_ancestry_gather + gdn_tree_verify + gdn_tree_commit")

@@ -280,6 +280,14 @@ int32_t gdn_path_resolve(const gdn_tree_desc *d_prev, const int32_t *path,
                          int32_t P, int32_t *path_rows, int32_t *path_n, int32_t *err,
                          void *stream);
 
+/* gdn_tree_desc_build(d) and gdn_path_resolve(d_prev, ...) in one launch:
+ * the step's shared work for every layer (d_prev->B == d->B).  Arguments,
+ * outputs and errors are those of the two calls. */
+int32_t gdn_step_prepare(const gdn_tree_desc *d, const gdn_tree_desc *d_prev,
+                         const int32_t *path, const int32_t *path_len, int32_t Lmax,
+                         const int32_t *state_idx, int32_t P, int32_t *path_rows,
+                         int32_t *path_n, int32_t *err, void *stream);
+
 /* One GDN layer's step in one launch.  With hist = hist_in copied to
  * hist_out first, it computes what these calls compute in order:
  *     y_prev = conv_ancestry_gather(d_prev, x_prev, hist)      (path rows only)
@@ -329,7 +337,7 @@ int32_t gdn_layer_step(const gdn_tree_desc *d, const void *x, const void *w, con
 const char *gdn_status_string(int32_t status);
 
 /* ABI version of this header: 3 (1, plus the two fused-step calls in 2,
- * plus gdn_path_resolve and gdn_layer_step). */
+ * plus gdn_path_resolve, gdn_step_prepare and gdn_layer_step). */
 int32_t gdn_abi_version(void);
 
 #ifdef __cplusplus

@@ -376,10 +376,11 @@ def run_gpu_two_steps(c1, c2, fused=True, y1_override=None, y2_override=None, fl
     return res
 
 
-def run_gpu_layer(c1, c2, flags=0, with_y=True, path_n_override=None):
+def run_gpu_layer(c1, c2, flags=0, with_y=True, prepare=False):
     """Step 2 of a conv configuration through the one-launch layer step:
-    gdn_path_resolve of step 1's path, then gdn_layer_step with step 1's conv
-    input, gates and history (hist_in) and a separate hist_out."""
+    step 2's descriptor and the resolution of step 1's path (two calls, or
+    gdn_step_prepare with prepare=True), then gdn_layer_step with step 1's
+    conv input, gates and history (hist_in) and a separate hist_out."""
     import torch
     import tree_speculative_verification_gdn_amd as g
 
@@ -389,7 +390,6 @@ def run_gpu_layer(c1, c2, flags=0, with_y=True, path_n_override=None):
     d1 = g.TreeDesc(to_dev(c1["parent"]), to_dev(c1["node_row"]), R, W)
     d2 = g.TreeDesc(to_dev(c2["parent"]), to_dev(c2["node_row"]), R, W)
     g.gdn_tree_desc_build(d1, err)
-    g.gdn_tree_desc_build(d2, err)
     pool = to_dev(c1["pool"])
     sidx = to_dev(c1["state_idx"])
     P = int(pool.shape[0])
@@ -397,9 +397,11 @@ def run_gpu_layer(c1, c2, flags=0, with_y=True, path_n_override=None):
     Lmax = int(path.shape[1])
     path_rows = torch.full((B, Lmax), -7, dtype=torch.int32, device="cuda")
     path_n = torch.full((B,), -9, dtype=torch.int32, device="cuda")
-    g.gdn_path_resolve(d1, path, to_dev(c1["path_len"]), sidx, P, path_rows, path_n, err)
-    if path_n_override is not None:
-        path_n.copy_(to_dev(np.asarray(path_n_override, np.int32)))
+    if prepare:
+        g.gdn_step_prepare(d2, d1, path, to_dev(c1["path_len"]), sidx, P, path_rows, path_n, err)
+    else:
+        g.gdn_tree_desc_build(d2, err)
+        g.gdn_path_resolve(d1, path, to_dev(c1["path_len"]), sidx, P, path_rows, path_n, err)
     hist_in = to_dev(c1["hist"])
     hist_out = torch.full_like(hist_in, float("nan"))
     out = torch.full((B, R, Hv, D), float("nan"), dtype=torch.float32, device="cuda")
@@ -412,7 +414,8 @@ def run_gpu_layer(c1, c2, flags=0, with_y=True, path_n_override=None):
     torch.cuda.synchronize()
     res = dict(err=int(err.item()), out=out.cpu().numpy(), pool=pool.cpu().numpy(),
                hist_out=bits(hist_out), hist_in=bits(hist_in), path_n=path_n.cpu().numpy(),
-               path_rows=path_rows.cpu().numpy(), status2=d2.status.cpu().numpy())
+               path_rows=path_rows.cpu().numpy(), status2=d2.status.cpu().numpy(),
+               desc2=[t.cpu().numpy() for t in (d2.depth, d2.anc, d2.conv_src, d2.status)])
     if with_y:
         res["y2"] = bits(y)
     return res

@@ -31,7 +31,7 @@ def test_header_declares_the_entry_points():
     decl = declared_functions()
     for name in ("gdn_tree_desc_build", "conv_ancestry_gather", "gdn_tree_verify", "gdn_tree_commit",
                  "conv_ancestry_gather_publish", "gdn_tree_commit_verify", "gdn_path_resolve",
-                 "gdn_layer_step"):
+                 "gdn_step_prepare", "gdn_layer_step"):
         assert name in decl
     assert set(decl) == set(g.EXPORTED)
 
@@ -141,6 +141,11 @@ def test_layer_step_argument_checks_fail_before_launch(lib):
     assert Rz(d, p, p, 65, p, 4, p, p, err, None) == g.GDN_ERR_UNSUPPORTED
     assert Rz(d, p, p, 7, p, 0, p, p, err, None) == g.GDN_ERR_ARG
     assert Rz(None, p, p, 7, p, 4, p, p, err, None) == g.GDN_ERR_ARG
+    # step prepare: previous tree of another batch, Lmax out of range, missing rows
+    Sp = lib.gdn_step_prepare
+    assert Sp(d, other_b, p, p, 7, p, 4, p, p, err, None) == g.GDN_ERR_ARG
+    assert Sp(d, d, p, p, 65, p, 4, p, p, err, None) == g.GDN_ERR_UNSUPPORTED
+    assert Sp(d, d, p, p, 7, p, 4, None, p, err, None) == g.GDN_ERR_ARG
     # layer step: C = 2*16*128 + 32*128 = 8192 channels, history bytes P*(W-1)*C*2
     L = lib.gdn_layer_step
     hbytes = 4 * 3 * 8192 * 2

@@ -159,6 +159,17 @@ def test_layer_step_edge_cases():
     assert orr["err"] == g.GDN_EV_PARENT | g.GDN_EV_PATH | g.GDN_EV_STATE
     _check_resolve(c1, gr, c1["P"])
     _cmp(c1, c2, gr, orr)
+    # gdn_step_prepare = gdn_tree_desc_build + gdn_path_resolve in one launch
+    gp = run_gpu_layer(c1, c2, prepare=True)
+    assert gp["err"] == gr["err"]
+    for a, b2 in zip(gp["desc2"], gr["desc2"]):
+        assert np.array_equal(a, b2)
+    assert np.array_equal(gp["path_n"], gr["path_n"])
+    for b in range(c1["B"]):
+        n = max(int(gr["path_n"][b]), 0)
+        assert np.array_equal(gp["path_rows"][b, :n], gr["path_rows"][b, :n])
+    assert np.array_equal(gp["out"], gr["out"], equal_nan=True)
+    assert np.array_equal(gp["pool"], gr["pool"], equal_nan=True)
 
 
 def test_layer_step_silu_against_oracle_and_separate_calls():
@@ -189,7 +200,7 @@ def test_layer_step_full_size_sampled():
     # the bench's workload at full size on the device; the oracle on a sample
     cfg = _exact(gi.CONFIGS[4])
     c1, c2 = two_step_case(cfg, seed=2026, packing="bfs", conv_values="dyadic")
-    gr = run_gpu_layer(c1, c2)
+    gr = run_gpu_layer(c1, c2, prepare=True)
     assert gr["err"] == 0
     used = c1["state_idx"]
     bs = np.array([0, 33, 64, 127])

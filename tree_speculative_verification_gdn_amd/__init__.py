@@ -10,8 +10,8 @@ the shared library is missing, every call raises.
 Entry points (same names as the C ABI):
     gdn_tree_desc_build, conv_ancestry_gather, gdn_tree_verify, gdn_tree_commit,
     the fused steady-state step: conv_ancestry_gather_publish,
-    gdn_tree_commit_verify; and one launch per layer: gdn_path_resolve (once
-    per step) + gdn_layer_step (once per layer)
+    gdn_tree_commit_verify; and one launch per layer: gdn_path_resolve or
+    gdn_step_prepare (once per step) + gdn_layer_step (once per layer)
 Helper: TreeDesc (owns the descriptor's device arrays and the C struct).
 """
 from __future__ import annotations
@@ -27,7 +27,7 @@ __all__ = [
     "GDN_ACT_NONE", "GDN_ACT_SILU", "GdnError", "TreeDesc", "library_path", "load_library",
     "gdn_tree_desc_build", "conv_ancestry_gather", "gdn_tree_verify", "gdn_tree_commit",
     "conv_ancestry_gather_publish", "gdn_tree_commit_verify", "gdn_path_resolve",
-    "gdn_layer_step",
+    "gdn_step_prepare", "gdn_layer_step",
 ]
 
 # values mirror include/gdn_tree.h
@@ -39,7 +39,8 @@ GDN_ACT_NONE, GDN_ACT_SILU = 0, 1
 
 EXPORTED = ("gdn_tree_desc_build", "conv_ancestry_gather", "gdn_tree_verify",
             "gdn_tree_commit", "conv_ancestry_gather_publish", "gdn_tree_commit_verify",
-            "gdn_path_resolve", "gdn_layer_step", "gdn_status_string", "gdn_abi_version")
+            "gdn_path_resolve", "gdn_step_prepare", "gdn_layer_step", "gdn_status_string",
+            "gdn_abi_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lock = threading.Lock()
@@ -97,6 +98,8 @@ def load_library():
                                                i32, i32, i32, i32, i32, i32, vp, vp]
         lib.gdn_path_resolve.restype = i32
         lib.gdn_path_resolve.argtypes = [dp, vp, vp, i32, vp, i32, vp, vp, vp, vp]
+        lib.gdn_step_prepare.restype = i32
+        lib.gdn_step_prepare.argtypes = [dp, dp, vp, vp, i32, vp, i32, vp, vp, vp, vp]
         lib.gdn_layer_step.restype = i32
         lib.gdn_layer_step.argtypes = [dp, vp, vp, vp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp,
                                        dp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
@@ -307,6 +310,16 @@ def gdn_path_resolve(prev: TreeDesc, path, path_len, state_idx, P: int, path_row
                                            _ptr(state_idx), int(P), _ptr(path_rows),
                                            _ptr(path_n), _ptr(err), _stream(stream))
     return _check(code, "gdn_path_resolve", raise_on_error)
+
+
+def gdn_step_prepare(desc: TreeDesc, prev: TreeDesc, path, path_len, state_idx, P: int, path_rows,
+                     path_n, err, stream=None, raise_on_error=True) -> int:
+    """gdn_tree_desc_build(desc) and gdn_path_resolve(prev, ...) in one launch."""
+    Lmax = int(path.shape[1])
+    code = load_library().gdn_step_prepare(desc.ref(), prev.ref(), _ptr(path), _ptr(path_len), Lmax,
+                                           _ptr(state_idx), int(P), _ptr(path_rows), _ptr(path_n),
+                                           _ptr(err), _stream(stream))
+    return _check(code, "gdn_step_prepare", raise_on_error)
 
 
 def gdn_layer_step(desc: TreeDesc, x, w, bias, act: int, hist_in, hist_out, alpha, beta,

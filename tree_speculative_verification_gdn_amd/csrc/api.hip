@@ -211,6 +211,20 @@ int32_t gdn_path_resolve(const gdn_tree_desc* d_prev, const int32_t* path, const
                                                static_cast<hipStream_t>(stream)));
 }
 
+int32_t gdn_step_prepare(const gdn_tree_desc* d, const gdn_tree_desc* d_prev, const int32_t* path,
+                         const int32_t* path_len, int32_t Lmax, const int32_t* state_idx, int32_t P,
+                         int32_t* path_rows, int32_t* path_n, int32_t* err, void* stream) {
+    int32_t st = check_desc(d);
+    if (st != GDN_OK) return st;
+    st = check_desc(d_prev);
+    if (st != GDN_OK) return st;
+    if (d_prev->B != d->B) return GDN_ERR_ARG;
+    if (!path || !path_len || !state_idx || !path_rows || !path_n || !err || P < 1) return GDN_ERR_ARG;
+    if (Lmax < 1 || Lmax > GDN_MAX_NODES) return GDN_ERR_UNSUPPORTED;
+    return map_launch(gdn::launch_step_prepare(*d, *d_prev, path, path_len, Lmax, state_idx, P, path_rows,
+                                               path_n, err, static_cast<hipStream_t>(stream)));
+}
+
 int32_t gdn_layer_step(const gdn_tree_desc* d, const void* x, const void* w, const float* bias,
                        int32_t act, const void* hist_in, void* hist_out, const float* alpha,
                        const float* beta, float* state_pool, int32_t P, const int32_t* state_idx,

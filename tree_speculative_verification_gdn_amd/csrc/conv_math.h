@@ -16,12 +16,13 @@ typedef __bf16 conv_bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float conv_f32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float conv_silu(float z) {
-    // z * sigmoid(z) on the hardware exp2 and reciprocal (about 1 ulp each,
-    // far below the bf16 rounding that follows); the exponential is taken of
-    // a non-positive argument, so it never overflows
-    const float e = __builtin_amdgcn_exp2f(-fabsf(z) * 1.4426950408889634f);
-    const float r = __builtin_amdgcn_rcpf(1.f + e);
-    return z * ((z >= 0.f) ? r : e * r);
+    // z * sigmoid(z) = z / (1 + 2^(-z log2 e)) on the hardware exp2 and
+    // reciprocal (about 1 ulp each, far below the bf16 rounding that
+    // follows).  For z below about -88 the exponential is +inf, the
+    // reciprocal 0 and the result -0, which is z * sigmoid(z) rounded to
+    // bf16 there (|z| e^z < 2^-133).
+    const float e = __builtin_amdgcn_exp2f(z * -1.4426950408889634f);
+    return z * __builtin_amdgcn_rcpf(1.f + e);
 }
 
 // two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)

@@ -8,17 +8,14 @@
 
 namespace gdn {
 
-__global__ void __launch_bounds__(64) desc_build_kernel(int N, int R, int W,
-                                                        const int32_t* __restrict__ parent,
-                                                        const int32_t* __restrict__ node_row,
-                                                        int32_t* __restrict__ depth,
-                                                        uint64_t* __restrict__ anc,
-                                                        int32_t* __restrict__ conv_src,
-                                                        int32_t* __restrict__ status,
-                                                        int32_t* __restrict__ err) {
+// tree t of the descriptor, by one 64-lane workgroup
+__device__ __forceinline__ void build_tree(int t, int N, int R, int W, const int32_t* __restrict__ parent,
+                                           const int32_t* __restrict__ node_row,
+                                           int32_t* __restrict__ depth, uint64_t* __restrict__ anc,
+                                           int32_t* __restrict__ conv_src,
+                                           int32_t* __restrict__ status, int32_t* __restrict__ err) {
     __shared__ int32_t s_par[kMaxNodes];
     __shared__ int32_t s_row[kMaxNodes];
-    const int t = blockIdx.x;
     const int i = threadIdx.x;
     const size_t base = static_cast<size_t>(t) * N;
     if (i < N) {
@@ -76,6 +73,17 @@ __global__ void __launch_bounds__(64) desc_build_kernel(int N, int R, int W,
     }
 }
 
+__global__ void __launch_bounds__(64) desc_build_kernel(int N, int R, int W,
+                                                        const int32_t* __restrict__ parent,
+                                                        const int32_t* __restrict__ node_row,
+                                                        int32_t* __restrict__ depth,
+                                                        uint64_t* __restrict__ anc,
+                                                        int32_t* __restrict__ conv_src,
+                                                        int32_t* __restrict__ status,
+                                                        int32_t* __restrict__ err) {
+    build_tree(blockIdx.x, N, R, W, parent, node_row, depth, anc, conv_src, status, err);
+}
+
 hipError_t launch_desc_build(const gdn_tree_desc& d, int32_t* err, hipStream_t s) {
     const int T = d.shared ? 1 : d.B;
     hipLaunchKernelGGL(desc_build_kernel, dim3(T), dim3(64), 0, s, d.N, d.R, d.W, d.parent,
@@ -88,13 +96,28 @@ hipError_t launch_desc_build(const gdn_tree_desc& d, int32_t* err, hipStream_t s
 // per request, lane j holds path entry j (Lmax <= 64).  The path must be a
 // parent chain from a node whose parent is -1 (the same checks the commit
 // makes); its rows are the previous tree's node_row of each entry.
-__global__ void __launch_bounds__(64) path_resolve_kernel(
-    int B, int Np, int shared_p, int Lmax, const int32_t* __restrict__ parent_p,
-    const int32_t* __restrict__ node_row_p, const int32_t* __restrict__ status_p,
-    const int32_t* __restrict__ path, const int32_t* __restrict__ path_len,
-    const int32_t* __restrict__ state_idx, int P, int32_t* __restrict__ path_rows,
-    int32_t* __restrict__ path_n, int32_t* __restrict__ err) {
-    const int b = blockIdx.x;
+struct ResolveArgs {
+    int B, Np, shared_p, Lmax, P;
+    const int32_t* parent_p;
+    const int32_t* node_row_p;
+    const int32_t* status_p;
+    const int32_t* path;
+    const int32_t* path_len;
+    const int32_t* state_idx;
+    int32_t* path_rows;
+    int32_t* path_n;
+};
+
+__device__ __forceinline__ void resolve_path(int b, const ResolveArgs& a, int32_t* __restrict__ err) {
+    const int B = a.B, Np = a.Np, shared_p = a.shared_p, Lmax = a.Lmax, P = a.P;
+    const int32_t* __restrict__ parent_p = a.parent_p;
+    const int32_t* __restrict__ node_row_p = a.node_row_p;
+    const int32_t* __restrict__ status_p = a.status_p;
+    const int32_t* __restrict__ path = a.path;
+    const int32_t* __restrict__ path_len = a.path_len;
+    const int32_t* __restrict__ state_idx = a.state_idx;
+    int32_t* __restrict__ path_rows = a.path_rows;
+    int32_t* __restrict__ path_n = a.path_n;
     const int j = threadIdx.x;
     const int tp = shared_p ? 0 : b;
     const int st_p = status_p[tp];
@@ -128,12 +151,60 @@ __global__ void __launch_bounds__(64) path_resolve_kernel(
     if (st_p == 0 && !path_bad && j < len) path_rows[static_cast<size_t>(b) * Lmax + j] = row;
 }
 
+__global__ void __launch_bounds__(64) path_resolve_kernel(const ResolveArgs a, int32_t* __restrict__ err) {
+    resolve_path(blockIdx.x, a, err);
+}
+
+// One launch for a step's shared work: the new tree's descriptor (workgroups
+// t < T) and the previous path's rows (workgroups b < B).
+__global__ void __launch_bounds__(64) step_prepare_kernel(int T, int N, int R, int W,
+                                                          const int32_t* __restrict__ parent,
+                                                          const int32_t* __restrict__ node_row,
+                                                          int32_t* __restrict__ depth,
+                                                          uint64_t* __restrict__ anc,
+                                                          int32_t* __restrict__ conv_src,
+                                                          int32_t* __restrict__ status,
+                                                          const ResolveArgs a, int32_t* __restrict__ err) {
+    if (static_cast<int>(blockIdx.x) < T)  // uniform per workgroup
+        build_tree(blockIdx.x, N, R, W, parent, node_row, depth, anc, conv_src, status, err);
+    if (static_cast<int>(blockIdx.x) < a.B) resolve_path(blockIdx.x, a, err);
+}
+
+static ResolveArgs resolve_args(const gdn_tree_desc& prev, int B, const int32_t* path,
+                                const int32_t* path_len, int Lmax, const int32_t* state_idx, int P,
+                                int32_t* path_rows, int32_t* path_n) {
+    ResolveArgs a{};
+    a.B = B;
+    a.Np = prev.N;
+    a.shared_p = prev.shared;
+    a.Lmax = Lmax;
+    a.P = P;
+    a.parent_p = prev.parent;
+    a.node_row_p = prev.node_row;
+    a.status_p = prev.status;
+    a.path = path;
+    a.path_len = path_len;
+    a.state_idx = state_idx;
+    a.path_rows = path_rows;
+    a.path_n = path_n;
+    return a;
+}
+
 hipError_t launch_path_resolve(const gdn_tree_desc& prev, int B, const int32_t* path,
                                const int32_t* path_len, int Lmax, const int32_t* state_idx, int P,
                                int32_t* path_rows, int32_t* path_n, int32_t* err, hipStream_t s) {
-    hipLaunchKernelGGL(path_resolve_kernel, dim3(B), dim3(64), 0, s, B, prev.N, prev.shared, Lmax,
-                       prev.parent, prev.node_row, prev.status, path, path_len, state_idx, P,
-                       path_rows, path_n, err);
+    const ResolveArgs a = resolve_args(prev, B, path, path_len, Lmax, state_idx, P, path_rows, path_n);
+    hipLaunchKernelGGL(path_resolve_kernel, dim3(B), dim3(64), 0, s, a, err);
+    return hipGetLastError();
+}
+
+hipError_t launch_step_prepare(const gdn_tree_desc& d, const gdn_tree_desc& prev, const int32_t* path,
+                               const int32_t* path_len, int Lmax, const int32_t* state_idx, int P,
+                               int32_t* path_rows, int32_t* path_n, int32_t* err, hipStream_t s) {
+    const int T = d.shared ? 1 : d.B;
+    const ResolveArgs a = resolve_args(prev, d.B, path, path_len, Lmax, state_idx, P, path_rows, path_n);
+    hipLaunchKernelGGL(step_prepare_kernel, dim3(T > d.B ? T : d.B), dim3(64), 0, s, T, d.N, d.R, d.W,
+                       d.parent, d.node_row, d.depth, d.anc, d.conv_src, d.status, a, err);
     return hipGetLastError();
 }
 

@@ -158,5 +158,9 @@ hipError_t launch_layer_step(const gdn_tree_desc& d, const LayerArgs& a, hipStre
 hipError_t launch_path_resolve(const gdn_tree_desc& prev, int B, const int32_t* path,
                                const int32_t* path_len, int Lmax, const int32_t* state_idx, int P,
                                int32_t* path_rows, int32_t* path_n, int32_t* err, hipStream_t s);
+// The new tree's descriptor and the previous path's resolution in one launch.
+hipError_t launch_step_prepare(const gdn_tree_desc& d, const gdn_tree_desc& prev, const int32_t* path,
+                               const int32_t* path_len, int Lmax, const int32_t* state_idx, int P,
+                               int32_t* path_rows, int32_t* path_n, int32_t* err, hipStream_t s);
 
 }  // namespace gdn
