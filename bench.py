@@ -16,7 +16,7 @@ Three step shapes (``--mode``):
             history into the other of two history buffers, and convolves and
             verifies the new tree: the state is read once and written once,
             the conv output never goes to memory.
-  fused     gdn_tree_desc_build -> conv_ancestry_gather_publish ->
+  fused     gdn_step_prepare -> conv_ancestry_gather_publish ->
               gdn_tree_commit_verify
             the same step in two launches, the conv output written and read.
   separate  gdn_tree_desc_build -> conv_ancestry_gather -> gdn_tree_verify
@@ -139,6 +139,7 @@ def byte_model(cfg, cur, prev, mode):
         out = {"prepare": out["desc"] + bytes_resolve(cfg, prev), "layer": bytes_layer(cfg, cur, prev)}
     elif mode == "fused":
         state_w, path_rows = bytes_commit_state(cfg, prev)
+        out = {"prepare": out["desc"] + bytes_resolve(cfg, prev)}
         out["conv"] = bytes_conv(cfg, cur) + bytes_publish(cfg, prev)
         out["commit_verify"] = bytes_verify(cfg, cur) + state_w + path_rows
     else:
@@ -330,7 +331,7 @@ def main():
         f"{time.perf_counter() - t0:.1f} s")
 
     names = (("prepare", "layer") if layer else
-             ("desc", "conv", "commit_verify") if fused else ("desc", "conv", "verify", "commit"))
+             ("prepare", "conv", "commit_verify") if fused else ("desc", "conv", "verify", "commit"))
 
     def step(inst, ev=None):
         cur = inst.slots[inst.turn % len(inst.slots)]
@@ -356,19 +357,22 @@ def main():
                              flags=flags)
             mark()
             return cur, prev
-        g.gdn_tree_desc_build(cur.desc, err)
-        mark()
         if fused:
+            g.gdn_step_prepare(cur.desc, prev.desc, prev.path, prev.path_len, inst.state_idx, inst.P,
+                               inst.path_rows, inst.path_n, err)
+            mark()
             if cfg.conv_W > 0:
                 g.conv_ancestry_gather_publish(cur.desc, cur.x, inst.hist, inst.state_idx, inst.w,
-                                               None, cur.y, cfg.act, prev.desc, prev.path,
-                                               prev.path_len, prev.x, err)
+                                               None, cur.y, cfg.act, prev.desc, inst.path_rows,
+                                               inst.path_n, prev.x, err)
             mark()
             g.gdn_tree_commit_verify(cur.desc, cur.q, cur.k, cur.v, cur.alpha, cur.beta,
-                                     inst.pool, inst.state_idx, cur.out, prev.desc, prev.path,
-                                     prev.path_len, prev.k, prev.v, prev.alpha, prev.beta, err,
+                                     inst.pool, inst.state_idx, cur.out, prev.desc, inst.path_rows,
+                                     inst.path_n, prev.k, prev.v, prev.alpha, prev.beta, err,
                                      flags=flags)
         else:
+            g.gdn_tree_desc_build(cur.desc, err)
+            mark()
             if cfg.conv_W > 0:
                 g.conv_ancestry_gather(cur.desc, cur.x, inst.hist, inst.state_idx, inst.w, None,
                                        cur.y, cfg.act, err)
@@ -432,7 +436,7 @@ def main():
     steps_desc = ("gdn_step_prepare + gdn_layer_step (steady state: the previous "
                   "step's accepted path committed and its conv history published inside the "
                   "layer step, the conv output kept on chip)" if layer else
-                  "desc_build + conv_ancestry_gather_publish + gdn_tree_commit_verify (steady "
+                  "gdn_step_prepare + conv_ancestry_gather_publish + gdn_tree_commit_verify (steady "
                   "state: the previous step's accepted path committed and its conv history "
                   "published inside this step)" if fused else
                   "desc_build + conv_ancestry_gather + gdn_tree_verify + gdn_tree_commit")

@@ -190,8 +190,9 @@ int32_t gdn_tree_commit(const gdn_tree_desc *d, const int32_t *path, const int32
  * In a decode loop every step commits the previous step's accepted path and
  * then verifies a new tree from the committed state (LumoTree, Sec. IV-B and
  * V-A: the accepted path's recorded operands are replayed into the state
- * bank, and the same path drives the conv-history publication).  The two
- * calls below do exactly
+ * bank, and the same path drives the conv-history publication).  After
+ * gdn_path_resolve (or gdn_step_prepare) of the previous tree and path, the
+ * two calls below do exactly
  *     gdn_tree_commit(d_prev, path, ...);  conv_ancestry_gather(d, ...);
  *     gdn_tree_verify(d, ...)
  * in two launches instead of three, with the state read once and written
@@ -200,29 +201,30 @@ int32_t gdn_tree_commit(const gdn_tree_desc *d, const int32_t *path, const int32
  *                                  previous path, then convolves the new tree
  *   gdn_tree_commit_verify         replays the previous path into the state,
  *                                  writes it, and verifies the new tree from it
- * "Previous" arguments are what gdn_tree_commit takes: the previous step's
- * descriptor (built, same B), its accepted path, and the operands recorded
- * for it (its q/k/v rows, gates and conv input).  Errors are those of the
- * calls they replace: a malformed previous path (GDN_EV_PATH) or a slot two
- * requests share (GDN_EV_STATE) publishes and commits nothing for that
- * request, which is then convolved and verified from its unchanged history
- * and state; a malformed new tree still has its previous path committed. */
+ * The previous path is passed resolved: path_rows [B][Lmax] and path_n [B]
+ * as gdn_path_resolve wrote them for d_prev (values are clamped into range
+ * before use).  The resolution reports the path's errors: a malformed
+ * previous path (GDN_EV_PATH, n_b = 0) or a slot out of range or shared by
+ * two requests (GDN_EV_STATE, n_b = -1) publishes and commits nothing for
+ * that request, which is then convolved and verified from its unchanged
+ * history and state; a malformed new tree still has its previous path
+ * committed and published.  Other "previous" arguments are the operands
+ * recorded for the previous tree (its q/k/v rows, gates and conv input). */
 
-/* Conv with publication.  For each request whose previous path validates,
- * hist[state_idx[b]] first becomes the last W-1 entries of (hist ++ x_prev
- * rows of the path); then y is the conv of d's tree over that history, as in
+/* Conv with publication.  For each request with n_b > 0, hist[state_idx[b]]
+ * first becomes the last W-1 entries of (hist ++ x_prev rows of the path);
+ * then y is the conv of d's tree over that history, as in
  * conv_ancestry_gather.  hist is read and written in place.
- *   d_prev, path [B][Lmax], path_len [B], Lmax: the previous step's tree and
- *            accepted path, as in gdn_tree_commit (d_prev->B == d->B and
- *            d_prev->W == d->W)
+ *   d_prev   the previous step's tree (d_prev->B == d->B, d_prev->W == d->W)
+ *   path_rows [B][Lmax], path_n [B], Lmax: the previous path, resolved
  *   x_prev   bf16 [B][d_prev->R][C]: the previous step's conv input
  * Other arguments and requirements as in conv_ancestry_gather (x_prev 8-byte
  * aligned like x). */
 int32_t conv_ancestry_gather_publish(const gdn_tree_desc *d, const void *x, void *hist,
                                      int32_t P, const int32_t *state_idx, const void *w,
                                      const float *bias, void *y, int32_t C, int32_t act,
-                                     const gdn_tree_desc *d_prev, const int32_t *path,
-                                     const int32_t *path_len, int32_t Lmax, const void *x_prev,
+                                     const gdn_tree_desc *d_prev, const int32_t *path_rows,
+                                     const int32_t *path_n, int32_t Lmax, const void *x_prev,
                                      int32_t *err, void *stream);
 
 /* Commit of the previous path, then verify of d's tree from the committed
@@ -232,15 +234,15 @@ int32_t conv_ancestry_gather_publish(const gdn_tree_desc *d, const void *x, void
  *   q, k, v, strides, alpha, beta, out, flags: the new tree, as in verify
  *   k_prev, v_prev, row strides, alpha_prev, beta_prev: the operands
  *            recorded for the previous tree (same layout rules)
- *   d_prev, path, path_len, Lmax: as in gdn_tree_commit
+ *   d_prev, path_rows, path_n, Lmax: the previous tree and its path, resolved
  * bf16 operands at d = 128 run as one matrix-core kernel; other shapes run
  * the commit and verify kernels one after the other. */
 int32_t gdn_tree_commit_verify(const gdn_tree_desc *d, const void *q, const void *k,
                                const void *v, int64_t row_stride_qk, int64_t row_stride_v,
                                const float *alpha, const float *beta, float *state_pool,
                                int32_t P, const int32_t *state_idx, void *out,
-                               const gdn_tree_desc *d_prev, const int32_t *path,
-                               const int32_t *path_len, int32_t Lmax, const void *k_prev,
+                               const gdn_tree_desc *d_prev, const int32_t *path_rows,
+                               const int32_t *path_n, int32_t Lmax, const void *k_prev,
                                const void *v_prev, int64_t row_stride_qk_prev,
                                int64_t row_stride_v_prev, const float *alpha_prev,
                                const float *beta_prev, int32_t Hqk, int32_t Hv, int32_t dk,

@@ -320,12 +320,17 @@ def run_gpu_two_steps(c1, c2, fused=True, y1_override=None, y2_override=None, fl
     d1 = g.TreeDesc(to_dev(c1["parent"]), to_dev(c1["node_row"]), R, W)
     d2 = g.TreeDesc(to_dev(c2["parent"]), to_dev(c2["node_row"]), R, W)
     g.gdn_tree_desc_build(d1, err)
-    g.gdn_tree_desc_build(d2, err)
     pool = to_dev(c1["pool"])
     sidx = to_dev(c1["state_idx"])
     a1, b1 = to_dev(c1["alpha"]), to_dev(c1["beta"])
     a2, b2 = to_dev(c2["alpha"]), to_dev(c2["beta"])
     p1, l1 = to_dev(c1["path"]), to_dev(c1["path_len"])
+    if fused:  # the fused calls take the path resolved; step 2's descriptor in the same launch
+        prow = torch.full(p1.shape, -7, dtype=torch.int32, device="cuda")
+        pn = torch.full((B,), -9, dtype=torch.int32, device="cuda")
+        g.gdn_step_prepare(d2, d1, p1, l1, sidx, int(pool.shape[0]), prow, pn, err)
+    else:
+        g.gdn_tree_desc_build(d2, err)
     res = {}
     if cfg.conv_W > 0:
         C = cfg.conv_C
@@ -343,7 +348,7 @@ def run_gpu_two_steps(c1, c2, fused=True, y1_override=None, y2_override=None, fl
         v1 = y1[:, :, 2 * Hqk * D:].unflatten(-1, (Hv, D))
         y2 = torch.full((B, R, C), float("nan"), dtype=torch.bfloat16, device="cuda")
         if fused:
-            g.conv_ancestry_gather_publish(d2, x2, hist, sidx, w2, None, y2, cfg.act, d1, p1, l1,
+            g.conv_ancestry_gather_publish(d2, x2, hist, sidx, w2, None, y2, cfg.act, d1, prow, pn,
                                            x1, err)
         else:
             g.gdn_tree_commit(d1, p1, l1, k1, v1, a1, b1, pool, sidx, err, Hqk=Hqk,
@@ -361,7 +366,7 @@ def run_gpu_two_steps(c1, c2, fused=True, y1_override=None, y2_override=None, fl
         q2, k2, v2 = to_dev(c2["q"]), to_dev(c2["k"]), to_dev(c2["v"])
     out = torch.full((B, R, Hv, D), float("nan"), dtype=torch.float32, device="cuda")
     if fused:
-        g.gdn_tree_commit_verify(d2, q2, k2, v2, a2, b2, pool, sidx, out, d1, p1, l1, k1, v1, a1,
+        g.gdn_tree_commit_verify(d2, q2, k2, v2, a2, b2, pool, sidx, out, d1, prow, pn, k1, v1, a1,
                                  b1, err, flags=flags)
     else:
         if cfg.conv_W == 0:

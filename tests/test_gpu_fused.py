@@ -124,6 +124,7 @@ def test_two_steps_conv4_edge_cases():
     c1, c2 = two_step_case(cfg, seed=12, extra_slots=1)
     c1["path_len"][0] = 0
     c1["path"][1, 0] = 4                           # malformed: no publication either
+    c2["parent"][2, 5] = 9                         # step-2 tree malformed: still published
     orr = run_oracle_two_steps(c1, c2)
     gr = run_gpu_two_steps(c1, c2, y1_override=orr["y1"], y2_override=orr["y2"])
     _cmp(c1, c2, gr, orr, conv=True)

@@ -258,28 +258,30 @@ def gdn_tree_commit(desc: TreeDesc, path, path_len, k, v, alpha, beta, state_poo
 
 
 def conv_ancestry_gather_publish(desc: TreeDesc, x, hist, state_idx, w, bias, y, act: int,
-                                 prev: TreeDesc, path, path_len, x_prev, err, stream=None,
+                                 prev: TreeDesc, path_rows, path_n, x_prev, err, stream=None,
                                  raise_on_error=True) -> int:
     """Publish the conv history of the previous step's accepted path (prev's
-    tree, path [B, Lmax], path_len [B], its conv input x_prev [B, prev R, C]),
-    then convolve desc's tree as conv_ancestry_gather does."""
+    tree; the path resolved by gdn_path_resolve into path_rows [B, Lmax] and
+    path_n [B]; its conv input x_prev [B, prev R, C]), then convolve desc's
+    tree as conv_ancestry_gather does."""
     C = int(x.shape[-1])
     P = int(hist.shape[0]) if hist is not None else 1
-    Lmax = int(path.shape[1])
+    Lmax = int(path_rows.shape[1])
     code = load_library().conv_ancestry_gather_publish(
         desc.ref(), _ptr(x), _ptr(hist), P, _ptr(state_idx), _ptr(w), _ptr(bias), _ptr(y), C,
-        int(act), prev.ref(), _ptr(path), _ptr(path_len), Lmax, _ptr(x_prev), _ptr(err),
+        int(act), prev.ref(), _ptr(path_rows), _ptr(path_n), Lmax, _ptr(x_prev), _ptr(err),
         _stream(stream))
     return _check(code, "conv_ancestry_gather_publish", raise_on_error)
 
 
 def gdn_tree_commit_verify(desc: TreeDesc, q, k, v, alpha, beta, state_pool, state_idx, out,
-                           prev: TreeDesc, path, path_len, k_prev, v_prev, alpha_prev,
+                           prev: TreeDesc, path_rows, path_n, k_prev, v_prev, alpha_prev,
                            beta_prev, err, flags: int = 0, stream=None,
                            raise_on_error=True) -> int:
-    """Commit the previous step's accepted path (prev's tree; its recorded
-    k_prev, v_prev, alpha_prev, beta_prev) into state_pool, then verify desc's
-    tree from the committed state into out (layouts as in gdn_tree_verify)."""
+    """Commit the previous step's accepted path (prev's tree; the path resolved
+    into path_rows / path_n; its recorded k_prev, v_prev, alpha_prev,
+    beta_prev) into state_pool, then verify desc's tree from the committed
+    state into out (layouts as in gdn_tree_verify)."""
     rs_qk, Hqk, dk = _rows_view(q, "q")
     rs_k, Hk, dk2 = _rows_view(k, "k")
     rs_v, Hv, dv = _rows_view(v, "v")
@@ -290,10 +292,10 @@ def gdn_tree_commit_verify(desc: TreeDesc, q, k, v, alpha, beta, state_pool, sta
     if Hkp != Hqk or Hvp != Hv or k_prev.dtype != q.dtype or v_prev.dtype != q.dtype:
         raise ValueError("previous operands must match the new ones in heads and dtype")
     P = int(state_pool.shape[0])
-    Lmax = int(path.shape[1])
+    Lmax = int(path_rows.shape[1])
     code = load_library().gdn_tree_commit_verify(
         desc.ref(), _ptr(q), _ptr(k), _ptr(v), rs_qk, rs_v, _ptr(alpha), _ptr(beta),
-        _ptr(state_pool), P, _ptr(state_idx), _ptr(out), prev.ref(), _ptr(path), _ptr(path_len),
+        _ptr(state_pool), P, _ptr(state_idx), _ptr(out), prev.ref(), _ptr(path_rows), _ptr(path_n),
         Lmax, _ptr(k_prev), _ptr(v_prev), rs_qkp, rs_vp, _ptr(alpha_prev), _ptr(beta_prev), Hqk,
         Hv, dk, dv, _dtype_code(q), int(flags), _ptr(err), _stream(stream))
     return _check(code, "gdn_tree_commit_verify", raise_on_error)

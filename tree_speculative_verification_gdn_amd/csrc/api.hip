@@ -125,21 +125,21 @@ int32_t gdn_tree_commit(const gdn_tree_desc* d, const int32_t* path, const int32
     if (!aligned(state_pool, 16)) return GDN_ERR_ARG;
     gdn::CommitArgs a{path, path_len, Lmax, k, v, row_stride_qk, row_stride_v, alpha, beta,
                       state_pool, P, state_idx, static_cast<const uint16_t*>(x),
-                      static_cast<uint16_t*>(hist), x ? C : 0, Hqk, Hv, dk, dtype, flags, err};
+                      static_cast<uint16_t*>(hist), x ? C : 0, Hqk, Hv, dk, dtype, flags, err, 0};
     return map_launch(gdn::launch_commit(*d, a, static_cast<hipStream_t>(stream)));
 }
 
 int32_t conv_ancestry_gather_publish(const gdn_tree_desc* d, const void* x, void* hist, int32_t P,
                                      const int32_t* state_idx, const void* w, const float* bias,
                                      void* y, int32_t C, int32_t act, const gdn_tree_desc* d_prev,
-                                     const int32_t* path, const int32_t* path_len, int32_t Lmax,
+                                     const int32_t* path_rows, const int32_t* path_n, int32_t Lmax,
                                      const void* x_prev, int32_t* err, void* stream) {
     int32_t st = check_desc(d);
     if (st != GDN_OK) return st;
     st = check_desc(d_prev);
     if (st != GDN_OK) return st;
     if (d_prev->B != d->B || d_prev->W != d->W) return GDN_ERR_ARG;
-    if (!x || !state_idx || !w || !y || !err || !path || !path_len || !x_prev || P < 1)
+    if (!x || !state_idx || !w || !y || !err || !path_rows || !path_n || !x_prev || P < 1)
         return GDN_ERR_ARG;
     if (d->W > 1 && !hist) return GDN_ERR_ARG;
     if (Lmax < 1 || Lmax > GDN_MAX_NODES) return GDN_ERR_UNSUPPORTED;
@@ -147,7 +147,7 @@ int32_t conv_ancestry_gather_publish(const gdn_tree_desc* d, const void* x, void
     if (act != GDN_ACT_NONE && act != GDN_ACT_SILU) return GDN_ERR_ARG;
     if (!aligned(x, 8) || !aligned(y, 8) || !aligned(x_prev, 8) || (hist && !aligned(hist, 8)))
         return GDN_ERR_ARG;
-    const gdn::ConvPublish pub{d_prev, path, path_len, Lmax, static_cast<const uint16_t*>(x_prev)};
+    const gdn::ConvPublish pub{d_prev, path_rows, path_n, Lmax, static_cast<const uint16_t*>(x_prev)};
     return map_launch(gdn::launch_conv(*d, static_cast<const uint16_t*>(x),
                                        static_cast<const uint16_t*>(hist), P, state_idx,
                                        static_cast<const uint16_t*>(w), bias,
@@ -159,7 +159,7 @@ int32_t gdn_tree_commit_verify(const gdn_tree_desc* d, const void* q, const void
                                int64_t row_stride_qk, int64_t row_stride_v, const float* alpha,
                                const float* beta, float* state_pool, int32_t P,
                                const int32_t* state_idx, void* out, const gdn_tree_desc* d_prev,
-                               const int32_t* path, const int32_t* path_len, int32_t Lmax,
+                               const int32_t* path_rows, const int32_t* path_n, int32_t Lmax,
                                const void* k_prev, const void* v_prev, int64_t row_stride_qk_prev,
                                int64_t row_stride_v_prev, const float* alpha_prev,
                                const float* beta_prev, int32_t Hqk, int32_t Hv, int32_t dk,
@@ -173,7 +173,7 @@ int32_t gdn_tree_commit_verify(const gdn_tree_desc* d, const void* q, const void
     st = check_heads(Hqk, Hv, dk, dv, dtype);
     if (st != GDN_OK) return st;
     if (!q || !k || !v || !alpha || !beta || !state_pool || !state_idx || !out || !err || P < 1 ||
-        !path || !path_len || !k_prev || !v_prev || !alpha_prev || !beta_prev)
+        !path_rows || !path_n || !k_prev || !v_prev || !alpha_prev || !beta_prev)
         return GDN_ERR_ARG;
     if (Lmax < 1 || Lmax > GDN_MAX_NODES) return GDN_ERR_UNSUPPORTED;
     if ((flags & ~(GDN_F_NORM_QK | GDN_F_OUT_BF16 | GDN_F_VALU)) != 0) return GDN_ERR_ARG;
@@ -187,8 +187,8 @@ int32_t gdn_tree_commit_verify(const gdn_tree_desc* d, const void* q, const void
                                state_idx, out, Hqk, Hv, dk, dtype, flags, err};
     a.pool = state_pool;
     a.prev = d_prev;
-    a.path = path;
-    a.path_len = path_len;
+    a.path_rows = path_rows;
+    a.path_n = path_n;
     a.Lmax = Lmax;
     a.k_prev = k_prev;
     a.v_prev = v_prev;

@@ -68,13 +68,11 @@ struct ConvKArgs {
     const float* bias;
     uint16_t* y;
     int32_t* err;
-    // previous step: its tree, accepted path and conv input
-    int B, Np, Rp, shared_p, Lmax;
-    const int32_t* parent_p;
-    const int32_t* node_row_p;
-    const int32_t* status_p;
-    const int32_t* path;
-    const int32_t* path_len;
+    // previous step: its accepted path resolved to rows and node counts,
+    // the previous tree's R and its conv input
+    int Rp, Lmax;
+    const int32_t* path_rows;
+    const int32_t* path_n;
     const uint16_t* x_prev;
 };
 
@@ -124,42 +122,35 @@ __global__ void __launch_bounds__(kConvThreads) conv_gather_kernel(const ConvKAr
     const int my_src = (H > 0) ? src_t[min(tid, N * H - 1)] : 0;  // N * H <= 192 < 256
     const int st = status[t];
     const int slot = state_idx[b];
-    // previous step's accepted path (PUB): its length, nodes, tree status and
-    // whether another request shares the slot
-    int len = 0, pnode = 0, pprev = 0, st_p = 1, dup = 0;
+    // previous step's accepted path (PUB), resolved: the node count n (-1
+    // and 0 publish nothing) and the physical rows
+    int n = 0, prow = 0;
     if constexpr (PUB) {
-        st_p = a.status_p[a.shared_p ? 0 : b];
-        len = a.path_len[b];
-        pnode = a.path[static_cast<size_t>(b) * a.Lmax + min(tid, a.Lmax - 1)];
-        pprev = __shfl(pnode, tid > 0 ? tid - 1 : 0, 64);  // path[tid - 1] (wave 0)
-        const int s2 = state_idx[min(tid, a.B - 1)];
-        dup = (tid < a.B && tid != b && s2 == slot) ? 1 : 0;
-        for (int b2 = tid + kConvThreads; b2 < a.B; b2 += kConvThreads)  // B > 256 only
-            dup |= (b2 != b && state_idx[b2] == slot) ? 1 : 0;
+        n = min(max(a.path_n[b], -1), a.Lmax);
+        prow = a.path_rows[static_cast<size_t>(b) * a.Lmax + min(tid, a.Lmax - 1)];
     }
-    if (st != 0) return;
+    // the new tree is convolved only if it is well formed; the publication of
+    // the previous path happens either way
+    const bool conv_ok = st == 0;
+    if (!PUB && !conv_ok) return;
     if (slot < 0 || slot >= P) {
-        if (blockIdx.x == 0 && tid == 0) atomicOr(err, GDN_EV_STATE);
+        if ((PUB || conv_ok) && blockIdx.x == 0 && tid == 0) atomicOr(err, GDN_EV_STATE);
         return;
     }
-    // the previous path nodes' parents and rows, ahead of the node rows below
-    // so that validating the path waits for them alone
-    int par = 0, prow = 0;
-    if constexpr (PUB) {
-        const size_t ti = static_cast<size_t>(a.shared_p ? 0 : b) * a.Np + min(max(pnode, 0), a.Np - 1);
-        par = a.parent_p[ti];
-        prow = a.node_row_p[ti];
+    __shared__ int32_t s_prow[kMaxNodes + 1];
+    if constexpr (PUB) s_prow[min(tid, a.Lmax)] = min(max(prow, 0), a.Rp - 1);  // spare entry Lmax
+    if (conv_ok) {  // uniform
+        for (int r = tid; r < R; r += kConvThreads) s_node_of_row[r] = -1;
     }
-    for (int r = tid; r < R; r += kConvThreads) s_node_of_row[r] = -1;
     __syncthreads();
-    if (tid < N) {
+    if (conv_ok && tid < N) {
         s_row[tid] = my_row;
         s_node_of_row[my_row] = tid;  // rows of a valid tree are injective and < R
     }
     __syncthreads();
     // tap sources as LDS rows; a source the descriptor build cannot have
     // produced (outside this tree's rows or history) is reported, not followed
-    if (tid < N * H) {
+    if (conv_ok && tid < N * H) {
         const int sv = my_src;
         int tap = (sv >= 0) ? ((sv < R) ? s_node_of_row[sv] : -1) : N + (-sv - 1);
         const bool bad = (sv >= 0) ? (tap < 0) : (sv < -H);
@@ -182,18 +173,18 @@ __global__ void __launch_bounds__(kConvThreads) conv_gather_kernel(const ConvKAr
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
         const int i = rs + p * kRowsPerPass;
-        if (p * kRowsPerPass < N)  // uniform: whole passes beyond N are skipped
+        if (conv_ok && p * kRowsPerPass < N)  // uniform: whole passes beyond N are skipped
             xin[p] = load_chunk<CPT>(x + (xb + s_row[min(i, N - 1)]) * C + c0);
     }
     // history entry m = rs (threads with rs >= H load entry H - 1 again); with
-    // publication also entry len + rs, which becomes entry rs when the path
+    // publication also entry n + rs, which becomes entry rs when the path
     // is shorter than the history
     Chunk<CPT> hc, hc_shift;
     const uint16_t* hs = hist + static_cast<size_t>(slot) * (H > 0 ? H : 1) * C;
     if (H > 0) hc = load_chunk<CPT>(hs + static_cast<size_t>(min(rs, H - 1)) * C + c0);
     if constexpr (PUB) {
         if (H > 0)
-            hc_shift = load_chunk<CPT>(hs + static_cast<size_t>(min(max(len, 0) + rs, H - 1)) * C + c0);
+            hc_shift = load_chunk<CPT>(hs + static_cast<size_t>(min(max(n, 0) + rs, H - 1)) * C + c0);
     }
     // weights w[c][0..W-1] of the lane's CPT channels as tap pairs per channel,
     // (w[c][2p], w[c][2p+1] or 0).  With W even that is the memory layout:
@@ -229,38 +220,20 @@ __global__ void __launch_bounds__(kConvThreads) conv_gather_kernel(const ConvKAr
                          bias[c0 + 4 * (rs & 1) + 1 < C ? c0 + 4 * (rs & 1) + 1 : c0],
                          bias[c0 + 4 * (rs & 1) + 2 < C ? c0 + 4 * (rs & 1) + 2 : c0],
                          bias[c0 + 4 * (rs & 1) + 3 < C ? c0 + 4 * (rs & 1) + 3 : c0]);
-    bool pub = false;
+    // publication (the path resolution validated the path): the x row of
+    // path node n + rs - H, oldest first
+    const bool pub = PUB && n > 0 && H > 0;
     Chunk<CPT> xp;
     if constexpr (PUB) {
-        // validate the previous path as the commit does: length in range, a
-        // parent chain from a root-level node of the previous tree, a slot no
-        // other request shares; a malformed path publishes nothing
-        __shared__ int s_bad;
-        __shared__ int32_t s_prow[kMaxNodes];
-        if (tid == 0) s_bad = 0;
-        __syncthreads();
-        const bool len_ok = len >= 0 && len <= a.Lmax;
-        int bad = dup ? GDN_EV_STATE : 0;
-        if (!len_ok) {
-            bad |= GDN_EV_PATH;
-        } else if (tid < len) {  // len <= Lmax <= 64: all in wave 0
-            if (pnode < 0 || pnode >= a.Np || par != (tid == 0 ? -1 : pprev)) bad |= GDN_EV_PATH;
-            s_prow[tid] = prow;
-        }
-        if (st_p == 0 && bad) atomicOr(&s_bad, bad);
-        __syncthreads();
-        bad = s_bad;
-        if (bad && blockIdx.x == 0 && tid == 0) atomicOr(err, bad);
-        pub = st_p == 0 && !bad && len > 0 && H > 0;
-        if (pub) {  // uniform: the x row of path node len + rs - H (oldest first)
-            const int j = min(max(len + rs - H, 0), len - 1);
+        if (pub) {  // uniform
+            const int j = min(max(n + rs - H, 0), n - 1);
             xp = load_chunk<CPT>(a.x_prev + (static_cast<size_t>(b) * a.Rp + s_prow[j]) * C + c0);
         }
     }
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
         const int i = rs + p * kRowsPerPass;
-        if (i < N) s_x[i * kTileLanes + lane] = xin[p];
+        if (conv_ok && i < N) s_x[i * kTileLanes + lane] = xin[p];
     }
     if constexpr (PUB) {
         // the old history must be in registers before any lane overwrites it
@@ -271,8 +244,8 @@ __global__ void __launch_bounds__(kConvThreads) conv_gather_kernel(const ConvKAr
             for (int e = 0; e < CPT / 2; ++e) asm volatile("" ::"v"(h0[e]), "v"(h1[e]));
         }
         __syncthreads();
-        if (pub) {  // new entry m = rs: old entry len + rs, or the x row above
-            hc = (len + rs < H) ? hc_shift : xp;
+        if (pub) {  // new entry m = rs: old entry n + rs, or the x row above
+            hc = (n + rs < H) ? hc_shift : xp;
             if (rs < H && active)
                 *reinterpret_cast<decltype(hc.u)*>(hist + (static_cast<size_t>(slot) * H + rs) * C + c0) = hc.u;
         }
@@ -294,7 +267,7 @@ __global__ void __launch_bounds__(kConvThreads) conv_gather_kernel(const ConvKAr
     }
     if (bias && rs < CPT / 4) *reinterpret_cast<float4*>(s_b + lane * CPT + 4 * rs) = bq;
     __syncthreads();
-    if (!active) return;
+    if (!active || !conv_ok) return;
 
     // taps in bf16 pairs on v_dot2_f32_bf16 (exact bf16 products, fp32 sums):
     // for channel c and pair p, (x of tap 2p, x of tap 2p+1) . (w[c][2p], w[c][2p+1])
@@ -356,9 +329,10 @@ hipError_t launch_conv(const gdn_tree_desc& d, const uint16_t* x, const uint16_t
     a.x = x; a.hist = const_cast<uint16_t*>(hist); a.state_idx = state_idx; a.w = w; a.bias = bias;
     a.y = y; a.err = err;
     if (pub != nullptr) {
-        a.B = d.B; a.Np = pub->prev->N; a.Rp = pub->prev->R; a.shared_p = pub->prev->shared;
-        a.Lmax = pub->Lmax; a.parent_p = pub->prev->parent; a.node_row_p = pub->prev->node_row;
-        a.status_p = pub->prev->status; a.path = pub->path; a.path_len = pub->path_len;
+        a.Rp = pub->prev->R;
+        a.Lmax = pub->Lmax;
+        a.path_rows = pub->path_rows;
+        a.path_n = pub->path_n;
         a.x_prev = pub->x_prev;
     }
     const bool small = d.N <= (kMaxPasses / 2) * kRowsPerPass;  // fewer row registers

@@ -54,9 +54,9 @@ hipError_t launch_desc_build(const gdn_tree_desc& d, int32_t* err, hipStream_t s
 // Conv-history publication of the previous step's accepted path, done by the
 // conv of the next step before its taps read the history.
 struct ConvPublish {
-    const gdn_tree_desc* prev;  // previous step's tree (validated, status built)
-    const int32_t* path;
-    const int32_t* path_len;
+    const gdn_tree_desc* prev;  // previous step's tree (its R)
+    const int32_t* path_rows;   // [B][Lmax] physical rows of the accepted path (resolved)
+    const int32_t* path_n;      // [B] nodes to publish; -1 / 0: none
     int Lmax;
     const uint16_t* x_prev;     // previous step's conv input [B][prev R][C]
 };
@@ -87,8 +87,8 @@ bool verify_uses_mfma(const gdn_tree_desc& d, const VerifyArgs& a);
 size_t verify_valu_lds_bytes(int N, int D);
 
 struct CommitArgs {
-    const int32_t* path;
-    const int32_t* path_len;
+    const int32_t* path;      // logical ids [B][Lmax], or physical rows when resolved
+    const int32_t* path_len;  // [B], or the resolved node counts (-1: nothing written)
     int Lmax;
     const void* k;
     const void* v;
@@ -104,6 +104,7 @@ struct CommitArgs {
     int Hqk, Hv, D;
     int dtype, flags;
     int32_t* err;
+    int resolved;  // 1: path / path_len come from the path resolution (no validation here)
 };
 hipError_t launch_commit(const gdn_tree_desc& d, const CommitArgs& a, hipStream_t s);
 size_t commit_lds_bytes(int Lmax, int D, int dtype);
@@ -114,8 +115,8 @@ struct CommitVerifyArgs {
     VerifyArgs verify;          // the next tree; verify.pool is the pool below
     float* pool;                // written: the committed states
     const gdn_tree_desc* prev;  // the previous step's tree
-    const int32_t* path;
-    const int32_t* path_len;
+    const int32_t* path_rows;   // resolved accepted path: rows [B][Lmax] and node counts [B]
+    const int32_t* path_n;
     int Lmax;
     const void* k_prev;
     const void* v_prev;

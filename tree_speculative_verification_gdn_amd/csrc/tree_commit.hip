@@ -146,7 +146,7 @@ size_t commit_lds_bytes(int Lmax, int D, int dtype) {
                                                     : commit_lds_layout<float>(Lmax, D).total);
 }
 
-template <int D, typename T, bool VEC>
+template <int D, typename T, bool VEC, bool RES>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
     commit_kernel(int B, int N, int R, int W, int shared, const int32_t* __restrict__ parent,
                   const int32_t* __restrict__ node_row, const int32_t* __restrict__ status,
@@ -180,42 +180,50 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
     const int r = tid / TPR;
     const int part = tid % TPR;
 
-    // ---- round trip 1: everything that depends only on (b, h); slot, path
+    // ---- round trip 1: everything that depends only on (b, h); slot, path.
+    //      RES: path / path_len are the resolved rows and node counts (the
+    //      path resolution validated them and reported any error)
     const int st = status[t];
     const int slot = state_idx[b];
-    const int len = path_len[b];
+    const int len = RES ? min(path_len[b], Lmax) : path_len[b];
     // Loads are unconditional, from indexes clamped into range; what a lane
     // does not need is dropped afterwards (a load under a per-lane condition
     // becomes a branch that waits for it before anything else issues).
     const int pnode = path[static_cast<size_t>(b) * Lmax + min(tid, Lmax - 1)];
-    const int prev = __shfl(pnode, tid > 0 ? tid - 1 : 0, 64);  // path[tid - 1] (wave 0)
-    int dup = 0;
-    for (int b2 = tid; b2 < B; b2 += kThreads) dup |= (b2 != b && state_idx[b2] == slot) ? 1 : 0;
-    if (st != 0) return;  // malformed tree: reported by the descriptor build
-    if (tid == 0) s_bad = 0;
+    if constexpr (RES) {
+        if (st != 0 || len <= 0 || slot < 0 || slot >= P) return;  // nothing to commit
+        s_rows[min(tid, Lmax - 1)] = min(max(pnode, 0), R - 1);    // lanes past Lmax repeat the last
+        __syncthreads();
+    } else {
+        const int prev = __shfl(pnode, tid > 0 ? tid - 1 : 0, 64);  // path[tid - 1] (wave 0)
+        int dup = 0;
+        for (int b2 = tid; b2 < B; b2 += kThreads) dup |= (b2 != b && state_idx[b2] == slot) ? 1 : 0;
+        if (st != 0) return;  // malformed tree: reported by the descriptor build
+        if (tid == 0) s_bad = 0;
 
-    // ---- round trip 2: the path nodes' parents and rows; validation
-    const bool slot_ok = slot >= 0 && slot < P;
-    const bool len_ok = len >= 0 && len <= Lmax;
-    const size_t ti = static_cast<size_t>(t) * N + min(max(pnode, 0), N - 1);
-    const int par = parent[ti];
-    const int prow = node_row[ti];
-    int bad = (slot_ok ? 0 : GDN_EV_STATE) | (dup ? GDN_EV_STATE : 0);
-    if (!len_ok) {
-        bad |= GDN_EV_PATH;
-    } else if (tid < len) {  // len <= Lmax <= 64: all in wave 0
-        if (pnode < 0 || pnode >= N || par != (tid == 0 ? -1 : prev)) bad |= GDN_EV_PATH;
-        s_rows[tid] = prow;
+        // ---- round trip 2: the path nodes' parents and rows; validation
+        const bool slot_ok = slot >= 0 && slot < P;
+        const bool len_ok = len >= 0 && len <= Lmax;
+        const size_t ti = static_cast<size_t>(t) * N + min(max(pnode, 0), N - 1);
+        const int par = parent[ti];
+        const int prow = node_row[ti];
+        int bad = (slot_ok ? 0 : GDN_EV_STATE) | (dup ? GDN_EV_STATE : 0);
+        if (!len_ok) {
+            bad |= GDN_EV_PATH;
+        } else if (tid < len) {  // len <= Lmax <= 64: all in wave 0
+            if (pnode < 0 || pnode >= N || par != (tid == 0 ? -1 : prev)) bad |= GDN_EV_PATH;
+            s_rows[tid] = prow;
+        }
+        __syncthreads();  // s_bad initialised
+        if (bad) atomicOr(&s_bad, bad);
+        __syncthreads();
+        bad = s_bad;
+        if (bad) {
+            if (h == 0 && tid == 0) atomicOr(err, bad);
+            return;
+        }
+        if (len == 0) return;  // nothing accepted: state and history stay as they are
     }
-    __syncthreads();  // s_bad initialised
-    if (bad) atomicOr(&s_bad, bad);
-    __syncthreads();
-    bad = s_bad;
-    if (bad) {
-        if (h == 0 && tid == 0) atomicOr(err, bad);
-        return;
-    }
-    if (len == 0) return;  // nothing accepted: state and history stay as they are
 
     // ---- round trip 3: the path's gates and k/v rows, the conv rows, then the
     //      state.  A wave's loads retire in issue order, so everything staged
@@ -393,7 +401,7 @@ hipError_t launch_commit_t(const gdn_tree_desc& d, const CommitArgs& a, int norm
     const int hvec = (a.x != nullptr && (a.C & 3) == 0 &&
                       (reinterpret_cast<uintptr_t>(a.x) & 7) == 0 &&
                       (reinterpret_cast<uintptr_t>(a.hist) & 7) == 0) ? 1 : 0;
-    auto kfn = commit_kernel<D, T, VEC>;
+    auto kfn = a.resolved ? commit_kernel<D, T, VEC, true> : commit_kernel<D, T, VEC, false>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(lds));

@@ -98,7 +98,7 @@ __host__ __device__ inline MfmaLds mfma_lds_layout(int N, int NPB, int Lp = 0) {
     // their own; the rest is staged after the M solve and may overlay the
     // Gram block.
     const int lp = Lp > 0 ? Lp : 0;
-    L.rowp = off; off += align_up(lp * 4, 16);
+    L.rowp = off; off += align_up((lp + 1) * 4, 16);  // one spare entry
     const int gsz = lp > 0 ? kMfmaPath * kMfmaPath * 4 : 0;  // after the scales: a segment Gram
     const int psize = align_up(lp * kKQStride, 16) + align_up(lp * kD * 2, 16) + 2 * align_up(lp * 4, 16) +
                       align_up(lp * 4 + gsz, 16);
@@ -172,14 +172,12 @@ __host__ __device__ inline MfmaLds layer_lds_layout(int N, int H, int Lmax) {
     return L;
 }
 
-// The previous step's accepted path for the fused commit (kernel argument).
+// The previous step's accepted path for the fused commit, resolved to
+// physical rows (kernel argument), and its recorded operands.
 struct CommitPrev {
-    int B, Np, Rp, shared_p, Lmax;
-    const int32_t* parent_p;
-    const int32_t* node_row_p;
-    const int32_t* status_p;
-    const int32_t* path;
-    const int32_t* path_len;
+    int Rp, Lmax;
+    const int32_t* path_rows;
+    const int32_t* path_n;
     const uint16_t* kp;
     const uint16_t* vp;
     int64_t rs_qk_p, rs_v_p;
@@ -406,22 +404,17 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     const int my_row = node_row[tb + my_node];
     const uint64_t my_anc = anc_g[tb + my_node];
     const int my_dep = depth_g[tb + my_node];
-    //   (a1') fused: the previous step's accepted path, its tree's status and
-    //   whether another request shares the slot
-    int len = 0, pnode = 0, pprev = 0, st_p = 1, dup = 0;
-    if constexpr (FUSED) {
-        st_p = cp.status_p[cp.shared_p ? 0 : b];
-        len = cp.path_len[b];
-        pnode = cp.path[static_cast<size_t>(b) * cp.Lmax + min(tid, cp.Lmax - 1)];
-        pprev = __shfl(pnode, tid > 0 ? tid - 1 : 0, 64);  // path[tid - 1] (wave 0)
-        const int s2 = state_idx[min(tid, cp.B - 1)];
-        dup = (tid < cp.B && tid != b && s2 == slot) ? 1 : 0;
-        for (int b2 = tid + kThreads; b2 < cp.B; b2 += kThreads)  // B > 256 only
-            dup |= (b2 != b && state_idx[b2] == slot) ? 1 : 0;
-    }
-    //   (a1'') layer step: the resolved path, the tree's parents (conv taps),
-    //   the conv weights (as tap pairs) and bias of the unit's channels
+    //   (a1') the previous step's accepted path, resolved to its node count
+    //   (-1: neither state nor history is written) and physical rows
+    const int LmaxP = LAYER ? li.Lmax : (FUSED ? cp.Lmax : 1);
+    const int RpP = LAYER ? li.Rp : (FUSED ? cp.Rp : 1);
     int pn = 0, prow = 0, my_par = -1;
+    if constexpr (FUSED) {
+        pn = cp.path_n[b];
+        prow = cp.path_rows[static_cast<size_t>(b) * cp.Lmax + min(tid, cp.Lmax - 1)];
+    }
+    //   (a1'') layer step: the tree's parents (conv taps), the conv weights
+    //   (as tap pairs) and bias of the unit's channels
     uint32_t wq[3] = {0u, 0u, 0u};
     float bq[3] = {0.f, 0.f, 0.f};
     if constexpr (LAYER) {
@@ -453,9 +446,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     float* s_bia = reinterpret_cast<float*>(lds + L.bia);
     int32_t* s_par = reinterpret_cast<int32_t*>(lds + L.par);
     uint8_t* s_tap = reinterpret_cast<uint8_t*>(lds + L.tap);
-    // layer step: n = -1 writes neither state nor history; nc path nodes commit
-    const int n_res = LAYER ? min(max(pn, -1), li.Lmax) : 0;
+    // n = -1 writes neither state nor history; nc path nodes commit
+    const int n_res = COMMIT ? min(max(pn, -1), LmaxP) : 0;
     const int nc = n_res > 0 ? n_res : 0;
+    if constexpr (FUSED) {
+        s_rowp[min(tid, cp.Lmax)] = prow;  // every lane writes (spare entry Lmax)
+        __syncthreads();
+    }
     if constexpr (LAYER) {
         // every lane writes (spare entries Lmax and N)
         s_rowp[min(tid, li.Lmax)] = prow;
@@ -473,8 +470,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     }
     // physical row of path node j of the previous tree, clamped into range
     auto prow_at = [&](int j) -> int {
-        const int r = s_rowp[min(max(j, 0), li.Lmax - 1)];
-        return min(max(r, 0), li.Rp - 1);
+        const int r = s_rowp[min(max(j, 0), LmaxP - 1)];
+        return min(max(r, 0), RpP - 1);
     };
     //   (a2) K/Q/V chunks and the gates of every node (rows of a valid tree are
     //        in range, so the clamped loads are too)
@@ -530,12 +527,17 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
         p_al = li.alpha_p[gi];
         p_be = li.beta_p[gi];
     }
-    //   (a2') fused: parents and rows of the previous path's nodes
-    int ppar = 0, pprow = 0;
+    //   (a2') fused: the previous path's k/v rows (its first kMfmaPath rows)
+    //   and gates
     if constexpr (FUSED) {
-        const size_t ti = static_cast<size_t>(cp.shared_p ? 0 : b) * cp.Np + min(max(pnode, 0), cp.Np - 1);
-        ppar = cp.parent_p[ti];
-        pprow = cp.node_row_p[ti];
+        const size_t rbp = static_cast<size_t>(b) * cp.Rp + prow_at(min(tid >> 5, nc - 1));
+        pk_val = *reinterpret_cast<const uint2*>(cp.kp + rbp * cp.rs_qk_p + static_cast<size_t>(g) * kD +
+                                                 (tid & 31) * 4);
+        pv_val = *reinterpret_cast<const uint2*>(cp.vp + rbp * cp.rs_v_p + static_cast<size_t>(h) * kD +
+                                                 (tid & 31) * 4);
+        const size_t gi = (static_cast<size_t>(b) * cp.Rp + prow_at(min(tid, nc - 1))) * Hv + h;
+        p_al = cp.alpha_p[gi];
+        p_be = cp.beta_p[gi];
     }
     asm volatile("" ::: "memory");  // keep the state loads behind the loads above
     //   (a3) the committed state: lane (r_own, hf) holds 64 elements of row r_own
@@ -548,40 +550,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
         sreg[2 * s + 1] = *reinterpret_cast<const float4*>(Sb + 16 * s + 8);
     }
 
-    // fused: validate the previous path as the commit does (length in range,
-    // a parent chain from a root-level node of the previous tree, a slot no
-    // other request shares), then load its k/v rows and gates
-    bool cok = false;
     if constexpr (FUSED) {
-        __shared__ int s_bad;
-        if (tid == 0) s_bad = 0;
-        __syncthreads();
-        const bool len_ok = len >= 0 && len <= cp.Lmax;
-        int bad = dup ? GDN_EV_STATE : 0;
-        if (!len_ok) {
-            bad |= GDN_EV_PATH;
-        } else if (tid < len) {  // len <= Lmax <= 64: all in wave 0
-            if (pnode < 0 || pnode >= cp.Np || ppar != (tid == 0 ? -1 : pprev)) bad |= GDN_EV_PATH;
-            s_rowp[tid] = pprow;
-        }
-        if (st_p == 0 && bad) atomicOr(&s_bad, bad);
-        __syncthreads();
-        bad = s_bad;
-        if (bad && h == 0 && tid == 0) atomicOr(err, bad);
-        cok = st_p == 0 && !bad && len > 0;
-        if (cok) {  // uniform: the first 8 path rows' k/v chunks and every gate
-            const int gp = static_cast<int>((static_cast<int64_t>(h) * Hqk) / Hv);
-            const size_t rowbp = static_cast<size_t>(b) * cp.Rp;
-            const int jj = min(tid >> 5, len - 1);
-            const size_t rbp = rowbp + s_rowp[jj];
-            pk_val = *reinterpret_cast<const uint2*>(cp.kp + rbp * cp.rs_qk_p + static_cast<size_t>(gp) * kD +
-                                                     (tid & 31) * 4);
-            pv_val = *reinterpret_cast<const uint2*>(cp.vp + rbp * cp.rs_v_p + static_cast<size_t>(h) * kD +
-                                                     (tid & 31) * 4);
-            const size_t gi = (rowbp + s_rowp[min(tid, len - 1)]) * Hv + h;
-            p_al = cp.alpha_p[gi];
-            p_be = cp.beta_p[gi];
-        }
+        // used under per-lane conditions after the M solve: take delivery
+        // here (the state, issued after them, stays in flight)
+        asm volatile("" ::"v"(pk_val.x), "v"(pk_val.y), "v"(pv_val.x), "v"(pv_val.y), "v"(p_al), "v"(p_be));
     }
 
     // layer step: publish the new conv history, convolve the previous path's
@@ -958,14 +930,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     // publish the state (LumoTree, Sec. IV-B):
     //   u = b_j (v_j - a_j S k^_j),  S <- a_j S + u k^_j^T,  k^_j = sc_j k_j
     if constexpr (COMMIT) {
-        const bool do_commit = FUSED ? cok : nc > 0;
-        const int plen = FUSED ? len : nc;
+        const bool do_commit = nc > 0;
+        const int plen = nc;
         if (do_commit) {  // uniform
             const int jj = tid >> 5;
             const int chp = tid & 31;
           if constexpr (FUSED) {
             // the staged path overlays the Gram block, dead after the M solve
-            const int cpl = len * 32;  // 8-byte chunks of the path's k (and of v)
+            const int cpl = nc * 32;  // 8-byte chunks of the path's k (and of v)
             float ss = sumsq_bf16x4(pk_val);
 #pragma unroll
             for (int off = 16; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
@@ -976,11 +948,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
             }
             for (int it0 = kThreads; it0 < cpl; it0 += kThreads) {  // paths longer than 8 rows
                 const int it = it0 + tid;
-                const int j2 = min(it >> 5, len - 1);
-                const size_t rbp = static_cast<size_t>(b) * cp.Rp + s_rowp[j2];
-                const int gp = static_cast<int>((static_cast<int64_t>(h) * Hqk) / Hv);
+                const size_t rbp = static_cast<size_t>(b) * cp.Rp + prow_at(min(it >> 5, nc - 1));
                 const uint2 kc = *reinterpret_cast<const uint2*>(
-                    cp.kp + rbp * cp.rs_qk_p + static_cast<size_t>(gp) * kD + chp * 4);
+                    cp.kp + rbp * cp.rs_qk_p + static_cast<size_t>(g) * kD + chp * 4);
                 const uint2 vc = *reinterpret_cast<const uint2*>(
                     cp.vp + rbp * cp.rs_v_p + static_cast<size_t>(h) * kD + chp * 4);
                 float s2 = sumsq_bf16x4(kc);
@@ -992,7 +962,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                     if (chp == 0) s_scp[it >> 5] = norm ? 1.0f / sqrtf(s2 + 1e-6f) : 1.0f;
                 }
             }
-            if (tid < len) {
+            if (tid < nc) {
                 s_alp[tid] = p_al;
                 s_bep[tid] = p_be;
             }
@@ -1540,16 +1510,10 @@ hipError_t launch_commit_verify(const gdn_tree_desc& d, const CommitVerifyArgs& 
         const size_t lds = static_cast<size_t>(mfma_lds_layout(d.N, NPB, a.Lmax).total);
         if (lds <= kMaxLds) {
             CommitPrev cp{};
-            cp.B = d.B;
-            cp.Np = dp.N;
             cp.Rp = dp.R;
-            cp.shared_p = dp.shared;
             cp.Lmax = a.Lmax;
-            cp.parent_p = dp.parent;
-            cp.node_row_p = dp.node_row;
-            cp.status_p = dp.status;
-            cp.path = a.path;
-            cp.path_len = a.path_len;
+            cp.path_rows = a.path_rows;
+            cp.path_n = a.path_n;
             cp.kp = static_cast<const uint16_t*>(a.k_prev);
             cp.vp = static_cast<const uint16_t*>(a.v_prev);
             cp.rs_qk_p = a.rs_qk_prev;
@@ -1566,9 +1530,9 @@ hipError_t launch_commit_verify(const gdn_tree_desc& d, const CommitVerifyArgs& 
         }
     }
     // other shapes: the commit, then the verify (the same result in two launches)
-    CommitArgs ca{a.path, a.path_len, a.Lmax, a.k_prev, a.v_prev, a.rs_qk_prev, a.rs_v_prev,
+    CommitArgs ca{a.path_rows, a.path_n, a.Lmax, a.k_prev, a.v_prev, a.rs_qk_prev, a.rs_v_prev,
                   a.alpha_prev, a.beta_prev, a.pool, va.P, va.state_idx, nullptr, nullptr, 0,
-                  va.Hqk, va.Hv, va.D, va.dtype, va.flags & GDN_F_NORM_QK, va.err};
+                  va.Hqk, va.Hv, va.D, va.dtype, va.flags & GDN_F_NORM_QK, va.err, 1};
     hipError_t e = launch_commit(dp, ca, s);
     if (e != hipSuccess) return e;
     return launch_verify(d, va, s);
