@@ -8,7 +8,13 @@ state): the descriptor build, the ancestry-gathered conv, the tree verify, the
 commit of an accepted path into the state and the conv-history publication.
 
 Three step shapes (``--mode``):
-  layer     (default) the steady-state decode step in one launch per layer:
+  fused     (default) gdn_step_prepare -> conv_ancestry_gather_publish ->
+              gdn_tree_commit_verify
+            the steady-state decode step in two launches per layer (after the
+            step's shared prepare): the previous step's accepted path is
+            committed and its conv history published inside this step's conv
+            and verify, so the state is read once and written once.
+  layer     the same step in one launch per layer:
               gdn_step_prepare -> gdn_layer_step
             (the first once per step for all layers: the new tree's
             descriptor and the previous path's rows); the layer step
@@ -16,9 +22,6 @@ Three step shapes (``--mode``):
             history into the other of two history buffers, and convolves and
             verifies the new tree: the state is read once and written once,
             the conv output never goes to memory.
-  fused     gdn_step_prepare -> conv_ancestry_gather_publish ->
-              gdn_tree_commit_verify
-            the same step in two launches, the conv output written and read.
   separate  gdn_tree_desc_build -> conv_ancestry_gather -> gdn_tree_verify
             -> gdn_tree_commit (this step's own path), the state read twice.
 All three commit one path and verify one tree per step.
@@ -140,11 +143,13 @@ def byte_model(cfg, cur, prev, mode):
     elif mode == "fused":
         state_w, path_rows = bytes_commit_state(cfg, prev)
         out = {"prepare": out["desc"] + bytes_resolve(cfg, prev)}
-        out["conv"] = bytes_conv(cfg, cur) + bytes_publish(cfg, prev)
+        if cfg.conv_W > 0:
+            out["conv"] = bytes_conv(cfg, cur) + bytes_publish(cfg, prev)
         out["commit_verify"] = bytes_verify(cfg, cur) + state_w + path_rows
     else:
         state_w, path_rows = bytes_commit_state(cfg, cur)
-        out["conv"] = bytes_conv(cfg, cur)
+        if cfg.conv_W > 0:
+            out["conv"] = bytes_conv(cfg, cur)
         out["verify"] = bytes_verify(cfg, cur)
         B, N, D, Hv, Hqk, W, C = _common(cfg, cur)
         hist_read = int((cur["path_len"] > 0).sum()) * (W - 1) * C * 2 if cfg.conv_W > 1 else 0
@@ -270,10 +275,10 @@ class Instance:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=4)
-    ap.add_argument("--mode", choices=("layer", "fused", "separate"), default="layer")
+    ap.add_argument("--mode", choices=("fused", "layer", "separate"), default="fused")
     ap.add_argument("--seed", type=int, default=2026)
     ap.add_argument("--sets", type=int, default=2, help="independent layer instances rotated per step")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -330,8 +335,10 @@ def main():
     log(f"[bench] {args.mode} mode: inputs for {cfg.name} x{args.sets} ready in "
         f"{time.perf_counter() - t0:.1f} s")
 
+    has_conv = cfg.conv_W > 0
     names = (("prepare", "layer") if layer else
-             ("prepare", "conv", "commit_verify") if fused else ("desc", "conv", "verify", "commit"))
+             ("prepare",) + (("conv",) if has_conv else ()) + ("commit_verify",) if fused else
+             ("desc",) + (("conv",) if has_conv else ()) + ("verify", "commit"))
 
     def step(inst, ev=None):
         cur = inst.slots[inst.turn % len(inst.slots)]
@@ -361,11 +368,11 @@ def main():
             g.gdn_step_prepare(cur.desc, prev.desc, prev.path, prev.path_len, inst.state_idx, inst.P,
                                inst.path_rows, inst.path_n, err)
             mark()
-            if cfg.conv_W > 0:
+            if has_conv:
                 g.conv_ancestry_gather_publish(cur.desc, cur.x, inst.hist, inst.state_idx, inst.w,
                                                None, cur.y, cfg.act, prev.desc, inst.path_rows,
                                                inst.path_n, prev.x, err)
-            mark()
+                mark()
             g.gdn_tree_commit_verify(cur.desc, cur.q, cur.k, cur.v, cur.alpha, cur.beta,
                                      inst.pool, inst.state_idx, cur.out, prev.desc, inst.path_rows,
                                      inst.path_n, prev.k, prev.v, prev.alpha, prev.beta, err,
@@ -373,10 +380,10 @@ def main():
         else:
             g.gdn_tree_desc_build(cur.desc, err)
             mark()
-            if cfg.conv_W > 0:
+            if has_conv:
                 g.conv_ancestry_gather(cur.desc, cur.x, inst.hist, inst.state_idx, inst.w, None,
                                        cur.y, cfg.act, err)
-            mark()
+                mark()
             g.gdn_tree_verify(cur.desc, cur.q, cur.k, cur.v, cur.alpha, cur.beta, inst.pool,
                               inst.state_idx, cur.out, err, flags=flags)
             mark()
@@ -391,22 +398,33 @@ def main():
         step(insts[i % len(insts)])
     torch.cuda.synchronize()
 
-    nmarks = len(names) + 1
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nmarks)] for _ in range(args.steps)]
+    # the timed steps: events only around the whole run (an event recorded
+    # between two launches adds a few µs of its own to the timeline)
     bytes_steps = []
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
+    e0.record()
     for i in range(args.steps):
-        cur, prev = step(insts[i % len(insts)], evs[i])
+        cur, prev = step(insts[i % len(insts)])
         bytes_steps.append(byte_model(cfg, cur.case, prev.case, args.mode))
+    e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
+    total_ms = e0.elapsed_time(e1)
+    # then the same number of steps again with an event between launches, for
+    # the per-kernel durations
+    nmarks = len(names) + 1
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nmarks)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(insts[i % len(insts)], evs[i])
+    torch.cuda.synchronize()
     if int(err.item()) != 0:
         log(f"[bench] device error word {int(err.item())}")
         sys.exit(3)
 
     per = {n: [ev[j].elapsed_time(ev[j + 1]) for ev in evs] for j, n in enumerate(names)}
-    total_ms = evs[0][0].elapsed_time(evs[-1][-1])
     ms_per_step = total_ms / args.steps
     avg = {n: float(np.mean(per[n])) for n in names}
     bytes_avg = {n: float(np.mean([b[n] for b in bytes_steps])) for n in names}
@@ -417,7 +435,9 @@ def main():
         gbs = bytes_avg[n] / (avg[n] / 1e3) / 1e9 if avg[n] > 0 else 0.0
         log(f"[bench] {n:13s} {avg[n] * 1e3:9.1f} us  {bytes_avg[n] / 1e6:8.1f} MB  "
             f"{gbs:8.1f} GB/s  {gbs / PEAK_HBM_GBS * 100:5.1f}% of 8 TB/s")
-    log(f"[bench] step {ms_per_step * 1e3:.1f} us (events), wall {wall / args.steps * 1e6:.1f} us, "
+    log(f"[bench] step {ms_per_step * 1e3:.1f} us (events around the run), wall "
+        f"{wall / args.steps * 1e6:.1f} us; with an event between launches "
+        f"{evs[0][0].elapsed_time(evs[-1][-1]) / args.steps * 1e3:.1f} us; "
         f"{step_bytes / 1e6:.1f} MB -> {step_bytes / (ms_per_step / 1e3) / 1e9:.1f} GB/s")
 
     dom = max((n for n in names if n not in ("desc", "prepare")), key=lambda n: avg[n])

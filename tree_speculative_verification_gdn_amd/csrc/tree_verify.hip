@@ -70,49 +70,56 @@ struct MfmaLds {
 __host__ __device__ inline int align_up(int x, int a) { return (x + a - 1) / a * a; }
 
 __host__ __device__ inline MfmaLds mfma_lds_layout(int N, int NPB, int Lp = 0) {
-    MfmaLds L;
+    MfmaLds L{};
     const int NP = 32 * NPB;
     const int MB = 2 * NPB;
+    const int T = N * (N + 1) / 2;  // Gram entries j <= i (ancestors have smaller indices)
     int off = 0;
     L.mstride = NP * 2 + 8;
+    // live for the whole kernel (V too while one 32-row block is staged early)
     L.a = off;    off += align_up(MB * 32 * kKQStride, 16);  // K/Q rows (bf16)
-    L.v = off;    off += align_up(N * kD * 2, 16);           // V rows (bf16)
-    L.gk = off;   off += align_up(NP * NP * 4, 16);  // [i][j]: k_i . k_j (raw operands)
-    L.gq = off;   off += align_up(NP * NP * 4, 16);  // [i][j]: q_i . k_j
-    L.nrm = off;  off += align_up(2 * NP * 4, 16);   // squared norms by slot
-    L.sk = off;   off += align_up(N * 4, 16);
-    L.sq = off;   off += align_up(N * 4, 16);
+    if (NPB == 1) {
+        L.v = off;  off += align_up(N * kD * 2, 16);          // V rows (bf16)
+    }
     // per-node arrays written by every lane carry one spare entry (index N)
-    L.al = off;   off += align_up((N + 1) * 4, 16);
     L.be = off;   off += align_up((N + 1) * 4, 16);
     L.rows = off; off += align_up((N + 1) * 4, 16);
-    L.dep = off;  off += align_up((N + 1) * 4, 16);
-    L.anc = off;  off += align_up((N + 1) * 8, 16);
-    L.cidx = off; off += align_up(N * N, 16);      // [i][p]: node at depth p+1 on i's root path
     L.mh = off;   off += align_up(NP * L.mstride, 16);
     L.ml = off;   off += align_up(NP * L.mstride, 16);
     L.cr = off;   off += align_up(N * 4, 16);      // P_i / |k_i|
     L.cq = off;   off += align_up(N * 4, 16);      // P_i / |q_i|
-    // previous path region, Lp rows (0: none).  The path's rows are written
-    // at validation, before the Gram block is formed, so they get space of
-    // their own; the rest is staged after the M solve and may overlay the
-    // Gram block.
+    // the previous path's rows are written at the start, so they get space of their own
     const int lp = Lp > 0 ? Lp : 0;
     L.rowp = off; off += align_up((lp + 1) * 4, 16);  // one spare entry
-    const int gsz = lp > 0 ? kMfmaPath * kMfmaPath * 4 : 0;  // after the scales: a segment Gram
-    const int psize = align_up(lp * kKQStride, 16) + align_up(lp * kD * 2, 16) + 2 * align_up(lp * 4, 16) +
-                      align_up(lp * 4 + gsz, 16);
-    int poff = (psize <= 2 * NP * NP * 4) ? L.gk : off;
-    if (poff == off) off += psize;
-    L.kp = poff;   poff += align_up(lp * kKQStride, 16);
-    L.vp = poff;   poff += align_up(lp * kD * 2, 16);
-    L.alp = poff;  poff += align_up(lp * 4, 16);
-    L.bep = poff;  poff += align_up(lp * 4, 16);
-    L.scp = poff;  poff += align_up(lp * 4 + gsz, 16);  // scales, then the segment Gram
-    L.total = off;
+    // one region, used up to the M solve by the Gram block and the node
+    // metadata, after it by the V rows (two 32-row blocks: staged late) and
+    // the previous path's staged rows
+    const int U = off;
+    int f = U;
+    L.gk = f;   f += align_up(T * 4, 16);   // k_i . k_j (raw operands), row-major lower triangle
+    L.gq = f;   f += align_up(T * 4, 16);   // q_i . k_j
+    L.nrm = f;  f += align_up(2 * NP * 4, 16);   // squared norms by slot
+    L.sk = f;   f += align_up(N * 4, 16);
+    L.sq = f;   f += align_up(N * 4, 16);
+    L.al = f;   f += align_up((N + 1) * 4, 16);
+    L.dep = f;  f += align_up((N + 1) * 4, 16);
+    L.anc = f;  f += align_up((N + 1) * 8, 16);
+    L.cidx = f; f += align_up(N * N, 16);        // [i][p]: node at depth p+1 on i's root path
+    int uend = f;
+    f = U;
+    if (NPB != 1) {
+        L.v = f;  f += align_up(N * kD * 2, 16);
+    }
+    const int gsz = lp > 0 ? kMfmaPath * kMfmaPath * 4 : 0;
+    L.kp = f;   f += align_up(lp * kKQStride, 16);
+    L.vp = f;   f += align_up(lp * kD * 2, 16);
+    L.alp = f;  f += align_up(lp * 4, 16);
+    L.bep = f;  f += align_up(lp * 4, 16);
+    L.scp = f;  f += align_up(lp * 4 + gsz, 16);  // scales, then the segment Gram
+    uend = uend > f ? uend : f;
+    L.total = uend;
     return L;
 }
-
 
 __host__ __device__ inline int imax(int a, int b) { return a > b ? a : b; }
 
@@ -132,8 +139,8 @@ __host__ __device__ inline MfmaLds layer_lds_layout(int N, int H, int Lmax) {
     L.v = off;    off += align_up(N * kD * 2, 16);
     const int F = off;
     int f = F;
-    L.gk = f;   f += align_up(NP * NP * 4, 16);
-    L.gq = f;   f += align_up(NP * NP * 4, 16);
+    L.gk = f;   f += align_up(N * (N + 1) / 2 * 4, 16);  // lower triangle, j <= i
+    L.gq = f;   f += align_up(N * (N + 1) / 2 * 4, 16);
     L.nrm = f;  f += align_up(2 * NP * 4, 16);
     L.sk = f;   f += align_up(N * 4, 16);
     L.sq = f;   f += align_up(N * 4, 16);
@@ -794,11 +801,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
             for (int off = 16; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
             if (ch == 0) s_nrm[sl] = ss;
         }
+        if constexpr (NPB == 1) {  // two blocks: staged after the M solve, over the Gram block
     #pragma unroll
-        for (int u = 0; u < kVItems; ++u) {
-            const int it = tid + u * kThreads;
-            const int node = it >> 5;
-            if (node < N) *reinterpret_cast<uint2*>(s_v + node * kD + (it & 31) * 4) = v_val[u];
+            for (int u = 0; u < kVItems; ++u) {
+                const int it = tid + u * kThreads;
+                const int node = it >> 5;
+                if (node < N) *reinterpret_cast<uint2*>(s_v + node * kD + (it & 31) * 4) = v_val[u];
+            }
         }
         }
         __syncthreads();
@@ -817,13 +826,15 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
             s_cidx[tid * N + p] = static_cast<uint8_t>(tid);
         }
 
-        // (c) Gram block on the matrix cores (exact bf16 products, fp32 sums),
-        //     stored dense: k_i . k_j and q_i . k_j for every pair of slots
+        // (c) Gram block on the matrix cores (exact bf16 products, fp32 sums):
+        //     k_i . k_j and q_i . k_j for j <= i (every ancestor has a smaller
+        //     index), stored as row-major lower triangles
         {
             constexpr int kTiles = MB * NPB;  // all query/key row blocks x key column blocks
             for (int tile = wave; tile < kTiles; tile += kThreads / 64) {
                 const int ta = tile / NPB;
                 const int tcol = tile % NPB;
+                if (tcol > ta % NPB) continue;  // wholly above the diagonal (uniform per wave)
                 f32x16_t acc = {};
     #pragma unroll
                 for (int s = 0; s < 8; ++s) {
@@ -831,10 +842,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                     const bf16x8_t bb = lds_operand(s_a, tcol * 32 + l32, s, hf);
                     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc, 0, 0, 0);
                 }
-                float* gdst = (ta < NPB) ? s_gk + ta * 32 * NP : s_gq + (ta - NPB) * 32 * NP;
+                float* gdst = (ta < NPB) ? s_gk : s_gq;
                 const int col = tcol * 32 + l32;
     #pragma unroll
-                for (int e = 0; e < 16; ++e) gdst[(8 * (e >> 2) + 4 * hf + (e & 3)) * NP + col] = acc[e];
+                for (int e = 0; e < 16; ++e) {
+                    const int row = (ta % NPB) * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
+                    if (row < N && col <= row) gdst[row * (row + 1) / 2 + col] = acc[e];
+                }
             }
         }
         __syncthreads();
@@ -866,10 +880,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                     const bool in = sp > p && sp < d;
                     const int m = path[min(sp, d - 1)];
                     r *= in ? s_al[m] : 1.0f;
-                    gco[sp] = in ? s_be[m] * s_sk[m] * sk_j * s_gk[m * NP + j] * r : 0.0f;
+                    gco[sp] = in ? s_be[m] * s_sk[m] * sk_j * s_gk[m * (m + 1) / 2 + j] * r : 0.0f;
                 }
                 // r = P_i / P_j now
-                float val = r * s_sq[ii] * sk_j * s_gq[ii * NP + j];
+                float val = r * s_sq[ii] * sk_j * s_gq[ii * (ii + 1) / 2 + j];
     #pragma unroll
                 for (int sp = kLP - 1; sp >= 1; --sp) {
                     const float ms = __shfl(val, grp_lane0 | sp, 64);  // final M at position sp
@@ -901,12 +915,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                 for (int pp = d - 1; pp >= 0; --pp) {
                     const int jj = path[pp];
                     const float sk_j = s_sk[jj];
-                    float val = wq * sq_i * sk_j * s_gq[i * NP + jj];
+                    float val = wq * sq_i * sk_j * s_gq[i * (i + 1) / 2 + jj];
                     float wg = 1.0f;
                     for (int sp = pp + 1; sp < d; ++sp) {
                         const int m = path[sp];
                         wg *= s_al[m];
-                        const float gmj = s_be[m] * wg * s_sk[m] * sk_j * s_gk[m * NP + jj];
+                        const float gmj = s_be[m] * wg * s_sk[m] * sk_j * s_gk[m * (m + 1) / 2 + jj];
                         const float msv = bf16_bits_to_f32(mh[m]) + bf16_bits_to_f32(ml[m]);
                         val = fmaf(-msv, gmj, val);
                     }
@@ -922,6 +936,15 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
             }
         }
         __syncthreads();
+        if constexpr (NPB != 1) {  // V rows, over the Gram block (dead after the M solve)
+    #pragma unroll
+            for (int u = 0; u < kVItems; ++u) {
+                const int it = tid + u * kThreads;
+                const int node = it >> 5;
+                if (node < N) *reinterpret_cast<uint2*>(s_v + node * kD + (it & 31) * 4) = v_val[u];
+            }
+            __syncthreads();
+        }
     }
 
     // fused: replay the previous path into the state in registers, in this
