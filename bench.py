@@ -272,6 +272,163 @@ class Instance:
         self.turn = 0
 
 
+class LayerStack:
+    """L layers back to back on the same requests: one tree and accepted path
+    per request for every layer (host-drawn, two step slots), and per layer
+    its own operands and state pool, drawn on the device with the workload's
+    distributions (q, k unit rows in bf16, v ~N(0,1) bf16, a = exp(-softplus(n)),
+    b = sigmoid(n), state ~N(0, s_std^2)) from a seeded generator per layer and
+    slot.  Outputs share one buffer per slot (no layer reads them)."""
+
+    def __init__(self, g, cfg, seed, layers, to_dev, dev, torch):
+        import gdn_inputs as gi
+        cases = [gi.make_case(cfg, seed=seed + 7919 * j, layer=0, packing="bfs", with_pool=False)
+                 for j in range(2)]
+        B, R, D, Hv, Hqk, N = cfg.B, cfg.R, cfg.D, cfg.Hv, cfg.Hqk, cfg.N
+        self.cases = cases
+        self.desc = [g.TreeDesc(to_dev(c["parent"]), to_dev(c["node_row"]), R, 1) for c in cases]
+        self.path = [to_dev(c["path"]) for c in cases]
+        self.path_len = [to_dev(c["path_len"]) for c in cases]
+        self.state_idx = to_dev(cases[0]["state_idx"])
+        self.P = int(cases[0]["P"])
+        self.out = [torch.empty((B, R, Hv, D), dtype=torch.float32, device=dev) for _ in range(2)]
+        self.path_rows = torch.zeros(cases[0]["path"].shape, dtype=torch.int32, device=dev)
+        self.path_n = torch.zeros((B,), dtype=torch.int32, device=dev)
+        used = torch.zeros((2, B, R), dtype=torch.bool, device=dev)
+        for j, c in enumerate(cases):
+            for b in range(B):
+                used[j, b, torch.as_tensor(c["node_row"][b], device=dev).long()] = True
+        self.layers = []
+        for l in range(layers):
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(seed * 1000003 + l)
+
+            def unit_rows(shape):
+                x = torch.randn(shape, generator=gen, device=dev)
+                return (x / x.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+
+            lay = {"pool": torch.randn((self.P, Hv, D, D), generator=gen, device=dev) * cfg.s_std,
+                   "slots": []}
+            for j in range(2):
+                sl = {"q": unit_rows((B, R, Hqk, D)), "k": unit_rows((B, R, Hqk, D)),
+                      "v": torch.randn((B, R, Hv, D), generator=gen, device=dev).to(torch.bfloat16),
+                      "alpha": torch.exp(-torch.nn.functional.softplus(
+                          torch.randn((B, R, Hv), generator=gen, device=dev))),
+                      "beta": torch.sigmoid(torch.randn((B, R, Hv), generator=gen, device=dev))}
+                pad = ~used[j]
+                for key in ("alpha", "beta"):
+                    sl[key][pad] = float("nan")
+                lay["slots"].append(sl)
+            self.layers.append(lay)
+        self.turn = 0
+
+
+def run_layers(args, cfg, g, torch, dev, to_dev):
+    """The step of an L-layer model: the step's shared prepare (descriptor,
+    path rows), then every layer's commit + verify (fused: one launch per
+    layer; separate: verify, then commit of this step's path)."""
+    L = args.layers
+    fused = args.mode == "fused"
+    t0 = time.perf_counter()
+    st = LayerStack(g, cfg, args.seed, L, to_dev, dev, torch)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] {args.mode} mode: {L} layers of {cfg.name} ready in {time.perf_counter() - t0:.1f} s")
+
+    def step(ev=None):
+        cur, prev = st.turn % 2, (st.turn - 1) % 2
+        st.turn += 1
+        marks = iter(ev) if ev is not None else None
+
+        def mark():
+            if marks is not None:
+                next(marks).record()
+
+        mark()
+        if fused:
+            g.gdn_step_prepare(st.desc[cur], st.desc[prev], st.path[prev], st.path_len[prev],
+                               st.state_idx, st.P, st.path_rows, st.path_n, err)
+        else:
+            g.gdn_tree_desc_build(st.desc[cur], err)
+        mark()
+        for lay in st.layers:
+            c, p = lay["slots"][cur], lay["slots"][prev]
+            if fused:
+                g.gdn_tree_commit_verify(st.desc[cur], c["q"], c["k"], c["v"], c["alpha"], c["beta"],
+                                         lay["pool"], st.state_idx, st.out[cur], st.desc[prev],
+                                         st.path_rows, st.path_n, p["k"], p["v"], p["alpha"],
+                                         p["beta"], err)
+            else:
+                g.gdn_tree_verify(st.desc[cur], c["q"], c["k"], c["v"], c["alpha"], c["beta"],
+                                  lay["pool"], st.state_idx, st.out[cur], err)
+                g.gdn_tree_commit(st.desc[cur], st.path[cur], st.path_len[cur], c["k"], c["v"],
+                                  c["alpha"], c["beta"], lay["pool"], st.state_idx, err, Hqk=cfg.Hqk)
+            mark()
+        return cur, prev
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record()
+    steps_bytes = []
+    for _ in range(args.steps):
+        cur, prev = step()
+        ccase, pcase = st.cases[cur], st.cases[prev]
+        steps_bytes.append(byte_model(cfg, ccase, pcase, args.mode))
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    # per-layer launch durations, in a second pass with an event between launches
+    nsteps_b = min(args.steps, 10)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(L + 2)] for _ in range(nsteps_b)]
+    for i in range(nsteps_b):
+        step(evs[i])
+    torch.cuda.synchronize()
+    if int(err.item()) != 0:
+        log(f"[bench] device error word {int(err.item())}")
+        sys.exit(3)
+    prep_ms = float(np.mean([ev[0].elapsed_time(ev[1]) for ev in evs]))
+    layer_ms = float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in evs for j in range(1, L + 1)]))
+    kname = "commit_verify" if fused else "verify+commit"
+    per_layer_bytes = float(np.mean([sum(v for k, v in b.items() if k not in ("desc", "prepare"))
+                                     for b in steps_bytes]))
+    step_bytes = L * per_layer_bytes + float(np.mean([b.get("prepare", b.get("desc", 0)) for b in steps_bytes]))
+    B, N = cfg.B, cfg.N
+    value = B * N * L / (ms_per_step / 1e3)
+    achieved = per_layer_bytes / (layer_ms / 1e3) / 1e9
+    log(f"[bench] prepare {prep_ms * 1e3:.1f} us; per layer {layer_ms * 1e3:.1f} us "
+        f"{per_layer_bytes / 1e6:.1f} MB -> {achieved:.1f} GB/s ({achieved / PEAK_HBM_GBS * 100:.1f}% of 8 TB/s)")
+    log(f"[bench] step of {L} layers {ms_per_step * 1e3:.1f} us (wall {wall / args.steps * 1e6:.1f} us): "
+        f"{ms_per_step * 1e3 / L:.1f} us per layer, {step_bytes / (ms_per_step / 1e3) / 1e9:.1f} GB/s")
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tree nodes/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: {N}-node draft trees (branching<={cfg.bmax}, depth<={cfg.depth_max}), "
+                        f"B={B}, Hv={cfg.Hv} over Hqk={cfg.Hqk}, d={cfg.D}, bf16 operands, fp32 state, "
+                        f"{L} GDN layers back to back (own operands and state pool per layer; one tree "
+                        f"and accepted path per request shared by the layers)",
+            "mode": args.mode,
+            "step": ("gdn_step_prepare + gdn_tree_commit_verify per layer" if fused else
+                     "gdn_tree_desc_build + gdn_tree_verify and gdn_tree_commit per layer"),
+            "value_is": "tree nodes verified per second per GDN layer: B*N*layers / step time",
+            "global_batch": B, "nodes_per_request": N, "layers": L, "parallelism": "single GPU",
+            "step_bytes": int(step_bytes), "us_per_layer": round(ms_per_step * 1e3 / L, 2),
+            "step_hbm_gbs": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
+        },
+        "roofline": dict(bound="hbm", kernel=kname, achieved=round(achieved, 1), peak=PEAK_HBM_GBS,
+                         unit="GB/s", frac=round(achieved / PEAK_HBM_GBS, 4), traffic=None,
+                         avg_us=round(layer_ms * 1e3, 2), algorithmic_bytes=int(per_layer_bytes)),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -281,6 +438,8 @@ def main():
     ap.add_argument("--mode", choices=("fused", "layer", "separate"), default="fused")
     ap.add_argument("--seed", type=int, default=2026)
     ap.add_argument("--sets", type=int, default=2, help="independent layer instances rotated per step")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="layers per step for the multi-layer workload (default: the workload's)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -325,6 +484,16 @@ def main():
         if a.dtype == np.uint16:
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
+
+    if args.layers == 0:
+        args.layers = cfg.layers
+    if args.layers > 1:
+        if cfg.conv_W > 0 or layer:
+            print("--layers > 1 covers the workloads without conv (fused or separate mode)",
+                  file=sys.stderr)
+            sys.exit(2)
+        run_layers(args, cfg, g, torch, dev, to_dev)
+        return
 
     t0 = time.perf_counter()
     insts = [Instance(g, cfg, args.seed, li, to_dev, dev, torch, 2 if (fused or layer) else 1)

@@ -162,3 +162,23 @@ def test_two_steps_conv4_full_size_sampled():
     d = bf16_ulp_diff(g1["y2"][node_rows_mask(s2)], orr["y2"][node_rows_mask(s2)])
     assert d.max() <= 1
     assert np.isfinite(g1["out"][node_rows_mask(s2)]).all()
+
+
+def test_two_steps_tree64_b256_full_size_sampled():
+    # the wide workload at full size (two 32-row blocks per request, paths of up
+    # to 9 rows: a segment of 8 and a second one) on the device; the oracle on
+    # a sample of requests
+    cfg = gi.CONFIGS[5]
+    c1, c2 = two_step_case(cfg, seed=2026, packing="bfs")
+    gr = run_gpu_two_steps(c1, c2)
+    assert gr["err"] == 0
+    used = c1["state_idx"]
+    longest = np.nonzero(c1["path_len"] == c1["path_len"].max())[0][:2]
+    bs = np.unique(np.concatenate([[0, 77, 128, 255], longest]))
+    assert c1["path_len"][bs].max() > 8            # a second replay segment is checked
+    s1, s2 = subset(c1, bs), subset(c2, bs)
+    s2["pool"] = s1["pool"]
+    orr = run_oracle_two_steps(s1, s2)
+    m = node_rows_mask(s2)
+    assert max_rel_rows(gr["out"][bs][m], orr["out"][m], 2) <= TOL
+    assert max_rel_rows(gr["pool"][used[bs]], orr["pool"], 2) <= TOL
