@@ -298,8 +298,18 @@ class LayerStack:
         for j, c in enumerate(cases):
             for b in range(B):
                 used[j, b, torch.as_tensor(c["node_row"][b], device=dev).long()] = True
+        # stacked per kind ([L, ...] with layer l at index l) so that one
+        # launch can commit every layer; layer l's tensors are views
+        L = layers
+        self.pool_all = torch.empty((L, self.P, Hv, D, D), dtype=torch.float32, device=dev)
+        self.slot_all = [{"q": torch.empty((L, B, R, Hqk, D), dtype=torch.bfloat16, device=dev),
+                          "k": torch.empty((L, B, R, Hqk, D), dtype=torch.bfloat16, device=dev),
+                          "v": torch.empty((L, B, R, Hv, D), dtype=torch.bfloat16, device=dev),
+                          "alpha": torch.empty((L, B, R, Hv), dtype=torch.float32, device=dev),
+                          "beta": torch.empty((L, B, R, Hv), dtype=torch.float32, device=dev)}
+                         for _ in range(2)]
         self.layers = []
-        for l in range(layers):
+        for l in range(L):
             gen = torch.Generator(device=dev)
             gen.manual_seed(seed * 1000003 + l)
 
@@ -307,14 +317,16 @@ class LayerStack:
                 x = torch.randn(shape, generator=gen, device=dev)
                 return (x / x.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
 
-            lay = {"pool": torch.randn((self.P, Hv, D, D), generator=gen, device=dev) * cfg.s_std,
-                   "slots": []}
+            self.pool_all[l].copy_(torch.randn((self.P, Hv, D, D), generator=gen, device=dev) * cfg.s_std)
+            lay = {"pool": self.pool_all[l], "slots": []}
             for j in range(2):
-                sl = {"q": unit_rows((B, R, Hqk, D)), "k": unit_rows((B, R, Hqk, D)),
-                      "v": torch.randn((B, R, Hv, D), generator=gen, device=dev).to(torch.bfloat16),
-                      "alpha": torch.exp(-torch.nn.functional.softplus(
-                          torch.randn((B, R, Hv), generator=gen, device=dev))),
-                      "beta": torch.sigmoid(torch.randn((B, R, Hv), generator=gen, device=dev))}
+                sl = {key: t[l] for key, t in self.slot_all[j].items()}
+                sl["q"].copy_(unit_rows((B, R, Hqk, D)))
+                sl["k"].copy_(unit_rows((B, R, Hqk, D)))
+                sl["v"].copy_(torch.randn((B, R, Hv, D), generator=gen, device=dev).to(torch.bfloat16))
+                sl["alpha"].copy_(torch.exp(-torch.nn.functional.softplus(
+                    torch.randn((B, R, Hv), generator=gen, device=dev))))
+                sl["beta"].copy_(torch.sigmoid(torch.randn((B, R, Hv), generator=gen, device=dev)))
                 pad = ~used[j]
                 for key in ("alpha", "beta"):
                     sl[key][pad] = float("nan")
@@ -326,7 +338,8 @@ class LayerStack:
 def run_layers(args, cfg, g, torch, dev, to_dev):
     """The step of an L-layer model: the step's shared prepare (descriptor,
     path rows), then every layer's commit + verify (fused: one launch per
-    layer; separate: verify, then commit of this step's path)."""
+    layer; separate: every layer's verify, then one launch that commits this
+    step's path into all layers)."""
     L = args.layers
     fused = args.mode == "fused"
     t0 = time.perf_counter()
@@ -361,8 +374,13 @@ def run_layers(args, cfg, g, torch, dev, to_dev):
             else:
                 g.gdn_tree_verify(st.desc[cur], c["q"], c["k"], c["v"], c["alpha"], c["beta"],
                                   lay["pool"], st.state_idx, st.out[cur], err)
-                g.gdn_tree_commit(st.desc[cur], st.path[cur], st.path_len[cur], c["k"], c["v"],
-                                  c["alpha"], c["beta"], lay["pool"], st.state_idx, err, Hqk=cfg.Hqk)
+            mark()
+        if not fused:
+            # after acceptance: this step's path into every layer's state, one launch
+            sa = st.slot_all[cur]
+            g.gdn_tree_commit_layers(st.desc[cur], st.path[cur], st.path_len[cur], sa["k"], sa["v"],
+                                     sa["alpha"], sa["beta"], st.pool_all, st.state_idx, err,
+                                     Hqk=cfg.Hqk)
             mark()
         return cur, prev
 
@@ -383,7 +401,8 @@ def run_layers(args, cfg, g, torch, dev, to_dev):
     ms_per_step = e0.elapsed_time(e1) / args.steps
     # per-layer launch durations, in a second pass with an event between launches
     nsteps_b = min(args.steps, 10)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(L + 2)] for _ in range(nsteps_b)]
+    nev = L + 2 if fused else L + 3
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(nsteps_b)]
     for i in range(nsteps_b):
         step(evs[i])
     torch.cuda.synchronize()
@@ -392,6 +411,11 @@ def run_layers(args, cfg, g, torch, dev, to_dev):
         sys.exit(3)
     prep_ms = float(np.mean([ev[0].elapsed_time(ev[1]) for ev in evs]))
     layer_ms = float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in evs for j in range(1, L + 1)]))
+    if not fused:
+        commit_ms = float(np.mean([ev[L + 1].elapsed_time(ev[L + 2]) for ev in evs]))
+        log(f"[bench] verify {layer_ms * 1e3:.1f} us per layer; commit of {L} layers in one launch "
+            f"{commit_ms * 1e3:.1f} us ({commit_ms * 1e3 / L:.1f} us per layer)")
+        layer_ms += commit_ms / L
     kname = "commit_verify" if fused else "verify+commit"
     per_layer_bytes = float(np.mean([sum(v for k, v in b.items() if k not in ("desc", "prepare"))
                                      for b in steps_bytes]))
@@ -415,7 +439,7 @@ def run_layers(args, cfg, g, torch, dev, to_dev):
                         f"and accepted path per request shared by the layers)",
             "mode": args.mode,
             "step": ("gdn_step_prepare + gdn_tree_commit_verify per layer" if fused else
-                     "gdn_tree_desc_build + gdn_tree_verify and gdn_tree_commit per layer"),
+                     "gdn_tree_desc_build + gdn_tree_verify per layer + one gdn_tree_commit_layers"),
             "value_is": "tree nodes verified per second per GDN layer: B*N*layers / step time",
             "global_batch": B, "nodes_per_request": N, "layers": L, "parallelism": "single GPU",
             "step_bytes": int(step_bytes), "us_per_layer": round(ms_per_step * 1e3 / L, 2),

@@ -186,6 +186,28 @@ int32_t gdn_tree_commit(const gdn_tree_desc *d, const int32_t *path, const int32
                         int32_t dk, int32_t dv, int32_t dtype, int32_t flags, int32_t *err,
                         void *stream);
 
+/* Commit of one accepted path into L layers' states in one launch (the
+ * publication after acceptance covers every GDN layer of the model: LumoTree,
+ * Sec. IV-B and V-A; the same tree, path and slots for every layer).  Layer
+ * l's k, v, gates and state pool are the given buffers offset by l times the
+ * layer strides, in elements; each layer's buffers follow gdn_tree_commit's
+ * layouts and must not overlap the next layer's.  The result equals
+ * gdn_tree_commit called once per layer (without conv history: x / hist are
+ * per layer and go through gdn_tree_commit or the fused calls).
+ *   layers            1..; B * Hv * layers < 2^31
+ *   layer_stride_qk   >= B * R * row_stride_qk (k), layer_stride_v likewise
+ *   layer_stride_gate >= B * R * Hv (alpha and beta)
+ *   layer_stride_pool >= P * Hv * dv * dk, a multiple of 4 (16-byte alignment) */
+int32_t gdn_tree_commit_layers(const gdn_tree_desc *d, const int32_t *path,
+                               const int32_t *path_len, int32_t Lmax, int32_t layers,
+                               const void *k, const void *v, int64_t row_stride_qk,
+                               int64_t row_stride_v, int64_t layer_stride_qk,
+                               int64_t layer_stride_v, const float *alpha, const float *beta,
+                               int64_t layer_stride_gate, float *state_pool,
+                               int64_t layer_stride_pool, int32_t P, const int32_t *state_idx,
+                               int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv, int32_t dtype,
+                               int32_t flags, int32_t *err, void *stream);
+
 /* ---- fused steady-state step ---------------------------------------------
  * In a decode loop every step commits the previous step's accepted path and
  * then verifies a new tree from the committed state (LumoTree, Sec. IV-B and
@@ -338,8 +360,9 @@ int32_t gdn_layer_step(const gdn_tree_desc *d, const void *x, const void *w, con
 /* Human-readable name of a return code (host; static string). */
 const char *gdn_status_string(int32_t status);
 
-/* ABI version of this header: 3 (1, plus the two fused-step calls in 2,
- * plus gdn_path_resolve, gdn_step_prepare and gdn_layer_step). */
+/* ABI version of this header: 4 (1, plus the two fused-step calls in 2,
+ * plus gdn_path_resolve, gdn_step_prepare and gdn_layer_step in 3, plus
+ * gdn_tree_commit_layers). */
 int32_t gdn_abi_version(void);
 
 #ifdef __cplusplus

@@ -30,8 +30,8 @@ def lib():
 def test_header_declares_the_entry_points():
     decl = declared_functions()
     for name in ("gdn_tree_desc_build", "conv_ancestry_gather", "gdn_tree_verify", "gdn_tree_commit",
-                 "conv_ancestry_gather_publish", "gdn_tree_commit_verify", "gdn_path_resolve",
-                 "gdn_step_prepare", "gdn_layer_step"):
+                 "gdn_tree_commit_layers", "conv_ancestry_gather_publish", "gdn_tree_commit_verify",
+                 "gdn_path_resolve", "gdn_step_prepare", "gdn_layer_step"):
         assert name in decl
     assert set(decl) == set(g.EXPORTED)
 
@@ -46,7 +46,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.gdn_abi_version() == 3
+    assert lib.gdn_abi_version() == 4
     assert lib.gdn_status_string(0) == b"ok"
     assert lib.gdn_status_string(-1) == b"invalid argument"
     assert lib.gdn_status_string(-4) == b"unsupported size"
@@ -85,6 +85,22 @@ def test_argument_checks_fail_before_launch(lib):
     assert Cm(d, p, p, 0, p, p, 2048, 4096, p, p, p, 4, p, None, None, 0, 16, 32, 128, 128, 0, 0, err, None) == g.GDN_ERR_UNSUPPORTED
     assert Cm(d, p, p, 65, p, p, 2048, 4096, p, p, p, 4, p, None, None, 0, 16, 32, 128, 128, 0, 0, err, None) == g.GDN_ERR_UNSUPPORTED
     assert Cm(d, p, p, 7, p, p, 2048, 4096, p, p, p, 4, p, p, None, 8, 16, 32, 128, 128, 0, 0, err, None) == g.GDN_ERR_ARG
+    # commit over layers (B = 2, R = 8: 16 rows; P = 4): no layers, overlapping
+    # layer strides, an unknown flag, a pool stride that breaks alignment
+    Cl = lib.gdn_tree_commit_layers
+    ok = (16 * 2048, 16 * 4096, 16 * 32, 4 * 32 * 128 * 128)
+
+    def cl(layers=3, strides=ok, flags=0, Lmax=7):
+        return Cl(d, p, p, Lmax, layers, p, p, 2048, 4096, strides[0], strides[1], p, p, strides[2], p,
+                  strides[3], 4, p, 16, 32, 128, 128, 0, flags, err, None)
+    assert cl(layers=0) == g.GDN_ERR_ARG
+    assert cl(strides=(15 * 2048,) + ok[1:]) == g.GDN_ERR_ARG
+    assert cl(strides=ok[:1] + (16 * 4096 - 1,) + ok[2:]) == g.GDN_ERR_ARG
+    assert cl(strides=ok[:2] + (16 * 31,) + ok[3:]) == g.GDN_ERR_ARG
+    assert cl(strides=ok[:3] + (ok[3] - 4,)) == g.GDN_ERR_ARG
+    assert cl(strides=ok[:3] + (ok[3] + 2,)) == g.GDN_ERR_ARG
+    assert cl(flags=g.GDN_F_OUT_BF16) == g.GDN_ERR_ARG
+    assert cl(Lmax=65) == g.GDN_ERR_UNSUPPORTED
     # conv: channel count not a multiple of 4, bad activation
     Cv = lib.conv_ancestry_gather
     assert Cv(d, p, p, 4, p, p, None, p, 8190, 1, err, None) == g.GDN_ERR_UNSUPPORTED

@@ -38,7 +38,7 @@ GDN_F_NORM_QK, GDN_F_OUT_BF16, GDN_F_VALU = 1, 2, 4
 GDN_ACT_NONE, GDN_ACT_SILU = 0, 1
 
 EXPORTED = ("gdn_tree_desc_build", "conv_ancestry_gather", "gdn_tree_verify",
-            "gdn_tree_commit", "conv_ancestry_gather_publish", "gdn_tree_commit_verify",
+            "gdn_tree_commit", "gdn_tree_commit_layers", "conv_ancestry_gather_publish", "gdn_tree_commit_verify",
             "gdn_path_resolve", "gdn_step_prepare", "gdn_layer_step", "gdn_status_string",
             "gdn_abi_version")
 
@@ -89,6 +89,10 @@ def load_library():
         lib.gdn_tree_commit.restype = i32
         lib.gdn_tree_commit.argtypes = [dp, vp, vp, i32, vp, vp, i64, i64, vp, vp, vp, i32, vp,
                                         vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp]
+        lib.gdn_tree_commit_layers.restype = i32
+        lib.gdn_tree_commit_layers.argtypes = [dp, vp, vp, i32, i32, vp, vp, i64, i64, i64, i64,
+                                               vp, vp, i64, vp, i64, i32, vp, i32, i32, i32, i32,
+                                               i32, i32, vp, vp]
         lib.conv_ancestry_gather_publish.restype = i32
         lib.conv_ancestry_gather_publish.argtypes = [dp, vp, vp, i32, vp, vp, vp, vp, i32, i32,
                                                      dp, vp, vp, i32, vp, vp, vp]
@@ -255,6 +259,41 @@ def gdn_tree_commit(desc: TreeDesc, path, path_len, k, v, alpha, beta, state_poo
                                           _ptr(hist), C, Hqk, Hv, dk, dv, _dtype_code(k),
                                           int(flags), _ptr(err), _stream(stream))
     return _check(code, "gdn_tree_commit", raise_on_error)
+
+
+def _layer_stride(t, name, L):
+    if t.dim() < 1 or int(t.shape[0]) != L:
+        raise ValueError(f"{name} must have the layer count {L} as its first dimension")
+    return int(t.stride(0)) if L > 1 else 0
+
+
+def gdn_tree_commit_layers(desc: TreeDesc, path, path_len, k, v, alpha, beta, state_pool,
+                           state_idx, err, Hqk: int | None = None, flags: int = 0, stream=None,
+                           raise_on_error=True) -> int:
+    """Replay path [B, Lmax] into every layer's state in one launch: k
+    [L, B, R, Hqk, dk], v [L, B, R, Hv, dv], alpha / beta [L, B, R, Hv],
+    state_pool [L, P, Hv, dv, dk]; layer l is gdn_tree_commit on the l-th
+    slices."""
+    L = int(k.shape[0])
+    rs_qk, Hk, dk = _rows_view(k[0], "k")
+    rs_v, Hv, dv = _rows_view(v[0], "v")
+    Hqk = Hk if Hqk is None else Hqk
+    for t, name in ((alpha, "alpha"), (beta, "beta")):
+        if t.dim() != 4 or not t[0].is_contiguous():
+            raise ValueError(f"{name} must be [L, B, R, Hv] with contiguous layers")
+    if alpha.stride(0) != beta.stride(0):
+        raise ValueError("alpha and beta need the same layer stride")
+    if not state_pool[0].is_contiguous():
+        raise ValueError("state_pool must be [L, P, Hv, dv, dk] with contiguous layers")
+    P = int(state_pool.shape[1])
+    Lmax = int(path.shape[1])
+    code = load_library().gdn_tree_commit_layers(
+        desc.ref(), _ptr(path), _ptr(path_len), Lmax, L, _ptr(k), _ptr(v), rs_qk, rs_v,
+        _layer_stride(k, "k", L), _layer_stride(v, "v", L), _ptr(alpha), _ptr(beta),
+        _layer_stride(alpha, "alpha", L), _ptr(state_pool),
+        _layer_stride(state_pool, "state_pool", L), P, _ptr(state_idx), Hqk, Hv, dk, dv,
+        _dtype_code(k), int(flags), _ptr(err), _stream(stream))
+    return _check(code, "gdn_tree_commit_layers", raise_on_error)
 
 
 def conv_ancestry_gather_publish(desc: TreeDesc, x, hist, state_idx, w, bias, y, act: int,

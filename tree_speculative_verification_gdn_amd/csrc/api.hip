@@ -36,7 +36,7 @@ int32_t check_heads(int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv, int32_t dty
 
 extern "C" {
 
-int32_t gdn_abi_version(void) { return 3; }
+int32_t gdn_abi_version(void) { return 4; }
 
 const char* gdn_status_string(int32_t status) {
     switch (status) {
@@ -126,6 +126,43 @@ int32_t gdn_tree_commit(const gdn_tree_desc* d, const int32_t* path, const int32
     gdn::CommitArgs a{path, path_len, Lmax, k, v, row_stride_qk, row_stride_v, alpha, beta,
                       state_pool, P, state_idx, static_cast<const uint16_t*>(x),
                       static_cast<uint16_t*>(hist), x ? C : 0, Hqk, Hv, dk, dtype, flags, err, 0};
+    return map_launch(gdn::launch_commit(*d, a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t gdn_tree_commit_layers(const gdn_tree_desc* d, const int32_t* path, const int32_t* path_len,
+                               int32_t Lmax, int32_t layers, const void* k, const void* v,
+                               int64_t row_stride_qk, int64_t row_stride_v, int64_t layer_stride_qk,
+                               int64_t layer_stride_v, const float* alpha, const float* beta,
+                               int64_t layer_stride_gate, float* state_pool,
+                               int64_t layer_stride_pool, int32_t P, const int32_t* state_idx,
+                               int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv, int32_t dtype,
+                               int32_t flags, int32_t* err, void* stream) {
+    int32_t st = check_desc(d);
+    if (st != GDN_OK) return st;
+    st = check_heads(Hqk, Hv, dk, dv, dtype);
+    if (st != GDN_OK) return st;
+    if (!path || !path_len || !k || !v || !alpha || !beta || !state_pool || !state_idx || !err ||
+        P < 1 || layers < 1)
+        return GDN_ERR_ARG;
+    if (Lmax < 1 || Lmax > GDN_MAX_NODES) return GDN_ERR_UNSUPPORTED;
+    if ((flags & ~GDN_F_NORM_QK) != 0) return GDN_ERR_ARG;
+    if (row_stride_qk < static_cast<int64_t>(Hqk) * dk || row_stride_v < static_cast<int64_t>(Hv) * dv)
+        return GDN_ERR_ARG;
+    // a layer's buffers must not overlap the next layer's
+    const int64_t rows = static_cast<int64_t>(d->B) * d->R;
+    if (layers > 1 && (layer_stride_qk < rows * row_stride_qk || layer_stride_v < rows * row_stride_v ||
+                       layer_stride_gate < rows * Hv ||
+                       layer_stride_pool < static_cast<int64_t>(P) * Hv * dk * dv))
+        return GDN_ERR_ARG;
+    if (static_cast<int64_t>(d->B) * Hv * layers > 0x7fffffffLL) return GDN_ERR_UNSUPPORTED;
+    if (!aligned(state_pool, 16) || (layer_stride_pool % 4) != 0) return GDN_ERR_ARG;
+    gdn::CommitArgs a{path, path_len, Lmax, k, v, row_stride_qk, row_stride_v, alpha, beta,
+                      state_pool, P, state_idx, nullptr, nullptr, 0, Hqk, Hv, dk, dtype, flags, err, 0};
+    a.layers = layers;
+    a.ls_qk = layer_stride_qk;
+    a.ls_v = layer_stride_v;
+    a.ls_gate = layer_stride_gate;
+    a.ls_pool = layer_stride_pool;
     return map_launch(gdn::launch_commit(*d, a, static_cast<hipStream_t>(stream)));
 }
 

@@ -105,6 +105,10 @@ struct CommitArgs {
     int dtype, flags;
     int32_t* err;
     int resolved;  // 1: path / path_len come from the path resolution (no validation here)
+    // several layers in one launch: layer l's k, v, gates and pool at these
+    // element strides from the first layer's (layers = 1: one layer)
+    int layers = 1;
+    int64_t ls_qk = 0, ls_v = 0, ls_gate = 0, ls_pool = 0;
 };
 hipError_t launch_commit(const gdn_tree_desc& d, const CommitArgs& a, hipStream_t s);
 size_t commit_lds_bytes(int Lmax, int D, int dtype);

@@ -155,7 +155,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
                   const float* __restrict__ alpha, const float* __restrict__ beta,
                   float* __restrict__ pool, int P, const int32_t* __restrict__ state_idx,
                   const uint16_t* __restrict__ x, uint16_t* __restrict__ hist, int C, int hvec,
-                  int Hqk, int Hv, int norm, int32_t* __restrict__ err) {
+                  int Hqk, int Hv, int norm, int32_t* __restrict__ err, int64_t ls_qk, int64_t ls_v,
+                  int64_t ls_gate, int64_t ls_pool) {
     constexpr int TPR = kThreads / D;             // lanes per value row
     constexpr int EPT = D / TPR;                  // state elements per lane
     constexpr int CW = EPT >= 8 ? 8 : EPT;        // columns per chunk
@@ -172,9 +173,19 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
     int32_t* s_rows = reinterpret_cast<int32_t*>(lds + L.rows);
     __shared__ int s_bad;
 
-    const uint32_t unit = xcd_local_order(blockIdx.x, gridDim.x);
+    // workgroup -> (layer, request, head); layer l's operands and pool sit at
+    // fixed element strides from the first layer's (0 for a single layer)
+    const uint32_t unit_all = xcd_local_order(blockIdx.x, gridDim.x);
+    const uint32_t per_layer = static_cast<uint32_t>(B) * static_cast<uint32_t>(Hv);
+    const int64_t layer = static_cast<int64_t>(unit_all / per_layer);
+    const uint32_t unit = unit_all % per_layer;
     const int b = static_cast<int>(unit / Hv);
     const int h = static_cast<int>(unit % Hv);
+    k += layer * ls_qk;
+    v += layer * ls_v;
+    alpha += layer * ls_gate;
+    beta += layer * ls_gate;
+    pool += layer * ls_pool;
     const int t = shared ? 0 : b;
     const int tid = threadIdx.x;
     const int r = tid / TPR;
@@ -406,20 +417,22 @@ hipError_t launch_commit_t(const gdn_tree_desc& d, const CommitArgs& a, int norm
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(lds));
     if (e != hipSuccess) return e;
-    const dim3 grid(static_cast<unsigned>(d.B) * static_cast<unsigned>(a.Hv));
+    const dim3 grid(static_cast<unsigned>(d.B) * static_cast<unsigned>(a.Hv) * static_cast<unsigned>(a.layers));
     hipLaunchKernelGGL(kfn, grid, dim3(kThreads), lds, s, d.B, d.N, d.R, d.W, d.shared, d.parent,
                        d.node_row, d.status, a.path, a.path_len, a.Lmax,
                        static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.rs_qk, a.rs_v,
                        a.alpha, a.beta, a.pool, a.P, a.state_idx, a.x, a.hist, a.C, hvec, a.Hqk,
-                       a.Hv, norm, a.err);
+                       a.Hv, norm, a.err, a.ls_qk, a.ls_v, a.ls_gate, a.ls_pool);
     return hipGetLastError();
 }
 
 template <int D, typename T>
 hipError_t launch_commit_d(const gdn_tree_desc& d, const CommitArgs& a, int norm, size_t lds,
                            hipStream_t s) {
-    // vector loads need every 4-element group of k and v aligned to 4 elements
-    const bool vec = (a.rs_qk % 4 == 0) && (a.rs_v % 4 == 0) &&
+    // vector loads need every 4-element group of k and v (in every layer)
+    // aligned to 4 elements
+    const bool vec = (a.rs_qk % 4 == 0) && (a.rs_v % 4 == 0) && (a.ls_qk % 4 == 0) &&
+                     (a.ls_v % 4 == 0) &&
                      (reinterpret_cast<uintptr_t>(a.k) % (4 * sizeof(T)) == 0) &&
                      (reinterpret_cast<uintptr_t>(a.v) % (4 * sizeof(T)) == 0);
     return vec ? launch_commit_t<D, T, true>(d, a, norm, lds, s)
