@@ -28,6 +28,7 @@ BF16_NAN = np.uint16(0x7FC0)
 # random stream ids
 _S_ROWS, _S_Q, _S_K, _S_V, _S_A, _S_B, _S_POOL, _S_IDX, _S_PATH = range(1, 10)
 _S_X, _S_HIST, _S_W = 10, 11, 12
+_S_RAW_A, _S_RAW_B, _S_GATE_P = 13, 14, 15
 _S_TREE0 = 1_000_000  # + request index
 
 
@@ -296,4 +297,28 @@ def make_case(cfg: Config, seed: int = 2026, layer: int = 0, B: int | None = Non
             mask[perm] = False
             pool[mask] = np.nan
         out["pool"] = pool
+    return out
+
+
+def with_raw_gates(case: dict, gate_params: np.ndarray | None = None) -> dict:
+    """A copy of ``case`` whose gates are raw inputs (for GDN_F_RAW_GATES):
+    alpha and beta become a, b ~ N(0, 1) float32, NaN where the case's gates
+    are NaN (rows no node uses), and gate_params float32 [2][Hv] holds the
+    per-head A_log ~ U(0, log 16) and dt_bias ~ U(-7, -2) (so exp(A_log) lies
+    in [1, 16] and softplus(a + dt_bias) mostly between 1e-3 and 0.3).  Pass
+    the first step's gate_params to later steps of the same layer."""
+    cfg = case["cfg"]
+    seed, layer = case["seed"], case["layer"]
+    shape = case["alpha"].shape
+    a = rng(seed, cfg.cfg_id, layer, _S_RAW_A).standard_normal(shape, dtype=np.float32)
+    b = rng(seed, cfg.cfg_id, layer, _S_RAW_B).standard_normal(shape, dtype=np.float32)
+    pad = np.isnan(case["alpha"])
+    a[pad] = np.nan
+    b[pad] = np.nan
+    if gate_params is None:
+        g = rng(seed, cfg.cfg_id, layer, _S_GATE_P)
+        gate_params = np.stack([g.uniform(0.0, np.log(16.0), cfg.Hv),
+                                g.uniform(-7.0, -2.0, cfg.Hv)]).astype(np.float32)
+    out = dict(case)
+    out.update(alpha=a, beta=b, gate_params=np.asarray(gate_params, np.float32))
     return out
