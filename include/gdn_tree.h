@@ -79,6 +79,15 @@ extern "C" {
 #define GDN_F_NORM_QK 1  /* q, k <- x / sqrt(sum x^2 + 1e-6) inside verify and commit */
 #define GDN_F_OUT_BF16 2 /* verify writes o as bfloat16 (default float32) */
 #define GDN_F_VALU 4     /* verify: force the generic vector-ALU kernel (testing) */
+/* Raw gate inputs (LumoTree, Sec. IV-B: the verifier takes raw gate inputs
+ * and evaluates the gates in-kernel).  alpha and beta then hold the raw
+ * per-node inputs a and b (same layout), and gate_params the per-value-head
+ * parameters, float32 [2][Hv] (A_log, then dt_bias); every kernel uses
+ *   alpha = exp(-exp(A_log[h]) * softplus(a + dt_bias[h])),
+ *   beta  = 1 / (1 + exp(-b)),   softplus(x) = log(1 + exp(x)),
+ * evaluated in fp32.  Without the flag gate_params is ignored (may be NULL);
+ * with it a NULL gate_params is GDN_ERR_ARG. */
+#define GDN_F_RAW_GATES 8
 
 #define GDN_ACT_NONE 0
 #define GDN_ACT_SILU 1 /* z / (1 + exp(-z)) */
@@ -146,7 +155,8 @@ int32_t conv_ancestry_gather(const gdn_tree_desc *d, const void *x, const void *
  *          (strides let q/k/v alias the conv output: stride C, q at 0,
  *          k at Hqk*dk, v at 2*Hqk*dk)
  *   alpha, beta  float32 [B][R][Hv]: decay a_i and write strength b_i,
- *          already activated
+ *          already activated (or raw inputs with GDN_F_RAW_GATES)
+ *   gate_params  float32 [2][Hv] with GDN_F_RAW_GATES, else ignored
  *   state_pool   float32 [P][Hv][dv][dk]: committed states, read only
  *   state_idx    int32 [B]: pool slot of each request
  *   out    [B][R][Hv][dv] float32 (bf16 with GDN_F_OUT_BF16); node rows only
@@ -159,7 +169,7 @@ int32_t gdn_tree_verify(const gdn_tree_desc *d, const void *q, const void *k, co
                         const float *beta, const float *state_pool, int32_t P,
                         const int32_t *state_idx, void *out, int32_t Hqk, int32_t Hv,
                         int32_t dk, int32_t dv, int32_t dtype, int32_t flags,
-                        int32_t *err, void *stream);
+                        const float *gate_params, int32_t *err, void *stream);
 
 /* Accepted-path commit (LumoTree, Sec. IV-B: recorded accepted operands are
  * replayed through the gated delta update, in place into the fp32 state bank;
@@ -176,19 +186,22 @@ int32_t gdn_tree_verify(const gdn_tree_desc *d, const void *q, const void *k, co
  *             W is 1): conv input bf16 [B][R][C] and conv history bf16
  *             [P][W-1][C]; the history of slot state_idx[b] becomes the last
  *             W-1 entries of (old history ++ x rows of the path).
- * flags: GDN_F_NORM_QK (must match verify).  state_idx values must be
- * distinct across requests (a shared slot is GDN_EV_STATE for both). */
+ * flags: GDN_F_NORM_QK, GDN_F_RAW_GATES (both must match verify; gate_params
+ * as in verify).  state_idx values must be distinct across requests (a
+ * shared slot is GDN_EV_STATE for both). */
 int32_t gdn_tree_commit(const gdn_tree_desc *d, const int32_t *path, const int32_t *path_len,
                         int32_t Lmax, const void *k, const void *v, int64_t row_stride_qk,
                         int64_t row_stride_v, const float *alpha, const float *beta,
                         float *state_pool, int32_t P, const int32_t *state_idx,
                         const void *x, void *hist, int32_t C, int32_t Hqk, int32_t Hv,
-                        int32_t dk, int32_t dv, int32_t dtype, int32_t flags, int32_t *err,
-                        void *stream);
+                        int32_t dk, int32_t dv, int32_t dtype, int32_t flags,
+                        const float *gate_params, int32_t *err, void *stream);
 
-/* Commit of one accepted path into L layers' states in one launch (the
- * publication after acceptance covers every GDN layer of the model: LumoTree,
- * Sec. IV-B and V-A; the same tree, path and slots for every layer).  Layer
+/* Commit of one accepted path into L layers' states in one launch (technical
+ * review of Bole, Sec. 7, unified cross-layer state commit: one batched
+ * launch after acceptance for every recurrent layer; LumoTree, Sec. IV-B and
+ * V-A: one accepted path drives every layer's publication -- the same tree,
+ * path and slots for every layer).  Layer
  * l's k, v, gates and state pool are the given buffers offset by l times the
  * layer strides, in elements; each layer's buffers follow gdn_tree_commit's
  * layouts and must not overlap the next layer's.  The result equals
@@ -197,7 +210,9 @@ int32_t gdn_tree_commit(const gdn_tree_desc *d, const int32_t *path, const int32
  *   layers            1..; B * Hv * layers < 2^31
  *   layer_stride_qk   >= B * R * row_stride_qk (k), layer_stride_v likewise
  *   layer_stride_gate >= B * R * Hv (alpha and beta)
- *   layer_stride_pool >= P * Hv * dv * dk, a multiple of 4 (16-byte alignment) */
+ *   layer_stride_pool >= P * Hv * dv * dk, a multiple of 4 (16-byte alignment)
+ *   gate_params       with GDN_F_RAW_GATES: float32 [layers][2][Hv], each
+ *                     layer's A_log and dt_bias */
 int32_t gdn_tree_commit_layers(const gdn_tree_desc *d, const int32_t *path,
                                const int32_t *path_len, int32_t Lmax, int32_t layers,
                                const void *k, const void *v, int64_t row_stride_qk,
@@ -206,7 +221,8 @@ int32_t gdn_tree_commit_layers(const gdn_tree_desc *d, const int32_t *path,
                                int64_t layer_stride_gate, float *state_pool,
                                int64_t layer_stride_pool, int32_t P, const int32_t *state_idx,
                                int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv, int32_t dtype,
-                               int32_t flags, int32_t *err, void *stream);
+                               int32_t flags, const float *gate_params, int32_t *err,
+                               void *stream);
 
 /* ---- fused steady-state step ---------------------------------------------
  * In a decode loop every step commits the previous step's accepted path and
@@ -253,7 +269,9 @@ int32_t conv_ancestry_gather_publish(const gdn_tree_desc *d, const void *x, void
  * state.  state_pool is updated in place (as gdn_tree_commit does, without
  * the history, which conv_ancestry_gather_publish handles) and out receives
  * d's outputs (as gdn_tree_verify).
- *   q, k, v, strides, alpha, beta, out, flags: the new tree, as in verify
+ *   q, k, v, strides, alpha, beta, out, flags, gate_params: the new tree,
+ *            as in verify (with GDN_F_RAW_GATES the previous tree's gates
+ *            are raw inputs too, of the same layer's gate_params)
  *   k_prev, v_prev, row strides, alpha_prev, beta_prev: the operands
  *            recorded for the previous tree (same layout rules)
  *   d_prev, path_rows, path_n, Lmax: the previous tree and its path, resolved
@@ -268,8 +286,8 @@ int32_t gdn_tree_commit_verify(const gdn_tree_desc *d, const void *q, const void
                                const void *v_prev, int64_t row_stride_qk_prev,
                                int64_t row_stride_v_prev, const float *alpha_prev,
                                const float *beta_prev, int32_t Hqk, int32_t Hv, int32_t dk,
-                               int32_t dv, int32_t dtype, int32_t flags, int32_t *err,
-                               void *stream);
+                               int32_t dv, int32_t dtype, int32_t flags,
+                               const float *gate_params, int32_t *err, void *stream);
 
 /* ---- one launch per layer ------------------------------------------------
  * A model runs the same step for every GDN layer: commit the previous step's
@@ -344,7 +362,8 @@ int32_t gdn_step_prepare(const gdn_tree_desc *d, const gdn_tree_desc *d_prev,
  *             range before use, so no access leaves the buffers)
  * Requirements: bf16, dk = dv = 128, d->N <= 32, d_prev->B == d->B,
  * 1 <= Lmax <= 64, x, x_prev, hist_in, hist_out 16-byte aligned, state_pool
- * 16-byte aligned.  flags: GDN_F_NORM_QK, GDN_F_OUT_BF16.  Errors: a
+ * 16-byte aligned.  flags: GDN_F_NORM_QK, GDN_F_OUT_BF16, GDN_F_RAW_GATES
+ * (gate_params as in verify; both trees' gates raw).  Errors: a
  * malformed new tree gets no outputs (its path is still committed and its
  * history published); n_b = -1 writes neither state nor history. */
 int32_t gdn_layer_step(const gdn_tree_desc *d, const void *x, const void *w, const float *bias,
@@ -355,14 +374,15 @@ int32_t gdn_layer_step(const gdn_tree_desc *d, const void *x, const void *w, con
                        const float *alpha_prev, const float *beta_prev,
                        const int32_t *path_rows, const int32_t *path_n, int32_t Lmax,
                        int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv, int32_t flags,
-                       int32_t *err, void *stream);
+                       const float *gate_params, int32_t *err, void *stream);
 
 /* Human-readable name of a return code (host; static string). */
 const char *gdn_status_string(int32_t status);
 
-/* ABI version of this header: 4 (1, plus the two fused-step calls in 2,
+/* ABI version of this header: 5 (1, plus the two fused-step calls in 2,
  * plus gdn_path_resolve, gdn_step_prepare and gdn_layer_step in 3, plus
- * gdn_tree_commit_layers). */
+ * gdn_tree_commit_layers in 4, plus GDN_F_RAW_GATES and the gate_params
+ * argument of verify, commit and the fused calls). */
 int32_t gdn_abi_version(void);
 
 #ifdef __cplusplus

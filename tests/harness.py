@@ -10,6 +10,7 @@ import numpy as np
 
 import gdn_inputs as gi
 import oracle
+from oracle.gates import gates_from_raw as oracle_gate_eval
 
 NAN_BF16 = 0x7FC0
 
@@ -123,13 +124,15 @@ def run_gpu(case, flags=0, commit=True, shared=False, out_bf16=False, raise_on_e
     odt = torch.bfloat16 if out_bf16 else torch.float32
     out = torch.full((B, R, Hv, D), float("nan"), dtype=odt, device="cuda")
     vflags = flags | (g.GDN_F_OUT_BF16 if out_bf16 else 0)
+    gp = dev_gate_params(case)
     res["rc_verify"] = g.gdn_tree_verify(desc, q, k, v, alpha, beta, pool, sidx, out, err,
-                                         flags=vflags, raise_on_error=raise_on_error)
+                                         flags=vflags, raise_on_error=raise_on_error,
+                                         gate_params=gp)
     if commit:
         res["rc_commit"] = g.gdn_tree_commit(desc, to_dev(case["path"]), to_dev(case["path_len"]),
                                              k, v, alpha, beta, pool, sidx, err, Hqk=Hqk,
                                              flags=flags & g.GDN_F_NORM_QK, x=x, hist=hist,
-                                             raise_on_error=raise_on_error)
+                                             raise_on_error=raise_on_error, gate_params=gp)
     torch.cuda.synchronize()
     res.update(err=int(err.item()), depth=desc.depth.cpu().numpy(),
                anc=desc.anc.cpu().numpy().view(np.uint64), conv_src=desc.conv_src.cpu().numpy()[:, :, :W - 1],
@@ -166,13 +169,14 @@ def run_oracle(case, commit=True, shared=False):
     else:
         q, k, v = case["q"], case["k"], case["v"]
         norm = False
-    out, e = oracle.verify(parent, rows, d["status"], q, k, v, case["alpha"], case["beta"],
+    alpha, beta = oracle_gates(case)
+    out, e = oracle.verify(parent, rows, d["status"], q, k, v, alpha, beta,
                            case["pool"], case["state_idx"], Hqk, Hv, norm, shared=shared)
     res["err"] |= e
     res["out"] = out
     if commit:
         pool, hist, e = oracle.commit(parent, rows, d["status"], case["path"], case["path_len"], k, v,
-                                      case["alpha"], case["beta"], case["pool"], case["state_idx"],
+                                      alpha, beta, case["pool"], case["state_idx"],
                                       Hqk, Hv, norm, x=case.get("x"), hist=case.get("hist"), W=W,
                                       shared=shared)
         res["err"] |= e
@@ -180,6 +184,18 @@ def run_oracle(case, commit=True, shared=False):
         if hist is not None:
             res["hist"] = hist
     return res
+
+
+def oracle_gates(case):
+    """The gates the oracle uses: the case's own, or, for raw gate inputs,
+    the oracle's fp64 evaluation of them."""
+    if "gate_params" in case:
+        return oracle_gate_eval(case["alpha"], case["beta"], case["gate_params"])
+    return case["alpha"], case["beta"]
+
+
+def dev_gate_params(case):
+    return to_dev(case["gate_params"]) if "gate_params" in case else None
 
 
 def hist_to_bits(h64):
@@ -279,8 +295,9 @@ def run_oracle_two_steps(c1, c2):
         res["y1"] = y1b
     else:
         k1, v1 = c1["k"], c1["v"]
+    a1, b1 = oracle_gates(c1)
     pool, hist, e = oracle.commit(c1["parent"], c1["node_row"], d1["status"], c1["path"],
-                                  c1["path_len"], k1, v1, c1["alpha"], c1["beta"], c1["pool"],
+                                  c1["path_len"], k1, v1, a1, b1, c1["pool"],
                                   c1["state_idx"], Hqk, Hv, norm, x=c1.get("x"), hist=c1.get("hist"),
                                   W=W)
     res["err"] |= e
@@ -296,8 +313,9 @@ def run_oracle_two_steps(c1, c2):
         res["y2"] = y2b
     else:
         q2, k2, v2 = c2["q"], c2["k"], c2["v"]
-    out, e = oracle.verify(c2["parent"], c2["node_row"], d2["status"], q2, k2, v2, c2["alpha"],
-                           c2["beta"], pool, c2["state_idx"], Hqk, Hv, norm)
+    a2, b2 = oracle_gates(c2)
+    out, e = oracle.verify(c2["parent"], c2["node_row"], d2["status"], q2, k2, v2, a2, b2, pool,
+                           c2["state_idx"], Hqk, Hv, norm)
     res["err"] |= e
     res["out"] = out
     return res
@@ -324,6 +342,7 @@ def run_gpu_two_steps(c1, c2, fused=True, y1_override=None, y2_override=None, fl
     sidx = to_dev(c1["state_idx"])
     a1, b1 = to_dev(c1["alpha"]), to_dev(c1["beta"])
     a2, b2 = to_dev(c2["alpha"]), to_dev(c2["beta"])
+    gp = dev_gate_params(c1)  # the layer's gate parameters (both steps)
     p1, l1 = to_dev(c1["path"]), to_dev(c1["path_len"])
     if fused:  # the fused calls take the path resolved; step 2's descriptor in the same launch
         prow = torch.full(p1.shape, -7, dtype=torch.int32, device="cuda")
@@ -352,7 +371,7 @@ def run_gpu_two_steps(c1, c2, fused=True, y1_override=None, y2_override=None, fl
                                            x1, err)
         else:
             g.gdn_tree_commit(d1, p1, l1, k1, v1, a1, b1, pool, sidx, err, Hqk=Hqk,
-                              flags=flags & g.GDN_F_NORM_QK, x=x1, hist=hist)
+                              flags=flags & g.GDN_F_NORM_QK, x=x1, hist=hist, gate_params=gp)
             g.conv_ancestry_gather(d2, x2, hist, sidx, w2, None, y2, cfg.act, err)
         res["y2"] = bits(y2)
         if y2_override is not None:
@@ -367,12 +386,12 @@ def run_gpu_two_steps(c1, c2, fused=True, y1_override=None, y2_override=None, fl
     out = torch.full((B, R, Hv, D), float("nan"), dtype=torch.float32, device="cuda")
     if fused:
         g.gdn_tree_commit_verify(d2, q2, k2, v2, a2, b2, pool, sidx, out, d1, prow, pn, k1, v1, a1,
-                                 b1, err, flags=flags)
+                                 b1, err, flags=flags, gate_params=gp)
     else:
         if cfg.conv_W == 0:
             g.gdn_tree_commit(d1, p1, l1, k1, v1, a1, b1, pool, sidx, err, Hqk=Hqk,
-                              flags=flags & g.GDN_F_NORM_QK)
-        g.gdn_tree_verify(d2, q2, k2, v2, a2, b2, pool, sidx, out, err, flags=flags)
+                              flags=flags & g.GDN_F_NORM_QK, gate_params=gp)
+        g.gdn_tree_verify(d2, q2, k2, v2, a2, b2, pool, sidx, out, err, flags=flags, gate_params=gp)
     torch.cuda.synchronize()
     res.update(err=int(err.item()), out=out.cpu().numpy(), pool=pool.cpu().numpy(),
                status1=d1.status.cpu().numpy(), status2=d2.status.cpu().numpy())
@@ -415,7 +434,7 @@ def run_gpu_layer(c1, c2, flags=0, with_y=True, prepare=False):
     g.gdn_layer_step(d2, to_dev(c2["x"]), to_dev(c2["w"]), None, cfg.act, hist_in, hist_out,
                      to_dev(c2["alpha"]), to_dev(c2["beta"]), pool, sidx, out, d1, to_dev(c1["x"]),
                      to_dev(c1["alpha"]), to_dev(c1["beta"]), path_rows, path_n, err, Hqk,
-                     flags=flags, y=y)
+                     flags=flags, y=y, gate_params=dev_gate_params(c1))
     torch.cuda.synchronize()
     res = dict(err=int(err.item()), out=out.cpu().numpy(), pool=pool.cpu().numpy(),
                hist_out=bits(hist_out), hist_in=bits(hist_in), path_n=path_n.cpu().numpy(),

@@ -46,7 +46,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.gdn_abi_version() == 4
+    assert lib.gdn_abi_version() == 5
     assert lib.gdn_status_string(0) == b"ok"
     assert lib.gdn_status_string(-1) == b"invalid argument"
     assert lib.gdn_status_string(-4) == b"unsupported size"
@@ -73,26 +73,26 @@ def test_argument_checks_fail_before_launch(lib):
     p = ctypes.c_void_p(256)
     # verify: bad head ratio, d_k != d_v, bad dtype, unknown flag, short row stride
     V = lib.gdn_tree_verify
-    assert V(d, p, p, p, 2048, 4096, p, p, p, 4, p, p, 3, 32, 128, 128, 0, 0, err, None) == g.GDN_ERR_ARG
-    assert V(d, p, p, p, 2048, 4096, p, p, p, 4, p, p, 16, 32, 128, 64, 0, 0, err, None) == g.GDN_ERR_UNSUPPORTED
-    assert V(d, p, p, p, 2048, 4096, p, p, p, 4, p, p, 16, 32, 96, 96, 0, 0, err, None) == g.GDN_ERR_UNSUPPORTED
-    assert V(d, p, p, p, 2048, 4096, p, p, p, 4, p, p, 16, 32, 128, 128, 7, 0, err, None) == g.GDN_ERR_ARG
-    assert V(d, p, p, p, 2048, 4096, p, p, p, 4, p, p, 16, 32, 128, 128, 0, 64, err, None) == g.GDN_ERR_ARG
-    assert V(d, p, p, p, 100, 4096, p, p, p, 4, p, p, 16, 32, 128, 128, 0, 0, err, None) == g.GDN_ERR_ARG
-    assert V(d, None, p, p, 2048, 4096, p, p, p, 4, p, p, 16, 32, 128, 128, 0, 0, err, None) == g.GDN_ERR_ARG
+    assert V(d, p, p, p, 2048, 4096, p, p, p, 4, p, p, 3, 32, 128, 128, 0, 0, None, err, None) == g.GDN_ERR_ARG
+    assert V(d, p, p, p, 2048, 4096, p, p, p, 4, p, p, 16, 32, 128, 64, 0, 0, None, err, None) == g.GDN_ERR_UNSUPPORTED
+    assert V(d, p, p, p, 2048, 4096, p, p, p, 4, p, p, 16, 32, 96, 96, 0, 0, None, err, None) == g.GDN_ERR_UNSUPPORTED
+    assert V(d, p, p, p, 2048, 4096, p, p, p, 4, p, p, 16, 32, 128, 128, 7, 0, None, err, None) == g.GDN_ERR_ARG
+    assert V(d, p, p, p, 2048, 4096, p, p, p, 4, p, p, 16, 32, 128, 128, 0, 64, None, err, None) == g.GDN_ERR_ARG
+    assert V(d, p, p, p, 100, 4096, p, p, p, 4, p, p, 16, 32, 128, 128, 0, 0, None, err, None) == g.GDN_ERR_ARG
+    assert V(d, None, p, p, 2048, 4096, p, p, p, 4, p, p, 16, 32, 128, 128, 0, 0, None, err, None) == g.GDN_ERR_ARG
     # commit: Lmax out of range, x without hist
     Cm = lib.gdn_tree_commit
-    assert Cm(d, p, p, 0, p, p, 2048, 4096, p, p, p, 4, p, None, None, 0, 16, 32, 128, 128, 0, 0, err, None) == g.GDN_ERR_UNSUPPORTED
-    assert Cm(d, p, p, 65, p, p, 2048, 4096, p, p, p, 4, p, None, None, 0, 16, 32, 128, 128, 0, 0, err, None) == g.GDN_ERR_UNSUPPORTED
-    assert Cm(d, p, p, 7, p, p, 2048, 4096, p, p, p, 4, p, p, None, 8, 16, 32, 128, 128, 0, 0, err, None) == g.GDN_ERR_ARG
+    assert Cm(d, p, p, 0, p, p, 2048, 4096, p, p, p, 4, p, None, None, 0, 16, 32, 128, 128, 0, 0, None, err, None) == g.GDN_ERR_UNSUPPORTED
+    assert Cm(d, p, p, 65, p, p, 2048, 4096, p, p, p, 4, p, None, None, 0, 16, 32, 128, 128, 0, 0, None, err, None) == g.GDN_ERR_UNSUPPORTED
+    assert Cm(d, p, p, 7, p, p, 2048, 4096, p, p, p, 4, p, p, None, 8, 16, 32, 128, 128, 0, 0, None, err, None) == g.GDN_ERR_ARG
     # commit over layers (B = 2, R = 8: 16 rows; P = 4): no layers, overlapping
     # layer strides, an unknown flag, a pool stride that breaks alignment
     Cl = lib.gdn_tree_commit_layers
     ok = (16 * 2048, 16 * 4096, 16 * 32, 4 * 32 * 128 * 128)
 
-    def cl(layers=3, strides=ok, flags=0, Lmax=7):
+    def cl(layers=3, strides=ok, flags=0, Lmax=7, gp=None):
         return Cl(d, p, p, Lmax, layers, p, p, 2048, 4096, strides[0], strides[1], p, p, strides[2], p,
-                  strides[3], 4, p, 16, 32, 128, 128, 0, flags, err, None)
+                  strides[3], 4, p, 16, 32, 128, 128, 0, flags, gp, err, None)
     assert cl(layers=0) == g.GDN_ERR_ARG
     assert cl(strides=(15 * 2048,) + ok[1:]) == g.GDN_ERR_ARG
     assert cl(strides=ok[:1] + (16 * 4096 - 1,) + ok[2:]) == g.GDN_ERR_ARG
@@ -101,6 +101,8 @@ def test_argument_checks_fail_before_launch(lib):
     assert cl(strides=ok[:3] + (ok[3] + 2,)) == g.GDN_ERR_ARG
     assert cl(flags=g.GDN_F_OUT_BF16) == g.GDN_ERR_ARG
     assert cl(Lmax=65) == g.GDN_ERR_UNSUPPORTED
+    assert cl(flags=g.GDN_F_RAW_GATES) == g.GDN_ERR_ARG      # raw gates without parameters
+    assert cl(flags=g.GDN_F_RAW_GATES, gp=ctypes.c_void_p(258)) == g.GDN_ERR_ARG  # misaligned
     # conv: channel count not a multiple of 4, bad activation
     Cv = lib.conv_ancestry_gather
     assert Cv(d, p, p, 4, p, p, None, p, 8190, 1, err, None) == g.GDN_ERR_UNSUPPORTED
@@ -134,9 +136,10 @@ def test_fused_step_argument_checks_fail_before_launch(lib):
         return F(d, a["q"], a["k"], a["v"], a["rqk"], a["rv"], a["a"], a["b"], a["pool"], a["P"],
                  a["sidx"], a["out"], a["prev"], a["path"], a["plen"], a["Lmax"], a["kp"], a["vp"],
                  a["rqkp"], a["rvp"], a["ap"], a["bp"], a["Hqk"], a["Hv"], a["dk"], a["dv"], a["dt"],
-                 a["fl"], err, None)
+                 a["fl"], a.get("gp"), err, None)
     assert call(prev=other_b) == g.GDN_ERR_ARG
     assert call(Lmax=65) == g.GDN_ERR_UNSUPPORTED
+    assert call(fl=g.GDN_F_RAW_GATES) == g.GDN_ERR_ARG      # raw gates without parameters
     assert call(rqkp=100) == g.GDN_ERR_ARG
     assert call(bp=None) == g.GDN_ERR_ARG
     assert call(fl=64) == g.GDN_ERR_ARG
@@ -175,13 +178,15 @@ def test_layer_step_argument_checks_fail_before_launch(lib):
         a.update(kw)
         return L(a["d"], a["x"], a["w"], a["bias"], a["act"], a["hin"], a["hout"], a["a"], a["b"],
                  a["pool"], a["P"], a["sidx"], a["out"], a["y"], a["prev"], a["xp"], a["ap"], a["bp"],
-                 a["prow"], a["pn"], a["Lmax"], a["Hqk"], a["Hv"], a["dk"], a["dv"], a["fl"], err, None)
+                 a["prow"], a["pn"], a["Lmax"], a["Hqk"], a["Hv"], a["dk"], a["dv"], a["fl"], a.get("gp"),
+                 err, None)
     assert call(prev=other_b) == g.GDN_ERR_ARG              # previous tree of another batch
     assert call(d=big) == g.GDN_ERR_UNSUPPORTED             # N > 32
     assert call(dk=64, dv=64) == g.GDN_ERR_UNSUPPORTED      # d != 128
     assert call(Lmax=65) == g.GDN_ERR_UNSUPPORTED
     assert call(act=2) == g.GDN_ERR_ARG
-    assert call(fl=4) == g.GDN_ERR_ARG                      # only NORM_QK and OUT_BF16
+    assert call(fl=4) == g.GDN_ERR_ARG                      # only NORM_QK, OUT_BF16, RAW_GATES
+    assert call(fl=1 | g.GDN_F_RAW_GATES) == g.GDN_ERR_ARG  # raw gates without parameters
     assert call(hout=None) == g.GDN_ERR_ARG
     assert call(hout=args["hin"]) == g.GDN_ERR_ARG          # history buffers overlap
     assert call(hout=ctypes.c_void_p((1 << 20) + hbytes - 16)) == g.GDN_ERR_ARG

@@ -34,7 +34,7 @@ __all__ = [
 GDN_OK, GDN_ERR_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, -1, -4, -5
 GDN_EV_PARENT, GDN_EV_ROW, GDN_EV_STATE, GDN_EV_PATH = 1, 2, 4, 8
 GDN_DT_BF16, GDN_DT_F32 = 0, 1
-GDN_F_NORM_QK, GDN_F_OUT_BF16, GDN_F_VALU = 1, 2, 4
+GDN_F_NORM_QK, GDN_F_OUT_BF16, GDN_F_VALU, GDN_F_RAW_GATES = 1, 2, 4, 8
 GDN_ACT_NONE, GDN_ACT_SILU = 0, 1
 
 EXPORTED = ("gdn_tree_desc_build", "conv_ancestry_gather", "gdn_tree_verify",
@@ -85,21 +85,21 @@ def load_library():
         lib.conv_ancestry_gather.argtypes = [dp, vp, vp, i32, vp, vp, vp, vp, i32, i32, vp, vp]
         lib.gdn_tree_verify.restype = i32
         lib.gdn_tree_verify.argtypes = [dp, vp, vp, vp, i64, i64, vp, vp, vp, i32, vp, vp,
-                                        i32, i32, i32, i32, i32, i32, vp, vp]
+                                        i32, i32, i32, i32, i32, i32, vp, vp, vp]
         lib.gdn_tree_commit.restype = i32
         lib.gdn_tree_commit.argtypes = [dp, vp, vp, i32, vp, vp, i64, i64, vp, vp, vp, i32, vp,
-                                        vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp]
+                                        vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp]
         lib.gdn_tree_commit_layers.restype = i32
         lib.gdn_tree_commit_layers.argtypes = [dp, vp, vp, i32, i32, vp, vp, i64, i64, i64, i64,
                                                vp, vp, i64, vp, i64, i32, vp, i32, i32, i32, i32,
-                                               i32, i32, vp, vp]
+                                               i32, i32, vp, vp, vp]
         lib.conv_ancestry_gather_publish.restype = i32
         lib.conv_ancestry_gather_publish.argtypes = [dp, vp, vp, i32, vp, vp, vp, vp, i32, i32,
                                                      dp, vp, vp, i32, vp, vp, vp]
         lib.gdn_tree_commit_verify.restype = i32
         lib.gdn_tree_commit_verify.argtypes = [dp, vp, vp, vp, i64, i64, vp, vp, vp, i32, vp, vp,
                                                dp, vp, vp, i32, vp, vp, i64, i64, vp, vp,
-                                               i32, i32, i32, i32, i32, i32, vp, vp]
+                                               i32, i32, i32, i32, i32, i32, vp, vp, vp]
         lib.gdn_path_resolve.restype = i32
         lib.gdn_path_resolve.argtypes = [dp, vp, vp, i32, vp, i32, vp, vp, vp, vp]
         lib.gdn_step_prepare.restype = i32
@@ -107,7 +107,7 @@ def load_library():
         lib.gdn_layer_step.restype = i32
         lib.gdn_layer_step.argtypes = [dp, vp, vp, vp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp,
                                        dp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
-                                       vp, vp]
+                                       vp, vp, vp]
         lib.gdn_status_string.restype = ctypes.c_char_p
         lib.gdn_status_string.argtypes = [i32]
         lib.gdn_abi_version.restype = i32
@@ -161,6 +161,13 @@ def _rows_view(t, name):
     if s3 != 1 or s2 != D or (B > 1 and s0 != R * s1):
         raise ValueError(f"{name}: layout not expressible as rows of stride {s1}")
     return s1, H, D
+
+
+def _gate_flags(flags, gate_params):
+    """flags, with GDN_F_RAW_GATES set when gate parameters are passed: alpha
+    and beta then hold raw gate inputs, gate_params the per-head A_log and
+    dt_bias (float32 [2, Hv], or [L, 2, Hv] for the layer-batched commit)."""
+    return int(flags) | (GDN_F_RAW_GATES if gate_params is not None else 0)
 
 
 def _check(code, what, raise_on_error):
@@ -225,7 +232,7 @@ def conv_ancestry_gather(desc: TreeDesc, x, hist, state_idx, w, bias, y, act: in
 
 
 def gdn_tree_verify(desc: TreeDesc, q, k, v, alpha, beta, state_pool, state_idx, out, err,
-                    flags: int = 0, stream=None, raise_on_error=True) -> int:
+                    flags: int = 0, stream=None, raise_on_error=True, gate_params=None) -> int:
     """Every node's output.  q, k: [B, R, Hqk, D] views (row-strided), v: [B, R, Hv, D],
     alpha/beta fp32 [B, R, Hv], state_pool fp32 [P, Hv, D, D], state_idx int32 [B],
     out [B, R, Hv, D] fp32 (bf16 with GDN_F_OUT_BF16)."""
@@ -238,13 +245,14 @@ def gdn_tree_verify(desc: TreeDesc, q, k, v, alpha, beta, state_pool, state_idx,
     code = load_library().gdn_tree_verify(desc.ref(), _ptr(q), _ptr(k), _ptr(v), rs_qk, rs_v,
                                           _ptr(alpha), _ptr(beta), _ptr(state_pool), P,
                                           _ptr(state_idx), _ptr(out), Hqk, Hv, dk, dv,
-                                          _dtype_code(q), int(flags), _ptr(err), _stream(stream))
+                                          _dtype_code(q), _gate_flags(flags, gate_params),
+                                          _ptr(gate_params), _ptr(err), _stream(stream))
     return _check(code, "gdn_tree_verify", raise_on_error)
 
 
 def gdn_tree_commit(desc: TreeDesc, path, path_len, k, v, alpha, beta, state_pool, state_idx,
                     err, Hqk: int | None = None, flags: int = 0, x=None, hist=None,
-                    stream=None, raise_on_error=True) -> int:
+                    stream=None, raise_on_error=True, gate_params=None) -> int:
     """Replay path [B, Lmax] (len path_len [B]) into state_pool in place; with
     x / hist also publish the conv history."""
     rs_qk, Hk, dk = _rows_view(k, "k")
@@ -257,7 +265,8 @@ def gdn_tree_commit(desc: TreeDesc, path, path_len, k, v, alpha, beta, state_poo
                                           _ptr(v), rs_qk, rs_v, _ptr(alpha), _ptr(beta),
                                           _ptr(state_pool), P, _ptr(state_idx), _ptr(x),
                                           _ptr(hist), C, Hqk, Hv, dk, dv, _dtype_code(k),
-                                          int(flags), _ptr(err), _stream(stream))
+                                          _gate_flags(flags, gate_params), _ptr(gate_params),
+                                          _ptr(err), _stream(stream))
     return _check(code, "gdn_tree_commit", raise_on_error)
 
 
@@ -269,7 +278,7 @@ def _layer_stride(t, name, L):
 
 def gdn_tree_commit_layers(desc: TreeDesc, path, path_len, k, v, alpha, beta, state_pool,
                            state_idx, err, Hqk: int | None = None, flags: int = 0, stream=None,
-                           raise_on_error=True) -> int:
+                           raise_on_error=True, gate_params=None) -> int:
     """Replay path [B, Lmax] into every layer's state in one launch: k
     [L, B, R, Hqk, dk], v [L, B, R, Hv, dv], alpha / beta [L, B, R, Hv],
     state_pool [L, P, Hv, dv, dk]; layer l is gdn_tree_commit on the l-th
@@ -292,7 +301,8 @@ def gdn_tree_commit_layers(desc: TreeDesc, path, path_len, k, v, alpha, beta, st
         _layer_stride(k, "k", L), _layer_stride(v, "v", L), _ptr(alpha), _ptr(beta),
         _layer_stride(alpha, "alpha", L), _ptr(state_pool),
         _layer_stride(state_pool, "state_pool", L), P, _ptr(state_idx), Hqk, Hv, dk, dv,
-        _dtype_code(k), int(flags), _ptr(err), _stream(stream))
+        _dtype_code(k), _gate_flags(flags, gate_params), _ptr(gate_params), _ptr(err),
+        _stream(stream))
     return _check(code, "gdn_tree_commit_layers", raise_on_error)
 
 
@@ -316,7 +326,7 @@ def conv_ancestry_gather_publish(desc: TreeDesc, x, hist, state_idx, w, bias, y,
 def gdn_tree_commit_verify(desc: TreeDesc, q, k, v, alpha, beta, state_pool, state_idx, out,
                            prev: TreeDesc, path_rows, path_n, k_prev, v_prev, alpha_prev,
                            beta_prev, err, flags: int = 0, stream=None,
-                           raise_on_error=True) -> int:
+                           raise_on_error=True, gate_params=None) -> int:
     """Commit the previous step's accepted path (prev's tree; the path resolved
     into path_rows / path_n; its recorded k_prev, v_prev, alpha_prev,
     beta_prev) into state_pool, then verify desc's tree from the committed
@@ -336,7 +346,8 @@ def gdn_tree_commit_verify(desc: TreeDesc, q, k, v, alpha, beta, state_pool, sta
         desc.ref(), _ptr(q), _ptr(k), _ptr(v), rs_qk, rs_v, _ptr(alpha), _ptr(beta),
         _ptr(state_pool), P, _ptr(state_idx), _ptr(out), prev.ref(), _ptr(path_rows), _ptr(path_n),
         Lmax, _ptr(k_prev), _ptr(v_prev), rs_qkp, rs_vp, _ptr(alpha_prev), _ptr(beta_prev), Hqk,
-        Hv, dk, dv, _dtype_code(q), int(flags), _ptr(err), _stream(stream))
+        Hv, dk, dv, _dtype_code(q), _gate_flags(flags, gate_params), _ptr(gate_params), _ptr(err),
+        _stream(stream))
     return _check(code, "gdn_tree_commit_verify", raise_on_error)
 
 
@@ -366,6 +377,7 @@ def gdn_step_prepare(desc: TreeDesc, prev: TreeDesc, path, path_len, state_idx, 
 def gdn_layer_step(desc: TreeDesc, x, w, bias, act: int, hist_in, hist_out, alpha, beta,
                    state_pool, state_idx, out, prev: TreeDesc, x_prev, alpha_prev, beta_prev,
                    path_rows, path_n, err, Hqk: int, flags: int = 0, y=None, stream=None,
+                   gate_params=None,
                    raise_on_error=True) -> int:
     """One GDN layer's step in one launch: commit the previous path (resolved
     by gdn_path_resolve) with its k/v recomputed from x_prev and hist_in,
@@ -378,5 +390,6 @@ def gdn_layer_step(desc: TreeDesc, x, w, bias, act: int, hist_in, hist_out, alph
         desc.ref(), _ptr(x), _ptr(w), _ptr(bias), int(act), _ptr(hist_in), _ptr(hist_out),
         _ptr(alpha), _ptr(beta), _ptr(state_pool), P, _ptr(state_idx), _ptr(out), _ptr(y),
         prev.ref(), _ptr(x_prev), _ptr(alpha_prev), _ptr(beta_prev), _ptr(path_rows),
-        _ptr(path_n), Lmax, int(Hqk), Hv, dk, dv, int(flags), _ptr(err), _stream(stream))
+        _ptr(path_n), Lmax, int(Hqk), Hv, dk, dv, _gate_flags(flags, gate_params), _ptr(gate_params),
+        _ptr(err), _stream(stream))
     return _check(code, "gdn_layer_step", raise_on_error)

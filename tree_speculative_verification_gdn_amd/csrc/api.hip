@@ -36,7 +36,13 @@ int32_t check_heads(int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv, int32_t dty
 
 extern "C" {
 
-int32_t gdn_abi_version(void) { return 4; }
+// GDN_F_RAW_GATES needs the per-head gate parameters (4-byte aligned floats)
+static int32_t check_gates(int32_t flags, const float* gate_params) {
+    if ((flags & GDN_F_RAW_GATES) == 0) return GDN_OK;
+    return (gate_params != nullptr && aligned(gate_params, 4)) ? GDN_OK : GDN_ERR_ARG;
+}
+
+int32_t gdn_abi_version(void) { return 5; }
 
 const char* gdn_status_string(int32_t status) {
     switch (status) {
@@ -81,19 +87,21 @@ int32_t gdn_tree_verify(const gdn_tree_desc* d, const void* q, const void* k, co
                         int64_t row_stride_qk, int64_t row_stride_v, const float* alpha,
                         const float* beta, const float* state_pool, int32_t P,
                         const int32_t* state_idx, void* out, int32_t Hqk, int32_t Hv, int32_t dk,
-                        int32_t dv, int32_t dtype, int32_t flags, int32_t* err, void* stream) {
+                        int32_t dv, int32_t dtype, int32_t flags, const float* gate_params,
+                        int32_t* err, void* stream) {
     int32_t st = check_desc(d);
     if (st != GDN_OK) return st;
     st = check_heads(Hqk, Hv, dk, dv, dtype);
     if (st != GDN_OK) return st;
     if (!q || !k || !v || !alpha || !beta || !state_pool || !state_idx || !out || !err || P < 1)
         return GDN_ERR_ARG;
-    if ((flags & ~(GDN_F_NORM_QK | GDN_F_OUT_BF16 | GDN_F_VALU)) != 0) return GDN_ERR_ARG;
+    if ((flags & ~(GDN_F_NORM_QK | GDN_F_OUT_BF16 | GDN_F_VALU | GDN_F_RAW_GATES)) != 0) return GDN_ERR_ARG;
+    if (check_gates(flags, gate_params) != GDN_OK) return GDN_ERR_ARG;
     if (row_stride_qk < static_cast<int64_t>(Hqk) * dk || row_stride_v < static_cast<int64_t>(Hv) * dv)
         return GDN_ERR_ARG;
     if (!aligned(state_pool, 16)) return GDN_ERR_ARG;
     gdn::VerifyArgs a{q, k, v, row_stride_qk, row_stride_v, alpha, beta, state_pool, P,
-                      state_idx, out, Hqk, Hv, dk, dtype, flags, err};
+                      state_idx, out, Hqk, Hv, dk, dtype, flags, err, gate_params};
     return map_launch(gdn::launch_verify(*d, a, static_cast<hipStream_t>(stream)));
 }
 
@@ -102,7 +110,8 @@ int32_t gdn_tree_commit(const gdn_tree_desc* d, const int32_t* path, const int32
                         int64_t row_stride_v, const float* alpha, const float* beta,
                         float* state_pool, int32_t P, const int32_t* state_idx, const void* x,
                         void* hist, int32_t C, int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv,
-                        int32_t dtype, int32_t flags, int32_t* err, void* stream) {
+                        int32_t dtype, int32_t flags, const float* gate_params, int32_t* err,
+                        void* stream) {
     int32_t st = check_desc(d);
     if (st != GDN_OK) return st;
     st = check_heads(Hqk, Hv, dk, dv, dtype);
@@ -110,6 +119,7 @@ int32_t gdn_tree_commit(const gdn_tree_desc* d, const int32_t* path, const int32
     if (!path || !path_len || !k || !v || !alpha || !beta || !state_pool || !state_idx || !err ||
         P < 1)
         return GDN_ERR_ARG;
+    if (check_gates(flags, gate_params) != GDN_OK) return GDN_ERR_ARG;
     if (Lmax < 1 || Lmax > GDN_MAX_NODES) return GDN_ERR_UNSUPPORTED;
     // the conv history exists only for W > 1; with W == 1 x and hist are ignored
     if (d->W == 1) {
@@ -119,13 +129,14 @@ int32_t gdn_tree_commit(const gdn_tree_desc* d, const int32_t* path, const int32
     if ((x == nullptr) != (hist == nullptr)) return GDN_ERR_ARG;
     if (x != nullptr && C < 1) return GDN_ERR_ARG;
     if (x != nullptr && (!aligned(x, 2) || !aligned(hist, 2))) return GDN_ERR_ARG;
-    if ((flags & ~GDN_F_NORM_QK) != 0) return GDN_ERR_ARG;
+    if ((flags & ~(GDN_F_NORM_QK | GDN_F_RAW_GATES)) != 0) return GDN_ERR_ARG;
     if (row_stride_qk < static_cast<int64_t>(Hqk) * dk || row_stride_v < static_cast<int64_t>(Hv) * dv)
         return GDN_ERR_ARG;
     if (!aligned(state_pool, 16)) return GDN_ERR_ARG;
     gdn::CommitArgs a{path, path_len, Lmax, k, v, row_stride_qk, row_stride_v, alpha, beta,
                       state_pool, P, state_idx, static_cast<const uint16_t*>(x),
                       static_cast<uint16_t*>(hist), x ? C : 0, Hqk, Hv, dk, dtype, flags, err, 0};
+    a.gate_params = gate_params;
     return map_launch(gdn::launch_commit(*d, a, static_cast<hipStream_t>(stream)));
 }
 
@@ -136,7 +147,7 @@ int32_t gdn_tree_commit_layers(const gdn_tree_desc* d, const int32_t* path, cons
                                int64_t layer_stride_gate, float* state_pool,
                                int64_t layer_stride_pool, int32_t P, const int32_t* state_idx,
                                int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv, int32_t dtype,
-                               int32_t flags, int32_t* err, void* stream) {
+                               int32_t flags, const float* gate_params, int32_t* err, void* stream) {
     int32_t st = check_desc(d);
     if (st != GDN_OK) return st;
     st = check_heads(Hqk, Hv, dk, dv, dtype);
@@ -145,7 +156,8 @@ int32_t gdn_tree_commit_layers(const gdn_tree_desc* d, const int32_t* path, cons
         P < 1 || layers < 1)
         return GDN_ERR_ARG;
     if (Lmax < 1 || Lmax > GDN_MAX_NODES) return GDN_ERR_UNSUPPORTED;
-    if ((flags & ~GDN_F_NORM_QK) != 0) return GDN_ERR_ARG;
+    if ((flags & ~(GDN_F_NORM_QK | GDN_F_RAW_GATES)) != 0) return GDN_ERR_ARG;
+    if (check_gates(flags, gate_params) != GDN_OK) return GDN_ERR_ARG;
     if (row_stride_qk < static_cast<int64_t>(Hqk) * dk || row_stride_v < static_cast<int64_t>(Hv) * dv)
         return GDN_ERR_ARG;
     // a layer's buffers must not overlap the next layer's
@@ -163,6 +175,7 @@ int32_t gdn_tree_commit_layers(const gdn_tree_desc* d, const int32_t* path, cons
     a.ls_v = layer_stride_v;
     a.ls_gate = layer_stride_gate;
     a.ls_pool = layer_stride_pool;
+    a.gate_params = gate_params;
     return map_launch(gdn::launch_commit(*d, a, static_cast<hipStream_t>(stream)));
 }
 
@@ -200,8 +213,8 @@ int32_t gdn_tree_commit_verify(const gdn_tree_desc* d, const void* q, const void
                                const void* k_prev, const void* v_prev, int64_t row_stride_qk_prev,
                                int64_t row_stride_v_prev, const float* alpha_prev,
                                const float* beta_prev, int32_t Hqk, int32_t Hv, int32_t dk,
-                               int32_t dv, int32_t dtype, int32_t flags, int32_t* err,
-                               void* stream) {
+                               int32_t dv, int32_t dtype, int32_t flags, const float* gate_params,
+                               int32_t* err, void* stream) {
     int32_t st = check_desc(d);
     if (st != GDN_OK) return st;
     st = check_desc(d_prev);
@@ -213,7 +226,8 @@ int32_t gdn_tree_commit_verify(const gdn_tree_desc* d, const void* q, const void
         !path_rows || !path_n || !k_prev || !v_prev || !alpha_prev || !beta_prev)
         return GDN_ERR_ARG;
     if (Lmax < 1 || Lmax > GDN_MAX_NODES) return GDN_ERR_UNSUPPORTED;
-    if ((flags & ~(GDN_F_NORM_QK | GDN_F_OUT_BF16 | GDN_F_VALU)) != 0) return GDN_ERR_ARG;
+    if ((flags & ~(GDN_F_NORM_QK | GDN_F_OUT_BF16 | GDN_F_VALU | GDN_F_RAW_GATES)) != 0) return GDN_ERR_ARG;
+    if (check_gates(flags, gate_params) != GDN_OK) return GDN_ERR_ARG;
     if (row_stride_qk < static_cast<int64_t>(Hqk) * dk || row_stride_v < static_cast<int64_t>(Hv) * dv ||
         row_stride_qk_prev < static_cast<int64_t>(Hqk) * dk ||
         row_stride_v_prev < static_cast<int64_t>(Hv) * dv)
@@ -221,7 +235,7 @@ int32_t gdn_tree_commit_verify(const gdn_tree_desc* d, const void* q, const void
     if (!aligned(state_pool, 16)) return GDN_ERR_ARG;
     gdn::CommitVerifyArgs a{};
     a.verify = gdn::VerifyArgs{q, k, v, row_stride_qk, row_stride_v, alpha, beta, state_pool, P,
-                               state_idx, out, Hqk, Hv, dk, dtype, flags, err};
+                               state_idx, out, Hqk, Hv, dk, dtype, flags, err, gate_params};
     a.pool = state_pool;
     a.prev = d_prev;
     a.path_rows = path_rows;
@@ -268,7 +282,8 @@ int32_t gdn_layer_step(const gdn_tree_desc* d, const void* x, const void* w, con
                        void* out, void* y, const gdn_tree_desc* d_prev, const void* x_prev,
                        const float* alpha_prev, const float* beta_prev, const int32_t* path_rows,
                        const int32_t* path_n, int32_t Lmax, int32_t Hqk, int32_t Hv, int32_t dk,
-                       int32_t dv, int32_t flags, int32_t* err, void* stream) {
+                       int32_t dv, int32_t flags, const float* gate_params, int32_t* err,
+                       void* stream) {
     int32_t st = check_desc(d);
     if (st != GDN_OK) return st;
     st = check_desc(d_prev);
@@ -282,7 +297,8 @@ int32_t gdn_layer_step(const gdn_tree_desc* d, const void* x, const void* w, con
         return GDN_ERR_ARG;
     if (Lmax < 1 || Lmax > GDN_MAX_NODES) return GDN_ERR_UNSUPPORTED;
     if (act != GDN_ACT_NONE && act != GDN_ACT_SILU) return GDN_ERR_ARG;
-    if ((flags & ~(GDN_F_NORM_QK | GDN_F_OUT_BF16)) != 0) return GDN_ERR_ARG;
+    if ((flags & ~(GDN_F_NORM_QK | GDN_F_OUT_BF16 | GDN_F_RAW_GATES)) != 0) return GDN_ERR_ARG;
+    if (check_gates(flags, gate_params) != GDN_OK) return GDN_ERR_ARG;
     const int64_t C = 2 * static_cast<int64_t>(Hqk) * dk + static_cast<int64_t>(Hv) * dv;
     if (d->W > 1) {
         if (!hist_in || !hist_out) return GDN_ERR_ARG;
@@ -324,6 +340,7 @@ int32_t gdn_layer_step(const gdn_tree_desc* d, const void* x, const void* w, con
     a.Hv = Hv;
     a.flags = flags;
     a.err = err;
+    a.gate_params = gate_params;
     return map_launch(gdn::launch_layer_step(*d, a, static_cast<hipStream_t>(stream)));
 }
 

@@ -35,6 +35,30 @@ __device__ __forceinline__ float load_elem<float>(const float* p) {
     return *p;
 }
 
+// Gates from raw inputs (GDN_F_RAW_GATES; LumoTree, Sec. IV-B: the verifier
+// takes raw gate inputs and evaluates the gates itself).  Per value head the
+// parameters A_log and dt_bias, per node the raw inputs a and b:
+//   alpha = exp(-exp(A_log) * softplus(a + dt_bias)),  beta = 1 / (1 + exp(-b)),
+// softplus(x) = max(x, 0) + log(1 + exp(-|x|)) (no overflow for any x), on
+// the hardware exp2 / log2 / reciprocal (about 1 ulp each; the log of
+// 1 + e loses e below 2^-24, an absolute error under 6e-8 in softplus).
+struct RawGate {
+    float A2;   // exp(A_log) * log2(e)
+    float dtb;  // dt_bias
+};
+__device__ __forceinline__ RawGate raw_gate_params(float A_log, float dt_bias) {
+    return RawGate{__builtin_amdgcn_exp2f(A_log * 1.4426950408889634f) * 1.4426950408889634f, dt_bias};
+}
+__device__ __forceinline__ float raw_gate_alpha(float a, RawGate g) {
+    const float x = a + g.dtb;
+    const float e = __builtin_amdgcn_exp2f(fabsf(x) * -1.4426950408889634f);  // exp(-|x|) in (0, 1]
+    const float sp = fmaxf(x, 0.0f) + __builtin_amdgcn_logf(1.0f + e) * 0.6931471805599453f;
+    return __builtin_amdgcn_exp2f(-g.A2 * sp);
+}
+__device__ __forceinline__ float raw_gate_beta(float b) {
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(b * -1.4426950408889634f));
+}
+
 // Make a wave-uniform value scalar (all lanes hold the same value).
 __device__ __forceinline__ uint32_t uniform_u32(uint32_t x) {
     return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(x)));
@@ -79,6 +103,7 @@ struct VerifyArgs {
     int Hqk, Hv, D;
     int dtype, flags;
     int32_t* err;
+    const float* gate_params = nullptr;  // [2][Hv] A_log, dt_bias with GDN_F_RAW_GATES
 };
 // Returns hipErrorNotSupported (without launching) when no kernel covers the
 // shape; the API maps that to GDN_ERR_UNSUPPORTED.
@@ -109,6 +134,7 @@ struct CommitArgs {
     // element strides from the first layer's (layers = 1: one layer)
     int layers = 1;
     int64_t ls_qk = 0, ls_v = 0, ls_gate = 0, ls_pool = 0;
+    const float* gate_params = nullptr;  // [layers][2][Hv] with GDN_F_RAW_GATES
 };
 hipError_t launch_commit(const gdn_tree_desc& d, const CommitArgs& a, hipStream_t s);
 size_t commit_lds_bytes(int Lmax, int D, int dtype);
@@ -156,6 +182,7 @@ struct LayerArgs {
     int Lmax;
     int Hqk, Hv, flags;
     int32_t* err;
+    const float* gate_params = nullptr;  // [2][Hv] with GDN_F_RAW_GATES
 };
 hipError_t launch_layer_step(const gdn_tree_desc& d, const LayerArgs& a, hipStream_t s);
 

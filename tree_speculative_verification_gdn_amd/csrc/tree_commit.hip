@@ -156,7 +156,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
                   float* __restrict__ pool, int P, const int32_t* __restrict__ state_idx,
                   const uint16_t* __restrict__ x, uint16_t* __restrict__ hist, int C, int hvec,
                   int Hqk, int Hv, int norm, int32_t* __restrict__ err, int64_t ls_qk, int64_t ls_v,
-                  int64_t ls_gate, int64_t ls_pool) {
+                  int64_t ls_gate, int64_t ls_pool, const float* __restrict__ gate_params) {
     constexpr int TPR = kThreads / D;             // lanes per value row
     constexpr int EPT = D / TPR;                  // state elements per lane
     constexpr int CW = EPT >= 8 ? 8 : EPT;        // columns per chunk
@@ -186,6 +186,15 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
     alpha += layer * ls_gate;
     beta += layer * ls_gate;
     pool += layer * ls_pool;
+    // raw gate inputs: the head's parameters, loaded with the first round
+    // trip and used when the gates are staged
+    const bool raw = gate_params != nullptr;  // uniform
+    float g_alog = 0.0f, g_dtb = 0.0f;
+    if (raw) {
+        const float* gp = gate_params + layer * 2 * Hv;
+        g_alog = gp[h];
+        g_dtb = gp[Hv + h];
+    }
     const int t = shared ? 0 : b;
     const int tid = threadIdx.x;
     const int r = tid / TPR;
@@ -296,8 +305,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
     // stage gates, k (input type, per-row scale) and v in LDS; every lane
     // stores (past the end into a spare entry) so that no load above is sunk
     // into a branch behind the state loads
-    s_al[tid < len ? tid : Lmax] = my_al;
-    s_be[tid < len ? tid : Lmax] = my_be;
+    if (raw) {  // uniform
+        const RawGate rg = raw_gate_params(g_alog, g_dtb);
+        s_al[tid < len ? tid : Lmax] = raw_gate_alpha(my_al, rg);
+        s_be[tid < len ? tid : Lmax] = raw_gate_beta(my_be);
+    } else {
+        s_al[tid < len ? tid : Lmax] = my_al;
+        s_be[tid < len ? tid : Lmax] = my_be;
+    }
     for (int it0 = 0; it0 < chunks; it0 += 2 * kThreads) {
         if (it0 > 0) {  // paths longer than 2 * kThreads / CPR rows (rare)
 #pragma unroll
@@ -422,7 +437,8 @@ hipError_t launch_commit_t(const gdn_tree_desc& d, const CommitArgs& a, int norm
                        d.node_row, d.status, a.path, a.path_len, a.Lmax,
                        static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.rs_qk, a.rs_v,
                        a.alpha, a.beta, a.pool, a.P, a.state_idx, a.x, a.hist, a.C, hvec, a.Hqk,
-                       a.Hv, norm, a.err, a.ls_qk, a.ls_v, a.ls_gate, a.ls_pool);
+                       a.Hv, norm, a.err, a.ls_qk, a.ls_v, a.ls_gate, a.ls_pool,
+                       (a.flags & GDN_F_RAW_GATES) ? a.gate_params : nullptr);
     return hipGetLastError();
 }
 

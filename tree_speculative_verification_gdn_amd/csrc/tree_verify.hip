@@ -326,7 +326,7 @@ __device__ __forceinline__ bf16x8_t lds_operand_m(const char* base, int stride, 
     return __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
-template <int NPB, int MODE, int CW>
+template <int NPB, int MODE, int CW, bool RAW>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NPB == 1 ? 4 : 2, 8)))
     verify_mfma_kernel(int N, int R, int shared, const int32_t* __restrict__ node_row,
                        const uint64_t* __restrict__ anc_g, const int32_t* __restrict__ depth_g,
@@ -336,7 +336,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                        const float* __restrict__ beta, float* __restrict__ pool, int P,
                        const int32_t* __restrict__ state_idx, void* __restrict__ out, int Hqk,
                        int Hv, int norm, int out_bf16, int32_t* __restrict__ err,
-                       const CommitPrev cp, const LayerIn li) {
+                       const float* __restrict__ gate_params, const CommitPrev cp, const LayerIn li) {
     constexpr bool FUSED = MODE == kModeCommitVerify;  // commit of a path given as k/v rows
     constexpr bool LAYER = MODE == kModeLayer || MODE == kModeLayerLong;  // the whole layer step
     constexpr bool LONGP = MODE == kModeLayerLong;
@@ -411,6 +411,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     const int my_row = node_row[tb + my_node];
     const uint64_t my_anc = anc_g[tb + my_node];
     const int my_dep = depth_g[tb + my_node];
+    //   raw gate inputs: the head's gate parameters (used when the gates are
+    //   staged)
+    float g_alog = 0.0f, g_dtb = 0.0f;
+    if constexpr (RAW) {
+        g_alog = gate_params[h];
+        g_dtb = gate_params[Hv + h];
+    }
     //   (a1') the previous step's accepted path, resolved to its node count
     //   (-1: neither state nor history is written) and physical rows
     const int LmaxP = LAYER ? li.Lmax : (FUSED ? cp.Lmax : 1);
@@ -601,8 +608,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
         const int c4 = tid & 31;
         if (nc > 0) {  // uniform
             // the path's gates (nc <= Lmax <= 64: wave 0; spare entry Lmax)
-            s_alp[min(tid, li.Lmax)] = p_al;
-            s_bep[min(tid, li.Lmax)] = p_be;
+            if constexpr (RAW) {
+                s_alp[min(tid, li.Lmax)] = raw_gate_alpha(p_al, raw_gate_params(g_alog, g_dtb));
+                s_bep[min(tid, li.Lmax)] = raw_gate_beta(p_be);
+            } else {
+                s_alp[min(tid, li.Lmax)] = p_al;
+                s_bep[min(tid, li.Lmax)] = p_be;
+            }
             uint4* s_pc = reinterpret_cast<uint4*>(lds + L.pc);  // [H + 8][32]: k half, v half
 #pragma unroll
             for (int u = 0; u < kPItems; ++u) {
@@ -613,8 +625,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
         if (vok) {  // uniform
             {
                 const int slot_i = tid < N ? tid : N;  // lanes past N write the spare entry
-                s_al[slot_i] = my_al;
-                s_be[slot_i] = my_be;
+                if constexpr (RAW) {
+                    s_al[slot_i] = raw_gate_alpha(my_al, raw_gate_params(g_alog, g_dtb));
+                    s_be[slot_i] = raw_gate_beta(my_be);
+                } else {
+                    s_al[slot_i] = my_al;
+                    s_be[slot_i] = my_be;
+                }
             }
 #pragma unroll
             for (int u = 0; u < kSlots; ++u) {
@@ -768,8 +785,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
             s_rows[slot_i] = my_row;
             s_anc[slot_i] = my_anc;
             s_dep[slot_i] = my_dep;
-            s_al[slot_i] = my_al;
-            s_be[slot_i] = my_be;
+            if constexpr (RAW) {
+                s_al[slot_i] = raw_gate_alpha(my_al, raw_gate_params(g_alog, g_dtb));
+                s_be[slot_i] = raw_gate_beta(my_be);
+            } else {
+                s_al[slot_i] = my_al;
+                s_be[slot_i] = my_be;
+            }
         }
         // M halves start as zero (entries off the ancestor pattern stay zero)
         for (int e = tid; e < NP * mstride / 4; e += kThreads) {
@@ -986,8 +1008,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                 }
             }
             if (tid < nc) {
-                s_alp[tid] = p_al;
-                s_bep[tid] = p_be;
+                if constexpr (RAW) {
+                    s_alp[tid] = raw_gate_alpha(p_al, raw_gate_params(g_alog, g_dtb));
+                    s_bep[tid] = raw_gate_beta(p_be);
+                } else {
+                    s_alp[tid] = p_al;
+                    s_bep[tid] = p_be;
+                }
             }
           } else {
             // the first segment's k/v rows (their conv ran with the tree's)
@@ -1299,7 +1326,8 @@ __global__ void __launch_bounds__(kThreads)
                        int64_t rs_qk, int64_t rs_v, const float* __restrict__ alpha,
                        const float* __restrict__ beta, const float* __restrict__ pool, int P,
                        const int32_t* __restrict__ state_idx, void* __restrict__ out, int Hqk,
-                       int Hv, int norm, int out_bf16, int32_t* __restrict__ err) {
+                       int Hv, int norm, int out_bf16, int32_t* __restrict__ err,
+                       const float* __restrict__ gate_params) {
     constexpr int TPR = kThreads / D;  // lanes per value row
     constexpr int EPT = D / TPR;       // state elements per lane
     constexpr int NQ = EPT / 4;        // float4 chunks per lane
@@ -1345,8 +1373,13 @@ __global__ void __launch_bounds__(kThreads)
         s_rows[tid] = row;
         s_anc[tid] = anc_g[tb + tid];
         const size_t gi = (static_cast<size_t>(b) * R + row) * Hv + h;
-        s_al[tid] = alpha[gi];
-        s_be[tid] = beta[gi];
+        if (gate_params) {  // uniform: raw gate inputs
+            s_al[tid] = raw_gate_alpha(alpha[gi], raw_gate_params(gate_params[h], gate_params[Hv + h]));
+            s_be[tid] = raw_gate_beta(beta[gi]);
+        } else {
+            s_al[tid] = alpha[gi];
+            s_be[tid] = beta[gi];
+        }
     }
     __syncthreads();
     for (int e = tid; e < N * D; e += kThreads) {
@@ -1449,11 +1482,11 @@ hipError_t set_lds(K kernel, size_t bytes) {
                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
 }
 
-template <int NPB, int MODE, int CW = 0>
-hipError_t launch_mfma_t(const gdn_tree_desc& d, const VerifyArgs& a, float* pool, int norm,
-                         int obf, size_t lds, const CommitPrev& cp, hipStream_t s,
-                         const LayerIn& li = LayerIn{}) {
-    auto kfn = verify_mfma_kernel<NPB, MODE, CW>;
+template <int NPB, int MODE, int CW, bool RAW>
+hipError_t launch_mfma_raw(const gdn_tree_desc& d, const VerifyArgs& a, float* pool, int norm,
+                           int obf, size_t lds, const CommitPrev& cp, hipStream_t s,
+                           const LayerIn& li) {
+    auto kfn = verify_mfma_kernel<NPB, MODE, CW, RAW>;
     hipError_t e = set_lds(kfn, lds);
     if (e != hipSuccess) return e;
     const dim3 grid(static_cast<unsigned>(d.B) * static_cast<unsigned>(a.Hv));
@@ -1461,8 +1494,19 @@ hipError_t launch_mfma_t(const gdn_tree_desc& d, const VerifyArgs& a, float* poo
                        d.depth, d.status, static_cast<const uint16_t*>(a.q),
                        static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                        a.rs_qk, a.rs_v, a.alpha, a.beta, pool, a.P, a.state_idx, a.out, a.Hqk,
-                       a.Hv, norm, obf, a.err, cp, li);
+                       a.Hv, norm, obf, a.err, a.gate_params, cp, li);
     return hipGetLastError();
+}
+
+// raw gate inputs select their own instantiation, so the plain kernels keep
+// their register allocation
+template <int NPB, int MODE, int CW = 0>
+hipError_t launch_mfma_t(const gdn_tree_desc& d, const VerifyArgs& a, float* pool, int norm,
+                         int obf, size_t lds, const CommitPrev& cp, hipStream_t s,
+                         const LayerIn& li = LayerIn{}) {
+    if (a.flags & GDN_F_RAW_GATES)
+        return launch_mfma_raw<NPB, MODE, CW, true>(d, a, pool, norm, obf, lds, cp, s, li);
+    return launch_mfma_raw<NPB, MODE, CW, false>(d, a, pool, norm, obf, lds, cp, s, li);
 }
 
 template <int D, typename T>
@@ -1475,7 +1519,8 @@ hipError_t launch_valu_t(const gdn_tree_desc& d, const VerifyArgs& a, int norm, 
     hipLaunchKernelGGL(kfn, grid, dim3(kThreads), lds, s, d.N, d.R, d.shared, d.node_row, d.anc,
                        d.status, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.rs_qk, a.rs_v, a.alpha, a.beta, a.pool, a.P,
-                       a.state_idx, a.out, a.Hqk, a.Hv, norm, obf, a.err);
+                       a.state_idx, a.out, a.Hqk, a.Hv, norm, obf, a.err,
+                       (a.flags & GDN_F_RAW_GATES) ? a.gate_params : nullptr);
     return hipGetLastError();
 }
 }  // namespace
@@ -1555,7 +1600,8 @@ hipError_t launch_commit_verify(const gdn_tree_desc& d, const CommitVerifyArgs& 
     // other shapes: the commit, then the verify (the same result in two launches)
     CommitArgs ca{a.path_rows, a.path_n, a.Lmax, a.k_prev, a.v_prev, a.rs_qk_prev, a.rs_v_prev,
                   a.alpha_prev, a.beta_prev, a.pool, va.P, va.state_idx, nullptr, nullptr, 0,
-                  va.Hqk, va.Hv, va.D, va.dtype, va.flags & GDN_F_NORM_QK, va.err, 1};
+                  va.Hqk, va.Hv, va.D, va.dtype, va.flags & (GDN_F_NORM_QK | GDN_F_RAW_GATES), va.err, 1};
+    ca.gate_params = va.gate_params;
     hipError_t e = launch_commit(dp, ca, s);
     if (e != hipSuccess) return e;
     return launch_verify(d, va, s);
@@ -1583,7 +1629,7 @@ hipError_t launch_layer_step(const gdn_tree_desc& d, const LayerArgs& a, hipStre
     li.path_n = a.path_n;
     li.parent = d.parent;
     const VerifyArgs va{nullptr, nullptr, nullptr, 0, 0, a.alpha, a.beta, a.pool, a.P, a.state_idx,
-                        a.out, a.Hqk, a.Hv, kD, GDN_DT_BF16, a.flags, a.err};
+                        a.out, a.Hqk, a.Hv, kD, GDN_DT_BF16, a.flags, a.err, a.gate_params};
     const int norm = (a.flags & GDN_F_NORM_QK) ? 1 : 0;
     const int obf = (a.flags & GDN_F_OUT_BF16) ? 1 : 0;
     const CommitPrev none{};
