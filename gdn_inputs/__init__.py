@@ -29,6 +29,7 @@ BF16_NAN = np.uint16(0x7FC0)
 _S_ROWS, _S_Q, _S_K, _S_V, _S_A, _S_B, _S_POOL, _S_IDX, _S_PATH = range(1, 10)
 _S_X, _S_HIST, _S_W = 10, 11, 12
 _S_RAW_A, _S_RAW_B, _S_GATE_P = 13, 14, 15
+_S_BIAS = 16
 _S_TREE0 = 1_000_000  # + request index
 
 
@@ -322,3 +323,13 @@ def with_raw_gates(case: dict, gate_params: np.ndarray | None = None) -> dict:
     out = dict(case)
     out.update(alpha=a, beta=b, gate_params=np.asarray(gate_params, np.float32))
     return out
+
+
+def conv_bias(cfg: Config, seed: int, layer: int = 0, dyadic: bool = False) -> np.ndarray:
+    """A conv bias float32 [C] for the layer: N(0, 0.1^2), or with ``dyadic``
+    multiples of 1/64 up to 1/4 in magnitude (exact in every fp32 tap sum,
+    like the dyadic conv inputs)."""
+    g = rng(seed, cfg.cfg_id, layer, _S_BIAS)
+    if dyadic:
+        return (g.integers(-16, 17, cfg.conv_C) / 64.0).astype(np.float32)
+    return (g.standard_normal(cfg.conv_C) * 0.1).astype(np.float32)

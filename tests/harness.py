@@ -109,7 +109,7 @@ def run_gpu(case, flags=0, commit=True, shared=False, out_bf16=False, raise_on_e
         hist = to_dev(case["hist"])
         w = to_dev(case["w"])
         y = torch.full((B, R, C), float("nan"), dtype=torch.bfloat16, device="cuda")
-        res["rc_conv"] = g.conv_ancestry_gather(desc, x, hist, sidx, w, None, y, cfg.act, err,
+        res["rc_conv"] = g.conv_ancestry_gather(desc, x, hist, sidx, w, dev_bias(case), y, cfg.act, err,
                                                 raise_on_error=raise_on_error)
         if y_override is not None:
             res["y_own"] = bits(y)
@@ -156,7 +156,7 @@ def run_oracle(case, commit=True, shared=False):
     res = dict(err=d["err"], depth=d["depth"], anc=d["anc"], conv_src=d["conv_src"], status=d["status"])
     if cfg.conv_W > 0:
         y, e = oracle.conv(rows, d["conv_src"], d["status"], case["x"], case["hist"], case["state_idx"],
-                           case["w"], None, cfg.act, R, cfg.conv_C, W, shared=shared)
+                           case["w"], case.get("bias"), cfg.act, R, cfg.conv_C, W, shared=shared)
         res["err"] |= e
         ybits = oracle.round_f64_to_bf16_bits(y)
         ybits = np.where(np.isnan(y), NAN_BF16, ybits).astype(np.uint16)
@@ -192,6 +192,10 @@ def oracle_gates(case):
     if "gate_params" in case:
         return oracle_gate_eval(case["alpha"], case["beta"], case["gate_params"])
     return case["alpha"], case["beta"]
+
+
+def dev_bias(case):
+    return to_dev(case["bias"]) if "bias" in case else None
 
 
 def dev_gate_params(case):
@@ -261,7 +265,7 @@ def two_step_case(cfg, seed, B=None, extra_slots=0, packing="perm", conv_values=
                       conv_values=conv_values)
     # the pool, the history and the conv weights belong to the layer: the
     # same at both steps
-    for key in ("pool", "state_idx", "P", "hist", "w"):
+    for key in ("pool", "state_idx", "P", "hist", "w", "bias"):
         if key in c1:
             c2[key] = c1[key]
     return c1, c2
@@ -288,7 +292,7 @@ def run_oracle_two_steps(c1, c2):
     norm = cfg.norm_qk if cfg.conv_W > 0 else False
     if cfg.conv_W > 0:
         y1, e = oracle.conv(c1["node_row"], d1["conv_src"], d1["status"], c1["x"], c1["hist"],
-                            c1["state_idx"], c1["w"], None, cfg.act, R, cfg.conv_C, W)
+                            c1["state_idx"], c1["w"], c1.get("bias"), cfg.act, R, cfg.conv_C, W)
         res["err"] |= e
         y1b = np.where(np.isnan(y1), NAN_BF16, oracle.round_f64_to_bf16_bits(y1)).astype(np.uint16)
         q1, k1, v1 = _qkv_of(cfg, B, y1b)
@@ -306,7 +310,7 @@ def run_oracle_two_steps(c1, c2):
         res["hist"] = hist
         hbits = oracle.round_f64_to_bf16_bits(hist)
         y2, e = oracle.conv(c2["node_row"], d2["conv_src"], d2["status"], c2["x"], hbits,
-                            c2["state_idx"], c2["w"], None, cfg.act, R, cfg.conv_C, W)
+                            c2["state_idx"], c2["w"], c2.get("bias"), cfg.act, R, cfg.conv_C, W)
         res["err"] |= e
         y2b = np.where(np.isnan(y2), NAN_BF16, oracle.round_f64_to_bf16_bits(y2)).astype(np.uint16)
         q2, k2, v2 = _qkv_of(cfg, B, y2b)
@@ -358,7 +362,8 @@ def run_gpu_two_steps(c1, c2, fused=True, y1_override=None, y2_override=None, fl
         w1, w2 = to_dev(c1["w"]), to_dev(c2["w"])
         x1, x2 = to_dev(c1["x"]), to_dev(c2["x"])
         y1 = torch.full((B, R, C), float("nan"), dtype=torch.bfloat16, device="cuda")
-        g.conv_ancestry_gather(d1, x1, hist, sidx, w1, None, y1, cfg.act, err)
+        bias = dev_bias(c1)  # the layer's (both steps)
+        g.conv_ancestry_gather(d1, x1, hist, sidx, w1, bias, y1, cfg.act, err)
         res["y1"] = bits(y1)
         if y1_override is not None:
             y1.copy_(to_dev(np.where(y1_override == NAN_BF16, res["y1"], y1_override).astype(np.uint16)))
@@ -367,12 +372,12 @@ def run_gpu_two_steps(c1, c2, fused=True, y1_override=None, y2_override=None, fl
         v1 = y1[:, :, 2 * Hqk * D:].unflatten(-1, (Hv, D))
         y2 = torch.full((B, R, C), float("nan"), dtype=torch.bfloat16, device="cuda")
         if fused:
-            g.conv_ancestry_gather_publish(d2, x2, hist, sidx, w2, None, y2, cfg.act, d1, prow, pn,
+            g.conv_ancestry_gather_publish(d2, x2, hist, sidx, w2, bias, y2, cfg.act, d1, prow, pn,
                                            x1, err)
         else:
             g.gdn_tree_commit(d1, p1, l1, k1, v1, a1, b1, pool, sidx, err, Hqk=Hqk,
                               flags=flags & g.GDN_F_NORM_QK, x=x1, hist=hist, gate_params=gp)
-            g.conv_ancestry_gather(d2, x2, hist, sidx, w2, None, y2, cfg.act, err)
+            g.conv_ancestry_gather(d2, x2, hist, sidx, w2, bias, y2, cfg.act, err)
         res["y2"] = bits(y2)
         if y2_override is not None:
             y2.copy_(to_dev(np.where(y2_override == NAN_BF16, res["y2"], y2_override).astype(np.uint16)))
@@ -431,7 +436,7 @@ def run_gpu_layer(c1, c2, flags=0, with_y=True, prepare=False):
     out = torch.full((B, R, Hv, D), float("nan"), dtype=torch.float32, device="cuda")
     y = torch.full((B, R, C), float("nan"), dtype=torch.bfloat16, device="cuda") if with_y else None
     flags |= g.GDN_F_NORM_QK if cfg.norm_qk else 0
-    g.gdn_layer_step(d2, to_dev(c2["x"]), to_dev(c2["w"]), None, cfg.act, hist_in, hist_out,
+    g.gdn_layer_step(d2, to_dev(c2["x"]), to_dev(c2["w"]), dev_bias(c1), cfg.act, hist_in, hist_out,
                      to_dev(c2["alpha"]), to_dev(c2["beta"]), pool, sidx, out, d1, to_dev(c1["x"]),
                      to_dev(c1["alpha"]), to_dev(c1["beta"]), path_rows, path_n, err, Hqk,
                      flags=flags, y=y, gate_params=dev_gate_params(c1))

@@ -212,3 +212,18 @@ def test_layer_step_full_size_sampled():
     s1c = dict(s1)
     s1c["state_idx"] = np.arange(len(bs), dtype=np.int32)
     _cmp(s1c, s2, g1, orr)
+
+
+def test_layer_step_with_bias_matches_oracle_and_separate_calls():
+    # a conv bias (dyadic: the conv stays exact); the layer step, the fused
+    # calls and the oracle agree
+    cfg = _exact(gi.CONFIGS[4])
+    c1, c2 = two_step_case(cfg, seed=808, B=5, extra_slots=1, conv_values="dyadic")
+    c1["bias"] = c2["bias"] = gi.conv_bias(cfg, seed=808, dyadic=True)
+    gr = run_gpu_layer(c1, c2)
+    orr = run_oracle_two_steps(c1, c2)
+    _cmp(c1, c2, gr, orr)
+    gf = run_gpu_two_steps(c1, c2)
+    m = node_rows_mask(c2)
+    assert np.array_equal(gf["y2"][m], orr["y2"][m])
+    assert max_rel_rows(gf["out"][m], orr["out"][m], 2) <= TOL

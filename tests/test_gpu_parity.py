@@ -335,3 +335,40 @@ def test_tree64_b256_two_layers_sampled():
         m = node_rows_mask(sub)
         assert max_rel_rows(gr["out"][bs][m], orr["out"][m], 2) <= TOL
         assert max_rel_rows(gr["pool"][case["state_idx"][bs]], orr["pool"], 2) <= TOL
+
+
+@pytest.mark.parametrize("N,R,C,act,with_bias", [(27, 32, 1024, 0, False), (27, 40, 1024, 0, True),
+                                                 (27, 32, 1028, 0, True), (40, 48, 1024, 0, False),
+                                                 (40, 70, 1024, 1, True), (64, 64, 512, 1, False)])
+def test_conv_row_layouts(N, R, C, act, with_bias):
+    # row counts and padding of one and two passes of rows, 8- and 4-channel
+    # accesses (C = 1028), with and without the activation and the bias
+    import torch
+    g = _g()
+    from harness import bits, to_dev
+    import oracle
+    cfg = gi.CONFIGS[4].replace(N=N, R=R, conv_C=C, act=act, B=5, bmax=4, depth_max=8)
+    case = gi.make_case(cfg, seed=N + R + C, extra_slots=1, conv_values="dyadic" if act == 0 else "normal")
+    W = cfg.conv_W
+    desc = g.TreeDesc(to_dev(case["parent"]), to_dev(case["node_row"]), R, W)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    g.gdn_tree_desc_build(desc, err)
+    y = torch.full((case["B"], R, C), float("nan"), dtype=torch.bfloat16, device="cuda")
+    hist = to_dev(case["hist"])
+    bias = gi.conv_bias(cfg, seed=N, dyadic=act == 0) if with_bias else None
+    g.conv_ancestry_gather(desc, to_dev(case["x"]), hist, to_dev(case["state_idx"]), to_dev(case["w"]),
+                           None if bias is None else to_dev(bias), y, act, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    d = oracle.desc_build(case["parent"], case["node_row"], R, W)
+    yo, e = oracle.conv(case["node_row"], d["conv_src"], d["status"], case["x"], case["hist"],
+                        case["state_idx"], case["w"], bias, act, R, C, W)
+    assert e == 0
+    yb = bits(y)
+    m = node_rows_mask(case)
+    ob = oracle.round_f64_to_bf16_bits(yo)
+    if act == 0:
+        assert np.array_equal(yb[m], ob[m])
+    else:
+        assert (bf16_ulp_diff(yb[m], ob[m]) <= 1).all()
+    assert (yb[~m] == 0x7FC0).all()

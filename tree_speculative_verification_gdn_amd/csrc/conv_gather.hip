@@ -14,6 +14,8 @@
 // tile, the W-1 history entries and the weights, all in flight together.
 // Node rows are kept in LDS, so an x element is read from HBM once however
 // many descendants tap it.  HBM-bound: x (node rows), hist, y.
+#include <type_traits>
+
 #include "conv_math.h"
 #include "gdn_internal.h"
 
@@ -275,31 +277,48 @@ __global__ void __launch_bounds__(kConvThreads) conv_gather_kernel(const ConvKAr
 #pragma unroll
     for (int e = 0; e < kWW; ++e) wr[e] = s_w[lane * kWW + e];
     constexpr int NW = CPT / 2;  // 32-bit words of a row chunk
-    for (int i = rs; i < N; i += kRowsPerPass) {
-        // the node's window, oldest first: its H taps, then the node itself
-        uint32_t xw[W][NW];
+    float bl[CPT];
 #pragma unroll
-        for (int t = 0; t < W; ++t) {
-            const int row = (t < H) ? s_tap[i * H + t] : i;
-            const Chunk<CPT> ch = s_x[row * kTileLanes + lane];
-            const uint32_t* cw = reinterpret_cast<const uint32_t*>(&ch.u);
+    for (int c = 0; c < CPT; ++c) bl[c] = bias ? s_b[lane * CPT + c] : 0.0f;
+    // one copy of the loop per (bias, activation) pair: both are uniform, and
+    // fixing them outside the loop leaves only the arithmetic they need
+    auto rows = [&](auto with_bias, auto silu) {
+        constexpr bool kBias = decltype(with_bias)::value;
+        constexpr int kAct = decltype(silu)::value ? GDN_ACT_SILU : GDN_ACT_NONE;
+        for (int i = rs; i < N; i += kRowsPerPass) {
+            // the node's window, oldest first: its H taps, then the node itself
+            uint32_t xw[W][NW];
 #pragma unroll
-            for (int q = 0; q < NW; ++q) xw[t][q] = cw[q];
+            for (int t = 0; t < W; ++t) {
+                const int row = (t < H) ? s_tap[i * H + t] : i;
+                const Chunk<CPT> ch = s_x[row * kTileLanes + lane];
+                const uint32_t* cw = reinterpret_cast<const uint32_t*>(&ch.u);
+#pragma unroll
+                for (int q = 0; q < NW; ++q) xw[t][q] = cw[q];
+            }
+            float z[CPT];
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+                uint32_t tw[W];
+#pragma unroll
+                for (int t = 0; t < W; ++t) tw[t] = xw[t][c >> 1];
+                z[c] = conv_channel<W>(tw, c & 1, &wr[c * kWP], kBias, bl[c], kAct);
+            }
+            Chunk<CPT> o;
+            uint32_t* ow = reinterpret_cast<uint32_t*>(&o.u);
+#pragma unroll
+            for (int e = 0; e < CPT / 2; ++e) ow[e] = conv_pack_bf16x2(z[2 * e], z[2 * e + 1]);
+            *reinterpret_cast<decltype(o.u)*>(y + (xb + s_row[i]) * C + c0) = o.u;
         }
-        float z[CPT];
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            uint32_t tw[W];
-#pragma unroll
-            for (int t = 0; t < W; ++t) tw[t] = xw[t][c >> 1];
-            z[c] = conv_channel<W>(tw, c & 1, &wr[c * kWP], bias != nullptr,
-                                   bias ? s_b[lane * CPT + c] : 0.0f, act);
-        }
-        Chunk<CPT> o;
-        uint32_t* ow = reinterpret_cast<uint32_t*>(&o.u);
-#pragma unroll
-        for (int e = 0; e < CPT / 2; ++e) ow[e] = conv_pack_bf16x2(z[2 * e], z[2 * e + 1]);
-        *reinterpret_cast<decltype(o.u)*>(y + (xb + s_row[i]) * C + c0) = o.u;
+    };
+    using yes = std::integral_constant<bool, true>;
+    using no = std::integral_constant<bool, false>;
+    if (act == GDN_ACT_SILU) {
+        if (bias) rows(yes{}, yes{});
+        else rows(no{}, yes{});
+    } else {
+        if (bias) rows(yes{}, no{});
+        else rows(no{}, no{});
     }
 }
 

@@ -34,14 +34,15 @@ __device__ __forceinline__ uint32_t conv_pack_bf16x2(float a, float b) {
 // One output channel.  xw[t] is the 32-bit word holding this channel (low
 // half when hi == 0, high half when hi == 1) and its neighbour in tap t,
 // oldest first, the node itself last (t = W - 1).  wp[p] holds the channel's
-// weights (w[2p], w[2p+1] or 0) as a bf16 pair.  Taps go in pairs through
-// v_dot2_f32_bf16 (exact bf16 products, fp32 sums), then bias, activation.
+// weights (w[2p], w[2p+1] or 0) as a bf16 pair.  The sum starts from the
+// bias (0 without one); taps go in pairs through v_dot2_f32_bf16 (exact bf16
+// products, fp32 sums), then the activation.
 template <int W>
 __device__ __forceinline__ float conv_channel(const uint32_t (&xw)[W], int hi, const uint32_t* wp,
                                               bool has_bias, float bias, int act) {
     constexpr int kWP = (W + 1) / 2;
     const uint32_t sel = hi ? 0x07060302u : 0x05040100u;  // halves hi of two words
-    float acc = 0.0f;
+    float acc = has_bias ? bias : 0.0f;
 #pragma unroll
     for (int p = 0; p < kWP; ++p) {
         const uint32_t lo_w = xw[2 * p];
@@ -50,7 +51,6 @@ __device__ __forceinline__ float conv_channel(const uint32_t (&xw)[W], int hi, c
         acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(conv_bf16x2_t, xp),
                                               __builtin_bit_cast(conv_bf16x2_t, wp[p]), acc, false);
     }
-    if (has_bias) acc += bias;
     if (act == GDN_ACT_SILU) acc = conv_silu(acc);
     return acc;
 }
