@@ -30,6 +30,8 @@ _S_ROWS, _S_Q, _S_K, _S_V, _S_A, _S_B, _S_POOL, _S_IDX, _S_PATH = range(1, 10)
 _S_X, _S_HIST, _S_W = 10, 11, 12
 _S_RAW_A, _S_RAW_B, _S_GATE_P = 13, 14, 15
 _S_BIAS = 16
+_S_ATT_Q, _S_ATT_K, _S_ATT_V, _S_ATT_ROWS = 17, 18, 19, 20
+ATTN_CFG = 100  # generator id of the attention inputs
 _S_TREE0 = 1_000_000  # + request index
 
 
@@ -333,3 +335,41 @@ def conv_bias(cfg: Config, seed: int, layer: int = 0, dyadic: bool = False) -> n
     if dyadic:
         return (g.integers(-16, 17, cfg.conv_C) / 64.0).astype(np.float32)
     return (g.standard_normal(cfg.conv_C) * 0.1).astype(np.float32)
+
+
+def make_attention_case(seed: int, B: int, N: int, R: int, Hq: int, Hkv: int, D: int, ctx, S: int,
+                        bmax: int = 3, depth_max: int = 6, packing: str = "perm",
+                        poison: bool = True, shared: bool = False) -> dict:
+    """Inputs of one tree-attention layer: B trees of N nodes (the random-tree
+    rule above) with physical rows in [0, R) (a seeded injective map, or
+    breadth-first); q [B][N][Hq][D] and the KV cache k, v [B][S][Hkv][D] as
+    bf16 bit patterns of N(0, 1) values; ctx [B] committed prefix lengths.
+    With ``poison`` the cache positions past ctx + R and the candidate rows no
+    node occupies hold NaN (nothing may read them).  With ``shared`` every
+    request has request 0's tree and rows."""
+    ctx = np.asarray(ctx, np.int32)
+    parents = np.stack([random_tree(rng(seed, ATTN_CFG, 0 if shared else b, _S_TREE0), N, bmax, depth_max)
+                        for b in range(B)]).astype(np.int32)
+    g_rows = rng(seed, ATTN_CFG, 0, _S_ATT_ROWS)
+    if packing == "bfs":
+        rows = np.stack([bfs_rows(parents[b]) for b in range(B)])
+    else:
+        rows = np.stack([random_rows(g_rows, N, R) for _ in range(B)])
+    if shared:
+        rows = np.repeat(rows[:1], B, axis=0)
+    q = rng(seed, ATTN_CFG, 0, _S_ATT_Q).standard_normal((B, N, Hq, D), dtype=np.float32)
+    k = rng(seed, ATTN_CFG, 0, _S_ATT_K).standard_normal((B, S, Hkv, D), dtype=np.float32)
+    v = rng(seed, ATTN_CFG, 0, _S_ATT_V).standard_normal((B, S, Hkv, D), dtype=np.float32)
+    if poison:
+        for b in range(B):
+            L = int(ctx[b])
+            if L < 0 or L + R > S:
+                continue
+            k[b, L + R:] = np.nan
+            v[b, L + R:] = np.nan
+            unused = np.setdiff1d(np.arange(R), rows[b])
+            k[b, L + unused] = np.nan
+            v[b, L + unused] = np.nan
+    return dict(parent=parents, node_row=rows.astype(np.int32), q=f32_to_bf16_bits(q),
+                k=f32_to_bf16_bits(k), v=f32_to_bf16_bits(v), ctx=ctx, B=B, N=N, R=R, Hq=Hq,
+                Hkv=Hkv, D=D, S=S)

@@ -71,6 +71,7 @@ extern "C" {
 #define GDN_EV_STATE 4  /* state_idx[b] outside [0, P); commit also: shared by two requests */
 #define GDN_EV_PATH 8   /* path_len outside [0, Lmax] or path not a parent chain from a
                            node whose parent is -1 */
+#define GDN_EV_CTX 16   /* tree attention / KV publication: ctx_len[b] outside [0, S - R] */
 
 /* ---- operand dtypes and flags ----------------------------------------- */
 #define GDN_DT_BF16 0 /* q, k, v are bfloat16 */
@@ -376,13 +377,66 @@ int32_t gdn_layer_step(const gdn_tree_desc *d, const void *x, const void *w, con
                        int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv, int32_t flags,
                        const float *gate_params, int32_t *err, void *stream);
 
+/* ---- tree attention (the softmax-attention layers of the same model) -----
+ * LumoTree, Sec. III-C and V-B: query rows stay in logical node order; the
+ * candidates' keys and values are written into the KV cache after the
+ * committed prefix at physical slots given by the descriptor's slot map
+ * (node_row), and the ancestry mask names which of them a node sees -- its
+ * own slot and its ancestors' -- on top of the whole prefix.  Publication
+ * moves the accepted path's entries through the same slot map to the
+ * continuation positions right after the prefix. */
+
+/* Bytes of the workspace gdn_tree_attention needs (split partial results). */
+size_t gdn_tree_attention_workspace_bytes(int32_t B, int32_t N, int32_t Hq, int32_t D,
+                                          int32_t splits);
+
+/* o[b][i][h] = sum_j softmax_j(scale * q[b][i][h] . k_j) v_j over the keys
+ * node i sees: positions 0 .. ctx_len[b]-1 and ctx_len[b] + node_row[a] for
+ * every a on i's root path.  Query head h reads kv head h / (Hq / Hkv).
+ *   q        bf16 [B][N][Hq][D], logical node rows
+ *   k_cache, v_cache  bf16 [B][S][Hkv][D]; the candidates' entries are
+ *            already written at ctx_len[b] + node_row
+ *   ctx_len  int32 [B], each in [0, S - R] (else GDN_EV_CTX, request skipped)
+ *   out      [B][N][Hq][D] float32 (bfloat16 with GDN_F_OUT_BF16); rows of
+ *            skipped requests (malformed tree, bad ctx_len) are not written
+ *   workspace, workspace_bytes: device scratch of at least
+ *            gdn_tree_attention_workspace_bytes(B, N, Hq, D, splits) bytes,
+ *            16-byte aligned, owned by the caller; its contents on entry do
+ *            not matter
+ *   splits   1..1024: partitions of the prefix (each an equal share of
+ *            S - R positions), plus one for the candidates
+ *   scale    softmax scale (e.g. 1 / sqrt(D))
+ * bf16, D in {128, 256}, N <= 64, R <= 64, Hq % Hkv == 0; q, k_cache,
+ * v_cache 16-byte aligned.  flags: GDN_F_OUT_BF16. */
+int32_t gdn_tree_attention(const gdn_tree_desc *d, const void *q, const void *k_cache,
+                           const void *v_cache, int32_t S, const int32_t *ctx_len, void *out,
+                           void *workspace, size_t workspace_bytes, int32_t splits, int32_t Hq,
+                           int32_t Hkv, int32_t D, float scale, int32_t flags, int32_t *err,
+                           void *stream);
+
+/* KV publication of the accepted path: for every request with n_b =
+ * path_n[b] > 0, cache positions ctx_len[b] + j (j < n_b) receive the
+ * entries at ctx_len[b] + path_rows[b][j] (every source is read before any
+ * destination is written), in k_cache and v_cache, all kv heads.
+ *   d_prev   the tree the path was accepted from (its B and R)
+ *   path_rows, path_n, Lmax: the path resolved by gdn_path_resolve or
+ *            gdn_step_prepare (rows are clamped into [0, R) before use)
+ *   k_cache, v_cache, S, ctx_len, Hkv, D: as in gdn_tree_attention
+ * The caller then advances ctx_len by n_b.  ctx_len outside [0, S - R] is
+ * GDN_EV_CTX and leaves the request's cache alone. */
+int32_t gdn_tree_kv_publish(const gdn_tree_desc *d_prev, const int32_t *path_rows,
+                            const int32_t *path_n, int32_t Lmax, void *k_cache, void *v_cache,
+                            int32_t S, const int32_t *ctx_len, int32_t Hkv, int32_t D,
+                            int32_t *err, void *stream);
+
 /* Human-readable name of a return code (host; static string). */
 const char *gdn_status_string(int32_t status);
 
-/* ABI version of this header: 5 (1, plus the two fused-step calls in 2,
+/* ABI version of this header: 6 (1, plus the two fused-step calls in 2,
  * plus gdn_path_resolve, gdn_step_prepare and gdn_layer_step in 3, plus
  * gdn_tree_commit_layers in 4, plus GDN_F_RAW_GATES and the gate_params
- * argument of verify, commit and the fused calls). */
+ * argument of verify, commit and the fused calls in 5, plus tree attention
+ * and KV publication). */
 int32_t gdn_abi_version(void);
 
 #ifdef __cplusplus

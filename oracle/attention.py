@@ -42,13 +42,14 @@ def root_path(parent, i):
 
 
 def tree_attention(parent, node_row, status, q, k, v, ctx_len, R: int, Hq: int, Hkv: int,
-                   scale: float, shared: bool = False):
+                   scale: float, shared: bool = False, nodes=None):
     """o[b, i, h] = sum_j softmax_j(scale * q[b, i, h] . k_j) v_j over the keys
     node i sees: prefix positions 0 .. ctx_len[b]-1 and ctx_len[b] +
     node_row[b, a] for every node a on i's root path (LumoTree, Sec. V-B:
     the ancestry mask over physically placed candidate keys).  Requests whose
     tree is malformed (status != 0, reported by the descriptor build) or whose
-    ctx_len is outside [0, S - R] (EV_CTX) get no output.
+    ctx_len is outside [0, S - R] (EV_CTX) get no output.  With ``nodes``
+    (pairs (b, i)) only those rows are computed (the rest stay NaN).
     Returns (out float64, err)."""
     q64, k64, v64 = _f64(q), _f64(k), _f64(v)
     B, N = q64.shape[0], q64.shape[1]
@@ -69,14 +70,15 @@ def tree_attention(parent, node_row, status, q, k, v, ctx_len, R: int, Hq: int, 
             err |= EV_CTX
             continue
         for i in range(N):
-            keys = list(range(L)) + [L + int(node_row[t, a]) for a in root_path(parent[t], i)]
+            if nodes is not None and (b, i) not in nodes:
+                continue
+            cand = [L + int(node_row[t, a]) for a in root_path(parent[t], i)]
             for h in range(Hq):
                 g = h // G
-                kk = k64[b, keys, g, :]
-                vv = v64[b, keys, g, :]
-                s = scale * (kk @ q64[b, i, h])
+                # the prefix keys, then the root path's candidates
+                s = scale * np.concatenate([k64[b, :L, g, :] @ q64[b, i, h], k64[b, cand, g, :] @ q64[b, i, h]])
                 w = np.exp(s - s.max())
-                out[b, i, h] = (w @ vv) / w.sum()
+                out[b, i, h] = (w[:L] @ v64[b, :L, g, :] + w[L:] @ v64[b, cand, g, :]) / w.sum()
     return out, err
 
 

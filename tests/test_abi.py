@@ -31,7 +31,8 @@ def test_header_declares_the_entry_points():
     decl = declared_functions()
     for name in ("gdn_tree_desc_build", "conv_ancestry_gather", "gdn_tree_verify", "gdn_tree_commit",
                  "gdn_tree_commit_layers", "conv_ancestry_gather_publish", "gdn_tree_commit_verify",
-                 "gdn_path_resolve", "gdn_step_prepare", "gdn_layer_step"):
+                 "gdn_path_resolve", "gdn_step_prepare", "gdn_layer_step", "gdn_tree_attention",
+                 "gdn_tree_kv_publish"):
         assert name in decl
     assert set(decl) == set(g.EXPORTED)
 
@@ -46,7 +47,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.gdn_abi_version() == 5
+    assert lib.gdn_abi_version() == 6
     assert lib.gdn_status_string(0) == b"ok"
     assert lib.gdn_status_string(-1) == b"invalid argument"
     assert lib.gdn_status_string(-4) == b"unsupported size"
@@ -194,6 +195,41 @@ def test_layer_step_argument_checks_fail_before_launch(lib):
     assert call(xp=None) == g.GDN_ERR_ARG
     assert call(pn=None) == g.GDN_ERR_ARG
     assert call(Hqk=3) == g.GDN_ERR_ARG
+
+
+def test_attention_argument_checks_fail_before_launch(lib):
+    err = ctypes.c_void_p(128)
+    d = ctypes.byref(_desc(N=27, R=32))
+    big_r = ctypes.byref(_desc(N=27, R=65))
+    p = ctypes.c_void_p(256)
+    W = lib.gdn_tree_attention_workspace_bytes
+    assert W(2, 27, 16, 256, 8) == 9 * 2 * 16 * 27 * 258 * 4
+    assert W(0, 27, 16, 256, 8) == 0
+    A = lib.gdn_tree_attention
+    ws = W(2, 27, 16, 256, 8)
+    args = dict(d=d, q=p, k=p, v=p, S=4096, ctx=p, out=p, ws=p, wsb=ws, splits=8, Hq=16, Hkv=2, D=256,
+                scale=0.0625, fl=0)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return A(a["d"], a["q"], a["k"], a["v"], a["S"], a["ctx"], a["out"], a["ws"], a["wsb"], a["splits"],
+                 a["Hq"], a["Hkv"], a["D"], a["scale"], a["fl"], err, None)
+    assert call(D=64) == g.GDN_ERR_UNSUPPORTED
+    assert call(Hq=15) == g.GDN_ERR_ARG                      # Hq not a multiple of Hkv
+    assert call(splits=0) == g.GDN_ERR_UNSUPPORTED
+    assert call(wsb=ws - 4) == g.GDN_ERR_ARG                 # workspace too small
+    assert call(S=31) == g.GDN_ERR_ARG                       # cache shorter than the candidates
+    assert call(scale=0.0) == g.GDN_ERR_ARG
+    assert call(fl=g.GDN_F_NORM_QK) == g.GDN_ERR_ARG
+    assert call(d=big_r) == g.GDN_ERR_UNSUPPORTED            # R > 64
+    assert call(k=ctypes.c_void_p(264)) == g.GDN_ERR_ARG     # not 16-byte aligned
+    assert call(ctx=None) == g.GDN_ERR_ARG
+    K = lib.gdn_tree_kv_publish
+    assert K(d, p, p, 0, p, p, 4096, p, 2, 256, err, None) == g.GDN_ERR_UNSUPPORTED
+    assert K(d, p, p, 8, p, p, 4096, p, 2, 64, err, None) == g.GDN_ERR_UNSUPPORTED
+    assert K(d, p, None, 8, p, p, 4096, p, 2, 256, err, None) == g.GDN_ERR_ARG
+    assert K(d, p, p, 8, p, p, 16, p, 2, 256, err, None) == g.GDN_ERR_ARG
 
 
 def test_binding_refuses_when_library_missing(monkeypatch, tmp_path):

@@ -22,25 +22,27 @@ import threading
 
 __all__ = [
     "GDN_OK", "GDN_ERR_ARG", "GDN_ERR_UNSUPPORTED", "GDN_ERR_HIP",
-    "GDN_EV_PARENT", "GDN_EV_ROW", "GDN_EV_STATE", "GDN_EV_PATH",
-    "GDN_DT_BF16", "GDN_DT_F32", "GDN_F_NORM_QK", "GDN_F_OUT_BF16", "GDN_F_VALU",
+    "GDN_EV_PARENT", "GDN_EV_ROW", "GDN_EV_STATE", "GDN_EV_PATH", "GDN_EV_CTX",
+    "GDN_DT_BF16", "GDN_DT_F32", "GDN_F_NORM_QK", "GDN_F_OUT_BF16", "GDN_F_VALU", "GDN_F_RAW_GATES",
     "GDN_ACT_NONE", "GDN_ACT_SILU", "GdnError", "TreeDesc", "library_path", "load_library",
     "gdn_tree_desc_build", "conv_ancestry_gather", "gdn_tree_verify", "gdn_tree_commit",
-    "conv_ancestry_gather_publish", "gdn_tree_commit_verify", "gdn_path_resolve",
-    "gdn_step_prepare", "gdn_layer_step",
+    "gdn_tree_commit_layers", "conv_ancestry_gather_publish", "gdn_tree_commit_verify",
+    "gdn_path_resolve", "gdn_step_prepare", "gdn_layer_step", "gdn_tree_attention_workspace_bytes",
+    "gdn_tree_attention", "gdn_tree_kv_publish",
 ]
 
 # values mirror include/gdn_tree.h
 GDN_OK, GDN_ERR_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, -1, -4, -5
-GDN_EV_PARENT, GDN_EV_ROW, GDN_EV_STATE, GDN_EV_PATH = 1, 2, 4, 8
+GDN_EV_PARENT, GDN_EV_ROW, GDN_EV_STATE, GDN_EV_PATH, GDN_EV_CTX = 1, 2, 4, 8, 16
 GDN_DT_BF16, GDN_DT_F32 = 0, 1
 GDN_F_NORM_QK, GDN_F_OUT_BF16, GDN_F_VALU, GDN_F_RAW_GATES = 1, 2, 4, 8
 GDN_ACT_NONE, GDN_ACT_SILU = 0, 1
 
 EXPORTED = ("gdn_tree_desc_build", "conv_ancestry_gather", "gdn_tree_verify",
             "gdn_tree_commit", "gdn_tree_commit_layers", "conv_ancestry_gather_publish", "gdn_tree_commit_verify",
-            "gdn_path_resolve", "gdn_step_prepare", "gdn_layer_step", "gdn_status_string",
-            "gdn_abi_version")
+            "gdn_path_resolve", "gdn_step_prepare", "gdn_layer_step",
+            "gdn_tree_attention_workspace_bytes", "gdn_tree_attention", "gdn_tree_kv_publish",
+            "gdn_status_string", "gdn_abi_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lock = threading.Lock()
@@ -108,6 +110,13 @@ def load_library():
         lib.gdn_layer_step.argtypes = [dp, vp, vp, vp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp,
                                        dp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                        vp, vp, vp]
+        lib.gdn_tree_attention_workspace_bytes.restype = ctypes.c_size_t
+        lib.gdn_tree_attention_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        lib.gdn_tree_attention.restype = i32
+        lib.gdn_tree_attention.argtypes = [dp, vp, vp, vp, i32, vp, vp, vp, ctypes.c_size_t, i32, i32,
+                                           i32, i32, ctypes.c_float, i32, vp, vp]
+        lib.gdn_tree_kv_publish.restype = i32
+        lib.gdn_tree_kv_publish.argtypes = [dp, vp, vp, i32, vp, vp, i32, vp, i32, i32, vp, vp]
         lib.gdn_status_string.restype = ctypes.c_char_p
         lib.gdn_status_string.argtypes = [i32]
         lib.gdn_abi_version.restype = i32
@@ -349,6 +358,43 @@ def gdn_tree_commit_verify(desc: TreeDesc, q, k, v, alpha, beta, state_pool, sta
         Hv, dk, dv, _dtype_code(q), _gate_flags(flags, gate_params), _ptr(gate_params), _ptr(err),
         _stream(stream))
     return _check(code, "gdn_tree_commit_verify", raise_on_error)
+
+
+def gdn_tree_attention_workspace_bytes(B: int, N: int, Hq: int, D: int, splits: int) -> int:
+    return int(load_library().gdn_tree_attention_workspace_bytes(B, N, Hq, D, splits))
+
+
+def gdn_tree_attention(desc: TreeDesc, q, k_cache, v_cache, ctx_len, out, workspace, err,
+                       splits: int, scale: float | None = None, flags: int = 0, stream=None,
+                       raise_on_error=True) -> int:
+    """Tree attention: q [B, N, Hq, D] (logical node rows), k_cache / v_cache
+    [B, S, Hkv, D] with the candidates at ctx_len[b] + node_row, out
+    [B, N, Hq, D]; workspace: a device buffer of at least
+    gdn_tree_attention_workspace_bytes(...) bytes."""
+    B, N, Hq, D = (int(x) for x in q.shape)
+    S, Hkv = int(k_cache.shape[1]), int(k_cache.shape[2])
+    for t, name in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (out, "out")):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    scale = 1.0 / float(D) ** 0.5 if scale is None else float(scale)
+    nbytes = workspace.numel() * workspace.element_size()
+    code = load_library().gdn_tree_attention(desc.ref(), _ptr(q), _ptr(k_cache), _ptr(v_cache), S,
+                                             _ptr(ctx_len), _ptr(out), _ptr(workspace), nbytes,
+                                             int(splits), Hq, Hkv, D, scale, int(flags), _ptr(err),
+                                             _stream(stream))
+    return _check(code, "gdn_tree_attention", raise_on_error)
+
+
+def gdn_tree_kv_publish(prev: TreeDesc, path_rows, path_n, k_cache, v_cache, ctx_len, err,
+                        stream=None, raise_on_error=True) -> int:
+    """Move the accepted path's KV entries (resolved rows path_rows [B, Lmax],
+    counts path_n [B]) to the positions right after each request's prefix."""
+    S, Hkv, D = int(k_cache.shape[1]), int(k_cache.shape[2]), int(k_cache.shape[3])
+    Lmax = int(path_rows.shape[1])
+    code = load_library().gdn_tree_kv_publish(prev.ref(), _ptr(path_rows), _ptr(path_n), Lmax,
+                                              _ptr(k_cache), _ptr(v_cache), S, _ptr(ctx_len), Hkv,
+                                              D, _ptr(err), _stream(stream))
+    return _check(code, "gdn_tree_kv_publish", raise_on_error)
 
 
 def gdn_path_resolve(prev: TreeDesc, path, path_len, state_idx, P: int, path_rows, path_n, err,

@@ -42,7 +42,7 @@ static int32_t check_gates(int32_t flags, const float* gate_params) {
     return (gate_params != nullptr && aligned(gate_params, 4)) ? GDN_OK : GDN_ERR_ARG;
 }
 
-int32_t gdn_abi_version(void) { return 5; }
+int32_t gdn_abi_version(void) { return 6; }
 
 const char* gdn_status_string(int32_t status) {
     switch (status) {
@@ -342,6 +342,53 @@ int32_t gdn_layer_step(const gdn_tree_desc* d, const void* x, const void* w, con
     a.err = err;
     a.gate_params = gate_params;
     return map_launch(gdn::launch_layer_step(*d, a, static_cast<hipStream_t>(stream)));
+}
+
+size_t gdn_tree_attention_workspace_bytes(int32_t B, int32_t N, int32_t Hq, int32_t D,
+                                          int32_t splits) {
+    if (B < 1 || N < 1 || Hq < 1 || D < 1 || splits < 1) return 0;
+    return gdn::tree_attention_workspace_bytes(B, N, Hq, D, splits);
+}
+
+int32_t gdn_tree_attention(const gdn_tree_desc* d, const void* q, const void* k_cache,
+                           const void* v_cache, int32_t S, const int32_t* ctx_len, void* out,
+                           void* workspace, size_t workspace_bytes, int32_t splits, int32_t Hq,
+                           int32_t Hkv, int32_t D, float scale, int32_t flags, int32_t* err,
+                           void* stream) {
+    int32_t st = check_desc(d);
+    if (st != GDN_OK) return st;
+    if (!q || !k_cache || !v_cache || !ctx_len || !out || !workspace || !err) return GDN_ERR_ARG;
+    if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return GDN_ERR_ARG;
+    if (D != 128 && D != 256) return GDN_ERR_UNSUPPORTED;
+    if (d->R > 64) return GDN_ERR_UNSUPPORTED;
+    if (splits < 1 || splits > 1024) return GDN_ERR_UNSUPPORTED;
+    if (S < d->R) return GDN_ERR_ARG;
+    if (!(scale > 0.0f) || (flags & ~GDN_F_OUT_BF16) != 0) return GDN_ERR_ARG;
+    if (workspace_bytes < gdn::tree_attention_workspace_bytes(d->B, d->N, Hq, D, splits)) return GDN_ERR_ARG;
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(workspace, 16) ||
+        !aligned(out, (flags & GDN_F_OUT_BF16) ? 2 : 4))
+        return GDN_ERR_ARG;
+    const int64_t units = static_cast<int64_t>(d->B) * Hkv * (splits + 1) * Hq;
+    if (units > 0x7fffffffLL || static_cast<int64_t>(d->B) * S * Hkv * D > (int64_t{1} << 40))
+        return GDN_ERR_UNSUPPORTED;
+    gdn::TreeAttnArgs a{q, k_cache, v_cache, S, ctx_len, out, workspace, splits, Hq, Hkv, D,
+                        scale, flags, err};
+    return map_launch(gdn::launch_tree_attention(*d, a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t gdn_tree_kv_publish(const gdn_tree_desc* d_prev, const int32_t* path_rows,
+                            const int32_t* path_n, int32_t Lmax, void* k_cache, void* v_cache,
+                            int32_t S, const int32_t* ctx_len, int32_t Hkv, int32_t D,
+                            int32_t* err, void* stream) {
+    int32_t st = check_desc(d_prev);
+    if (st != GDN_OK) return st;
+    if (!path_rows || !path_n || !k_cache || !v_cache || !ctx_len || !err || Hkv < 1) return GDN_ERR_ARG;
+    if (Lmax < 1 || Lmax > GDN_MAX_NODES) return GDN_ERR_UNSUPPORTED;
+    if (D != 128 && D != 256) return GDN_ERR_UNSUPPORTED;
+    if (S < d_prev->R) return GDN_ERR_ARG;
+    if (!aligned(k_cache, 16) || !aligned(v_cache, 16)) return GDN_ERR_ARG;
+    return map_launch(gdn::launch_kv_publish(*d_prev, path_rows, path_n, Lmax, k_cache, v_cache, S, ctx_len,
+                                             Hkv, D, err, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

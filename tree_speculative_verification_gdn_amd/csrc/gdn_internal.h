@@ -186,6 +186,27 @@ struct LayerArgs {
 };
 hipError_t launch_layer_step(const gdn_tree_desc& d, const LayerArgs& a, hipStream_t s);
 
+// Tree attention over the committed prefix and the candidate suffix, and
+// the accepted path's KV publication (bf16, D = 128 or 256).
+struct TreeAttnArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    int S;
+    const int32_t* ctx_len;
+    void* out;
+    void* workspace;
+    int splits, Hq, Hkv, D;
+    float scale;
+    int flags;
+    int32_t* err;
+};
+size_t tree_attention_workspace_bytes(int B, int N, int Hq, int D, int splits);
+hipError_t launch_tree_attention(const gdn_tree_desc& d, const TreeAttnArgs& a, hipStream_t s);
+hipError_t launch_kv_publish(const gdn_tree_desc& prev, const int32_t* path_rows, const int32_t* path_n,
+                             int Lmax, void* k, void* v, int S, const int32_t* ctx_len, int Hkv, int D,
+                             int32_t* err, hipStream_t s);
+
 // Validation of the previous step's path and its physical rows, once per step.
 hipError_t launch_path_resolve(const gdn_tree_desc& prev, int B, const int32_t* path,
                                const int32_t* path_len, int Lmax, const int32_t* state_idx, int P,

@@ -1,0 +1,437 @@
+// Ancestry-aware tree attention over a physically placed candidate suffix,
+// and the accepted path's KV publication (LumoTree, Sec. III-C and V-B: one
+// slot map places the candidates' keys/values after the committed prefix and
+// names the mask's key columns; grouped query heads share staged KV tiles;
+// the context is split into partitions for parallel work at small batch).
+//
+// Attention: one 256-thread workgroup per (request, kv head, pair of query
+// heads, key partition).  Partitions 0..splits-1 cover the committed prefix
+// in equal ranges; partition `splits` covers the R candidate slots under the
+// ancestry mask.  A workgroup holds up to 64 query rows (the N nodes of two
+// heads, or of one head when N > 32), 16 per wave, and walks its keys in
+// tiles of 32: the tile's keys row-major and its values transposed go to LDS,
+// S^T = K Q^T runs on v_mfma_f32_16x16x32_bf16 (a wave's lane holds one query
+// row's scores for four keys per 16-key block), an online softmax keeps each
+// row's running maximum and sum in the log2 domain, and O += P V on the same
+// instruction with P split into bf16 hi + lo (P's rounding error stays near
+// 2^-17 of a weight).  Each partition writes its unnormalised O, maximum and
+// sum; a second kernel merges the partitions (the standard split-softmax
+// merge) into the output.
+//
+// Layouts: q [B][N][Hq][D] logical node rows; k, v [B][S][Hkv][D] bf16, the
+// prefix at positions [0, ctx_len[b]), candidate physical row r at
+// ctx_len[b] + r.
+#include "gdn_internal.h"
+
+namespace gdn {
+
+namespace {
+typedef __bf16 abf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 abf16x2_t __attribute__((ext_vector_type(2)));
+typedef float af32x2_t __attribute__((ext_vector_type(2)));
+typedef float af32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kAThreads = 256;
+constexpr int kTileKeys = 32;  // keys per tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct AttnArgs {
+    int B, N, R, S, Hq, Hkv, splits, HPW, pairs, chunk, shared;
+    const int32_t* node_row;
+    const uint64_t* anc;
+    const int32_t* status;
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const int32_t* ctx_len;
+    float scale2;   // softmax scale * log2(e)
+    float* ws_o;    // [splits + 1][B][Hq][N][D] unnormalised partial outputs
+    float* ws_ml;   // [splits + 1][B][Hq][N][2] running maximum (log2 domain) and sum
+    void* out;      // [B][N][Hq][D]
+    int out_bf16;
+    int32_t* err;
+};
+
+template <int D>
+struct AttnLds {
+    static constexpr int kKStride = D + 8;          // bf16 per staged key row (16-byte pad)
+    static constexpr int kVStride = kTileKeys + 4;  // bf16 per transposed value row
+    static constexpr int K = 0;
+    static constexpr int V = K + kTileKeys * kKStride * 2;
+    static constexpr int ROW = V + D * kVStride * 2;   // int32 node_row[64]
+    static constexpr int VIS = ROW + 64 * 4;           // uint64 visible rows [64]
+    static constexpr int total = VIS + 64 * 8;
+};
+
+// two finite fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t bf16_pack_rne(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((af32x2_t){a, b}, abf16x2_t));
+}
+
+// Is request b skipped (malformed tree or context out of range)?  Uniform.
+__device__ __forceinline__ bool attn_skip(const AttnArgs& a, int b, int& L) {
+    const int t = a.shared ? 0 : b;
+    L = a.ctx_len[b];
+    return a.status[t] != 0 || L < 0 || L + a.R > a.S;
+}
+}  // namespace
+
+template <int D>
+__global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) {
+    using Lds = AttnLds<D>;
+    constexpr int kDS = D / 32;   // 32-wide d steps of S^T
+    constexpr int kDB = D / 16;   // 16-wide d blocks of O
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    uint16_t* s_k = reinterpret_cast<uint16_t*>(lds + Lds::K);
+    uint16_t* s_vt = reinterpret_cast<uint16_t*>(lds + Lds::V);
+    int32_t* s_row = reinterpret_cast<int32_t*>(lds + Lds::ROW);
+    uint64_t* s_vis = reinterpret_cast<uint64_t*>(lds + Lds::VIS);
+
+    // workgroup -> (request, kv head, key partition, head pair); the pairs of
+    // one kv head and partition are neighbours (same XCD: shared KV tiles)
+    const int nsp = a.splits + 1;
+    const uint32_t unit = xcd_local_order(blockIdx.x, gridDim.x);
+    const int p = static_cast<int>(unit % a.pairs);
+    const int sp = static_cast<int>((unit / a.pairs) % nsp);
+    const int g = static_cast<int>((unit / (a.pairs * nsp)) % a.Hkv);
+    const int b = static_cast<int>(unit / (a.pairs * nsp * a.Hkv));
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, l = tid & 63, lg = l >> 4, l16 = l & 15;
+    const int G = a.Hq / a.Hkv;
+    const int h0 = g * G + p * a.HPW;
+    const int nh = min(a.HPW, G - p * a.HPW);
+    const int NPH = a.HPW == 2 ? 32 : 64;  // rows per head in the workgroup
+    const int N = a.N;
+    const int t = a.shared ? 0 : b;
+
+    int L;
+    if (attn_skip(a, b, L)) {
+        if (a.status[t] == 0 && tid == 0 && sp == 0 && p == 0 && g == 0) atomicOr(a.err, GDN_EV_CTX);
+        return;
+    }
+    const bool tree = sp == a.splits;
+    const int lo = tree ? L : min(sp * a.chunk, L);
+    const int hi = tree ? L + a.R : min((sp + 1) * a.chunk, L);
+
+    // this lane's query row (S^T column): row r = 16 w + l16
+    const int rq = 16 * w + l16;
+    const int iq = rq % NPH, hq = rq / NPH;
+    const bool vq = iq < N && hq < nh;
+    abf16x8_t qreg[kDS];
+    {
+        const uint16_t* qp = a.q + ((static_cast<size_t>(b) * N + min(iq, N - 1)) * a.Hq + h0 + min(hq, nh - 1)) * D;
+#pragma unroll
+        for (int ds = 0; ds < kDS; ++ds) {
+            uint4 u = *reinterpret_cast<const uint4*>(qp + ds * 32 + 8 * lg);
+            if (!vq) u = make_uint4(0u, 0u, 0u, 0u);
+            qreg[ds] = __builtin_bit_cast(abf16x8_t, u);
+        }
+    }
+    // the candidates visible to each node: its own row and its ancestors';
+    // the rows some node occupies (the others may hold anything)
+    uint64_t my_vis = 0ull, used = ~0ull;
+    if (tree) {  // uniform
+        if (tid < 64) s_row[tid] = a.node_row[static_cast<size_t>(t) * N + min(tid, N - 1)];
+        __syncthreads();
+        used = 0ull;
+        for (int i = 0; i < N; ++i) used |= 1ull << s_row[i];
+        if (tid < N) {
+            uint64_t anc = a.anc[static_cast<size_t>(t) * N + tid];
+            uint64_t vis = 1ull << s_row[tid];
+            while (anc) {
+                const int j = __builtin_ctzll(anc);
+                anc &= anc - 1;
+                vis |= 1ull << s_row[j];
+            }
+            s_vis[tid] = vis;
+        }
+        __syncthreads();
+        my_vis = s_vis[min(iq, N - 1)];
+    }
+
+    const uint64_t vis_or = tree ? my_vis : ~0ull;  // context keys: every row sees them
+    af32x4_t o[kDB];
+#pragma unroll
+    for (int db = 0; db < kDB; ++db) o[db] = af32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    const int ntiles = (hi - lo + kTileKeys - 1) / kTileKeys;
+    constexpr int kChunks = kTileKeys * D / 8;  // 16-byte chunks of a K (or V) tile
+    for (int tile = 0; tile < ntiles; ++tile) {
+        const int key0 = lo + tile * kTileKeys;
+        // stage the tile: K row-major, V transposed (value row d holds the
+        // tile's keys in order).  Keys no row may see (past the partition,
+        // or candidate rows no node occupies) are staged as zeros: their
+        // weights are 0, and 0 times whatever the cache holds there must
+        // not reach the output.  The masks here and below are computed
+        // without branches: the scores are read from the matrix-core
+        // results right after them, and code between the two stays one
+        // basic block (a read in a later block after a branch got stale
+        // results here)
+#pragma unroll
+        for (int u = 0; u < kChunks / kAThreads; ++u) {
+            const int c = tid + u * kAThreads;
+            const int kk = c / (D / 8), d8 = (c % (D / 8)) * 8;
+            const int key = key0 + kk;
+            const size_t pos = static_cast<size_t>(min(key, a.S - 1));
+            const size_t off = ((static_cast<size_t>(b) * a.S + pos) * a.Hkv + g) * D + d8;
+            uint4 kc = *reinterpret_cast<const uint4*>(a.k + off);
+            uint4 vc = *reinterpret_cast<const uint4*>(a.v + off);
+            const int sh = tree ? ((key - L) & 63) : 0;
+            const uint32_t keep = ((key < hi) & (((used >> sh) & 1ull) != 0ull)) ? 0xffffffffu : 0u;
+            kc.x &= keep; kc.y &= keep; kc.z &= keep; kc.w &= keep;
+            vc.x &= keep; vc.y &= keep; vc.z &= keep; vc.w &= keep;
+            *reinterpret_cast<uint4*>(s_k + kk * Lds::kKStride + d8) = kc;
+            const uint32_t vw[4] = {vc.x, vc.y, vc.z, vc.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                s_vt[(d8 + 2 * e) * Lds::kVStride + kk] = static_cast<uint16_t>(vw[e] & 0xffffu);
+                s_vt[(d8 + 2 * e + 1) * Lds::kVStride + kk] = static_cast<uint16_t>(vw[e] >> 16);
+            }
+        }
+        __syncthreads();
+
+        // S^T blocks: lane (lg, l16) holds keys 16 kb + 4 lg + i of query row rq
+        float s[2][4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            af32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ds = 0; ds < kDS; ++ds) {
+                const abf16x8_t ka = *reinterpret_cast<const abf16x8_t*>(
+                    s_k + (kb * 16 + l16) * Lds::kKStride + ds * 32 + 8 * lg);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qreg[ds], acc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                // branch-free: visible if inside the partition and (for the
+                // candidates) on the row's root path
+                const int key = key0 + kb * 16 + 4 * lg + i;
+                const int sh = tree ? ((key - L) & 63) : 0;
+                const bool ok = (key < hi) & (((vis_or >> sh) & 1ull) != 0ull);
+                s[kb][i] = ok ? acc[i] * a.scale2 : -INFINITY;
+            }
+        }
+        // online softmax per query row (the row's scores sit in lanes l16,
+        // l16 + 16, l16 + 32, l16 + 48)
+        float mt = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mt = fmaxf(mt, s[kb][i]);
+        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const float m_new = fmaxf(m_run, mt);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float factor = __builtin_amdgcn_exp2f(m_run - m_use);  // 0 while nothing was seen
+        float pr[2][4];
+        float ps = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pr[kb][i] = __builtin_amdgcn_exp2f(s[kb][i] - m_use);
+                ps += pr[kb][i];
+            }
+        ps += __shfl_xor(ps, 16, 64);
+        ps += __shfl_xor(ps, 32, 64);
+        l_run = l_run * factor + ps;
+        m_run = m_new;
+        // rescale the output rows 4 lg + i of this lane's blocks
+        float fr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fr[i] = __shfl(factor, 4 * lg + i, 64);
+#pragma unroll
+        for (int db = 0; db < kDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[db][i] *= fr[i];
+        // P as the A operand (row rq; k slots: keys 4 lg + j of block 0, then
+        // of block 1), split into bf16 hi + lo
+        uint32_t ph[4], pl[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int kb = e >> 1, i0 = 2 * (e & 1);
+            const float x0 = pr[kb][i0], x1 = pr[kb][i0 + 1];
+            ph[e] = bf16_pack_rne(x0, x1);
+            const float h0f = bf16_bits_to_f32(static_cast<uint16_t>(ph[e] & 0xffffu));
+            const float h1f = bf16_bits_to_f32(static_cast<uint16_t>(ph[e] >> 16));
+            pl[e] = bf16_pack_rne(x0 - h0f, x1 - h1f);
+        }
+        const abf16x8_t pa_hi = __builtin_bit_cast(abf16x8_t, make_uint4(ph[0], ph[1], ph[2], ph[3]));
+        const abf16x8_t pa_lo = __builtin_bit_cast(abf16x8_t, make_uint4(pl[0], pl[1], pl[2], pl[3]));
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+            const uint16_t* vr = s_vt + (db * 16 + l16) * Lds::kVStride + 4 * lg;
+            const uint2 v0 = *reinterpret_cast<const uint2*>(vr);
+            const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16);
+            const abf16x8_t vb = __builtin_bit_cast(abf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
+            o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, vb, o[db], 0, 0, 0);
+            o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, vb, o[db], 0, 0, 0);
+        }
+        __syncthreads();  // the next tile overwrites the staged keys and values
+    }
+
+    // partial results: O rows 4 lg + i of this wave, maximum and sum of row rq
+    const size_t base = (static_cast<size_t>(sp) * a.B + b) * a.Hq;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 16 * w + 4 * lg + i;
+        const int ir = r % NPH, hr = r / NPH;
+        if (ir < N && hr < nh) {
+            float* dst = a.ws_o + ((base + h0 + hr) * N + ir) * D + l16;
+#pragma unroll
+            for (int db = 0; db < kDB; ++db) dst[db * 16] = o[db][i];
+        }
+    }
+    if (lg == 0 && vq) {
+        float* ml = a.ws_ml + ((base + h0 + hq) * N + iq) * 2;
+        ml[0] = m_run;
+        ml[1] = l_run;
+    }
+}
+
+// Merge of the key partitions: one workgroup per (request, head, node) row,
+// one thread per output element.
+template <int D>
+__global__ void __launch_bounds__(D) tree_attn_merge_kernel(const AttnArgs a) {
+    const int row = blockIdx.x;  // ((b * Hq) + h) * N + i
+    const int N = a.N;
+    const int i = row % N;
+    const int h = (row / N) % a.Hq;
+    const int b = row / (N * a.Hq);
+    int L;
+    if (attn_skip(a, b, L)) return;
+    const int d = threadIdx.x;
+    const size_t per_split = static_cast<size_t>(a.B) * a.Hq * N;
+    const int nsp = a.splits + 1;
+    float M = -INFINITY;
+    for (int s = 0; s < nsp; ++s) M = fmaxf(M, a.ws_ml[(s * per_split + row) * 2]);
+    float acc = 0.f, den = 0.f;
+    for (int s = 0; s < nsp; ++s) {
+        const float* ml = a.ws_ml + (s * per_split + row) * 2;
+        const float wgt = __builtin_amdgcn_exp2f(ml[0] - M);  // 0 for an empty partition
+        den += wgt * ml[1];
+        acc += wgt * a.ws_o[(s * per_split + row) * D + d];
+    }
+    const float val = acc / den;
+    const size_t oi = ((static_cast<size_t>(b) * N + i) * a.Hq + h) * D + d;
+    if (a.out_bf16)
+        static_cast<uint16_t*>(a.out)[oi] = f32_to_bf16_bits(val);
+    else
+        static_cast<float*>(a.out)[oi] = val;
+}
+
+size_t tree_attention_workspace_bytes(int B, int N, int Hq, int D, int splits) {
+    const size_t rows = static_cast<size_t>(splits + 1) * B * Hq * N;
+    return rows * (static_cast<size_t>(D) + 2) * sizeof(float);
+}
+
+hipError_t launch_tree_attention(const gdn_tree_desc& d, const TreeAttnArgs& ta, hipStream_t s) {
+    AttnArgs a{};
+    a.B = d.B;
+    a.N = d.N;
+    a.R = d.R;
+    a.S = ta.S;
+    a.Hq = ta.Hq;
+    a.Hkv = ta.Hkv;
+    a.splits = ta.splits;
+    a.HPW = d.N <= 32 ? 2 : 1;
+    const int G = ta.Hq / ta.Hkv;
+    a.pairs = (G + a.HPW - 1) / a.HPW;
+    a.shared = d.shared;
+    a.node_row = d.node_row;
+    a.anc = d.anc;
+    a.status = d.status;
+    a.q = static_cast<const uint16_t*>(ta.q);
+    a.k = static_cast<const uint16_t*>(ta.k);
+    a.v = static_cast<const uint16_t*>(ta.v);
+    a.ctx_len = ta.ctx_len;
+    a.scale2 = ta.scale * kLog2e;
+    const size_t rows = static_cast<size_t>(ta.splits + 1) * d.B * ta.Hq * d.N;
+    a.ws_o = static_cast<float*>(ta.workspace);
+    a.ws_ml = a.ws_o + rows * ta.D;
+    a.out = ta.out;
+    a.out_bf16 = (ta.flags & GDN_F_OUT_BF16) ? 1 : 0;
+    a.err = ta.err;
+    // context keys per partition: the longest context the cache can hold
+    // (S - R) split evenly, in whole tiles
+    const int max_ctx = ta.S - d.R;
+    a.chunk = ((max_ctx + ta.splits - 1) / ta.splits + kTileKeys - 1) / kTileKeys * kTileKeys;
+    if (a.chunk < kTileKeys) a.chunk = kTileKeys;
+    const unsigned units = static_cast<unsigned>(d.B) * ta.Hkv * (ta.splits + 1) * a.pairs;
+    const unsigned mrows = static_cast<unsigned>(d.B) * ta.Hq * d.N;
+    if (ta.D == 128) {
+        hipLaunchKernelGGL(tree_attn_kernel<128>, dim3(units), dim3(kAThreads), AttnLds<128>::total, s, a);
+        hipLaunchKernelGGL(tree_attn_merge_kernel<128>, dim3(mrows), dim3(128), 0, s, a);
+    } else if (ta.D == 256) {
+        hipLaunchKernelGGL(tree_attn_kernel<256>, dim3(units), dim3(kAThreads), AttnLds<256>::total, s, a);
+        hipLaunchKernelGGL(tree_attn_merge_kernel<256>, dim3(mrows), dim3(256), 0, s, a);
+    } else {
+        return hipErrorNotSupported;
+    }
+    return hipGetLastError();
+}
+
+// ---- KV publication ----------------------------------------------------
+// One workgroup per (request, kv head): every source entry of the accepted
+// path is read into LDS before any destination is written (sources and
+// destinations overlap inside the candidate suffix).
+template <int D>
+__global__ void __launch_bounds__(256) kv_publish_kernel(int B, int R, int S, int Hkv, int Lmax,
+                                                         const int32_t* __restrict__ path_rows,
+                                                         const int32_t* __restrict__ path_n,
+                                                         uint16_t* __restrict__ k, uint16_t* __restrict__ v,
+                                                         const int32_t* __restrict__ ctx_len,
+                                                         int32_t* __restrict__ err) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    uint4* s_k = reinterpret_cast<uint4*>(lds);                          // [Lmax][D / 8]
+    uint4* s_v = s_k + static_cast<size_t>(Lmax) * (D / 8);
+    const int b = blockIdx.x / Hkv;
+    const int g = blockIdx.x % Hkv;
+    const int n = min(min(path_n[b], Lmax), R);  // a path has at most R distinct nodes
+    if (n <= 0) return;
+    const int L = ctx_len[b];
+    if (L < 0 || L + R > S) {
+        if (g == 0 && threadIdx.x == 0) atomicOr(err, GDN_EV_CTX);
+        return;
+    }
+    constexpr int C8 = D / 8;  // 16-byte chunks per entry
+    for (int c = threadIdx.x; c < n * C8; c += blockDim.x) {
+        const int j = c / C8, e = c % C8;
+        const int r = min(max(path_rows[static_cast<size_t>(b) * Lmax + j], 0), R - 1);
+        const size_t src = ((static_cast<size_t>(b) * S + L + r) * Hkv + g) * D / 8 + e;
+        s_k[c] = reinterpret_cast<const uint4*>(k)[src];
+        s_v[c] = reinterpret_cast<const uint4*>(v)[src];
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < n * C8; c += blockDim.x) {
+        const int j = c / C8, e = c % C8;
+        const size_t dst = ((static_cast<size_t>(b) * S + L + j) * Hkv + g) * D / 8 + e;
+        reinterpret_cast<uint4*>(k)[dst] = s_k[c];
+        reinterpret_cast<uint4*>(v)[dst] = s_v[c];
+    }
+}
+
+hipError_t launch_kv_publish(const gdn_tree_desc& prev, const int32_t* path_rows, const int32_t* path_n,
+                             int Lmax, void* k, void* v, int S, const int32_t* ctx_len, int Hkv, int D,
+                             int32_t* err, hipStream_t s) {
+    const size_t lds = static_cast<size_t>(Lmax) * D * 2 * 2;
+    const dim3 grid(static_cast<unsigned>(prev.B) * Hkv);
+    if (D == 128) {
+        hipLaunchKernelGGL(kv_publish_kernel<128>, grid, dim3(256), lds, s, prev.B, prev.R, S, Hkv, Lmax,
+                           path_rows, path_n, static_cast<uint16_t*>(k), static_cast<uint16_t*>(v), ctx_len,
+                           err);
+    } else if (D == 256) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kv_publish_kernel<256>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kv_publish_kernel<256>, grid, dim3(256), lds, s, prev.B, prev.R, S, Hkv, Lmax,
+                           path_rows, path_n, static_cast<uint16_t*>(k), static_cast<uint16_t*>(v), ctx_len,
+                           err);
+    } else {
+        return hipErrorNotSupported;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace gdn
