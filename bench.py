@@ -463,13 +463,127 @@ def run_layers(args, cfg, g, torch, dev, to_dev):
     print(json.dumps(line), flush=True)
 
 
+ATTN = dict(N=27, R=32, Hq=16, Hkv=2, D=256, bmax=3, depth_max=6)
+
+
+def attention_cpu_baseline(args, budget_s):
+    """The fp64 oracle's tree attention on the host, on one request of the
+    same workload (all its nodes and heads), repeated until ``budget_s``."""
+    import oracle  # noqa: F401  (the package; the attention oracle is NumPy)
+    from oracle.attention import tree_attention
+    import gdn_inputs as gi
+    a = ATTN
+    c = gi.make_attention_case(args.seed, 1, a["N"], a["R"], a["Hq"], a["Hkv"], a["D"], [args.ctx],
+                               args.ctx + a["R"], bmax=a["bmax"], depth_max=a["depth_max"], packing="bfs")
+    st = np.zeros(1, np.int32)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        tree_attention(c["parent"], c["node_row"], st, c["q"], c["k"], c["v"], c["ctx"], a["R"], a["Hq"],
+                       a["Hkv"], 1.0 / np.sqrt(a["D"]))
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 20:
+            break
+    return dict(value=reps * a["N"] / el, unit="tree nodes/s", cores=1, kind="oracle",
+                sample=f"one request of the workload (N={a['N']}, {args.ctx} prefix positions, all "
+                       f"{a['Hq']} heads) in fp64 NumPy, {reps} repetition(s), {el:.1f} s wall")
+
+
+def run_attention(args, g, torch, dev):
+    """Tree attention of one softmax-attention layer: B requests, each a
+    27-node tree (branching <= 3, depth <= 6, breadth-first rows) over a
+    committed prefix of ``--ctx`` positions; 16 query heads over 2 kv heads,
+    d = 256, bf16 cache.  Inputs drawn on the device; three instances in turn
+    so a step's 134 MB per request of keys and values do not stay in the
+    256 MB last-level cache."""
+    import gdn_inputs as gi
+    a = ATTN
+    B, N, R, Hq, Hkv, D = args.batch, a["N"], a["R"], a["Hq"], a["Hkv"], a["D"]
+    S = args.ctx + R
+    splits = args.splits
+    t0 = time.perf_counter()
+    insts = []
+    for j in range(3):
+        parents = np.stack([gi.random_tree(gi.rng(args.seed + j, gi.ATTN_CFG, b, 0), N, a["bmax"], a["depth_max"])
+                            for b in range(B)]).astype(np.int32)
+        rows = np.stack([gi.bfs_rows(p) for p in parents]).astype(np.int32)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(args.seed * 7 + j)
+        inst = dict(desc=g.TreeDesc(torch.from_numpy(parents).to(dev), torch.from_numpy(rows).to(dev), R, 1, B=B),
+                    q=torch.randn((B, N, Hq, D), generator=gen, device=dev).to(torch.bfloat16),
+                    k=torch.randn((B, S, Hkv, D), generator=gen, device=dev).to(torch.bfloat16),
+                    v=torch.randn((B, S, Hkv, D), generator=gen, device=dev).to(torch.bfloat16),
+                    ctx=torch.full((B,), args.ctx, dtype=torch.int32, device=dev),
+                    out=torch.empty((B, N, Hq, D), dtype=torch.float32, device=dev))
+        insts.append(inst)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    for inst in insts:
+        g.gdn_tree_desc_build(inst["desc"], err)
+    nbytes = g.gdn_tree_attention_workspace_bytes(B, N, Hq, D, splits)
+    ws = torch.empty((nbytes // 4 + 4,), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] attention mode: {B} x {N}-node trees over {args.ctx} prefix positions, Hq={Hq} "
+        f"Hkv={Hkv} d={D}, {splits} partitions; inputs ready in {time.perf_counter() - t0:.1f} s")
+
+    def step(i):
+        inst = insts[i % 3]
+        g.gdn_tree_attention(inst["desc"], inst["q"], inst["k"], inst["v"], inst["ctx"], inst["out"], ws, err,
+                             splits=splits)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    if int(err.item()) != 0:
+        log(f"[bench] device error word {int(err.item())}")
+        sys.exit(3)
+    ms = e0.elapsed_time(e1) / args.steps
+    # algorithmic bytes: the prefix keys and values once, the candidates',
+    # the queries and the outputs; flops of Q K^T and P V
+    kv = B * args.ctx * Hkv * D * 2 * 2
+    byts = kv + B * R * Hkv * D * 2 * 2 + B * N * Hq * D * 2 + B * N * Hq * D * 4
+    flops = 2 * 2 * B * N * Hq * (args.ctx + 7) * D
+    achieved = byts / (ms / 1e3) / 1e9
+    log(f"[bench] tree attention {ms * 1e3:.1f} us per layer: {byts / 1e6:.1f} MB -> {achieved:.1f} GB/s "
+        f"({achieved / PEAK_HBM_GBS * 100:.1f}% of 8 TB/s); {flops / 1e9:.1f} GFLOP -> "
+        f"{flops / (ms / 1e3) / 1e12:.1f} TFLOP/s")
+    cpu = None if args.no_cpu_baseline else attention_cpu_baseline(args, args.cpu_budget)
+    line = {
+        "metric": METRIC, "value": round(B * N / (ms / 1e3), 1), "unit": "tree nodes/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"tree attention: {B} request(s), {N}-node trees (branching<=3, depth<=6), "
+                               f"{args.ctx} prefix positions, Hq={Hq} over Hkv={Hkv}, d={D}, bf16 KV cache, "
+                               f"{splits} prefix partitions",
+                   "mode": "attention", "step": "gdn_tree_attention (partitions + merge), one layer",
+                   "value_is": "tree nodes attended per second per attention layer",
+                   "global_batch": B, "nodes_per_request": N, "parallelism": "single GPU",
+                   "step_bytes": int(byts), "step_gflop": round(flops / 1e9, 2)},
+        "roofline": dict(bound="hbm", kernel="tree_attention", achieved=round(achieved, 1), peak=PEAK_HBM_GBS,
+                         unit="GB/s", frac=round(achieved / PEAK_HBM_GBS, 4), traffic=None,
+                         avg_us=round(ms * 1e3, 2), algorithmic_bytes=int(byts)),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=4)
-    ap.add_argument("--mode", choices=("fused", "layer", "separate"), default="fused")
+    ap.add_argument("--mode", choices=("fused", "layer", "separate", "attention"), default="fused")
+    ap.add_argument("--ctx", type=int, default=65536, help="attention mode: committed prefix per request")
+    ap.add_argument("--splits", type=int, default=63,
+                    help="attention mode: prefix partitions (63: with the candidate partition, "
+                         "2 kv heads x 2 head groups x 64 = 256 workgroups, one per CU)")
+    ap.add_argument("--batch", type=int, default=1, help="attention mode: requests")
     ap.add_argument("--seed", type=int, default=2026)
     ap.add_argument("--sets", type=int, default=2, help="independent layer instances rotated per step")
     ap.add_argument("--layers", type=int, default=0,
@@ -519,6 +633,9 @@ def main():
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
 
+    if args.mode == "attention":
+        run_attention(args, g, torch, dev)
+        return
     if args.layers == 0:
         args.layers = cfg.layers
     if args.layers > 1:

@@ -31,7 +31,8 @@ typedef __bf16 abf16x2_t __attribute__((ext_vector_type(2)));
 typedef float af32x2_t __attribute__((ext_vector_type(2)));
 typedef float af32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kAThreads = 256;
+constexpr int kAThreads = 512;  // 8 waves of 16 query rows
+constexpr int kRows = 128;      // query rows per workgroup
 constexpr int kTileKeys = 32;  // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -54,11 +55,15 @@ struct AttnArgs {
 
 template <int D>
 struct AttnLds {
-    static constexpr int kKStride = D + 8;          // bf16 per staged key row (16-byte pad)
+    static constexpr int kKStride = D + 8;          // bf16 per staged key or query row (16-byte pad)
     static constexpr int kVStride = kTileKeys + 4;  // bf16 per transposed value row
-    static constexpr int K = 0;
-    static constexpr int V = K + kTileKeys * kKStride * 2;
-    static constexpr int ROW = V + D * kVStride * 2;   // int32 node_row[64]
+    static constexpr int Q = 0;                     // the workgroup's query rows
+    static constexpr int kKBytes = kTileKeys * kKStride * 2;
+    static constexpr int kVBytes = D * kVStride * 2;
+    static constexpr int K = Q + kRows * kKStride * 2;  // two buffers: K, V, K, V
+    static constexpr int V = K + kKBytes;
+    static constexpr int kBuf = kKBytes + kVBytes;      // offset of the second buffer
+    static constexpr int ROW = K + 2 * kBuf;            // int32 node_row[64]
     static constexpr int VIS = ROW + 64 * 4;           // uint64 visible rows [64]
     static constexpr int total = VIS + 64 * 8;
 };
@@ -82,13 +87,14 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
     constexpr int kDS = D / 32;   // 32-wide d steps of S^T
     constexpr int kDB = D / 16;   // 16-wide d blocks of O
     extern __shared__ __attribute__((aligned(16))) char lds[];
+    uint16_t* s_q = reinterpret_cast<uint16_t*>(lds + Lds::Q);
     uint16_t* s_k = reinterpret_cast<uint16_t*>(lds + Lds::K);
     uint16_t* s_vt = reinterpret_cast<uint16_t*>(lds + Lds::V);
     int32_t* s_row = reinterpret_cast<int32_t*>(lds + Lds::ROW);
     uint64_t* s_vis = reinterpret_cast<uint64_t*>(lds + Lds::VIS);
 
-    // workgroup -> (request, kv head, key partition, head pair); the pairs of
-    // one kv head and partition are neighbours (same XCD: shared KV tiles)
+    // workgroup -> (request, kv head, key partition, head group); the groups
+    // of one kv head and partition are neighbours (same XCD: shared KV tiles)
     const int nsp = a.splits + 1;
     const uint32_t unit = xcd_local_order(blockIdx.x, gridDim.x);
     const int p = static_cast<int>(unit % a.pairs);
@@ -100,7 +106,7 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
     const int G = a.Hq / a.Hkv;
     const int h0 = g * G + p * a.HPW;
     const int nh = min(a.HPW, G - p * a.HPW);
-    const int NPH = a.HPW == 2 ? 32 : 64;  // rows per head in the workgroup
+    const int NPH = kRows / a.HPW;  // rows per head in the workgroup (N <= NPH)
     const int N = a.N;
     const int t = a.shared ? 0 : b;
 
@@ -113,20 +119,22 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
     const int lo = tree ? L : min(sp * a.chunk, L);
     const int hi = tree ? L + a.R : min((sp + 1) * a.chunk, L);
 
+    // the query rows (row r = head r / NPH, node r % NPH; rows past the
+    // nodes or heads are zeros) staged in LDS once
+#pragma unroll
+    for (int u = 0; u < kRows * D / 8 / kAThreads; ++u) {
+        const int c = tid + u * kAThreads;
+        const int r = c / (D / 8), d8 = (c % (D / 8)) * 8;
+        const int ir = r % NPH, hr = r / NPH;
+        const uint16_t* qp = a.q + ((static_cast<size_t>(b) * N + min(ir, N - 1)) * a.Hq + h0 + min(hr, nh - 1)) * D;
+        uint4 qc = *reinterpret_cast<const uint4*>(qp + d8);
+        if (!(ir < N && hr < nh)) qc = make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(s_q + r * Lds::kKStride + d8) = qc;
+    }
     // this lane's query row (S^T column): row r = 16 w + l16
     const int rq = 16 * w + l16;
     const int iq = rq % NPH, hq = rq / NPH;
     const bool vq = iq < N && hq < nh;
-    abf16x8_t qreg[kDS];
-    {
-        const uint16_t* qp = a.q + ((static_cast<size_t>(b) * N + min(iq, N - 1)) * a.Hq + h0 + min(hq, nh - 1)) * D;
-#pragma unroll
-        for (int ds = 0; ds < kDS; ++ds) {
-            uint4 u = *reinterpret_cast<const uint4*>(qp + ds * 32 + 8 * lg);
-            if (!vq) u = make_uint4(0u, 0u, 0u, 0u);
-            qreg[ds] = __builtin_bit_cast(abf16x8_t, u);
-        }
-    }
     // the candidates visible to each node: its own row and its ancestors';
     // the rows some node occupies (the others may hold anything)
     uint64_t my_vis = 0ull, used = ~0ull;
@@ -157,39 +165,77 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
 
     const int ntiles = (hi - lo + kTileKeys - 1) / kTileKeys;
     constexpr int kChunks = kTileKeys * D / 8;  // 16-byte chunks of a K (or V) tile
-    for (int tile = 0; tile < ntiles; ++tile) {
-        const int key0 = lo + tile * kTileKeys;
-        // stage the tile: K row-major, V transposed (value row d holds the
-        // tile's keys in order).  Keys no row may see (past the partition,
-        // or candidate rows no node occupies) are staged as zeros: their
-        // weights are 0, and 0 times whatever the cache holds there must
-        // not reach the output.  The masks here and below are computed
-        // without branches: the scores are read from the matrix-core
-        // results right after them, and code between the two stays one
-        // basic block (a read in a later block after a branch got stale
-        // results here)
+    constexpr int kU = kChunks / kAThreads;     // chunks per lane
+    // a tile's keys and values in registers: the next tile's loads are issued
+    // before the current tile's matrix work, so the two overlap
+    // chunk c of a tile: keys row-contiguous (key c / (D/8)); values key-fastest
+    // (key c % 32), so that the lanes of a wave write consecutive keys of one
+    // transposed value row
+    uint4 kc[kU], vc[kU];
+    auto load_tile = [&](int key0) {
 #pragma unroll
-        for (int u = 0; u < kChunks / kAThreads; ++u) {
+        for (int u = 0; u < kU; ++u) {
             const int c = tid + u * kAThreads;
             const int kk = c / (D / 8), d8 = (c % (D / 8)) * 8;
-            const int key = key0 + kk;
-            const size_t pos = static_cast<size_t>(min(key, a.S - 1));
-            const size_t off = ((static_cast<size_t>(b) * a.S + pos) * a.Hkv + g) * D + d8;
-            uint4 kc = *reinterpret_cast<const uint4*>(a.k + off);
-            uint4 vc = *reinterpret_cast<const uint4*>(a.v + off);
+            const int vk = c % kTileKeys, vd8 = (c / kTileKeys) * 8;
+            const size_t kpos = static_cast<size_t>(min(key0 + kk, a.S - 1));
+            const size_t vpos = static_cast<size_t>(min(key0 + vk, a.S - 1));
+            kc[u] = *reinterpret_cast<const uint4*>(a.k + ((static_cast<size_t>(b) * a.S + kpos) * a.Hkv + g) * D + d8);
+            vc[u] = *reinterpret_cast<const uint4*>(a.v + ((static_cast<size_t>(b) * a.S + vpos) * a.Hkv + g) * D + vd8);
+        }
+    };
+    // stage a tile from the registers into buffer `buf`: K row-major, V
+    // transposed (value row d holds the tile's keys in order).  Keys no row
+    // may see (past the partition, or candidate rows no node occupies) are
+    // staged as zeros: their weights are 0, and 0 times whatever the cache
+    // holds there must not reach the output.  The masks here and below are
+    // computed without branches: the scores are read from the matrix-core
+    // results right after them, and code between the two stays one basic
+    // block (a read in a later block after a branch got stale results here)
+    auto stage = [&](int key0, int buf) {
+        uint16_t* sk = s_k + buf * (Lds::kBuf / 2);
+        uint16_t* svt = s_vt + buf * (Lds::kBuf / 2);
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int c = tid + u * kAThreads;
+            const int kk = c / (D / 8), d8 = (c % (D / 8)) * 8;
+            const int vk = c % kTileKeys, vd8 = (c / kTileKeys) * 8;
+            const int key = key0 + kk, vkey = key0 + vk;
             const int sh = tree ? ((key - L) & 63) : 0;
+            const int vsh = tree ? ((vkey - L) & 63) : 0;
             const uint32_t keep = ((key < hi) & (((used >> sh) & 1ull) != 0ull)) ? 0xffffffffu : 0u;
-            kc.x &= keep; kc.y &= keep; kc.z &= keep; kc.w &= keep;
-            vc.x &= keep; vc.y &= keep; vc.z &= keep; vc.w &= keep;
-            *reinterpret_cast<uint4*>(s_k + kk * Lds::kKStride + d8) = kc;
-            const uint32_t vw[4] = {vc.x, vc.y, vc.z, vc.w};
+            const uint32_t vkeep = ((vkey < hi) & (((used >> vsh) & 1ull) != 0ull)) ? 0xffffffffu : 0u;
+            const uint4 kw = make_uint4(kc[u].x & keep, kc[u].y & keep, kc[u].z & keep, kc[u].w & keep);
+            const uint32_t vw[4] = {vc[u].x & vkeep, vc[u].y & vkeep, vc[u].z & vkeep, vc[u].w & vkeep};
+            *reinterpret_cast<uint4*>(sk + kk * Lds::kKStride + d8) = kw;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                s_vt[(d8 + 2 * e) * Lds::kVStride + kk] = static_cast<uint16_t>(vw[e] & 0xffffu);
-                s_vt[(d8 + 2 * e + 1) * Lds::kVStride + kk] = static_cast<uint16_t>(vw[e] >> 16);
+                svt[(vd8 + 2 * e) * Lds::kVStride + vk] = static_cast<uint16_t>(vw[e] & 0xffffu);
+                svt[(vd8 + 2 * e + 1) * Lds::kVStride + vk] = static_cast<uint16_t>(vw[e] >> 16);
             }
         }
-        __syncthreads();
+    };
+    // two LDS buffers: while the waves work on tile t in one, tile t + 1 is
+    // staged into the other and tile t + 2 is on its way into registers
+    if (ntiles > 0) {
+        load_tile(lo);
+        stage(lo, 0);
+        load_tile(lo + kTileKeys);
+    }
+    __syncthreads();  // queries and the first tile staged
+    abf16x8_t qreg[kDS];  // this lane's query row, as the B operand of S^T
+#pragma unroll
+    for (int ds = 0; ds < kDS; ++ds)
+        qreg[ds] = *reinterpret_cast<const abf16x8_t*>(s_q + rq * Lds::kKStride + ds * 32 + 8 * lg);
+    for (int tile = 0; tile < ntiles; ++tile) {
+        const int key0 = lo + tile * kTileKeys;
+        const int cur = tile & 1;
+        if (tile + 1 < ntiles) stage(key0 + kTileKeys, cur ^ 1);  // uniform
+        // clamped positions: past the last tile these re-read valid memory
+        // and are never staged
+        load_tile(key0 + 2 * kTileKeys);
+        const uint16_t* s_kc = s_k + cur * (Lds::kBuf / 2);
+        const uint16_t* s_vc = s_vt + cur * (Lds::kBuf / 2);
 
         // S^T blocks: lane (lg, l16) holds keys 16 kb + 4 lg + i of query row rq
         float s[2][4];
@@ -199,7 +245,7 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
 #pragma unroll
             for (int ds = 0; ds < kDS; ++ds) {
                 const abf16x8_t ka = *reinterpret_cast<const abf16x8_t*>(
-                    s_k + (kb * 16 + l16) * Lds::kKStride + ds * 32 + 8 * lg);
+                    s_kc + (kb * 16 + l16) * Lds::kKStride + ds * 32 + 8 * lg);
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qreg[ds], acc, 0, 0, 0);
             }
 #pragma unroll
@@ -261,14 +307,14 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
         const abf16x8_t pa_lo = __builtin_bit_cast(abf16x8_t, make_uint4(pl[0], pl[1], pl[2], pl[3]));
 #pragma unroll
         for (int db = 0; db < kDB; ++db) {
-            const uint16_t* vr = s_vt + (db * 16 + l16) * Lds::kVStride + 4 * lg;
+            const uint16_t* vr = s_vc + (db * 16 + l16) * Lds::kVStride + 4 * lg;
             const uint2 v0 = *reinterpret_cast<const uint2*>(vr);
             const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16);
             const abf16x8_t vb = __builtin_bit_cast(abf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
             o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, vb, o[db], 0, 0, 0);
             o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, vb, o[db], 0, 0, 0);
         }
-        __syncthreads();  // the next tile overwrites the staged keys and values
+        __syncthreads();  // tile t + 1 staged; tile t's buffer free for tile t + 2
     }
 
     // partial results: O rows 4 lg + i of this wave, maximum and sum of row rq
@@ -305,8 +351,10 @@ __global__ void __launch_bounds__(D) tree_attn_merge_kernel(const AttnArgs a) {
     const size_t per_split = static_cast<size_t>(a.B) * a.Hq * N;
     const int nsp = a.splits + 1;
     float M = -INFINITY;
+#pragma unroll 8
     for (int s = 0; s < nsp; ++s) M = fmaxf(M, a.ws_ml[(s * per_split + row) * 2]);
     float acc = 0.f, den = 0.f;
+#pragma unroll 8
     for (int s = 0; s < nsp; ++s) {
         const float* ml = a.ws_ml + (s * per_split + row) * 2;
         const float wgt = __builtin_amdgcn_exp2f(ml[0] - M);  // 0 for an empty partition
@@ -335,7 +383,7 @@ hipError_t launch_tree_attention(const gdn_tree_desc& d, const TreeAttnArgs& ta,
     a.Hq = ta.Hq;
     a.Hkv = ta.Hkv;
     a.splits = ta.splits;
-    a.HPW = d.N <= 32 ? 2 : 1;
+    a.HPW = d.N <= 32 ? 4 : 2;  // query heads per workgroup (kRows rows)
     const int G = ta.Hq / ta.Hkv;
     a.pairs = (G + a.HPW - 1) / a.HPW;
     a.shared = d.shared;
@@ -361,9 +409,17 @@ hipError_t launch_tree_attention(const gdn_tree_desc& d, const TreeAttnArgs& ta,
     const unsigned units = static_cast<unsigned>(d.B) * ta.Hkv * (ta.splits + 1) * a.pairs;
     const unsigned mrows = static_cast<unsigned>(d.B) * ta.Hq * d.N;
     if (ta.D == 128) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(tree_attn_kernel<128>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 static_cast<int>(AttnLds<128>::total));
+        if (e != hipSuccess) return e;
         hipLaunchKernelGGL(tree_attn_kernel<128>, dim3(units), dim3(kAThreads), AttnLds<128>::total, s, a);
         hipLaunchKernelGGL(tree_attn_merge_kernel<128>, dim3(mrows), dim3(128), 0, s, a);
     } else if (ta.D == 256) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(tree_attn_kernel<256>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 static_cast<int>(AttnLds<256>::total));
+        if (e != hipSuccess) return e;
         hipLaunchKernelGGL(tree_attn_kernel<256>, dim3(units), dim3(kAThreads), AttnLds<256>::total, s, a);
         hipLaunchKernelGGL(tree_attn_merge_kernel<256>, dim3(mrows), dim3(256), 0, s, a);
     } else {
