@@ -176,6 +176,20 @@ def library_source_hash():
     return h.hexdigest()[:16]
 
 
+def measured_traffic_sum(workload, mode, prefix):
+    """HBM bytes of one call of every kernel whose name starts with ``prefix``
+    (summed), from the committed counter summary, or None (as below)."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_{mode}_hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha256_16") != library_source_hash():
+        return None
+    tot = [k["traffic_bytes"] for name, k in rec["kernels"].items() if name.startswith(prefix)]
+    return int(round(sum(tot))) if tot else None
+
+
 def measured_traffic(workload, mode, stage):
     """HBM bytes per launch of ``stage``'s kernel from the committed counter
     summary (FETCH_SIZE and WRITE_SIZE passes, scaled by a known-size copy),
@@ -564,8 +578,11 @@ def run_attention(args, g, torch, dev):
                    "value_is": "tree nodes attended per second per attention layer",
                    "global_batch": B, "nodes_per_request": N, "parallelism": "single GPU",
                    "step_bytes": int(byts), "step_gflop": round(flops / 1e9, 2)},
-        "roofline": dict(bound="hbm", kernel="tree_attention", achieved=round(achieved, 1), peak=PEAK_HBM_GBS,
-                         unit="GB/s", frac=round(achieved / PEAK_HBM_GBS, 4), traffic=None,
+        "roofline": dict(bound="hbm", kernel="tree_attention (partitions + merge launches)",
+                         achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                         frac=round(achieved / PEAK_HBM_GBS, 4),
+                         traffic=(measured_traffic_sum("tree27_ctx64k", "attention", "gdn::tree_attn")
+                                  if (B, args.ctx, splits) == (1, 65536, 63) else None),
                          avg_us=round(ms * 1e3, 2), algorithmic_bytes=int(byts)),
         "cpu_baseline": cpu,
     }
