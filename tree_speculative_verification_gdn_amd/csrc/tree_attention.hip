@@ -239,15 +239,22 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
 
         // S^T blocks: lane (lg, l16) holds keys 16 kb + 4 lg + i of query row rq
         float s[2][4];
+        // four independent accumulation chains (block x even/odd d step) keep
+        // the matrix pipeline busy instead of waiting on one chain
+        af32x4_t acc4[2][2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            af32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (int kb = 0; kb < 2; ++kb) acc4[kb][0] = acc4[kb][1] = af32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ds = 0; ds < kDS; ++ds) {
+        for (int ds = 0; ds < kDS; ++ds)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
                 const abf16x8_t ka = *reinterpret_cast<const abf16x8_t*>(
                     s_kc + (kb * 16 + l16) * Lds::kKStride + ds * 32 + 8 * lg);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qreg[ds], acc, 0, 0, 0);
+                acc4[kb][ds & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qreg[ds], acc4[kb][ds & 1], 0, 0, 0);
             }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const af32x4_t acc = acc4[kb][0] + acc4[kb][1];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 // branch-free: visible if inside the partition and (for the
@@ -305,14 +312,26 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
         }
         const abf16x8_t pa_hi = __builtin_bit_cast(abf16x8_t, make_uint4(ph[0], ph[1], ph[2], ph[3]));
         const abf16x8_t pa_lo = __builtin_bit_cast(abf16x8_t, make_uint4(pl[0], pl[1], pl[2], pl[3]));
+        // value operands for eight d blocks at a time, then the hi products
+        // of all eight, then the lo products (independent accumulators back
+        // to back)
+        constexpr int kDBH = kDB < 8 ? kDB : 8;
 #pragma unroll
-        for (int db = 0; db < kDB; ++db) {
-            const uint16_t* vr = s_vc + (db * 16 + l16) * Lds::kVStride + 4 * lg;
-            const uint2 v0 = *reinterpret_cast<const uint2*>(vr);
-            const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16);
-            const abf16x8_t vb = __builtin_bit_cast(abf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
-            o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, vb, o[db], 0, 0, 0);
-            o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, vb, o[db], 0, 0, 0);
+        for (int d0 = 0; d0 < kDB; d0 += kDBH) {
+            abf16x8_t vb[kDBH];
+#pragma unroll
+            for (int j = 0; j < kDBH; ++j) {
+                const uint16_t* vr = s_vc + ((d0 + j) * 16 + l16) * Lds::kVStride + 4 * lg;
+                const uint2 v0 = *reinterpret_cast<const uint2*>(vr);
+                const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16);
+                vb[j] = __builtin_bit_cast(abf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
+            }
+#pragma unroll
+            for (int j = 0; j < kDBH; ++j)
+                o[d0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, vb[j], o[d0 + j], 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < kDBH; ++j)
+                o[d0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, vb[j], o[d0 + j], 0, 0, 0);
         }
         __syncthreads();  // tile t + 1 staged; tile t's buffer free for tile t + 2
     }
