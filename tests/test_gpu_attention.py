@@ -91,8 +91,8 @@ def test_partition_counts_agree(splits):
     _cmp(go, oo)
 
 
-def test_wide_tree_one_head_per_workgroup():
-    # N > 32: 64 query rows of one head per workgroup
+def test_wide_tree_two_heads_per_workgroup():
+    # N > 32: the N rows of two query heads per workgroup
     c = gi.make_attention_case(14, B=2, N=40, R=48, Hq=4, Hkv=4, D=128, ctx=[64, 250], S=320,
                                bmax=4, depth_max=8)
     go, err, st = run_attention(c, splits=4)
@@ -199,3 +199,16 @@ def test_repeat_runs_are_bit_identical():
         if splits == 1:
             assert np.array_equal(again, first)
         _cmp(again, oo)
+
+
+@pytest.mark.parametrize("N,R,ctx", [(1, 1, [0, 3]), (64, 64, [37, 0]), (32, 64, [100, 1])])
+def test_node_count_edges(N, R, ctx):
+    # a single node (its own key, or the prefix and itself), the largest tree
+    # (64 nodes in 64 rows, two heads filling a workgroup's 128 query rows)
+    # and 32 nodes spread over 64 rows
+    c = gi.make_attention_case(20 + N, B=2, N=N, R=R, Hq=4, Hkv=2, D=128, ctx=ctx, S=max(ctx) + R + 5,
+                               bmax=4, depth_max=12)
+    go, err, st = run_attention(c, splits=3)
+    oo, oerr = oracle(c, st)
+    assert err == oerr == 0
+    _cmp(go, oo)

@@ -4,11 +4,11 @@
 // names the mask's key columns; grouped query heads share staged KV tiles;
 // the context is split into partitions for parallel work at small batch).
 //
-// Attention: one 256-thread workgroup per (request, kv head, pair of query
+// Attention: one 512-thread workgroup per (request, kv head, group of query
 // heads, key partition).  Partitions 0..splits-1 cover the committed prefix
 // in equal ranges; partition `splits` covers the R candidate slots under the
-// ancestry mask.  A workgroup holds up to 64 query rows (the N nodes of two
-// heads, or of one head when N > 32), 16 per wave, and walks its keys in
+// ancestry mask.  A workgroup holds up to 128 query rows (the N nodes of four
+// heads, or of two heads when N > 32), 16 per wave, and walks its keys in
 // tiles of 32: the tile's keys row-major and its values transposed go to LDS,
 // S^T = K Q^T runs on v_mfma_f32_16x16x32_bf16 (a wave's lane holds one query
 // row's scores for four keys per 16-key block), an online softmax keeps each
