@@ -155,6 +155,34 @@ def test_node_count_edges(N, bmax, depth):
     _cmp_pool(case, gr, orr)
 
 
+def test_wide_tree_every_depth_class():
+    # 64 nodes: a 24-node spine with 40 leaves hung at depths 7 .. 24, so the
+    # M solve meets nodes of path length <= 8, more than 16 of length 9 .. 16
+    # (two rounds of 16-lane groups) and longer ones (one thread per node);
+    # each request commits the root chain of one of its leaves
+    cfg = gi.CONFIGS[3].replace(N=64, R=67, bmax=64, depth_max=30, B=4)
+    case = gi.make_case(cfg, seed=64, extra_slots=1)
+    rng = np.random.default_rng(64)
+    for b in range(cfg.B):
+        par = np.arange(-1, 63, dtype=np.int32)
+        par[24:] = rng.integers(6, 24, 40)
+        case["parent"][b] = par
+        chain, i = [], int(rng.integers(24, 64))
+        while i >= 0:
+            chain.append(i)
+            i = int(par[i])
+        case["path"][b] = -1
+        case["path"][b, :len(chain)] = chain[::-1]
+        case["path_len"][b] = len(chain)
+    gr, orr = run_gpu(case), run_oracle(case)
+    d = orr["depth"]
+    assert (((d > 8) & (d <= 16)).sum(axis=1) > 16).all() and (d > 16).any(axis=1).all()
+    _cmp_desc(gr, orr)
+    assert gr["err"] == orr["err"] == 0
+    _cmp_out(case, gr, orr)
+    _cmp_pool(case, gr, orr)
+
+
 def test_forest_and_len0_paths():
     cfg = gi.CONFIGS[3].replace(B=6)
     case = gi.make_case(cfg, seed=3, extra_slots=1)

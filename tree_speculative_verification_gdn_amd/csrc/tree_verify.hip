@@ -881,10 +881,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
         //     decay ratios taken as products of the decays strictly below j.  A group
         //     of kLP lanes holds one node, lane p its path position p: each lane forms
         //     its G column, then the deepest position is final and is eliminated from
-        //     the shallower ones, one position per step.  Nodes deeper than kLP are
-        //     solved one thread per node afterwards.
+        //     the shallower ones, one position per step.  In trees of more than
+        //     32 nodes, nodes of depth 9..16 go through the same in groups of 16
+        //     lanes; deeper ones are solved one thread per node afterwards.
         {
             constexpr int kLP = 8;
+            // wide trees only: at N <= 32 the 16-lane groups' registers would
+            // spill in the kernels capped at 128 VGPRs
+            constexpr int kLP2 = NPB == 1 ? kLP : 16;
             const int p = tid & (kLP - 1);
             const int grp_lane0 = lane & ~(kLP - 1);
             for (int i0 = 0; i0 < N; i0 += kThreads / kLP) {
@@ -924,9 +928,56 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                     }
                 }
             }
-            // nodes deeper than kLP: one thread per node, the same elimination in
+            if constexpr (kLP2 > kLP) {
+                // the nodes of depth kLP+1 .. kLP2 (a mask every wave forms
+                // alike), one per group of kLP2 lanes, as above
+                const int dl = s_dep[min(lane, N - 1)];
+                const uint64_t deep = __ballot(lane < N && dl > kLP && dl <= kLP2);
+                const int ndeep = __popcll(deep);
+                const int p2 = tid & (kLP2 - 1);
+                const int grp2 = lane & ~(kLP2 - 1);
+                for (int q0 = 0; q0 < ndeep; q0 += kThreads / kLP2) {  // uniform
+                    const int qi = q0 + tid / kLP2;
+                    uint64_t dm = deep;
+                    for (int c = 0; c < min(qi, ndeep - 1); ++c) dm &= dm - 1ull;
+                    const int i = __builtin_ctzll(dm);  // the qi-th deep node
+                    const int d = s_dep[i];
+                    const bool act = qi < ndeep && p2 < d;
+                    const uint8_t* path = s_cidx + i * N;
+                    const int j = path[min(p2, d - 1)];
+                    const float sk_j = s_sk[j];
+                    float gco[kLP2];
+                    float r = 1.0f;
+    #pragma unroll
+                    for (int sp = 1; sp < kLP2; ++sp) {
+                        const bool in = sp > p2 && sp < d;
+                        const int m = path[min(sp, d - 1)];
+                        r *= in ? s_al[m] : 1.0f;
+                        gco[sp] = in ? s_be[m] * s_sk[m] * sk_j * s_gk[m * (m + 1) / 2 + j] * r : 0.0f;
+                    }
+                    float val = r * s_sq[i] * sk_j * s_gq[i * (i + 1) / 2 + j];
+    #pragma unroll
+                    for (int sp = kLP2 - 1; sp >= 1; --sp) {
+                        const float ms = __shfl(val, grp2 | sp, 64);
+                        val = (sp < d && p2 < sp) ? fmaf(-ms, gco[sp], val) : val;
+                    }
+                    if (act) {
+                        const uint32_t hv = cvt_pk_bf16(val, 0.0f) & 0xffffu;
+                        const float rest = val - __uint_as_float(hv << 16);
+                        const uint32_t lv = cvt_pk_bf16(rest, 0.0f) & 0xffffu;
+                        reinterpret_cast<uint16_t*>(s_mh + i * mstride)[j] = static_cast<uint16_t>(hv);
+                        reinterpret_cast<uint16_t*>(s_ml + i * mstride)[j] = static_cast<uint16_t>(lv);
+                        if (p2 == 0) {
+                            const float P_i = r * s_al[j];
+                            s_cr[i] = P_i * s_sk[i];
+                            s_cq[i] = P_i * s_sq[i];
+                        }
+                    }
+                }
+            }
+            // nodes deeper than kLP2: one thread per node, the same elimination in
             // place (M values so far read back from their hi + lo halves)
-            if (tid < N && s_dep[tid] > kLP) {
+            if (tid < N && s_dep[tid] > kLP2) {
                 const int i = tid;
                 const int d = s_dep[i];
                 const uint8_t* path = s_cidx + i * N;
