@@ -84,8 +84,15 @@ __host__ __device__ inline MfmaLds mfma_lds_layout(int N, int NPB, int Lp = 0) {
     // per-node arrays written by every lane carry one spare entry (index N)
     L.be = off;   off += align_up((N + 1) * 4, 16);
     L.rows = off; off += align_up((N + 1) * 4, 16);
-    L.mh = off;   off += align_up(NP * L.mstride, 16);
-    L.ml = off;   off += align_up(NP * L.mstride, 16);
+    if (NPB == 1) {
+        L.mh = off;   off += align_up(NP * L.mstride, 16);
+        L.ml = off;   off += align_up(NP * L.mstride, 16);
+    } else {
+        // wide trees: M is solved in place of the q.k triangle (fp32) and read
+        // from it, masked by the ancestor bits, as the readout's operand
+        L.gq = off;   off += align_up(T * 4, 16);
+        L.anc = off;  off += align_up((N + 1) * 8, 16);
+    }
     L.cr = off;   off += align_up(N * 4, 16);      // P_i / |k_i|
     L.cq = off;   off += align_up(N * 4, 16);      // P_i / |q_i|
     // the previous path's rows are written at the start, so they get space of their own
@@ -97,19 +104,23 @@ __host__ __device__ inline MfmaLds mfma_lds_layout(int N, int NPB, int Lp = 0) {
     const int U = off;
     int f = U;
     L.gk = f;   f += align_up(T * 4, 16);   // k_i . k_j (raw operands), row-major lower triangle
-    L.gq = f;   f += align_up(T * 4, 16);   // q_i . k_j
+    if (NPB == 1) {
+        L.gq = f;   f += align_up(T * 4, 16);   // q_i . k_j
+    }
     L.nrm = f;  f += align_up(2 * NP * 4, 16);   // squared norms by slot
     L.sk = f;   f += align_up(N * 4, 16);
     L.sq = f;   f += align_up(N * 4, 16);
     L.al = f;   f += align_up((N + 1) * 4, 16);
     L.dep = f;  f += align_up((N + 1) * 4, 16);
-    L.anc = f;  f += align_up((N + 1) * 8, 16);
-    L.cidx = f; f += align_up(N * N, 16);        // [i][p]: node at depth p+1 on i's root path
+    if (NPB == 1) {
+        L.anc = f;  f += align_up((N + 1) * 8, 16);
+    }
+    if (NPB == 1) {
+        L.cidx = f; f += align_up(N * N, 16);    // [i][p]: node at depth p+1 on i's root path
+    }
     int uend = f;
     f = U;
-    if (NPB != 1) {
-        L.v = f;  f += align_up(N * kD * 2, 16);
-    }
+    if (NPB != 1) L.v = L.a;  // staged after the state contraction, the block's last use
     const int gsz = lp > 0 ? kMfmaPath * kMfmaPath * 4 : 0;
     L.kp = f;   f += align_up(lp * kKQStride, 16);
     L.vp = f;   f += align_up(lp * kD * 2, 16);
@@ -289,6 +300,17 @@ __device__ __forceinline__ void split_hi_lo(const float4& x0, const float4& x1, 
     lo = __builtin_bit_cast(bf16x8_t, make_uint4(l[0], l[1], l[2], l[3]));
 }
 
+// Root path as a bit mask of node indexes (ancestors have smaller indexes, so
+// the set bits in ascending order are the path from its root-level node):
+// the node at position q, for q below the path length.
+template <int KMAX>
+__device__ __forceinline__ int path_node(uint64_t pm, int q) {
+#pragma unroll
+    for (int c = 0; c < KMAX - 1; ++c)
+        if (c < q) pm &= pm - 1ull;
+    return __builtin_ctzll(pm | (1ull << 63));
+}
+
 __device__ __forceinline__ float sumsq_bf16x4(uint2 u) {
     const float a = __uint_as_float(u.x << 16), b = __uint_as_float(u.x & 0xffff0000u);
     const float c = __uint_as_float(u.y << 16), d = __uint_as_float(u.y & 0xffff0000u);
@@ -327,7 +349,7 @@ __device__ __forceinline__ bf16x8_t lds_operand_m(const char* base, int stride, 
 }
 
 template <int NPB, int MODE, int CW, bool RAW>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NPB == 1 ? 4 : 2, 8)))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NPB == 1 ? 4 : 3, 8)))
     verify_mfma_kernel(int N, int R, int shared, const int32_t* __restrict__ node_row,
                        const uint64_t* __restrict__ anc_g, const int32_t* __restrict__ depth_g,
                        const int32_t* __restrict__ status, const uint16_t* __restrict__ q,
@@ -793,10 +815,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                 s_be[slot_i] = my_be;
             }
         }
-        // M halves start as zero (entries off the ancestor pattern stay zero)
-        for (int e = tid; e < NP * mstride / 4; e += kThreads) {
-            reinterpret_cast<uint32_t*>(s_mh)[e] = 0u;
-            reinterpret_cast<uint32_t*>(s_ml)[e] = 0u;
+        if constexpr (NPB == 1) {
+            // M halves start as zero (entries off the ancestor pattern stay zero)
+            for (int e = tid; e < NP * mstride / 4; e += kThreads) {
+                reinterpret_cast<uint32_t*>(s_mh)[e] = 0u;
+                reinterpret_cast<uint32_t*>(s_ml)[e] = 0u;
+            }
         }
         if constexpr (LAYER) {  // K/Q/V rows are staged; squared norms from them
     #pragma unroll
@@ -838,14 +862,16 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
         if (tid < N) {
             s_sk[tid] = norm ? 1.0f / sqrtf(s_nrm[tid] + 1e-6f) : 1.0f;
             s_sq[tid] = norm ? 1.0f / sqrtf(s_nrm[NP + tid] + 1e-6f) : 1.0f;
-            uint64_t m = s_anc[tid];
-            int p = 0;
-            while (m) {  // ancestors in index order are root first
-                const int j = __builtin_ctzll(m);
-                m &= m - 1ull;
-                s_cidx[tid * N + p++] = static_cast<uint8_t>(j);
+            if constexpr (NPB == 1) {  // wide trees read the paths from the ancestor bits
+                uint64_t m = s_anc[tid];
+                int p = 0;
+                while (m) {  // ancestors in index order are root first
+                    const int j = __builtin_ctzll(m);
+                    m &= m - 1ull;
+                    s_cidx[tid * N + p++] = static_cast<uint8_t>(j);
+                }
+                s_cidx[tid * N + p] = static_cast<uint8_t>(tid);
             }
-            s_cidx[tid * N + p] = static_cast<uint8_t>(tid);
         }
 
         // (c) Gram block on the matrix cores (exact bf16 products, fp32 sums):
@@ -897,14 +923,25 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                 const int d = s_dep[ii];
                 const bool act = i < N && d <= kLP && p < d;
                 const uint8_t* path = s_cidx + ii * N;
-                const int j = path[min(p, d - 1)];
+                // wide trees: the path from the ancestor bits (running mask)
+                const uint64_t pm = (NPB == 1) ? 0ull : (s_anc[ii] | (1ull << ii));
+                uint64_t pr = pm;
+                int j;
+                if constexpr (NPB == 1) j = path[min(p, d - 1)];
+                else j = path_node<kLP>(pm, min(p, d - 1));
                 const float sk_j = s_sk[j];
                 float gco[kLP];
                 float r = 1.0f;  // decays of positions p+1 .. s
     #pragma unroll
                 for (int sp = 1; sp < kLP; ++sp) {
                     const bool in = sp > p && sp < d;
-                    const int m = path[min(sp, d - 1)];
+                    int m;
+                    if constexpr (NPB == 1) {
+                        m = path[min(sp, d - 1)];
+                    } else {
+                        pr &= pr - 1ull;  // drops position sp - 1
+                        m = sp < d ? __builtin_ctzll(pr | (1ull << 63)) : ii;
+                    }
                     r *= in ? s_al[m] : 1.0f;
                     gco[sp] = in ? s_be[m] * s_sk[m] * sk_j * s_gk[m * (m + 1) / 2 + j] * r : 0.0f;
                 }
@@ -916,11 +953,15 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                     val = (sp < d && p < sp) ? fmaf(-ms, gco[sp], val) : val;
                 }
                 if (act) {
-                    const uint32_t hv = cvt_pk_bf16(val, 0.0f) & 0xffffu;
-                    const float rest = val - __uint_as_float(hv << 16);
-                    const uint32_t lv = cvt_pk_bf16(rest, 0.0f) & 0xffffu;
-                    reinterpret_cast<uint16_t*>(s_mh + i * mstride)[j] = static_cast<uint16_t>(hv);
-                    reinterpret_cast<uint16_t*>(s_ml + i * mstride)[j] = static_cast<uint16_t>(lv);
+                    if constexpr (NPB == 1) {
+                        const uint32_t hv = cvt_pk_bf16(val, 0.0f) & 0xffffu;
+                        const float rest = val - __uint_as_float(hv << 16);
+                        const uint32_t lv = cvt_pk_bf16(rest, 0.0f) & 0xffffu;
+                        reinterpret_cast<uint16_t*>(s_mh + i * mstride)[j] = static_cast<uint16_t>(hv);
+                        reinterpret_cast<uint16_t*>(s_ml + i * mstride)[j] = static_cast<uint16_t>(lv);
+                    } else {
+                        s_gq[i * (i + 1) / 2 + j] = val;  // only this lane reads that entry
+                    }
                     if (p == 0) {
                         const float P_i = r * s_al[j];  // j = n_0: times the root-level decay
                         s_cr[i] = P_i * s_sk[i];
@@ -943,15 +984,17 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                     const int i = __builtin_ctzll(dm);  // the qi-th deep node
                     const int d = s_dep[i];
                     const bool act = qi < ndeep && p2 < d;
-                    const uint8_t* path = s_cidx + i * N;
-                    const int j = path[min(p2, d - 1)];
+                    const uint64_t pm = s_anc[i] | (1ull << i);
+                    uint64_t pr = pm;
+                    const int j = path_node<kLP2>(pm, min(p2, d - 1));
                     const float sk_j = s_sk[j];
                     float gco[kLP2];
                     float r = 1.0f;
     #pragma unroll
                     for (int sp = 1; sp < kLP2; ++sp) {
                         const bool in = sp > p2 && sp < d;
-                        const int m = path[min(sp, d - 1)];
+                        pr &= pr - 1ull;
+                        const int m = sp < d ? __builtin_ctzll(pr | (1ull << 63)) : i;
                         r *= in ? s_al[m] : 1.0f;
                         gco[sp] = in ? s_be[m] * s_sk[m] * sk_j * s_gk[m * (m + 1) / 2 + j] * r : 0.0f;
                     }
@@ -962,11 +1005,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                         val = (sp < d && p2 < sp) ? fmaf(-ms, gco[sp], val) : val;
                     }
                     if (act) {
-                        const uint32_t hv = cvt_pk_bf16(val, 0.0f) & 0xffffu;
-                        const float rest = val - __uint_as_float(hv << 16);
-                        const uint32_t lv = cvt_pk_bf16(rest, 0.0f) & 0xffffu;
-                        reinterpret_cast<uint16_t*>(s_mh + i * mstride)[j] = static_cast<uint16_t>(hv);
-                        reinterpret_cast<uint16_t*>(s_ml + i * mstride)[j] = static_cast<uint16_t>(lv);
+                        s_gq[i * (i + 1) / 2 + j] = val;
                         if (p2 == 0) {
                             const float P_i = r * s_al[j];
                             s_cr[i] = P_i * s_sk[i];
@@ -976,7 +1015,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                 }
             }
             // nodes deeper than kLP2: one thread per node, the same elimination in
-            // place (M values so far read back from their hi + lo halves)
+            // place (M values so far read back from their hi + lo halves, or in
+            // wide trees from the fp32 row that holds them)
             if (tid < N && s_dep[tid] > kLP2) {
                 const int i = tid;
                 const int d = s_dep[i];
@@ -984,24 +1024,50 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                 const float sq_i = s_sq[i];
                 uint16_t* mh = reinterpret_cast<uint16_t*>(s_mh + i * mstride);
                 uint16_t* ml = reinterpret_cast<uint16_t*>(s_ml + i * mstride);
+                float* mrow = s_gq + i * (i + 1) / 2;
+                // wide trees: positions from the ancestor bits, deepest first
+                const uint64_t pm = (NPB == 1) ? 0ull : (s_anc[i] | (1ull << i));
+                uint64_t rem = pm;
                 float wq = 1.0f;  // decays of the positions below p
                 for (int pp = d - 1; pp >= 0; --pp) {
-                    const int jj = path[pp];
+                    int jj;
+                    uint64_t deeper = 0ull;  // wide trees: the positions below jj
+                    if constexpr (NPB == 1) {
+                        jj = path[pp];
+                    } else {
+                        jj = 63 - __builtin_clzll(rem);
+                        rem &= ~(1ull << jj);
+                        deeper = pm & ~(((1ull << jj) << 1) - 1ull);
+                    }
                     const float sk_j = s_sk[jj];
-                    float val = wq * sq_i * sk_j * s_gq[i * (i + 1) / 2 + jj];
+                    float val = wq * sq_i * sk_j * mrow[jj];
                     float wg = 1.0f;
                     for (int sp = pp + 1; sp < d; ++sp) {
-                        const int m = path[sp];
+                        int m;
+                        if constexpr (NPB == 1) {
+                            m = path[sp];
+                        } else {
+                            m = __builtin_ctzll(deeper | (1ull << 63));
+                            deeper &= deeper - 1ull;
+                        }
                         wg *= s_al[m];
                         const float gmj = s_be[m] * wg * s_sk[m] * sk_j * s_gk[m * (m + 1) / 2 + jj];
-                        const float msv = bf16_bits_to_f32(mh[m]) + bf16_bits_to_f32(ml[m]);
+                        float msv;
+                        if constexpr (NPB == 1)
+                            msv = bf16_bits_to_f32(mh[m]) + bf16_bits_to_f32(ml[m]);
+                        else
+                            msv = mrow[m];
                         val = fmaf(-msv, gmj, val);
                     }
-                    const uint32_t hv = cvt_pk_bf16(val, 0.0f) & 0xffffu;
-                    const float rest = val - __uint_as_float(hv << 16);
-                    const uint32_t lv = cvt_pk_bf16(rest, 0.0f) & 0xffffu;
-                    mh[jj] = static_cast<uint16_t>(hv);
-                    ml[jj] = static_cast<uint16_t>(lv);
+                    if constexpr (NPB == 1) {
+                        const uint32_t hv = cvt_pk_bf16(val, 0.0f) & 0xffffu;
+                        const float rest = val - __uint_as_float(hv << 16);
+                        const uint32_t lv = cvt_pk_bf16(rest, 0.0f) & 0xffffu;
+                        mh[jj] = static_cast<uint16_t>(hv);
+                        ml[jj] = static_cast<uint16_t>(lv);
+                    } else {
+                        mrow[jj] = val;
+                    }
                     wq *= s_al[jj];
                 }
                 s_cr[i] = wq * s_sk[i];
@@ -1009,15 +1075,6 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
             }
         }
         __syncthreads();
-        if constexpr (NPB != 1) {  // V rows, over the Gram block (dead after the M solve)
-    #pragma unroll
-            for (int u = 0; u < kVItems; ++u) {
-                const int it = tid + u * kThreads;
-                const int node = it >> 5;
-                if (node < N) *reinterpret_cast<uint2*>(s_v + node * kD + (it & 31) * 4) = v_val[u];
-            }
-            __syncthreads();
-        }
     }
 
     // fused: replay the previous path into the state in registers, in this
@@ -1273,6 +1330,17 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
             acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, slo, acc[mb], 0, 0, 0);
         }
     }
+    if constexpr (NPB != 1) {
+        // V rows, over the key/query block once every wave has read it
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kVItems; ++u) {
+            const int it = tid + u * kThreads;
+            const int node = it >> 5;
+            if (node < N) *reinterpret_cast<uint2*>(s_v + node * kD + (it & 31) * 4) = v_val[u];
+        }
+        __syncthreads();
+    }
 
     // (f) R = beta (v - P k^ S_pre) from the key blocks, as bf16 hi/lo MFMA
     //     operands (a key block's output layout is a permutation of the
@@ -1312,11 +1380,27 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
             const int i = ob * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
             o[e] *= (i < N) ? s_cq[i] : 0.0f;
         }
+        // wide trees: row ob*32 + l32 of M from the triangle, zero off its root path
+        const int mr = min(ob * 32 + l32, N - 1);
+        const uint64_t mpath = (ob * 32 + l32 < N) ? (s_anc[mr] | (1ull << mr)) : 0ull;
 #pragma unroll
         for (int ks = 0; ks < 2 * NPB; ++ks) {
             if (ks > 2 * ob + 1) break;  // M is zero right of the diagonal block
-            const bf16x8_t mh = lds_operand_m(s_mh, mstride, ob * 32 + l32, ks, hf);
-            const bf16x8_t ml = lds_operand_m(s_ml, mstride, ob * 32 + l32, ks, hf);
+            bf16x8_t mh, ml;
+            if constexpr (NPB == 1) {
+                mh = lds_operand_m(s_mh, mstride, ob * 32 + l32, ks, hf);
+                ml = lds_operand_m(s_ml, mstride, ob * 32 + l32, ks, hf);
+            } else {
+                float mv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int col = 16 * ks + 4 * hf + (e & 3) + 8 * (e >> 2);
+                    const float x = s_gq[mr * (mr + 1) / 2 + min(col, mr)];
+                    mv[e] = ((mpath >> col) & 1ull) ? x : 0.0f;
+                }
+                split_hi_lo(make_float4(mv[0], mv[1], mv[2], mv[3]), make_float4(mv[4], mv[5], mv[6], mv[7]),
+                            mh, ml);
+            }
             o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mh, rhi[ks], o, 0, 0, 0);
             o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mh, rlo[ks], o, 0, 0, 0);
             o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ml, rhi[ks], o, 0, 0, 0);
