@@ -211,6 +211,20 @@ def test_out_bf16_flag():
     assert (d <= 1).mean() > 0.99
 
 
+def test_tree64_out_bf16_and_shared_topology():
+    # the wide-tree kernel with one topology for every request and bf16 outputs
+    cfg = gi.CONFIGS[5]
+    case = gi.make_case(cfg, seed=78, B=4, packing="bfs")
+    case["parent"][:] = case["parent"][0]
+    case["node_row"][:] = case["node_row"][0]
+    gr = run_gpu(case, shared=True, out_bf16=True, commit=False)
+    orr = run_oracle(case, shared=True, commit=False)
+    assert gr["err"] == orr["err"] == 0
+    m = node_rows_mask(case)
+    got = gi.bf16_bits_to_f32(gr["out"][m])
+    assert max_rel_rows(got, orr["out"][m], 2) <= TOL + 2.0 ** -9
+
+
 def test_malformed_inputs_skip_requests():
     g = _g()
     cfg = gi.CONFIGS[3].replace(B=8)

@@ -51,6 +51,12 @@ def test_verify_and_commit_tree27(valu):
     _cmp_single(case, gr, orr)
 
 
+def test_verify_and_commit_tree64():
+    # two 32-row blocks: the wide-tree kernel with the gates evaluated in it
+    case = gi.with_raw_gates(gi.make_case(gi.CONFIGS[5], seed=65, B=4))
+    _cmp_single(case, run_gpu(case), run_oracle(case))
+
+
 def test_verify_and_commit_f32_small():
     case = gi.with_raw_gates(gi.make_case(gi.CONFIGS[1], seed=62, B=3))
     _cmp_single(case, run_gpu(case), run_oracle(case))
@@ -70,7 +76,7 @@ def test_raw_gates_differ_from_taking_them_as_gates():
     assert max_rel_rows(a["out"][m], b["out"][m], 2) > 1e-2
 
 
-@pytest.mark.parametrize("cfg_id", [3, 2])
+@pytest.mark.parametrize("cfg_id", [3, 2, 5])
 def test_fused_commit_verify(cfg_id):
     c1, c2 = two_step_case(gi.CONFIGS[cfg_id], seed=64, B=5, extra_slots=1)
     r1, r2 = _raw_two_steps(c1, c2)
