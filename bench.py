@@ -613,8 +613,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build runs the path on a single MI355X; "
-              "see DESIGN.md for how it would shard. Use --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the path runs on a single MI355X, one process "
+              "and one device. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -9,8 +9,8 @@ uint16 bit patterns (round-to-nearest-even from float32).
 Workloads.  The pages measure their GDN component on synthetic operands with
 a fixed tree geometry (LumoTree, Sec. VII-D and VII-H: 48 instances, 28 active
 nodes packed in 32 rows).  The five configurations below stand in for those
-component workloads; their shapes and value distributions are the ones named
-for this build ("Inputs").
+component workloads; their shapes and value distributions are stated with
+each configuration below.
 
 Random streams: NumPy PCG64 seeded with SeedSequence([seed, cfg, layer,
 stream]).  Trees use layer 0 so that every layer of a multi-layer config

@@ -29,9 +29,8 @@
  *    convolution history, taps applied oldest to newest, unused history kept
  *    as padding (LumoTree, Sec. V-C).
  *
- * Readings where the pages are silent are listed in the design doc; the ones that
- * shape this file: parent -1 means "child of the committed state"; q/k
- * normalisation (when asked for) is x / sqrt(sum x^2 + 1e-6); gates a, b are
+ * Where the pages are silent this file reads them as follows: parent -1
+ * means "child of the committed state"; q/k normalisation (when asked for) is x / sqrt(sum x^2 + 1e-6); gates a, b are
  * given post-activation; no 1/sqrt(d_k) query scale; value head h reads qk
  * head floor(h * Hqk / Hv).
  *
