@@ -30,9 +30,9 @@
  *    as padding (LumoTree, Sec. V-C).
  *
  * Where the pages are silent this file reads them as follows: parent -1
- * means "child of the committed state"; q/k normalisation (when asked for) is x / sqrt(sum x^2 + 1e-6); gates a, b are
- * given post-activation; no 1/sqrt(d_k) query scale; value head h reads qk
- * head floor(h * Hqk / Hv).
+ * means "child of the committed state"; q/k normalisation (when asked for)
+ * is x / sqrt(sum x^2 + 1e-6); gates a, b are given post-activation; no
+ * 1/sqrt(d_k) query scale; value head h reads qk head floor(h * Hqk / Hv).
  *
  * Parity pins live in tests/test_oracle_pins.py and tests/test_oracle_bruteforce.py.
  *
