@@ -156,7 +156,8 @@ __global__ void __launch_bounds__(64) path_resolve_kernel(const ResolveArgs a, i
 }
 
 // One launch for a step's shared work: the new tree's descriptor (workgroups
-// t < T) and the previous path's rows (workgroups b < B).
+// t < T) and the previous path's rows (workgroups T + b), side by side: the
+// two are independent, so neither waits for the other's memory round trips.
 __global__ void __launch_bounds__(64) step_prepare_kernel(int T, int N, int R, int W,
                                                           const int32_t* __restrict__ parent,
                                                           const int32_t* __restrict__ node_row,
@@ -167,7 +168,8 @@ __global__ void __launch_bounds__(64) step_prepare_kernel(int T, int N, int R, i
                                                           const ResolveArgs a, int32_t* __restrict__ err) {
     if (static_cast<int>(blockIdx.x) < T)  // uniform per workgroup
         build_tree(blockIdx.x, N, R, W, parent, node_row, depth, anc, conv_src, status, err);
-    if (static_cast<int>(blockIdx.x) < a.B) resolve_path(blockIdx.x, a, err);
+    else
+        resolve_path(static_cast<int>(blockIdx.x) - T, a, err);
 }
 
 static ResolveArgs resolve_args(const gdn_tree_desc& prev, int B, const int32_t* path,
@@ -203,7 +205,7 @@ hipError_t launch_step_prepare(const gdn_tree_desc& d, const gdn_tree_desc& prev
                                int32_t* path_rows, int32_t* path_n, int32_t* err, hipStream_t s) {
     const int T = d.shared ? 1 : d.B;
     const ResolveArgs a = resolve_args(prev, d.B, path, path_len, Lmax, state_idx, P, path_rows, path_n);
-    hipLaunchKernelGGL(step_prepare_kernel, dim3(T > d.B ? T : d.B), dim3(64), 0, s, T, d.N, d.R, d.W,
+    hipLaunchKernelGGL(step_prepare_kernel, dim3(T + d.B), dim3(64), 0, s, T, d.N, d.R, d.W,
                        d.parent, d.node_row, d.depth, d.anc, d.conv_src, d.status, a, err);
     return hipGetLastError();
 }
