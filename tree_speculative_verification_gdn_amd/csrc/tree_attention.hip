@@ -164,24 +164,33 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
     float m_run = -INFINITY, l_run = 0.f;
 
     const int ntiles = (hi - lo + kTileKeys - 1) / kTileKeys;
-    constexpr int kChunks = kTileKeys * D / 8;  // 16-byte chunks of a K (or V) tile
-    constexpr int kU = kChunks / kAThreads;     // chunks per lane
+    constexpr int kChunks = kTileKeys * D / 8;  // 16-byte chunks of a K tile
+    constexpr int kU = kChunks / kAThreads;     // key chunks per lane
+    constexpr int kPairs = kTileKeys / 2 * (D / 8);              // (key pair, 8 values) items of a V tile
+    constexpr int kVP = (kPairs + kAThreads - 1) / kAThreads;    // value items per lane
     // a tile's keys and values in registers: the next tile's loads are issued
-    // before the current tile's matrix work, so the two overlap
-    // chunk c of a tile: keys row-contiguous (key c / (D/8)); values key-fastest
-    // (key c % 32), so that the lanes of a wave write consecutive keys of one
-    // transposed value row
-    uint4 kc[kU], vc[kU];
+    // before the current tile's matrix work, so the two overlap.  Key chunk c:
+    // key c / (D/8), row-contiguous.  Value item c: keys 2 (c % 16) and
+    // 2 (c % 16) + 1, values 8 (c / 16) .. + 7, so that each lane writes whole
+    // 32-bit words (two keys) of the transposed value rows, 16 lanes to
+    // consecutive words of one row and the four rows of a wave 16 banks apart
+    uint4 kc[kU], vc0[kVP], vc1[kVP];
     auto load_tile = [&](int key0) {
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const int c = tid + u * kAThreads;
             const int kk = c / (D / 8), d8 = (c % (D / 8)) * 8;
-            const int vk = c % kTileKeys, vd8 = (c / kTileKeys) * 8;
             const size_t kpos = static_cast<size_t>(min(key0 + kk, a.S - 1));
-            const size_t vpos = static_cast<size_t>(min(key0 + vk, a.S - 1));
             kc[u] = *reinterpret_cast<const uint4*>(a.k + ((static_cast<size_t>(b) * a.S + kpos) * a.Hkv + g) * D + d8);
-            vc[u] = *reinterpret_cast<const uint4*>(a.v + ((static_cast<size_t>(b) * a.S + vpos) * a.Hkv + g) * D + vd8);
+        }
+#pragma unroll
+        for (int u = 0; u < kVP; ++u) {
+            const int c = min(tid + u * kAThreads, kPairs - 1);  // lanes past the items load a valid chunk
+            const int pm = c % 16, vd8 = (c / 16) * 8;
+            const size_t p0 = static_cast<size_t>(min(key0 + 2 * pm, a.S - 1));
+            const size_t p1 = static_cast<size_t>(min(key0 + 2 * pm + 1, a.S - 1));
+            vc0[u] = *reinterpret_cast<const uint4*>(a.v + ((static_cast<size_t>(b) * a.S + p0) * a.Hkv + g) * D + vd8);
+            vc1[u] = *reinterpret_cast<const uint4*>(a.v + ((static_cast<size_t>(b) * a.S + p1) * a.Hkv + g) * D + vd8);
         }
     };
     // stage a tile from the registers into buffer `buf`: K row-major, V
@@ -199,19 +208,32 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
         for (int u = 0; u < kU; ++u) {
             const int c = tid + u * kAThreads;
             const int kk = c / (D / 8), d8 = (c % (D / 8)) * 8;
-            const int vk = c % kTileKeys, vd8 = (c / kTileKeys) * 8;
-            const int key = key0 + kk, vkey = key0 + vk;
+            const int key = key0 + kk;
             const int sh = tree ? ((key - L) & 63) : 0;
-            const int vsh = tree ? ((vkey - L) & 63) : 0;
             const uint32_t keep = ((key < hi) & (((used >> sh) & 1ull) != 0ull)) ? 0xffffffffu : 0u;
-            const uint32_t vkeep = ((vkey < hi) & (((used >> vsh) & 1ull) != 0ull)) ? 0xffffffffu : 0u;
             const uint4 kw = make_uint4(kc[u].x & keep, kc[u].y & keep, kc[u].z & keep, kc[u].w & keep);
-            const uint32_t vw[4] = {vc[u].x & vkeep, vc[u].y & vkeep, vc[u].z & vkeep, vc[u].w & vkeep};
             *reinterpret_cast<uint4*>(sk + kk * Lds::kKStride + d8) = kw;
+        }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                svt[(vd8 + 2 * e) * Lds::kVStride + vk] = static_cast<uint16_t>(vw[e] & 0xffffu);
-                svt[(vd8 + 2 * e + 1) * Lds::kVStride + vk] = static_cast<uint16_t>(vw[e] >> 16);
+        for (int u = 0; u < kVP; ++u) {
+            const int c = tid + u * kAThreads;
+            if (kPairs % kAThreads == 0 || c < kPairs) {  // uniform per wave
+                const int pm = c % 16, vd8 = (c / 16) * 8;
+                const int k0 = key0 + 2 * pm;
+                const int sh0 = tree ? ((k0 - L) & 63) : 0;
+                const int sh1 = tree ? ((k0 + 1 - L) & 63) : 0;
+                const uint32_t keep0 = ((k0 < hi) & (((used >> sh0) & 1ull) != 0ull)) ? 0xffffffffu : 0u;
+                const uint32_t keep1 = ((k0 + 1 < hi) & (((used >> sh1) & 1ull) != 0ull)) ? 0xffffffffu : 0u;
+                const uint32_t w0[4] = {vc0[u].x & keep0, vc0[u].y & keep0, vc0[u].z & keep0, vc0[u].w & keep0};
+                const uint32_t w1[4] = {vc1[u].x & keep1, vc1[u].y & keep1, vc1[u].z & keep1, vc1[u].w & keep1};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // value rows vd8 + 2e (low halves) and vd8 + 2e + 1 (high halves)
+                    *reinterpret_cast<uint32_t*>(svt + (vd8 + 2 * e) * Lds::kVStride + 2 * pm) =
+                        (w0[e] & 0xffffu) | (w1[e] << 16);
+                    *reinterpret_cast<uint32_t*>(svt + (vd8 + 2 * e + 1) * Lds::kVStride + 2 * pm) =
+                        (w0[e] >> 16) | (w1[e] & 0xffff0000u);
+                }
             }
         }
     };
