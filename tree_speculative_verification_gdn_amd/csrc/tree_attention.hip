@@ -312,14 +312,18 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
         ps += __shfl_xor(ps, 32, 64);
         l_run = l_run * factor + ps;
         m_run = m_new;
-        // rescale the output rows 4 lg + i of this lane's blocks
-        float fr[4];
+        // rescale the output rows 4 lg + i of this lane's blocks, unless no
+        // row of the wave has a new maximum (factor exactly 1 for all: most
+        // tiles once the first few have been seen); the test is wave-uniform
+        if (__ballot(factor != 1.0f) != 0ull) {
+            float fr[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) fr[i] = __shfl(factor, 4 * lg + i, 64);
+            for (int i = 0; i < 4; ++i) fr[i] = __shfl(factor, 4 * lg + i, 64);
 #pragma unroll
-        for (int db = 0; db < kDB; ++db)
+            for (int db = 0; db < kDB; ++db)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[db][i] *= fr[i];
+                for (int i = 0; i < 4; ++i) o[db][i] *= fr[i];
+        }
         // P as the A operand (row rq; k slots: keys 4 lg + j of block 0, then
         // of block 1), split into bf16 hi + lo
         uint32_t ph[4], pl[4];
