@@ -229,9 +229,48 @@ def cpu_baseline(cfg, seed, budget_s):
         if el >= budget_s or reps >= 50:
             break
     nodes = reps * case["B"] * cfg.N
-    return dict(value=nodes / el, unit="tree nodes/s", cores=oracle.threads(), kind="oracle",
-                sample=f"full layer of {cfg.name} (B={case['B']}, N={cfg.N}): desc+conv+verify+commit "
-                       f"in fp64, {reps} repetition(s), {el:.1f} s wall, inputs converted per call")
+    cores = oracle.threads()
+    out = dict(value=nodes / el, unit="tree nodes/s", cores=cores, kind="oracle",
+               sample=f"full layer of {cfg.name} (B={case['B']}, N={cfg.N}): desc+conv+verify+commit "
+                      f"in fp64, {reps} repetition(s), {el:.1f} s wall, inputs converted per call",
+               cpu_model=cpu_model())
+    # the same oracle on one thread, over the first requests of the layer
+    # (a bounded sample: about a sixteenth of the layer, repeated up to half
+    # the budget)
+    nb = max(1, case["B"] // 16)
+    sub = subset(case, np.arange(nb))
+    oracle.set_threads(1)
+    try:
+        reps1, t1 = 0, time.perf_counter()
+        while True:
+            run_oracle(sub)
+            reps1 += 1
+            el1 = time.perf_counter() - t1
+            if el1 >= budget_s / 2 or reps1 >= 50:
+                break
+    finally:
+        oracle.set_threads(cores)
+    out["single_thread"] = dict(
+        value=round(reps1 * nb * cfg.N / el1, 1), unit="tree nodes/s", cores=1,
+        sample=f"first {nb} request(s) of the same layer, {reps1} repetition(s), {el1:.1f} s wall")
+    return out
+
+
+def cpu_model():
+    """The host CPU's model name (Linux), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def spread(xs):
+    """[p10, median, p90] of a list of durations in ms, as us."""
+    return [round(float(v) * 1e3, 2) for v in np.percentile(np.asarray(xs), [10, 50, 90])]
 
 
 # --------------------------------------------------------------------------
@@ -468,6 +507,11 @@ def run_layers(args, cfg, g, torch, dev, to_dev):
             "global_batch": B, "nodes_per_request": N, "layers": L, "parallelism": "single GPU",
             "step_bytes": int(step_bytes), "us_per_layer": round(ms_per_step * 1e3 / L, 2),
             "step_hbm_gbs": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
+            "node_heads_per_s": round(value * cfg.Hv, 1),
+            # spread over the launches of the pass with an event between launches
+            "layer_us_p10_p50_p90": spread([ev[j].elapsed_time(ev[j + 1]) for ev in evs
+                                            for j in range(1, L + 1)]),
+            "prepare_us_p10_p50_p90": spread([ev[0].elapsed_time(ev[1]) for ev in evs]),
         },
         "roofline": dict(bound="hbm", kernel=kname, achieved=round(achieved, 1), peak=PEAK_HBM_GBS,
                          unit="GB/s", frac=round(achieved / PEAK_HBM_GBS, 4), traffic=traffic,
@@ -824,6 +868,10 @@ def main():
             "step_hbm_gbs": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
             "step_frac_of_peak": round(step_bytes / (ms_per_step / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
             "kernel_us": {n: round(avg[n] * 1e3, 2) for n in names},
+            # per-launch spread from the pass with an event between launches
+            "kernel_us_p10_p50_p90": {n: spread(per[n]) for n in names},
+            "step_us_p10_p50_p90": spread([ev[0].elapsed_time(ev[-1]) for ev in evs]),
+            "node_heads_per_s": round(nodes_per_s * cfg.Hv, 1),
         },
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -63,6 +63,8 @@ def _bind(lib):
     ci = ctypes.c_int
     lib.ora_threads.restype = ci
     lib.ora_threads.argtypes = []
+    lib.ora_set_threads.restype = None
+    lib.ora_set_threads.argtypes = [ci]
     lib.ora_desc_build.restype = ci
     lib.ora_desc_build.argtypes = [ci, ci, ci, ci, i32p, i32p, i32p, u64p, i32p, i32p]
     lib.ora_conv.restype = ci
@@ -93,6 +95,11 @@ def load(path: str | None = None):
 def threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return int(load().ora_threads())
+
+
+def set_threads(n: int) -> None:
+    """Set the OpenMP threads of the oracle's parallel loops (calling thread)."""
+    load().ora_set_threads(int(n))
 
 
 # --------------------------------------------------------------------------

@@ -68,6 +68,16 @@ int ora_threads(void)
 #endif
 }
 
+/* Threads for the parallel loops that follow (n < 1: leave as is). */
+void ora_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------- */
 /* Descriptor: validation, depth, strict-ancestor mask, conv tap sources.     */
 /* ------------------------------------------------------------------------- */
