@@ -182,3 +182,42 @@ def test_two_steps_tree64_b256_full_size_sampled():
     m = node_rows_mask(s2)
     assert max_rel_rows(gr["out"][bs][m], orr["out"][m], 2) <= TOL
     assert max_rel_rows(gr["pool"][used[bs]], orr["pool"], 2) <= TOL
+
+
+def _every_node_a_frontier(c1):
+    """Give every request step 1's tree of request 0 and request b the root
+    chain of node b mod N as its accepted path, so each node of the tree is
+    the accepted frontier of some request (BFS packing puts the node rows of
+    every tree at 0..N-1, so the rows stay valid)."""
+    N = c1["cfg"].N
+    c1["parent"][:] = c1["parent"][0]
+    c1["node_row"][:] = c1["node_row"][0]
+    par = c1["parent"][0]
+    c1["path"][:] = -1
+    for b in range(c1["B"]):
+        chain, i = [], b % N
+        while i >= 0:
+            chain.append(i)
+            i = int(par[i])
+        chain.reverse()
+        assert len(chain) <= c1["path"].shape[1]
+        c1["path"][b, :len(chain)] = chain
+        c1["path_len"][b] = len(chain)
+
+
+@pytest.mark.parametrize("cfg_id", [3, 4])
+def test_every_node_as_accepted_frontier(cfg_id):
+    """Publication of each of the 27 possible frontiers of one tree, fused and
+    separate, against the oracle (the pages' component test cycles its paths
+    through every possible frontier)."""
+    cfg = gi.CONFIGS[cfg_id]
+    c1, c2 = two_step_case(cfg, seed=4242 + cfg_id, B=cfg.N, packing="bfs")
+    _every_node_a_frontier(c1)
+    orr = run_oracle_two_steps(c1, c2)
+    conv = cfg.conv_W > 0
+    kw = dict(y1_override=orr["y1"], y2_override=orr["y2"]) if conv else {}
+    gf = run_gpu_two_steps(c1, c2, **kw)
+    _cmp(c1, c2, gf, orr, conv=conv)
+    gs = run_gpu_two_steps(c1, c2, fused=False, **kw)
+    _cmp(c1, c2, gs, orr, conv=conv)
+    assert _committed(c1, orr).all()

@@ -7,6 +7,8 @@ committed states within 2e-3 of the oracle in the max-relative-per-row metric
 (each output row (b, node, h) and each committed state (b, h) is normalised by
 its own largest magnitude).
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -271,6 +273,26 @@ def test_deterministic_repeat():
     b = run_gpu(case)
     assert np.array_equal(a["out"], b["out"], equal_nan=True)
     assert np.array_equal(a["pool"], b["pool"], equal_nan=True)
+
+
+def test_bitwise_identical_across_processes():
+    """Two runs here and one in a fresh process give the same bits: outputs,
+    committed states, conv outputs and published histories of the fused
+    step, the layer step and the separate calls (no atomics or
+    order-dependent reductions on the path)."""
+    import json
+    import subprocess
+    import sys
+
+    from repeat_digest import digests
+
+    first = digests()
+    assert digests() == first
+    script = os.path.join(os.path.dirname(os.path.abspath(__file__)), "repeat_digest.py")
+    proc = subprocess.run([sys.executable, script], capture_output=True, text=True, timeout=300)
+    assert proc.returncode == 0, proc.stderr[-2000:]
+    other = json.loads(proc.stdout.strip().splitlines()[-1])
+    assert other == first
 
 
 # ---------------------------------------------------------------------------
