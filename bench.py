@@ -211,15 +211,15 @@ def measured_traffic(workload, mode, stage):
 # CPU baseline: the oracle as it stands
 # --------------------------------------------------------------------------
 
-def cpu_baseline(cfg, seed, budget_s):
+def cpu_baseline(cfg, seed, budget_s, B=None):
     """The fp64 oracle on the host cores, on the same workload (all B
-    requests of one layer: desc, conv, verify, commit), repeated until
-    ``budget_s`` of wall time."""
+    requests of one layer, or the first ``B`` of them: desc, conv, verify,
+    commit), repeated until ``budget_s`` of wall time."""
     import oracle
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from harness import run_oracle, subset
     import gdn_inputs as gi
-    case = gi.make_case(cfg, seed=seed, layer=0, packing="bfs")
+    case = gi.make_case(cfg, seed=seed, layer=0, packing="bfs", B=B)
     run_oracle(subset(case, np.arange(1)))  # build / load outside the timing
     reps, t0 = 0, time.perf_counter()
     while True:
@@ -231,7 +231,9 @@ def cpu_baseline(cfg, seed, budget_s):
     nodes = reps * case["B"] * cfg.N
     cores = oracle.threads()
     out = dict(value=nodes / el, unit="tree nodes/s", cores=cores, kind="oracle",
-               sample=f"full layer of {cfg.name} (B={case['B']}, N={cfg.N}): desc+conv+verify+commit "
+               sample=f"{'full layer' if case['B'] == cfg.B else 'one layer, first %d requests,' % case['B']} "
+                      f"of {cfg.name} (B={case['B']}, N={cfg.N}): "
+                      f"{'desc+conv+verify+commit' if cfg.conv_W else 'desc+verify+commit'} "
                       f"in fp64, {reps} repetition(s), {el:.1f} s wall, inputs converted per call",
                cpu_model=cpu_model())
     # the same oracle on one thread, over the first requests of the layer
@@ -518,6 +520,14 @@ def run_layers(args, cfg, g, torch, dev, to_dev):
                          avg_us=round(layer_ms * 1e3, 2), algorithmic_bytes=int(per_layer_bytes)),
         "cpu_baseline": None,
     }
+    if not args.no_cpu_baseline:
+        # one layer's oracle on a bounded sample of the requests (a full
+        # layer of this workload is minutes of fp64 work); per layer, so the
+        # 48-layer step is this rate divided by the layer count
+        cpu = cpu_baseline(cfg, args.seed, args.cpu_budget, B=min(cfg.B, 16))
+        cpu["value"] = round(cpu["value"], 1)
+        cpu["per_step_of_layers"] = round(cpu["value"] / L, 2)
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 
