@@ -25,20 +25,10 @@
  *                           publish the state in place, and publish the conv
  *                           history along the same path (LumoTree, Sec. IV-B and
  *                           V-A; Bole review, Algorithm 2 Phase C)
- *   then, declared after them:
- *     gdn_tree_commit_layers        the commit of one path into every layer's
- *                                   state in one launch
- *     gdn_path_resolve,             the previous step's path validated and
- *     gdn_step_prepare              resolved to rows once per step (with the
- *                                   new tree's descriptor: gdn_step_prepare)
- *     conv_ancestry_gather_publish, the fused steady-state step: the previous
- *     gdn_tree_commit_verify        path's commit and history publication with
- *                                   the conv and the verify of the next tree
- *     gdn_layer_step                a whole layer's step in one launch
- *     gdn_tree_attention,           ancestry-aware tree attention over a
- *     gdn_tree_attention_workspace_bytes, gdn_tree_kv_publish
- *                                   committed KV prefix, and the accepted
- *                                   path's KV publication through the slot map
+ *   two that fuse the steady-state step (commit of the previous path with
+ *   the conv and the verify of the next tree): conv_ancestry_gather_publish
+ *   and gdn_tree_commit_verify; and gdn_path_resolve + gdn_layer_step, which
+ *   run a whole layer's step in one launch.  These are declared at the end.
  *
  * Conventions shared by every call
  *   - Every pointer is device memory unless the comment says "host".  The
