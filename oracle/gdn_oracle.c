@@ -199,7 +199,11 @@ static void l2norm(double *x, int D)
     double ss = 0.0;
     for (int c = 0; c < D; c++)
         ss += x[c] * x[c];
+#if ORA_MUTATION == 8
+    const double inv = 1.0 / (sqrt(ss) + 1e-6); /* planted: floor outside the root */
+#else
     const double inv = 1.0 / sqrt(ss + 1e-6);
+#endif
     for (int c = 0; c < D; c++)
         x[c] *= inv;
 }
@@ -415,7 +419,11 @@ int ora_commit(int B, int N, int R, int shared, const int32_t *parent,
                     seq[n++] = x[((size_t)b * R + row) * C + c];
                 }
                 for (int m = 0; m < H; m++)
+#if ORA_MUTATION == 9
+                    hist[((size_t)s * H + m) * C + c] = seq[n - 1 - m]; /* planted: newest first */
+#else
                     hist[((size_t)s * H + m) * C + c] = seq[n - H + m];
+#endif
             }
         }
         free(seq);

@@ -23,6 +23,13 @@ hold.  None of them re-types the oracle's own formula:
 * pin_conv_w1            W = 1 conv == pointwise scale
 * pin_desc_enumeration   depth / ancestors / conv sources == explicit path walk
 * pin_norm_flag          normalise flag == pre-normalised operands
+* pin_norm_invariance    normalised outputs do not change when a q/k row is
+                         scaled by a positive factor; unit rows are (nearly)
+                         left alone; a row of tiny norm becomes the first D
+                         coordinates of the unit vector of (x, sqrt(1e-6))
+* pin_conv_publish       the history a commit publishes continues the causal
+                         conv: the next tree's conv == numpy.convolve over
+                         old history ++ accepted inputs ++ new inputs
 """
 from __future__ import annotations
 
@@ -436,11 +443,115 @@ def pin_norm_flag(lib):
     assert relerr(out_flag[0, rows], out_pre[0, rows]) < 1e-13
 
 
+def pin_norm_invariance(lib):
+    """q/k normalisation is a property of direction, not length (LumoTree,
+    Sec. IV-B: the verifier normalises q and k itself).  Three facts that do
+    not restate the normalisation formula:
+      (1) large rows (|x| ~ 1e3, so the 1e-6 floor moves nothing by more than
+          ~1e-12): scaling each q/k row by its own positive factor leaves every
+          output unchanged, and the result equals the outputs on rows divided
+          by numpy.linalg.norm;
+      (2) rows already of unit length change the outputs by at most ~1e-6;
+      (3) rows of tiny norm (|x|^2 ~ 1e-6): the normalised row is the first D
+          coordinates of the unit vector of x with one more coordinate
+          sqrt(1e-6) appended (the floor inside the square root, read R4)."""
+    g = np.random.default_rng(35)
+    par = random_parent(g, 11)
+    D = 8
+    pb = small_problem(61, [par], D=D, unit_k=False)
+    rows = pb["node_row"][0]
+    big = dict(pb)
+    big["q"] = pb["q"] * 1e3
+    big["k"] = pb["k"] * 1e3
+    out_big, err = run_verify(big, lib, norm=True, want_states=False)
+    assert err == 0
+    scaled = dict(big)
+    scaled["q"] = big["q"] * g.uniform(0.25, 4.0, big["q"].shape[:-1] + (1,))
+    scaled["k"] = big["k"] * g.uniform(0.25, 4.0, big["k"].shape[:-1] + (1,))
+    out_scaled, _ = run_verify(scaled, lib, norm=True, want_states=False)
+    assert relerr(out_scaled[0, rows], out_big[0, rows]) < 1e-10
+    unit = dict(pb)
+    unit["q"] = pb["q"] / np.linalg.norm(pb["q"], axis=-1, keepdims=True)
+    unit["k"] = pb["k"] / np.linalg.norm(pb["k"], axis=-1, keepdims=True)
+    out_unit_raw, _ = run_verify(unit, lib, norm=False, want_states=False)
+    assert relerr(out_big[0, rows], out_unit_raw[0, rows]) < 1e-10
+    out_unit_norm, _ = run_verify(unit, lib, norm=True, want_states=False)
+    d_unit = relerr(out_unit_norm[0, rows], out_unit_raw[0, rows])
+    assert d_unit < 2e-6
+    tiny = dict(pb)
+    tiny["q"] = pb["q"] / np.linalg.norm(pb["q"], axis=-1, keepdims=True) * 1e-3
+    tiny["k"] = pb["k"] / np.linalg.norm(pb["k"], axis=-1, keepdims=True) * 2e-3
+    out_tiny, _ = run_verify(tiny, lib, norm=True, want_states=False)
+
+    def aug_unit(x):
+        ext = np.concatenate([x, np.full(x.shape[:-1] + (1,), np.sqrt(1e-6))], axis=-1)
+        return (ext / np.linalg.norm(ext, axis=-1, keepdims=True))[..., :-1]
+
+    ref = dict(pb)
+    ref["q"], ref["k"] = aug_unit(tiny["q"]), aug_unit(tiny["k"])
+    out_ref, _ = run_verify(ref, lib, norm=False, want_states=False)
+    assert relerr(out_tiny[0, rows], out_ref[0, rows]) < 1e-12
+
+
+def pin_conv_publish(lib):
+    """The conv history a commit publishes is what the causal conv of the
+    token sequence needs next (LumoTree, Sec. V-A: the accepted path drives
+    the convolution publication; Sec. V-C: windows continue from the prior
+    history).  Step 1: a tree convolved over history h0, a root chain of it
+    accepted (len 0, shorter than W-1, equal, longer).  Step 2: a chain tree
+    convolved over the published history.  Every step-2 output must equal
+    numpy.convolve over h0 ++ x of the accepted nodes ++ x of the chain."""
+    g = np.random.default_rng(36)
+    # a tree with a root path of 6 nodes (plus side branches)
+    par1 = np.array([-1, 0, 1, 0, 2, 3, 4, 1, 6, 8, 5], np.int32)
+    chain = [0, 1, 2, 4, 6, 8]  # root path of node 8 (parents 1->0, 2->1, 4->2, 6->4, 8->6)
+    for j in range(1, len(chain)):
+        assert par1[chain[j]] == chain[j - 1]
+    N1, N2 = len(par1), 5
+    par2 = np.arange(-1, N2 - 1, dtype=np.int32)
+    C = 4
+    for W in (2, 3, 4):
+        H = W - 1
+        lengths = [0, 1, 2, 3, 4, 6]
+        B = len(lengths)
+        R1, R2 = N1 + 2, N2 + 3
+        rows1 = np.stack([g.permutation(R1)[:N1] for _ in range(B)]).astype(np.int32)
+        rows2 = np.stack([g.permutation(R2)[:N2] for _ in range(B)]).astype(np.int32)
+        x1 = g.standard_normal((B, R1, C))
+        x2 = g.standard_normal((B, R2, C))
+        P = B + 1
+        h0 = g.standard_normal((P, H, C))
+        w = g.standard_normal((C, W))
+        sidx = g.permutation(P)[:B].astype(np.int32)
+        path = np.full((B, len(chain)), -1, np.int32)
+        for b, L in enumerate(lengths):
+            path[b, :L] = chain[:L]
+        plen = np.array(lengths, np.int32)
+        # commit of step 1's accepted paths (state operands are irrelevant here)
+        pb = small_problem(62 + W, [par1] * B, R=R1, D=4, Hv=1)
+        d1 = oracle.desc_build(np.tile(par1, (B, 1)), rows1, R1, 1, lib=lib)
+        _, h1, err = oracle.commit(np.tile(par1, (B, 1)), rows1, d1["status"], path, plen, pb["k"],
+                                   pb["v"], pb["alpha"], pb["beta"], pb["pool"][:P], sidx, 1, 1,
+                                   False, x=x1, hist=h0, W=W, lib=lib)
+        assert err == 0
+        d2 = oracle.desc_build(np.tile(par2, (B, 1)), rows2, R2, W, lib=lib)
+        y2, err = oracle.conv(rows2, d2["conv_src"], d2["status"], x2, h1, sidx, w, None, 0, R2, C,
+                              W, lib=lib)
+        assert err == 0
+        for b, L in enumerate(lengths):
+            for c in range(C):
+                seq = np.concatenate([h0[sidx[b], :, c], x1[b, rows1[b][chain[:L]], c],
+                                      x2[b, rows2[b], c]])
+                ref = _np_causal(seq, w[c])[L:]
+                got = y2[b, rows2[b], c]
+                assert np.max(np.abs(got - ref)) < 1e-12, (W, L, c)
+
+
 ALL_PINS = [
     pin_chain_textbook, pin_paths_are_chains, pin_sibling_isolation, pin_commit_is_replay,
     pin_closed_form, pin_treewy_states, pin_nilpotent, pin_factorized_commit, pin_pure_decay,
     pin_delta_write, pin_conv_chain, pin_conv_tree_paths, pin_conv_w1, pin_desc_enumeration,
-    pin_norm_flag,
+    pin_norm_flag, pin_norm_invariance, pin_conv_publish,
 ]
 
 
