@@ -324,6 +324,77 @@ __device__ __forceinline__ void store_out(void* out, size_t idx, float o, bool o
         static_cast<float*>(out)[idx] = o;
 }
 
+// ---------------------------------------------------------------------------
+// State traffic in whole cache lines.  The matrix-core layout gives lane
+// (row r, half hf) the float4 chunks 2t + hf (t = 0..15) of one state row, so
+// a load or store instruction written in that layout touches 32 rows at
+// 32 bytes each; measured on this part, a 64 KiB-per-workgroup read + write
+// of the state runs about 17% faster when every store instruction covers
+// whole 128-byte lines and every load whole 64-byte segments.  The state is
+// therefore loaded and stored in those shapes and moved into the matrix-core
+// layout (and back, for the store) inside groups of lanes with DPP quad
+// permutes: one exchange stage after the load, two before the store.
+// ---------------------------------------------------------------------------
+constexpr int kDppXor1 = 0xB1;  // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;  // quad_perm [2, 3, 0, 1]
+
+template <int CTRL>
+__device__ __forceinline__ float4 dpp4(const float4& x) {
+    auto m = [](float v) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+    };
+    return make_float4(m(x.x), m(x.y), m(x.z), m(x.w));
+}
+
+__device__ __forceinline__ float4 sel4(bool c, const float4& a, const float4& b) {
+    return make_float4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
+}
+
+// Float offset of load s (0..15) of lane (l32 = 2a + i, hf) from the wave's
+// 32-row block: row 2a + (s & 1), float4 chunk 4 (s >> 1) + 2i + hf, i.e.
+// every instruction reads 16 rows x 64 contiguous bytes.
+__device__ __forceinline__ int state_load_lane_off(int l32, int hf) {
+    return (l32 >> 1) * 256 + (l32 & 1) * 8 + hf * 4;
+}
+constexpr int state_load_off(int s) { return (s & 1) * 128 + (s >> 1) * 16; }
+
+// After the loads above arrived: register t of lane (2a + i, hf) must hold
+// chunk 2t + hf of row 2a + i.  Load t holds it when t and i have the same
+// parity; otherwise the partner lane (i ^ 1) holds it in load t ^ 1.
+__device__ __forceinline__ void state_fix_loaded(float4 (&sr)[16], int l32) {
+    const bool odd = (l32 & 1) != 0;
+#pragma unroll
+    for (int t = 0; t < 16; t += 2) {
+        const float4 p0 = dpp4<kDppXor1>(sr[t + 1]);
+        const float4 p1 = dpp4<kDppXor1>(sr[t]);
+        sr[t] = sel4(odd, p0, sr[t]);
+        sr[t + 1] = sel4(odd, sr[t + 1], p1);
+    }
+}
+
+// Store of the state held in the matrix-core layout: store 4m + j of lane
+// (l32 = 4a + i, hf) writes chunk 8m + 2i + hf of row 4a + j, which lane
+// 4a + j holds in register 4m + i (a 4 x 4 transpose inside each lane quad,
+// as two exchange stages, into temporaries: the registers stay as they are),
+// so every instruction writes 8 rows' whole 128-byte lines.  One register
+// group at a time (scheduling barriers keep the groups' temporaries apart).
+__device__ __forceinline__ void state_store_lines(float* wave_base, const float4 (&sr)[16], int l32, int hf) {
+    const int i = l32 & 3;
+    float* lb = wave_base + (l32 >> 2) * 512 + i * 8 + hf * 4;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        float4 y[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            y[j] = sel4(((i ^ j) & 1) == 0, sr[4 * m + j], dpp4<kDppXor1>(sr[4 * m + (j ^ 1)]));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<float4*>(lb + j * 128 + m * 32) =
+                sel4(((i ^ j) & 2) == 0, y[j], dpp4<kDppXor2>(y[j ^ 2]));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -394,7 +465,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     constexpr int kSlots = NP / 8;      // node slots per thread: node tid/32 + 8u
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar addressing
     const int hf = lane >> 5;
     const int l32 = lane & 31;
     const int r_own = wave * 32 + l32;  // value row this lane owns in every MFMA
@@ -575,16 +646,23 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
         p_al = cp.alpha_p[gi];
         p_be = cp.beta_p[gi];
     }
-    asm volatile("" ::: "memory");  // keep the state loads behind the loads above
-    //   (a3) the committed state: lane (r_own, hf) holds 64 elements of row r_own
-    float* Sb = pool + (static_cast<size_t>(slot) * Hv + h) * (kD * kD) +
-                static_cast<size_t>(r_own) * kD + 4 * hf;
+    //   (a3) the committed state, loaded in 64-byte row segments; after the
+    //        fix-up at its first use, lane (r_own, hf) holds chunks 2t + hf of
+    //        row r_own in register t.  The layer step issues it only once its
+    //        conv input is staged in LDS (below): the input rows then do not
+    //        queue behind every unit's state, the registers that held them
+    //        are free, and the conv, Gram block and M solve still cover the
+    //        state's latency.
+    float* Sw = pool + (static_cast<size_t>(slot) * Hv + h) * (kD * kD) + static_cast<size_t>(wave) * 32 * kD;
     float4 sreg[16];
+    auto issue_state_loads = [&]() {
+        asm volatile("" ::: "memory");  // keep the state loads behind the loads above
+        const float* Sl = Sw + state_load_lane_off(l32, hf);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        sreg[2 * s] = *reinterpret_cast<const float4*>(Sb + 16 * s);
-        sreg[2 * s + 1] = *reinterpret_cast<const float4*>(Sb + 16 * s + 8);
-    }
+        for (int s = 0; s < 16; ++s) sreg[s] = *reinterpret_cast<const float4*>(Sl + state_load_off(s));
+    };
+    if constexpr (!LAYER) issue_state_loads();
+    bool sfixed = false;  // uniform: the state is in the matrix-core layout
 
     if constexpr (FUSED) {
         // used under per-lane conditions after the M solve: take delivery
@@ -599,7 +677,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     // then the history)
     if constexpr (LAYER) {
         // the loads above are used under per-lane conditions below: take
-        // delivery here (the state, issued after them, stays in flight)
+        // delivery here (the state is issued once they are staged)
 #pragma unroll
         for (int u = 0; u < kPItems; ++u)
             asm volatile("" ::"v"(pc_val[u].x), "v"(pc_val[u].y), "v"(pc_val[u].z), "v"(pc_val[u].w));
@@ -734,6 +812,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
             }
         }
         __syncthreads();
+        issue_state_loads();  // the conv input is in LDS now
         if (nc > 0) {  // uniform: the previous path's first segment, k and v channels
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
@@ -1145,6 +1224,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
             // rank-n update is four 32-column contractions whose output layout
             // is this lane's own state layout.
             float* s_gp = s_scp + (FUSED ? cp.Lmax : kMfmaPath);  // [kMfmaPath][kMfmaPath] scaled segment Gram
+            state_fix_loaded(sreg, l32);
+            sfixed = true;
             for (int j0 = 0; j0 < plen; j0 += kMfmaPath) {
                 const int n = min(plen - j0, kMfmaPath);
                 const int kr0 = FUSED ? j0 : 0;  // staged row of the segment's first node
@@ -1305,17 +1386,15 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                 }
                 __syncthreads();  // the segment Gram is rewritten by the next segment
             }
-#pragma unroll
-            for (int s8 = 0; s8 < 8; ++s8) {
-                *reinterpret_cast<float4*>(Sb + 16 * s8) = sreg[2 * s8];
-                *reinterpret_cast<float4*>(Sb + 16 * s8 + 8) = sreg[2 * s8 + 1];
-            }
+            state_store_lines(Sw, sreg, l32, hf);
         }
         if (!vok) return;
     }
 
     // (d) CT = [K;Q] S_pre^T on the matrix cores, state split into bf16 hi + lo
-    //     (the first use of the state: the only wait for it)
+    //     (the first use of the state when nothing was replayed: the only wait
+    //     for it)
+    if (!sfixed) state_fix_loaded(sreg, l32);
     f32x16_t acc[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x16_t{};
