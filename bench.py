@@ -8,13 +8,7 @@ state): the descriptor build, the ancestry-gathered conv, the tree verify, the
 commit of an accepted path into the state and the conv-history publication.
 
 Three step shapes (``--mode``):
-  fused     (default) gdn_step_prepare -> conv_ancestry_gather_publish ->
-              gdn_tree_commit_verify
-            the steady-state decode step in two launches per layer (after the
-            step's shared prepare): the previous step's accepted path is
-            committed and its conv history published inside this step's conv
-            and verify, so the state is read once and written once.
-  layer     the same step in one launch per layer:
+  layer     (default) the steady-state decode step in one launch per layer:
               gdn_step_prepare -> gdn_layer_step
             (the first once per step for all layers: the new tree's
             descriptor and the previous path's rows); the layer step
@@ -22,11 +16,18 @@ Three step shapes (``--mode``):
             history into the other of two history buffers, and convolves and
             verifies the new tree: the state is read once and written once,
             the conv output never goes to memory.
+  fused     the same step in two launches per layer:
+              gdn_step_prepare -> conv_ancestry_gather_publish ->
+              gdn_tree_commit_verify
+            (the conv output goes to memory and is read back).
   separate  gdn_tree_desc_build -> conv_ancestry_gather -> gdn_tree_verify
             -> gdn_tree_commit (this step's own path), the state read twice.
 All three commit one path and verify one tree per step.
 
-Inputs are resident in HBM before the timed region.  Two independent layer
+Before the W warm-up steps the step runs back to back for --settle-ms
+(300 ms by default) so that the GPU's clocks are at their steady state, as
+in a decode loop that runs continuously.  Inputs are resident in HBM before
+the timed region.  Two independent layer
 instances (pool, history, weights, about 0.5 GB each with their step data)
 alternate step by step, so no step reads data the previous step left in the
 256 MB last-level cache; in fused mode each instance alternates between two
@@ -66,8 +67,15 @@ def log(*a):
 
 
 # --------------------------------------------------------------------------
-# byte model: what each kernel must move through its interface, read once
-# and written once (re-reads, padding rows and cache effects never credited)
+# byte model: what the method must move (read once, written once), per the
+# survey's measurement section: the state read once per step (by verify, or
+# by the fused kernels that verify from it) and written for requests with an
+# accepted path; q/k/v counted once as the conv input x when the conv feeds
+# them (the conv output y is never credited, whichever kernel reads or writes
+# it); outputs, gates, the accepted path's k/v rows and gates, the conv
+# history read and written, the weights and the accepted rows' conv inputs
+# that enter the history.  Re-reads, padding rows and cache effects are
+# never credited.
 # --------------------------------------------------------------------------
 
 def _common(cfg, case):
@@ -79,39 +87,6 @@ def bytes_desc(cfg, case):
     return B * N * (4 + 4) + B * N * (4 + 8 + 4 * (W - 1)) + B * 4
 
 
-def bytes_conv(cfg, case):
-    B, N, D, Hv, Hqk, W, C = _common(cfg, case)
-    if cfg.conv_W == 0:
-        return 0
-    return B * N * C * 2 + B * (W - 1) * C * 2 + C * W * 2 + B * N * C * 2
-
-
-def bytes_publish(cfg, prev):
-    """History publication of prev's accepted paths: new entries written, the
-    x rows they come from (the old entries are read by the conv anyway)."""
-    B, N, D, Hv, Hqk, W, C = _common(cfg, prev)
-    L = prev["path_len"].astype(np.int64)
-    if cfg.conv_W <= 1:
-        return 0
-    active = int((L > 0).sum())
-    return active * (W - 1) * C * 2 + int(np.minimum(L, W - 1).sum()) * C * 2
-
-
-def bytes_verify(cfg, case):
-    B, N, D, Hv, Hqk, W, C = _common(cfg, case)
-    return (B * Hv * D * D * 4 + B * N * (2 * Hqk * D + Hv * D) * 2 + B * N * Hv * 8
-            + B * N * Hv * D * 4)
-
-
-def bytes_commit_state(cfg, case):
-    """State write (and, for the separate commit, the read) of the committed
-    requests plus the path's recorded k/v rows and gates."""
-    B, N, D, Hv, Hqk, W, C = _common(cfg, case)
-    L = case["path_len"].astype(np.int64)
-    active = int((L > 0).sum())
-    return active * Hv * D * D * 4, int(L.sum()) * ((Hqk * D + Hv * D) * 2 + Hv * 8)
-
-
 def bytes_resolve(cfg, prev):
     """Path validation: path ids and length in, parents and rows of the path
     nodes, the slots for the duplicate check; rows and counts out."""
@@ -119,41 +94,58 @@ def bytes_resolve(cfg, prev):
     return B * Lmax * (4 + 4 + 4 + 4) + B * (4 + 4 + 4 + 4)
 
 
-def bytes_layer(cfg, cur, prev):
-    """The one-launch layer step: the state (read; written for requests with
-    an accepted path), the new tree's conv input rows, gates and outputs, the
-    old history read and the new one written, the weights, and of the
-    previous path its k/v-channel conv rows, the q channels of the rows that
-    enter the new history, and its gates."""
-    B, N, D, Hv, Hqk, W, C = _common(cfg, cur)
-    L = prev["path_len"].astype(np.int64)
+def bytes_conv(cfg, case, path_case):
+    """x rows of the tree, the history read and written, the weights, and the
+    conv inputs of the accepted path's rows that enter the history."""
+    B, N, D, Hv, Hqk, W, C = _common(cfg, case)
+    if cfg.conv_W == 0:
+        return 0
+    L = path_case["path_len"].astype(np.int64)
+    return (B * N * C * 2 + B * (W - 1) * C * 2 * 2 + C * W * 2
+            + int(np.minimum(L, W - 1).sum()) * C * 2)
+
+
+def bytes_verify_io(cfg, case):
+    """Verify's bytes besides the state: q/k/v (unless the conv produced
+    them), gates and outputs."""
+    B, N, D, Hv, Hqk, W, C = _common(cfg, case)
+    qkv = 0 if cfg.conv_W > 0 else B * N * (2 * Hqk * D + Hv * D) * 2
+    return qkv + B * N * Hv * 8 + B * N * Hv * D * 4
+
+
+def bytes_commit_parts(cfg, case):
+    """(state bytes of one pass over the committed requests' states, the
+    accepted path's k/v rows and gates)."""
+    B, N, D, Hv, Hqk, W, C = _common(cfg, case)
+    L = case["path_len"].astype(np.int64)
     active = int((L > 0).sum())
-    state = B * Hv * D * D * 4 + active * Hv * D * D * 4
-    tree = B * N * C * 2 + B * N * Hv * 8 + B * N * Hv * D * 4
-    hist = 2 * B * (W - 1) * C * 2 + C * W * 2
-    path = (int(L.sum()) * ((Hqk * D + Hv * D) * 2 + Hv * 8)
-            + int(np.minimum(L, W - 1).sum()) * Hqk * D * 2)
-    return state + tree + hist + path
+    return active * Hv * D * D * 4, int(L.sum()) * ((Hqk * D + Hv * D) * 2 + Hv * 8)
 
 
 def byte_model(cfg, cur, prev, mode):
+    """Algorithmic bytes per launch of each kernel of one step."""
+    B, N, D, Hv, Hqk, W, C = _common(cfg, cur)
+    state = B * Hv * D * D * 4
+    if mode in ("fused", "layer"):
+        # the step commits prev's path and verifies cur's tree from that state
+        sw, path = bytes_commit_parts(cfg, prev)
+        commit_verify = state + sw + bytes_verify_io(cfg, cur) + path
+        conv = bytes_conv(cfg, cur, prev)
+        prep = bytes_desc(cfg, cur) + bytes_resolve(cfg, prev)
+        if mode == "layer":
+            return {"prepare": prep, "layer": commit_verify + conv}
+        out = {"prepare": prep}
+        if cfg.conv_W > 0:
+            out["conv"] = conv
+        out["commit_verify"] = commit_verify
+        return out
+    # separate calls: this step's own path; verify and commit each pass over the state
+    sw, path = bytes_commit_parts(cfg, cur)
     out = {"desc": bytes_desc(cfg, cur)}
-    if mode == "layer":
-        out = {"prepare": out["desc"] + bytes_resolve(cfg, prev), "layer": bytes_layer(cfg, cur, prev)}
-    elif mode == "fused":
-        state_w, path_rows = bytes_commit_state(cfg, prev)
-        out = {"prepare": out["desc"] + bytes_resolve(cfg, prev)}
-        if cfg.conv_W > 0:
-            out["conv"] = bytes_conv(cfg, cur) + bytes_publish(cfg, prev)
-        out["commit_verify"] = bytes_verify(cfg, cur) + state_w + path_rows
-    else:
-        state_w, path_rows = bytes_commit_state(cfg, cur)
-        if cfg.conv_W > 0:
-            out["conv"] = bytes_conv(cfg, cur)
-        out["verify"] = bytes_verify(cfg, cur)
-        B, N, D, Hv, Hqk, W, C = _common(cfg, cur)
-        hist_read = int((cur["path_len"] > 0).sum()) * (W - 1) * C * 2 if cfg.conv_W > 1 else 0
-        out["commit"] = 2 * state_w + path_rows + bytes_publish(cfg, cur) + hist_read
+    if cfg.conv_W > 0:
+        out["conv"] = bytes_conv(cfg, cur, cur)
+    out["verify"] = state + bytes_verify_io(cfg, cur)
+    out["commit"] = 2 * sw + path
     return out
 
 
@@ -162,8 +154,9 @@ def byte_model(cfg, cur, prev, mode):
 # --------------------------------------------------------------------------
 
 def library_source_hash():
-    """sha256[:16] over the library's kernel sources and the ABI header, in
-    the order the profile summaries under profiles/ record it."""
+    """sha256[:16] over the library's kernel sources (csrc/*.hip, csrc/*.h),
+    the value the counter summaries under profiles/ record: documentation of
+    the ABI header does not invalidate them."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "tree_speculative_verification_gdn_amd", "csrc")
     for f in sorted(os.listdir(d)):
@@ -171,8 +164,6 @@ def library_source_hash():
             h.update(f.encode())
             with open(os.path.join(d, f), "rb") as fh:
                 h.update(fh.read())
-    with open(os.path.join(ROOT, "include", "gdn_tree.h"), "rb") as fh:
-        h.update(fh.read())
     return h.hexdigest()[:16]
 
 
@@ -268,6 +259,23 @@ def cpu_model():
     except OSError:
         pass
     return None
+
+
+def settle(step_fn, ms, torch):
+    """Run the step back to back for ``ms`` of wall time before the warm-up
+    steps and return how many ran.  After idle this GPU runs the first
+    100-200 steps of the conv-fed workload 6-19% slower than in steady state
+    (its clocks and power settle over tens of ms under load); a decode loop
+    runs continuously, so the timed steps are taken at the steady state."""
+    if ms <= 0:
+        return 0
+    n, t0 = 0, time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(16):
+            step_fn(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
 
 
 def spread(xs):
@@ -439,6 +447,7 @@ def run_layers(args, cfg, g, torch, dev, to_dev):
             mark()
         return cur, prev
 
+    settle_steps = settle(lambda i: step(), args.settle_ms, torch)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -505,6 +514,7 @@ def run_layers(args, cfg, g, torch, dev, to_dev):
             "mode": args.mode,
             "step": ("gdn_step_prepare + gdn_tree_commit_verify per layer" if fused else
                      "gdn_tree_desc_build + gdn_tree_verify per layer + one gdn_tree_commit_layers"),
+            "settle_ms": args.settle_ms, "settle_steps": settle_steps,
             "value_is": "tree nodes verified per second per GDN layer: B*N*layers / step time",
             "global_batch": B, "nodes_per_request": N, "layers": L, "parallelism": "single GPU",
             "step_bytes": int(step_bytes), "us_per_layer": round(ms_per_step * 1e3 / L, 2),
@@ -517,6 +527,7 @@ def run_layers(args, cfg, g, torch, dev, to_dev):
         },
         "roofline": dict(bound="hbm", kernel=kname, achieved=round(achieved, 1), peak=PEAK_HBM_GBS,
                          unit="GB/s", frac=round(achieved / PEAK_HBM_GBS, 4), traffic=traffic,
+                         traffic_over_algorithmic=(round(traffic / per_layer_bytes, 3) if traffic else None),
                          avg_us=round(layer_ms * 1e3, 2), algorithmic_bytes=int(per_layer_bytes)),
         "cpu_baseline": None,
     }
@@ -652,7 +663,10 @@ def main():
     # ms); 200 untimed steps (about 40 ms) reach the steady state
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--config", type=int, default=4)
-    ap.add_argument("--mode", choices=("fused", "layer", "separate", "attention"), default="fused")
+    ap.add_argument("--mode", choices=("fused", "layer", "separate", "attention"), default="layer")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="run the step for this long before the warm-up steps: after idle the GPU's "
+                         "clocks take tens of ms of load to reach their steady state")
     ap.add_argument("--ctx", type=int, default=65536, help="attention mode: committed prefix per request")
     ap.add_argument("--splits", type=int, default=63,
                     help="attention mode: prefix partitions (63: with the candidate partition, "
@@ -787,7 +801,9 @@ def main():
         mark()
         return cur, prev
 
-    # the first step of each instance fills its slots' conv outputs
+    # clock settle, then the warm-up steps (the first step of each instance
+    # also fills its slots' conv outputs)
+    settle_steps = settle(lambda i: step(insts[i % len(insts)]), args.settle_ms, torch)
     for i in range(args.warmup + (2 * args.sets if fused else 0)):
         step(insts[i % len(insts)])
     torch.cuda.synchronize()
@@ -837,9 +853,10 @@ def main():
     dom = max((n for n in names if n not in ("desc", "prepare")), key=lambda n: avg[n])
     achieved = bytes_avg[dom] / (avg[dom] / 1e3) / 1e9
     tag = WORKLOAD_TAG.get(cfg.name, cfg.name)
+    traffic = measured_traffic(tag, args.mode, dom)
     roofline = dict(bound="hbm", kernel=dom, achieved=round(achieved, 1), peak=PEAK_HBM_GBS,
-                    unit="GB/s", frac=round(achieved / PEAK_HBM_GBS, 4),
-                    traffic=measured_traffic(tag, args.mode, dom),
+                    unit="GB/s", frac=round(achieved / PEAK_HBM_GBS, 4), traffic=traffic,
+                    traffic_over_algorithmic=(round(traffic / bytes_avg[dom], 3) if traffic else None),
                     avg_us=round(avg[dom] * 1e3, 2), algorithmic_bytes=int(bytes_avg[dom]))
 
     cpu = None
@@ -880,6 +897,7 @@ def main():
             "step_bytes": int(step_bytes),
             "step_hbm_gbs": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
             "step_frac_of_peak": round(step_bytes / (ms_per_step / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+            "settle_ms": args.settle_ms, "settle_steps": settle_steps,
             "kernel_us": {n: round(avg[n] * 1e3, 2) for n in names},
             # per-launch spread from the pass with an event between launches
             "kernel_us_p10_p50_p90": {n: spread(per[n]) for n in names},

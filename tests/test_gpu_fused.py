@@ -130,6 +130,19 @@ def test_two_steps_conv4_edge_cases():
     _cmp(c1, c2, gr, orr, conv=True)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_two_steps_fallback_n64_d128(dtype):
+    # 64-node trees at d = 128 on the commit-then-verify fallback (fp32
+    # operands, or bf16 with GDN_F_VALU): both kernels have a layout for this
+    # size, so the call launches both
+    cfg = gi.CONFIGS[5].replace(dtype=dtype, Hv=4, Hqk=2)
+    c1, c2 = two_step_case(cfg, seed=64 + (dtype == "f32"), B=3)
+    import tree_speculative_verification_gdn_amd as g
+    gr = run_gpu_two_steps(c1, c2, flags=0 if dtype == "f32" else g.GDN_F_VALU)
+    orr = run_oracle_two_steps(c1, c2)
+    _cmp(c1, c2, gr, orr)
+
+
 def test_two_steps_fallback_d32_f32():
     # fp32 operands at d = 32: commit and verify kernels one after the other
     c1, c2 = two_step_case(gi.CONFIGS[1], seed=3)

@@ -157,6 +157,22 @@ def test_node_count_edges(N, bmax, depth):
     _cmp_pool(case, gr, orr)
 
 
+@pytest.mark.parametrize("dtype,valu,tree", [("f32", False, "chain"), ("f32", False, "random"),
+                                             ("bf16", True, "chain"), ("bf16", True, "random")])
+def test_n64_d128_vector_alu_paths(dtype, valu, tree):
+    # 64 nodes at d = 128 on the vector-ALU kernel (fp32 operands, or bf16 with
+    # GDN_F_VALU): its layout keeps the ancestor Gram entries as lower
+    # triangles, so this size fits the 160 KiB of LDS
+    cfg = gi.CONFIGS[3].replace(N=64, R=67, dtype=dtype, tree=tree, bmax=4 if tree == "random" else 1,
+                                depth_max=8 if tree == "random" else 63, B=4, Hv=4, Hqk=2)
+    case = gi.make_case(cfg, seed=640 + (dtype == "f32") + 2 * (tree == "chain"), extra_slots=1)
+    gr = run_gpu(case, flags=_g().GDN_F_VALU if valu else 0)
+    orr = run_oracle(case)
+    assert gr["err"] == orr["err"] == 0
+    _cmp_out(case, gr, orr)
+    _cmp_pool(case, gr, orr)
+
+
 def test_wide_tree_every_depth_class():
     # 64 nodes: a 24-node spine with 40 leaves hung at depths 7 .. 24, so the
     # M solve meets nodes of path length <= 8, more than 16 of length 9 .. 16

@@ -1512,10 +1512,11 @@ __host__ __device__ inline ValuLds valu_lds_layout(int N, int D) {
     off += nd;
     L.U = off;
     off += nd;
+    // Gram entries of ancestor pairs only (j <= i): row-major lower triangles
     L.kk = off;
-    off += align_up(N * N * 4, 16);
+    off += align_up(N * (N + 1) / 2 * 4, 16);
     L.kq = off;
-    off += align_up(N * N * 4, 16);
+    off += align_up(N * (N + 1) / 2 * 4, 16);
     L.al = off;
     off += align_up(N * 4, 16);
     L.be = off;
@@ -1638,8 +1639,8 @@ __global__ void __launch_bounds__(kThreads)
             dkk = fmaf(ki[c], kj[c], dkk);
             dkq = fmaf(qi[c], kj[c], dkq);
         }
-        s_kk[e] = dkk;
-        s_kq[e] = dkq;
+        s_kk[i * (i + 1) / 2 + j] = dkk;
+        s_kq[i * (i + 1) / 2 + j] = dkq;
     }
     __syncthreads();
 
@@ -1671,11 +1672,11 @@ __global__ void __launch_bounds__(kThreads)
             const int j = __builtin_ctzll(am);
             am &= am - 1ull;
             const float uj = s_U[j * D + r];
-            yk = fmaf(s_al[j], yk, uj * s_kk[i * N + j]);
-            yq = fmaf(s_al[j], yq, uj * s_kq[i * N + j]);
+            yk = fmaf(s_al[j], yk, uj * s_kk[i * (i + 1) / 2 + j]);
+            yq = fmaf(s_al[j], yq, uj * s_kq[i * (i + 1) / 2 + j]);
         }
         const float u = s_be[i] * (s_V[i * D + r] - s_al[i] * yk);
-        const float o = fmaf(s_al[i], yq, u * s_kq[i * N + i]);
+        const float o = fmaf(s_al[i], yq, u * s_kq[i * (i + 1) / 2 + i]);
         if (part == 0) {
             s_U[i * D + r] = u;
             const size_t oi = ((static_cast<size_t>(b) * R + s_rows[i]) * Hv + h) * D + r;
@@ -1747,6 +1748,16 @@ bool verify_uses_mfma(const gdn_tree_desc& d, const VerifyArgs& a) {
     return a.dtype == GDN_DT_BF16 && a.D == kD && !(a.flags & GDN_F_VALU) && aligned && d.N >= 1;
 }
 
+// Whether launch_verify has a kernel for these arguments (checked by the
+// fused call before it launches anything).
+bool verify_supported(const gdn_tree_desc& d, const VerifyArgs& a) {
+    if (verify_uses_mfma(d, a)) {
+        const int NPB = (d.N + 31) / 32;
+        return NPB <= 2 && static_cast<size_t>(mfma_lds_layout(d.N, NPB).total) <= kMaxLds;
+    }
+    return (a.D == 32 || a.D == 64 || a.D == 128) && verify_valu_lds_bytes(d.N, a.D) <= kMaxLds;
+}
+
 hipError_t launch_verify(const gdn_tree_desc& d, const VerifyArgs& a, hipStream_t s) {
     const int norm = (a.flags & GDN_F_NORM_QK) ? 1 : 0;
     const int obf = (a.flags & GDN_F_OUT_BF16) ? 1 : 0;
@@ -1811,7 +1822,11 @@ hipError_t launch_commit_verify(const gdn_tree_desc& d, const CommitVerifyArgs& 
             }
         }
     }
-    // other shapes: the commit, then the verify (the same result in two launches)
+    // other shapes: the commit, then the verify (the same result in two
+    // launches).  Nothing is launched unless both have a kernel: the commit
+    // writes the pool in place, so a verify refused after it would leave
+    // the call half done.
+    if (!verify_supported(d, va)) return hipErrorNotSupported;
     CommitArgs ca{a.path_rows, a.path_n, a.Lmax, a.k_prev, a.v_prev, a.rs_qk_prev, a.rs_v_prev,
                   a.alpha_prev, a.beta_prev, a.pool, va.P, va.state_idx, nullptr, nullptr, 0,
                   va.Hqk, va.Hv, va.D, va.dtype, va.flags & (GDN_F_NORM_QK | GDN_F_RAW_GATES), va.err, 1};
