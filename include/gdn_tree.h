@@ -14,7 +14,7 @@
  *   "Background" and the packed-buffer example).  parent = -1 means the
  *   committed state S_pre.
  *
- *   Four entry points, in the order one speculative step calls them:
+ *   Entry points, in the order one speculative step calls them:
  *     gdn_tree_desc_build   shared descriptor: validation, depth, strict-ancestor
  *                           mask, conv gather sources (LumoTree, Sec. III-C and V-C)
  *     conv_ancestry_gather  causal conv1d whose window for node i is its own
@@ -25,15 +25,26 @@
  *                           publish the state in place, and publish the conv
  *                           history along the same path (LumoTree, Sec. IV-B and
  *                           V-A; Bole review, Algorithm 2 Phase C)
- *   two that fuse the steady-state step (commit of the previous path with
- *   the conv and the verify of the next tree): conv_ancestry_gather_publish
- *   and gdn_tree_commit_verify; and gdn_path_resolve + gdn_layer_step, which
- *   run a whole layer's step in one launch.  These are declared at the end.
+ *     gdn_tree_commit_layers  the same commit for every layer in one launch
+ *   The steady-state step (commit of the previous path with the conv and the
+ *   verify of the next tree), once per step for all layers:
+ *     gdn_path_resolve      validate the previous path, resolve its rows
+ *     gdn_step_prepare      gdn_tree_desc_build + gdn_path_resolve, one launch
+ *   then per layer, either two launches
+ *     conv_ancestry_gather_publish, gdn_tree_commit_verify
+ *   or one:
+ *     gdn_layer_step
+ *   The softmax-attention layers of the same model, on the same descriptor:
+ *     gdn_tree_attention (+ gdn_tree_attention_workspace_bytes)
+ *     gdn_tree_attention_noalloc   the same without a workspace argument
+ *     gdn_tree_kv_publish   the accepted path's KV entries after the prefix
+ *   Host helpers: gdn_status_string, gdn_abi_version.
  *
  * Conventions shared by every call
  *   - Every pointer is device memory unless the comment says "host".  The
  *     caller owns every buffer; the library allocates nothing and keeps no
- *     mutable global state (reentrant).
+ *     mutable global state (reentrant), except the scratch array of
+ *     gdn_tree_attention_noalloc (see there).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *     the library never synchronises with the host.  The caller orders
  *     desc_build -> conv -> verify -> commit on one stream.
@@ -414,6 +425,23 @@ int32_t gdn_tree_attention(const gdn_tree_desc *d, const void *q, const void *k_
                            int32_t Hkv, int32_t D, float scale, int32_t flags, int32_t *err,
                            void *stream);
 
+/* gdn_tree_attention without the workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The split partial results go to
+ * a scratch array inside the library (GDN_ATTN_NOALLOC_SCRATCH_BYTES per GPU,
+ * held from the library's load until the process ends); the call allocates
+ * nothing.  Arguments and errors are those of gdn_tree_attention, plus
+ * GDN_ERR_UNSUPPORTED (nothing launched) when
+ * gdn_tree_attention_workspace_bytes(B, N, Hq, D, splits) exceeds the
+ * scratch size.  Every call on one GPU uses the same scratch: calls that
+ * overlap on a GPU (other streams, other threads) race and must be ordered
+ * by the caller.  The scratch's contents on entry do not matter. */
+#define GDN_ATTN_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
+int32_t gdn_tree_attention_noalloc(const gdn_tree_desc *d, const void *q, const void *k_cache,
+                                   const void *v_cache, int32_t S, const int32_t *ctx_len,
+                                   void *out, int32_t splits, int32_t Hq, int32_t Hkv, int32_t D,
+                                   float scale, int32_t flags, int32_t *err, void *stream);
+
 /* KV publication of the accepted path: for every request with n_b =
  * path_n[b] > 0, cache positions ctx_len[b] + j (j < n_b) receive the
  * entries at ctx_len[b] + path_rows[b][j] (every source is read before any
@@ -432,11 +460,11 @@ int32_t gdn_tree_kv_publish(const gdn_tree_desc *d_prev, const int32_t *path_row
 /* Human-readable name of a return code (host; static string). */
 const char *gdn_status_string(int32_t status);
 
-/* ABI version of this header: 6 (1, plus the two fused-step calls in 2,
+/* ABI version of this header: 7 (1, plus the two fused-step calls in 2,
  * plus gdn_path_resolve, gdn_step_prepare and gdn_layer_step in 3, plus
  * gdn_tree_commit_layers in 4, plus GDN_F_RAW_GATES and the gate_params
  * argument of verify, commit and the fused calls in 5, plus tree attention
- * and KV publication). */
+ * and KV publication in 6, plus gdn_tree_attention_noalloc). */
 int32_t gdn_abi_version(void);
 
 #ifdef __cplusplus

@@ -47,7 +47,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.gdn_abi_version() == 6
+    assert lib.gdn_abi_version() == 7
     assert lib.gdn_status_string(0) == b"ok"
     assert lib.gdn_status_string(-1) == b"invalid argument"
     assert lib.gdn_status_string(-4) == b"unsupported size"
@@ -225,6 +225,20 @@ def test_attention_argument_checks_fail_before_launch(lib):
     assert call(d=big_r) == g.GDN_ERR_UNSUPPORTED            # R > 64
     assert call(k=ctypes.c_void_p(264)) == g.GDN_ERR_ARG     # not 16-byte aligned
     assert call(ctx=None) == g.GDN_ERR_ARG
+    # the no-alloc variant: the same checks, and a request past its scratch
+    Z = lib.gdn_tree_attention_noalloc
+
+    def call_z(**kw):
+        a = dict(args)
+        a.update(kw)
+        return Z(a["d"], a["q"], a["k"], a["v"], a["S"], a["ctx"], a["out"], a["splits"], a["Hq"], a["Hkv"],
+                 a["D"], a["scale"], a["fl"], err, None)
+    assert call_z(D=64) == g.GDN_ERR_UNSUPPORTED
+    assert call_z(Hq=15) == g.GDN_ERR_ARG
+    assert call_z(scale=0.0) == g.GDN_ERR_ARG
+    assert call_z(out=None) == g.GDN_ERR_ARG
+    assert W(2, 27, 16, 256, 1024) > g.GDN_ATTN_NOALLOC_SCRATCH_BYTES
+    assert call_z(splits=1024) == g.GDN_ERR_UNSUPPORTED       # partials past the scratch
     K = lib.gdn_tree_kv_publish
     assert K(d, p, p, 0, p, p, 4096, p, 2, 256, err, None) == g.GDN_ERR_UNSUPPORTED
     assert K(d, p, p, 8, p, p, 4096, p, 2, 64, err, None) == g.GDN_ERR_UNSUPPORTED

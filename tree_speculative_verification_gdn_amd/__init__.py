@@ -28,7 +28,7 @@ __all__ = [
     "gdn_tree_desc_build", "conv_ancestry_gather", "gdn_tree_verify", "gdn_tree_commit",
     "gdn_tree_commit_layers", "conv_ancestry_gather_publish", "gdn_tree_commit_verify",
     "gdn_path_resolve", "gdn_step_prepare", "gdn_layer_step", "gdn_tree_attention_workspace_bytes",
-    "gdn_tree_attention", "gdn_tree_kv_publish",
+    "gdn_tree_attention", "gdn_tree_attention_noalloc", "GDN_ATTN_NOALLOC_SCRATCH_BYTES", "gdn_tree_kv_publish",
 ]
 
 # values mirror include/gdn_tree.h
@@ -37,11 +37,13 @@ GDN_EV_PARENT, GDN_EV_ROW, GDN_EV_STATE, GDN_EV_PATH, GDN_EV_CTX = 1, 2, 4, 8, 1
 GDN_DT_BF16, GDN_DT_F32 = 0, 1
 GDN_F_NORM_QK, GDN_F_OUT_BF16, GDN_F_VALU, GDN_F_RAW_GATES = 1, 2, 4, 8
 GDN_ACT_NONE, GDN_ACT_SILU = 0, 1
+GDN_ATTN_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 
 EXPORTED = ("gdn_tree_desc_build", "conv_ancestry_gather", "gdn_tree_verify",
             "gdn_tree_commit", "gdn_tree_commit_layers", "conv_ancestry_gather_publish", "gdn_tree_commit_verify",
             "gdn_path_resolve", "gdn_step_prepare", "gdn_layer_step",
-            "gdn_tree_attention_workspace_bytes", "gdn_tree_attention", "gdn_tree_kv_publish",
+            "gdn_tree_attention_workspace_bytes", "gdn_tree_attention", "gdn_tree_attention_noalloc",
+            "gdn_tree_kv_publish",
             "gdn_status_string", "gdn_abi_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -115,6 +117,9 @@ def load_library():
         lib.gdn_tree_attention.restype = i32
         lib.gdn_tree_attention.argtypes = [dp, vp, vp, vp, i32, vp, vp, vp, ctypes.c_size_t, i32, i32,
                                            i32, i32, ctypes.c_float, i32, vp, vp]
+        lib.gdn_tree_attention_noalloc.restype = i32
+        lib.gdn_tree_attention_noalloc.argtypes = [dp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32,
+                                                   ctypes.c_float, i32, vp, vp]
         lib.gdn_tree_kv_publish.restype = i32
         lib.gdn_tree_kv_publish.argtypes = [dp, vp, vp, i32, vp, vp, i32, vp, i32, i32, vp, vp]
         lib.gdn_status_string.restype = ctypes.c_char_p
@@ -383,6 +388,24 @@ def gdn_tree_attention(desc: TreeDesc, q, k_cache, v_cache, ctx_len, out, worksp
                                              int(splits), Hq, Hkv, D, scale, int(flags), _ptr(err),
                                              _stream(stream))
     return _check(code, "gdn_tree_attention", raise_on_error)
+
+
+def gdn_tree_attention_noalloc(desc: TreeDesc, q, k_cache, v_cache, ctx_len, out, err, splits: int,
+                               scale: float | None = None, flags: int = 0, stream=None,
+                               raise_on_error=True) -> int:
+    """gdn_tree_attention without a workspace: the split partials go to the
+    library's own scratch (GDN_ATTN_NOALLOC_SCRATCH_BYTES per GPU); the call
+    allocates nothing.  Calls that overlap on one GPU share that scratch."""
+    B, N, Hq, D = (int(x) for x in q.shape)
+    S, Hkv = int(k_cache.shape[1]), int(k_cache.shape[2])
+    for t, name in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (out, "out")):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    scale = 1.0 / float(D) ** 0.5 if scale is None else float(scale)
+    code = load_library().gdn_tree_attention_noalloc(desc.ref(), _ptr(q), _ptr(k_cache), _ptr(v_cache), S,
+                                                     _ptr(ctx_len), _ptr(out), int(splits), Hq, Hkv, D,
+                                                     scale, int(flags), _ptr(err), _stream(stream))
+    return _check(code, "gdn_tree_attention_noalloc", raise_on_error)
 
 
 def gdn_tree_kv_publish(prev: TreeDesc, path_rows, path_n, k_cache, v_cache, ctx_len, err,

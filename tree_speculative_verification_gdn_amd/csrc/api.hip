@@ -42,7 +42,7 @@ static int32_t check_gates(int32_t flags, const float* gate_params) {
     return (gate_params != nullptr && aligned(gate_params, 4)) ? GDN_OK : GDN_ERR_ARG;
 }
 
-int32_t gdn_abi_version(void) { return 6; }
+int32_t gdn_abi_version(void) { return 7; }
 
 const char* gdn_status_string(int32_t status) {
     switch (status) {
@@ -350,28 +350,61 @@ size_t gdn_tree_attention_workspace_bytes(int32_t B, int32_t N, int32_t Hq, int3
     return gdn::tree_attention_workspace_bytes(B, N, Hq, D, splits);
 }
 
-int32_t gdn_tree_attention(const gdn_tree_desc* d, const void* q, const void* k_cache,
-                           const void* v_cache, int32_t S, const int32_t* ctx_len, void* out,
-                           void* workspace, size_t workspace_bytes, int32_t splits, int32_t Hq,
-                           int32_t Hkv, int32_t D, float scale, int32_t flags, int32_t* err,
-                           void* stream) {
+namespace {
+
+// Argument checks shared by the two attention entry points (all but the
+// workspace).
+int32_t check_attention(const gdn_tree_desc* d, const void* q, const void* k_cache, const void* v_cache,
+                        int32_t S, const int32_t* ctx_len, const void* out, int32_t splits, int32_t Hq,
+                        int32_t Hkv, int32_t D, float scale, int32_t flags, const int32_t* err) {
     int32_t st = check_desc(d);
     if (st != GDN_OK) return st;
-    if (!q || !k_cache || !v_cache || !ctx_len || !out || !workspace || !err) return GDN_ERR_ARG;
+    if (!q || !k_cache || !v_cache || !ctx_len || !out || !err) return GDN_ERR_ARG;
     if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return GDN_ERR_ARG;
     if (D != 128 && D != 256) return GDN_ERR_UNSUPPORTED;
     if (d->R > 64) return GDN_ERR_UNSUPPORTED;
     if (splits < 1 || splits > 1024) return GDN_ERR_UNSUPPORTED;
     if (S < d->R) return GDN_ERR_ARG;
     if (!(scale > 0.0f) || (flags & ~GDN_F_OUT_BF16) != 0) return GDN_ERR_ARG;
-    if (workspace_bytes < gdn::tree_attention_workspace_bytes(d->B, d->N, Hq, D, splits)) return GDN_ERR_ARG;
-    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(workspace, 16) ||
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
         !aligned(out, (flags & GDN_F_OUT_BF16) ? 2 : 4))
         return GDN_ERR_ARG;
     const int64_t units = static_cast<int64_t>(d->B) * Hkv * (splits + 1) * Hq;
     if (units > 0x7fffffffLL || static_cast<int64_t>(d->B) * S * Hkv * D > (int64_t{1} << 40))
         return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+}  // namespace
+
+int32_t gdn_tree_attention(const gdn_tree_desc* d, const void* q, const void* k_cache,
+                           const void* v_cache, int32_t S, const int32_t* ctx_len, void* out,
+                           void* workspace, size_t workspace_bytes, int32_t splits, int32_t Hq,
+                           int32_t Hkv, int32_t D, float scale, int32_t flags, int32_t* err,
+                           void* stream) {
+    const int32_t st = check_attention(d, q, k_cache, v_cache, S, ctx_len, out, splits, Hq, Hkv, D, scale,
+                                       flags, err);
+    if (st != GDN_OK) return st;
+    if (!workspace || !aligned(workspace, 16)) return GDN_ERR_ARG;
+    if (workspace_bytes < gdn::tree_attention_workspace_bytes(d->B, d->N, Hq, D, splits)) return GDN_ERR_ARG;
     gdn::TreeAttnArgs a{q, k_cache, v_cache, S, ctx_len, out, workspace, splits, Hq, Hkv, D,
+                        scale, flags, err};
+    return map_launch(gdn::launch_tree_attention(*d, a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t gdn_tree_attention_noalloc(const gdn_tree_desc* d, const void* q, const void* k_cache,
+                                   const void* v_cache, int32_t S, const int32_t* ctx_len, void* out,
+                                   int32_t splits, int32_t Hq, int32_t Hkv, int32_t D, float scale,
+                                   int32_t flags, int32_t* err, void* stream) {
+    const int32_t st = check_attention(d, q, k_cache, v_cache, S, ctx_len, out, splits, Hq, Hkv, D, scale,
+                                       flags, err);
+    if (st != GDN_OK) return st;
+    if (gdn::tree_attention_workspace_bytes(d->B, d->N, Hq, D, splits) > gdn::kNoAllocScratchBytes)
+        return GDN_ERR_UNSUPPORTED;
+    hipError_t e = hipSuccess;
+    void* ws = gdn::noalloc_scratch(&e);
+    if (ws == nullptr) return GDN_ERR_HIP;
+    gdn::TreeAttnArgs a{q, k_cache, v_cache, S, ctx_len, out, ws, splits, Hq, Hkv, D,
                         scale, flags, err};
     return map_launch(gdn::launch_tree_attention(*d, a, static_cast<hipStream_t>(stream)));
 }

@@ -202,6 +202,10 @@ struct TreeAttnArgs {
     int32_t* err;
 };
 size_t tree_attention_workspace_bytes(int B, int N, int Hq, int D, int splits);
+// The no-alloc attention's scratch: its size, and its device address on the
+// current device (nullptr and *status set if that address cannot be had).
+constexpr size_t kNoAllocScratchBytes = GDN_ATTN_NOALLOC_SCRATCH_BYTES;
+void* noalloc_scratch(hipError_t* status);
 hipError_t launch_tree_attention(const gdn_tree_desc& d, const TreeAttnArgs& a, hipStream_t s);
 hipError_t launch_kv_publish(const gdn_tree_desc& prev, const int32_t* path_rows, const int32_t* path_n,
                              int Lmax, void* k, void* v, int S, const int32_t* ctx_len, int Hkv, int D,

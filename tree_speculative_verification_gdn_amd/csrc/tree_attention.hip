@@ -21,6 +21,8 @@
 // Layouts: q [B][N][Hq][D] logical node rows; k, v [B][S][Hkv][D] bf16, the
 // prefix at positions [0, ctx_len[b]), candidate physical row r at
 // ctx_len[b] + r.
+#include <mutex>
+
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -412,6 +414,41 @@ __global__ void __launch_bounds__(D) tree_attn_merge_kernel(const AttnArgs a) {
         static_cast<uint16_t*>(a.out)[oi] = f32_to_bf16_bits(val);
     else
         static_cast<float*>(a.out)[oi] = val;
+}
+
+// ---- scratch of the no-alloc entry point ---------------------------------
+// For callers that cannot allocate (code under HIP graph capture, tight
+// serving loops, harnesses that forbid hipMalloc): the split partial results
+// go to this file-scope array instead of a caller workspace.  Every GPU the
+// library runs on holds its own copy until the process ends; calls that
+// overlap on one GPU share it and race.  In host code its name is only a
+// stand-in: the device address comes from hipGetSymbolAddress, taken once
+// per device with that device current.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+void* noalloc_scratch(hipError_t* status) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess && (dev < 0 || dev >= kMaxDevices)) e = hipErrorInvalidDevice;
+    if (e != hipSuccess) {
+        *status = e;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr) {
+            *status = e != hipSuccess ? e : hipErrorInvalidSymbol;
+            return nullptr;
+        }
+        addr[dev] = ptr;
+    }
+    *status = hipSuccess;
+    return addr[dev];
 }
 
 size_t tree_attention_workspace_bytes(int B, int N, int Hq, int D, int splits) {
