@@ -26,6 +26,8 @@
  *                           history along the same path (LumoTree, Sec. IV-B and
  *                           V-A; Bole review, Algorithm 2 Phase C)
  *     gdn_tree_commit_layers  the same commit for every layer in one launch
+ *   The stored-U alternative to the replay commit:
+ *     gdn_tree_verify_store_u, gdn_tree_commit_factored
  *   The steady-state step (commit of the previous path with the conv and the
  *   verify of the next tree), once per step for all layers:
  *     gdn_path_resolve      validate the previous path, resolve its rows
@@ -208,6 +210,51 @@ int32_t gdn_tree_commit(const gdn_tree_desc *d, const int32_t *path, const int32
                         const void *x, void *hist, int32_t C, int32_t Hqk, int32_t Hv,
                         int32_t dk, int32_t dv, int32_t dtype, int32_t flags,
                         const float *gate_params, int32_t *err, void *stream);
+
+/* ---- stored-U mode (alternative to the replay commit) ---------------------
+ * Bole review, Sec. 5.2 (Algorithm 2 keeps the corrections U of its verify,
+ * Phase A, and publishes the accepted frontier's state from them, Phase C,
+ * by Eq. (10)); TreeWY, Sec. 3 (the same factored publish from
+ * pseudo-values).  The verify writes, besides o, every node's delta
+ * correction
+ *     u_i = b_i (v_i - a_i S_parent k^_i)
+ * (the rows of U in (I + G) U = R, Bole review, Lemma 2), and the commit
+ * rebuilds the frontier's state without replaying the path:
+ *     S_new = P_a S_pre + sum_{j on the path} (P_a / P_j) u_j k^_j^T
+ * (a the frontier, P_x the product of the decays on the root-to-x path).
+ * The stored U costs a write of B*R*Hv*dv*4 bytes per verify; the replay
+ * commit stores nothing. */
+
+/* gdn_tree_verify, plus u: float32 [B][R][Hv][dv], node rows written (the
+ * layout of a float32 out).  bf16 operands at d = 128 with N <= 32 run on the
+ * matrix cores (W = (I + G)^-1 solved along each root path beside M, then
+ * U = W R), other shapes on the vector ALU.  Arguments, flags and errors as
+ * gdn_tree_verify; u 4-byte aligned. */
+int32_t gdn_tree_verify_store_u(const gdn_tree_desc *d, const void *q, const void *k, const void *v,
+                                int64_t row_stride_qk, int64_t row_stride_v, const float *alpha,
+                                const float *beta, const float *state_pool, int32_t P,
+                                const int32_t *state_idx, void *out, float *u, int32_t Hqk,
+                                int32_t Hv, int32_t dk, int32_t dv, int32_t dtype, int32_t flags,
+                                const float *gate_params, int32_t *err, void *stream);
+
+/* Commit of the accepted path from stored corrections, in place: one rank-8
+ * matrix-core update of P_a S_pre per 8 path nodes, no sequential replay.
+ *   path, path_len, Lmax, state_pool, P, state_idx, err: as gdn_tree_commit
+ *   (same validation and error bits; len 0 leaves the state untouched)
+ *   k, row_stride_qk  the bf16 k rows the verify read (dk = dv = 128; k
+ *            8-byte aligned, stride a multiple of 4)
+ *   u        float32 [B][R][Hv][128] as gdn_tree_verify_store_u wrote it
+ *            (16-byte aligned)
+ *   alpha    float32 [B][R][Hv] (raw inputs with GDN_F_RAW_GATES)
+ * flags: GDN_F_NORM_QK, GDN_F_RAW_GATES (as the verify; gate_params as
+ * there).  No conv history: that publication goes through gdn_tree_commit
+ * or the fused calls. */
+int32_t gdn_tree_commit_factored(const gdn_tree_desc *d, const int32_t *path, const int32_t *path_len,
+                                 int32_t Lmax, const void *k, int64_t row_stride_qk, const float *u,
+                                 const float *alpha, float *state_pool, int32_t P,
+                                 const int32_t *state_idx, int32_t Hqk, int32_t Hv, int32_t dk,
+                                 int32_t dv, int32_t flags, const float *gate_params, int32_t *err,
+                                 void *stream);
 
 /* Commit of one accepted path into L layers' states in one launch (technical
  * review of Bole, Sec. 7, unified cross-layer state commit: one batched
@@ -460,11 +507,12 @@ int32_t gdn_tree_kv_publish(const gdn_tree_desc *d_prev, const int32_t *path_row
 /* Human-readable name of a return code (host; static string). */
 const char *gdn_status_string(int32_t status);
 
-/* ABI version of this header: 7 (1, plus the two fused-step calls in 2,
+/* ABI version of this header: 8 (1, plus the two fused-step calls in 2,
  * plus gdn_path_resolve, gdn_step_prepare and gdn_layer_step in 3, plus
  * gdn_tree_commit_layers in 4, plus GDN_F_RAW_GATES and the gate_params
  * argument of verify, commit and the fused calls in 5, plus tree attention
- * and KV publication in 6, plus gdn_tree_attention_noalloc). */
+ * and KV publication in 6, plus gdn_tree_attention_noalloc in 7, plus
+ * gdn_tree_verify_store_u and gdn_tree_commit_factored). */
 int32_t gdn_abi_version(void);
 
 #ifdef __cplusplus

@@ -72,7 +72,7 @@ def _bind(lib):
                              ci, i32p, f64p, f64p, ci, f64p]
     lib.ora_verify.restype = ci
     lib.ora_verify.argtypes = [ci, ci, ci, ci, i32p, i32p, i32p, f64p, f64p, f64p,
-                               f64p, f64p, f64p, ci, i32p, ci, ci, ci, ci, f64p, f64p]
+                               f64p, f64p, f64p, ci, i32p, ci, ci, ci, ci, f64p, f64p, f64p]
     lib.ora_commit.restype = ci
     lib.ora_commit.argtypes = [ci, ci, ci, ci, i32p, i32p, i32p, i32p, i32p, ci,
                                f64p, f64p, f64p, f64p, f64p, ci, i32p, ci, ci, ci,
@@ -215,7 +215,7 @@ def conv(node_row, conv_src, status, x, hist, state_idx, w, bias, act: int,
 
 def verify(parent, node_row, status, q, k, v, alpha, beta, pool, state_idx,
            Hqk: int, Hv: int, norm: bool, shared: bool = False,
-           want_states: bool = False, lib=None):
+           want_states: bool = False, want_u: bool = False, lib=None):
     """Tree verify in fp64: for every node i (topological order) and value head
     h, start from the parent's state (the committed state for parent -1), apply
     the gated delta update with node i's operands, read out o_i = S_i q_i.
@@ -225,7 +225,10 @@ def verify(parent, node_row, status, q, k, v, alpha, beta, pool, state_idx,
     "Background" (the parent is not the previous packed row).
     q, k: [B][R][Hqk][D]; v: [B][R][Hv][D]; alpha, beta: [B][R][Hv];
     pool: [P][Hv][D][D] (d_v x d_k, row-major); out: [B][R][Hv][D], NaN where
-    no node writes.  With ``want_states`` also returns S_i as [B][N][Hv][D][D].
+    no node writes.  With ``want_states`` also returns S_i as [B][N][Hv][D][D];
+    with ``want_u`` (last) every node's delta correction
+    u_i = beta_i (v_i - alpha_i S_parent k_i) as [B][R][Hv][D] (Bole review,
+    Lemma 2: the rows of U in (I + G) U = R).
     """
     lib = lib or load()
     q64, k64, v64 = as_f64(q), as_f64(k), as_f64(v)
@@ -237,6 +240,7 @@ def verify(parent, node_row, status, q, k, v, alpha, beta, pool, state_idx,
     P = p64.shape[0]
     out = np.full((B, R, Hv, D), np.nan, np.float64)
     states = np.full((B, N, Hv, D, D), np.nan, np.float64) if want_states else None
+    u = np.full((B, R, Hv, D), np.nan, np.float64) if want_u else None
     err = lib.ora_verify(B, N, R, int(shared), _p(_i32(parent), ctypes.c_int32),
                          _p(_i32(node_row), ctypes.c_int32), _p(_i32(status), ctypes.c_int32),
                          _p(q64, ctypes.c_double), _p(k64, ctypes.c_double),
@@ -244,10 +248,14 @@ def verify(parent, node_row, status, q, k, v, alpha, beta, pool, state_idx,
                          _p(b64, ctypes.c_double), _p(p64, ctypes.c_double), P,
                          _p(_i32(state_idx), ctypes.c_int32), Hqk, Hv, D, int(norm),
                          _p(out, ctypes.c_double),
-                         None if states is None else _p(states, ctypes.c_double))
+                         None if states is None else _p(states, ctypes.c_double),
+                         None if u is None else _p(u, ctypes.c_double))
+    res = (out, int(err))
     if want_states:
-        return out, int(err), states
-    return out, int(err)
+        res = res + (states,)
+    if want_u:
+        res = res + (u,)
+    return res
 
 
 def commit(parent, node_row, status, path, path_len, k, v, alpha, beta, pool,

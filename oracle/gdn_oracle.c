@@ -258,7 +258,7 @@ int ora_verify(int B, int N, int R, int shared, const int32_t *parent,
                const double *k, const double *v, const double *alpha,
                const double *beta, const double *pool, int P,
                const int32_t *state_idx, int Hqk, int Hv, int D, int norm,
-               double *out, double *states)
+               double *out, double *states, double *u_out)
 {
     int err = 0;
     char *ok = (char *)calloc((size_t)B, 1);
@@ -306,6 +306,14 @@ int ora_verify(int B, int N, int R, int shared, const int32_t *parent,
             gdn_update(S + (size_t)i * DD, Sp, alpha[gate], beta[gate], kv,
                        v + v_off, qv, u, o, D);
             memcpy(out + v_off, o, sizeof(double) * D);
+            if (u_out) { /* the node's delta correction u_i (Bole review, Lemma 2) */
+#if ORA_MUTATION == 10
+                for (int r = 0; r < D; r++) /* planted: u before the write strength */
+                    u_out[v_off + r] = u[r] / beta[gate];
+#else
+                memcpy(u_out + v_off, u, sizeof(double) * D);
+#endif
+            }
             if (states)
                 memcpy(states + (((size_t)b * N + i) * Hv + h) * DD,
                        S + (size_t)i * DD, sizeof(double) * DD);

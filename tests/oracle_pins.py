@@ -27,6 +27,10 @@ hold.  None of them re-types the oracle's own formula:
                          scaled by a positive factor; unit rows are (nearly)
                          left alone; a row of tiny norm becomes the first D
                          coordinates of the unit vector of (x, sqrt(1e-6))
+* pin_u_closed_form      the oracle's per-node delta corrections u_i == the
+                         rows of U from the dense solve of (I + G) U = R
+                         (Bole review, Lemma 2), and Eq. (10) from them ==
+                         the oracle's commit
 * pin_conv_publish       the history a commit publishes continues the causal
                          conv: the next tree's conv == numpy.convolve over
                          old history ++ accepted inputs ++ new inputs
@@ -493,6 +497,47 @@ def pin_norm_invariance(lib):
     assert relerr(out_tiny[0, rows], out_ref[0, rows]) < 1e-12
 
 
+def pin_u_closed_form(lib):
+    g = np.random.default_rng(37)
+    pars = [random_parent(g, 13, bmax=2), random_parent(g, 13, bmax=4)]
+    pb = small_problem(63, pars, D=10, Hv=2, Hqk=1)
+    out, err, u = oracle.verify(pb["parent"], pb["node_row"], np.zeros(2, np.int32), pb["q"], pb["k"],
+                                pb["v"], pb["alpha"], pb["beta"], pb["pool"], pb["state_idx"], pb["Hqk"],
+                                pb["Hv"], False, want_u=True, lib=lib)
+    assert err == 0
+    d = oracle.desc_build(pb["parent"], pb["node_row"], pb["R"], 1, lib=lib)
+    for b in range(pb["B"]):
+        rows = pb["node_row"][b]
+        for h in range(pb["Hv"]):
+            ops = [operands(pb, b, h, i) for i in range(pb["N"])]
+            Q, K, V = (np.stack([o[c] for o in ops]) for c in range(3))
+            al = np.array([o[3] for o in ops])
+            be = np.array([o[4] for o in ops])
+            S0 = pb["pool"][pb["state_idx"][b], h]
+            _, U = cf.solve_tree(pars[b], al, be, Q, K, V, S0)
+            assert relerr(u[b, rows, h], U) < 1e-11, "u differs from the solve of (I + G) U = R"
+        # Eq. (10) with the oracle's own u == the oracle's replayed commit
+        fr = int(np.argmax([len(a) for a in cf.ancestors(pars[b])]))
+        pth = cf.ancestors(pars[b])[fr] + [fr]
+        path = np.full((pb["B"], 13), -1, np.int32)
+        path[:, :len(pth)] = pth
+        plen = np.zeros(pb["B"], np.int32)
+        plen[b] = len(pth)
+        path_b = path.copy()
+        if b == 0:
+            path_b[1] = -1
+        pool_new, _, err = oracle.commit(pb["parent"], pb["node_row"], d["status"], path_b, plen, pb["k"],
+                                         pb["v"], pb["alpha"], pb["beta"], pb["pool"], pb["state_idx"],
+                                         pb["Hqk"], pb["Hv"], False, lib=lib)
+        assert err == 0
+        for h in range(pb["Hv"]):
+            ops = [operands(pb, b, h, i) for i in range(pb["N"])]
+            K = np.stack([o[1] for o in ops])
+            al = np.array([o[3] for o in ops])
+            Snew = cf.commit_factorized(pars[b], al, pth, K, u[b, rows, h], pb["pool"][pb["state_idx"][b], h])
+            assert relerr(pool_new[pb["state_idx"][b], h], Snew) < 1e-11
+
+
 def pin_conv_publish(lib):
     """The conv history a commit publishes is what the causal conv of the
     token sequence needs next (LumoTree, Sec. V-A: the accepted path drives
@@ -551,7 +596,7 @@ ALL_PINS = [
     pin_chain_textbook, pin_paths_are_chains, pin_sibling_isolation, pin_commit_is_replay,
     pin_closed_form, pin_treewy_states, pin_nilpotent, pin_factorized_commit, pin_pure_decay,
     pin_delta_write, pin_conv_chain, pin_conv_tree_paths, pin_conv_w1, pin_desc_enumeration,
-    pin_norm_flag, pin_norm_invariance, pin_conv_publish,
+    pin_norm_flag, pin_norm_invariance, pin_conv_publish, pin_u_closed_form,
 ]
 
 

@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
     for name in ("gdn_tree_desc_build", "conv_ancestry_gather", "gdn_tree_verify", "gdn_tree_commit",
                  "gdn_tree_commit_layers", "conv_ancestry_gather_publish", "gdn_tree_commit_verify",
                  "gdn_path_resolve", "gdn_step_prepare", "gdn_layer_step", "gdn_tree_attention",
-                 "gdn_tree_kv_publish"):
+                 "gdn_tree_kv_publish", "gdn_tree_verify_store_u", "gdn_tree_commit_factored"):
         assert name in decl
     assert set(decl) == set(g.EXPORTED)
 
@@ -47,7 +47,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.gdn_abi_version() == 7
+    assert lib.gdn_abi_version() == 8
     assert lib.gdn_status_string(0) == b"ok"
     assert lib.gdn_status_string(-1) == b"invalid argument"
     assert lib.gdn_status_string(-4) == b"unsupported size"
@@ -86,6 +86,20 @@ def test_argument_checks_fail_before_launch(lib):
     assert Cm(d, p, p, 0, p, p, 2048, 4096, p, p, p, 4, p, None, None, 0, 16, 32, 128, 128, 0, 0, None, err, None) == g.GDN_ERR_UNSUPPORTED
     assert Cm(d, p, p, 65, p, p, 2048, 4096, p, p, p, 4, p, None, None, 0, 16, 32, 128, 128, 0, 0, None, err, None) == g.GDN_ERR_UNSUPPORTED
     assert Cm(d, p, p, 7, p, p, 2048, 4096, p, p, p, 4, p, p, None, 8, 16, 32, 128, 128, 0, 0, None, err, None) == g.GDN_ERR_ARG
+    # stored-U verify: no u buffer, misaligned u; factored commit: d != 128,
+    # unknown flag, Lmax out of range, misaligned u
+    VU = lib.gdn_tree_verify_store_u
+    assert VU(d, p, p, p, 2048, 4096, p, p, p, 4, p, p, None, 16, 32, 128, 128, 0, 0, None, err, None) == g.GDN_ERR_ARG
+    assert VU(d, p, p, p, 2048, 4096, p, p, p, 4, p, p, ctypes.c_void_p(258), 16, 32, 128, 128, 0, 0, None, err,
+              None) == g.GDN_ERR_ARG
+    assert VU(d, p, p, p, 2048, 4096, p, p, p, 4, p, p, p, 16, 32, 128, 128, 0, 64, None, err, None) == g.GDN_ERR_ARG
+    CF = lib.gdn_tree_commit_factored
+    assert CF(d, p, p, 7, p, 2048, p, p, p, 4, p, 16, 32, 64, 64, 0, None, err, None) == g.GDN_ERR_UNSUPPORTED
+    assert CF(d, p, p, 7, p, 2048, p, p, p, 4, p, 16, 32, 128, 128, g.GDN_F_OUT_BF16, None, err, None) == g.GDN_ERR_ARG
+    assert CF(d, p, p, 65, p, 2048, p, p, p, 4, p, 16, 32, 128, 128, 0, None, err, None) == g.GDN_ERR_UNSUPPORTED
+    assert CF(d, p, p, 7, p, 2048, ctypes.c_void_p(264), p, p, 4, p, 16, 32, 128, 128, 0, None, err,
+              None) == g.GDN_ERR_ARG
+    assert CF(d, p, p, 7, p, 2046, p, p, p, 4, p, 16, 32, 128, 128, 0, None, err, None) == g.GDN_ERR_ARG
     # commit over layers (B = 2, R = 8: 16 rows; P = 4): no layers, overlapping
     # layer strides, an unknown flag, a pool stride that breaks alignment
     Cl = lib.gdn_tree_commit_layers

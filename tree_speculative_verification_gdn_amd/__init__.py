@@ -27,6 +27,7 @@ __all__ = [
     "GDN_ACT_NONE", "GDN_ACT_SILU", "GdnError", "TreeDesc", "library_path", "load_library",
     "gdn_tree_desc_build", "conv_ancestry_gather", "gdn_tree_verify", "gdn_tree_commit",
     "gdn_tree_commit_layers", "conv_ancestry_gather_publish", "gdn_tree_commit_verify",
+    "gdn_tree_verify_store_u", "gdn_tree_commit_factored",
     "gdn_path_resolve", "gdn_step_prepare", "gdn_layer_step", "gdn_tree_attention_workspace_bytes",
     "gdn_tree_attention", "gdn_tree_attention_noalloc", "GDN_ATTN_NOALLOC_SCRATCH_BYTES", "gdn_tree_kv_publish",
 ]
@@ -40,6 +41,7 @@ GDN_ACT_NONE, GDN_ACT_SILU = 0, 1
 GDN_ATTN_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 
 EXPORTED = ("gdn_tree_desc_build", "conv_ancestry_gather", "gdn_tree_verify",
+            "gdn_tree_verify_store_u", "gdn_tree_commit_factored",
             "gdn_tree_commit", "gdn_tree_commit_layers", "conv_ancestry_gather_publish", "gdn_tree_commit_verify",
             "gdn_path_resolve", "gdn_step_prepare", "gdn_layer_step",
             "gdn_tree_attention_workspace_bytes", "gdn_tree_attention", "gdn_tree_attention_noalloc",
@@ -90,6 +92,12 @@ def load_library():
         lib.gdn_tree_verify.restype = i32
         lib.gdn_tree_verify.argtypes = [dp, vp, vp, vp, i64, i64, vp, vp, vp, i32, vp, vp,
                                         i32, i32, i32, i32, i32, i32, vp, vp, vp]
+        lib.gdn_tree_verify_store_u.restype = i32
+        lib.gdn_tree_verify_store_u.argtypes = [dp, vp, vp, vp, i64, i64, vp, vp, vp, i32, vp, vp, vp,
+                                                i32, i32, i32, i32, i32, i32, vp, vp, vp]
+        lib.gdn_tree_commit_factored.restype = i32
+        lib.gdn_tree_commit_factored.argtypes = [dp, vp, vp, i32, vp, i64, vp, vp, vp, i32, vp, i32, i32,
+                                                 i32, i32, i32, vp, vp, vp]
         lib.gdn_tree_commit.restype = i32
         lib.gdn_tree_commit.argtypes = [dp, vp, vp, i32, vp, vp, i64, i64, vp, vp, vp, i32, vp,
                                         vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp]
@@ -262,6 +270,41 @@ def gdn_tree_verify(desc: TreeDesc, q, k, v, alpha, beta, state_pool, state_idx,
                                           _dtype_code(q), _gate_flags(flags, gate_params),
                                           _ptr(gate_params), _ptr(err), _stream(stream))
     return _check(code, "gdn_tree_verify", raise_on_error)
+
+
+def gdn_tree_verify_store_u(desc: TreeDesc, q, k, v, alpha, beta, state_pool, state_idx, out, u, err,
+                            flags: int = 0, stream=None, raise_on_error=True, gate_params=None) -> int:
+    """gdn_tree_verify, plus every node's delta correction into u (fp32
+    [B, R, Hv, D], the layout of out)."""
+    rs_qk, Hqk, dk = _rows_view(q, "q")
+    rs_k, Hk, dk2 = _rows_view(k, "k")
+    rs_v, Hv, dv = _rows_view(v, "v")
+    if rs_k != rs_qk or Hk != Hqk or dk2 != dk or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q and k must share layout and dtype with v")
+    P = int(state_pool.shape[0])
+    code = load_library().gdn_tree_verify_store_u(desc.ref(), _ptr(q), _ptr(k), _ptr(v), rs_qk, rs_v,
+                                                  _ptr(alpha), _ptr(beta), _ptr(state_pool), P,
+                                                  _ptr(state_idx), _ptr(out), _ptr(u), Hqk, Hv, dk, dv,
+                                                  _dtype_code(q), _gate_flags(flags, gate_params),
+                                                  _ptr(gate_params), _ptr(err), _stream(stream))
+    return _check(code, "gdn_tree_verify_store_u", raise_on_error)
+
+
+def gdn_tree_commit_factored(desc: TreeDesc, path, path_len, k, u, alpha, state_pool, state_idx, err,
+                             flags: int = 0, stream=None, raise_on_error=True, gate_params=None) -> int:
+    """Commit path [B, Lmax] (len path_len [B]) into state_pool in place from
+    the stored corrections u [B, R, Hv, 128] (S = P_a S_pre + sum (P_a/P_j)
+    u_j k_j^T) and the bf16 k rows [B, R, Hqk, 128]."""
+    rs_qk, Hqk, dk = _rows_view(k, "k")
+    Hv = int(u.shape[2])
+    P = int(state_pool.shape[0])
+    Lmax = int(path.shape[1])
+    code = load_library().gdn_tree_commit_factored(desc.ref(), _ptr(path), _ptr(path_len), Lmax, _ptr(k),
+                                                   rs_qk, _ptr(u), _ptr(alpha), _ptr(state_pool), P,
+                                                   _ptr(state_idx), Hqk, Hv, dk, int(u.shape[3]),
+                                                   _gate_flags(flags, gate_params), _ptr(gate_params),
+                                                   _ptr(err), _stream(stream))
+    return _check(code, "gdn_tree_commit_factored", raise_on_error)
 
 
 def gdn_tree_commit(desc: TreeDesc, path, path_len, k, v, alpha, beta, state_pool, state_idx,

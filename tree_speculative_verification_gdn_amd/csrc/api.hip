@@ -42,7 +42,7 @@ static int32_t check_gates(int32_t flags, const float* gate_params) {
     return (gate_params != nullptr && aligned(gate_params, 4)) ? GDN_OK : GDN_ERR_ARG;
 }
 
-int32_t gdn_abi_version(void) { return 7; }
+int32_t gdn_abi_version(void) { return 8; }
 
 const char* gdn_status_string(int32_t status) {
     switch (status) {
@@ -103,6 +103,50 @@ int32_t gdn_tree_verify(const gdn_tree_desc* d, const void* q, const void* k, co
     gdn::VerifyArgs a{q, k, v, row_stride_qk, row_stride_v, alpha, beta, state_pool, P,
                       state_idx, out, Hqk, Hv, dk, dtype, flags, err, gate_params};
     return map_launch(gdn::launch_verify(*d, a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t gdn_tree_verify_store_u(const gdn_tree_desc* d, const void* q, const void* k, const void* v,
+                                int64_t row_stride_qk, int64_t row_stride_v, const float* alpha,
+                                const float* beta, const float* state_pool, int32_t P,
+                                const int32_t* state_idx, void* out, float* u, int32_t Hqk, int32_t Hv,
+                                int32_t dk, int32_t dv, int32_t dtype, int32_t flags,
+                                const float* gate_params, int32_t* err, void* stream) {
+    int32_t st = check_desc(d);
+    if (st != GDN_OK) return st;
+    st = check_heads(Hqk, Hv, dk, dv, dtype);
+    if (st != GDN_OK) return st;
+    if (!q || !k || !v || !alpha || !beta || !state_pool || !state_idx || !out || !u || !err || P < 1)
+        return GDN_ERR_ARG;
+    if ((flags & ~(GDN_F_NORM_QK | GDN_F_OUT_BF16 | GDN_F_VALU | GDN_F_RAW_GATES)) != 0) return GDN_ERR_ARG;
+    if (check_gates(flags, gate_params) != GDN_OK) return GDN_ERR_ARG;
+    if (row_stride_qk < static_cast<int64_t>(Hqk) * dk || row_stride_v < static_cast<int64_t>(Hv) * dv)
+        return GDN_ERR_ARG;
+    if (!aligned(state_pool, 16) || !aligned(u, 4)) return GDN_ERR_ARG;
+    gdn::VerifyArgs a{q, k, v, row_stride_qk, row_stride_v, alpha, beta, state_pool, P,
+                      state_idx, out, Hqk, Hv, dk, dtype, flags, err, gate_params, u};
+    return map_launch(gdn::launch_verify(*d, a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t gdn_tree_commit_factored(const gdn_tree_desc* d, const int32_t* path, const int32_t* path_len,
+                                 int32_t Lmax, const void* k, int64_t row_stride_qk, const float* u,
+                                 const float* alpha, float* state_pool, int32_t P, const int32_t* state_idx,
+                                 int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv, int32_t flags,
+                                 const float* gate_params, int32_t* err, void* stream) {
+    int32_t st = check_desc(d);
+    if (st != GDN_OK) return st;
+    st = check_heads(Hqk, Hv, dk, dv, GDN_DT_BF16);
+    if (st != GDN_OK) return st;
+    if (dk != 128) return GDN_ERR_UNSUPPORTED;
+    if (!path || !path_len || !k || !u || !alpha || !state_pool || !state_idx || !err || P < 1)
+        return GDN_ERR_ARG;
+    if (Lmax < 1 || Lmax > GDN_MAX_NODES) return GDN_ERR_UNSUPPORTED;
+    if ((flags & ~(GDN_F_NORM_QK | GDN_F_RAW_GATES)) != 0) return GDN_ERR_ARG;
+    if (check_gates(flags, gate_params) != GDN_OK) return GDN_ERR_ARG;
+    if (row_stride_qk < static_cast<int64_t>(Hqk) * dk || row_stride_qk % 4 != 0) return GDN_ERR_ARG;
+    if (!aligned(k, 8) || !aligned(u, 16) || !aligned(state_pool, 16)) return GDN_ERR_ARG;
+    gdn::FactoredCommitArgs a{path, path_len, Lmax, k, row_stride_qk, u, alpha, state_pool, P, state_idx,
+                              Hqk, Hv, flags, err, gate_params};
+    return map_launch(gdn::launch_commit_factored(*d, a, static_cast<hipStream_t>(stream)));
 }
 
 int32_t gdn_tree_commit(const gdn_tree_desc* d, const int32_t* path, const int32_t* path_len,

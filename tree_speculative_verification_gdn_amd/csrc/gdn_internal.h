@@ -104,6 +104,7 @@ struct VerifyArgs {
     int dtype, flags;
     int32_t* err;
     const float* gate_params = nullptr;  // [2][Hv] A_log, dt_bias with GDN_F_RAW_GATES
+    float* u = nullptr;  // stored-U mode: every node's delta correction [B][R][Hv][D], or none
 };
 // Returns hipErrorNotSupported (without launching) when no kernel covers the
 // shape; the API maps that to GDN_ERR_UNSUPPORTED.
@@ -138,6 +139,25 @@ struct CommitArgs {
 };
 hipError_t launch_commit(const gdn_tree_desc& d, const CommitArgs& a, hipStream_t s);
 size_t commit_lds_bytes(int Lmax, int D, int dtype);
+
+// Commit from the delta corrections a stored-U verify wrote (bf16 k, d = 128).
+struct FactoredCommitArgs {
+    const int32_t* path;      // logical ids [B][Lmax]
+    const int32_t* path_len;  // [B]
+    int Lmax;
+    const void* k;            // bf16 k rows, row stride rs_qk
+    int64_t rs_qk;
+    const float* u;           // [B][R][Hv][128]
+    const float* alpha;       // [B][R][Hv] (raw inputs with GDN_F_RAW_GATES)
+    float* pool;
+    int P;
+    const int32_t* state_idx;
+    int Hqk, Hv, flags;
+    int32_t* err;
+    const float* gate_params;
+};
+hipError_t launch_commit_factored(const gdn_tree_desc& d, const FactoredCommitArgs& a, hipStream_t s);
+size_t commit_factored_lds_bytes(int Lmax);
 
 // Commit of the previous step's accepted path followed by the verify of the
 // next tree, from the committed state (one launch on the matrix-core path).

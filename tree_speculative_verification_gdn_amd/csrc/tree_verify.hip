@@ -55,13 +55,15 @@ struct MfmaLds {
     // layout), v rows, gates, k scales, rows; placed over the Gram block when
     // it fits (the Gram block is dead by the time the path is staged)
     int kp, vp, alp, bep, scp, rowp;
+    // stored-U verify: hi / lo halves of W = (I + G)^-1 (the M halves' layout)
+    int wh, wl;
     // one-launch layer step: conv staging (tree, path), conv weights and
     // bias, tap rows, parents, and the staging of a later path segment's conv
     int xg, pc, wts, bia, tap, par, stg, sw, sb;
 };
 
 
-__host__ __device__ inline MfmaLds mfma_lds_layout(int N, int NPB, int Lp = 0) {
+__host__ __device__ inline MfmaLds mfma_lds_layout(int N, int NPB, int Lp = 0, bool wsolve = false) {
     MfmaLds L{};
     const int NP = 32 * NPB;
     const int MB = 2 * NPB;
@@ -79,6 +81,10 @@ __host__ __device__ inline MfmaLds mfma_lds_layout(int N, int NPB, int Lp = 0) {
     if (NPB == 1) {
         L.mh = off;   off += align_up(NP * L.mstride, 16);
         L.ml = off;   off += align_up(NP * L.mstride, 16);
+        if (wsolve) {
+            L.wh = off;   off += align_up(NP * L.mstride, 16);
+            L.wl = off;   off += align_up(NP * L.mstride, 16);
+        }
     } else {
         // wide trees: M is solved in place of the q.k triangle (fp32) and read
         // from it, masked by the ancestor bits, as the readout's operand
@@ -198,6 +204,7 @@ constexpr int kModeVerify = 0;
 constexpr int kModeCommitVerify = 1;
 constexpr int kModeLayer = 2;      // paths of at most kMfmaPath nodes (Lmax <= kMfmaPath)
 constexpr int kModeLayerLong = 3;  // any Lmax: later path segments convolved inside the replay
+constexpr int kModeVerifyU = 4;    // verify that also writes every node's delta correction u_i
 
 }  // namespace
 
@@ -225,11 +232,18 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                        const float* __restrict__ beta, float* __restrict__ pool, int P,
                        const int32_t* __restrict__ state_idx, void* __restrict__ out, int Hqk,
                        int Hv, int norm, int out_bf16, int32_t* __restrict__ err,
-                       const float* __restrict__ gate_params, const CommitPrev cp, const LayerIn li) {
+                       const float* __restrict__ gate_params, const CommitPrev cp, const LayerIn li,
+                       float* __restrict__ u_out) {
     constexpr bool FUSED = MODE == kModeCommitVerify;  // commit of a path given as k/v rows
     constexpr bool LAYER = MODE == kModeLayer || MODE == kModeLayerLong;  // the whole layer step
     constexpr bool LONGP = MODE == kModeLayerLong;
     constexpr bool COMMIT = FUSED || LAYER;
+    // stored-U mode (Bole review, Sec. 5.2, Algorithm 2 steps 5-7): besides
+    // M = C (I + G)^-1 the path solve forms W = (I + G)^-1 (the same
+    // elimination from the identity), and U = W R, every node's u_i, is
+    // written out for a later factorised commit
+    constexpr bool STOREU = MODE == kModeVerifyU;
+    static_assert(!STOREU || NPB == 1, "stored-U verify: N <= 32 on the matrix cores");
     constexpr int H = CW > 0 ? CW - 1 : 0;             // conv history entries (layer step)
     constexpr int kWP = (CW + 1) / 2;                  // conv tap pairs per channel
     static_assert(!LAYER || (NPB == 1 && CW >= 1 && CW <= 4), "layer step: N <= 32, 1 <= W <= 4");
@@ -238,7 +252,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     constexpr int kKQItems = MB * 32 * 32 / kThreads;       // 8-byte K/Q chunks per thread
     constexpr int kVItems = (NP * 32 + kThreads - 1) / kThreads;
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    const MfmaLds L = LAYER ? layer_lds_layout(N, H, li.Lmax) : mfma_lds_layout(N, NPB, FUSED ? cp.Lmax : 0);
+    const MfmaLds L = LAYER ? layer_lds_layout(N, H, li.Lmax) : mfma_lds_layout(N, NPB, FUSED ? cp.Lmax : 0, STOREU);
     char* s_a = lds + L.a;
     uint16_t* s_v = reinterpret_cast<uint16_t*>(lds + L.v);
     float* s_gk = reinterpret_cast<float*>(lds + L.gk);
@@ -708,6 +722,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
             for (int e = tid; e < NP * mstride / 4; e += kThreads) {
                 reinterpret_cast<uint32_t*>(s_mh)[e] = 0u;
                 reinterpret_cast<uint32_t*>(s_ml)[e] = 0u;
+                if constexpr (STOREU) {
+                    reinterpret_cast<uint32_t*>(lds + L.wh)[e] = 0u;
+                    reinterpret_cast<uint32_t*>(lds + L.wl)[e] = 0u;
+                }
             }
         }
         if constexpr (LAYER) {  // K/Q/V rows are staged; squared norms from them
@@ -835,10 +853,15 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                 }
                 // r = P_i / P_j now
                 float val = r * s_sq[ii] * sk_j * s_gq[ii * (ii + 1) / 2 + j];
+                float wval = p == d - 1 ? 1.0f : 0.0f;  // W row i starts as the identity's
     #pragma unroll
                 for (int sp = kLP - 1; sp >= 1; --sp) {
                     const float ms = __shfl(val, grp_lane0 | sp, 64);  // final M at position sp
                     val = (sp < d && p < sp) ? fmaf(-ms, gco[sp], val) : val;
+                    if constexpr (STOREU) {
+                        const float ws = __shfl(wval, grp_lane0 | sp, 64);
+                        wval = (sp < d && p < sp) ? fmaf(-ws, gco[sp], wval) : wval;
+                    }
                 }
                 if (act) {
                     if constexpr (NPB == 1) {
@@ -847,6 +870,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                         const uint32_t lv = cvt_pk_bf16(rest, 0.0f) & 0xffffu;
                         reinterpret_cast<uint16_t*>(s_mh + i * mstride)[j] = static_cast<uint16_t>(hv);
                         reinterpret_cast<uint16_t*>(s_ml + i * mstride)[j] = static_cast<uint16_t>(lv);
+                        if constexpr (STOREU) {
+                            const uint32_t hw = cvt_pk_bf16(wval, 0.0f) & 0xffffu;
+                            const uint32_t lw2 = cvt_pk_bf16(wval - __uint_as_float(hw << 16), 0.0f) & 0xffffu;
+                            reinterpret_cast<uint16_t*>(lds + L.wh + i * mstride)[j] = static_cast<uint16_t>(hw);
+                            reinterpret_cast<uint16_t*>(lds + L.wl + i * mstride)[j] = static_cast<uint16_t>(lw2);
+                        }
                     } else {
                         s_gq[i * (i + 1) / 2 + j] = val;  // only this lane reads that entry
                     }
@@ -929,6 +958,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                     }
                     const float sk_j = s_sk[jj];
                     float val = wq * sq_i * sk_j * mrow[jj];
+                    float wval = pp == d - 1 ? 1.0f : 0.0f;  // W row i: the identity's
                     float wg = 1.0f;
                     for (int sp = pp + 1; sp < d; ++sp) {
                         int m;
@@ -946,6 +976,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                         else
                             msv = mrow[m];
                         val = fmaf(-msv, gmj, val);
+                        if constexpr (STOREU) {
+                            const uint16_t* wh = reinterpret_cast<const uint16_t*>(lds + L.wh + i * mstride);
+                            const uint16_t* wl = reinterpret_cast<const uint16_t*>(lds + L.wl + i * mstride);
+                            wval = fmaf(-(bf16_bits_to_f32(wh[m]) + bf16_bits_to_f32(wl[m])), gmj, wval);
+                        }
                     }
                     if constexpr (NPB == 1) {
                         const uint32_t hv = cvt_pk_bf16(val, 0.0f) & 0xffffu;
@@ -953,6 +988,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                         const uint32_t lv = cvt_pk_bf16(rest, 0.0f) & 0xffffu;
                         mh[jj] = static_cast<uint16_t>(hv);
                         ml[jj] = static_cast<uint16_t>(lv);
+                        if constexpr (STOREU) {
+                            const uint32_t hw = cvt_pk_bf16(wval, 0.0f) & 0xffffu;
+                            const uint32_t lw2 = cvt_pk_bf16(wval - __uint_as_float(hw << 16), 0.0f) & 0xffffu;
+                            reinterpret_cast<uint16_t*>(lds + L.wh + i * mstride)[jj] = static_cast<uint16_t>(hw);
+                            reinterpret_cast<uint16_t*>(lds + L.wl + i * mstride)[jj] = static_cast<uint16_t>(lw2);
+                        }
                     } else {
                         mrow[jj] = val;
                     }
@@ -1300,6 +1341,22 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                 store_out(out, ((rowb + s_rows[i]) * Hv + h) * kD + r_own, o[e], out_bf16 != 0);
         }
     }
+    if constexpr (STOREU) {  // U = W R: row i of U is node i's delta correction
+        f32x16_t uacc = {};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const bf16x8_t wh = lds_operand_m(lds + L.wh, mstride, l32, ks, hf);
+            const bf16x8_t wl = lds_operand_m(lds + L.wl, mstride, l32, ks, hf);
+            uacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh, rhi[ks], uacc, 0, 0, 0);
+            uacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh, rlo[ks], uacc, 0, 0, 0);
+            uacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl, rhi[ks], uacc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int i = 8 * (e >> 2) + 4 * hf + (e & 3);
+            if (i < N) u_out[((rowb + s_rows[i]) * Hv + h) * kD + r_own] = uacc[e];
+        }
+    }
 }
 
 // ===========================================================================
@@ -1351,7 +1408,7 @@ __global__ void __launch_bounds__(kThreads)
                        const float* __restrict__ beta, const float* __restrict__ pool, int P,
                        const int32_t* __restrict__ state_idx, void* __restrict__ out, int Hqk,
                        int Hv, int norm, int out_bf16, int32_t* __restrict__ err,
-                       const float* __restrict__ gate_params) {
+                       const float* __restrict__ gate_params, float* __restrict__ u_out) {
     constexpr int TPR = kThreads / D;  // lanes per value row
     constexpr int EPT = D / TPR;       // state elements per lane
     constexpr int NQ = EPT / 4;        // float4 chunks per lane
@@ -1490,6 +1547,7 @@ __global__ void __launch_bounds__(kThreads)
             s_U[i * D + r] = u;
             const size_t oi = ((static_cast<size_t>(b) * R + s_rows[i]) * Hv + h) * D + r;
             store_out(out, oi, o, out_bf16 != 0);
+            if (u_out) u_out[oi] = u;  // stored-U mode
         }
     }
 }
@@ -1518,7 +1576,7 @@ hipError_t launch_mfma_raw(const gdn_tree_desc& d, const VerifyArgs& a, float* p
                        d.depth, d.status, static_cast<const uint16_t*>(a.q),
                        static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                        a.rs_qk, a.rs_v, a.alpha, a.beta, pool, a.P, a.state_idx, a.out, a.Hqk,
-                       a.Hv, norm, obf, a.err, a.gate_params, cp, li);
+                       a.Hv, norm, obf, a.err, a.gate_params, cp, li, a.u);
     return hipGetLastError();
 }
 
@@ -1544,7 +1602,7 @@ hipError_t launch_valu_t(const gdn_tree_desc& d, const VerifyArgs& a, int norm, 
                        d.status, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.rs_qk, a.rs_v, a.alpha, a.beta, a.pool, a.P,
                        a.state_idx, a.out, a.Hqk, a.Hv, norm, obf, a.err,
-                       (a.flags & GDN_F_RAW_GATES) ? a.gate_params : nullptr);
+                       (a.flags & GDN_F_RAW_GATES) ? a.gate_params : nullptr, a.u);
     return hipGetLastError();
 }
 }  // namespace
@@ -1560,9 +1618,9 @@ bool verify_uses_mfma(const gdn_tree_desc& d, const VerifyArgs& a) {
 // Whether launch_verify has a kernel for these arguments (checked by the
 // fused call before it launches anything).
 bool verify_supported(const gdn_tree_desc& d, const VerifyArgs& a) {
-    if (verify_uses_mfma(d, a)) {
-        const int NPB = (d.N + 31) / 32;
-        return NPB <= 2 && static_cast<size_t>(mfma_lds_layout(d.N, NPB).total) <= kMaxLds;
+    const int NPB = (d.N + 31) / 32;
+    if (verify_uses_mfma(d, a) && (a.u == nullptr || NPB == 1)) {
+        return NPB <= 2 && static_cast<size_t>(mfma_lds_layout(d.N, NPB, 0, a.u != nullptr).total) <= kMaxLds;
     }
     return (a.D == 32 || a.D == 64 || a.D == 128) && verify_valu_lds_bytes(d.N, a.D) <= kMaxLds;
 }
@@ -1570,13 +1628,16 @@ bool verify_supported(const gdn_tree_desc& d, const VerifyArgs& a) {
 hipError_t launch_verify(const gdn_tree_desc& d, const VerifyArgs& a, hipStream_t s) {
     const int norm = (a.flags & GDN_F_NORM_QK) ? 1 : 0;
     const int obf = (a.flags & GDN_F_OUT_BF16) ? 1 : 0;
-    if (verify_uses_mfma(d, a)) {
-        const int NPB = (d.N + 31) / 32;
-        const size_t lds = static_cast<size_t>(mfma_lds_layout(d.N, NPB).total);
+    const int NPB = (d.N + 31) / 32;
+    // the stored-U mode runs on the matrix cores for N <= 32, on the vector
+    // ALU otherwise
+    if (verify_uses_mfma(d, a) && (a.u == nullptr || NPB == 1)) {
+        const size_t lds = static_cast<size_t>(mfma_lds_layout(d.N, NPB, 0, a.u != nullptr).total);
         if (lds > kMaxLds) return hipErrorNotSupported;
         const CommitPrev none{};
         // the non-fused kernel only reads the state
         float* pool = const_cast<float*>(a.pool);
+        if (a.u != nullptr) return launch_mfma_t<1, kModeVerifyU>(d, a, pool, norm, obf, lds, none, s);
         switch (NPB) {
             case 1: return launch_mfma_t<1, kModeVerify>(d, a, pool, norm, obf, lds, none, s);
             case 2: return launch_mfma_t<2, kModeVerify>(d, a, pool, norm, obf, lds, none, s);
