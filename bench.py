@@ -22,7 +22,11 @@ Three step shapes (``--mode``):
             (the conv output goes to memory and is read back).
   separate  gdn_tree_desc_build -> conv_ancestry_gather -> gdn_tree_verify
             -> gdn_tree_commit (this step's own path), the state read twice.
-All three commit one path and verify one tree per step.
+  factored  the stored-U form: gdn_step_prepare -> conv_ancestry_gather_publish
+            -> gdn_tree_verify_store_u -> gdn_tree_commit_factored (this
+            step's own path, from the corrections the verify stored; its conv
+            history published by the next step's conv).
+All four commit one path and verify one tree per step.
 
 Before the W warm-up steps the step runs back to back for --settle-ms
 (300 ms by default) so that the GPU's clocks are at their steady state, as
@@ -59,7 +63,8 @@ WORKLOAD_TAG = {"tree27_b128_h32_conv4": "tree27_b128_conv4"}
 KERNEL_PREFIX = {"conv": "gdn::conv_gather_kernel", "verify": "gdn::verify_",
                  "commit": "gdn::commit_kernel", "desc": "gdn::desc_build_kernel",
                  "commit_verify": "gdn::verify_", "prepare": "gdn::step_prepare_kernel",
-                 "layer": "gdn::verify_"}
+                 "layer": "gdn::verify_", "verify_u": "gdn::verify_",
+                 "commit_factored": "gdn::commit_factored_kernel"}
 
 
 def log(*a):
@@ -138,6 +143,18 @@ def byte_model(cfg, cur, prev, mode):
         if cfg.conv_W > 0:
             out["conv"] = conv
         out["commit_verify"] = commit_verify
+        return out
+    if mode == "factored":
+        # verify also writes every node's correction u (fp32, node rows); the
+        # commit reads the state, the path's k rows, u rows and decays, and
+        # writes the state
+        sw, _ = bytes_commit_parts(cfg, cur)
+        L = int(cur["path_len"].astype(np.int64).sum())
+        out = {"prepare": bytes_desc(cfg, cur) + bytes_resolve(cfg, prev)}
+        if cfg.conv_W > 0:
+            out["conv"] = bytes_conv(cfg, cur, prev)
+        out["verify_u"] = state + bytes_verify_io(cfg, cur) + B * N * Hv * D * 4
+        out["commit_factored"] = 2 * sw + L * (Hqk * D * 2 + Hv * D * 4 + Hv * 4)
         return out
     # separate calls: this step's own path; verify and commit each pass over the state
     sw, path = bytes_commit_parts(cfg, cur)
@@ -308,6 +325,7 @@ class Slot:
             self.x = None
             self.q, self.k, self.v = to_dev(case["q"]), to_dev(case["k"]), to_dev(case["v"])
         self.out = torch.zeros((B, R, Hv, D), dtype=torch.float32, device=dev)
+        self.u = None  # stored corrections (factored mode)
 
 
 class Instance:
@@ -663,7 +681,8 @@ def main():
     # ms); 200 untimed steps (about 40 ms) reach the steady state
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--config", type=int, default=4)
-    ap.add_argument("--mode", choices=("fused", "layer", "separate", "attention"), default="layer")
+    ap.add_argument("--mode", choices=("fused", "layer", "separate", "factored", "attention"),
+                    default="layer")
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="run the step for this long before the warm-up steps: after idle the GPU's "
                          "clocks take tens of ms of load to reach their steady state")
@@ -700,6 +719,7 @@ def main():
     dev = "cuda"
     fused = args.mode == "fused"
     layer = args.mode == "layer"
+    factored = args.mode == "factored"
     if layer and cfg.conv_W == 0:
         print("--mode layer needs a conv workload (the layer step starts from the conv input)",
               file=sys.stderr)
@@ -727,7 +747,7 @@ def main():
     if args.layers == 0:
         args.layers = cfg.layers
     if args.layers > 1:
-        if cfg.conv_W > 0 or layer:
+        if cfg.conv_W > 0 or layer or factored:
             print("--layers > 1 covers the workloads without conv (fused or separate mode)",
                   file=sys.stderr)
             sys.exit(2)
@@ -735,8 +755,12 @@ def main():
         return
 
     t0 = time.perf_counter()
-    insts = [Instance(g, cfg, args.seed, li, to_dev, dev, torch, 2 if (fused or layer) else 1)
+    insts = [Instance(g, cfg, args.seed, li, to_dev, dev, torch, 2 if (fused or layer or factored) else 1)
              for li in range(args.sets)]
+    if factored:
+        for inst in insts:
+            for sl in inst.slots:
+                sl.u = torch.zeros_like(sl.out)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
     flags = g.GDN_F_NORM_QK if cfg.norm_qk else 0
     torch.cuda.synchronize()
@@ -746,6 +770,7 @@ def main():
     has_conv = cfg.conv_W > 0
     names = (("prepare", "layer") if layer else
              ("prepare",) + (("conv",) if has_conv else ()) + ("commit_verify",) if fused else
+             ("prepare",) + (("conv",) if has_conv else ()) + ("verify_u", "commit_factored") if factored else
              ("desc",) + (("conv",) if has_conv else ()) + ("verify", "commit"))
 
     def step(inst, ev=None):
@@ -770,6 +795,22 @@ def main():
                              cur.beta, inst.pool, inst.state_idx, cur.out, prev.desc, prev.x,
                              prev.alpha, prev.beta, inst.path_rows, inst.path_n, err, cfg.Hqk,
                              flags=flags)
+            mark()
+            return cur, prev
+        if factored:
+            g.gdn_step_prepare(cur.desc, prev.desc, prev.path, prev.path_len, inst.state_idx, inst.P,
+                               inst.path_rows, inst.path_n, err)
+            mark()
+            if has_conv:
+                g.conv_ancestry_gather_publish(cur.desc, cur.x, inst.hist, inst.state_idx, inst.w,
+                                               None, cur.y, cfg.act, prev.desc, inst.path_rows,
+                                               inst.path_n, prev.x, err)
+                mark()
+            g.gdn_tree_verify_store_u(cur.desc, cur.q, cur.k, cur.v, cur.alpha, cur.beta, inst.pool,
+                                      inst.state_idx, cur.out, cur.u, err, flags=flags)
+            mark()
+            g.gdn_tree_commit_factored(cur.desc, cur.path, cur.path_len, cur.k, cur.u, cur.alpha,
+                                       inst.pool, inst.state_idx, err, flags=flags & g.GDN_F_NORM_QK)
             mark()
             return cur, prev
         if fused:
@@ -804,7 +845,7 @@ def main():
     # clock settle, then the warm-up steps (the first step of each instance
     # also fills its slots' conv outputs)
     settle_steps = settle(lambda i: step(insts[i % len(insts)]), args.settle_ms, torch)
-    for i in range(args.warmup + (2 * args.sets if fused else 0)):
+    for i in range(args.warmup + (2 * args.sets if (fused or factored) else 0)):
         step(insts[i % len(insts)])
     torch.cuda.synchronize()
 
@@ -870,6 +911,9 @@ def main():
                   "gdn_step_prepare + conv_ancestry_gather_publish + gdn_tree_commit_verify (steady "
                   "state: the previous step's accepted path committed and its conv history "
                   "published inside this step)" if fused else
+                  "gdn_step_prepare + conv_ancestry_gather_publish + gdn_tree_verify_store_u + "
+                  "gdn_tree_commit_factored (the stored-U form: this step's path committed from the "
+                  "verify's corrections, its conv history published by the next step)" if factored else
                   "desc_build + conv_ancestry_gather + gdn_tree_verify + gdn_tree_commit")
     line = {
         "metric": METRIC,

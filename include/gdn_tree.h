@@ -102,6 +102,9 @@ extern "C" {
  * evaluated in fp32.  Without the flag gate_params is ignored (may be NULL);
  * with it a NULL gate_params is GDN_ERR_ARG. */
 #define GDN_F_RAW_GATES 8
+/* gdn_tree_verify_store_u: also write every node's state S_i (the state its
+ * output is read from) into the dump argument (debug; see there). */
+#define GDN_F_DUMP_STATES 16
 
 #define GDN_ACT_NONE 0
 #define GDN_ACT_SILU 1 /* z / (1 + exp(-z)) */
@@ -229,13 +232,24 @@ int32_t gdn_tree_commit(const gdn_tree_desc *d, const int32_t *path, const int32
  * layout of a float32 out).  bf16 operands at d = 128 with N <= 32 run on the
  * matrix cores (W = (I + G)^-1 solved along each root path beside M, then
  * U = W R), other shapes on the vector ALU.  Arguments, flags and errors as
- * gdn_tree_verify; u 4-byte aligned. */
+ * gdn_tree_verify; u 4-byte aligned.
+ *   dump  with GDN_F_DUMP_STATES (debug only; else ignored, may be NULL):
+ *         float32 [B][N][Hv][dv][dk], indexed by logical node, 16-byte
+ *         aligned; receives every node's state
+ *             S_i = P_i S_pre + sum_{j on i's root path} (P_i / P_j) u_j k^_j^T,
+ *         the state o_i = S_i q^_i is read from, rebuilt from the u just
+ *         written by the factored commit's arithmetic (so a factored commit
+ *         of i's root path reproduces dump[b][i] bit for bit, and a replay
+ *         commit can be compared against it: LumoTree, Sec. IV-B, the replay
+ *         and the verifier may differ numerically).  bf16 at d = 128 only
+ *         (else GDN_ERR_UNSUPPORTED); k 8-byte aligned with row_stride_qk a
+ *         multiple of 4, u 16-byte aligned.  Writes B*N*Hv*dv*dk*4 bytes. */
 int32_t gdn_tree_verify_store_u(const gdn_tree_desc *d, const void *q, const void *k, const void *v,
                                 int64_t row_stride_qk, int64_t row_stride_v, const float *alpha,
                                 const float *beta, const float *state_pool, int32_t P,
-                                const int32_t *state_idx, void *out, float *u, int32_t Hqk,
-                                int32_t Hv, int32_t dk, int32_t dv, int32_t dtype, int32_t flags,
-                                const float *gate_params, int32_t *err, void *stream);
+                                const int32_t *state_idx, void *out, float *u, float *dump,
+                                int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv, int32_t dtype,
+                                int32_t flags, const float *gate_params, int32_t *err, void *stream);
 
 /* Commit of the accepted path from stored corrections, in place: one rank-8
  * matrix-core update of P_a S_pre per 8 path nodes, no sequential replay.

@@ -86,13 +86,24 @@ def test_argument_checks_fail_before_launch(lib):
     assert Cm(d, p, p, 0, p, p, 2048, 4096, p, p, p, 4, p, None, None, 0, 16, 32, 128, 128, 0, 0, None, err, None) == g.GDN_ERR_UNSUPPORTED
     assert Cm(d, p, p, 65, p, p, 2048, 4096, p, p, p, 4, p, None, None, 0, 16, 32, 128, 128, 0, 0, None, err, None) == g.GDN_ERR_UNSUPPORTED
     assert Cm(d, p, p, 7, p, p, 2048, 4096, p, p, p, 4, p, p, None, 8, 16, 32, 128, 128, 0, 0, None, err, None) == g.GDN_ERR_ARG
-    # stored-U verify: no u buffer, misaligned u; factored commit: d != 128,
-    # unknown flag, Lmax out of range, misaligned u
+    # stored-U verify: no u buffer, misaligned u, unknown flag; the state
+    # dump without its buffer, misaligned, or at fp32 / d != 128
     VU = lib.gdn_tree_verify_store_u
-    assert VU(d, p, p, p, 2048, 4096, p, p, p, 4, p, p, None, 16, 32, 128, 128, 0, 0, None, err, None) == g.GDN_ERR_ARG
-    assert VU(d, p, p, p, 2048, 4096, p, p, p, 4, p, p, ctypes.c_void_p(258), 16, 32, 128, 128, 0, 0, None, err,
+    DS = g.GDN_F_DUMP_STATES
+    assert VU(d, p, p, p, 2048, 4096, p, p, p, 4, p, p, None, None, 16, 32, 128, 128, 0, 0, None, err,
               None) == g.GDN_ERR_ARG
-    assert VU(d, p, p, p, 2048, 4096, p, p, p, 4, p, p, p, 16, 32, 128, 128, 0, 64, None, err, None) == g.GDN_ERR_ARG
+    assert VU(d, p, p, p, 2048, 4096, p, p, p, 4, p, p, ctypes.c_void_p(258), None, 16, 32, 128, 128, 0, 0, None,
+              err, None) == g.GDN_ERR_ARG
+    assert VU(d, p, p, p, 2048, 4096, p, p, p, 4, p, p, p, None, 16, 32, 128, 128, 0, 64, None, err,
+              None) == g.GDN_ERR_ARG
+    assert VU(d, p, p, p, 2048, 4096, p, p, p, 4, p, p, p, None, 16, 32, 128, 128, 0, DS, None, err,
+              None) == g.GDN_ERR_ARG
+    assert VU(d, p, p, p, 2048, 4096, p, p, p, 4, p, p, p, ctypes.c_void_p(264), 16, 32, 128, 128, 0, DS, None, err,
+              None) == g.GDN_ERR_ARG
+    assert VU(d, p, p, p, 2048, 4096, p, p, p, 4, p, p, p, p, 16, 32, 128, 128, 1, DS, None, err,
+              None) == g.GDN_ERR_UNSUPPORTED
+    assert VU(d, p, p, p, 1024, 2048, p, p, p, 4, p, p, p, p, 16, 32, 64, 64, 0, DS, None, err,
+              None) == g.GDN_ERR_UNSUPPORTED
     CF = lib.gdn_tree_commit_factored
     assert CF(d, p, p, 7, p, 2048, p, p, p, 4, p, 16, 32, 64, 64, 0, None, err, None) == g.GDN_ERR_UNSUPPORTED
     assert CF(d, p, p, 7, p, 2048, p, p, p, 4, p, 16, 32, 128, 128, g.GDN_F_OUT_BF16, None, err, None) == g.GDN_ERR_ARG

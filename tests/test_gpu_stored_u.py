@@ -181,3 +181,75 @@ def test_f32_small_u():
     m = node_rows_mask(case)
     assert gr["err"] == orr["err"] == 0
     assert max_rel_rows(gr["u"][m], orr["u"][m], 2) <= TOL
+
+
+def test_state_dump_and_commit_consistency():
+    """GDN_F_DUMP_STATES: every node's state S_i next to the oracle's, the
+    outputs against S_i q_i, and the frontier's dumped state against both
+    commits of the accepted path (LumoTree, Sec. IV-B: the native replay and
+    the verifier may differ numerically).  The factored commit rebuilds the
+    frontier with the dump's own arithmetic, so it matches bit for bit; the
+    replay commit is held to the 2e-3 bar, and how many of its elements are
+    bitwise equal to the dump is reported."""
+    import torch
+    g = _g()
+    cfg = gi.CONFIGS[3].replace(Hv=8, Hqk=4)
+    case = gi.make_case(cfg, seed=291, B=5, extra_slots=1)
+    case["path_len"][1] = 0
+    B, N, R, D, Hv = case["B"], cfg.N, cfg.R, cfg.D, cfg.Hv
+    desc = g.TreeDesc(to_dev(case["parent"]), to_dev(case["node_row"]), R, 1, B=B)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    g.gdn_tree_desc_build(desc, err)
+    q, k, v = to_dev(case["q"]), to_dev(case["k"]), to_dev(case["v"])
+    alpha, beta = to_dev(case["alpha"]), to_dev(case["beta"])
+    pool0, sidx = to_dev(case["pool"]), to_dev(case["state_idx"])
+    out = torch.full((B, R, Hv, D), float("nan"), dtype=torch.float32, device="cuda")
+    u = torch.full_like(out, float("nan"))
+    dump = torch.full((B, N, Hv, D, D), float("nan"), dtype=torch.float32, device="cuda")
+    g.gdn_tree_verify_store_u(desc, q, k, v, alpha, beta, pool0, sidx, out, u, err, dump=dump)
+    path, plen = to_dev(case["path"]), to_dev(case["path_len"])
+    pool_f, pool_r = pool0.clone(), pool0.clone()
+    g.gdn_tree_commit_factored(desc, path, plen, k, u, alpha, pool_f, sidx, err)
+    g.gdn_tree_commit(desc, path, plen, k, v, alpha, beta, pool_r, sidx, err, Hqk=cfg.Hqk)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    dump_h, out_h = dump.cpu().numpy(), out.cpu().numpy()
+    pf, pr = pool_f.cpu().numpy(), pool_r.cpu().numpy()
+    assert np.array_equal(pool0.cpu().numpy(), case["pool"], equal_nan=True)  # the dump only reads the pool
+
+    # every node's state against the oracle's S_i
+    d = oracle.desc_build(case["parent"], case["node_row"], R, 1)
+    _, e, states = oracle.verify(case["parent"], case["node_row"], d["status"], case["q"], case["k"], case["v"],
+                                 case["alpha"], case["beta"], case["pool"], case["state_idx"], cfg.Hqk, Hv,
+                                 False, want_states=True)
+    rel = max_rel_rows(dump_h, states, 3)
+    assert rel <= TOL, f"dumped states max rel {rel:.3e}"
+    # each output against its own node's dumped state: o_i = S_i q_i
+    qf = gi.bf16_bits_to_f32(case["q"]).astype(np.float64)
+    g_of_h = np.arange(Hv) * cfg.Hqk // Hv
+    worst = 0.0
+    for b in range(B):
+        for i in range(N):
+            r = case["node_row"][b, i]
+            o_ref = np.einsum("hvk,hk->hv", dump_h[b, i].astype(np.float64), qf[b, r, g_of_h])
+            worst = max(worst, max_rel_rows(out_h[b, r], o_ref, 1))
+    assert worst <= TOL, f"outputs vs S_i q_i max rel {worst:.3e}"
+
+    # the frontier's dumped state against both commits
+    n_eq = n_all = 0
+    rel_r = 0.0
+    for b in range(B):
+        s = case["state_idx"][b]
+        L = case["path_len"][b]
+        if L == 0:
+            assert np.array_equal(pf[s], case["pool"][s]) and np.array_equal(pr[s], case["pool"][s])
+            continue
+        f = case["path"][b, L - 1]
+        assert np.array_equal(pf[s], dump_h[b, f]), f"factored commit of request {b} differs from its dump"
+        rel_r = max(rel_r, max_rel_rows(pr[s], dump_h[b, f], 1))
+        n_eq += int((pr[s] == dump_h[b, f]).sum())
+        n_all += pr[s].size
+    print(f"\n[consistency] replay commit vs dumped frontier: max rel {rel_r:.3e}, "
+          f"{n_eq}/{n_all} elements bitwise equal ({100.0 * n_eq / n_all:.1f}%); "
+          f"factored commit: bitwise equal on every committed slot")
+    assert rel_r <= TOL

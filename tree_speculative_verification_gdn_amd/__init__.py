@@ -24,6 +24,7 @@ __all__ = [
     "GDN_OK", "GDN_ERR_ARG", "GDN_ERR_UNSUPPORTED", "GDN_ERR_HIP",
     "GDN_EV_PARENT", "GDN_EV_ROW", "GDN_EV_STATE", "GDN_EV_PATH", "GDN_EV_CTX",
     "GDN_DT_BF16", "GDN_DT_F32", "GDN_F_NORM_QK", "GDN_F_OUT_BF16", "GDN_F_VALU", "GDN_F_RAW_GATES",
+    "GDN_F_DUMP_STATES",
     "GDN_ACT_NONE", "GDN_ACT_SILU", "GdnError", "TreeDesc", "library_path", "load_library",
     "gdn_tree_desc_build", "conv_ancestry_gather", "gdn_tree_verify", "gdn_tree_commit",
     "gdn_tree_commit_layers", "conv_ancestry_gather_publish", "gdn_tree_commit_verify",
@@ -36,7 +37,7 @@ __all__ = [
 GDN_OK, GDN_ERR_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, -1, -4, -5
 GDN_EV_PARENT, GDN_EV_ROW, GDN_EV_STATE, GDN_EV_PATH, GDN_EV_CTX = 1, 2, 4, 8, 16
 GDN_DT_BF16, GDN_DT_F32 = 0, 1
-GDN_F_NORM_QK, GDN_F_OUT_BF16, GDN_F_VALU, GDN_F_RAW_GATES = 1, 2, 4, 8
+GDN_F_NORM_QK, GDN_F_OUT_BF16, GDN_F_VALU, GDN_F_RAW_GATES, GDN_F_DUMP_STATES = 1, 2, 4, 8, 16
 GDN_ACT_NONE, GDN_ACT_SILU = 0, 1
 GDN_ATTN_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 
@@ -93,7 +94,7 @@ def load_library():
         lib.gdn_tree_verify.argtypes = [dp, vp, vp, vp, i64, i64, vp, vp, vp, i32, vp, vp,
                                         i32, i32, i32, i32, i32, i32, vp, vp, vp]
         lib.gdn_tree_verify_store_u.restype = i32
-        lib.gdn_tree_verify_store_u.argtypes = [dp, vp, vp, vp, i64, i64, vp, vp, vp, i32, vp, vp, vp,
+        lib.gdn_tree_verify_store_u.argtypes = [dp, vp, vp, vp, i64, i64, vp, vp, vp, i32, vp, vp, vp, vp,
                                                 i32, i32, i32, i32, i32, i32, vp, vp, vp]
         lib.gdn_tree_commit_factored.restype = i32
         lib.gdn_tree_commit_factored.argtypes = [dp, vp, vp, i32, vp, i64, vp, vp, vp, i32, vp, i32, i32,
@@ -273,9 +274,13 @@ def gdn_tree_verify(desc: TreeDesc, q, k, v, alpha, beta, state_pool, state_idx,
 
 
 def gdn_tree_verify_store_u(desc: TreeDesc, q, k, v, alpha, beta, state_pool, state_idx, out, u, err,
-                            flags: int = 0, stream=None, raise_on_error=True, gate_params=None) -> int:
+                            flags: int = 0, stream=None, raise_on_error=True, gate_params=None,
+                            dump=None) -> int:
     """gdn_tree_verify, plus every node's delta correction into u (fp32
-    [B, R, Hv, D], the layout of out)."""
+    [B, R, Hv, D], the layout of out).  With ``dump`` (fp32 [B, N, Hv, D, D],
+    debug) GDN_F_DUMP_STATES is set and every node's state is written there."""
+    if dump is not None:
+        flags |= GDN_F_DUMP_STATES
     rs_qk, Hqk, dk = _rows_view(q, "q")
     rs_k, Hk, dk2 = _rows_view(k, "k")
     rs_v, Hv, dv = _rows_view(v, "v")
@@ -284,7 +289,8 @@ def gdn_tree_verify_store_u(desc: TreeDesc, q, k, v, alpha, beta, state_pool, st
     P = int(state_pool.shape[0])
     code = load_library().gdn_tree_verify_store_u(desc.ref(), _ptr(q), _ptr(k), _ptr(v), rs_qk, rs_v,
                                                   _ptr(alpha), _ptr(beta), _ptr(state_pool), P,
-                                                  _ptr(state_idx), _ptr(out), _ptr(u), Hqk, Hv, dk, dv,
+                                                  _ptr(state_idx), _ptr(out), _ptr(u), _ptr(dump), Hqk, Hv,
+                                                  dk, dv,
                                                   _dtype_code(q), _gate_flags(flags, gate_params),
                                                   _ptr(gate_params), _ptr(err), _stream(stream))
     return _check(code, "gdn_tree_verify_store_u", raise_on_error)

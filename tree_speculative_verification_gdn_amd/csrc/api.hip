@@ -108,8 +108,8 @@ int32_t gdn_tree_verify(const gdn_tree_desc* d, const void* q, const void* k, co
 int32_t gdn_tree_verify_store_u(const gdn_tree_desc* d, const void* q, const void* k, const void* v,
                                 int64_t row_stride_qk, int64_t row_stride_v, const float* alpha,
                                 const float* beta, const float* state_pool, int32_t P,
-                                const int32_t* state_idx, void* out, float* u, int32_t Hqk, int32_t Hv,
-                                int32_t dk, int32_t dv, int32_t dtype, int32_t flags,
+                                const int32_t* state_idx, void* out, float* u, float* dump, int32_t Hqk,
+                                int32_t Hv, int32_t dk, int32_t dv, int32_t dtype, int32_t flags,
                                 const float* gate_params, int32_t* err, void* stream) {
     int32_t st = check_desc(d);
     if (st != GDN_OK) return st;
@@ -117,14 +117,30 @@ int32_t gdn_tree_verify_store_u(const gdn_tree_desc* d, const void* q, const voi
     if (st != GDN_OK) return st;
     if (!q || !k || !v || !alpha || !beta || !state_pool || !state_idx || !out || !u || !err || P < 1)
         return GDN_ERR_ARG;
-    if ((flags & ~(GDN_F_NORM_QK | GDN_F_OUT_BF16 | GDN_F_VALU | GDN_F_RAW_GATES)) != 0) return GDN_ERR_ARG;
+    if ((flags & ~(GDN_F_NORM_QK | GDN_F_OUT_BF16 | GDN_F_VALU | GDN_F_RAW_GATES | GDN_F_DUMP_STATES)) != 0)
+        return GDN_ERR_ARG;
     if (check_gates(flags, gate_params) != GDN_OK) return GDN_ERR_ARG;
     if (row_stride_qk < static_cast<int64_t>(Hqk) * dk || row_stride_v < static_cast<int64_t>(Hv) * dv)
         return GDN_ERR_ARG;
     if (!aligned(state_pool, 16) || !aligned(u, 4)) return GDN_ERR_ARG;
+    const bool want_dump = (flags & GDN_F_DUMP_STATES) != 0;
+    if (want_dump) {
+        // the dump rebuilds each node's state on the factored commit's kernel
+        if (dump == nullptr) return GDN_ERR_ARG;
+        if (dk != 128 || dtype != GDN_DT_BF16) return GDN_ERR_UNSUPPORTED;
+        if (row_stride_qk % 4 != 0 || !aligned(k, 8) || !aligned(u, 16) || !aligned(dump, 16))
+            return GDN_ERR_ARG;
+    }
+    const int vflags = flags & ~GDN_F_DUMP_STATES;
     gdn::VerifyArgs a{q, k, v, row_stride_qk, row_stride_v, alpha, beta, state_pool, P,
-                      state_idx, out, Hqk, Hv, dk, dtype, flags, err, gate_params, u};
-    return map_launch(gdn::launch_verify(*d, a, static_cast<hipStream_t>(stream)));
+                      state_idx, out, Hqk, Hv, dk, dtype, vflags, err, gate_params, u};
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    st = map_launch(gdn::launch_verify(*d, a, s));
+    if (st != GDN_OK || !want_dump) return st;
+    gdn::FactoredCommitArgs fa{nullptr, nullptr, 0, k, row_stride_qk, u, alpha, const_cast<float*>(state_pool),
+                               P, state_idx, Hqk, Hv, vflags & (GDN_F_NORM_QK | GDN_F_RAW_GATES), err,
+                               gate_params};
+    return map_launch(gdn::launch_dump_states(*d, fa, dump, s));
 }
 
 int32_t gdn_tree_commit_factored(const gdn_tree_desc* d, const int32_t* path, const int32_t* path_len,

@@ -157,6 +157,10 @@ struct FactoredCommitArgs {
     const float* gate_params;
 };
 hipError_t launch_commit_factored(const gdn_tree_desc& d, const FactoredCommitArgs& a, hipStream_t s);
+// Every node's state S_i rebuilt from its root path's stored corrections into
+// dump [B][N][Hv][128][128] (a.path, a.path_len and a.Lmax unused; the pool
+// only read).
+hipError_t launch_dump_states(const gdn_tree_desc& d, const FactoredCommitArgs& a, float* dump, hipStream_t s);
 size_t commit_factored_lds_bytes(int Lmax);
 
 // Commit of the previous step's accepted path followed by the verify of the

@@ -19,6 +19,13 @@
 // round trip 1 the slot, length, path and the duplicate-slot scan, round trip
 // 2 the path nodes' parents and rows (validation), round trip 3 the path's k
 // and u rows and decays, then the state.
+//
+// The same kernel also serves the verify's debug dump (DUMP): one workgroup
+// per (request, value head, node i) rebuilds S_i from node i's own root path
+// (its strict ancestors from the descriptor, then i) and writes it to the dump
+// instead of the pool, which it only reads.  S_i is the state the verify
+// reads o_i from (o_i = S_i q^_i): the pages' verifier never materialises
+// it, so the dump is what a commit of that path is compared against.
 #include "mfma_common.h"
 
 namespace gdn {
@@ -48,10 +55,11 @@ __host__ __device__ inline FacLds fac_lds_layout(int Lmax) {
 
 size_t commit_factored_lds_bytes(int Lmax) { return static_cast<size_t>(fac_lds_layout(Lmax).total); }
 
-template <bool RAW>
+template <bool RAW, bool DUMP>
 __global__ void __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
     commit_factored_kernel(int B, int N, int R, int shared, const int32_t* __restrict__ parent,
                            const int32_t* __restrict__ node_row, const int32_t* __restrict__ status,
+                           const uint64_t* __restrict__ anc, float* __restrict__ dump,
                            const int32_t* __restrict__ path, const int32_t* __restrict__ path_len, int Lmax,
                            const uint16_t* __restrict__ k, int64_t rs_qk, const float* __restrict__ u,
                            const float* __restrict__ alpha, float* __restrict__ pool, int P,
@@ -73,48 +81,69 @@ __global__ void __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(
     const int l32 = lane & 31;
     const int r_own = wave * 32 + l32;
     const uint32_t unit = xcd_local_order(blockIdx.x, gridDim.x);
-    const int b = static_cast<int>(unit / Hv);
-    const int h = static_cast<int>(unit % Hv);
+    const uint32_t bh = DUMP ? unit / static_cast<uint32_t>(N) : unit;
+    const int inode = DUMP ? static_cast<int>(unit % static_cast<uint32_t>(N)) : 0;
+    const int b = static_cast<int>(bh / Hv);
+    const int h = static_cast<int>(bh % Hv);
     const int t = shared ? 0 : b;
     const int g = static_cast<int>((static_cast<int64_t>(h) * Hqk) / Hv);
-
-    // round trip 1: status, slot, length, the path, the duplicate-slot scan;
-    // every load unconditional from an index clamped into range
-    const int st = status[t];
-    const int slot = state_idx[b];
-    const int len = path_len[b];
-    const int pnode = path[static_cast<size_t>(b) * Lmax + min(tid, Lmax - 1)];
-    const int prev = __shfl(pnode, tid > 0 ? tid - 1 : 0, 64);  // path[tid - 1] (wave 0: len <= 64)
-    int dup = 0;
-    for (int b2 = tid; b2 < B; b2 += kFThreads) dup |= (b2 != b && state_idx[b2] == slot) ? 1 : 0;
     float g_alog = 0.0f, g_dtb = 0.0f;
     if constexpr (RAW) {
         g_alog = gate_params[h];
         g_dtb = gate_params[Hv + h];
     }
-    if (st != 0) return;  // malformed tree: reported by its descriptor build
-    if (tid == 0) s_bad = 0;
+    int len;
+    int slot;
+    if constexpr (DUMP) {
+        // node i's root path: its strict ancestors in index order (a parent
+        // precedes its children), then i; lane j < N places node j's row
+        const int st = status[t];
+        slot = state_idx[b];
+        const uint64_t path_bits = anc[static_cast<size_t>(t) * N + inode] | (1ull << inode);
+        const int prow = node_row[static_cast<size_t>(t) * N + min(tid, N - 1)];
+        if (st != 0) return;  // malformed tree: reported by its descriptor build
+        if (slot < 0 || slot >= P) {  // the verify reports the same bit
+            if (h == 0 && inode == 0 && tid == 0) atomicOr(err, GDN_EV_STATE);
+            return;
+        }
+        len = __popcll(path_bits);
+        if (tid < N && ((path_bits >> tid) & 1ull))
+            s_rows[__popcll(path_bits & ((1ull << tid) - 1ull))] = min(max(prow, 0), R - 1);
+        __syncthreads();
+    } else {
+        // round trip 1: status, slot, length, the path, the duplicate-slot
+        // scan; every load unconditional from an index clamped into range
+        const int st = status[t];
+        slot = state_idx[b];
+        len = path_len[b];
+        const int pnode = path[static_cast<size_t>(b) * Lmax + min(tid, Lmax - 1)];
+        const int prev = __shfl(pnode, tid > 0 ? tid - 1 : 0, 64);  // path[tid - 1] (wave 0: len <= 64)
+        int dup = 0;
+        for (int b2 = tid; b2 < B; b2 += kFThreads) dup |= (b2 != b && state_idx[b2] == slot) ? 1 : 0;
+        if (st != 0) return;  // malformed tree: reported by its descriptor build
+        if (tid == 0) s_bad = 0;
 
-    // round trip 2: the path nodes' parents and rows; validation
-    const size_t ti = static_cast<size_t>(t) * N + min(max(pnode, 0), N - 1);
-    const int par = parent[ti];
-    const int prow = node_row[ti];
-    int bad = ((slot >= 0 && slot < P) ? 0 : GDN_EV_STATE) | (dup ? GDN_EV_STATE : 0);
-    if (len < 0 || len > Lmax) {
-        bad |= GDN_EV_PATH;
-    } else if (tid < len) {
-        if (pnode < 0 || pnode >= N || par != (tid == 0 ? -1 : prev)) bad |= GDN_EV_PATH;
+        // round trip 2: the path nodes' parents and rows; validation
+        const size_t ti = static_cast<size_t>(t) * N + min(max(pnode, 0), N - 1);
+        const int par = parent[ti];
+        const int prow = node_row[ti];
+        int bad = ((slot >= 0 && slot < P) ? 0 : GDN_EV_STATE) | (dup ? GDN_EV_STATE : 0);
+        if (len < 0 || len > Lmax) {
+            bad |= GDN_EV_PATH;
+        } else if (tid < len) {
+            if (pnode < 0 || pnode >= N || par != (tid == 0 ? -1 : prev)) bad |= GDN_EV_PATH;
+        }
+        s_rows[min(tid, Lmax)] = min(max(prow, 0), R - 1);  // every lane writes (spare entry Lmax)
+        __syncthreads();  // s_bad initialised
+        if (bad) atomicOr(&s_bad, bad);
+        __syncthreads();
+        bad = s_bad;
+        if (bad) {
+            if (h == 0 && tid == 0) atomicOr(err, bad);
+            return;
+        }
+        if (len == 0) return;  // nothing accepted: the state stays as it is
     }
-    s_rows[min(tid, Lmax)] = min(max(prow, 0), R - 1);  // every lane writes (spare entry Lmax)
-    __syncthreads();  // s_bad initialised
-    if (bad) atomicOr(&s_bad, bad);
-    __syncthreads();
-    bad = s_bad;
-    if (bad) {
-        if (h == 0 && tid == 0) atomicOr(err, bad);
-        return;
-    }
-    if (len == 0) return;  // nothing accepted: the state stays as it is
 
     // round trip 3: the path's k rows (qk head g), u rows (value head h) and
     // decays, zero past the path, then the state
@@ -144,6 +173,9 @@ __global__ void __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(
         s_al[min(tid, lp)] = a;  // every lane writes (spare entry lp)
     }
     float* Sw = pool + (static_cast<size_t>(slot) * Hv + h) * (kD * kD) + static_cast<size_t>(wave) * 32 * kD;
+    float* Sd = DUMP ? dump + ((static_cast<size_t>(b) * N + inode) * Hv + h) * (kD * kD) +
+                           static_cast<size_t>(wave) * 32 * kD
+                     : Sw;
     float4 sreg[16];
     {
         asm volatile("" ::: "memory");  // keep the state loads behind the loads above
@@ -209,24 +241,39 @@ __global__ void __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(
                 sreg[4 * cb + q4] = make_float4(sacc[4 * q4], sacc[4 * q4 + 1], sacc[4 * q4 + 2], sacc[4 * q4 + 3]);
         }
     }
-    state_store_lines(Sw, sreg, l32, hf);
+    state_store_lines(Sd, sreg, l32, hf);
 }
 
-hipError_t launch_commit_factored(const gdn_tree_desc& d, const FactoredCommitArgs& a, hipStream_t s) {
-    const size_t lds = commit_factored_lds_bytes(a.Lmax);
+namespace {
+
+template <bool DUMP>
+hipError_t launch_factored(const gdn_tree_desc& d, const FactoredCommitArgs& a, float* dump, hipStream_t s) {
+    const int Lmax = DUMP ? d.N : a.Lmax;  // a node's root path has at most N nodes
+    const size_t lds = commit_factored_lds_bytes(Lmax);
     if (lds > 160 * 1024) return hipErrorNotSupported;
     const int norm = (a.flags & GDN_F_NORM_QK) ? 1 : 0;
     const bool raw = (a.flags & GDN_F_RAW_GATES) != 0;
-    auto kfn = raw ? commit_factored_kernel<true> : commit_factored_kernel<false>;
+    auto kfn = raw ? commit_factored_kernel<true, DUMP> : commit_factored_kernel<false, DUMP>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
-    const dim3 grid(static_cast<unsigned>(d.B) * static_cast<unsigned>(a.Hv));
+    const dim3 grid(static_cast<unsigned>(d.B) * static_cast<unsigned>(a.Hv) *
+                    static_cast<unsigned>(DUMP ? d.N : 1));
     hipLaunchKernelGGL(kfn, grid, dim3(kFThreads), lds, s, d.B, d.N, d.R, d.shared, d.parent, d.node_row,
-                       d.status, a.path, a.path_len, a.Lmax, static_cast<const uint16_t*>(a.k), a.rs_qk, a.u,
-                       a.alpha, a.pool, a.P, a.state_idx, a.Hqk, a.Hv, norm, a.err,
+                       d.status, d.anc, dump, a.path, a.path_len, Lmax, static_cast<const uint16_t*>(a.k),
+                       a.rs_qk, a.u, a.alpha, a.pool, a.P, a.state_idx, a.Hqk, a.Hv, norm, a.err,
                        raw ? a.gate_params : nullptr);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_commit_factored(const gdn_tree_desc& d, const FactoredCommitArgs& a, hipStream_t s) {
+    return launch_factored<false>(d, a, nullptr, s);
+}
+
+hipError_t launch_dump_states(const gdn_tree_desc& d, const FactoredCommitArgs& a, float* dump, hipStream_t s) {
+    return launch_factored<true>(d, a, dump, s);
 }
 
 }  // namespace gdn
