@@ -13,8 +13,8 @@ import numpy as np
 import pytest
 
 import gdn_inputs as gi
-from harness import (bf16_ulp_diff, hist_to_bits, max_rel_rows, node_rows_mask,
-                     run_gpu_two_steps, run_oracle_two_steps, subset, two_step_case)
+from harness import (NAN_BF16, bf16_ulp_diff, hist_to_bits, max_rel_rows, node_rows_mask,
+                     run_gpu_two_steps, run_oracle_two_steps, straddle_rows, subset, two_step_case)
 
 pytestmark = pytest.mark.gpu
 
@@ -152,29 +152,52 @@ def test_two_steps_fallback_d32_f32():
 
 
 def test_two_steps_conv4_full_size_sampled():
-    # the bench's workload at full size on the device; the oracle on a sample
+    # the bench's workload at full size on the device (B = 128, BFS packing,
+    # the fused launch); the oracle on a sample of requests
     cfg = gi.CONFIGS[4]
     c1, c2 = two_step_case(cfg, seed=2026, packing="bfs")
     gr = run_gpu_two_steps(c1, c2)
     gs = run_gpu_two_steps(c1, c2, fused=False)
     assert gr["err"] == gs["err"] == 0
     assert np.array_equal(gr["hist"], gs["hist"]) and np.array_equal(gr["y2"], gs["y2"])
-    m = node_rows_mask(c2)
+    m_all = node_rows_mask(c2)
     # fused and separate differ only in the order of fp32 sums
-    assert max_rel_rows(gr["out"][m], gs["out"][m], 2) <= 1e-4
+    assert max_rel_rows(gr["out"][m_all], gs["out"][m_all], 2) <= 1e-4
     used = c1["state_idx"]
     assert max_rel_rows(gr["pool"][used], gs["pool"][used], 2) <= 1e-4
     bs = np.array([0, 33, 64, 127])
     s1, s2 = subset(c1, bs), subset(c2, bs)
     s2["pool"], s2["hist"] = s1["pool"], s1["hist"]
     orr = run_oracle_two_steps(s1, s2)
-    g1 = dict(out=gr["out"][bs], pool=gr["pool"][used[bs]], hist=gr["hist"][used[bs]], y2=gr["y2"][bs],
-              err=gr["err"], status1=gr["status1"][bs], status2=gr["status2"][bs])
-    # own conv outputs downstream: a one-ulp straddle may move an output by 2^-8
-    assert np.array_equal(g1["hist"], hist_to_bits(orr["hist"]))
-    d = bf16_ulp_diff(g1["y2"][node_rows_mask(s2)], orr["y2"][node_rows_mask(s2)])
-    assert d.max() <= 1
-    assert np.isfinite(g1["out"][node_rows_mask(s2)]).all()
+    m = node_rows_mask(s2)
+    # conv: history bit-exact, outputs within one bf16 ulp
+    assert np.array_equal(gr["hist"][used[bs]], hist_to_bits(orr["hist"]))
+    assert bf16_ulp_diff(gr["y2"][bs][m], orr["y2"][m]).max() <= 1
+    # (1) the same full-size launch with the oracle's conv outputs in place of
+    # the device's on the sampled requests: every output and committed state
+    # of those requests within the bar, nothing excluded
+    y1o = np.full(gr["y1"].shape, NAN_BF16, np.uint16)
+    y2o = np.full(gr["y2"].shape, NAN_BF16, np.uint16)
+    y1o[bs], y2o[bs] = orr["y1"], orr["y2"]
+    go = run_gpu_two_steps(c1, c2, y1_override=y1o, y2_override=y2o)
+    assert go["err"] == 0
+    assert max_rel_rows(go["out"][bs][m], orr["out"][m], 2) <= TOL
+    assert max_rel_rows(go["pool"][used[bs]], orr["pool"], 2) <= TOL
+    # (2) on the device's own conv outputs: rows downstream of a conv element
+    # that rounded the other way are excluded; the excluded share is reported
+    # and bounded, the rest meet the bar
+    om, _ = straddle_rows(s2, gr["y2"][bs], orr["y2"])
+    _, sm1 = straddle_rows(s1, gr["y1"][bs], orr["y1"])
+    om |= sm1[:, None, :]
+    mo = m[:, :, None] & ~om
+    excl = 1.0 - mo.sum() / (m.sum() * cfg.Hv)
+    excl_s = sm1.mean()
+    print(f"\n[straddles] fused full size, own conv: {100 * excl:.1f}% of output rows and "
+          f"{100 * excl_s:.1f}% of committed state heads excluded")
+    assert excl < 0.10 and excl_s < 0.10  # measured: 4.9% and 0.8%
+    assert max_rel_rows(gr["out"][bs][mo], orr["out"][mo], 1) <= TOL
+    keep = ~sm1
+    assert max_rel_rows(gr["pool"][used[bs]][keep], orr["pool"][keep], 1) <= TOL
 
 
 def test_two_steps_tree64_b256_full_size_sampled():

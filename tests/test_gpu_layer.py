@@ -214,6 +214,39 @@ def test_layer_step_full_size_sampled():
     _cmp(s1c, s2, g1, orr)
 
 
+def test_layer_step_silu_full_size_sampled():
+    # the bench's exact launch (gdn_step_prepare + gdn_layer_step, B = 128,
+    # BFS packing, SiLU on normal inputs) against the oracle on a sample of
+    # requests: rows downstream of a conv element that rounded the other way
+    # are excluded, their share reported and bounded, the rest meet the bar
+    cfg = gi.CONFIGS[4]
+    c1, c2 = two_step_case(cfg, seed=2026, packing="bfs")
+    gr = run_gpu_layer(c1, c2, prepare=True)
+    gs = run_gpu_two_steps(c1, c2)                 # step 1's conv output (same conv arithmetic)
+    assert gr["err"] == gs["err"] == 0
+    m_all = node_rows_mask(c2)
+    assert np.array_equal(gr["y2"][m_all], gs["y2"][m_all])
+    used = c1["state_idx"]
+    bs = np.array([0, 33, 64, 127])
+    s1, s2 = subset(c1, bs), subset(c2, bs)
+    s2["pool"], s2["hist"] = s1["pool"], s1["hist"]
+    orr = run_oracle_two_steps(s1, s2)
+    m = node_rows_mask(s2)
+    assert np.array_equal(gr["hist_out"][used[bs]], hist_to_bits(orr["hist"]))
+    assert bf16_ulp_diff(gr["y2"][bs][m], orr["y2"][m]).max() <= 1
+    om, _ = straddle_rows(s2, gr["y2"][bs], orr["y2"])
+    _, sm1 = straddle_rows(s1, gs["y1"][bs], orr["y1"])
+    om |= sm1[:, None, :]
+    mo = m[:, :, None] & ~om
+    excl = 1.0 - mo.sum() / (m.sum() * cfg.Hv)
+    print(f"\n[straddles] layer step full size, own conv: {100 * excl:.1f}% of output rows and "
+          f"{100 * sm1.mean():.1f}% of committed state heads excluded")
+    assert excl < 0.10 and sm1.mean() < 0.10  # measured: 4.9% and 0.8%
+    assert max_rel_rows(gr["out"][bs][mo], orr["out"][mo], 1) <= TOL
+    keep = ~sm1
+    assert max_rel_rows(gr["pool"][used[bs]][keep], orr["pool"][keep], 1) <= TOL
+
+
 def test_layer_step_with_bias_matches_oracle_and_separate_calls():
     # a conv bias (dyadic: the conv stays exact); the layer step, the fused
     # calls and the oracle agree
