@@ -170,18 +170,32 @@ def byte_model(cfg, cur, prev, mode):
 # measured traffic from the committed counter summaries
 # --------------------------------------------------------------------------
 
-def library_source_hash():
-    """sha256[:16] over the library's kernel sources (csrc/*.hip, csrc/*.h),
-    the value the counter summaries under profiles/ record: documentation of
-    the ABI header does not invalidate them."""
+ATTN_SOURCES = ("tree_attention.hip", "gdn_internal.h")
+
+
+def library_source_hash(scope="gdn"):
+    """sha256[:16] over the kernel sources a workload's kernels are built
+    from, the value its counter summary under profiles/ records: the tree
+    attention's file and the shared header for scope "attention", every
+    other csrc/*.hip and csrc/*.h for scope "gdn" (documentation of the ABI
+    header does not invalidate either)."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "tree_speculative_verification_gdn_amd", "csrc")
     for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".h")):
-            h.update(f.encode())
-            with open(os.path.join(d, f), "rb") as fh:
-                h.update(fh.read())
+        if not f.endswith((".hip", ".h")):
+            continue
+        if scope == "attention" and f not in ATTN_SOURCES:
+            continue
+        if scope == "gdn" and f == "tree_attention.hip":
+            continue
+        h.update(f.encode())
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def _scope(workload):
+    return "attention" if "attention" in workload or "ctx" in workload else "gdn"
 
 
 def measured_traffic_sum(workload, mode, prefix):
@@ -192,7 +206,7 @@ def measured_traffic_sum(workload, mode, prefix):
         return None
     with open(path) as fh:
         rec = json.load(fh)
-    if rec.get("source_sha256_16") != library_source_hash():
+    if rec.get("source_sha256_16") != library_source_hash(_scope(workload)):
         return None
     tot = [k["traffic_bytes"] for name, k in rec["kernels"].items() if name.startswith(prefix)]
     return int(round(sum(tot))) if tot else None
@@ -207,7 +221,7 @@ def measured_traffic(workload, mode, stage):
         return None
     with open(path) as fh:
         rec = json.load(fh)
-    if rec.get("source_sha256_16") != library_source_hash():
+    if rec.get("source_sha256_16") != library_source_hash(_scope(workload)):
         return None
     for name, k in rec["kernels"].items():
         if name.startswith(KERNEL_PREFIX[stage]):
@@ -293,6 +307,27 @@ def settle(step_fn, ms, torch):
             n += 1
         torch.cuda.synchronize()
     return n
+
+
+def stream_ceiling(torch, dev, mib=1024, reps=20):
+    """A measured streaming ceiling for read-modify-write traffic: an
+    in-place fp32 scale (x *= 0.5, then x *= 2, exact) over ``mib`` MiB, far
+    larger than the 256 MB last-level cache, timed with HIP events on the
+    current stream after 5 untimed passes.  Returns GB/s counting each pass's
+    read and write of the buffer."""
+    x = torch.ones(mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+    for i in range(5):
+        x.mul_(0.5 if i % 2 == 0 else 2.0)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(reps):
+        x.mul_(0.5 if i % 2 == 0 else 2.0)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del x
+    return 2.0 * mib * (1 << 20) / (ms / 1e3) / 1e9
 
 
 def spread(xs):
@@ -549,6 +584,12 @@ def run_layers(args, cfg, g, torch, dev, to_dev):
                          avg_us=round(layer_ms * 1e3, 2), algorithmic_bytes=int(per_layer_bytes)),
         "cpu_baseline": None,
     }
+    if not args.no_ceiling:
+        ceil = stream_ceiling(torch, dev)
+        log(f"[bench] streaming ceiling (in-place fp32 scale over 1 GiB, read + write): {ceil:.1f} GB/s")
+        line["roofline"]["stream_rmw_ceiling"] = dict(
+            kind="in-place fp32 x *= c over 1 GiB (torch elementwise kernel), read + write counted",
+            gbs=round(ceil, 1), frac_of_ceiling=round(achieved / ceil, 4))
     if not args.no_cpu_baseline:
         # one layer's oracle on a bounded sample of the requests (a full
         # layer of this workload is minutes of fp64 work); per layer, so the
@@ -627,6 +668,7 @@ def run_attention(args, g, torch, dev):
         g.gdn_tree_attention(inst["desc"], inst["q"], inst["k"], inst["v"], inst["ctx"], inst["out"], ws, err,
                              splits=splits)
 
+    settle_steps = settle(step, args.settle_ms, torch)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -658,6 +700,7 @@ def run_attention(args, g, torch, dev):
                                f"{args.ctx} prefix positions, Hq={Hq} over Hkv={Hkv}, d={D}, bf16 KV cache, "
                                f"{splits} prefix partitions",
                    "mode": "attention", "step": "gdn_tree_attention (partitions + merge), one layer",
+                   "settle_ms": args.settle_ms, "settle_steps": settle_steps,
                    "value_is": "tree nodes attended per second per attention layer",
                    "global_batch": B, "nodes_per_request": N, "parallelism": "single GPU",
                    "step_bytes": int(byts), "step_gflop": round(flops / 1e9, 2)},
@@ -697,6 +740,8 @@ def main():
                     help="layers per step for the multi-layer workload (default: the workload's)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming read-modify-write ceiling measured after the timed run")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain fp32 copy kernel (out = in * 1) over MIB MiB, three "
                          "times, as the known-size reference for HBM byte counters")
@@ -899,6 +944,13 @@ def main():
                     unit="GB/s", frac=round(achieved / PEAK_HBM_GBS, 4), traffic=traffic,
                     traffic_over_algorithmic=(round(traffic / bytes_avg[dom], 3) if traffic else None),
                     avg_us=round(avg[dom] * 1e3, 2), algorithmic_bytes=int(bytes_avg[dom]))
+    if not args.no_ceiling:
+        ceil = stream_ceiling(torch, dev)
+        log(f"[bench] streaming ceiling (in-place fp32 scale over 1 GiB, read + write): {ceil:.1f} GB/s; "
+            f"{dom} at {achieved / ceil * 100:.1f}% of it")
+        roofline["stream_rmw_ceiling"] = dict(
+            kind="in-place fp32 x *= c over 1 GiB (torch elementwise kernel), read + write counted",
+            gbs=round(ceil, 1), frac_of_ceiling=round(achieved / ceil, 4))
 
     cpu = None
     if not args.no_cpu_baseline:
