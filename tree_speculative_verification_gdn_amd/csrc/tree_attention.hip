@@ -75,6 +75,29 @@ __device__ __forceinline__ uint32_t bf16_pack_rne(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((af32x2_t){a, b}, abf16x2_t));
 }
 
+// x combined with the x of lane l ^ 16 (rows of 16 lanes swapped in pairs)
+// or of lane l ^ 32 (the two halves of the wave swapped) on the vector ALU:
+// a permlane swap of a register with itself leaves the value of the pair's
+// lower row (half) in the first result and the upper one's in the second,
+// in every lane of the pair.  Sums are exact in either order; the maximum
+// is the same value up to the sign of a zero.
+__device__ __forceinline__ float pair16_max(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair16_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Is request b skipped (malformed tree or context out of range)?  Uniform.
 __device__ __forceinline__ bool attn_skip(const AttnArgs& a, int b, int& L) {
     const int t = a.shared ? 0 : b;
@@ -296,8 +319,7 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) mt = fmaxf(mt, s[kb][i]);
-        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        mt = pair32_max(pair16_max(mt));
         const float m_new = fmaxf(m_run, mt);
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
         const float factor = __builtin_amdgcn_exp2f(m_run - m_use);  // 0 while nothing was seen
@@ -310,8 +332,7 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
                 pr[kb][i] = __builtin_amdgcn_exp2f(s[kb][i] - m_use);
                 ps += pr[kb][i];
             }
-        ps += __shfl_xor(ps, 16, 64);
-        ps += __shfl_xor(ps, 32, 64);
+        ps = pair32_sum(pair16_sum(ps));
         l_run = l_run * factor + ps;
         m_run = m_new;
         // rescale the output rows 4 lg + i of this lane's blocks, unless no
