@@ -133,6 +133,29 @@ __device__ __forceinline__ void store_out(void* out, size_t idx, float o, bool o
 constexpr int kDppXor1 = 0xB1;  // quad_perm [1, 0, 3, 2]
 constexpr int kDppXor2 = 0x4E;  // quad_perm [2, 3, 0, 1]
 
+constexpr int kDppRowMirror = 0x140;      // lane i of a 16-lane row <- lane 15 - i
+constexpr int kDppRowHalfMirror = 0x141;  // lane i of an 8-lane group <- lane 7 - i
+
+template <int CTRL>
+__device__ __forceinline__ float dpp1(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum of x over the 32 lanes of this lane's half-wave, in every lane of it,
+// on the vector ALU (no LDS permute): quads by two quad permutes, 8-lane
+// groups by the half-row mirror, 16-lane rows by the row mirror, then the
+// two rows of the half-wave combined by a permlane16 swap of the register
+// with itself (the even row's value in the first result, the odd row's in
+// the second, in both rows).
+__device__ __forceinline__ float sum_half_wave(float x) {
+    x += dpp1<0xB1>(x);
+    x += dpp1<0x4E>(x);
+    x += dpp1<kDppRowHalfMirror>(x);
+    x += dpp1<kDppRowMirror>(x);
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int CTRL>
 __device__ __forceinline__ float4 dpp4(const float4& x) {
     auto m = [](float v) {

@@ -160,8 +160,7 @@ __global__ void __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(
             uc = make_float4(0.f, 0.f, 0.f, 0.f);
         }
         float ss = sumsq_bf16x4(kc);  // a row's 32 chunks sit in 32 consecutive lanes
-#pragma unroll
-        for (int off = 16; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+        ss = sum_half_wave(ss);
         *reinterpret_cast<uint2*>(s_K + j * kKQStride + 8 * c) = kc;
         *reinterpret_cast<float4*>(s_U + j * kD + 4 * c) = uc;
         if (c == 0) s_sc[j] = j < len ? (norm ? 1.0f / sqrtf(ss + 1e-6f) : 1.0f) : 0.0f;

@@ -735,8 +735,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                 const int sl = it >> 5;
                 const int ch = it & 31;
                 float ss = sumsq_bf16x4(*reinterpret_cast<const uint2*>(s_a + sl * kKQStride + ch * 8));
-    #pragma unroll
-                for (int off = 16; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+                ss = sum_half_wave(ss);
                 if (ch == 0) s_nrm[sl] = ss;
             }
         } else {
@@ -749,8 +748,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
             if (node >= N) kq_val[u] = make_uint2(0u, 0u);  // zero pad rows of the MFMA blocks
             *reinterpret_cast<uint2*>(s_a + sl * kKQStride + ch * 8) = kq_val[u];
             float ss = sumsq_bf16x4(kq_val[u]);  // a row's 32 chunks sit in 32 consecutive lanes
-    #pragma unroll
-            for (int off = 16; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+            ss = sum_half_wave(ss);
             if (ch == 0) s_nrm[sl] = ss;
         }
         if constexpr (NPB == 1) {  // two blocks: staged after the M solve, over the Gram block
@@ -1021,8 +1019,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
             // the staged path overlays the Gram block, dead after the M solve
             const int cpl = nc * 32;  // 8-byte chunks of the path's k (and of v)
             float ss = sumsq_bf16x4(pk_val);
-#pragma unroll
-            for (int off = 16; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+            ss = sum_half_wave(ss);
             if (tid < cpl) {
                 *reinterpret_cast<uint2*>(s_kp + jj * kKQStride + chp * 8) = pk_val;
                 *reinterpret_cast<uint2*>(s_vp + jj * kD + chp * 4) = pv_val;
@@ -1036,8 +1033,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                 const uint2 vc = *reinterpret_cast<const uint2*>(
                     cp.vp + rbp * cp.rs_v_p + static_cast<size_t>(h) * kD + chp * 4);
                 float s2 = sumsq_bf16x4(kc);
-#pragma unroll
-                for (int off = 16; off > 0; off >>= 1) s2 += __shfl_xor(s2, off, 64);
+                s2 = sum_half_wave(s2);
                 if (it < cpl) {
                     *reinterpret_cast<uint2*>(s_kp + (it >> 5) * kKQStride + chp * 8) = kc;
                     *reinterpret_cast<uint2*>(s_vp + (it >> 5) * kD + chp * 4) = vc;
@@ -1058,8 +1054,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
             *reinterpret_cast<uint2*>(s_kp + jj * kKQStride + chp * 8) = pk_val;
             *reinterpret_cast<uint2*>(s_vp + jj * kD + chp * 4) = pv_val;
             float ss = sumsq_bf16x4(pk_val);
-#pragma unroll
-            for (int off = 16; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+            ss = sum_half_wave(ss);
             if (chp == 0) s_scp[jj] = norm ? 1.0f / sqrtf(ss + 1e-6f) : 1.0f;
           }
             __syncthreads();
@@ -1130,8 +1125,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                         *reinterpret_cast<uint2*>(s_kp + jj * kKQStride + chp * 8) = kc;
                         *reinterpret_cast<uint2*>(s_vp + jj * kD + chp * 4) = vc;
                         float ss = sumsq_bf16x4(kc);
-#pragma unroll
-                        for (int off = 16; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+                        ss = sum_half_wave(ss);
                         if (chp == 0) s_scp[jj] = norm ? 1.0f / sqrtf(ss + 1e-6f) : 1.0f;
                         __syncthreads();
                     }
