@@ -156,6 +156,30 @@ __device__ __forceinline__ float sum_half_wave(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// The value of lane SP of this lane's 8-lane group (lanes 8a .. 8a + 7),
+// p = lane & 7, on DPP: the quad broadcast gives lane SP & 3 of this lane's
+// own quad; lanes of the other quad take it through the half-row mirror
+// (lane 8a + k <- lane 8a + 7 - k, which lies in the other quad).
+template <int SP>
+__device__ __forceinline__ float group8_lane(float v, int p) {
+    const float t = dpp1<(SP & 3) * 0x55>(v);
+    const float m = dpp1<kDppRowHalfMirror>(t);
+    return ((p ^ SP) & 4) ? m : t;
+}
+
+// group8_lane for a position sp in 1 .. 7 known once loops are unrolled
+__device__ __forceinline__ float group8_lane_at(float v, int sp, int p) {
+    switch (sp) {
+        case 1: return group8_lane<1>(v, p);
+        case 2: return group8_lane<2>(v, p);
+        case 3: return group8_lane<3>(v, p);
+        case 4: return group8_lane<4>(v, p);
+        case 5: return group8_lane<5>(v, p);
+        case 6: return group8_lane<6>(v, p);
+        default: return group8_lane<7>(v, p);
+    }
+}
+
 template <int CTRL>
 __device__ __forceinline__ float4 dpp4(const float4& x) {
     auto m = [](float v) {

@@ -820,7 +820,6 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
             // spill in the kernels capped at 128 VGPRs
             constexpr int kLP2 = NPB == 1 ? kLP : 16;
             const int p = tid & (kLP - 1);
-            const int grp_lane0 = lane & ~(kLP - 1);
             for (int i0 = 0; i0 < N; i0 += kThreads / kLP) {
                 const int i = i0 + tid / kLP;
                 const int ii = min(i, N - 1);
@@ -854,10 +853,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                 float wval = p == d - 1 ? 1.0f : 0.0f;  // W row i starts as the identity's
     #pragma unroll
                 for (int sp = kLP - 1; sp >= 1; --sp) {
-                    const float ms = __shfl(val, grp_lane0 | sp, 64);  // final M at position sp
+                    const float ms = group8_lane_at(val, sp, p);  // final M at position sp
                     val = (sp < d && p < sp) ? fmaf(-ms, gco[sp], val) : val;
                     if constexpr (STOREU) {
-                        const float ws = __shfl(wval, grp_lane0 | sp, 64);
+                        const float ws = group8_lane_at(wval, sp, p);
                         wval = (sp < d && p < sp) ? fmaf(-ws, gco[sp], wval) : wval;
                     }
                 }
@@ -1162,11 +1161,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                 float ctp[kMfmaPath];
 #pragma unroll
                 for (int e = 0; e < kMfmaPath / 2; ++e) {
-                    const float own = pacc[e];
-                    const float oth = __shfl_xor(own, 32, 64);
+                    // the two halves' values in every lane (a permlane32
+                    // swap of the register with itself: the hf = 0 lane's
+                    // value first, the hf = 1 lane's second)
+                    const auto pr2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(pacc[e]),
+                                                                      __float_as_uint(pacc[e]), false, false);
                     const int jo = 8 * (e >> 2) + (e & 3);  // j held by the hf = 0 lane
-                    ctp[jo] = hf ? oth : own;
-                    ctp[jo + 4] = hf ? own : oth;
+                    ctp[jo] = __uint_as_float(pr2[0]);
+                    ctp[jo + 4] = __uint_as_float(pr2[1]);
                 }
                 float w[kMfmaPath];
                 float A = 1.0f;
