@@ -131,6 +131,13 @@ __host__ __device__ inline MfmaLds mfma_lds_layout(int N, int NPB, int Lp = 0, b
 }
 
 
+// Conv weights of the layer step in LDS: word e (tap pair e % kWP of channel
+// 4c + e / kWP) of lane chunk c at e * kWtsRow + c, so the lanes of a
+// half-wave read consecutive words (one word each) and a writer lane's word
+// lands in its own bank too.
+constexpr int kWtsRow = 33;
+constexpr int kWtsGroup = 8 * kWtsRow;  // words per channel group (up to 8 words per chunk)
+
 // Layer step (N <= 32, one 32-row block).  One region F is used in turn by
 // (1) the v rows and the new history of the tree's conv, (2) the verify
 // stages up to the M solve, (3) the replay of one path segment (and the
@@ -173,9 +180,9 @@ __host__ __device__ inline MfmaLds layer_lds_layout(int N, int H, int Lmax) {
     L.anc = off;  off += align_up((N + 1) * 8, 16);
     L.mh = off;
     L.ml = off + align_up(NP * L.mstride, 16);
-    L.wts = off;                 // [3][256] tap-pair words: k, q, v
-    L.bia = off + 3 * 256 * 4;   // [3][128]
-    off += imax(2 * align_up(NP * L.mstride, 16), 3 * 256 * 4 + 3 * kD * 4);
+    L.wts = off;                        // [3][kWtsGroup] tap-pair words: k, q, v
+    L.bia = off + 3 * kWtsGroup * 4;    // [3][128]
+    off += imax(2 * align_up(NP * L.mstride, 16), 3 * kWtsGroup * 4 + 3 * kD * 4);
     L.cr = off;   off += align_up(N * 4, 16);
     L.cq = off;   off += align_up(N * 4, 16);
     L.alp = off;  off += align_up((Lmax + 1) * 4, 16);
@@ -378,7 +385,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
         s_anc[min(tid, N)] = my_anc;
         s_dep[min(tid, N)] = my_dep;
 #pragma unroll
-        for (int u = 0; u < 3; ++u) s_wts[u * kThreads + tid] = wq[u];
+        for (int u = 0; u < 3; ++u)
+            if (tid < kD * kWP) s_wts[u * kWtsGroup + (tid % (4 * kWP)) * kWtsRow + tid / (4 * kWP)] = wq[u];
         if (li.bias) {
 #pragma unroll
             for (int u = 0; u < 3; ++u) s_bia[u * kD + (tid & (kD - 1))] = bq[u];
@@ -638,7 +646,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                 const int grp = half == 0 ? 0 : 2;
                 uint32_t wv[4 * kWP];
 #pragma unroll
-                for (int e = 0; e < 4 * kWP; ++e) wv[e] = s_wts[grp * kThreads + 4 * c4 * kWP + e];
+                for (int e = 0; e < 4 * kWP; ++e) wv[e] = s_wts[grp * kWtsGroup + e * kWtsRow + c4];
                 float bb[4] = {0.f, 0.f, 0.f, 0.f};
                 if (has_bias) {
 #pragma unroll
@@ -666,7 +674,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                 const int cb = grp == 0 ? ck0 : (grp == 1 ? cq0 : cv0);
                 uint32_t wv[4 * kWP];
 #pragma unroll
-                for (int e = 0; e < 4 * kWP; ++e) wv[e] = s_wts[grp * kThreads + 4 * c4 * kWP + e];
+                for (int e = 0; e < 4 * kWP; ++e) wv[e] = s_wts[grp * kWtsGroup + e * kWtsRow + c4];
                 float bb[4] = {0.f, 0.f, 0.f, 0.f};
                 if (has_bias) {
 #pragma unroll
