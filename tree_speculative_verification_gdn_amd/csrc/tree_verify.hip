@@ -194,6 +194,17 @@ __host__ __device__ inline MfmaLds layer_lds_layout(int N, int H, int Lmax) {
     return L;
 }
 
+// The layout's offsets as wave-uniform (scalar) values: the LDS array bases
+// then live in scalar registers instead of taking vector registers the state
+// kernels do not have.
+__device__ __forceinline__ MfmaLds uniform_layout(MfmaLds L) {
+    static_assert(sizeof(MfmaLds) % sizeof(int) == 0, "MfmaLds holds ints only");
+    int* f = reinterpret_cast<int*>(&L);
+#pragma unroll
+    for (int i = 0; i < static_cast<int>(sizeof(MfmaLds) / sizeof(int)); ++i) f[i] = __builtin_amdgcn_readfirstlane(f[i]);
+    return L;
+}
+
 // The previous step's accepted path for the fused commit, resolved to
 // physical rows (kernel argument), and its recorded operands.
 struct CommitPrev {
@@ -259,7 +270,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     constexpr int kKQItems = MB * 32 * 32 / kThreads;       // 8-byte K/Q chunks per thread
     constexpr int kVItems = (NP * 32 + kThreads - 1) / kThreads;
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    const MfmaLds L = LAYER ? layer_lds_layout(N, H, li.Lmax) : mfma_lds_layout(N, NPB, FUSED ? cp.Lmax : 0, STOREU);
+    const MfmaLds L = uniform_layout(LAYER ? layer_lds_layout(N, H, li.Lmax)
+                                           : mfma_lds_layout(N, NPB, FUSED ? cp.Lmax : 0, STOREU));
     char* s_a = lds + L.a;
     uint16_t* s_v = reinterpret_cast<uint16_t*>(lds + L.v);
     float* s_gk = reinterpret_cast<float*>(lds + L.gk);
@@ -1240,8 +1252,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                 }
                 __syncthreads();  // the segment Gram is rewritten by the next segment
             }
-            state_store_lines(Sw, sreg, l32, hf);
         }
+        // one 32-row block: the state goes out after the contraction below,
+        // its last use (a wave's vector memory counter covers stores, so a
+        // later wait for a load would also wait for these 16 KB per wave);
+        // two blocks: here, as the contraction's four accumulator blocks
+        // leave no registers to keep the state any longer
+        if (do_commit && (NPB != 1 || !vok)) state_store_lines(Sw, sreg, l32, hf);  // uniform
         if (!vok) return;
     }
 
@@ -1263,6 +1280,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
             acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, slo, acc[mb], 0, 0, 0);
         }
     }
+    if constexpr (COMMIT && NPB == 1) {  // the committed state, after its last use
+        if (nc > 0) state_store_lines(Sw, sreg, l32, hf);  // uniform
+    }
     if constexpr (NPB != 1) {
         // V rows, over the key/query block once every wave has read it
         __syncthreads();
@@ -1275,6 +1295,16 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
         __syncthreads();
     }
 
+    // this lane's indices again, from a fresh copy of the thread id: kept
+    // live from the start of the kernel they would be spilled, and their
+    // reload would wait for the state stores above (the vector memory
+    // counter covers stores)
+    int tid_o = tid;
+    asm volatile("" : "+v"(tid_o));
+    const int hfo = (tid_o >> 5) & 1;
+    const int l32o = tid_o & 31;
+    const int r_owno = wave * 32 + l32o;
+
     // (f) R = beta (v - P k^ S_pre) from the key blocks, as bf16 hi/lo MFMA
     //     operands (a key block's output layout is a permutation of the
     //     contraction index that the M operand reads in the same order)
@@ -1284,10 +1314,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
         float rv[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int i = kb * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
+            const int i = kb * 32 + 8 * (e >> 2) + 4 * hfo + (e & 3);
             float val = 0.0f;
             if (i < N)
-                val = s_be[i] * (bf16_bits_to_f32(s_v[i * kD + r_own]) - s_cr[i] * acc[kb][e]);
+                val = s_be[i] * (bf16_bits_to_f32(s_v[i * kD + r_owno]) - s_cr[i] * acc[kb][e]);
             rv[e] = val;
         }
 #pragma unroll
@@ -1310,24 +1340,24 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
         f32x16_t o = acc[NPB + ob];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int i = ob * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
+            const int i = ob * 32 + 8 * (e >> 2) + 4 * hfo + (e & 3);
             o[e] *= (i < N) ? s_cq[i] : 0.0f;
         }
-        // wide trees: row ob*32 + l32 of M from the triangle, zero off its root path
-        const int mr = min(ob * 32 + l32, N - 1);
-        const uint64_t mpath = (ob * 32 + l32 < N) ? (s_anc[mr] | (1ull << mr)) : 0ull;
+        // wide trees: row ob*32 + l32o of M from the triangle, zero off its root path
+        const int mr = min(ob * 32 + l32o, N - 1);
+        const uint64_t mpath = (ob * 32 + l32o < N) ? (s_anc[mr] | (1ull << mr)) : 0ull;
 #pragma unroll
         for (int ks = 0; ks < 2 * NPB; ++ks) {
             if (ks > 2 * ob + 1) break;  // M is zero right of the diagonal block
             bf16x8_t mh, ml;
             if constexpr (NPB == 1) {
-                mh = lds_operand_m(s_mh, mstride, ob * 32 + l32, ks, hf);
-                ml = lds_operand_m(s_ml, mstride, ob * 32 + l32, ks, hf);
+                mh = lds_operand_m(s_mh, mstride, ob * 32 + l32o, ks, hfo);
+                ml = lds_operand_m(s_ml, mstride, ob * 32 + l32o, ks, hfo);
             } else {
                 float mv[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const int col = 16 * ks + 4 * hf + (e & 3) + 8 * (e >> 2);
+                    const int col = 16 * ks + 4 * hfo + (e & 3) + 8 * (e >> 2);
                     const float x = s_gq[mr * (mr + 1) / 2 + min(col, mr)];
                     mv[e] = ((mpath >> col) & 1ull) ? x : 0.0f;
                 }
@@ -1340,25 +1370,25 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
         }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int i = ob * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
+            const int i = ob * 32 + 8 * (e >> 2) + 4 * hfo + (e & 3);
             if (i < N)
-                store_out(out, ((rowb + s_rows[i]) * Hv + h) * kD + r_own, o[e], out_bf16 != 0);
+                store_out(out, ((rowb + s_rows[i]) * Hv + h) * kD + r_owno, o[e], out_bf16 != 0);
         }
     }
     if constexpr (STOREU) {  // U = W R: row i of U is node i's delta correction
         f32x16_t uacc = {};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8_t wh = lds_operand_m(lds + L.wh, mstride, l32, ks, hf);
-            const bf16x8_t wl = lds_operand_m(lds + L.wl, mstride, l32, ks, hf);
+            const bf16x8_t wh = lds_operand_m(lds + L.wh, mstride, l32o, ks, hfo);
+            const bf16x8_t wl = lds_operand_m(lds + L.wl, mstride, l32o, ks, hfo);
             uacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh, rhi[ks], uacc, 0, 0, 0);
             uacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh, rlo[ks], uacc, 0, 0, 0);
             uacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl, rhi[ks], uacc, 0, 0, 0);
         }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int i = 8 * (e >> 2) + 4 * hf + (e & 3);
-            if (i < N) u_out[((rowb + s_rows[i]) * Hv + h) * kD + r_own] = uacc[e];
+            const int i = 8 * (e >> 2) + 4 * hfo + (e & 3);
+            if (i < N) u_out[((rowb + s_rows[i]) * Hv + h) * kD + r_owno] = uacc[e];
         }
     }
 }
