@@ -22,6 +22,7 @@
 // prefix at positions [0, ctx_len[b]), candidate physical row r at
 // ctx_len[b] + r.
 #include <mutex>
+#include <type_traits>
 
 #include "gdn_internal.h"
 
@@ -37,6 +38,9 @@ constexpr int kAThreads = 512;  // 8 waves of 16 query rows
 constexpr int kRows = 128;      // query rows per workgroup
 constexpr int kTileKeys = 32;  // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
+// word 3 of a buffer descriptor for raw 32-bit-element loads (a nonzero
+// data format; no swizzle, no index stride)
+constexpr int kRawBufferFlags = 0x00020000;
 
 struct AttnArgs {
     int B, N, R, S, Hq, Hkv, splits, HPW, pairs, chunk, shared;
@@ -193,39 +197,66 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
     constexpr int kU = kChunks / kAThreads;     // key chunks per lane
     constexpr int kPairs = kTileKeys / 2 * (D / 8);              // (key pair, 8 values) items of a V tile
     constexpr int kVP = (kPairs + kAThreads - 1) / kAThreads;    // value items per lane
+    // The cache is read with buffer loads: one descriptor per tile (scalar
+    // registers) covers request b's kv head g from the tile's first position
+    // to the end of the request's cache, so a lane's offset inside the tile
+    // is fixed for the whole loop and a read at or past position S returns
+    // zeros (the descriptor's range check) instead of needing a clamp.
+    const int rowb = a.Hkv * D * 2;  // bytes from one position to the next
+    auto cache_rsrc = [&](const uint16_t* cache, int key0) {
+        const int k0 = min(key0, a.S);
+        const int64_t left = static_cast<int64_t>(a.S - k0) * rowb - (k0 < a.S ? g * D * 2 : 0);
+        const int nrec = static_cast<int>(left > 0xffffffffLL ? 0xffffffffu : static_cast<uint32_t>(left));
+        const uint16_t* p = cache + ((static_cast<size_t>(b) * a.S + k0) * a.Hkv + g) * D;
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), static_cast<short>(0), nrec,
+                                                 kRawBufferFlags);
+    };
+    // Key chunk c: key c / (D/8), row-contiguous.  Value item c: keys
+    // 2 (c % 16) and 2 (c % 16) + 1, values 8 (c / 16) .. + 7, so that each
+    // lane writes whole 32-bit words (two keys) of the transposed value rows,
+    // 16 lanes to consecutive words of one row and the four rows of a wave
+    // 16 banks apart
+    uint32_t koff[kU], voff[kVP];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+        const int c = tid + u * kAThreads;
+        koff[u] = static_cast<uint32_t>((c / (D / 8)) * rowb + (c % (D / 8)) * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < kVP; ++u) {
+        const int c = min(tid + u * kAThreads, kPairs - 1);  // lanes past the items load a valid chunk
+        voff[u] = static_cast<uint32_t>(2 * (c % 16) * rowb + (c / 16) * 16);
+    }
     // a tile's keys and values in registers: the next tile's loads are issued
-    // before the current tile's matrix work, so the two overlap.  Key chunk c:
-    // key c / (D/8), row-contiguous.  Value item c: keys 2 (c % 16) and
-    // 2 (c % 16) + 1, values 8 (c / 16) .. + 7, so that each lane writes whole
-    // 32-bit words (two keys) of the transposed value rows, 16 lanes to
-    // consecutive words of one row and the four rows of a wave 16 banks apart
+    // before the current tile's matrix work, so the two overlap
     uint4 kc[kU], vc0[kVP], vc1[kVP];
     auto load_tile = [&](int key0) {
+        const auto rk = cache_rsrc(a.k, key0);
+        const auto rv = cache_rsrc(a.v, key0);
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            const int c = tid + u * kAThreads;
-            const int kk = c / (D / 8), d8 = (c % (D / 8)) * 8;
-            const size_t kpos = static_cast<size_t>(min(key0 + kk, a.S - 1));
-            kc[u] = *reinterpret_cast<const uint4*>(a.k + ((static_cast<size_t>(b) * a.S + kpos) * a.Hkv + g) * D + d8);
-        }
+        for (int u = 0; u < kU; ++u)
+            kc[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff[u], 0, 0));
 #pragma unroll
         for (int u = 0; u < kVP; ++u) {
-            const int c = min(tid + u * kAThreads, kPairs - 1);  // lanes past the items load a valid chunk
-            const int pm = c % 16, vd8 = (c / 16) * 8;
-            const size_t p0 = static_cast<size_t>(min(key0 + 2 * pm, a.S - 1));
-            const size_t p1 = static_cast<size_t>(min(key0 + 2 * pm + 1, a.S - 1));
-            vc0[u] = *reinterpret_cast<const uint4*>(a.v + ((static_cast<size_t>(b) * a.S + p0) * a.Hkv + g) * D + vd8);
-            vc1[u] = *reinterpret_cast<const uint4*>(a.v + ((static_cast<size_t>(b) * a.S + p1) * a.Hkv + g) * D + vd8);
+            vc0[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff[u], 0, 0));
+            vc1[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff[u] + rowb, 0, 0));
         }
     };
-    // stage a tile from the registers into buffer `buf`: K row-major, V
-    // transposed (value row d holds the tile's keys in order).  Keys no row
-    // may see (past the partition, or candidate rows no node occupies) are
-    // staged as zeros: their weights are 0, and 0 times whatever the cache
-    // holds there must not reach the output.  The masks here and below are
-    // computed without branches: the scores are read from the matrix-core
-    // results right after them, and code between the two stays one basic
-    // block (a read in a later block after a branch got stale results here)
+    // bit j: key key0 + j of a tile exists in the partition (below hi), and
+    // (candidates) lies in a row some node occupies (`rows`, uniform) or on
+    // this lane's query row's root path (`vis_or`, per lane)
+    auto tile_bits = [&](int key0, uint64_t rows) {
+        const int sh = tree ? ((key0 - L) & 63) : 0;  // uniform: 0 or 32 for the candidates
+        const int rem = hi - key0;
+        const uint32_t below = rem >= kTileKeys ? 0xffffffffu : (rem <= 0 ? 0u : (1u << rem) - 1u);
+        return static_cast<uint32_t>(rows >> sh) & below;
+    };
+    // stage a tile from the registers into LDS buffer `buf`: K row-major, V
+    // transposed (value row d holds the tile's keys in order).  Keys are
+    // staged as they are (the scores of keys a row may not see are masked);
+    // the values of keys no row may see (past the partition, candidate rows
+    // no node occupies, positions past S) are staged as zeros, since their
+    // weight 0 times whatever the cache holds there must not reach the output
     auto stage = [&](int key0, int buf) {
         uint16_t* sk = s_k + buf * (Lds::kBuf / 2);
         uint16_t* svt = s_vt + buf * (Lds::kBuf / 2);
@@ -233,31 +264,28 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
         for (int u = 0; u < kU; ++u) {
             const int c = tid + u * kAThreads;
             const int kk = c / (D / 8), d8 = (c % (D / 8)) * 8;
-            const int key = key0 + kk;
-            const int sh = tree ? ((key - L) & 63) : 0;
-            const uint32_t keep = ((key < hi) & (((used >> sh) & 1ull) != 0ull)) ? 0xffffffffu : 0u;
-            const uint4 kw = make_uint4(kc[u].x & keep, kc[u].y & keep, kc[u].z & keep, kc[u].w & keep);
-            *reinterpret_cast<uint4*>(sk + kk * Lds::kKStride + d8) = kw;
+            *reinterpret_cast<uint4*>(sk + kk * Lds::kKStride + d8) = kc[u];
         }
+        const uint32_t keepb = tile_bits(key0, used);  // uniform
 #pragma unroll
         for (int u = 0; u < kVP; ++u) {
             const int c = tid + u * kAThreads;
             if (kPairs % kAThreads == 0 || c < kPairs) {  // uniform per wave
                 const int pm = c % 16, vd8 = (c / 16) * 8;
-                const int k0 = key0 + 2 * pm;
-                const int sh0 = tree ? ((k0 - L) & 63) : 0;
-                const int sh1 = tree ? ((k0 + 1 - L) & 63) : 0;
-                const uint32_t keep0 = ((k0 < hi) & (((used >> sh0) & 1ull) != 0ull)) ? 0xffffffffu : 0u;
-                const uint32_t keep1 = ((k0 + 1 < hi) & (((used >> sh1) & 1ull) != 0ull)) ? 0xffffffffu : 0u;
-                const uint32_t w0[4] = {vc0[u].x & keep0, vc0[u].y & keep0, vc0[u].z & keep0, vc0[u].w & keep0};
-                const uint32_t w1[4] = {vc1[u].x & keep1, vc1[u].y & keep1, vc1[u].z & keep1, vc1[u].w & keep1};
+                const uint32_t kb2 = keepb >> (2 * pm);
+                // low half: key 2 pm, high half: key 2 pm + 1 (all ones or zeros)
+                const uint32_t keep = ((kb2 & 1u) ? 0x0000ffffu : 0u) | ((kb2 & 2u) ? 0xffff0000u : 0u);
+                const uint4& r0 = vc0[u];
+                const uint4& r1 = vc1[u];
+                const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w};
+                const uint32_t w1[4] = {r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     // value rows vd8 + 2e (low halves) and vd8 + 2e + 1 (high halves)
                     *reinterpret_cast<uint32_t*>(svt + (vd8 + 2 * e) * Lds::kVStride + 2 * pm) =
-                        (w0[e] & 0xffffu) | (w1[e] << 16);
+                        ((w0[e] & 0xffffu) | (w1[e] << 16)) & keep;
                     *reinterpret_cast<uint32_t*>(svt + (vd8 + 2 * e + 1) * Lds::kVStride + 2 * pm) =
-                        (w0[e] >> 16) | (w1[e] & 0xffff0000u);
+                        ((w0[e] >> 16) | (w1[e] & 0xffff0000u)) & keep;
                 }
             }
         }
@@ -274,18 +302,18 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
 #pragma unroll
     for (int ds = 0; ds < kDS; ++ds)
         qreg[ds] = *reinterpret_cast<const abf16x8_t*>(s_q + rq * Lds::kKStride + ds * 32 + 8 * lg);
+    const float scale2 = a.scale2;  // > 0 (checked on the host)
     for (int tile = 0; tile < ntiles; ++tile) {
         const int key0 = lo + tile * kTileKeys;
         const int cur = tile & 1;
-        if (tile + 1 < ntiles) stage(key0 + kTileKeys, cur ^ 1);  // uniform
-        // clamped positions: past the last tile these re-read valid memory
-        // and are never staged
+        // (uniform.)  Past the last tile the loads read zeros and are never
+        // staged
+        if (tile + 1 < ntiles) stage(key0 + kTileKeys, cur ^ 1);
         load_tile(key0 + 2 * kTileKeys);
         const uint16_t* s_kc = s_k + cur * (Lds::kBuf / 2);
         const uint16_t* s_vc = s_vt + cur * (Lds::kBuf / 2);
 
         // S^T blocks: lane (lg, l16) holds keys 16 kb + 4 lg + i of query row rq
-        float s[2][4];
         // four independent accumulation chains (block x even/odd d step) keep
         // the matrix pipeline busy instead of waiting on one chain
         af32x4_t acc4[2][2];
@@ -299,27 +327,33 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
                     s_kc + (kb * 16 + l16) * Lds::kKStride + ds * 32 + 8 * lg);
                 acc4[kb][ds & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qreg[ds], acc4[kb][ds & 1], 0, 0, 0);
             }
+        // masked raw scores, branch-free: the scores are read from the
+        // matrix-core results right after the contraction, and the code
+        // between the two stays one basic block (a read in a later block
+        // after a branch got stale results here).  A key row q may not see
+        // gets -inf; bit 16 kb + i of `vis` is this lane's key 16 kb + 4 lg + i
+        const uint32_t vis = tile_bits(key0, vis_or) >> (4 * lg);
+        float sr[2][4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const af32x4_t acc = acc4[kb][0] + acc4[kb][1];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                // branch-free: visible if inside the partition and (for the
-                // candidates) on the row's root path
-                const int key = key0 + kb * 16 + 4 * lg + i;
-                const int sh = tree ? ((key - L) & 63) : 0;
-                const bool ok = (key < hi) & (((vis_or >> sh) & 1ull) != 0ull);
-                s[kb][i] = ok ? acc[i] * a.scale2 : -INFINITY;
+                const int bit = 16 * kb + i;
+                const uint32_t okm = static_cast<uint32_t>(static_cast<int32_t>(vis << (31 - bit)) >> 31);
+                sr[kb][i] = __uint_as_float((__float_as_uint(acc[i]) & okm) | (0xff800000u & ~okm));
             }
         }
         // online softmax per query row (the row's scores sit in lanes l16,
-        // l16 + 16, l16 + 32, l16 + 48)
+        // l16 + 16, l16 + 32, l16 + 48), in the log2 domain: the scale is
+        // positive, so the row maximum of the scaled scores is the scaled
+        // maximum of the raw ones, and -inf stays -inf
         float mt = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) mt = fmaxf(mt, s[kb][i]);
-        mt = pair32_max(pair16_max(mt));
+            for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sr[kb][i]);
+        mt = pair32_max(pair16_max(mt)) * scale2;
         const float m_new = fmaxf(m_run, mt);
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
         const float factor = __builtin_amdgcn_exp2f(m_run - m_use);  // 0 while nothing was seen
@@ -329,7 +363,7 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                pr[kb][i] = __builtin_amdgcn_exp2f(s[kb][i] - m_use);
+                pr[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sr[kb][i], scale2, -m_use));
                 ps += pr[kb][i];
             }
         ps = pair32_sum(pair16_sum(ps));
