@@ -38,6 +38,7 @@ constexpr int kAThreads = 512;  // 8 waves of 16 query rows
 constexpr int kRows = 128;      // query rows per workgroup
 constexpr int kTileKeys = 32;  // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleSlack = 8.f;  // log2 units a score may exceed the reference maximum by
 // word 3 of a buffer descriptor for raw 32-bit-element loads (a nonzero
 // data format; no swizzle, no index stride)
 constexpr int kRawBufferFlags = 0x00020000;
@@ -354,9 +355,15 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
 #pragma unroll
             for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sr[kb][i]);
         mt = pair32_max(pair16_max(mt)) * scale2;
-        const float m_new = fmaxf(m_run, mt);
+        // The row's reference maximum m_run moves only when a score exceeds
+        // it by more than kRescaleSlack (log2 units): weights then stay below
+        // 2^kRescaleSlack, far inside fp32 and the hi + lo split, and the
+        // output rows are rescaled a few times per partition instead of at
+        // almost every tile.  The first finite score always moves it.
+        const bool grow = mt > m_run + kRescaleSlack;
+        const float m_new = grow ? mt : m_run;
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float factor = __builtin_amdgcn_exp2f(m_run - m_use);  // 0 while nothing was seen
+        const float factor = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // 0 while nothing was seen
         float pr[2][4];
         float ps = 0.f;
 #pragma unroll
@@ -370,9 +377,8 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
         l_run = l_run * factor + ps;
         m_run = m_new;
         // rescale the output rows 4 lg + i of this lane's blocks, unless no
-        // row of the wave has a new maximum (factor exactly 1 for all: most
-        // tiles once the first few have been seen); the test is wave-uniform
-        if (__ballot(factor != 1.0f) != 0ull) {
+        // row of the wave moved its reference; the test is wave-uniform
+        if (__ballot(grow) != 0ull) {
             float fr[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) fr[i] = __shfl(factor, 4 * lg + i, 64);
