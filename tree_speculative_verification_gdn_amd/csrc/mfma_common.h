@@ -180,6 +180,34 @@ __device__ __forceinline__ float group8_lane_at(float v, int sp, int p) {
     }
 }
 
+// The value of lane N_ of this lane's row of 16 lanes, in every lane of the
+// row (DPP row_newbcast)
+template <int N_>
+__device__ __forceinline__ float row16_lane(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + N_, 0xF, 0xF, false));
+}
+
+// row16_lane for a lane n in 1 .. 15 known once loops are unrolled
+__device__ __forceinline__ float row16_lane_at(float v, int n) {
+    switch (n) {
+        case 1: return row16_lane<1>(v);
+        case 2: return row16_lane<2>(v);
+        case 3: return row16_lane<3>(v);
+        case 4: return row16_lane<4>(v);
+        case 5: return row16_lane<5>(v);
+        case 6: return row16_lane<6>(v);
+        case 7: return row16_lane<7>(v);
+        case 8: return row16_lane<8>(v);
+        case 9: return row16_lane<9>(v);
+        case 10: return row16_lane<10>(v);
+        case 11: return row16_lane<11>(v);
+        case 12: return row16_lane<12>(v);
+        case 13: return row16_lane<13>(v);
+        case 14: return row16_lane<14>(v);
+        default: return row16_lane<15>(v);
+    }
+}
+
 template <int CTRL>
 __device__ __forceinline__ float4 dpp4(const float4& x) {
     auto m = [](float v) {

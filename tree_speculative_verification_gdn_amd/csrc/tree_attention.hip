@@ -53,6 +53,7 @@ struct AttnArgs {
     const uint16_t* v;
     const int32_t* ctx_len;
     float scale2;   // softmax scale * log2(e)
+    int kv_cap;     // positions one buffer descriptor may span (its byte range fits 32 bits)
     float* ws_o;    // [splits + 1][B][Hq][N][D] unnormalised partial outputs
     float* ws_ml;   // [splits + 1][B][Hq][N][2] running maximum (log2 domain) and sum
     void* out;      // [B][N][Hq][D]
@@ -206,8 +207,8 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
     const int rowb = a.Hkv * D * 2;  // bytes from one position to the next
     auto cache_rsrc = [&](const uint16_t* cache, int key0) {
         const int k0 = min(key0, a.S);
-        const int64_t left = static_cast<int64_t>(a.S - k0) * rowb - (k0 < a.S ? g * D * 2 : 0);
-        const int nrec = static_cast<int>(left > 0xffffffffLL ? 0xffffffffu : static_cast<uint32_t>(left));
+        const int nrec = static_cast<int>(static_cast<uint32_t>(min(a.S - k0, a.kv_cap)) * static_cast<uint32_t>(rowb) -
+                                          static_cast<uint32_t>(k0 < a.S ? g * D * 2 : 0));
         const uint16_t* p = cache + ((static_cast<size_t>(b) * a.S + k0) * a.Hkv + g) * D;
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), static_cast<short>(0), nrec,
                                                  kRawBufferFlags);
@@ -538,6 +539,7 @@ hipError_t launch_tree_attention(const gdn_tree_desc& d, const TreeAttnArgs& ta,
     a.v = static_cast<const uint16_t*>(ta.v);
     a.ctx_len = ta.ctx_len;
     a.scale2 = ta.scale * kLog2e;
+    a.kv_cap = static_cast<int>(0xffffffffu / (static_cast<uint32_t>(ta.Hkv) * ta.D * 2u));
     const size_t rows = static_cast<size_t>(ta.splits + 1) * d.B * ta.Hq * d.N;
     a.ws_o = static_cast<float*>(ta.workspace);
     a.ws_ml = a.ws_o + rows * ta.D;

@@ -846,27 +846,37 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                 const int d = s_dep[ii];
                 const bool act = i < N && d <= kLP && p < d;
                 const uint8_t* path = s_cidx + ii * N;
-                // wide trees: the path from the ancestor bits (running mask)
+                // wide trees: the path from the ancestor bits
                 const uint64_t pm = (NPB == 1) ? 0ull : (s_anc[ii] | (1ull << ii));
-                uint64_t pr = pm;
-                int j;
+                int j;  // the node at this lane's position
                 if constexpr (NPB == 1) j = path[min(p, d - 1)];
                 else j = path_node<kLP>(pm, min(p, d - 1));
                 const float sk_j = s_sk[j];
+                // the path's nodes first (lane sp of the group holds position
+                // sp's), then every LDS read at once (each index is a valid
+                // node, whether or not the position is in use), then the
+                // products: one LDS round trip, not one per position
+                int mm[kLP];
+    #pragma unroll
+                for (int sp = 1; sp < kLP; ++sp) {
+                    const int js = __float_as_int(group8_lane_at(__int_as_float(j), sp, p));
+                    mm[sp] = sp < d ? js : ii;
+                }
+                float al[kLP], bs[kLP], gk[kLP];
+    #pragma unroll
+                for (int sp = 1; sp < kLP; ++sp) {
+                    const int m = mm[sp];
+                    al[sp] = s_al[m];
+                    bs[sp] = s_be[m] * s_sk[m];
+                    gk[sp] = s_gk[m * (m + 1) / 2 + j];
+                }
                 float gco[kLP];
                 float r = 1.0f;  // decays of positions p+1 .. s
     #pragma unroll
                 for (int sp = 1; sp < kLP; ++sp) {
                     const bool in = sp > p && sp < d;
-                    int m;
-                    if constexpr (NPB == 1) {
-                        m = path[min(sp, d - 1)];
-                    } else {
-                        pr &= pr - 1ull;  // drops position sp - 1
-                        m = sp < d ? __builtin_ctzll(pr | (1ull << 63)) : ii;
-                    }
-                    r *= in ? s_al[m] : 1.0f;
-                    gco[sp] = in ? s_be[m] * s_sk[m] * sk_j * s_gk[m * (m + 1) / 2 + j] * r : 0.0f;
+                    r *= in ? al[sp] : 1.0f;
+                    gco[sp] = in ? bs[sp] * sk_j * gk[sp] * r : 0.0f;
                 }
                 // r = P_i / P_j now
                 float val = r * s_sq[ii] * sk_j * s_gq[ii * (ii + 1) / 2 + j];
@@ -910,7 +920,6 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                 const uint64_t deep = __ballot(lane < N && dl > kLP && dl <= kLP2);
                 const int ndeep = __popcll(deep);
                 const int p2 = tid & (kLP2 - 1);
-                const int grp2 = lane & ~(kLP2 - 1);
                 for (int q0 = 0; q0 < ndeep; q0 += kThreads / kLP2) {  // uniform
                     const int qi = q0 + tid / kLP2;
                     uint64_t dm = deep;
@@ -919,23 +928,37 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                     const int d = s_dep[i];
                     const bool act = qi < ndeep && p2 < d;
                     const uint64_t pm = s_anc[i] | (1ull << i);
-                    uint64_t pr = pm;
                     const int j = path_node<kLP2>(pm, min(p2, d - 1));
                     const float sk_j = s_sk[j];
+                    // as above: the nodes from the group's lanes, then all LDS
+                    // reads, then products
+                    // (in chunks of five positions, to bound the registers held)
                     float gco[kLP2];
                     float r = 1.0f;
     #pragma unroll
-                    for (int sp = 1; sp < kLP2; ++sp) {
-                        const bool in = sp > p2 && sp < d;
-                        pr &= pr - 1ull;
-                        const int m = sp < d ? __builtin_ctzll(pr | (1ull << 63)) : i;
-                        r *= in ? s_al[m] : 1.0f;
-                        gco[sp] = in ? s_be[m] * s_sk[m] * sk_j * s_gk[m * (m + 1) / 2 + j] * r : 0.0f;
+                    for (int s0 = 1; s0 < kLP2; s0 += 5) {
+                        float al[5], bs[5], gk[5];
+    #pragma unroll
+                        for (int c = 0; c < 5; ++c) {
+                            const int sp = s0 + c;
+                            const int js = __float_as_int(row16_lane_at(__int_as_float(j), sp));
+                            const int m = sp < d ? js : i;
+                            al[c] = s_al[m];
+                            bs[c] = s_be[m] * s_sk[m];
+                            gk[c] = s_gk[m * (m + 1) / 2 + j];
+                        }
+    #pragma unroll
+                        for (int c = 0; c < 5; ++c) {
+                            const int sp = s0 + c;
+                            const bool in = sp > p2 && sp < d;
+                            r *= in ? al[c] : 1.0f;
+                            gco[sp] = in ? bs[c] * sk_j * gk[c] * r : 0.0f;
+                        }
                     }
                     float val = r * s_sq[i] * sk_j * s_gq[i * (i + 1) / 2 + j];
     #pragma unroll
                     for (int sp = kLP2 - 1; sp >= 1; --sp) {
-                        const float ms = __shfl(val, grp2 | sp, 64);
+                        const float ms = row16_lane_at(val, sp);  // lane sp of the 16-lane group
                         val = (sp < d && p2 < sp) ? fmaf(-ms, gco[sp], val) : val;
                     }
                     if (act) {
