@@ -1331,17 +1331,28 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     // (f) R = beta (v - P k^ S_pre) from the key blocks, as bf16 hi/lo MFMA
     //     operands (a key block's output layout is a permutation of the
     //     contraction index that the M operand reads in the same order)
+    // (a lane's 16 entries of a block are four runs of four consecutive
+    // nodes: the per-node scalars are read four at a time; entries past N
+    // read padding or the next array and are masked)
     bf16x8_t rhi[2 * NPB], rlo[2 * NPB];
 #pragma unroll
     for (int kb = 0; kb < NPB; ++kb) {
         float rv[16];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int i = kb * 32 + 8 * (e >> 2) + 4 * hfo + (e & 3);
-            float val = 0.0f;
-            if (i < N)
-                val = s_be[i] * (bf16_bits_to_f32(s_v[i * kD + r_owno]) - s_cr[i] * acc[kb][e]);
-            rv[e] = val;
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const int i0 = kb * 32 + 8 * g4 + 4 * hfo;
+            const float4 be4 = *reinterpret_cast<const float4*>(s_be + i0);
+            const float4 cr4 = *reinterpret_cast<const float4*>(s_cr + i0);
+            const float bev[4] = {be4.x, be4.y, be4.z, be4.w};
+            const float crv[4] = {cr4.x, cr4.y, cr4.z, cr4.w};
+#pragma unroll
+            for (int e3 = 0; e3 < 4; ++e3) {
+                const int e = 4 * g4 + e3;
+                float val = 0.0f;
+                if (i0 + e3 < N)
+                    val = bev[e3] * (bf16_bits_to_f32(s_v[(i0 + e3) * kD + r_owno]) - crv[e3] * acc[kb][e]);
+                rv[e] = val;
+            }
         }
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -1362,9 +1373,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     for (int ob = 0; ob < NPB; ++ob) {
         f32x16_t o = acc[NPB + ob];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int i = ob * 32 + 8 * (e >> 2) + 4 * hfo + (e & 3);
-            o[e] *= (i < N) ? s_cq[i] : 0.0f;
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const int i0 = ob * 32 + 8 * g4 + 4 * hfo;
+            const float4 cq4 = *reinterpret_cast<const float4*>(s_cq + i0);
+            const float cqv[4] = {cq4.x, cq4.y, cq4.z, cq4.w};
+#pragma unroll
+            for (int e3 = 0; e3 < 4; ++e3) o[4 * g4 + e3] *= (i0 + e3 < N) ? cqv[e3] : 0.0f;
         }
         // wide trees: row ob*32 + l32o of M from the triangle, zero off its root path
         const int mr = min(ob * 32 + l32o, N - 1);
@@ -1392,10 +1406,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
             o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ml, rhi[ks], o, 0, 0, 0);
         }
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int i = ob * 32 + 8 * (e >> 2) + 4 * hfo + (e & 3);
-            if (i < N)
-                store_out(out, ((rowb + s_rows[i]) * Hv + h) * kD + r_owno, o[e], out_bf16 != 0);
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const int i0 = ob * 32 + 8 * g4 + 4 * hfo;
+            const int4 rw4 = *reinterpret_cast<const int4*>(s_rows + i0);
+            const int rwv[4] = {rw4.x, rw4.y, rw4.z, rw4.w};
+#pragma unroll
+            for (int e3 = 0; e3 < 4; ++e3)
+                if (i0 + e3 < N)
+                    store_out(out, ((rowb + rwv[e3]) * Hv + h) * kD + r_owno, o[4 * g4 + e3], out_bf16 != 0);
         }
     }
     if constexpr (STOREU) {  // U = W R: row i of U is node i's delta correction
