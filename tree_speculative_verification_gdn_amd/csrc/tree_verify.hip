@@ -843,14 +843,19 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
             for (int i0 = 0; i0 < N; i0 += kThreads / kLP) {
                 const int i = i0 + tid / kLP;
                 const int ii = min(i, N - 1);
-                const int d = s_dep[ii];
+                const int d0 = s_dep[ii];
+                // wide trees: a node one deeper than the lanes (depth 9) is
+                // solved here too: the lanes take path positions 1 .. 8
+                // exactly as a depth-8 path, and position 0 follows at the end
+                const int sh = (NPB != 1 && d0 == kLP + 1) ? 1 : 0;  // uniform in the group
+                const int d = d0 - sh;  // positions on the lanes
                 const bool act = i < N && d <= kLP && p < d;
                 const uint8_t* path = s_cidx + ii * N;
                 // wide trees: the path from the ancestor bits
                 const uint64_t pm = (NPB == 1) ? 0ull : (s_anc[ii] | (1ull << ii));
                 int j;  // the node at this lane's position
                 if constexpr (NPB == 1) j = path[min(p, d - 1)];
-                else j = path_node<kLP>(pm, min(p, d - 1));
+                else j = path_node<kLP + 1>(pm, min(p + sh, d0 - 1));
                 const float sk_j = s_sk[j];
                 // the path's nodes first (lane sp of the group holds position
                 // sp's), then every LDS read at once (each index is a valid
@@ -906,18 +911,53 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                     } else {
                         s_gq[i * (i + 1) / 2 + j] = val;  // only this lane reads that entry
                     }
-                    if (p == 0) {
+                    if (p == 0 && !sh) {
                         const float P_i = r * s_al[j];  // j = n_0: times the root-level decay
                         s_cr[i] = P_i * s_sk[i];
                         s_cq[i] = P_i * s_sq[i];
                     }
                 }
+                if constexpr (NPB != 1) {
+                    if (sh) {  // the group's node has depth 9 (uniform in the group)
+                        // position 0 (node j0, the lowest index on the path):
+                        //   M_i,j0 = (P_i / P_j0) q^_i . k^_j0 - sum_s M_i,n_s G_n_s,j0
+                        // over positions s = 1 .. 8, lane p holding s = p + 1;
+                        // G_m,j0 carries the decays of positions 1 .. s, an
+                        // inclusive prefix product over the lanes
+                        const int j0 = __builtin_ctzll(pm);
+                        float pref = s_al[j];
+                        {
+                            const float t1 = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                0, __builtin_bit_cast(int, pref), 0x111, 0xF, 0xF, false));  // row_shr:1
+                            pref = p >= 1 ? pref * t1 : pref;
+                            const float t2 = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                0, __builtin_bit_cast(int, pref), 0x112, 0xF, 0xF, false));  // row_shr:2
+                            pref = p >= 2 ? pref * t2 : pref;
+                            const float t4 = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                0, __builtin_bit_cast(int, pref), 0x114, 0xF, 0xF, false));  // row_shr:4
+                            pref = p >= 4 ? pref * t4 : pref;
+                        }
+                        const float sk_j0 = s_sk[j0];
+                        float term = val * (s_be[j] * s_sk[j] * sk_j0 * s_gk[j * (j + 1) / 2 + j0] * pref);
+                        term += dpp1<0xB1>(term);
+                        term += dpp1<0x4E>(term);
+                        term += dpp1<kDppRowHalfMirror>(term);
+                        const float r0 = group8_lane<7>(pref, p);  // P_i / P_j0
+                        const float v0 = r0 * s_sq[ii] * sk_j0 * s_gq[ii * (ii + 1) / 2 + j0] - term;
+                        if (i < N && p == 0) {
+                            s_gq[i * (i + 1) / 2 + j0] = v0;
+                            const float P_i = r0 * s_al[j0];
+                            s_cr[i] = P_i * s_sk[i];
+                            s_cq[i] = P_i * s_sq[i];
+                        }
+                    }
+                }
             }
             if constexpr (kLP2 > kLP) {
-                // the nodes of depth kLP+1 .. kLP2 (a mask every wave forms
+                // the nodes of depth kLP+2 .. kLP2 (a mask every wave forms
                 // alike), one per group of kLP2 lanes, as above
                 const int dl = s_dep[min(lane, N - 1)];
-                const uint64_t deep = __ballot(lane < N && dl > kLP && dl <= kLP2);
+                const uint64_t deep = __ballot(lane < N && dl > kLP + 1 && dl <= kLP2);  // depth 9: above
                 const int ndeep = __popcll(deep);
                 const int p2 = tid & (kLP2 - 1);
                 for (int q0 = 0; q0 < ndeep; q0 += kThreads / kLP2) {  // uniform
