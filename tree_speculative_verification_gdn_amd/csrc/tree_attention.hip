@@ -445,31 +445,56 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
     }
 }
 
-// Merge of the key partitions: one workgroup per (request, head, node) row,
-// one thread per output element.
+// Merge of the key partitions (the standard split-softmax merge): one
+// workgroup per (request, head, node) row, one thread per output element.
+// The partitions' maxima, weights exp2(m_s - M) and the denominator are
+// formed once per row, cooperatively, with the weights kept in LDS; then each
+// thread sums its element over the partitions with many loads in flight.
+constexpr int kMaxPartitions = 1025;  // splits <= 1024, plus the candidates'
 template <int D>
 __global__ void __launch_bounds__(D) tree_attn_merge_kernel(const AttnArgs a) {
+    __shared__ float s_w[kMaxPartitions];
+    __shared__ float s_red[D / 64];
     const int row = blockIdx.x;  // ((b * Hq) + h) * N + i
     const int N = a.N;
     const int i = row % N;
     const int h = (row / N) % a.Hq;
     const int b = row / (N * a.Hq);
     int L;
-    if (attn_skip(a, b, L)) return;
+    if (attn_skip(a, b, L)) return;  // uniform
     const int d = threadIdx.x;
+    const int wv = d >> 6;
     const size_t per_split = static_cast<size_t>(a.B) * a.Hq * N;
     const int nsp = a.splits + 1;
     float M = -INFINITY;
-#pragma unroll 8
-    for (int s = 0; s < nsp; ++s) M = fmaxf(M, a.ws_ml[(s * per_split + row) * 2]);
-    float acc = 0.f, den = 0.f;
-#pragma unroll 8
-    for (int s = 0; s < nsp; ++s) {
-        const float* ml = a.ws_ml + (s * per_split + row) * 2;
-        const float wgt = __builtin_amdgcn_exp2f(ml[0] - M);  // 0 for an empty partition
-        den += wgt * ml[1];
-        acc += wgt * a.ws_o[(s * per_split + row) * D + d];
+    for (int s = d; s < nsp; s += D) {
+        const float m = a.ws_ml[(s * per_split + row) * 2];
+        s_w[s] = m;
+        M = fmaxf(M, m);
     }
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) M = fmaxf(M, __shfl_xor(M, x, 64));
+    if ((d & 63) == 0) s_red[wv] = M;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) M = fmaxf(M, s_red[k]);
+    float den = 0.f;
+    for (int s = d; s < nsp; s += D) {
+        const float wgt = __builtin_amdgcn_exp2f(s_w[s] - M);  // 0 for an empty partition
+        s_w[s] = wgt;
+        den += wgt * a.ws_ml[(s * per_split + row) * 2 + 1];
+    }
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) den += __shfl_xor(den, x, 64);
+    __syncthreads();  // every lane has read s_red (the maxima)
+    if ((d & 63) == 0) s_red[wv] = den;
+    __syncthreads();  // the weights and the partial denominators
+    den = 0.f;
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) den += s_red[k];
+    float acc = 0.f;
+#pragma unroll 16
+    for (int s = 0; s < nsp; ++s) acc += s_w[s] * a.ws_o[(s * per_split + row) * D + d];
     const float val = acc / den;
     const size_t oi = ((static_cast<size_t>(b) * N + i) * a.Hq + h) * D + d;
     if (a.out_bf16)
