@@ -203,6 +203,33 @@ def test_repeat_runs_are_bit_identical():
         _cmp(again, oo)
 
 
+@pytest.mark.parametrize("profile", ["rising", "falling", "spike"])
+def test_score_range_across_tiles(profile):
+    # keys scaled along the prefix so that a partition's running maximum
+    # climbs far past the 2^8 slack the kernel allows before it rescales the
+    # output rows (rising), is set by the first tiles with later weights
+    # many orders of magnitude smaller (falling), or jumps at one late key
+    # (spike); about 14 tiles per partition
+    c = gi.make_attention_case(30, B=2, N=11, R=14, Hq=4, Hkv=2, D=128, ctx=[900, 640], S=1000)
+    k = (c["k"].astype(np.uint32) << 16).view(np.float32).copy()
+    for b in range(c["B"]):
+        L = int(c["ctx"][b])
+        pos = np.arange(L, dtype=np.float32) / max(L - 1, 1)
+        if profile == "rising":
+            f = 0.25 + 5.0 * pos
+        elif profile == "falling":
+            f = 5.25 - 5.0 * pos
+        else:
+            f = np.full(L, 0.5, np.float32)
+            f[(2 * L) // 3] = 12.0
+        k[b, :L] *= f[:, None, None]
+    c["k"] = gi.f32_to_bf16_bits(k)
+    go, err, st = run_attention(c, splits=2)
+    oo, oerr = oracle(c, st)
+    assert err == oerr == 0
+    _cmp(go, oo)
+
+
 @pytest.mark.parametrize("N,R,ctx", [(1, 1, [0, 3]), (64, 64, [37, 0]), (32, 64, [100, 1])])
 def test_node_count_edges(N, R, ctx):
     # a single node (its own key, or the prefix and itself), the largest tree
