@@ -104,7 +104,10 @@ __global__ void __launch_bounds__(kConvThreads) conv_gather_kernel(const ConvKAr
     // kTileLanes chunks; the tile's weights and bias; the row -> node map
     extern __shared__ __attribute__((aligned(16))) char lds[];
     Chunk<CPT>* s_x = reinterpret_cast<Chunk<CPT>*>(lds);  // [N + H][kTileLanes]
-    uint32_t* s_w = reinterpret_cast<uint32_t*>(lds + conv_lds_x_bytes(N, W, CPT));  // [kTileLanes][kWW]
+    // weights word-major: word e of lane chunk c at e * kTileLanes + c, so the
+    // lanes of a row read consecutive words (lane-major, 16 words apart, the
+    // reads of a half-wave shared a few banks)
+    uint32_t* s_w = reinterpret_cast<uint32_t*>(lds + conv_lds_x_bytes(N, W, CPT));  // [kWW][kTileLanes]
     float* s_b = reinterpret_cast<float*>(reinterpret_cast<char*>(s_w) + kTileLanes * kWW * 4);  // [kTileLanes][CPT]
     int32_t* s_node_of_row = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(s_b) + TILE * 4);  // [R]
     __shared__ int32_t s_row[kMaxNodes];
@@ -257,14 +260,13 @@ __global__ void __launch_bounds__(kConvThreads) conv_gather_kernel(const ConvKAr
         const uint32_t wv[4] = {wg4.x, wg4.y, wg4.z, wg4.w};
         if constexpr (W % 2 == 0) {
             if (rs < kWG) {
-                uint32_t* wd = s_w + lane * kWW + 4 * rs;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (4 * rs + e < kWW) wd[e] = wv[e];
+                    if (4 * rs + e < kWW) s_w[(4 * rs + e) * kTileLanes + lane] = wv[e];
             }
         } else if (rs < CPT) {
 #pragma unroll
-            for (int q = 0; q < kWP; ++q) s_w[lane * kWW + rs * kWP + q] = wv[q];
+            for (int q = 0; q < kWP; ++q) s_w[(rs * kWP + q) * kTileLanes + lane] = wv[q];
         }
     }
     if (bias && rs < CPT / 4) *reinterpret_cast<float4*>(s_b + lane * CPT + 4 * rs) = bq;
@@ -275,7 +277,7 @@ __global__ void __launch_bounds__(kConvThreads) conv_gather_kernel(const ConvKAr
     // for channel c and pair p, (x of tap 2p, x of tap 2p+1) . (w[c][2p], w[c][2p+1])
     uint32_t wr[kWW];
 #pragma unroll
-    for (int e = 0; e < kWW; ++e) wr[e] = s_w[lane * kWW + e];
+    for (int e = 0; e < kWW; ++e) wr[e] = s_w[e * kTileLanes + lane];
     constexpr int NW = CPT / 2;  // 32-bit words of a row chunk
     float bl[CPT];
 #pragma unroll
