@@ -1435,7 +1435,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int col = 16 * ks + 4 * hfo + (e & 3) + 8 * (e >> 2);
-                    const float x = s_gq[mr * (mr + 1) / 2 + min(col, mr)];
+                    // unclamped: past the row's end (col > mr) the read lands in
+                    // the next rows or the ancestor masks that follow the
+                    // triangle in LDS, and the mask drops it; consecutive
+                    // columns stay consecutive reads
+                    const float x = s_gq[mr * (mr + 1) / 2 + col];
                     mv[e] = ((mpath >> col) & 1ull) ? x : 0.0f;
                 }
                 split_hi_lo(make_float4(mv[0], mv[1], mv[2], mv[3]), make_float4(mv[4], mv[5], mv[6], mv[7]),
