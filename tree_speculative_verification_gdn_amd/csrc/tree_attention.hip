@@ -12,17 +12,17 @@
 // tiles of 32: the tile's keys row-major and its values transposed go to LDS,
 // S^T = K Q^T runs on v_mfma_f32_16x16x32_bf16 (a wave's lane holds one query
 // row's scores for four keys per 16-key block), an online softmax keeps each
-// row's running maximum and sum in the log2 domain, and O += P V on the same
+// row's reference maximum and sum in the log2 domain (the reference moves
+// only when a score exceeds it by more than 2^8), and O += P V on the same
 // instruction with P split into bf16 hi + lo (P's rounding error stays near
-// 2^-17 of a weight).  Each partition writes its unnormalised O, maximum and
-// sum; a second kernel merges the partitions (the standard split-softmax
-// merge) into the output.
+// 2^-17 of a weight).  Each partition writes its unnormalised O, reference
+// maximum and sum; a second kernel merges the partitions (the standard
+// split-softmax merge) into the output.
 //
 // Layouts: q [B][N][Hq][D] logical node rows; k, v [B][S][Hkv][D] bf16, the
 // prefix at positions [0, ctx_len[b]), candidate physical row r at
 // ctx_len[b] + r.
 #include <mutex>
-#include <type_traits>
 
 #include "gdn_internal.h"
 
