@@ -144,9 +144,12 @@ def test_tree27_bfs_packing_and_shared_topology():
 
 
 @pytest.mark.parametrize("N,bmax,depth", [(1, 1, 0), (16, 2, 5), (17, 4, 3), (32, 3, 6),
-                                          (33, 64, 1), (48, 2, 12), (64, 1, 63), (64, 64, 1)])
+                                          (33, 64, 1), (37, 3, 8), (48, 2, 12), (50, 2, 9),
+                                          (64, 1, 63), (64, 64, 1)])
 def test_node_count_edges(N, bmax, depth):
-    # MB = 1..4 kernel variants, deepest chain, widest star
+    # MB = 1..4 kernel variants, deepest chain, widest star; two blocks with
+    # a node count off the multiples of four and paths of length 9 (solved in
+    # the 8-lane pass) with and without longer ones
     tree = "chain" if bmax == 1 else "random"
     cfg = gi.CONFIGS[3].replace(N=N, R=N + 3, bmax=bmax, depth_max=depth, tree=tree, B=6)
     case = gi.make_case(cfg, seed=N * 7 + bmax, extra_slots=1)
