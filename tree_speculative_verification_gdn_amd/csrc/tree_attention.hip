@@ -9,8 +9,9 @@
 // in equal ranges; partition `splits` covers the R candidate slots under the
 // ancestry mask.  A workgroup holds up to 128 query rows (the N nodes of four
 // heads, or of two heads when N > 32), 16 per wave, and walks its keys in
-// tiles of 32: the tile's keys row-major and its values transposed go to LDS,
-// S^T = K Q^T runs on v_mfma_f32_16x16x32_bf16 (a wave's lane holds one query
+// tiles of 32: the tile's keys and values go to LDS row-major (the values
+// are read back with the transposing LDS read), S^T = K Q^T runs on
+// v_mfma_f32_16x16x32_bf16 (a wave's lane holds one query
 // row's scores for four keys per 16-key block), an online softmax keeps each
 // row's reference maximum and sum in the log2 domain (the reference moves
 // only when a score exceeds it by more than 2^8), and O += P V on the same
@@ -63,14 +64,16 @@ struct AttnArgs {
 
 template <int D>
 struct AttnLds {
-    // bf16 per staged key or query row: D + 16 (a 32-byte pad) puts the rows
-    // of a key block 8 banks apart, which keeps the 16-byte fragment reads
-    // free of bank conflicts (a 16-byte pad cost 10% of the launch in them)
+    // bf16 per staged key, value or query row: D + 16 (a 32-byte pad) puts
+    // the rows of a key block 8 banks apart, which keeps the 16-byte fragment
+    // reads of keys and queries free of bank conflicts (a 16-byte pad cost 10%
+    // of the launch in them), and the transposing 8-byte reads of values too
+    // (the eight keys one read of 32 lanes touches fall on distinct 32-byte
+    // bank groups)
     static constexpr int kKStride = D + 16;
-    static constexpr int kVStride = kTileKeys + 4;  // bf16 per transposed value row
-    static constexpr int Q = 0;                     // the workgroup's query rows
+    static constexpr int Q = 0;  // the workgroup's query rows
     static constexpr int kKBytes = kTileKeys * kKStride * 2;
-    static constexpr int kVBytes = D * kVStride * 2;
+    static constexpr int kVBytes = kKBytes;
     static constexpr int K = Q + kRows * kKStride * 2;  // two buffers: K, V, K, V
     static constexpr int V = K + kKBytes;
     static constexpr int kBuf = kKBytes + kVBytes;      // offset of the second buffer
@@ -82,6 +85,18 @@ struct AttnLds {
 // two finite fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t bf16_pack_rne(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((af32x2_t){a, b}, abf16x2_t));
+}
+
+typedef short ai16x4_t __attribute__((ext_vector_type(4)));
+typedef short ai16x8_t __attribute__((ext_vector_type(8)));
+
+// the transposing 8-byte LDS read (ds_read_b64_tr_b16) at an LDS address p
+// (8-byte aligned; each lane addresses four 16-bit values): within each row
+// of 16 lanes, lane 4 a + c receives value c of the pieces that lanes a,
+// 4 + a, 8 + a and 12 + a address, one from each, in that order
+__device__ __forceinline__ ai16x4_t lds_read_tr16x4(const uint16_t* p) {
+    typedef __attribute__((address_space(3))) ai16x4_t lds_i16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);  // generic -> LDS address
 }
 
 // x combined with the x of lane l ^ 16 (rows of 16 lanes swapped in pairs)
@@ -123,7 +138,7 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
     extern __shared__ __attribute__((aligned(16))) char lds[];
     uint16_t* s_q = reinterpret_cast<uint16_t*>(lds + Lds::Q);
     uint16_t* s_k = reinterpret_cast<uint16_t*>(lds + Lds::K);
-    uint16_t* s_vt = reinterpret_cast<uint16_t*>(lds + Lds::V);
+    uint16_t* s_v = reinterpret_cast<uint16_t*>(lds + Lds::V);
     int32_t* s_row = reinterpret_cast<int32_t*>(lds + Lds::ROW);
     uint64_t* s_vis = reinterpret_cast<uint64_t*>(lds + Lds::VIS);
 
@@ -198,10 +213,8 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
     float m_run = -INFINITY, l_run = 0.f;
 
     const int ntiles = (hi - lo + kTileKeys - 1) / kTileKeys;
-    constexpr int kChunks = kTileKeys * D / 8;  // 16-byte chunks of a K tile
-    constexpr int kU = kChunks / kAThreads;     // key chunks per lane
-    constexpr int kPairs = kTileKeys / 2 * (D / 8);              // (key pair, 8 values) items of a V tile
-    constexpr int kVP = (kPairs + kAThreads - 1) / kAThreads;    // value items per lane
+    constexpr int kChunks = kTileKeys * D / 8;  // 16-byte chunks of a K (or V) tile
+    constexpr int kU = kChunks / kAThreads;     // chunks of each per lane
     // The cache is read with buffer loads: one descriptor per tile (scalar
     // registers) covers request b's kv head g from the tile's first position
     // to the end of the request's cache, so a lane's offset inside the tile
@@ -216,35 +229,24 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), static_cast<short>(0), nrec,
                                                  kRawBufferFlags);
     };
-    // Key chunk c: key c / (D/8), row-contiguous.  Value item c: keys
-    // 2 (c % 16) and 2 (c % 16) + 1, values 8 (c / 16) .. + 7, so that each
-    // lane writes whole 32-bit words (two keys) of the transposed value rows,
-    // 16 lanes to consecutive words of one row and the four rows of a wave
-    // 16 banks apart
-    uint32_t koff[kU], voff[kVP];
+    // chunk c of a tile: key c / (D/8), values 8 (c % (D/8)) .. + 7, the
+    // same for keys and values
+    uint32_t koff[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
         const int c = tid + u * kAThreads;
         koff[u] = static_cast<uint32_t>((c / (D / 8)) * rowb + (c % (D / 8)) * 16);
     }
-#pragma unroll
-    for (int u = 0; u < kVP; ++u) {
-        const int c = min(tid + u * kAThreads, kPairs - 1);  // lanes past the items load a valid chunk
-        voff[u] = static_cast<uint32_t>(2 * (c % 16) * rowb + (c / 16) * 16);
-    }
     // a tile's keys and values in registers: the next tile's loads are issued
     // before the current tile's matrix work, so the two overlap
-    uint4 kc[kU], vc0[kVP], vc1[kVP];
+    uint4 kc[kU], vc[kU];
     auto load_tile = [&](int key0) {
         const auto rk = cache_rsrc(a.k, key0);
         const auto rv = cache_rsrc(a.v, key0);
 #pragma unroll
-        for (int u = 0; u < kU; ++u)
+        for (int u = 0; u < kU; ++u) {
             kc[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff[u], 0, 0));
-#pragma unroll
-        for (int u = 0; u < kVP; ++u) {
-            vc0[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff[u], 0, 0));
-            vc1[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff[u] + rowb, 0, 0));
+            vc[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, koff[u], 0, 0));
         }
     };
     // bit j: key key0 + j of a tile exists in the partition (below hi), and
@@ -256,43 +258,24 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
         const uint32_t below = rem >= kTileKeys ? 0xffffffffu : (rem <= 0 ? 0u : (1u << rem) - 1u);
         return static_cast<uint32_t>(rows >> sh) & below;
     };
-    // stage a tile from the registers into LDS buffer `buf`: K row-major, V
-    // transposed (value row d holds the tile's keys in order).  Keys are
-    // staged as they are (the scores of keys a row may not see are masked);
-    // the values of keys no row may see (past the partition, candidate rows
-    // no node occupies, positions past S) are staged as zeros, since their
-    // weight 0 times whatever the cache holds there must not reach the output
+    // stage a tile from the registers into LDS buffer `buf`, keys and values
+    // alike row-major (one row per key).  Keys are staged as they are (the
+    // scores of keys a row may not see are masked); the values of keys no row
+    // may see (past the partition, candidate rows no node occupies, positions
+    // past S) are staged as zeros, since their weight 0 times whatever the
+    // cache holds there must not reach the output
     auto stage = [&](int key0, int buf) {
         uint16_t* sk = s_k + buf * (Lds::kBuf / 2);
-        uint16_t* svt = s_vt + buf * (Lds::kBuf / 2);
+        uint16_t* sv = s_v + buf * (Lds::kBuf / 2);
+        const uint32_t keepb = tile_bits(key0, used);  // uniform
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const int c = tid + u * kAThreads;
             const int kk = c / (D / 8), d8 = (c % (D / 8)) * 8;
             *reinterpret_cast<uint4*>(sk + kk * Lds::kKStride + d8) = kc[u];
-        }
-        const uint32_t keepb = tile_bits(key0, used);  // uniform
-#pragma unroll
-        for (int u = 0; u < kVP; ++u) {
-            const int c = tid + u * kAThreads;
-            if (kPairs % kAThreads == 0 || c < kPairs) {  // uniform per wave
-                const int pm = c % 16, vd8 = (c / 16) * 8;
-                const uint32_t kb2 = keepb >> (2 * pm);
-                // low half: key 2 pm, high half: key 2 pm + 1 (all ones or zeros)
-                const uint32_t keep = ((kb2 & 1u) ? 0x0000ffffu : 0u) | ((kb2 & 2u) ? 0xffff0000u : 0u);
-                const uint4& r0 = vc0[u];
-                const uint4& r1 = vc1[u];
-                const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w};
-                const uint32_t w1[4] = {r1.x, r1.y, r1.z, r1.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    // value rows vd8 + 2e (low halves) and vd8 + 2e + 1 (high halves)
-                    *reinterpret_cast<uint32_t*>(svt + (vd8 + 2 * e) * Lds::kVStride + 2 * pm) =
-                        ((w0[e] & 0xffffu) | (w1[e] << 16)) & keep;
-                    *reinterpret_cast<uint32_t*>(svt + (vd8 + 2 * e + 1) * Lds::kVStride + 2 * pm) =
-                        ((w0[e] >> 16) | (w1[e] & 0xffff0000u)) & keep;
-                }
-            }
+            const uint32_t keep = 0u - ((keepb >> kk) & 1u);  // all ones or zeros
+            *reinterpret_cast<uint4*>(sv + kk * Lds::kKStride + d8) =
+                make_uint4(vc[u].x & keep, vc[u].y & keep, vc[u].z & keep, vc[u].w & keep);
         }
     };
     // two LDS buffers: while the waves work on tile t in one, tile t + 1 is
@@ -316,7 +299,7 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
         if (tile + 1 < ntiles) stage(key0 + kTileKeys, cur ^ 1);
         load_tile(key0 + 2 * kTileKeys);
         const uint16_t* s_kc = s_k + cur * (Lds::kBuf / 2);
-        const uint16_t* s_vc = s_vt + cur * (Lds::kBuf / 2);
+        const uint16_t* s_vc = s_v + cur * (Lds::kBuf / 2);
 
         // S^T blocks: lane (lg, l16) holds keys 16 kb + 4 lg + i of query row rq
         // four independent accumulation chains (block x even/odd d step) keep
@@ -407,17 +390,23 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
         const abf16x8_t pa_lo = __builtin_bit_cast(abf16x8_t, make_uint4(pl[0], pl[1], pl[2], pl[3]));
         // value operands for eight d blocks at a time, then the hi products
         // of all eight, then the lo products (independent accumulators back
-        // to back)
+        // to back).  Lane (lg, l16) needs value column 16 db + l16 of keys
+        // 4 lg .. + 3 and 16 + 4 lg .. + 3.  The transposing LDS read hands
+        // lane 4 a + c of each 16-lane row element c of the 4-value pieces
+        // that the row's lanes a, 4 + a, 8 + a, 12 + a address: so lane
+        // (lg, l16) addresses key 4 lg + l16 / 4, columns 16 db + 4 (l16 % 4)
+        // .. + 3, and 16 keys further for the second half
+        const uint16_t* vrow = s_vc + (4 * lg + (l16 >> 2)) * Lds::kKStride + 4 * (l16 & 3);
         constexpr int kDBH = kDB < 8 ? kDB : 8;
 #pragma unroll
         for (int d0 = 0; d0 < kDB; d0 += kDBH) {
             abf16x8_t vb[kDBH];
 #pragma unroll
             for (int j = 0; j < kDBH; ++j) {
-                const uint16_t* vr = s_vc + ((d0 + j) * 16 + l16) * Lds::kVStride + 4 * lg;
-                const uint2 v0 = *reinterpret_cast<const uint2*>(vr);
-                const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16);
-                vb[j] = __builtin_bit_cast(abf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
+                const uint16_t* vr = vrow + (d0 + j) * 16;
+                const ai16x4_t v0 = lds_read_tr16x4(vr);
+                const ai16x4_t v1 = lds_read_tr16x4(vr + 16 * Lds::kKStride);
+                vb[j] = __builtin_bit_cast(abf16x8_t, (ai16x8_t){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
             }
 #pragma unroll
             for (int j = 0; j < kDBH; ++j)
