@@ -273,9 +273,12 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
             const int c = tid + u * kAThreads;
             const int kk = c / (D / 8), d8 = (c % (D / 8)) * 8;
             *reinterpret_cast<uint4*>(sk + kk * Lds::kKStride + d8) = kc[u];
-            const uint32_t keep = 0u - ((keepb >> kk) & 1u);  // all ones or zeros
-            *reinterpret_cast<uint4*>(sv + kk * Lds::kKStride + d8) =
-                make_uint4(vc[u].x & keep, vc[u].y & keep, vc[u].z & keep, vc[u].w & keep);
+            uint4 vw = vc[u];
+            if (keepb != 0xffffffffu) {  // uniform: a tile with keys to drop
+                const uint32_t keep = 0u - ((keepb >> kk) & 1u);  // all ones or zeros
+                vw = make_uint4(vw.x & keep, vw.y & keep, vw.z & keep, vw.w & keep);
+            }
+            *reinterpret_cast<uint4*>(sv + kk * Lds::kKStride + d8) = vw;
         }
     };
     // two LDS buffers: while the waves work on tile t in one, tile t + 1 is
@@ -315,22 +318,29 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
                     s_kc + (kb * 16 + l16) * Lds::kKStride + ds * 32 + 8 * lg);
                 acc4[kb][ds & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qreg[ds], acc4[kb][ds & 1], 0, 0, 0);
             }
-        // masked raw scores, branch-free: the scores are read from the
-        // matrix-core results right after the contraction, and the code
-        // between the two stays one basic block (a read in a later block
-        // after a branch got stale results here).  A key row q may not see
-        // gets -inf; bit 16 kb + i of `vis` is this lane's key 16 kb + 4 lg + i
-        const uint32_t vis = tile_bits(key0, vis_or) >> (4 * lg);
+        // raw scores: the matrix-core results are first read right after
+        // the contraction, in its basic block (a read in a later block after
+        // a branch got stale results here)
         float sr[2][4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const af32x4_t acc = acc4[kb][0] + acc4[kb][1];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int bit = 16 * kb + i;
-                const uint32_t okm = static_cast<uint32_t>(static_cast<int32_t>(vis << (31 - bit)) >> 31);
-                sr[kb][i] = __uint_as_float((__float_as_uint(acc[i]) & okm) | (0xff800000u & ~okm));
-            }
+            for (int i = 0; i < 4; ++i) sr[kb][i] = acc[i];
+        }
+        // masked, unless every key of the tile is visible to every row (a
+        // whole tile of a prefix partition): a key row q may not see gets
+        // -inf; bit 16 kb + i of `vis` is this lane's key 16 kb + 4 lg + i
+        if (tree || hi - key0 < kTileKeys) {  // uniform
+            const uint32_t vis = tile_bits(key0, vis_or) >> (4 * lg);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int bit = 16 * kb + i;
+                    const uint32_t okm = static_cast<uint32_t>(static_cast<int32_t>(vis << (31 - bit)) >> 31);
+                    sr[kb][i] = __uint_as_float((__float_as_uint(sr[kb][i]) & okm) | (0xff800000u & ~okm));
+                }
         }
         // online softmax per query row (the row's scores sit in lanes l16,
         // l16 + 16, l16 + 32, l16 + 48), in the log2 domain: the scale is
@@ -348,24 +358,23 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
         // output rows are rescaled a few times per partition instead of at
         // almost every tile.  The first finite score always moves it.
         const bool grow = mt > m_run + kRescaleSlack;
-        const float m_new = grow ? mt : m_run;
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float factor = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // 0 while nothing was seen
+        const float m_old = m_run;
+        if (grow) m_run = mt;
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
         float pr[2][4];
-        float ps = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                pr[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sr[kb][i], scale2, -m_use));
-                ps += pr[kb][i];
-            }
+            for (int i = 0; i < 4; ++i) pr[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sr[kb][i], scale2, -m_use));
+        // the lane's eight weights summed pairwise (a chain three deep)
+        float ps = ((pr[0][0] + pr[0][1]) + (pr[0][2] + pr[0][3])) + ((pr[1][0] + pr[1][1]) + (pr[1][2] + pr[1][3]));
         ps = pair32_sum(pair16_sum(ps));
-        l_run = l_run * factor + ps;
-        m_run = m_new;
-        // rescale the output rows 4 lg + i of this lane's blocks, unless no
-        // row of the wave moved its reference; the test is wave-uniform
+        // rescale the row's sum and the output rows 4 lg + i of this lane's
+        // blocks, unless no row of the wave moved its reference; the test is
+        // wave-uniform
         if (__ballot(grow) != 0ull) {
+            const float factor = grow ? __builtin_amdgcn_exp2f(m_old - m_run) : 1.f;  // 0 while nothing was seen
+            l_run *= factor;
             float fr[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) fr[i] = __shfl(factor, 4 * lg + i, 64);
@@ -374,6 +383,7 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
 #pragma unroll
                 for (int i = 0; i < 4; ++i) o[db][i] *= fr[i];
         }
+        l_run += ps;
         // P as the A operand (row rq; k slots: keys 4 lg + j of block 0, then
         // of block 1), split into bf16 hi + lo
         uint32_t ph[4], pl[4];
