@@ -211,6 +211,9 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
 #pragma unroll
     for (int db = 0; db < kDB; ++db) o[db] = af32x4_t{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
+    // kept with m_run: the exponent offset (0 while nothing was seen) and the
+    // threshold a raw (unscaled) score must pass to move the reference
+    float m_use = 0.f, thr_raw = -INFINITY;
 
     const int ntiles = (hi - lo + kTileKeys - 1) / kTileKeys;
     constexpr int kChunks = kTileKeys * D / 8;  // 16-byte chunks of a K (or V) tile
@@ -350,29 +353,25 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sr[kb][i]);
-        mt = pair32_max(pair16_max(mt)) * scale2;
-        // The row's reference maximum m_run moves only when a score exceeds
-        // it by more than kRescaleSlack (log2 units): weights then stay below
-        // 2^kRescaleSlack, far inside fp32 and the hi + lo split, and the
-        // output rows are rescaled a few times per partition instead of at
-        // almost every tile.  The first finite score always moves it.
-        const bool grow = mt > m_run + kRescaleSlack;
-        const float m_old = m_run;
-        if (grow) m_run = mt;
-        const float m_use = m_run == -INFINITY ? 0.f : m_run;
-        float pr[2][4];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pr[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sr[kb][i], scale2, -m_use));
-        // the lane's eight weights summed pairwise (a chain three deep)
-        float ps = ((pr[0][0] + pr[0][1]) + (pr[0][2] + pr[0][3])) + ((pr[1][0] + pr[1][1]) + (pr[1][2] + pr[1][3]));
-        ps = pair32_sum(pair16_sum(ps));
-        // rescale the row's sum and the output rows 4 lg + i of this lane's
-        // blocks, unless no row of the wave moved its reference; the test is
-        // wave-uniform
-        if (__ballot(grow) != 0ull) {
+            for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sr[kb][i]);  // this lane's raw maximum
+        // The row's reference maximum m_run (the same in the row's four
+        // lanes) moves only when a score exceeds it by more than
+        // kRescaleSlack (log2 units): weights then stay below 2^kRescaleSlack,
+        // far inside fp32 and the hi + lo split, and the output rows are
+        // rescaled a few times per partition instead of at almost every
+        // tile.  The first finite score always moves it.  A row moves only
+        // when one of its lanes' raw maxima passes thr_raw, so the row
+        // maximum is formed only on tiles where some lane of the wave does
+        // (the test is wave-uniform).
+        if (__ballot(mt > thr_raw) != 0ull) {
+            const float mrow = pair32_max(pair16_max(mt)) * scale2;
+            const bool grow = mrow > m_run + kRescaleSlack;
+            const float m_old = m_run;
+            if (grow) m_run = mrow;
+            m_use = m_run == -INFINITY ? 0.f : m_run;
+            thr_raw = (m_run + kRescaleSlack) / scale2;
+            // rescale this lane's share of the row's sum and the output rows
+            // 4 lg + i of this lane's blocks
             const float factor = grow ? __builtin_amdgcn_exp2f(m_old - m_run) : 1.f;  // 0 while nothing was seen
             l_run *= factor;
             float fr[4];
@@ -383,7 +382,14 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
 #pragma unroll
                 for (int i = 0; i < 4; ++i) o[db][i] *= fr[i];
         }
-        l_run += ps;
+        float pr[2][4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pr[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sr[kb][i], scale2, -m_use));
+        // this lane's share of the row's sum: its eight weights summed
+        // pairwise (a chain three deep); the four shares are added at the end
+        l_run += ((pr[0][0] + pr[0][1]) + (pr[0][2] + pr[0][3])) + ((pr[1][0] + pr[1][1]) + (pr[1][2] + pr[1][3]));
         // P as the A operand (row rq; k slots: keys 4 lg + j of block 0, then
         // of block 1), split into bf16 hi + lo
         uint32_t ph[4], pl[4];
@@ -440,6 +446,7 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
             for (int db = 0; db < kDB; ++db) dst[db * 16] = o[db][i];
         }
     }
+    l_run = pair32_sum(pair16_sum(l_run));  // the row's sum from its four lanes' shares
     if (lg == 0 && vq) {
         float* ml = a.ws_ml + ((base + h0 + hq) * N + iq) * 2;
         ml[0] = m_run;
