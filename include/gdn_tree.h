@@ -477,7 +477,8 @@ size_t gdn_tree_attention_workspace_bytes(int32_t B, int32_t N, int32_t Hq, int3
  *            not matter
  *   splits   1..1024: partitions of the prefix (each an equal share of
  *            S - R positions), plus one for the candidates
- *   scale    softmax scale (e.g. 1 / sqrt(D))
+ *   scale    softmax scale (e.g. 1 / sqrt(D)); positive, with scale * log2(e)
+ *            finite (else GDN_ERR_ARG)
  * bf16, D in {128, 256}, N <= 64, R <= 64, Hq % Hkv == 0; q, k_cache,
  * v_cache 16-byte aligned.  flags: GDN_F_OUT_BF16. */
 int32_t gdn_tree_attention(const gdn_tree_desc *d, const void *q, const void *k_cache,

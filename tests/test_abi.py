@@ -246,6 +246,9 @@ def test_attention_argument_checks_fail_before_launch(lib):
     assert call(wsb=ws - 4) == g.GDN_ERR_ARG                 # workspace too small
     assert call(S=31) == g.GDN_ERR_ARG                       # cache shorter than the candidates
     assert call(scale=0.0) == g.GDN_ERR_ARG
+    assert call(scale=float("nan")) == g.GDN_ERR_ARG
+    assert call(scale=float("inf")) == g.GDN_ERR_ARG
+    assert call(scale=3.0e38) == g.GDN_ERR_ARG                 # scale * log2(e) overflows fp32
     assert call(fl=g.GDN_F_NORM_QK) == g.GDN_ERR_ARG
     assert call(d=big_r) == g.GDN_ERR_UNSUPPORTED            # R > 64
     assert call(k=ctypes.c_void_p(264)) == g.GDN_ERR_ARG     # not 16-byte aligned
@@ -261,6 +264,7 @@ def test_attention_argument_checks_fail_before_launch(lib):
     assert call_z(D=64) == g.GDN_ERR_UNSUPPORTED
     assert call_z(Hq=15) == g.GDN_ERR_ARG
     assert call_z(scale=0.0) == g.GDN_ERR_ARG
+    assert call_z(scale=float("inf")) == g.GDN_ERR_ARG
     assert call_z(out=None) == g.GDN_ERR_ARG
     assert W(2, 27, 16, 256, 1024) > g.GDN_ATTN_NOALLOC_SCRATCH_BYTES
     assert call_z(splits=1024) == g.GDN_ERR_UNSUPPORTED       # partials past the scratch

@@ -425,7 +425,10 @@ int32_t check_attention(const gdn_tree_desc* d, const void* q, const void* k_cac
     if (d->R > 64) return GDN_ERR_UNSUPPORTED;
     if (splits < 1 || splits > 1024) return GDN_ERR_UNSUPPORTED;
     if (S < d->R) return GDN_ERR_ARG;
-    if (!(scale > 0.0f) || (flags & ~GDN_F_OUT_BF16) != 0) return GDN_ERR_ARG;
+    // the kernels work with scale * log2(e) (the exponent base 2): it must
+    // be a finite positive number
+    const float scale2 = scale * 1.4426950408889634f;
+    if (!(scale > 0.0f) || !(scale2 <= 3.40282347e38f) || (flags & ~GDN_F_OUT_BF16) != 0) return GDN_ERR_ARG;
     if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
         !aligned(out, (flags & GDN_F_OUT_BF16) ? 2 : 4))
         return GDN_ERR_ARG;
