@@ -110,6 +110,19 @@ def test_odd_group_size_and_scale():
     _cmp(go, oo)
 
 
+@pytest.mark.parametrize("scale", [1e-4, 2.0])
+def test_extreme_scales(scale):
+    # a large scale makes each row's softmax nearly one-hot, so the rows'
+    # reference maxima move on many tiles (the cross-lane maximum and the
+    # rescale run often); a tiny one makes the weights nearly uniform and the
+    # references never move after the first tile
+    c = gi.make_attention_case(31, B=2, N=11, R=16, Hq=4, Hkv=2, D=256, ctx=[700, 300], S=720)
+    go, err, st = run_attention(c, splits=3, scale=scale)
+    assert err == 0
+    oo, _ = oracle(c, st, scale=scale)
+    _cmp(go, oo)
+
+
 def test_shared_topology():
     c = gi.make_attention_case(16, B=3, N=13, R=16, Hq=4, Hkv=2, D=128, ctx=[5, 40, 77], S=100,
                                shared=True)
