@@ -123,6 +123,30 @@ def test_extreme_scales(scale):
     _cmp(go, oo)
 
 
+# seeded random shapes: tree size, candidate rows, head grouping, head
+# dimension, context lengths (0 and lengths that end inside a tile among
+# them), partition count and softmax scale
+_SWEEP = [
+    # seed, B, N, R, Hq, Hkv, D, ctx, S, splits, scale
+    (101, 2, 1, 1, 2, 1, 128, [0, 33], 40, 1, 0.09),
+    (102, 3, 7, 8, 8, 2, 256, [31, 32, 95], 110, 5, 0.0625),
+    (103, 1, 40, 48, 4, 4, 128, [257], 320, 8, 0.3),
+    (104, 2, 64, 64, 2, 2, 256, [1, 200], 270, 3, 0.02),
+    (105, 2, 23, 30, 12, 4, 128, [63, 64], 100, 2, 0.125),
+    (106, 4, 5, 16, 6, 3, 256, [0, 17, 48, 160], 180, 7, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", _SWEEP, ids=[str(c[0]) for c in _SWEEP])
+def test_random_shape_sweep(case):
+    seed, B, N, R, Hq, Hkv, D, ctx, S, splits, scale = case
+    c = gi.make_attention_case(seed, B=B, N=N, R=R, Hq=Hq, Hkv=Hkv, D=D, ctx=ctx, S=S)
+    go, err, st = run_attention(c, splits=splits, scale=scale)
+    assert err == 0
+    oo, _ = oracle(c, st, scale=scale)
+    _cmp(go, oo)
+
+
 def test_shared_topology():
     c = gi.make_attention_case(16, B=3, N=13, R=16, Hq=4, Hkv=2, D=128, ctx=[5, 40, 77], S=100,
                                shared=True)
