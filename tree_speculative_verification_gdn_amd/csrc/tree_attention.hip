@@ -296,7 +296,7 @@ __global__ void __launch_bounds__(kAThreads) tree_attn_kernel(const AttnArgs a) 
 #pragma unroll
     for (int ds = 0; ds < kDS; ++ds)
         qreg[ds] = *reinterpret_cast<const abf16x8_t*>(s_q + rq * Lds::kKStride + ds * 32 + 8 * lg);
-    const float scale2 = a.scale2;  // > 0 (checked on the host)
+    const float scale2 = a.scale2;  // positive and finite (checked on the host)
     for (int tile = 0; tile < ntiles; ++tile) {
         const int key0 = lo + tile * kTileKeys;
         const int cur = tile & 1;
