@@ -130,6 +130,33 @@ def test_layer_step_chains(N):
     _cmp(c1, c2, gr, orr)
 
 
+# seeded random shapes of the one-launch layer step (exact conv): tree size
+# and shape, rows per request, conv width, head counts, q/k normalisation,
+# path rule; Lmax follows the tree depth (paths past one segment of 8 nodes
+# take the long-path kernel)
+_SWEEP = [
+    # seed, N, R, bmax, depth_max, W, Hv, Hqk, norm_qk, path
+    (301, 1, 1, 1, 0, 4, 2, 1, False, "uniform_len"),
+    (302, 5, 9, 2, 3, 2, 4, 2, True, "full"),
+    (303, 16, 16, 4, 2, 3, 6, 3, False, "leaf_full"),
+    (304, 31, 40, 2, 9, 4, 4, 4, True, "uniform_len"),
+    (305, 32, 32, 3, 6, 1, 2, 2, False, "full"),
+]
+
+
+@pytest.mark.parametrize("case", _SWEEP, ids=[str(c[0]) for c in _SWEEP])
+def test_layer_step_random_shape_sweep(case):
+    seed, N, R, bmax, depth, W, Hv, Hqk, norm, path = case
+    cfg = _exact(gi.CONFIGS[4], N=N, R=R, bmax=bmax, depth_max=depth, conv_W=W, Hv=Hv, Hqk=Hqk,
+                 conv_C=2 * Hqk * 128 + Hv * 128, norm_qk=norm, path=path)
+    c1, c2 = two_step_case(cfg, seed=seed, B=4, extra_slots=1, conv_values="dyadic")
+    gr = run_gpu_layer(c1, c2)
+    orr = run_oracle_two_steps(c1, c2)
+    assert gr["err"] == orr["err"] == 0
+    _check_resolve(c1, gr, c1["P"])
+    _cmp(c1, c2, gr, orr)
+
+
 def test_layer_step_first_step_and_no_output_buffer():
     # nothing accepted before (every path empty): history copied, states kept
     cfg = _exact(gi.CONFIGS[4])
