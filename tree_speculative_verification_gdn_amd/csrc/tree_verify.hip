@@ -32,7 +32,7 @@
 //
 // Work decomposition: one 256-thread workgroup per (request, value head); the
 // two value heads that share a qk head are placed on the same XCD so their
-// K/Q rows are read from HBM once.
+// K/Q rows are read from HBM once (except in the commit + verify steps).
 #include "mfma_common.h"
 
 namespace gdn {
@@ -299,7 +299,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     const int l32 = lane & 31;
     const int r_own = wave * 32 + l32;  // value row this lane owns in every MFMA
 
-    const uint32_t unit = xcd_local_order(blockIdx.x, gridDim.x);
+    // the steady-state steps (commit + verify) take units in plain workgroup
+    // order: measured faster than keeping a request's qk-sharing heads on one
+    // XCD on the 27-node, B = 128 workload (layer step 145-148 against
+    // 150-151 us per launch, commit + verify 127 against 129 us; 64-node
+    // trees unchanged), although the two heads of a qk group then fetch
+    // their shared rows on two XCDs
+    const uint32_t unit = COMMIT ? blockIdx.x : xcd_local_order(blockIdx.x, gridDim.x);
     const int b = static_cast<int>(unit / Hv);
     const int h = static_cast<int>(unit % Hv);
     const int t = shared ? 0 : b;
